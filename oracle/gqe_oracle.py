@@ -1,0 +1,328 @@
+"""CPU float64 oracle for the Grouped Query Experts (GQE) attention layer, prefill forward.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import or run this module; the product path never does.
+It shares no code with the HIP implementation: it is written from the pages
+that describe the method, in float64 numpy, plainly and slowly.
+
+Sources (the five pages describe one preprint, arXiv 2606.20945,
+"Grouped Query Experts: Mixture-of-Experts on GQA Self-Attention"):
+
+* [pptc]   review on pptc.cn (news/49069): Table 1 and the prefill speed-ups
+           (section 4.2), ablation (4.3), related work (5), limitations (6),
+           conclusion (7).
+* [gist-nl] gist.science/nl technical summary, "Architectuur en Routing",
+           "Training en Loss", "Experimentele Resultaten".
+* [gist-pt] gist.science/pt technical summary, "Arquitetura e Roteamento".
+* [hotpaper] hotpaper.ai summary, "핵심 아이디어" (core idea) and
+           "기술적 접근법" (technical approach).
+
+What the layer computes (the plain definition; the method reaches exactly this
+result, its sparsity being the routing itself):
+
+1. router logits r[t, g, e] = x[t] . W_r[g*E+e] + b_r[g*E+e]  (a router looks
+   at each token and scores the query-head experts of every GQA group;
+   [gist-nl] Architectuur en Routing).
+2. p[t, g, :] = softmax over the E experts of group g (softmax is taken first,
+   inside the group; [pptc] section 7).
+3. the k experts with the largest p are selected in every group (top-k within
+   each fixed group, every group participates; [pptc] section 5), listed in
+   rank order, ties to the lower expert index.
+4. w[t, g, j] = p of the j-th selected expert divided by the sum of p over the
+   k selected (renormalized scoring; [hotpaper] technical approach).
+5. dispatch: for every (b, g, e) the ascending list of positions t that chose
+   expert e, with the rank j it was chosen at.
+6. K and V are the dense, unchanged GQA projections of group g ([gist-nl]
+   Architectuur en Routing: the KV path stays dense).
+7. every selected expert (a query head with its own W_q block) attends
+   causally to its group's K/V; unselected experts compute nothing ([pptc]
+   section 5: a token that skips an expert still attends to that group's KV).
+8. one always-on shared head attends for every token ([gist-nl]).
+9. the weighted slot is the sum over groups and selected experts of w times
+   the expert output ([gist-nl]: a weighted sum of the selected experts'
+   outputs using router probabilities).
+10. the slot vector [k*G hard slots, shared, weighted] of width (k*G+2)*d_h
+    ([hotpaper] core idea: W_O resized to k*G+2 slots) ...
+11. ... goes through W_O.
+
+Readings where the pages are silent (each is listed in the design notes):
+scale 1/sqrt(d_h); hard slots ordered group-major then by rank; weighted slot
+is a plain sum over groups; renormalization is per group; the shared head has
+its own W_q rows and reads KV group ``shared_kv_group`` (0); no RoPE, no
+projection biases; causal mask s <= t; weights in [out, in] layout.
+
+Ranking on p is done on the logits r: within a group p is proportional to
+exp(r), so both orders are the same, and ranking on r avoids ties that
+rounding p could create.  Logits whose top-k decision is closer than 1e-12 are
+recomputed with an exactly rounded sum (math.fsum of the exact products).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# step 1-4: router, in-group softmax, top-k, renormalization
+# --------------------------------------------------------------------------
+
+
+def router_logits(x: np.ndarray, wr: np.ndarray, br: np.ndarray, n_groups: int,
+                  n_experts: int) -> np.ndarray:
+    """r[T, G, E] = x[T, d] . W_r[G*E, d]^T + b_r  (step 1, [gist-nl])."""
+    r = x @ wr.T + br[None, :]
+    return r.reshape(x.shape[0], n_groups, n_experts)
+
+
+def exact_logits(x_row: np.ndarray, wr: np.ndarray, br: np.ndarray) -> np.ndarray:
+    """Correctly rounded logits for one token: fsum of the exact products.
+
+    Products of two bf16 or two fp32 values are exact in float64; fsum rounds
+    their sum once.
+    """
+    return np.array([math.fsum(list(x_row * wr[c]) + [float(br[c])])
+                     for c in range(wr.shape[0])])
+
+
+def group_softmax(r: np.ndarray) -> np.ndarray:
+    """p = softmax over the experts of each group (step 2, [pptc] section 7)."""
+    z = r - r.max(axis=-1, keepdims=True)
+    ez = np.exp(z)
+    return ez / ez.sum(axis=-1, keepdims=True)
+
+
+def topk_in_group(r: np.ndarray, top_k: int) -> np.ndarray:
+    """idx[..., k]: the k best experts of every group, best first (step 3).
+
+    Order: larger logit first, then lower expert index (a stable sort of the
+    negated logits keeps the lower index first among equals).
+    """
+    order = np.argsort(-r, axis=-1, kind="stable")
+    return order[..., :top_k].astype(np.int32)
+
+
+def renormalize(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """w = p[idx] / sum(p[idx]) over the k selected of each group (step 4)."""
+    ps = np.take_along_axis(p, idx.astype(np.int64), axis=-1)
+    return ps / ps.sum(axis=-1, keepdims=True)
+
+
+def route(x: np.ndarray, wr: np.ndarray, br: np.ndarray, n_groups: int, n_experts: int,
+          top_k: int, exact_margin: float = 1e-12):
+    """Steps 1-4 for tokens x[T, d].  Returns (r, p, idx, w), shapes [T,G,E] / [T,G,k]."""
+    r = router_logits(x, wr, br, n_groups, n_experts)
+    # decisions that rounding could flip: recompute those tokens exactly
+    srt = -np.sort(-r, axis=-1)
+    m = min(top_k, n_experts - 1)                         # rank gaps that decide idx
+    gaps = srt[..., :m] - srt[..., 1:m + 1]
+    close = (gaps < exact_margin * (1.0 + np.abs(srt[..., :m]))).any(axis=(-1, -2))
+    for t in np.nonzero(close)[0]:
+        r[t] = exact_logits(x[t], wr, br).reshape(n_groups, n_experts)
+    p = group_softmax(r)
+    idx = topk_in_group(r, top_k)
+    w = renormalize(p, idx)
+    return r, p, idx, w
+
+
+# --------------------------------------------------------------------------
+# step 5: dispatch lists
+# --------------------------------------------------------------------------
+
+
+def dispatch(idx: np.ndarray, n_experts: int):
+    """Per-(b, g, e) token lists (step 5, [pptc] section 6: sparse scheduling).
+
+    idx is int [B, L, G, k].  Returns counts int32 [B, G, E]; offsets int32
+    [B*G*E+1] (exclusive prefix sum of counts in (b, g, e) row-major order);
+    pos and slot, int32 [B*L*G*k]: for list (b, g, e), entries
+    offsets[(b*G+g)*E+e] onwards hold the positions t that selected e, in
+    ascending order, and the rank j at which they selected it.
+    """
+    B, L, G, k = idx.shape
+    counts = np.zeros((B, G, n_experts), dtype=np.int32)
+    pos_lists, slot_lists = [], []
+    for b in range(B):
+        for g in range(G):
+            for e in range(n_experts):
+                hit = idx[b, :, g, :] == e              # [L, k]
+                t_sel, j_sel = np.nonzero(hit)           # row-major: ascending t
+                counts[b, g, e] = t_sel.size
+                pos_lists.append(t_sel)
+                slot_lists.append(j_sel)
+    offsets = np.zeros(B * G * n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts.reshape(-1))
+    pos = np.concatenate(pos_lists).astype(np.int32)
+    slot = np.concatenate(slot_lists).astype(np.int32)
+    return counts, offsets.astype(np.int32), pos, slot
+
+
+# --------------------------------------------------------------------------
+# steps 6-8: projections and causal attention
+# --------------------------------------------------------------------------
+
+
+def head_rows(w: np.ndarray, head: int, head_dim: int) -> np.ndarray:
+    """The d_h rows of an [out, in] projection that belong to one head."""
+    return w[head * head_dim:(head + 1) * head_dim]
+
+
+def kv_project(x_b: np.ndarray, w: np.ndarray, n_groups: int, head_dim: int,
+               upto: int) -> np.ndarray:
+    """Dense K (or V) of every group for positions < upto: [G, upto, d_h] (step 6)."""
+    out = np.empty((n_groups, upto, head_dim))
+    step = 32768
+    for t0 in range(0, upto, step):
+        t1 = min(upto, t0 + step)
+        blk = x_b[t0:t1] @ w.T                           # [n, G*d_h]
+        out[:, t0:t1] = blk.reshape(t1 - t0, n_groups, head_dim).transpose(1, 0, 2)
+    return out
+
+
+def causal_attention(q: np.ndarray, t: np.ndarray, K: np.ndarray, V: np.ndarray,
+                     scale: float) -> np.ndarray:
+    """o[i] = sum_{s <= t[i]} softmax_s(scale * q[i] . K[s]) V[s]  (step 7).
+
+    Exact two-pass softmax (maximum, then exponentials and their sum), rows
+    batched only by sharing the key range [0, max t].
+    """
+    o = np.empty((q.shape[0], V.shape[1]))
+    order = np.argsort(t, kind="stable")
+    chunk = 256
+    for c0 in range(0, len(order), chunk):
+        rows = order[c0:c0 + chunk]
+        tmax = int(t[rows].max()) + 1
+        s = scale * (q[rows] @ K[:tmax].T)               # [n, tmax]
+        s[np.arange(tmax)[None, :] > t[rows][:, None]] = -np.inf
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        o[rows] = (e @ V[:tmax]) / e.sum(axis=1, keepdims=True)
+    return o
+
+
+# --------------------------------------------------------------------------
+# steps 9-11: output construction
+# --------------------------------------------------------------------------
+
+
+def expert_head(g: int, e: int, n_experts: int) -> int:
+    """W_q head index of expert e of group g (the G*E routed heads, group-major)."""
+    return g * n_experts + e
+
+
+def weighted_slot(w_rows: np.ndarray, o_hard: np.ndarray) -> np.ndarray:
+    """o_w[n] = sum_g sum_j w[n, g, j] * o[n, g, j]  (step 9, [gist-nl], [gist-pt]).
+
+    w_rows [n, G, k]; o_hard [n, G, k, d_h].  A plain sum over groups.
+    """
+    return np.einsum("ngj,ngjd->nd", w_rows, o_hard)
+
+
+def slot_vector(o_hard: np.ndarray, o_sh: np.ndarray, o_w: np.ndarray) -> np.ndarray:
+    """[hard slots (group-major, rank-minor) | shared | weighted], width (k*G+2)*d_h (step 10)."""
+    n = o_hard.shape[0]
+    return np.concatenate([o_hard.reshape(n, -1), o_sh, o_w], axis=1)
+
+
+def output_projection(s: np.ndarray, wo: np.ndarray) -> np.ndarray:
+    """y = s . W_O^T with W_O in [out, in] layout, [d, (k*G+2)*d_h] (step 11)."""
+    return s @ wo.T
+
+
+# --------------------------------------------------------------------------
+# full layer
+# --------------------------------------------------------------------------
+
+
+def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
+                shared_kv_group=0, scale=None, positions=None):
+    """GQE prefill forward (steps 1-11) in float64.
+
+    x: [B, L, d]; wq [(G*E+1)*d_h, d]; wk, wv [G*d_h, d]; wr [G*E, d];
+    wo [d, (k*G+2)*d_h]; br [G*E].  All float64 holding the exact input values.
+    ``positions`` (sorted ints) restricts the attention/output steps to those
+    query positions in every sequence; routing and dispatch always cover
+    every token.  Returns a dict with r, p, idx, w ([B,L,G,*]), counts,
+    offsets, pos, slot, and for the checked positions: q [B,n,k*G+1,d_h]
+    (slot-head order: hard slot g*k+j, then the shared head), k_ and v
+    ([B,G,upto,d_h]), o [B,n,k*G+1,d_h] (attention outputs), s
+    [B,n,(k*G+2)*d_h] (slot vectors) and y [B,n,d].
+    """
+    B, L, d = x.shape
+    G, E, k, dh = n_groups, n_experts, top_k, head_dim
+    scale = 1.0 / math.sqrt(dh) if scale is None else scale
+    pos_q = np.arange(L) if positions is None else np.asarray(positions, dtype=np.int64)
+    n = len(pos_q)
+    upto = int(pos_q.max()) + 1
+
+    r, p, idx, w = route(x.reshape(B * L, d), wr, br, G, E, k)
+    r, p = r.reshape(B, L, G, E), p.reshape(B, L, G, E)
+    idx, w = idx.reshape(B, L, G, k), w.reshape(B, L, G, k)
+    counts, offsets, pos, slot = dispatch(idx, E)
+
+    S = k * G + 1                                         # attention slot-heads
+    q_all = np.empty((B, n, S, dh))
+    o_all = np.empty((B, n, S, dh))
+    s_all = np.empty((B, n, (k * G + 2) * dh))
+    K_all = np.empty((B, G, upto, dh))
+    V_all = np.empty((B, G, upto, dh))
+    for b in range(B):
+        xb = x[b]
+        K_all[b] = kv_project(xb, wk, G, dh, upto)
+        V_all[b] = kv_project(xb, wv, G, dh, upto)
+        xq = xb[pos_q]                                    # [n, d]
+        o_hard = np.empty((n, G, k, dh))
+        for g in range(G):
+            for j in range(k):
+                e_sel = idx[b, pos_q, g, j]               # [n]
+                qh = np.empty((n, dh))
+                for e in range(E):                        # the selected expert's own W_q rows
+                    m = e_sel == e
+                    if m.any():
+                        qh[m] = xq[m] @ head_rows(wq, expert_head(g, e, E), dh).T
+                q_all[b, :, g * k + j] = qh
+                o_hard[:, g, j] = causal_attention(qh, pos_q, K_all[b, g], V_all[b, g], scale)
+        q_sh = xq @ head_rows(wq, G * E, dh).T            # step 8: always-on shared head
+        o_sh = causal_attention(q_sh, pos_q, K_all[b, shared_kv_group],
+                                V_all[b, shared_kv_group], scale)
+        q_all[b, :, k * G] = q_sh
+        o_all[b, :, :k * G] = o_hard.reshape(n, G * k, dh)
+        o_all[b, :, k * G] = o_sh
+        o_w = weighted_slot(w[b, pos_q], o_hard)
+        s_all[b] = slot_vector(o_hard, o_sh, o_w)
+    y = output_projection(s_all, wo)
+    return dict(r=r, p=p, idx=idx, w=w, counts=counts, offsets=offsets, pos=pos, slot=slot,
+                q=q_all, k_=K_all, v=V_all, o=o_all, s=s_all, y=y, positions=pos_q)
+
+
+def gqa_forward(x, wq_dense, wk, wv, wo_dense, n_groups, n_experts, head_dim, scale=None,
+                positions=None):
+    """Dense GQA baseline: all G*E query heads active, head h reads KV group h // E.
+
+    wq_dense [G*E*d_h, d]; wo_dense [d, G*E*d_h].  Returns q, o [B,n,G*E,d_h] and
+    y [B,n,d] for the checked positions.  ([pptc] section 4.2: the all-active
+    GQA comparison model.)
+    """
+    B, L, d = x.shape
+    G, E, dh = n_groups, n_experts, head_dim
+    H = G * E
+    scale = 1.0 / math.sqrt(dh) if scale is None else scale
+    pos_q = np.arange(L) if positions is None else np.asarray(positions, dtype=np.int64)
+    n = len(pos_q)
+    upto = int(pos_q.max()) + 1
+    q_all = np.empty((B, n, H, dh))
+    o_all = np.empty((B, n, H, dh))
+    for b in range(B):
+        K = kv_project(x[b], wk, G, dh, upto)
+        V = kv_project(x[b], wv, G, dh, upto)
+        xq = x[b][pos_q]
+        for h in range(H):
+            qh = xq @ head_rows(wq_dense, h, dh).T
+            q_all[b, :, h] = qh
+            o_all[b, :, h] = causal_attention(qh, pos_q, K[h // E], V[h // E], scale)
+    y = output_projection(o_all.reshape(B, n, H * dh), wo_dense)
+    return dict(q=q_all, o=o_all, y=y, positions=pos_q)
+
+
+def attention_flops(batch: int, seq_len: int, heads: int, head_dim: int) -> int:
+    """Algorithmic flops of causal attention: QK^T and PV, 2*d_h each per pair s <= t."""
+    return 2 * 2 * head_dim * heads * batch * seq_len * (seq_len + 1) // 2

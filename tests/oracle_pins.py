@@ -1,0 +1,397 @@
+"""Checks that pin the CPU oracle to facts other than its own code.
+
+Each ``pin_*`` function takes an oracle module and raises AssertionError when
+the oracle disagrees with what the pages or the mathematics fix.  They are run
+on the real oracle (tests/test_oracle_pins.py) and on copies with planted
+mistakes (tests/test_oracle_mutations.py), which each must fail at least one.
+
+Sources: the pages about "Grouped Query Experts: Mixture-of-Experts on GQA
+Self-Attention" (arXiv 2606.20945): the pptc.cn review (sections 4.2, 5, 7),
+the gist.science technical summaries (Architectuur en Routing / Arquitetura e
+Roteamento, Experimentele Resultaten) and the hotpaper.ai summary (core idea,
+technical approach).
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny_layer(rng, B=2, L=7, d=12, G=2, E=3, k=2, dh=4, w_std=0.5):
+    """Random float64 weights of a tiny GQE layer ([out, in] layouts)."""
+    return dict(
+        x=rng.standard_normal((B, L, d)),
+        wq=rng.standard_normal(((G * E + 1) * dh, d)) * w_std,
+        wk=rng.standard_normal((G * dh, d)) * w_std,
+        wv=rng.standard_normal((G * dh, d)) * w_std,
+        wr=rng.standard_normal((G * E, d)) * w_std,
+        wo=rng.standard_normal((d, (k * G + 2) * dh)) * w_std,
+        br=np.zeros(G * E),
+        G=G, E=E, k=k, dh=dh)
+
+
+def run(orc, t, **kw):
+    args = dict(shared_kv_group=0)
+    args.update(kw)
+    return orc.gqe_forward(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"],
+                           t["G"], t["E"], t["k"], t["dh"], **args)
+
+
+# ---------------------------------------------------------------------------
+# P1: k = E with a uniform router reduces to dense GQA
+# ---------------------------------------------------------------------------
+
+def pin_k_equals_e_is_dense_gqa(orc):
+    """k=E, W_r=0 (uniform p, ties in index order), shared and weighted rows of
+    W_O zeroed  =>  the GQE layer equals dense GQA with W_O^dense = the hard-slot
+    columns of W_O (the all-active GQA comparison model, pptc.cn section 4.2)."""
+    rng = np.random.default_rng(11)
+    for (G, E) in [(2, 3), (3, 2)]:
+        t = tiny_layer(rng, G=G, E=E, k=E)
+        t["wr"] = np.zeros_like(t["wr"])
+        dh = t["dh"]
+        wo = t["wo"].copy()
+        wo[:, G * E * dh:] = 0.0
+        t["wo"] = wo
+        y = run(orc, t)["y"]
+        ref = orc.gqa_forward(t["x"], t["wq"][:G * E * dh], t["wk"], t["wv"],
+                              wo[:, :G * E * dh], G, E, dh)["y"]
+        assert np.allclose(y, ref, rtol=0, atol=1e-12), np.abs(y - ref).max()
+
+
+# ---------------------------------------------------------------------------
+# P2, P9, P11: renormalized weights
+# ---------------------------------------------------------------------------
+
+def pin_weights_sum_to_one(orc):
+    """Per (token, group) the k renormalized weights are >= 0 and sum to 1;
+    with k = 1 every weight is exactly 1 (hotpaper.ai: renormalized scoring)."""
+    rng = np.random.default_rng(12)
+    t = tiny_layer(rng)
+    out = run(orc, t)
+    w = out["w"]
+    assert (w >= 0).all()
+    assert np.abs(w.sum(-1) - 1.0).max() <= 1e-15
+    # the softmax itself is taken inside each group (pptc.cn section 7)
+    assert np.abs(out["p"].sum(-1) - 1.0).max() <= 1e-15
+    t1 = tiny_layer(rng, k=1)
+    w1 = run(orc, t1)["w"]
+    assert (w1 == 1.0).all()
+
+
+def pin_weights_closed_form(orc):
+    """softmax then top-k then renormalize equals a softmax over the selected
+    logits alone (the common denominator cancels)."""
+    rng = np.random.default_rng(13)
+    t = tiny_layer(rng, E=4, k=3)
+    out = run(orc, t)
+    r, idx, w = out["r"], out["idx"], out["w"]
+    rs = np.take_along_axis(r, idx.astype(np.int64), axis=-1)
+    e = np.exp(rs - rs.max(-1, keepdims=True))
+    assert np.allclose(w, e / e.sum(-1, keepdims=True), rtol=0, atol=1e-15)
+
+
+def pin_logit_shift_invariance(orc):
+    """Adding one constant to every logit of a group (through b_r) changes
+    neither the selection nor the weights (softmax inside the group)."""
+    rng = np.random.default_rng(14)
+    t = tiny_layer(rng, E=4, k=2)
+    a = run(orc, t)
+    t2 = dict(t)
+    shift = np.repeat(rng.standard_normal(t["G"]) * 3.0, t["E"])
+    t2["br"] = t["br"] + shift
+    b = run(orc, t2)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.allclose(a["w"], b["w"], rtol=0, atol=1e-14)
+    assert np.allclose(a["y"], b["y"], rtol=0, atol=1e-12)
+
+
+def pin_bias_selects(orc):
+    """A large router bias on one expert of one group makes it the first
+    choice of every token in that group, and only in that group."""
+    rng = np.random.default_rng(15)
+    t = tiny_layer(rng, G=3, E=4, k=2)
+    G, E = t["G"], t["E"]
+    br = np.zeros(G * E)
+    br[1 * E + 2] = 100.0                        # group 1, expert 2
+    t["br"] = br
+    out = run(orc, t)
+    assert (out["idx"][:, :, 1, 0] == 2).all()
+    for g in (0, 2):
+        assert not (out["idx"][:, :, g, 0] == 2).all()
+
+
+# ---------------------------------------------------------------------------
+# P3: top-k inside the group
+# ---------------------------------------------------------------------------
+
+def pin_topk_brute_force(orc):
+    """Against enumeration of every k-subset: the selected set has the
+    largest total probability, entries are distinct, in range and in
+    descending-p order, and no unselected expert beats a selected one
+    (pptc.cn section 5: top-k inside every fixed group)."""
+    rng = np.random.default_rng(16)
+    t = tiny_layer(rng, B=2, L=9, G=3, E=5, k=2)
+    out = run(orc, t)
+    p, idx = out["p"], out["idx"]
+    B, L, G, E = p.shape
+    k = idx.shape[-1]
+    for b, l, g in itertools.product(range(B), range(L), range(G)):
+        sel = [int(v) for v in idx[b, l, g]]
+        assert len(set(sel)) == k and all(0 <= v < E for v in sel)
+        best = max(itertools.combinations(range(E), k), key=lambda c: sum(p[b, l, g, list(c)]))
+        assert set(best) == set(sel)
+        ps = p[b, l, g, sel]
+        assert all(ps[i] >= ps[i + 1] for i in range(k - 1))
+        rest = [e for e in range(E) if e not in sel]
+        assert all(p[b, l, g, e] <= ps.min() for e in rest)
+
+
+def pin_tie_rule(orc):
+    """Exact ties go to the lower expert index: with W_r = 0 every group picks
+    experts 0..k-1 in that order; with integer-valued inputs and two equal
+    best rows, the lower of the two is ranked first."""
+    rng = np.random.default_rng(17)
+    t = tiny_layer(rng, G=2, E=4, k=3)
+    t["wr"] = np.zeros_like(t["wr"])
+    idx = run(orc, t)["idx"]
+    assert (idx == np.arange(3)[None, None, None, :]).all()
+    # integer-valued: every partial sum is exact in any order
+    t = tiny_layer(rng, G=2, E=4, k=2)
+    t["x"] = np.abs(rng.integers(1, 4, t["x"].shape)).astype(np.float64)
+    wr = rng.integers(-3, 1, t["wr"].shape).astype(np.float64)   # all rows <= 0 ...
+    wr[0 * 4 + 3] = 2.0                                            # ... group 0: experts 1 and 3 tie on top
+    wr[0 * 4 + 1] = 2.0
+    wr[1 * 4 + 0] = 1.0                                            # group 1: experts 0 and 2 tie on top
+    wr[1 * 4 + 2] = 1.0
+    t["wr"] = wr
+    idx = run(orc, t)["idx"]
+    assert (idx[:, :, 0, 0] == 1).all() and (idx[:, :, 0, 1] == 3).all()
+    assert (idx[:, :, 1, 0] == 0).all() and (idx[:, :, 1, 1] == 2).all()
+
+
+# ---------------------------------------------------------------------------
+# P5, P10: dispatch lists
+# ---------------------------------------------------------------------------
+
+def pin_dispatch_lists(orc):
+    """Per (b, g): counts sum to k*L; each list is strictly ascending; offsets
+    are the exclusive prefix sum in (b, g, e) order; (pos, slot) rebuild idx."""
+    rng = np.random.default_rng(18)
+    t = tiny_layer(rng, B=3, L=11, G=2, E=4, k=2)
+    out = run(orc, t)
+    idx, counts, offsets, pos, slot = (out[n] for n in ("idx", "counts", "offsets", "pos", "slot"))
+    B, L, G, k = idx.shape
+    E = counts.shape[-1]
+    assert (counts.sum(-1) == k * L).all()
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts.reshape(-1))
+    rebuilt = np.full_like(idx, -1)
+    for b, g, e in itertools.product(range(B), range(G), range(E)):
+        li = (b * G + g) * E + e
+        ps = pos[offsets[li]:offsets[li + 1]]
+        js = slot[offsets[li]:offsets[li + 1]]
+        assert (np.diff(ps) > 0).all()
+        assert ((0 <= js) & (js < k)).all()
+        rebuilt[b, ps, g, js] = e
+    assert np.array_equal(rebuilt, idx)
+
+
+def pin_active_query_ratio(orc):
+    """Every routing dispatches exactly k rows per (token, group), so the
+    causal attention work over the dispatched rows is sum_t (t+1) per row,
+    k*L(L+1)/2 per (b, g); with the always-on head the layer runs k*G+1 query
+    heads per token.  The pages' main setting (16 query heads, 8 KV groups,
+    k=1, one shared head) gives 9 of 16 active (tests/golden)."""
+    with open(os.path.join(GOLDEN, "active_query_heads.json")) as f:
+        gold = json.load(f)
+    rng = np.random.default_rng(19)
+    t = tiny_layer(rng, B=2, L=13, G=2, E=4, k=2)
+    t["br"] = np.tile([2.0, 0.0, -1.0, -4.0], 2)           # skewed loads
+    out = run(orc, t)
+    counts, offsets, pos = out["counts"], out["offsets"], out["pos"]
+    B, L, G, k = out["idx"].shape
+    E = counts.shape[-1]
+    for b, g in itertools.product(range(B), range(G)):
+        lo = offsets[(b * G + g) * E]
+        hi = offsets[(b * G + g) * E + E]
+        assert int((pos[lo:hi] + 1).sum()) == k * L * (L + 1) // 2
+    for case in gold["cases"]:
+        Gc, Ec, kc = case["kv_groups"], case["query_heads"] // case["kv_groups"], case["top_k"]
+        active = kc * Gc + 1
+        assert active == case["active_query_heads"]
+        assert active * case["ratio"][1] == case["query_heads"] * case["ratio"][0]
+        Lc = 4096
+        gqe = orc.attention_flops(1, Lc, active, 64)
+        gqa = orc.attention_flops(1, Lc, Gc * Ec, 64)
+        assert gqe * case["ratio"][1] == gqa * case["ratio"][0]
+        assert gqa == 2 * 2 * 64 * Gc * Ec * Lc * (Lc + 1) // 2
+
+
+# ---------------------------------------------------------------------------
+# P4, P7: attention against brute force and a library routine
+# ---------------------------------------------------------------------------
+
+def _loop_attention(q, K, V, t, scale):
+    """Scalar loops: o = sum_{s<=t} exp(a_s - max a) V_s / sum exp(a_s - max a)."""
+    a = [scale * sum(q[i] * K[s, i] for i in range(len(q))) for s in range(t + 1)]
+    m = max(a)
+    e = [math.exp(v - m) for v in a]
+    z = sum(e)
+    return np.array([sum(e[s] * V[s, c] for s in range(t + 1)) / z for c in range(V.shape[1])])
+
+
+def pin_attention_brute_force(orc):
+    """Every slot-head row of a tiny layer equals a scalar-loop causal
+    attention over its own group's K/V, 1e-12."""
+    rng = np.random.default_rng(20)
+    t = tiny_layer(rng, B=1, L=6, G=2, E=3, k=2, dh=3)
+    out = run(orc, t)
+    q, o, K, V = out["q"], out["o"], out["k_"], out["v"]
+    G, k, dh = t["G"], t["k"], t["dh"]
+    scale = 1.0 / math.sqrt(dh)
+    for tt in range(6):
+        for g in range(G):
+            for j in range(k):
+                ref = _loop_attention(q[0, tt, g * k + j], K[0, g], V[0, g], tt, scale)
+                assert np.allclose(o[0, tt, g * k + j], ref, rtol=0, atol=1e-12)
+        ref = _loop_attention(q[0, tt, G * k], K[0, 0], V[0, 0], tt, scale)
+        assert np.allclose(o[0, tt, G * k], ref, rtol=0, atol=1e-12)
+
+
+def pin_sdpa_cross_check(orc):
+    """The dense GQA path, and the GQE slot-heads, equal PyTorch's CPU
+    scaled_dot_product_attention in float64 with is_causal=True."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(21)
+    t = tiny_layer(rng, B=2, L=9, G=2, E=3, k=2, dh=4)
+    G, E, k, dh = t["G"], t["E"], t["k"], t["dh"]
+    dense = orc.gqa_forward(t["x"], t["wq"][:G * E * dh], t["wk"], t["wv"],
+                            t["wo"][:, :G * E * dh], G, E, dh)
+    x = torch.from_numpy(t["x"])
+    q = (x @ torch.from_numpy(t["wq"][:G * E * dh]).T).view(2, 9, G * E, dh).transpose(1, 2)
+    kk = (x @ torch.from_numpy(t["wk"]).T).view(2, 9, G, dh).transpose(1, 2)
+    vv = (x @ torch.from_numpy(t["wv"]).T).view(2, 9, G, dh).transpose(1, 2)
+    kk = kk.repeat_interleave(E, dim=1).contiguous()
+    vv = vv.repeat_interleave(E, dim=1).contiguous()
+    ref = F.scaled_dot_product_attention(q.contiguous(), kk, vv, is_causal=True)
+    assert np.allclose(dense["o"], ref.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+    out = run(orc, t, shared_kv_group=1)
+    qs = torch.from_numpy(out["q"]).transpose(1, 2).contiguous()        # [B, kG+1, L, dh]
+    grp = [g for g in range(G) for _ in range(k)] + [1]
+    kg = torch.from_numpy(out["k_"])[:, grp].contiguous()
+    vg = torch.from_numpy(out["v"])[:, grp].contiguous()
+    ref = F.scaled_dot_product_attention(qs, kg, vg, is_causal=True)
+    assert np.allclose(out["o"], ref.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(out["k_"][:, 1], kk[:, E].numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P6: closed form at the first position
+# ---------------------------------------------------------------------------
+
+def pin_first_position_closed_form(orc):
+    """At t = 0 a token attends only to itself, so every slot is that group's
+    V[0]: y[b, 0] = [V_0 (k times), ..., V_{G-1} (k times), V_shared, sum_g V_g] W_O^T,
+    whatever W_q and W_r are."""
+    rng = np.random.default_rng(22)
+    t = tiny_layer(rng, B=2, L=5, G=3, E=3, k=2)
+    G, k, dh = t["G"], t["k"], t["dh"]
+    for shared in (0, 2):
+        y0 = run(orc, t, shared_kv_group=shared)["y"][:, 0]
+        for b in range(2):
+            v0 = np.array([t["x"][b, 0] @ t["wv"][g * dh:(g + 1) * dh].T for g in range(G)])
+            slots = [v0[g] for g in range(G) for _ in range(k)] + [v0[shared], v0.sum(0)]
+            ref = np.concatenate(slots) @ t["wo"].T
+            assert np.allclose(y0[b], ref, rtol=0, atol=1e-12), np.abs(y0[b] - ref).max()
+        t2 = dict(t)
+        t2["wq"] = rng.standard_normal(t["wq"].shape)
+        t2["wr"] = rng.standard_normal(t["wr"].shape)
+        assert np.allclose(run(orc, t2, shared_kv_group=shared)["y"][:, 0], y0, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P8, P12, causality
+# ---------------------------------------------------------------------------
+
+def pin_expert_permutation(orc):
+    """Relabelling the experts inside a group (their W_q rows, W_r rows and
+    b_r entries together) leaves y unchanged when hard slots are in rank
+    order; it only renames idx."""
+    rng = np.random.default_rng(23)
+    t = tiny_layer(rng, B=1, L=8, G=2, E=4, k=2)
+    t["br"] = rng.standard_normal(t["br"].shape)
+    G, E, dh = t["G"], t["E"], t["dh"]
+    a = run(orc, t)
+    perm = [rng.permutation(E) for _ in range(G)]
+    wq, wr, br = t["wq"].copy(), t["wr"].copy(), t["br"].copy()
+    for g in range(G):
+        for e in range(E):
+            src = g * E + perm[g][e]
+            wq[(g * E + e) * dh:(g * E + e + 1) * dh] = t["wq"][src * dh:(src + 1) * dh]
+            wr[g * E + e] = t["wr"][src]
+            br[g * E + e] = t["br"][src]
+    t2 = dict(t, wq=wq, wr=wr, br=br)
+    b = run(orc, t2)
+    assert np.allclose(a["y"], b["y"], rtol=0, atol=1e-12)
+    for g in range(G):                       # new expert e is old expert perm[g][e]
+        assert np.array_equal(perm[g][b["idx"][..., g, :]], a["idx"][..., g, :])
+
+
+def pin_value_scaling(orc):
+    """y is linear in W_v: scaling W_v by alpha scales y by alpha."""
+    rng = np.random.default_rng(24)
+    t = tiny_layer(rng)
+    a = run(orc, t)["y"]
+    b = run(orc, dict(t, wv=t["wv"] * -2.5))["y"]
+    assert np.allclose(b, -2.5 * a, rtol=0, atol=1e-12)
+
+
+def pin_causality(orc):
+    """Changing tokens after position t leaves y at positions <= t unchanged
+    (causal prefill), and changing the token at t changes y at t."""
+    rng = np.random.default_rng(25)
+    t = tiny_layer(rng, B=1, L=9)
+    a = run(orc, t)["y"]
+    x2 = t["x"].copy()
+    x2[:, 5:] = rng.standard_normal(x2[:, 5:].shape)
+    b = run(orc, dict(t, x=x2))["y"]
+    assert np.allclose(a[:, :5], b[:, :5], rtol=0, atol=1e-12)
+    assert not np.allclose(a[:, 5], b[:, 5], rtol=0, atol=1e-6)
+
+
+def pin_sampled_rows_match_full(orc):
+    """Computing only some positions gives the same rows as the full layer."""
+    rng = np.random.default_rng(26)
+    t = tiny_layer(rng, B=2, L=10)
+    full = run(orc, t)
+    rows = np.array([0, 3, 4, 9])
+    part = run(orc, t, positions=rows)
+    assert np.allclose(full["y"][:, rows], part["y"], rtol=0, atol=1e-13)
+    assert np.array_equal(full["idx"], part["idx"])
+
+
+ALL_PINS = [
+    pin_k_equals_e_is_dense_gqa,
+    pin_weights_sum_to_one,
+    pin_weights_closed_form,
+    pin_logit_shift_invariance,
+    pin_bias_selects,
+    pin_topk_brute_force,
+    pin_tie_rule,
+    pin_dispatch_lists,
+    pin_active_query_ratio,
+    pin_attention_brute_force,
+    pin_sdpa_cross_check,
+    pin_first_position_closed_form,
+    pin_expert_permutation,
+    pin_value_scaling,
+    pin_causality,
+    pin_sampled_rows_match_full,
+]

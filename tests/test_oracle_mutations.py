@@ -1,0 +1,201 @@
+"""Plant plausible mistakes in copies of the CPU oracle; the pins must catch each.
+
+Every mutation below is a bug one could make while writing the oracle from
+the pages (a dropped term, a wrong sign or index, a transposed operand, a
+wrong order).  Each runs on a private copy of the oracle module, on the CPU,
+and at least one pin from tests/oracle_pins.py has to fail on it.
+"""
+import importlib.util
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle_pins import ALL_PINS
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "gqe_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("gqe_oracle_mutant", ORACLE_SRC)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _attention_variant(mod, *, scale_mult=1.0, strict=False, no_mask=False, no_max=False):
+    def causal_attention(q, t, K, V, scale):
+        o = np.empty((q.shape[0], V.shape[1]))
+        for i in range(q.shape[0]):
+            tmax = int(t.max()) + 1
+            s = scale * scale_mult * (K[:tmax] @ q[i])
+            if not no_mask:
+                keep = np.arange(tmax) < t[i] if strict else np.arange(tmax) <= t[i]
+                s = np.where(keep, s, -np.inf)
+            m = 0.0 if no_max else s[np.isfinite(s)].max() if np.isfinite(s).any() else 0.0
+            e = np.exp(s - m)
+            o[i] = (e @ V[:tmax]) / e.sum()
+        return o
+    mod.causal_attention = causal_attention
+
+
+def m_no_scale(mod):
+    _attention_variant(mod, scale_mult=math.sqrt(4.0))     # drops 1/sqrt(d_h) at d_h = 4
+
+
+def m_strict_causal(mod):
+    _attention_variant(mod, strict=True)
+
+
+def m_no_causal_mask(mod):
+    _attention_variant(mod, no_mask=True)
+
+
+def m_topk_lowest(mod):
+    mod.topk_in_group = lambda r, k: np.argsort(r, axis=-1, kind="stable")[..., :k].astype(np.int32)
+
+
+def m_tie_to_highest(mod):
+    def topk(r, k):
+        E = r.shape[-1]
+        rev = np.argsort(-r[..., ::-1], axis=-1, kind="stable")[..., :k]
+        return (E - 1 - rev).astype(np.int32)
+    mod.topk_in_group = topk
+
+
+def m_index_order_slots(mod):
+    orig = mod.topk_in_group
+    mod.topk_in_group = lambda r, k: np.sort(orig(r, k), axis=-1)
+
+
+def m_renorm_over_all_groups(mod):
+    def renorm(p, idx):
+        ps = np.take_along_axis(p, idx.astype(np.int64), axis=-1)
+        return ps / ps.sum(axis=(-1, -2), keepdims=True)
+    mod.renormalize = renorm
+
+
+def m_no_renorm(mod):
+    mod.renormalize = lambda p, idx: np.take_along_axis(p, idx.astype(np.int64), axis=-1)
+
+
+def m_softmax_over_groups(mod):
+    def sm(r):
+        z = np.exp(r - r.max(axis=(-1, -2), keepdims=True))
+        return z / z.sum(axis=(-1, -2), keepdims=True)
+    mod.group_softmax = sm
+
+
+def m_router_group_transposed(mod):
+    def logits(x, wr, br, G, E):
+        r = x @ wr.T + br[None, :]
+        return r.reshape(x.shape[0], E, G).transpose(0, 2, 1).copy()
+    mod.router_logits = logits
+
+
+def m_router_bias_dropped(mod):
+    def logits(x, wr, br, G, E):
+        return (x @ wr.T).reshape(x.shape[0], G, E)
+    mod.router_logits = logits
+
+
+def m_expert_head_transposed(mod):
+    mod.expert_head = lambda g, e, E: e * E + g          # group and expert swapped
+
+
+def m_expert_head_reversed(mod):
+    mod.expert_head = lambda g, e, E: g * E + (E - 1 - e)
+
+
+def m_weighted_mean(mod):
+    orig = mod.weighted_slot
+    mod.weighted_slot = lambda w_rows, o_hard: orig(w_rows, o_hard) / w_rows.shape[1]
+
+
+def m_weighted_missing(mod):
+    mod.weighted_slot = lambda w_rows, o_hard: np.zeros((o_hard.shape[0], o_hard.shape[-1]))
+
+
+def m_weighted_unweighted(mod):
+    mod.weighted_slot = lambda w_rows, o_hard: o_hard.sum(axis=(1, 2))
+
+
+def m_slots_rank_major(mod):
+    def sv(o_hard, o_sh, o_w):
+        n = o_hard.shape[0]
+        return np.concatenate([o_hard.transpose(0, 2, 1, 3).reshape(n, -1), o_sh, o_w], axis=1)
+    mod.slot_vector = sv
+
+
+def m_shared_weighted_swapped(mod):
+    def sv(o_hard, o_sh, o_w):
+        n = o_hard.shape[0]
+        return np.concatenate([o_hard.reshape(n, -1), o_w, o_sh], axis=1)
+    mod.slot_vector = sv
+
+
+def m_output_untransposed(mod):
+    def proj(s, wo):
+        # wrong operand orientation, made to fit: reads W_O column-major
+        return s @ wo.reshape(wo.shape[1], wo.shape[0])
+    mod.output_projection = proj
+
+
+def m_dispatch_descending(mod):
+    orig = mod.dispatch
+
+    def disp(idx, E):
+        counts, offsets, pos, slot = orig(idx, E)
+        pos, slot = pos.copy(), slot.copy()
+        for i in range(len(offsets) - 1):
+            pos[offsets[i]:offsets[i + 1]] = pos[offsets[i]:offsets[i + 1]][::-1]
+            slot[offsets[i]:offsets[i + 1]] = slot[offsets[i]:offsets[i + 1]][::-1]
+        return counts, offsets, pos, slot
+    mod.dispatch = disp
+
+
+def m_kv_heads_swapped(mod):
+    orig = mod.kv_project
+
+    def kvp(x_b, w, G, dh, upto):
+        out = orig(x_b, w, G, dh, upto)
+        return out[::-1].copy() if G > 1 else out
+    mod.kv_project = kvp
+
+
+def m_head_rows_shifted(mod):
+    mod.head_rows = lambda w, head, dh: w[head * dh + 1:(head + 1) * dh + 1] \
+        if (head + 1) * dh + 1 <= w.shape[0] else w[head * dh:(head + 1) * dh]
+
+
+MUTATIONS = [
+    m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
+    m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
+    m_router_group_transposed, m_router_bias_dropped, m_expert_head_transposed,
+    m_expert_head_reversed,
+    m_weighted_mean, m_weighted_missing, m_weighted_unweighted, m_slots_rank_major,
+    m_shared_weighted_swapped, m_output_untransposed, m_dispatch_descending,
+    m_kv_heads_swapped, m_head_rows_shifted,
+]
+
+
+@pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
+def test_pins_catch_planted_mistake(mutate):
+    mod = fresh_oracle()
+    mutate(mod)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            failed.append((pin.__name__, type(exc).__name__))
+    assert failed, f"no pin caught {mutate.__name__}"
+
+
+def test_unmutated_copy_passes_every_pin():
+    mod = fresh_oracle()
+    for pin in ALL_PINS:
+        pin(mod)
