@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the GQE prefill layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload l2k] [--long]
+
+One step = one gqe_forward (router, dispatch, projections, attention, output)
+over one batch of synthetic input already resident in HBM.  The timed region
+is exactly K steps between two device synchronizations; per-stage times come
+from HIP events recorded between the stage calls on the same stream.  The
+dense-GQA baseline (all G*E query heads) is timed the same way, giving the
+GQE-over-GQA prefill speed-up.  Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16 = 2516.6e12     # dense bf16 MFMA, FLOP/s
+PEAK_FP32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12         # bytes/s
+METRIC = "GQE prefill tokens/s per layer + speedup vs dense GQA; % bf16 MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_work(wl):
+    """Algorithmic work of every stage for one step: (kind, amount) with kind
+    'flop' (MFMA) or 'byte' (HBM)."""
+    B, L, d, G, E, k, D = (wl.batch, wl.seq_len, wl.d_model, wl.n_groups, wl.n_experts,
+                           wl.top_k, wl.head_dim)
+    T = B * L
+    es = 2 if wl.dtype == W.BF16 else 4
+    return {
+        "route": ("byte", T * d * es + T * G * k * 8 + G * E * d * es),
+        "dispatch": ("byte", T * G * k * 4 + T * G * k * 8),
+        "project": ("flop", 2 * T * d * D * (k * G + 2 * G + 1)),
+        "attention": ("flop", 2 * 2 * D * (k * G + 1) * B * L * (L + 1) // 2),
+        "output": ("flop", 2 * T * (k * G + 2) * D * d),
+    }
+
+
+def gqa_stage_work(wl):
+    B, L, d, G, E, D = wl.batch, wl.seq_len, wl.d_model, wl.n_groups, wl.n_experts, wl.head_dim
+    T = B * L
+    return {
+        "project": ("flop", 2 * T * d * D * (G * E + 2 * G)),
+        "attention": ("flop", 2 * 2 * D * G * E * B * L * (L + 1) // 2),
+        "output": ("flop", 2 * T * G * E * D * d),
+    }
+
+
+class Runner:
+    """Device inputs, workspaces and the per-stage call sequence of one workload."""
+
+    def __init__(self, wl, gqe, torch):
+        self.wl, self.gqe, self.torch = wl, gqe, torch
+        I = W.make_inputs(wl, with_gqa=True)
+        dev = {}
+        for key, v in I.items():
+            if v.dtype == np.uint16:
+                dev[key] = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(
+                    torch.bfloat16).to("cuda")
+            else:
+                dev[key] = torch.from_numpy(np.ascontiguousarray(v)).to("cuda")
+        self.I, self.dev = I, dev
+        self.cfg = gqe.make_config(wl.batch, wl.seq_len, wl.d_model, wl.n_groups, wl.n_experts,
+                                   wl.top_k, wl.head_dim, dtype=wl.dtype, router_bias=dev["br"])
+        self.ws = gqe.alloc_workspace(self.cfg)
+        self.ws_dense = gqe.alloc_workspace(self.cfg, dense=True)
+        shape = (wl.batch, wl.seq_len, wl.d_model)
+        self.out = torch.empty(shape, dtype=self.cfg.torch_dtype, device="cuda")
+        self.out_dense = torch.empty(shape, dtype=self.cfg.torch_dtype, device="cuda")
+
+    def gqe_stages(self):
+        g, c, d, ws = self.gqe, self.cfg, self.dev, self.ws
+        return [
+            ("route", lambda: g.gqe_route(c, d["x"], d["wr"], ws)),
+            ("dispatch", lambda: g.gqe_dispatch(c, ws)),
+            ("project", lambda: g.gqe_project(c, d["x"], d["wq"], d["wk"], d["wv"], ws)),
+            ("attention", lambda: g.gqe_attention(c, ws)),
+            ("output", lambda: g.gqe_output(c, d["wo"], self.out, ws)),
+        ]
+
+    def gqa_stages(self):
+        g, c, d, ws = self.gqe, self.cfg, self.dev, self.ws_dense
+        return [
+            ("project", lambda: g.gqa_project(c, d["x"], d["wq_dense"], d["wk"], d["wv"], ws)),
+            ("attention", lambda: g.gqa_attention(c, ws)),
+            ("output", lambda: g.gqa_output(c, d["wo_dense"], self.out_dense, ws)),
+        ]
+
+    def time(self, stages, steps, warmup):
+        """Warm up, then time `steps` full passes; returns (ms per step, {stage: avg ms})."""
+        torch = self.torch
+        for _ in range(warmup):
+            for _, fn in stages:
+                fn()
+        torch.cuda.synchronize()
+        n = len(stages)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for s in range(steps):
+            ev[s][0].record()
+            for i, (_, fn) in enumerate(stages):
+                fn()
+                ev[s][i + 1].record()
+        stop.record()
+        torch.cuda.synchronize()
+        total = start.elapsed_time(stop) / steps
+        per = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+               for i, (name, _) in enumerate(stages)}
+        return total, per
+
+
+def rate(kind, amount, ms):
+    v = amount / (ms * 1e-3)
+    return v / 1e12  # TFLOP/s or TB/s
+
+
+def measure(wl, gqe, torch, steps, warmup):
+    r = Runner(wl, gqe, torch)
+    t_gqe, st_gqe = r.time(r.gqe_stages(), steps, warmup)
+    t_gqa, st_gqa = r.time(r.gqa_stages(), steps, warmup)
+    tokens = wl.batch * wl.seq_len
+    work = stage_work(wl)
+    gwork = gqa_stage_work(wl)
+    peak = PEAK_BF16 if wl.dtype == W.BF16 else PEAK_FP32_MFMA
+    att = work["attention"][1] / (st_gqe["attention"] * 1e-3)
+    res = {
+        "workload": wl.name,
+        "tokens": tokens,
+        "gqe_ms": t_gqe,
+        "gqa_ms": t_gqa,
+        "gqe_tokens_per_s": tokens / (t_gqe * 1e-3),
+        "gqa_tokens_per_s": tokens / (t_gqa * 1e-3),
+        "speedup_vs_gqa": t_gqa / t_gqe,
+        "attention_speedup_vs_gqa": st_gqa["attention"] / st_gqe["attention"],
+        "gqe_stage_ms": {k: round(v, 5) for k, v in st_gqe.items()},
+        "gqa_stage_ms": {k: round(v, 5) for k, v in st_gqa.items()},
+        "attention_tflops": att / 1e12,
+        "attention_mfma_frac": att / peak,
+        "gqa_attention_mfma_frac": gwork["attention"][1] / (st_gqa["attention"] * 1e-3) / peak,
+    }
+    return r, res
+
+
+def roofline_for(wl, res):
+    """Roofline of the dominant kernel of the GQE step (the stage with the most time)."""
+    work = stage_work(wl)
+    stage = max(res["gqe_stage_ms"], key=res["gqe_stage_ms"].get)
+    kind, amount = work[stage]
+    ms = res["gqe_stage_ms"][stage]
+    if kind == "flop":
+        peak = (PEAK_BF16 if wl.dtype == W.BF16 else PEAK_FP32_MFMA) / 1e12
+        bound, unit = "mfma", "TFLOP/s"
+    else:
+        peak, bound, unit = PEAK_HBM / 1e12, "hbm", "TB/s"
+    ach = rate(kind, amount, ms)
+    if unit == "TB/s":
+        ach, peak, unit = ach * 1000, peak * 1000, "GB/s"
+    return {"kernel": stage, "bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3),
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+            "per_launch": {"amount": amount, "kind": kind, "avg_ms": round(ms, 5)}}
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The CPU oracle, as it stands, on full layers of the same workload until
+    about `budget_s` seconds have passed; tokens/s over the layers it finished."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    I = W.make_inputs(wl)
+    f = lambda a: W.to_f64(a, wl.dtype)  # noqa: E731
+    args = (f(I["x"]), f(I["wq"]), f(I["wk"]), f(I["wv"]), f(I["wr"]), f(I["wo"]),
+            I["br"].astype(np.float64), wl.n_groups, wl.n_experts, wl.top_k, wl.head_dim)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.gqe_forward(*args)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(n * wl.tokens / el, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} full layers of {wl.name} (B={wl.batch}, L={wl.seq_len}) in {el:.1f} s, float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="l2k", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--lengths", default="b4_l8k,l128k",
+                    help="other workloads timed for the per-length speed-up (comma list, '' = none)")
+    ap.add_argument("--long", action="store_true", help="also time the 1M-token workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_query_moe_amd import gqe
+
+    wl = W.WORKLOADS[args.workload]
+    log(f"[bench] {wl.description}: warmup {args.warmup}, steps {args.steps}")
+    _, res = measure(wl, gqe, torch, args.steps, args.warmup)
+    log(f"[bench] gqe {res['gqe_ms']:.4f} ms  gqa {res['gqa_ms']:.4f} ms  "
+        f"speed-up {res['speedup_vs_gqa']:.3f}  stages {res['gqe_stage_ms']}")
+
+    per_length = [res]
+    extra = [n for n in args.lengths.split(",") if n] + (["l1m_zipf"] if args.long else [])
+    for name in extra:
+        if name == wl.name:
+            continue
+        w2 = W.WORKLOADS[name]
+        steps = max(2, min(args.steps, int(2e12 / max(1, stage_work(w2)["attention"][1]) + 2)))
+        log(f"[bench] per-length {w2.description}: steps {steps}")
+        _, r2 = measure(w2, gqe, torch, steps, 1)
+        log(f"[bench]   gqe {r2['gqe_ms']:.3f} ms gqa {r2['gqa_ms']:.3f} ms "
+            f"speed-up {r2['speedup_vs_gqa']:.3f} attention {r2['attention_mfma_frac']:.3f} of peak")
+        per_length.append(r2)
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC,
+        "value": round(res["gqe_tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["gqe_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == W.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.description, "batch": wl.batch, "seq_len": wl.seq_len,
+                   "d_model": wl.d_model, "n_groups": wl.n_groups, "n_experts": wl.n_experts,
+                   "top_k": wl.top_k, "head_dim": wl.head_dim, "shared_heads": 1,
+                   "parallelism": "single GPU"},
+        "speedup_vs_gqa": round(res["speedup_vs_gqa"], 4),
+        "gqa_tokens_per_s": round(res["gqa_tokens_per_s"], 1),
+        "attention_mfma_frac": round(res["attention_mfma_frac"], 4),
+        "roofline": roofline_for(wl, res),
+        "per_length": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
+                       for r in per_length],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * gqe.h -- C ABI of the MI355X (gfx950) Grouped Query Experts prefill layer.
+ *
+ * The method: "Grouped Query Experts: Mixture-of-Experts on GQA
+ * Self-Attention" (arXiv 2606.20945), as described by the pptc.cn review
+ * (sections 4.2, 5, 6, 7), the gist.science technical summaries
+ * ("Architectuur en Routing" / "Arquitetura e Roteamento") and the
+ * hotpaper.ai summary ("core idea", "technical approach").  Inside every
+ * grouped-query-attention (GQA) group a per-token router picks k of the E
+ * query-head experts; K and V stay dense; the selected heads and one
+ * always-on shared head attend causally to their group's K/V; the outputs
+ * form k*G hard slots, a shared slot and one renormalized weighted slot,
+ * which W_O (k*G+2 slots wide) projects back to d_model.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer is a DEVICE pointer owned by the caller, except `cfg` and
+ *    `layout`, which are host pointers read (or written) before the call
+ *    returns.  The library never allocates or frees memory and keeps no
+ *    global mutable state: calls are reentrant.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream).  No call synchronizes the host.  The status returned
+ *    reports argument errors only (nothing is launched then); a fault inside
+ *    a kernel surfaces at the caller's next synchronization of `stream`.
+ *  - Tensors are contiguous and row-major.  Element type `cfg->dtype`:
+ *    bfloat16 (GQE_DTYPE_BF16) or float32 (GQE_DTYPE_FP32) for x, every
+ *    weight and `out`; router bias and weights w are float32; indices int32.
+ *  - Weights use the [out, in] layout of a PyTorch nn.Linear weight:
+ *      Wq  [(G*E+1)*d_h, d_model]  head h = g*E+e owns rows h*d_h .. h*d_h+d_h-1;
+ *                                  the shared head owns the last d_h rows
+ *      Wk, Wv [G*d_h, d_model]     group g owns rows g*d_h .. g*d_h+d_h-1
+ *      Wr  [G*E, d_model]          router row of expert e of group g is g*E+e
+ *      Wo  [d_model, (k*G+2)*d_h]  input columns: hard slot g*k+j, then the
+ *                                  shared slot (k*G), then the weighted slot
+ *  - x is [B, L, d_model]; out is [B, L, d_model] and must not alias any
+ *    input or the workspace.  Device pointers must be 16-byte aligned
+ *    (router_bias: 4-byte).
+ *  - B*L == 0 is valid: nothing is launched and GQE_OK is returned.
+ */
+#ifndef GQE_H_
+#define GQE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQE_OK = 0,
+  GQE_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or field  */
+  GQE_ERR_UNSUPPORTED = -2,   /* valid but not built: e.g. head_dim 96       */
+  GQE_ERR_WORKSPACE = -3,     /* ws_bytes smaller than gqe_workspace_bytes() */
+  GQE_ERR_HIP = -4            /* a launch was rejected by the HIP runtime    */
+} gqe_status;
+
+typedef enum { GQE_DTYPE_BF16 = 0, GQE_DTYPE_FP32 = 1 } gqe_dtype;
+
+/* Layer shape.  Limits: batch, seq_len >= 0; d_model a multiple of 8;
+ * 1 <= n_groups; 1 <= n_experts <= 32; 1 <= top_k <= n_experts;
+ * n_groups*n_experts <= 64; head_dim in {32, 64, 128};
+ * 0 <= shared_kv_group < n_groups; batch*seq_len*n_groups*top_k < 2^31. */
+typedef struct gqe_config {
+  int32_t batch;            /* B                                               */
+  int32_t seq_len;          /* L: prefill length, causal, no padding          */
+  int32_t d_model;          /* d                                               */
+  int32_t n_groups;         /* G: KV heads = GQA groups                        */
+  int32_t n_experts;        /* E: routed query-head experts per group          */
+  int32_t top_k;            /* k: experts selected per token in every group    */
+  int32_t head_dim;         /* d_h                                             */
+  int32_t shared_kv_group;  /* KV group read by the always-on shared head      */
+  int32_t dtype;            /* gqe_dtype                                       */
+  float softmax_scale;      /* attention scale; 0 selects 1/sqrt(head_dim)     */
+  const float* router_bias; /* device float32 [G*E] added to the logits, or NULL */
+} gqe_config;
+
+/* Byte offsets into the workspace of every intermediate, so that callers can
+ * read (or seed) them.  All offsets are 256-byte aligned.
+ *   idx     int32 [B, L, G, k]   selected experts, best first
+ *   w       float [B, L, G, k]   renormalized router weights
+ *   counts  int32 [B*G*E]        tokens routed to expert e of (b, g)
+ *   offsets int32 [B*G*E+1]      exclusive prefix sum of counts, (b,g,e) order
+ *   pos     int32 [B*L*G*k]      list (b,g,e) at offsets[(b*G+g)*E+e]: the
+ *   slot    int32 [B*L*G*k]      ascending positions t that chose e, and the
+ *                                rank j at which they chose it
+ *   q       dtype [B, k*G+1, L, d_h]   queries per slot-head (hard slot g*k+j,
+ *                                      then the shared head)
+ *   k       dtype [B, G, L, d_h]       keys
+ *   vt      dtype [B, G, d_h, vt_ld]   values, transposed; vt_ld >= L
+ *   s       dtype [B, L, (k*G+2)*d_h]  slot vectors (input of W_O)
+ *   the rest is private scratch (dispatch partial counts, tile maps). */
+typedef struct gqe_ws_layout {
+  size_t idx, w, counts, offsets, pos, slot;
+  size_t q, k, vt, s;
+  size_t scratch;
+  size_t total;
+  int64_t vt_ld;
+} gqe_ws_layout;
+
+/* Workspace size in bytes for gqe_forward and its stages (0 when cfg is
+ * invalid).  Monotone in B and L. */
+size_t gqe_workspace_bytes(const gqe_config* cfg);
+int gqe_workspace_layout(const gqe_config* cfg, gqe_ws_layout* layout);
+
+/* Router of every token (pptc.cn section 7: softmax first, then top-k, inside
+ * each group; hotpaper.ai technical approach: renormalized scoring; pptc.cn
+ * section 5: every group takes part).  Logits r = x . Wr^T + router_bias are
+ * accumulated in float64; the k largest of each group are written to
+ * ws.idx in rank order (ties to the lower expert index) and their weights,
+ * softmax over the selected logits (equal to the in-group softmax
+ * renormalized over the k), to ws.w. */
+int gqe_route(const gqe_config* cfg, const void* x, const void* Wr,
+              void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Per-(b, g, e) token lists from ws.idx (pptc.cn section 6: the sparse
+ * scheduling cost): ws.counts, ws.offsets, ws.pos, ws.slot as described in
+ * gqe_ws_layout.  Deterministic: no atomics decide any order. */
+int gqe_dispatch(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Projections (gist.science, Architectuur en Routing: the K/V path stays
+ * dense and only the query side is sparse).  Dense: K, V (transposed) and the
+ * shared head's queries for every token.  Gathered: for every list (b,g,e),
+ * the query rows x[pos] . Wq[head g*E+e]^T, written to slot-head g*k+slot at
+ * their original positions.  Reads ws.offsets/pos/slot. */
+int gqe_project(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                const void* Wv, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Causal attention of every slot-head row against its group's dense K/V
+ * (pptc.cn section 5: a token that skips an expert still attends with the
+ * experts it chose to that group's KV head; the shared head reads group
+ * shared_kv_group).  Writes the hard slots and the shared slot of ws.s. */
+int gqe_attention(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Output construction (gist.science, Architectuur en Routing: hard
+ * concatenation, renormalized weighted sum, always-on shared head;
+ * hotpaper.ai: W_O of k*G+2 slots): the weighted slot
+ * sum_g sum_j w[t,g,j] * o[t,g,j] is written to ws.s, then out = s . Wo^T
+ * with float32 accumulation and one final rounding. */
+int gqe_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace,
+               size_t ws_bytes, hipStream_t stream);
+
+/* The whole GQE prefill layer: gqe_route, gqe_dispatch, gqe_project,
+ * gqe_attention, gqe_output in that order on `stream`. */
+int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                const void* Wv, const void* Wr, const void* Wo, void* out,
+                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Dense GQA baseline, all G*E query heads active (pptc.cn section 4.2: the
+ * all-active comparison model).  Wq [G*E*d_h, d_model], Wo [d_model, G*E*d_h];
+ * head h reads KV group h / E.  top_k, shared_kv_group and router_bias are
+ * ignored.  Workspace: q [B, G*E, L, d_h], k, vt as above, o [B, L, G*E*d_h]
+ * (reported in the layout's `s` field). */
+size_t gqa_workspace_bytes(const gqe_config* cfg);
+int gqa_workspace_layout(const gqe_config* cfg, gqe_ws_layout* layout);
+int gqa_project(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                const void* Wv, void* workspace, size_t ws_bytes, hipStream_t stream);
+int gqa_attention(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream);
+int gqa_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace,
+               size_t ws_bytes, hipStream_t stream);
+int gqa_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                const void* Wv, const void* Wo, void* out, void* workspace, size_t ws_bytes,
+                hipStream_t stream);
+
+/* Static text for a gqe_status value; never NULL. */
+const char* gqe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQE_H_ */

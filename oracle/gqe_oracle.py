@@ -109,7 +109,16 @@ def renormalize(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
 
 def route(x: np.ndarray, wr: np.ndarray, br: np.ndarray, n_groups: int, n_experts: int,
           top_k: int, exact_margin: float = 1e-12):
-    """Steps 1-4 for tokens x[T, d].  Returns (r, p, idx, w), shapes [T,G,E] / [T,G,k]."""
+    """Steps 1-4 for tokens x[T, d].  Returns (r, p, idx, w), shapes [T,G,E] / [T,G,k].
+
+    Tokens are independent; long inputs are processed in blocks of 65536
+    tokens only to bound memory.
+    """
+    step = 65536
+    if x.shape[0] > step:
+        parts = [route(x[t0:t0 + step], wr, br, n_groups, n_experts, top_k, exact_margin)
+                 for t0 in range(0, x.shape[0], step)]
+        return tuple(np.concatenate([prt[i] for prt in parts]) for i in range(4))
     r = router_logits(x, wr, br, n_groups, n_experts)
     # decisions that rounding could flip: recompute those tokens exactly
     srt = -np.sort(-r, axis=-1)
@@ -187,9 +196,13 @@ def causal_attention(q: np.ndarray, t: np.ndarray, K: np.ndarray, V: np.ndarray,
     """
     o = np.empty((q.shape[0], V.shape[1]))
     order = np.argsort(t, kind="stable")
-    chunk = 256
-    for c0 in range(0, len(order), chunk):
+    c0 = 0
+    while c0 < len(order):
+        # rows per chunk bounded so that a chunk's score matrix stays ~16M entries
+        span = int(t[order[min(len(order) - 1, c0 + 255)]]) + 1
+        chunk = max(1, min(256, (1 << 24) // span))
         rows = order[c0:c0 + chunk]
+        c0 += chunk
         tmax = int(t[rows].max()) + 1
         s = scale * (q[rows] @ K[:tmax].T)               # [n, tmax]
         s[np.arange(tmax)[None, :] > t[rows][:, None]] = -np.inf

@@ -1,0 +1,369 @@
+// C ABI of the GQE prefill layer: argument validation, workspace layout and
+// the launch sequence of every stage (declared in include/gqe.h).
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/gqe.h"
+#include "kernels.h"
+
+using namespace gqe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t elem_bytes(const gqe_config* c) { return c->dtype == GQE_DTYPE_BF16 ? 2 : 4; }
+
+bool shape_ok(const gqe_config* c) {
+  if (c == nullptr) return false;
+  if (c->batch < 0 || c->seq_len < 0) return false;
+  if (c->d_model < 8 || c->d_model % 8 != 0) return false;
+  if (c->n_groups < 1 || c->n_experts < 1 || c->n_experts > 32) return false;
+  if (c->n_groups * c->n_experts > 64) return false;
+  if (c->top_k < 1 || c->top_k > c->n_experts) return false;
+  if (c->shared_kv_group < 0 || c->shared_kv_group >= c->n_groups) return false;
+  if (c->dtype != GQE_DTYPE_BF16 && c->dtype != GQE_DTYPE_FP32) return false;
+  if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return false;
+  const long long rows = static_cast<long long>(c->batch) * c->seq_len * c->n_groups * c->top_k;
+  if (rows >= (1LL << 31)) return false;
+  if (static_cast<long long>(c->batch) * c->seq_len * c->n_groups * c->n_experts >= (1LL << 31))
+    return false;
+  return true;
+}
+
+bool head_dim_ok(const gqe_config* c) {
+  return c->head_dim == 32 || c->head_dim == 64 || c->head_dim == 128;
+}
+
+int check_cfg(const gqe_config* c) {
+  if (c == nullptr) return GQE_ERR_INVALID_ARG;
+  if (c->head_dim < 1) return GQE_ERR_INVALID_ARG;
+  if (!shape_ok(c)) return GQE_ERR_INVALID_ARG;
+  if (!head_dim_ok(c)) return GQE_ERR_UNSUPPORTED;
+  return GQE_OK;
+}
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  gqe_ws_layout pub;
+  size_t chunk_counts, tile_off;
+};
+
+// Workspace of gqe_forward (dense == false) or gqa_forward (dense == true).
+Layout make_layout(const gqe_config* c, bool dense) {
+  const size_t B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts, k = c->top_k;
+  const size_t D = c->head_dim, es = elem_bytes(c);
+  const size_t vt_ld = align_up(L, 64);
+  Layout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  if (!dense) {
+    const size_t rows = B * L * G * k;
+    const size_t lists = B * G * E;
+    l.pub.idx = take(rows * 4);
+    l.pub.w = take(rows * 4);
+    l.pub.counts = take(lists * 4);
+    l.pub.offsets = take((lists + 1) * 4);
+    l.pub.pos = take(rows * 4);
+    l.pub.slot = take(rows * 4);
+    l.pub.scratch = off;
+    l.chunk_counts = take(B * static_cast<size_t>(dispatch_chunks(static_cast<int>(L))) * G * E * 4);
+    l.tile_off = take((lists + 1) * 4);
+    l.pub.q = take(B * (G * k + 1) * L * D * es);
+    l.pub.s = 0;
+  } else {
+    l.pub.q = take(B * G * E * L * D * es);
+  }
+  l.pub.k = take(B * G * L * D * es);
+  l.pub.vt = take(B * G * D * vt_ld * es);
+  l.pub.s = take(B * L * (dense ? G * E : G * k + 2) * D * es);
+  if (dense) l.pub.scratch = off;
+  l.pub.total = off;
+  l.pub.vt_ld = static_cast<int64_t>(vt_ld);
+  return l;
+}
+
+float scale_log2(const gqe_config* c) {
+  const float s = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / sqrtf(static_cast<float>(c->head_dim));
+  return s * 1.4426950408889634f;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GQE_OK : GQE_ERR_HIP; }
+
+template <typename T> T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// common entry checks: cfg, workspace.  Returns GQE_OK or an error status.
+int check_common(const gqe_config* c, void* ws, size_t ws_bytes, bool dense) {
+  int st = check_cfg(c);
+  if (st != GQE_OK) return st;
+  if (static_cast<long long>(c->batch) * c->seq_len == 0) return GQE_OK;
+  if (!aligned16(ws)) return GQE_ERR_INVALID_ARG;
+  if (ws_bytes < make_layout(c, dense).pub.total) return GQE_ERR_WORKSPACE;
+  return GQE_OK;
+}
+
+bool empty(const gqe_config* c) { return static_cast<long long>(c->batch) * c->seq_len == 0; }
+
+int max_gather_tiles(const gqe_config* c) {
+  const long long rows = static_cast<long long>(c->batch) * c->seq_len * c->n_groups * c->top_k;
+  return static_cast<int>((rows + kGatherRows - 1) / kGatherRows) +
+         c->batch * c->n_groups * c->n_experts;
+}
+
+template <typename T>
+int project_impl(const gqe_config* c, const void* x, const void* wq, const void* wk,
+                 const void* wv, void* ws, bool dense, hipStream_t stream) {
+  const Layout l = make_layout(c, dense);
+  const int B = c->batch, L = c->seq_len, d = c->d_model, G = c->n_groups, E = c->n_experts;
+  const int k = c->top_k, D = c->head_dim;
+  ProjSeg seg[3];
+  const int nq_cols = dense ? G * E * D : D;
+  seg[0].w = dense ? wq : static_cast<const void*>(static_cast<const T*>(wq) +
+                                                    static_cast<size_t>(G) * E * D * d);
+  seg[0].out = at<T>(ws, l.pub.q);
+  seg[0].n_begin = 0;
+  seg[0].n = nq_cols;
+  seg[0].heads = dense ? G * E : G * k + 1;
+  seg[0].head_base = dense ? 0 : G * k;
+  seg[0].transposed = 0;
+  seg[1].w = wk;
+  seg[1].out = at<T>(ws, l.pub.k);
+  seg[1].n_begin = nq_cols;
+  seg[1].n = G * D;
+  seg[1].heads = G;
+  seg[1].head_base = 0;
+  seg[1].transposed = 0;
+  seg[2].w = wv;
+  seg[2].out = at<T>(ws, l.pub.vt);
+  seg[2].n_begin = nq_cols + G * D;
+  seg[2].n = G * D;
+  seg[2].heads = G;
+  seg[2].head_base = 0;
+  seg[2].transposed = 1;
+  hipError_t e = launch_dense_proj<T>(static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_ld, seg,
+                                      3, stream);
+  if (e != hipSuccess || dense) return hip_status(e);
+  e = launch_gather_q<T>(static_cast<const T*>(x), static_cast<const T*>(wq), at<T>(ws, l.pub.q),
+                         at<int32_t>(ws, l.pub.counts), at<int32_t>(ws, l.pub.offsets),
+                         at<int32_t>(ws, l.pub.pos), at<int32_t>(ws, l.pub.slot),
+                         at<int32_t>(ws, l.tile_off), B, L, d, G, E, k, D, max_gather_tiles(c),
+                         stream);
+  return hip_status(e);
+}
+
+template <typename T>
+int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream) {
+  const Layout l = make_layout(c, dense);
+  const int G = c->n_groups, E = c->n_experts, k = c->top_k, D = c->head_dim;
+  AttnParams p;
+  p.q = at<T>(ws, l.pub.q);
+  p.k = at<T>(ws, l.pub.k);
+  p.vt = at<T>(ws, l.pub.vt);
+  p.o = at<T>(ws, l.pub.s);
+  p.vt_ld = l.pub.vt_ld;
+  p.B = c->batch;
+  p.G = G;
+  p.L = c->seq_len;
+  if (dense) {
+    p.H = G * E;
+    p.heads_per_group = E;
+    p.n_grouped = G * E;
+    p.extra_group = 0;
+    p.ld_o = static_cast<int64_t>(G) * E * D;
+  } else {
+    p.H = G * k + 1;
+    p.heads_per_group = k;
+    p.n_grouped = G * k;
+    p.extra_group = c->shared_kv_group;
+    p.ld_o = static_cast<int64_t>(G * k + 2) * D;
+  }
+  p.scale_log2 = scale_log2(c);
+  return hip_status(launch_attention<T>(p, D, stream));
+}
+
+template <typename T>
+int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool dense,
+                hipStream_t stream) {
+  const Layout l = make_layout(c, dense);
+  const int G = c->n_groups, E = c->n_experts, k = c->top_k, D = c->head_dim;
+  const int M = c->batch * c->seq_len;
+  hipError_t e = hipSuccess;
+  int K;
+  if (!dense) {
+    e = launch_weighted_slot<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), M, G, k, D, stream);
+    if (e != hipSuccess) return GQE_ERR_HIP;
+    K = (G * k + 2) * D;
+  } else {
+    K = G * E * D;
+  }
+  e = launch_out_proj<T>(at<T>(ws, l.pub.s), static_cast<const T*>(wo), static_cast<T*>(out), M,
+                         c->d_model, K, stream);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqe_status_string(int status) {
+  switch (status) {
+    case GQE_OK: return "GQE_OK";
+    case GQE_ERR_INVALID_ARG: return "GQE_ERR_INVALID_ARG: invalid argument";
+    case GQE_ERR_UNSUPPORTED: return "GQE_ERR_UNSUPPORTED: configuration not built";
+    case GQE_ERR_WORKSPACE: return "GQE_ERR_WORKSPACE: workspace too small";
+    case GQE_ERR_HIP: return "GQE_ERR_HIP: the HIP runtime rejected a launch";
+    default: return "unknown gqe status";
+  }
+}
+
+size_t gqe_workspace_bytes(const gqe_config* cfg) {
+  if (check_cfg(cfg) != GQE_OK) return 0;
+  return make_layout(cfg, false).pub.total;
+}
+
+int gqe_workspace_layout(const gqe_config* cfg, gqe_ws_layout* layout) {
+  const int st = check_cfg(cfg);
+  if (st != GQE_OK) return st;
+  if (layout == nullptr) return GQE_ERR_INVALID_ARG;
+  *layout = make_layout(cfg, false).pub;
+  return GQE_OK;
+}
+
+size_t gqa_workspace_bytes(const gqe_config* cfg) {
+  if (check_cfg(cfg) != GQE_OK) return 0;
+  return make_layout(cfg, true).pub.total;
+}
+
+int gqa_workspace_layout(const gqe_config* cfg, gqe_ws_layout* layout) {
+  const int st = check_cfg(cfg);
+  if (st != GQE_OK) return st;
+  if (layout == nullptr) return GQE_ERR_INVALID_ARG;
+  *layout = make_layout(cfg, true).pub;
+  return GQE_OK;
+}
+
+int gqe_route(const gqe_config* cfg, const void* x, const void* Wr, void* workspace,
+              size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, false);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if (!aligned16(x) || !aligned16(Wr)) return GQE_ERR_INVALID_ARG;
+  if (cfg->router_bias && (reinterpret_cast<uintptr_t>(cfg->router_bias) & 3u))
+    return GQE_ERR_INVALID_ARG;
+  const Layout l = make_layout(cfg, false);
+  hipError_t e;
+  if (cfg->dtype == GQE_DTYPE_BF16)
+    e = launch_router<bf16_t>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(Wr),
+                              cfg->router_bias, at<int32_t>(workspace, l.pub.idx),
+                              at<float>(workspace, l.pub.w), cfg->batch * cfg->seq_len,
+                              cfg->d_model, cfg->n_groups, cfg->n_experts, cfg->top_k, stream);
+  else
+    e = launch_router<float>(static_cast<const float*>(x), static_cast<const float*>(Wr),
+                             cfg->router_bias, at<int32_t>(workspace, l.pub.idx),
+                             at<float>(workspace, l.pub.w), cfg->batch * cfg->seq_len,
+                             cfg->d_model, cfg->n_groups, cfg->n_experts, cfg->top_k, stream);
+  return hip_status(e);
+}
+
+int gqe_dispatch(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, false);
+  if (st != GQE_OK || empty(cfg)) return st;
+  const Layout l = make_layout(cfg, false);
+  return hip_status(launch_dispatch(
+      at<int32_t>(workspace, l.pub.idx), at<int32_t>(workspace, l.chunk_counts),
+      at<int32_t>(workspace, l.pub.counts), at<int32_t>(workspace, l.pub.offsets),
+      at<int32_t>(workspace, l.tile_off), at<int32_t>(workspace, l.pub.pos),
+      at<int32_t>(workspace, l.pub.slot), cfg->batch, cfg->seq_len, cfg->n_groups,
+      cfg->n_experts, cfg->top_k, kGatherRows, stream));
+}
+
+int gqe_project(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                const void* Wv, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, false);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if (!aligned16(x) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv))
+    return GQE_ERR_INVALID_ARG;
+  return cfg->dtype == GQE_DTYPE_BF16
+             ? project_impl<bf16_t>(cfg, x, Wq, Wk, Wv, workspace, false, stream)
+             : project_impl<float>(cfg, x, Wq, Wk, Wv, workspace, false, stream);
+}
+
+int gqe_attention(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, false);
+  if (st != GQE_OK || empty(cfg)) return st;
+  return cfg->dtype == GQE_DTYPE_BF16 ? attention_impl<bf16_t>(cfg, workspace, false, stream)
+                                      : attention_impl<float>(cfg, workspace, false, stream);
+}
+
+int gqe_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace,
+               size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, false);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if (!aligned16(Wo) || !aligned16(out)) return GQE_ERR_INVALID_ARG;
+  return cfg->dtype == GQE_DTYPE_BF16
+             ? output_impl<bf16_t>(cfg, Wo, out, workspace, false, stream)
+             : output_impl<float>(cfg, Wo, out, workspace, false, stream);
+}
+
+int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                const void* Wv, const void* Wr, const void* Wo, void* out, void* workspace,
+                size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, false);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if (!aligned16(x) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(Wr) ||
+      !aligned16(Wo) || !aligned16(out))
+    return GQE_ERR_INVALID_ARG;
+  if ((st = gqe_route(cfg, x, Wr, workspace, ws_bytes, stream)) != GQE_OK) return st;
+  if ((st = gqe_dispatch(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
+  if ((st = gqe_project(cfg, x, Wq, Wk, Wv, workspace, ws_bytes, stream)) != GQE_OK) return st;
+  if ((st = gqe_attention(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
+  return gqe_output(cfg, Wo, out, workspace, ws_bytes, stream);
+}
+
+int gqa_project(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                const void* Wv, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, true);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if (!aligned16(x) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv))
+    return GQE_ERR_INVALID_ARG;
+  return cfg->dtype == GQE_DTYPE_BF16
+             ? project_impl<bf16_t>(cfg, x, Wq, Wk, Wv, workspace, true, stream)
+             : project_impl<float>(cfg, x, Wq, Wk, Wv, workspace, true, stream);
+}
+
+int gqa_attention(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, true);
+  if (st != GQE_OK || empty(cfg)) return st;
+  return cfg->dtype == GQE_DTYPE_BF16 ? attention_impl<bf16_t>(cfg, workspace, true, stream)
+                                      : attention_impl<float>(cfg, workspace, true, stream);
+}
+
+int gqa_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace,
+               size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, true);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if (!aligned16(Wo) || !aligned16(out)) return GQE_ERR_INVALID_ARG;
+  return cfg->dtype == GQE_DTYPE_BF16
+             ? output_impl<bf16_t>(cfg, Wo, out, workspace, true, stream)
+             : output_impl<float>(cfg, Wo, out, workspace, true, stream);
+}
+
+int gqa_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                const void* Wv, const void* Wo, void* out, void* workspace, size_t ws_bytes,
+                hipStream_t stream) {
+  int st = check_common(cfg, workspace, ws_bytes, true);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if ((st = gqa_project(cfg, x, Wq, Wk, Wv, workspace, ws_bytes, stream)) != GQE_OK) return st;
+  if ((st = gqa_attention(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
+  return gqa_output(cfg, Wo, out, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"

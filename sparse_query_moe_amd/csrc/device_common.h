@@ -1,0 +1,132 @@
+// Device-side helpers shared by the gfx950 kernels of the GQE layer:
+// element types, 8-element MFMA operand fragments, the 32x32 MFMA wrappers and
+// the swizzled LDS addressing used by every tiled kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqe {
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// An MFMA operand fragment: the 8 consecutive K-elements one lane supplies.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ float to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+// float -> storage type, round to nearest even.
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+  __bf16 b = static_cast<__bf16>(v);
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+// Load / store 8 elements (16 B for bf16, 32 B for fp32) at an aligned address.
+__device__ __forceinline__ bf16x8 load_frag(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ f32x8 load_frag(const float* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint4 a = q[0], b = q[1];
+  f32x8 r;
+  r[0] = __uint_as_float(a.x); r[1] = __uint_as_float(a.y);
+  r[2] = __uint_as_float(a.z); r[3] = __uint_as_float(a.w);
+  r[4] = __uint_as_float(b.x); r[5] = __uint_as_float(b.y);
+  r[6] = __uint_as_float(b.z); r[7] = __uint_as_float(b.w);
+  return r;
+}
+
+// acc += A . B for one 32x32 output tile and 16 K-elements.  Lane l supplies
+// A[l % 32][k in its half] and B[k in its half][l % 32]; the two operands use
+// the same K assignment, so any fixed permutation of K inside a fragment
+// leaves the product unchanged.
+__device__ __forceinline__ void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+}
+
+// Output layout of a 32x32 MFMA accumulator: value i of lane l is
+// C[row_of(i, l)][l % 32].
+__device__ __forceinline__ int acc_row(int i, int lane) {
+  return ((i >> 2) << 3) + ((lane >> 5) << 2) + (i & 3);
+}
+
+// Convert 8 float32 values to a fragment of type T.
+__device__ __forceinline__ bf16x8 to_frag_bf16(float a0, float a1, float a2, float a3, float a4,
+                                               float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = static_cast<__bf16>(a0); r[1] = static_cast<__bf16>(a1);
+  r[2] = static_cast<__bf16>(a2); r[3] = static_cast<__bf16>(a3);
+  r[4] = static_cast<__bf16>(a4); r[5] = static_cast<__bf16>(a5);
+  r[6] = static_cast<__bf16>(a6); r[7] = static_cast<__bf16>(a7);
+  return r;
+}
+template <typename T> struct FragFromAcc;
+template <> struct FragFromAcc<bf16_t> {
+  static __device__ __forceinline__ bf16x8 get(const f32x16& s, int base) {
+    return to_frag_bf16(s[base + 0], s[base + 1], s[base + 2], s[base + 3], s[base + 4],
+                        s[base + 5], s[base + 6], s[base + 7]);
+  }
+};
+template <> struct FragFromAcc<float> {
+  static __device__ __forceinline__ f32x8 get(const f32x16& s, int base) {
+    f32x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = s[base + j];
+    return r;
+  }
+};
+
+// LDS tiles are stored as rows of 16-byte chunks; the chunk index is XORed
+// with the low three bits of the row so that the 32 rows an MFMA fragment
+// read touches spread over all banks.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  constexpr int mask = (ROWB / 16 - 1) < 7 ? (ROWB / 16 - 1) : 7;
+  return row * ROWB + ((chunk ^ (row & mask)) << 4);
+}
+
+// 8 K-elements of row `row`, starting at element `elem`, from a swizzled LDS
+// tile with ROWB-byte rows.
+template <typename T, int ROWB> struct LdsFrag;
+template <int ROWB> struct LdsFrag<bf16_t, ROWB> {
+  static __device__ __forceinline__ bf16x8 get(const char* base, int row, int elem) {
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const uint4*>(base + swz<ROWB>(row, elem >> 3)));
+  }
+};
+template <int ROWB> struct LdsFrag<float, ROWB> {
+  static __device__ __forceinline__ f32x8 get(const char* base, int row, int elem) {
+    const uint4 a = *reinterpret_cast<const uint4*>(base + swz<ROWB>(row, elem >> 2));
+    const uint4 b = *reinterpret_cast<const uint4*>(base + swz<ROWB>(row, (elem >> 2) + 1));
+    f32x8 r;
+    r[0] = __uint_as_float(a.x); r[1] = __uint_as_float(a.y);
+    r[2] = __uint_as_float(a.z); r[3] = __uint_as_float(a.w);
+    r[4] = __uint_as_float(b.x); r[5] = __uint_as_float(b.y);
+    r[6] = __uint_as_float(b.z); r[7] = __uint_as_float(b.w);
+    return r;
+  }
+};
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+}  // namespace gqe

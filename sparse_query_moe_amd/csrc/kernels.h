@@ -1,0 +1,75 @@
+// Launchers of the gfx950 kernels (host side).  Every launcher enqueues on
+// `stream` and returns the launch status; none synchronizes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqe {
+
+typedef uint16_t bf16_t;
+
+// rows of one gathered query-projection tile (the dispatch tile map unit)
+constexpr int kGatherRows = 128;
+
+// ---- K1 router ---------------------------------------------------------------
+size_t router_smem_bytes(int G, int E);
+template <typename T>
+hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* idx, float* w,
+                         int n_tokens, int d, int G, int E, int k, hipStream_t stream);
+
+// ---- K2 dispatch -------------------------------------------------------------
+int dispatch_chunks(int L);
+hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* counts,
+                           int32_t* offsets, int32_t* tile_off, int32_t* pos, int32_t* slot,
+                           int B, int L, int G, int E, int k, int tile_rows, hipStream_t stream);
+
+// ---- K3 projections ----------------------------------------------------------
+// One output segment of a dense projection: columns [n_begin, n_begin + n)
+// of the concatenated output come from `w` (rows of [out, in] layout) and go
+// to head-split tensor `out`, [B, heads, L, D] or, transposed, [B, heads, D, ld_t].
+struct ProjSeg {
+  const void* w;
+  void* out;
+  int n_begin;
+  int n;
+  int heads;
+  int head_base;
+  int transposed;
+};
+template <typename T>
+hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t ld_t,
+                             const ProjSeg* segs, int nseg, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
+                           const int32_t* offsets, const int32_t* pos, const int32_t* slot,
+                           const int32_t* tile_off, int B, int L, int d, int G, int E, int k,
+                           int D, int max_tiles, hipStream_t stream);
+
+// ---- K4 attention ------------------------------------------------------------
+struct AttnParams {
+  const void* q;       // [B, H, L, D]
+  const void* k;       // [B, G, L, D]
+  const void* vt;      // [B, G, D, vt_ld]
+  void* o;             // o[(b*L + t)*ld_o + head*D + d]
+  int64_t vt_ld;
+  int64_t ld_o;
+  int B, H, G, L;
+  int heads_per_group;  // heads h < n_grouped read group h / heads_per_group
+  int n_grouped;
+  int extra_group;      // heads h >= n_grouped read this group
+  float scale_log2;     // softmax scale * log2(e)
+};
+template <typename T>
+hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream);
+
+// ---- K5 output -----------------------------------------------------------------
+template <typename T>
+hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int G, int k, int D,
+                                hipStream_t stream);
+template <typename T>
+hipError_t launch_out_proj(const T* a, const T* wo, T* out, int M, int N, int K,
+                           hipStream_t stream);
+
+}  // namespace gqe

@@ -1,0 +1,222 @@
+"""ctypes binding of libgqe.so (include/gqe.h), one Python function per C entry point.
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU (PyTorch provides device memory
+and streams); they are passed as raw device pointers.  The functions raise
+GqeError when the library returns an error status, and the import fails
+loudly when libgqe.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgqe.so")
+
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+_TORCH_DTYPE = {DTYPE_BF16: torch.bfloat16, DTYPE_FP32: torch.float32}
+
+# every entry point include/gqe.h declares
+EXPORTS = (
+    "gqe_workspace_bytes", "gqe_workspace_layout", "gqe_route", "gqe_dispatch", "gqe_project",
+    "gqe_attention", "gqe_output", "gqe_forward", "gqa_workspace_bytes", "gqa_workspace_layout",
+    "gqa_project", "gqa_attention", "gqa_output", "gqa_forward", "gqe_status_string",
+)
+
+
+class GqeError(RuntimeError):
+    pass
+
+
+class GqeConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("d_model", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("shared_kv_group", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("router_bias", ctypes.c_void_p),
+    ]
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.dtype]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("idx", "w", "counts", "offsets", "pos", "slot", "q", "k", "vt", "s", "scratch",
+                 "total")] + [("vt_ld", ctypes.c_int64)]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m sparse_query_moe_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, cfgp, sz = ctypes.c_void_p, ctypes.POINTER(GqeConfig), ctypes.c_size_t
+    sig = {
+        "gqe_workspace_bytes": (sz, [cfgp]),
+        "gqa_workspace_bytes": (sz, [cfgp]),
+        "gqe_workspace_layout": (ctypes.c_int, [cfgp, ctypes.POINTER(WsLayout)]),
+        "gqa_workspace_layout": (ctypes.c_int, [cfgp, ctypes.POINTER(WsLayout)]),
+        "gqe_route": (ctypes.c_int, [cfgp, vp, vp, vp, sz, vp]),
+        "gqe_dispatch": (ctypes.c_int, [cfgp, vp, sz, vp]),
+        "gqe_project": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, sz, vp]),
+        "gqe_attention": (ctypes.c_int, [cfgp, vp, sz, vp]),
+        "gqe_output": (ctypes.c_int, [cfgp, vp, vp, vp, sz, vp]),
+        "gqe_forward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "gqa_project": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, sz, vp]),
+        "gqa_attention": (ctypes.c_int, [cfgp, vp, sz, vp]),
+        "gqa_output": (ctypes.c_int, [cfgp, vp, vp, vp, sz, vp]),
+        "gqa_forward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "gqe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load_library()
+
+
+def status_string(status: int) -> str:
+    return _lib.gqe_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise GqeError(f"{what}: {status_string(status)} ({status})")
+
+
+def make_config(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim, dtype="bf16",
+                shared_kv_group=0, softmax_scale=0.0, router_bias=None) -> GqeConfig:
+    """Fill a gqe_config.  `router_bias` is a float32 device tensor [G*E] or None;
+    the caller keeps it alive while the config is in use."""
+    dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}.get(dtype, dtype)
+    return GqeConfig(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim,
+                     shared_kv_group, dt, float(softmax_scale),
+                     None if router_bias is None else router_bias.data_ptr())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gqe_workspace_bytes(cfg: GqeConfig) -> int:
+    return int(_lib.gqe_workspace_bytes(ctypes.byref(cfg)))
+
+
+def gqa_workspace_bytes(cfg: GqeConfig) -> int:
+    return int(_lib.gqa_workspace_bytes(ctypes.byref(cfg)))
+
+
+def gqe_workspace_layout(cfg: GqeConfig) -> WsLayout:
+    lay = WsLayout()
+    _check(_lib.gqe_workspace_layout(ctypes.byref(cfg), ctypes.byref(lay)), "gqe_workspace_layout")
+    return lay
+
+
+def gqa_workspace_layout(cfg: GqeConfig) -> WsLayout:
+    lay = WsLayout()
+    _check(_lib.gqa_workspace_layout(ctypes.byref(cfg), ctypes.byref(lay)), "gqa_workspace_layout")
+    return lay
+
+
+def alloc_workspace(cfg: GqeConfig, dense: bool = False, device="cuda") -> torch.Tensor:
+    n = gqa_workspace_bytes(cfg) if dense else gqe_workspace_bytes(cfg)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def gqe_route(cfg, x, wr, ws, stream=None):
+    _check(_lib.gqe_route(ctypes.byref(cfg), _ptr(x), _ptr(wr), _ptr(ws), ws.numel(),
+                          _stream(stream)), "gqe_route")
+
+
+def gqe_dispatch(cfg, ws, stream=None):
+    _check(_lib.gqe_dispatch(ctypes.byref(cfg), _ptr(ws), ws.numel(), _stream(stream)),
+           "gqe_dispatch")
+
+
+def gqe_project(cfg, x, wq, wk, wv, ws, stream=None):
+    _check(_lib.gqe_project(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(ws),
+                            ws.numel(), _stream(stream)), "gqe_project")
+
+
+def gqe_attention(cfg, ws, stream=None):
+    _check(_lib.gqe_attention(ctypes.byref(cfg), _ptr(ws), ws.numel(), _stream(stream)),
+           "gqe_attention")
+
+
+def gqe_output(cfg, wo, out, ws, stream=None):
+    _check(_lib.gqe_output(ctypes.byref(cfg), _ptr(wo), _ptr(out), _ptr(ws), ws.numel(),
+                           _stream(stream)), "gqe_output")
+
+
+def gqe_forward(cfg, x, wq, wk, wv, wr, wo, out, ws, stream=None):
+    _check(_lib.gqe_forward(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wr),
+                            _ptr(wo), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "gqe_forward")
+
+
+def gqa_project(cfg, x, wq, wk, wv, ws, stream=None):
+    _check(_lib.gqa_project(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(ws),
+                            ws.numel(), _stream(stream)), "gqa_project")
+
+
+def gqa_attention(cfg, ws, stream=None):
+    _check(_lib.gqa_attention(ctypes.byref(cfg), _ptr(ws), ws.numel(), _stream(stream)),
+           "gqa_attention")
+
+
+def gqa_output(cfg, wo, out, ws, stream=None):
+    _check(_lib.gqa_output(ctypes.byref(cfg), _ptr(wo), _ptr(out), _ptr(ws), ws.numel(),
+                           _stream(stream)), "gqa_output")
+
+
+def gqa_forward(cfg, x, wq, wk, wv, wo, out, ws, stream=None):
+    _check(_lib.gqa_forward(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+                            _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "gqa_forward")
+
+
+def workspace_views(cfg: GqeConfig, ws: torch.Tensor, dense: bool = False) -> dict:
+    """Typed views of the intermediates inside a workspace (see gqe_ws_layout)."""
+    lay = gqa_workspace_layout(cfg) if dense else gqe_workspace_layout(cfg)
+    B, L, G, E, k, D = (cfg.batch, cfg.seq_len, cfg.n_groups, cfg.n_experts, cfg.top_k,
+                        cfg.head_dim)
+    dt = cfg.torch_dtype
+    es = 2 if dt == torch.bfloat16 else 4
+
+    def view(off, shape, dtype, esize):
+        n = 1
+        for s in shape:
+            n *= s
+        return ws[off:off + n * esize].view(dtype).view(*shape)
+
+    out = {}
+    if not dense:
+        rows = B * L * G * k
+        out["idx"] = view(lay.idx, (B, L, G, k), torch.int32, 4)
+        out["w"] = view(lay.w, (B, L, G, k), torch.float32, 4)
+        out["counts"] = view(lay.counts, (B, G, E), torch.int32, 4)
+        out["offsets"] = view(lay.offsets, (B * G * E + 1,), torch.int32, 4)
+        out["pos"] = view(lay.pos, (rows,), torch.int32, 4)
+        out["slot"] = view(lay.slot, (rows,), torch.int32, 4)
+        out["q"] = view(lay.q, (B, G * k + 1, L, D), dt, es)
+        out["s"] = view(lay.s, (B, L, (G * k + 2) * D), dt, es)
+    else:
+        out["q"] = view(lay.q, (B, G * E, L, D), dt, es)
+        out["s"] = view(lay.s, (B, L, G * E * D), dt, es)
+    out["k"] = view(lay.k, (B, G, L, D), dt, es)
+    out["vt"] = view(lay.vt, (B, G, D, int(lay.vt_ld)), dt, es)
+    return out

@@ -1,0 +1,65 @@
+"""Helpers shared by the GPU tests: moving seeded inputs to the device, reading
+results back as exact float64, and the output gates."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import torch
+
+import workloads as W
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return W.bf16_bits_to_f32(t.contiguous().view(torch.int16).numpy().view(np.uint16)).astype(np.float64)
+    return t.double().numpy()
+
+
+def round_like(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to the stored element type (bf16 RNE or fp32); returns stored form."""
+    a32 = np.asarray(a, dtype=np.float32)
+    return W.f32_to_bf16_bits(a32) if dtype == W.BF16 else a32
+
+
+def output_gate(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+    """The output tolerances: max-abs 2e-2 and mean-abs 2e-3 for bf16 with fp32
+    accumulation; 1e-5 for float32 layers.  Also returns the relative L2 error."""
+    err = np.abs(gpu - ref)
+    rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
+    if dtype == W.BF16:
+        assert err.max() <= 2e-2, f"{what}: max-abs {err.max():.3e} > 2e-2 (rel L2 {rel:.2e})"
+        assert err.mean() <= 2e-3, f"{what}: mean-abs {err.mean():.3e} > 2e-3 (rel L2 {rel:.2e})"
+    else:
+        assert err.max() <= 1e-5, f"{what}: max-abs {err.max():.3e} > 1e-5 (rel L2 {rel:.2e})"
+    return float(err.max()), float(err.mean()), rel
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(name: str, seq_len: int = 0, batch: int = 0):
+    wl = W.WORKLOADS[name]
+    if seq_len:
+        wl = wl.with_(seq_len=seq_len)
+    if batch:
+        wl = wl.with_(batch=batch)
+    return wl, W.make_inputs(wl, with_gqa=True)
+
+
+def f64_inputs(wl, I):
+    f = lambda a: W.to_f64(a, wl.dtype)  # noqa: E731
+    x = W.bf16_bits_to_f32(I["x"]) if wl.dtype == W.BF16 else I["x"]   # exact, float32 storage
+    return dict(x=x, wq=f(I["wq"]), wk=f(I["wk"]), wv=f(I["wv"]), wr=f(I["wr"]), wo=f(I["wo"]),
+                br=I["br"].astype(np.float64), wq_dense=f(I["wq_dense"]), wo_dense=f(I["wo_dense"]))

@@ -1,0 +1,98 @@
+"""The C ABI library: it loads, exports every declared entry point, and rejects
+bad arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqe.h")
+LIB = os.path.join(ROOT, "sparse_query_moe_amd", "libgqe.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gq[ae]_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def gqe():
+    if not os.path.exists(LIB):
+        from sparse_query_moe_amd import build
+        build.build()
+    from sparse_query_moe_amd import gqe as mod
+    return mod
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("gqe_forward", "gqa_forward", "gqe_workspace_bytes", "gqe_workspace_layout",
+              "gqe_route", "gqe_dispatch", "gqe_project", "gqe_attention", "gqe_output",
+              "gqe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(gqe):
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared_functions()) == set(gqe.EXPORTS)
+
+
+def _cfg(gqe, **kw):
+    base = dict(batch=1, seq_len=2048, d_model=1024, n_groups=4, n_experts=4, top_k=2, head_dim=64)
+    base.update(kw)
+    return gqe.make_config(**base)
+
+
+def test_config_validation(gqe):
+    assert gqe.gqe_workspace_bytes(_cfg(gqe)) > 0
+    bad = [dict(top_k=0), dict(top_k=5), dict(d_model=1020), dict(n_groups=0), dict(seq_len=-1),
+           dict(n_experts=33), dict(n_groups=9, n_experts=8), dict(shared_kv_group=4),
+           dict(head_dim=0), dict(dtype=7), dict(softmax_scale=-1.0)]
+    for b in bad:
+        assert gqe.gqe_workspace_bytes(_cfg(gqe, **b)) == 0, b
+    assert gqe.gqe_workspace_bytes(_cfg(gqe, head_dim=96)) == 0
+    lib = gqe._lib
+    lay = gqe.WsLayout()
+    assert lib.gqe_workspace_layout(ctypes.byref(_cfg(gqe, head_dim=96)), ctypes.byref(lay)) == -2
+    assert lib.gqe_workspace_layout(ctypes.byref(_cfg(gqe, top_k=9)), ctypes.byref(lay)) == -1
+
+
+def test_workspace_monotone_and_aligned(gqe):
+    prev = 0
+    for L in (1, 63, 64, 65, 2048, 8192, 131072):
+        n = gqe.gqe_workspace_bytes(_cfg(gqe, seq_len=L))
+        assert n >= prev
+        prev = n
+        lay = gqe.gqe_workspace_layout(_cfg(gqe, seq_len=L))
+        for f in ("idx", "w", "counts", "offsets", "pos", "slot", "q", "k", "vt", "s"):
+            assert getattr(lay, f) % 256 == 0
+        assert lay.vt_ld >= L and lay.vt_ld % 64 == 0
+    assert gqe.gqe_workspace_bytes(_cfg(gqe, batch=2)) > gqe.gqe_workspace_bytes(_cfg(gqe))
+
+
+def test_host_errors_before_any_launch(gqe):
+    """Invalid arguments return a status on the host; nothing touches a device."""
+    lib = gqe._lib
+    cfg = _cfg(gqe)
+    n = gqe.gqe_workspace_bytes(cfg)
+    # null pointers
+    st = lib.gqe_forward(ctypes.byref(cfg), None, None, None, None, None, None, None, None, n, None)
+    assert st == -1
+    # misaligned workspace
+    st = lib.gqe_dispatch(ctypes.byref(cfg), ctypes.c_void_p(8), n, None)
+    assert st == -1
+    # workspace too small
+    st = lib.gqe_dispatch(ctypes.byref(cfg), ctypes.c_void_p(256), n - 1, None)
+    assert st == -3
+    # invalid config
+    st = lib.gqe_attention(ctypes.byref(_cfg(gqe, top_k=0)), ctypes.c_void_p(256), n, None)
+    assert st == -1
+    # empty input: nothing to do
+    st = lib.gqe_forward(ctypes.byref(_cfg(gqe, seq_len=0)), None, None, None, None, None, None,
+                         None, None, 0, None)
+    assert st == 0
+    assert gqe.status_string(-3).startswith("GQE_ERR_WORKSPACE")

@@ -1,0 +1,297 @@
+"""HIP path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Stage tests seed each stage with the oracle's inputs so errors do not
+compound; layer tests run gqe_forward / gqa_forward end to end.  Routing and
+dispatch must match bit for bit; floating outputs must meet max-abs 2e-2 and
+mean-abs 2e-3 (bf16 with fp32 accumulation) or 1e-5 (float32 layers).
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from gpu_util import f64_inputs, inputs, log, output_gate, round_like, to_dev, to_f64  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gqe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_query_moe_amd import gqe as mod
+    return mod
+
+
+def cfg_for(gqe, wl, bias_dev=None, **kw):
+    return gqe.make_config(wl.batch, wl.seq_len, wl.d_model, wl.n_groups, wl.n_experts, wl.top_k,
+                           wl.head_dim, dtype=wl.dtype, router_bias=bias_dev, **kw)
+
+
+def device_inputs(wl, I):
+    return {k: to_dev(v, wl.dtype) for k, v in I.items()}
+
+
+def run_gqe(gqe, wl, I, dev=None, **cfgkw):
+    dev = dev or device_inputs(wl, I)
+    cfg = cfg_for(gqe, wl, dev["br"], **cfgkw)
+    ws = gqe.alloc_workspace(cfg)
+    out = torch.empty((wl.batch, wl.seq_len, wl.d_model), dtype=cfg.torch_dtype, device="cuda")
+    gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], out, ws)
+    torch.cuda.synchronize()
+    return cfg, ws, out
+
+
+def oracle_gqe(wl, F, positions=None, **kw):
+    return oracle.gqe_forward(F["x"], F["wq"], F["wk"], F["wv"], F["wr"], F["wo"], F["br"],
+                              wl.n_groups, wl.n_experts, wl.top_k, wl.head_dim,
+                              positions=positions, **kw)
+
+
+def check_routing(gqe, cfg, ws, ref):
+    v = gqe.workspace_views(cfg, ws)
+    idx = v["idx"].cpu().numpy()
+    assert np.array_equal(idx, ref["idx"]), f"idx mismatches: {(idx != ref['idx']).sum()}"
+    w = v["w"].cpu().numpy().astype(np.float64)
+    assert np.abs(w - ref["w"]).max() <= 2e-7
+    assert np.array_equal(v["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(v["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(v["pos"].cpu().numpy(), ref["pos"])
+    assert np.array_equal(v["slot"].cpu().numpy(), ref["slot"])
+
+
+# ---------------------------------------------------------------------------
+# stage parity (tiny fp32 layer, the 2k bf16 layer, and a ragged shape)
+# ---------------------------------------------------------------------------
+
+STAGE_CASES = [("tiny_fp32", 0, 0), ("l2k", 0, 0), ("l2k", 333, 2)]
+
+
+@pytest.mark.parametrize("name,L,B", STAGE_CASES)
+def test_stage_route_and_dispatch(gqe, name, L, B):
+    wl, I = inputs(name, L, B)
+    log(f"[route+dispatch] {name} B={wl.batch} L={wl.seq_len}")
+    F = f64_inputs(wl, I)
+    r, p, idx, w = oracle.route(F["x"].reshape(-1, wl.d_model), F["wr"], F["br"], wl.n_groups,
+                                wl.n_experts, wl.top_k)
+    idx = idx.reshape(wl.batch, wl.seq_len, wl.n_groups, wl.top_k)
+    counts, offsets, pos, slot = oracle.dispatch(idx, wl.n_experts)
+    dev = device_inputs(wl, I)
+    cfg = cfg_for(gqe, wl, dev["br"])
+    ws = gqe.alloc_workspace(cfg)
+    gqe.gqe_route(cfg, dev["x"], dev["wr"], ws)
+    gqe.gqe_dispatch(cfg, ws)
+    torch.cuda.synchronize()
+    check_routing(gqe, cfg, ws, dict(idx=idx, w=w.reshape(idx.shape), counts=counts,
+                                     offsets=offsets, pos=pos, slot=slot))
+
+
+@pytest.mark.parametrize("pattern", ["uniform_ties", "one_expert_empty", "all_same", "random"])
+def test_stage_dispatch_patterns(gqe, pattern):
+    """Dispatch alone on seeded idx patterns: ties everywhere, an empty expert,
+    every token picking the same pair, and random selections; B=3, L=1000."""
+    B, L, G, E, k = 3, 1000, 4, 4, 2
+    rng = np.random.default_rng(5)
+    if pattern == "uniform_ties":
+        idx = np.broadcast_to(np.arange(k), (B, L, G, k)).copy()
+    elif pattern == "one_expert_empty":
+        idx = np.stack([rng.permutation(3)[:k] for _ in range(B * L * G)]).reshape(B, L, G, k)
+    elif pattern == "all_same":
+        idx = np.broadcast_to(np.array([3, 1]), (B, L, G, k)).copy()
+    else:
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(B * L * G)]).reshape(B, L, G, k)
+    idx = idx.astype(np.int32)
+    log(f"[dispatch] pattern={pattern}")
+    cfg = gqe.make_config(B, L, 64, G, E, k, 64)
+    ws = gqe.alloc_workspace(cfg)
+    v = gqe.workspace_views(cfg, ws)
+    v["idx"].copy_(torch.from_numpy(idx))
+    gqe.gqe_dispatch(cfg, ws)
+    torch.cuda.synchronize()
+    counts, offsets, pos, slot = oracle.dispatch(idx, E)
+    assert np.array_equal(v["counts"].cpu().numpy(), counts)
+    assert np.array_equal(v["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(v["pos"].cpu().numpy(), pos)
+    assert np.array_equal(v["slot"].cpu().numpy(), slot)
+
+
+@pytest.mark.parametrize("name,L,B", STAGE_CASES)
+def test_stage_project(gqe, name, L, B):
+    wl, I = inputs(name, L, B)
+    log(f"[project] {name} B={wl.batch} L={wl.seq_len}")
+    F = f64_inputs(wl, I)
+    ref = oracle_gqe(wl, F)
+    dev = device_inputs(wl, I)
+    cfg = cfg_for(gqe, wl, dev["br"])
+    ws = gqe.alloc_workspace(cfg)
+    gqe.gqe_route(cfg, dev["x"], dev["wr"], ws)
+    gqe.gqe_dispatch(cfg, ws)
+    gqe.gqe_project(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], ws)
+    torch.cuda.synchronize()
+    v = gqe.workspace_views(cfg, ws)
+    q = to_f64(v["q"]).transpose(0, 2, 1, 3)            # [B, L, kG+1, D]
+    k = to_f64(v["k"])
+    vt = to_f64(v["vt"])[..., :wl.seq_len]
+    tol = 2.0 ** -8 if wl.dtype == W.BF16 else 1e-6
+    for got, want, what in ((q, ref["q"], "q"), (k, ref["k_"], "k"),
+                            (vt, ref["v"].transpose(0, 1, 3, 2), "vt")):
+        err = np.abs(got - want)
+        bound = tol * np.abs(want) + 1e-6 * np.abs(want).max()
+        assert (err <= bound).all(), f"{what}: worst {err.max():.3e}"
+
+
+@pytest.mark.parametrize("name,L,B", STAGE_CASES)
+def test_stage_attention(gqe, name, L, B):
+    """gqe_attention on oracle Q/K/V rounded to the storage type, against the
+    oracle's attention of the same rounded values."""
+    wl, I = inputs(name, L, B)
+    log(f"[attention] {name} B={wl.batch} L={wl.seq_len}")
+    F = f64_inputs(wl, I)
+    ref = oracle_gqe(wl, F)
+    cfg = cfg_for(gqe, wl)
+    ws = gqe.alloc_workspace(cfg)
+    v = gqe.workspace_views(cfg, ws)
+    q_st = round_like(ref["q"].transpose(0, 2, 1, 3), wl.dtype)      # [B, H, L, D]
+    k_st = round_like(ref["k_"], wl.dtype)
+    v_st = round_like(ref["v"], wl.dtype)
+    v["q"].copy_(to_dev(q_st, wl.dtype))
+    v["k"].copy_(to_dev(k_st, wl.dtype))
+    v["vt"][..., :wl.seq_len].copy_(to_dev(np.ascontiguousarray(v_st.transpose(0, 1, 3, 2)), wl.dtype))
+    gqe.gqe_attention(cfg, ws)
+    torch.cuda.synchronize()
+    qf = W.to_f64(q_st, wl.dtype)
+    kf, vf = W.to_f64(k_st, wl.dtype), W.to_f64(v_st, wl.dtype)
+    H = wl.slot_heads
+    s = to_f64(v["s"]).reshape(wl.batch, wl.seq_len, H + 1, wl.head_dim)
+    t = np.arange(wl.seq_len)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    for b in range(wl.batch):
+        for h in range(H):
+            g = h // wl.top_k if h < H - 1 else 0
+            want = oracle.causal_attention(qf[b, h], t, kf[b, g], vf[b, g], scale)
+            output_gate(s[b, :, h], want, wl.dtype, f"attention b={b} h={h}")
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+LAYER_CASES = ["tiny_fp32", "l2k", "b4_l8k", "l128k", "l1m_zipf"]
+
+
+@pytest.mark.parametrize("name", LAYER_CASES)
+def test_gqe_forward(gqe, name):
+    wl, I = inputs(name)
+    rows = W.sample_rows(wl)
+    log(f"[gqe_forward] {name} B={wl.batch} L={wl.seq_len} rows={len(rows)}")
+    cfg, ws, out = run_gqe(gqe, wl, I)
+    log("  gpu done; oracle ...")
+    F = f64_inputs(wl, I)
+    ref = oracle_gqe(wl, F, positions=None if wl.sample_rows == 0 else rows)
+    check_routing(gqe, cfg, ws, ref)
+    y = to_f64(out[:, rows])
+    mx, mean, rel = output_gate(y, ref["y"], wl.dtype, f"{name} y")
+    log(f"  y: max-abs {mx:.3e} mean-abs {mean:.3e} rel-L2 {rel:.3e}")
+    assert rel <= (2e-2 if wl.dtype == W.BF16 else 1e-5)
+    # slot vectors (hard, shared and weighted) too
+    s = to_f64(gqe.workspace_views(cfg, ws)["s"][:, rows])
+    output_gate(s, ref["s"], wl.dtype, f"{name} s")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "l2k", "b4_l8k"])
+def test_gqa_forward(gqe, name):
+    wl, I = inputs(name)
+    log(f"[gqa_forward] {name} B={wl.batch} L={wl.seq_len}")
+    dev = device_inputs(wl, I)
+    cfg = cfg_for(gqe, wl)
+    ws = gqe.alloc_workspace(cfg, dense=True)
+    out = torch.empty((wl.batch, wl.seq_len, wl.d_model), dtype=cfg.torch_dtype, device="cuda")
+    gqe.gqa_forward(cfg, dev["x"], dev["wq_dense"].contiguous(), dev["wk"], dev["wv"],
+                    dev["wo_dense"], out, ws)
+    torch.cuda.synchronize()
+    F = f64_inputs(wl, I)
+    ref = oracle.gqa_forward(F["x"], F["wq_dense"], F["wk"], F["wv"], F["wo_dense"],
+                             wl.n_groups, wl.n_experts, wl.head_dim)
+    mx, mean, rel = output_gate(to_f64(out), ref["y"], wl.dtype, f"gqa {name}")
+    log(f"  y: max-abs {mx:.3e} mean-abs {mean:.3e} rel-L2 {rel:.3e}")
+
+
+def test_gqe_with_k_equal_e_matches_gqa_on_gpu(gqe):
+    """k=E with a zero router (ties resolve in index order) and the shared and
+    weighted W_O rows zeroed is dense GQA: both GPU paths must agree."""
+    wl, I = inputs("l2k", 512)
+    wl = wl.with_(top_k=wl.n_experts)
+    G, E, D, d = wl.n_groups, wl.n_experts, wl.head_dim, wl.d_model
+    J = dict(I)
+    J["wr"] = np.zeros_like(I["wr"])
+    wo = np.zeros((d, (E * G + 2) * D), dtype=np.uint16)
+    wo[:, :G * E * D] = I["wo_dense"]
+    J["wo"] = wo
+    _, _, y_gqe = run_gqe(gqe, wl, J)
+    dev = device_inputs(wl, J)
+    cfg = cfg_for(gqe, wl)
+    ws = gqe.alloc_workspace(cfg, dense=True)
+    y_gqa = torch.empty_like(y_gqe)
+    gqe.gqa_forward(cfg, dev["x"], dev["wq_dense"].contiguous(), dev["wk"], dev["wv"],
+                    dev["wo_dense"], y_gqa, ws)
+    torch.cuda.synchronize()
+    output_gate(to_f64(y_gqe), to_f64(y_gqa), wl.dtype, "k=E vs gqa")
+
+
+def test_determinism(gqe):
+    wl, I = inputs("l2k")
+    dev = device_inputs(wl, I)
+    _, ws1, y1 = run_gqe(gqe, wl, I, dev)
+    _, ws2, y2 = run_gqe(gqe, wl, I, dev)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(ws1, ws2)
+
+
+@pytest.mark.parametrize("L,B,G,E,k,D,dtype", [
+    (1, 1, 4, 4, 2, 64, "bf16"),
+    (65, 2, 4, 4, 2, 64, "bf16"),
+    (200, 1, 2, 3, 3, 32, "fp32"),
+    (130, 1, 1, 1, 1, 128, "bf16"),
+    (97, 2, 3, 5, 2, 128, "fp32"),
+    (300, 1, 8, 2, 1, 64, "bf16"),
+])
+def test_edge_shapes(gqe, L, B, G, E, k, D, dtype):
+    """Ragged lengths, a single token, one group / one expert, k = E, every head size."""
+    wl = W.Workload("edge", B, L, 128, G, E, k, D, dtype, 1.0, 0.05)
+    log(f"[edge] {wl}")
+    I = W.make_inputs(wl, seed=3, with_gqa=True)
+    cfg, ws, out = run_gqe(gqe, wl, I)
+    F = f64_inputs(wl, I)
+    ref = oracle_gqe(wl, F)
+    check_routing(gqe, cfg, ws, ref)
+    output_gate(to_f64(out), ref["y"], wl.dtype, "edge y")
+
+
+def test_shared_head_group_and_scale(gqe):
+    """shared_kv_group and an explicit softmax scale are honoured."""
+    wl, I = inputs("l2k", 256)
+    cfg, ws, out = run_gqe(gqe, wl, I, shared_kv_group=2, softmax_scale=0.3)
+    F = f64_inputs(wl, I)
+    ref = oracle_gqe(wl, F, shared_kv_group=2, scale=0.3)
+    output_gate(to_f64(out), ref["y"], wl.dtype, "shared group 2 / scale 0.3")
+
+
+def test_empty_and_errors(gqe):
+    wl, I = inputs("l2k", 64)
+    dev = device_inputs(wl, I)
+    cfg = gqe.make_config(1, 0, wl.d_model, 4, 4, 2, 64)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(0, device="cuda", dtype=torch.bfloat16)
+    gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], out, ws)
+    cfg = cfg_for(gqe, wl)
+    small = torch.empty(gqe.gqe_workspace_bytes(cfg) - 256, dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 64, wl.d_model), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gqe.GqeError, match="WORKSPACE"):
+        gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], out,
+                        small)
+    with pytest.raises(gqe.GqeError, match="UNSUPPORTED"):
+        gqe.gqe_workspace_layout(gqe.make_config(1, 64, wl.d_model, 4, 4, 2, 80))
