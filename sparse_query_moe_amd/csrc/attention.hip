@@ -26,6 +26,8 @@
 //   Blocks are issued heaviest query block first to shorten the causal tail.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -35,9 +37,9 @@ namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-template <typename T, int D>
+template <typename T, int D, int QB = 1>
 struct AttnShape {
-  static constexpr int BQ = 128, BKV = 64;
+  static constexpr int BQ = 4 * 32 * QB, BKV = 64;  // 4 waves, QB 32-query blocks each
   static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
   static constexpr int KROW = D * static_cast<int>(sizeof(T));    // bytes per K tile row (a key)
   static constexpr int VROW = BKV * static_cast<int>(sizeof(T));  // bytes per V^T tile row (a dim)
@@ -88,10 +90,33 @@ __device__ __forceinline__ uint4 mask_keys(uint4 v, int k0, int L) {
   return v;
 }
 
-template <typename T, int D>
+// q . scale * log2(e), rounded back to the storage type: scores come out of the
+// MFMA already in log2 units.
+__device__ __forceinline__ bf16x8 scale_frag(const bf16x8& f, float c) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = static_cast<__bf16>(static_cast<float>(f[j]) * c);
+  return r;
+}
+__device__ __forceinline__ f32x8 scale_frag(const f32x8& f, float c) { return f * c; }
+
+__device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s = fmaf(static_cast<float>(a[j]), static_cast<float>(b[j]), s);
+  return s;
+}
+__device__ __forceinline__ float dot8(const f32x8& a, const f32x8& b) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s = fmaf(a[j], b[j], s);
+  return s;
+}
+
+template <typename T, int D, int QB>
 __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void attention_kernel(
     AttnParams p) {
-  typedef AttnShape<T, D> S;
+  typedef AttnShape<T, D, QB> S;
   typedef typename Frag<T>::type F;
   extern __shared__ __align__(16) char smem[];
 
@@ -110,19 +135,41 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
   const T* Vg = static_cast<const T*>(p.vt) + (static_cast<size_t>(b) * p.G + g) * D * p.vt_ld;
 
   const int q0 = qblk * S::BQ;
-  const int qw0 = q0 + 32 * wave;
-  const int qrow = qw0 + (lane & 31);
+  const int qw0 = q0 + 32 * QB * wave;                 // first query of this wave
+  const int wave_last = min(qw0 + 32 * QB - 1, L - 1);  // last valid query of this wave
   const bool wave_active = qw0 < L;
-  const int q_last = min(qw0 + 31, L - 1);
 
-  F qf[S::NKS];
+  // queries (pre-scaled) in registers; the running maximum starts at the score
+  // against key 0, which every causal row sees, so it is finite from the start
+  int qrow[QB];
+  F qf[QB][S::NKS];
+  float m_run[QB], l_run[QB];
+  f32x16 o[QB][S::NDB];
+  {
+    F k0[S::NKS];
 #pragma unroll
-  for (int ks = 0; ks < S::NKS; ++ks) {
-    if (qrow < L) {
-      qf[ks] = load_frag(Q + static_cast<size_t>(qrow) * D + ks * 16 + 8 * half);
-    } else {
+    for (int ks = 0; ks < S::NKS; ++ks) k0[ks] = load_frag(Kg + ks * 16 + 8 * half);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qf[ks][j] = 0;
+    for (int qb = 0; qb < QB; ++qb) {
+      qrow[qb] = qw0 + 32 * qb + (lane & 31);
+      float dot = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < S::NKS; ++ks) {
+        if (qrow[qb] < L) {
+          qf[qb][ks] = scale_frag(load_frag(Q + static_cast<size_t>(qrow[qb]) * D + ks * 16 + 8 * half),
+                                  p.scale_log2);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qf[qb][ks][j] = 0;
+        }
+        dot += dot8(qf[qb][ks], k0[ks]);
+      }
+      m_run[qb] = dot + __shfl_xor(dot, 32, 64);
+      l_run[qb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
     }
   }
 
@@ -168,12 +215,89 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 o[S::NDB];
+  // one 64-key tile for this wave's QB query blocks
+  auto tile = [&](const char* Ks, const char* Vs, int j0, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    // S^T - m: the accumulator starts at -m_run, so exp2 applies directly
+    f32x16 s[QB][2];
 #pragma unroll
-  for (int db = 0; db < S::NDB; ++db)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[qb][kb][i] = -m_run[qb];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < S::NKS; ++ks) {
+        const F kf = LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mma32(s[qb][kb], kf, qf[qb][ks]);
+      }
+    if constexpr (MASK) {  // drop keys after the query
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (j0 + 32 * kb + acc_row(i, lane) > qrow[qb]) s[qb][kb][i] = -INFINITY;
+    }
+    float mx[QB];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float v = s[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v = fmaxf(v, s[qb][kb][i]);
+      mx[qb] = fmaxf(v, __shfl_xor(v, 32, 64));
+      need = need || (mx[qb] > kRescaleThreshold);
+    }
+    if (__any(need)) {  // raise the running maximum (wave-uniform branch)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float sh = fmaxf(mx[qb], 0.f);
+        const float alpha = __builtin_amdgcn_exp2f(-sh);
+        m_run[qb] += sh;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[qb][kb][i] -= sh;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(s[qb][kb][i]);
+          s[qb][kb][i] = pv;
+          ls += pv;
+        }
+      l_run[qb] += ls;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      F pf[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) pf[qb] = FragFromAcc<T>::get(s[qb][ks >> 1], 8 * (ks & 1));
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db) {
+        const F vf = LdsFrag<T, S::VROW>::get(Vs, 32 * db + (lane & 31), ks * 16 + 8 * half);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mma32(o[qb][db], vf, pf[qb]);
+      }
+    }
+  };
 
   gload(0);
   sstore(0);
@@ -183,110 +307,78 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
     const char* Ks = smem + (jt & 1) * S::STAGE;
     const char* Vs = Ks + S::KT;
     const int j0 = jt * S::BKV;
-    if (wave_active && j0 <= q_last) {
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < S::NKS; ++ks)
-          mma32(s[kb], LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half),
-                qf[ks]);
-      }
-      if (j0 + S::BKV - 1 > qw0) {  // diagonal tile: drop keys after the query
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (j0 + 32 * kb + acc_row(i, lane) > qrow) s[kb][i] = -INFINITY;
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mxs = mx * p.scale_log2;
-      if (__any(mxs > m_run + kRescaleThreshold)) {
-        const float mn = fmaxf(m_run, mxs);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < S::NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        m_run = mn;
-      }
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -m_run));
-          s[kb][i] = pv;
-          ls += pv;
-        }
-      l_run += ls;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const F pf = FragFromAcc<T>::get(s[ks >> 1], 8 * (ks & 1));
-#pragma unroll
-        for (int db = 0; db < S::NDB; ++db)
-          mma32(o[db], LdsFrag<T, S::VROW>::get(Vs, 32 * db + (lane & 31), ks * 16 + 8 * half), pf);
-      }
+    if (wave_active && j0 <= wave_last) {
+      if (j0 + S::BKV - 1 <= qw0)
+        tile(Ks, Vs, j0, std::false_type{});
+      else
+        tile(Ks, Vs, j0, std::true_type{});
     }
     if (jt + 1 < ntiles) sstore((jt + 1) & 1);
     __syncthreads();
   }
 
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (qrow < L) {
-    const float inv = 1.f / l_run;
-    T* out = static_cast<T*>(p.o) + (static_cast<size_t>(b) * L + qrow) * p.ld_o +
-             static_cast<size_t>(head) * D;
 #pragma unroll
-    for (int db = 0; db < S::NDB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    if (qrow[qb] < L) {
+      const float inv = 1.f / l_tot;
+      T* out = static_cast<T*>(p.o) + (static_cast<size_t>(b) * L + qrow[qb]) * p.ld_o +
+               static_cast<size_t>(head) * D;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = 32 * db + 8 * a + 4 * half;
-        T v[4];
+      for (int db = 0; db < S::NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = from_f32<T>(o[db][4 * a + r] * inv);
-        if constexpr (sizeof(T) == 2)
-          *reinterpret_cast<uint2*>(out + d0) = *reinterpret_cast<const uint2*>(v);
-        else
-          *reinterpret_cast<uint4*>(out + d0) = *reinterpret_cast<const uint4*>(v);
-      }
+        for (int a = 0; a < 4; ++a) {
+          const int d0 = 32 * db + 8 * a + 4 * half;
+          T v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = from_f32<T>(o[qb][db][4 * a + r] * inv);
+          if constexpr (sizeof(T) == 2)
+            *reinterpret_cast<uint2*>(out + d0) = *reinterpret_cast<const uint2*>(v);
+          else
+            *reinterpret_cast<uint4*>(out + d0) = *reinterpret_cast<const uint4*>(v);
+        }
+    }
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int QB>
 hipError_t launch_attention_d(const AttnParams& p, hipStream_t stream) {
-  typedef AttnShape<T, D> S;
+  typedef AttnShape<T, D, QB> S;
   const int nq = (p.L + S::BQ - 1) / S::BQ;
   const long long blocks = static_cast<long long>(nq) * p.B * p.H;
   if (blocks == 0) return hipSuccess;
   if (S::LDS > 65536) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attention_kernel<T, D>),
+        reinterpret_cast<const void*>(&attention_kernel<T, D, QB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((attention_kernel<T, D>), dim3(static_cast<unsigned>(blocks)), dim3(256),
+  hipLaunchKernelGGL((attention_kernel<T, D, QB>), dim3(static_cast<unsigned>(blocks)), dim3(256),
                      S::LDS, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Two 32-query blocks per wave halve the LDS traffic per MFMA; short
+// sequences keep one so that the grid still covers the chip.
 template <typename T>
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream) {
-  switch (D) {
-    case 32: return launch_attention_d<T, 32>(p, stream);
-    case 64: return launch_attention_d<T, 64>(p, stream);
-    case 128: return launch_attention_d<T, 128>(p, stream);
-    default: return hipErrorInvalidValue;
+  if constexpr (sizeof(T) == 2) {
+    const bool wide = static_cast<long long>(p.L) * p.B * p.H >= 256LL * 256 * 4;
+    switch (D) {
+      case 32: return wide ? launch_attention_d<T, 32, 2>(p, stream) : launch_attention_d<T, 32, 1>(p, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 2>(p, stream) : launch_attention_d<T, 64, 1>(p, stream);
+      case 128: return launch_attention_d<T, 128, 1>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (D) {
+      case 32: return launch_attention_d<T, 32, 1>(p, stream);
+      case 64: return launch_attention_d<T, 64, 1>(p, stream);
+      case 128: return launch_attention_d<T, 128, 1>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 

@@ -145,11 +145,20 @@ struct DenseProb {
   const DenseArgs& a;
   int m0, n0, K;
   __device__ DenseProb(const DenseArgs& args, int m0_, int n0_) : a(args), m0(m0_), n0(n0_), K(args.K) {}
-  __device__ __forceinline__ int seg_of(int col) const {
-    int s = 0;
-    if (a.nseg > 1 && col >= a.seg[1].n_begin) s = 1;
-    if (a.nseg > 2 && col >= a.seg[2].n_begin) s = 2;
-    return s;
+  // the segment holding output column col, selected field by field (a dynamic
+  // index into the argument array would spill it to scratch)
+  __device__ __forceinline__ ProjSeg seg_of(int col) const {
+    const bool s1 = a.nseg > 1 && col >= a.seg[1].n_begin;
+    const bool s2 = a.nseg > 2 && col >= a.seg[2].n_begin;
+    ProjSeg r;
+    r.w = s2 ? a.seg[2].w : s1 ? a.seg[1].w : a.seg[0].w;
+    r.out = s2 ? a.seg[2].out : s1 ? a.seg[1].out : a.seg[0].out;
+    r.n_begin = s2 ? a.seg[2].n_begin : s1 ? a.seg[1].n_begin : a.seg[0].n_begin;
+    r.n = 0;
+    r.heads = s2 ? a.seg[2].heads : s1 ? a.seg[1].heads : a.seg[0].heads;
+    r.head_base = s2 ? a.seg[2].head_base : s1 ? a.seg[1].head_base : a.seg[0].head_base;
+    r.transposed = s2 ? a.seg[2].transposed : s1 ? a.seg[1].transposed : a.seg[0].transposed;
+    return r;
   }
   __device__ __forceinline__ const T* a_row(int r) const {
     const int m = m0 + r;
@@ -158,13 +167,13 @@ struct DenseProb {
   __device__ __forceinline__ const T* b_row(int n) const {
     const int col = n0 + n;
     if (col >= a.N) return nullptr;
-    const ProjSeg& sg = a.seg[seg_of(col)];
+    const ProjSeg sg = seg_of(col);
     return static_cast<const T*>(sg.w) + static_cast<size_t>(col - sg.n_begin) * a.K;
   }
   __device__ __forceinline__ void store(int r, int n, float v) const {
     const int m = m0 + r, col = n0 + n;
     if (m >= a.M || col >= a.N) return;
-    const ProjSeg& sg = a.seg[seg_of(col)];
+    const ProjSeg sg = seg_of(col);
     const int c = col - sg.n_begin;
     const int hh = sg.head_base + c / a.D, dd = c % a.D;
     const int b = m / a.L, t = m % a.L;

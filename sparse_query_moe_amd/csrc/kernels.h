@@ -13,7 +13,6 @@ typedef uint16_t bf16_t;
 constexpr int kGatherRows = 128;
 
 // ---- K1 router ---------------------------------------------------------------
-size_t router_smem_bytes(int G, int E);
 template <typename T>
 hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* idx, float* w,
                          int n_tokens, int d, int G, int E, int k, hipStream_t stream);

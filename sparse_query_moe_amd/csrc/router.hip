@@ -10,15 +10,18 @@
 //   w[t, g, j]  = exp(r_j - r_0) / sum_j' exp(r_j' - r_0), which equals the
 //                  in-group softmax renormalized over the selected k.
 //
-// The logits are accumulated in float64: products of two bf16 (or two fp32)
-// values are exact in float64, so the only rounding is in the sums, far below
-// the gaps that decide the selection.
+// The logits are accumulated in float64 on the fp64 matrix cores
+// (v_mfma_f64_16x16x4: 16 tokens x 16 experts x 4 model dims per
+// instruction): bf16 or fp32 inputs are exact in float64, so the only rounding
+// is in the sums, far below the gaps that decide the selection.
 //
-// Work split: a block of 256 threads handles 64 tokens; thread (tok, part)
-// accumulates the experts e = part + 4m.  x and Wr stream through LDS in
-// chunks of 64 model dimensions; the selection then runs one thread per
-// (token, group).  HBM traffic is x once plus idx/w: the kernel is bound by
-// float64 FMA throughput at about 16 FMAs per loaded x element.
+// A block of 4 waves takes 16 tokens; each wave accumulates a quarter of the
+// model dimension and the four partial 16x16 tiles are added in LDS in a fixed
+// order (deterministic).  Every lane loads 8 consecutive elements of x and of
+// Wr per 32-dimension step and feeds them to 8 MFMAs; the K index each
+// (lane, step) pair covers is the same for both operands, so the products
+// pair up correctly.  The selection computes each expert's rank (number of
+// experts ahead of it), which needs no per-thread arrays.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -26,147 +29,117 @@ namespace gqe {
 
 namespace {
 
-constexpr int kTokPerBlock = 64;
-constexpr int kDChunk = 64;
-constexpr int kXStride = kDChunk + 1;  // odd float stride: conflict-free row reads
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTok = 16;
+
+template <typename T>
+__device__ __forceinline__ void load8_f64(const T* p, bool ok, double (&v)[8]) {
+  if (!ok) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.0;
+    return;
+  }
+  if constexpr (sizeof(T) == 2) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = static_cast<double>(__uint_as_float(w[j] << 16));
+      v[2 * j + 1] = static_cast<double>(__uint_as_float(w[j] & 0xffff0000u));
+    }
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint4 b = *reinterpret_cast<const uint4*>(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int n_tokens, int d, int G, int E,
     int k) {
-  extern __shared__ __align__(16) char smem[];
+  __shared__ double part[4][kTok][17];
+  __shared__ double logit[kTok][65];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, h = lane >> 4;
+  const int t0 = blockIdx.x * kTok;
+  const int tok = t0 + row;
   const int GE = G * E;
-  float* xs = reinterpret_cast<float*>(smem);                                   // [64][65]
-  double* ws = reinterpret_cast<double*>(smem + kTokPerBlock * kXStride * 4 + 16);  // [GE][64]
-  double* rl = ws;  // reused after the dot products: [64][GE+1]
+  const int nsteps = (d + 31) >> 5;
 
-  const int tid = threadIdx.x;
-  const int tok = tid & 63;
-  const int part = tid >> 6;
-  const int t0 = blockIdx.x * kTokPerBlock;
-  const int ept = (GE + 3) >> 2;  // experts per thread (<= 16)
-
-  double acc[16];
+  for (int eb = 0; eb < GE; eb += 16) {
+    const int e = eb + row;
+    const T* xp = x + static_cast<size_t>(tok < n_tokens ? tok : 0) * d;
+    const T* wp = wr + static_cast<size_t>(e < GE ? e : 0) * d;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+    for (int st = wave; st < nsteps; st += 4) {
+      const int d0 = st * 32 + 8 * h;
+      double xv[8], wv[8];
+      load8_f64(xp + d0, tok < n_tokens && d0 < d, xv);
+      load8_f64(wp + d0, e < GE && d0 < d, wv);
 #pragma unroll
-  for (int m = 0; m < 16; ++m) acc[m] = 0.0;
-
-  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
-  for (int d0 = 0; d0 < d; d0 += kDChunk) {
-    const int dn = min(kDChunk, d - d0);
-    // x chunk: 64 tokens x 64 dims
-    for (int c = tid; c < kTokPerBlock * (kDChunk / EPC); c += 256) {
-      const int r = c / (kDChunk / EPC);
-      const int cc = c % (kDChunk / EPC);
-      const int gt = t0 + r;
-      float v[EPC];
-      if (gt < n_tokens && cc * EPC < dn) {
-        const T* p = x + static_cast<size_t>(gt) * d + d0 + cc * EPC;
-        uint4 raw = *reinterpret_cast<const uint4*>(p);
-        const T* e = reinterpret_cast<const T*>(&raw);
-#pragma unroll
-        for (int j = 0; j < EPC; ++j) v[j] = to_f32(e[j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < EPC; ++j) v[j] = 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < EPC; ++j) xs[r * kXStride + cc * EPC + j] = v[j];
+      for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[j], wv[j], acc, 0, 0, 0);
     }
-    // router weight chunk: GE rows x 64 dims, widened to float64
-    for (int c = tid; c < GE * (kDChunk / EPC); c += 256) {
-      const int r = c / (kDChunk / EPC);
-      const int cc = c % (kDChunk / EPC);
-      double v[EPC];
-      if (cc * EPC < dn) {
-        const T* p = wr + static_cast<size_t>(r) * d + d0 + cc * EPC;
-        uint4 raw = *reinterpret_cast<const uint4*>(p);
-        const T* e = reinterpret_cast<const T*>(&raw);
+    // accumulator of the f64 16x16 MFMA: value i of lane l is C[4i + l/16][l % 16],
+    // i.e. token 4i + h, expert eb + row
 #pragma unroll
-        for (int j = 0; j < EPC; ++j) v[j] = static_cast<double>(to_f32(e[j]));
-      } else {
-#pragma unroll
-        for (int j = 0; j < EPC; ++j) v[j] = 0.0;
-      }
-#pragma unroll
-      for (int j = 0; j < EPC; ++j) ws[r * kDChunk + cc * EPC + j] = v[j];
-    }
+    for (int i = 0; i < 4; ++i) part[wave][4 * i + h][row] = acc[i];
     __syncthreads();
-    for (int i = 0; i < kDChunk; ++i) {
-      const double xv = static_cast<double>(xs[tok * kXStride + i]);
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        if (m < ept) {
-          const int e = part + 4 * m;
-          if (e < GE) acc[m] = fma(xv, ws[e * kDChunk + i], acc[m]);
-        }
+    {
+      const int tt = tid >> 4, ee = tid & 15;  // 256 threads = 16 tokens x 16 experts
+      if (eb + ee < GE) {
+        double s = part[0][tt][ee];
+        s += part[1][tt][ee];
+        s += part[2][tt][ee];
+        s += part[3][tt][ee];
+        logit[tt][eb + ee] = s + (bias ? static_cast<double>(bias[eb + ee]) : 0.0);
       }
     }
     __syncthreads();
   }
-
-  // logits (+ bias) to LDS, one row per token
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int e = part + 4 * m;
-    if (m < ept && e < GE) {
-      const double b = bias ? static_cast<double>(bias[e]) : 0.0;
-      rl[tok * (GE + 1) + e] = acc[m] + b;
-    }
-  }
-  __syncthreads();
 
   // selection: one thread per (token, group)
-  for (int task = tid; task < kTokPerBlock * G; task += 256) {
-    const int tt = task % kTokPerBlock;
-    const int g = task / kTokPerBlock;
+  for (int task = tid; task < kTok * G; task += 256) {
+    const int tt = task / G, g = task % G;
     const int gt = t0 + tt;
     if (gt >= n_tokens) continue;
-    const double* r = rl + tt * (GE + 1) + g * E;
-    uint32_t taken = 0u;
-    double rsel[32];
-    int isel[32];
-    for (int j = 0; j < k; ++j) {
-      int best = -1;
-      double bv = 0.0;
-      for (int e = 0; e < E; ++e) {
-        if (taken & (1u << e)) continue;
-        const double v = r[e];
-        if (best < 0 || v > bv) {  // strict: equal values keep the lower index
-          best = e;
-          bv = v;
-        }
-      }
-      taken |= 1u << best;
-      rsel[j] = bv;
-      isel[j] = best;
-    }
+    const double* r = &logit[tt][g * E];
+    double rmax = r[0];
+    for (int e = 1; e < E; ++e) rmax = fmax(rmax, r[e]);
+    // rank of e: experts with a larger logit, or an equal one and a lower index
     double z = 0.0;
-    for (int j = 0; j < k; ++j) z += exp(rsel[j] - rsel[0]);
+    for (int e = 0; e < E; ++e) {
+      int rank = 0;
+      for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
+      if (rank < k) z += exp(r[e] - rmax);
+    }
     const size_t o = (static_cast<size_t>(gt) * G + g) * k;
-    for (int j = 0; j < k; ++j) {
-      idx_out[o + j] = isel[j];
-      w_out[o + j] = static_cast<float>(exp(rsel[j] - rsel[0]) / z);
+    for (int e = 0; e < E; ++e) {
+      int rank = 0;
+      for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
+      if (rank < k) {
+        idx_out[o + rank] = e;
+        w_out[o + rank] = static_cast<float>(exp(r[e] - rmax) / z);
+      }
     }
   }
 }
 
 }  // namespace
 
-size_t router_smem_bytes(int G, int E) {
-  const int GE = G * E;
-  size_t a = static_cast<size_t>(GE) * kDChunk * 8;
-  size_t b = static_cast<size_t>(kTokPerBlock) * (GE + 1) * 8;
-  return kTokPerBlock * kXStride * 4 + 16 + (a > b ? a : b);
-}
-
 template <typename T>
 hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* idx, float* w,
                          int n_tokens, int d, int G, int E, int k, hipStream_t stream) {
-  const int blocks = (n_tokens + kTokPerBlock - 1) / kTokPerBlock;
+  const int blocks = (n_tokens + kTok - 1) / kTok;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_topk_kernel<T>, dim3(blocks), dim3(256), router_smem_bytes(G, E),
-                     stream, x, wr, bias, idx, w, n_tokens, d, G, E, k);
+  hipLaunchKernelGGL(router_topk_kernel<T>, dim3(blocks), dim3(256), 0, stream, x, wr, bias, idx,
+                     w, n_tokens, d, G, E, k);
   return hipGetLastError();
 }
 

@@ -248,7 +248,13 @@ def test_determinism(gqe):
     _, ws1, y1 = run_gqe(gqe, wl, I, dev)
     _, ws2, y2 = run_gqe(gqe, wl, I, dev)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-    assert torch.equal(ws1, ws2)
+    cfg = cfg_for(gqe, wl)
+    v1, v2 = gqe.workspace_views(cfg, ws1), gqe.workspace_views(cfg, ws2)
+    for key in ("idx", "w", "counts", "offsets", "pos", "slot", "q", "k", "s"):
+        assert torch.equal(v1[key].view(torch.uint8), v2[key].view(torch.uint8)), key
+    L = wl.seq_len
+    assert torch.equal(v1["vt"][..., :L].contiguous().view(torch.uint8),
+                       v2["vt"][..., :L].contiguous().view(torch.uint8))
 
 
 @pytest.mark.parametrize("L,B,G,E,k,D,dtype", [
