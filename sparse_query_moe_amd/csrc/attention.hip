@@ -37,6 +37,7 @@ namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
+
 template <typename T, int D, int QB = 1>
 struct AttnShape {
   static constexpr int BQ = 4 * 32 * QB, BKV = 64;  // 4 waves, QB 32-query blocks each
@@ -114,7 +115,7 @@ __device__ __forceinline__ float dot8(const f32x8& a, const f32x8& b) {
 }
 
 template <typename T, int D, int QB>
-__global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void attention_kernel(
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attention_kernel(
     AttnParams p) {
   typedef AttnShape<T, D, QB> S;
   typedef typename Frag<T>::type F;
@@ -221,18 +222,15 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
     // S^T - m: the accumulator starts at -m_run, so exp2 applies directly
     f32x16 s[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[qb][kb][i] = -m_run[qb];
-#pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < S::NKS; ++ks) {
         const F kf = LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mma32(s[qb][kb], kf, qf[qb][ks]);
+        for (int qb = 0; qb < QB; ++qb) {
+          if (ks == 0) s[qb][kb] = splat16(-m_run[qb]);  // S^T - m: exp2 applies directly
+          mma32(s[qb][kb], kf, qf[qb][ks]);
+        }
       }
     if constexpr (MASK) {  // drop keys after the query
 #pragma unroll
@@ -301,7 +299,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
 
   gload(0);
   sstore(0);
-  __syncthreads();
+  lds_barrier();
   for (int jt = 0; jt < ntiles; ++jt) {
     if (jt + 1 < ntiles) gload(jt + 1);
     const char* Ks = smem + (jt & 1) * S::STAGE;
@@ -314,7 +312,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
         tile(Ks, Vs, j0, std::true_type{});
     }
     if (jt + 1 < ntiles) sstore((jt + 1) & 1);
-    __syncthreads();
+    lds_barrier();
   }
 
 #pragma unroll

@@ -64,6 +64,27 @@ __device__ __forceinline__ void mma32(f32x16& acc, const f32x8& a, const f32x8& 
   for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
 }
 
+// A . B + C with a separate accumulator input (C is left unchanged).
+__device__ __forceinline__ f32x16 mma32c(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32c(const f32x8& a, const f32x8& b, const f32x16& c) {
+  f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
+#pragma unroll
+  for (int j = 1; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+  return acc;
+}
+
+// A 16-float accumulator with every element v, built with 64-bit moves.
+__device__ __forceinline__ f32x16 splat16(float v) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef double f64x8 __attribute__((ext_vector_type(8)));
+  const f32x2 pair = {v, v};
+  const double d = __builtin_bit_cast(double, pair);
+  const f64x8 dv = {d, d, d, d, d, d, d, d};
+  return __builtin_bit_cast(f32x16, dv);
+}
+
 // Output layout of a 32x32 MFMA accumulator: value i of lane l is
 // C[row_of(i, l)][l % 32].
 __device__ __forceinline__ int acc_row(int i, int lane) {
@@ -96,13 +117,17 @@ template <> struct FragFromAcc<float> {
   }
 };
 
-// LDS tiles are stored as rows of 16-byte chunks; the chunk index is XORed
-// with the low three bits of the row so that the 32 rows an MFMA fragment
-// read touches spread over all banks.
+// LDS tiles are stored as rows of 16-byte chunks.  gfx950's LDS serves 256
+// bytes (64 banks x 4 B) per cycle, i.e. sixteen 16-byte units.  An MFMA
+// fragment read has consecutive lanes read the same logical chunk of
+// consecutive rows, so the chunk index is XORed with the row's index in units
+// of 256 bytes: any 16 consecutive rows then hit 16 different units.
 template <int ROWB>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  constexpr int mask = (ROWB / 16 - 1) < 7 ? (ROWB / 16 - 1) : 7;
-  return row * ROWB + ((chunk ^ (row & mask)) << 4);
+  constexpr int CPR = ROWB / 16;                       // chunks per row
+  constexpr int RP = ROWB >= 256 ? 1 : 256 / ROWB;     // rows per 256 bytes
+  constexpr int mask = CPR < 16 ? CPR - 1 : 15;
+  return row * ROWB + ((chunk ^ ((row / RP) & mask)) << 4);
 }
 
 // 8 K-elements of row `row`, starting at element `elem`, from a swizzled LDS
@@ -128,5 +153,15 @@ template <int ROWB> struct LdsFrag<float, ROWB> {
 };
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// Block barrier that orders LDS accesses only.  __syncthreads() is a full
+// workgroup fence and also waits for every global load still in flight,
+// which would expose the latency of the next tile's prefetch at each
+// barrier; the prefetch only targets registers, so the LDS fence suffices.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace gqe

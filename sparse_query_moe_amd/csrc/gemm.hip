@@ -95,7 +95,7 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
 
   gload(0);
   sstore(0);
-  __syncthreads();
+  lds_barrier();
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) gload(kt + 1);
     const char* sa = smem + (kt & 1) * S::STAGE;
@@ -116,7 +116,7 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
         for (int b = 0; b < S::TN; ++b) mma32(acc[a][b], af[a], bf[b]);
     }
     if (kt + 1 < nk) sstore((kt + 1) & 1);
-    __syncthreads();
+    lds_barrier();
   }
 
 #pragma unroll

@@ -68,7 +68,8 @@ def check_routing(gqe, cfg, ws, ref):
 # stage parity (tiny fp32 layer, the 2k bf16 layer, and a ragged shape)
 # ---------------------------------------------------------------------------
 
-STAGE_CASES = [("tiny_fp32", 0, 0), ("l2k", 0, 0), ("l2k", 333, 2)]
+# the last case is long enough (B*L*heads) for the ping-pong attention schedule
+STAGE_CASES = [("tiny_fp32", 0, 0), ("l2k", 0, 0), ("l2k", 333, 2), ("l2k", 8269, 4)]
 
 
 @pytest.mark.parametrize("name,L,B", STAGE_CASES)
