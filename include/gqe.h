@@ -59,10 +59,14 @@ typedef enum {
 
 typedef enum { GQE_DTYPE_BF16 = 0, GQE_DTYPE_FP32 = 1 } gqe_dtype;
 
-/* Layer shape.  Limits: batch, seq_len >= 0; d_model a multiple of 8;
- * 1 <= n_groups; 1 <= n_experts <= 32; 1 <= top_k <= n_experts;
- * n_groups*n_experts <= 64; head_dim in {32, 64, 128};
- * 0 <= shared_kv_group < n_groups; batch*seq_len*n_groups*top_k < 2^31. */
+/* Layer shape.  Limits (GQE_ERR_INVALID_ARG when broken): batch, seq_len >= 0;
+ * d_model a positive multiple of 8; 1 <= n_groups; 1 <= n_experts <= 32;
+ * 1 <= top_k <= n_experts; n_groups*n_experts <= 64;
+ * 0 <= shared_kv_group < n_groups; batch*seq_len*n_groups*n_experts < 2^31.
+ * Built subset (GQE_ERR_UNSUPPORTED otherwise): head_dim in {32, 64, 128};
+ * the projections stream their reduction dimension in 128-byte steps, so
+ * d_model, (top_k*n_groups+2)*head_dim and n_groups*n_experts*head_dim must
+ * be multiples of 64 elements for bf16 and of 32 for fp32. */
 typedef struct gqe_config {
   int32_t batch;            /* B                                               */
   int32_t seq_len;          /* L: prefill length, causal, no padding          */

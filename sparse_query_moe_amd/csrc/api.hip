@@ -37,11 +37,21 @@ bool head_dim_ok(const gqe_config* c) {
   return c->head_dim == 32 || c->head_dim == 64 || c->head_dim == 128;
 }
 
+// The projections stream K in steps of 128 bytes (64 bf16 or 32 fp32
+// elements): d_model, the slot width (k*G+2)*d_h and the dense head width
+// G*E*d_h must be multiples of it.
+bool k_steps_ok(const gqe_config* c) {
+  const int step = c->dtype == GQE_DTYPE_BF16 ? 64 : 32;
+  const int D = c->head_dim;
+  return c->d_model % step == 0 && ((c->top_k * c->n_groups + 2) * D) % step == 0 &&
+         (c->n_groups * c->n_experts * D) % step == 0;
+}
+
 int check_cfg(const gqe_config* c) {
   if (c == nullptr) return GQE_ERR_INVALID_ARG;
   if (c->head_dim < 1) return GQE_ERR_INVALID_ARG;
   if (!shape_ok(c)) return GQE_ERR_INVALID_ARG;
-  if (!head_dim_ok(c)) return GQE_ERR_UNSUPPORTED;
+  if (!head_dim_ok(c) || !k_steps_ok(c)) return GQE_ERR_UNSUPPORTED;
   return GQE_OK;
 }
 
@@ -75,7 +85,7 @@ Layout make_layout(const gqe_config* c, bool dense) {
     l.pub.slot = take(rows * 4);
     l.pub.scratch = off;
     l.chunk_counts = take(B * static_cast<size_t>(dispatch_chunks(static_cast<int>(L))) * G * E * 4);
-    l.tile_off = take((lists + 1) * 4);
+    l.tile_off = take(B * G * (E + 1) * 4);
     l.pub.q = take(B * (G * k + 1) * L * D * es);
     l.pub.s = 0;
   } else {
@@ -113,10 +123,11 @@ int check_common(const gqe_config* c, void* ws, size_t ws_bytes, bool dense) {
 
 bool empty(const gqe_config* c) { return static_cast<long long>(c->batch) * c->seq_len == 0; }
 
-int max_gather_tiles(const gqe_config* c) {
-  const long long rows = static_cast<long long>(c->batch) * c->seq_len * c->n_groups * c->top_k;
-  return static_cast<int>((rows + kGatherRows - 1) / kGatherRows) +
-         c->batch * c->n_groups * c->n_experts;
+// Upper bound of the gathered-projection tiles of one (b, g): its lists hold
+// L*k rows in E lists.
+int gather_tiles_per_bg(const gqe_config* c) {
+  const long long rows = static_cast<long long>(c->seq_len) * c->top_k;
+  return static_cast<int>((rows + kGatherRows - 1) / kGatherRows) + c->n_experts;
 }
 
 template <typename T>
@@ -155,7 +166,7 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   e = launch_gather_q<T>(static_cast<const T*>(x), static_cast<const T*>(wq), at<T>(ws, l.pub.q),
                          at<int32_t>(ws, l.pub.counts), at<int32_t>(ws, l.pub.offsets),
                          at<int32_t>(ws, l.pub.pos), at<int32_t>(ws, l.pub.slot),
-                         at<int32_t>(ws, l.tile_off), B, L, d, G, E, k, D, max_gather_tiles(c),
+                         at<int32_t>(ws, l.tile_off), B, L, d, G, E, k, D, gather_tiles_per_bg(c),
                          stream);
   return hip_status(e);
 }

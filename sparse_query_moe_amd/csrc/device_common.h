@@ -154,6 +154,9 @@ template <int ROWB> struct LdsFrag<float, ROWB> {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// an LDS address as the direct-load builtins want it
+#define GQE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 // Block barrier that orders LDS accesses only.  __syncthreads() is a full
 // workgroup fence and also waits for every global load still in flight,
 // which would expose the latency of the next tile's prefetch at each

@@ -29,60 +29,106 @@ namespace gqe {
 
 namespace {
 
-template <typename T, int BM_, int BN_, int WGM_, int WGN_>
+template <typename T, int BM_, int BN_, int WGM_, int WGN_, int NST_ = 3>
 struct GemmShape {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, NST = NST_;
   static constexpr int EPC = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
   static constexpr int BKE = 8 * EPC;                            // K elements per LDS row
-  static constexpr int A_CH = BM / 32;                           // A chunks per thread
+  static constexpr int A_CH = BM / 32;                           // A chunks per thread per stage
   static constexpr int B_CH = BN / 32;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int STAGE = (BM + BN) * 128;
-  static constexpr int LDS = 2 * STAGE;
+  // the finished tile is staged in LDS as T, rows padded by 16 bytes for bf16
+  static constexpr int LDC = BN + (sizeof(T) == 2 ? 8 : 0);
+  static constexpr int CBYTES = BM * LDC * static_cast<int>(sizeof(T));
+  static constexpr int LDS = NST * STAGE > CBYTES ? NST * STAGE : CBYTES;
   static_assert(WGM * WGN == 4, "4 waves");
   static_assert(TM >= 1 && TN >= 1, "wave tile at least 32x32");
+  static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
 };
 
-// The main loop: P supplies K, a_row(r), b_row(n) (row pointers or nullptr
-// for rows outside the problem, read as zeros) and store(r, n, value).
+// wait until at most n of this wave's vector-memory operations are in flight
+// (and all its LDS operations are done); n is small and known per call site
+__device__ __forceinline__ void wait_vm(int n) {
+#define GQE_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4))
+  switch (n) {
+    case 0: GQE_VM(0); break;
+    case 1: GQE_VM(1); break;
+    case 2: GQE_VM(2); break;
+    case 3: GQE_VM(3); break;
+    case 4: GQE_VM(4); break;
+    case 5: GQE_VM(5); break;
+    case 6: GQE_VM(6); break;
+    case 7: GQE_VM(7); break;
+    case 8: GQE_VM(8); break;
+    case 9: GQE_VM(9); break;
+    case 10: GQE_VM(10); break;
+    case 11: GQE_VM(11); break;
+    case 12: GQE_VM(12); break;
+    case 13: GQE_VM(13); break;
+    case 14: GQE_VM(14); break;
+    case 15: GQE_VM(15); break;
+    case 16: GQE_VM(16); break;
+    case 17: GQE_VM(17); break;
+    case 18: GQE_VM(18); break;
+    case 19: GQE_VM(19); break;
+    case 20: GQE_VM(20); break;
+    case 21: GQE_VM(21); break;
+    case 22: GQE_VM(22); break;
+    case 23: GQE_VM(23); break;
+    case 24: GQE_VM(24); break;
+    default: GQE_VM(0); break;
+  }
+#undef GQE_VM
+}
+
+// The main loop: P supplies K (a multiple of S::BKE), a_row(r) and b_row(n)
+// (row pointers, or nullptr for rows outside the problem), a_any() (any valid
+// row, loaded in place of missing ones: their results are never written) and
+// write_tile(staged tile).
+//
+// K streams through an NST-stage ring of LDS tiles filled by direct
+// global-to-LDS loads (global_load_lds_dwordx4): NST-1 stages are in flight
+// while one is consumed, without any VGPR staging.  Each wave fills whole
+// 1 KB runs of LDS (64 lanes x 16 B); a lane picks the source chunk so that
+// the data lands in the swizzled position the fragment reads expect.  One
+// barrier per K step, preceded by a wait for this wave's loads of that step
+// only (no fence: a fence would also drain the later stages).
 template <typename T, class S, class P>
 __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
   typedef typename Frag<T>::type F;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
-  const int ch = tid & 7;
   const int r0 = tid >> 3;
+  const int pc = tid & 7;  // physical 16-byte chunk this lane fills in its row
 
   const T* ap[S::A_CH];
   const T* bp[S::B_CH];
 #pragma unroll
-  for (int i = 0; i < S::A_CH; ++i) ap[i] = prob.a_row(r0 + 32 * i);
+  for (int i = 0; i < S::A_CH; ++i) {
+    const int r = r0 + 32 * i;
+    const T* p = prob.a_row(r);
+    ap[i] = (p != nullptr ? p : prob.a_any()) + ((pc ^ ((r >> 1) & 7)) * S::EPC);
+  }
 #pragma unroll
-  for (int i = 0; i < S::B_CH; ++i) bp[i] = prob.b_row(r0 + 32 * i);
+  for (int i = 0; i < S::B_CH; ++i) {
+    const int r = r0 + 32 * i;
+    const T* p = prob.b_row(r);
+    bp[i] = (p != nullptr ? p : prob.b_any()) + ((pc ^ ((r >> 1) & 7)) * S::EPC);
+  }
 
-  uint4 ra[S::A_CH], rb[S::B_CH];
-  const int K = prob.K;
-  const int nk = (K + S::BKE - 1) / S::BKE;
-
-  auto gload = [&](int kt) {
-    const int ke = kt * S::BKE + ch * S::EPC;
+  const int nk = prob.K / S::BKE;
+  constexpr int per_stage = S::A_CH + S::B_CH;
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % S::NST) * S::STAGE;
 #pragma unroll
     for (int i = 0; i < S::A_CH; ++i)
-      ra[i] = (ap[i] != nullptr && ke < K) ? *reinterpret_cast<const uint4*>(ap[i] + ke) : zero4();
+      __builtin_amdgcn_global_load_lds(ap[i] + kt * S::BKE, GQE_LDS(st + (4 * i + wave) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < S::B_CH; ++i)
-      rb[i] = (bp[i] != nullptr && ke < K) ? *reinterpret_cast<const uint4*>(bp[i] + ke) : zero4();
-  };
-  auto sstore = [&](int buf) {
-    char* sa = smem + buf * S::STAGE;
-    char* sb = sa + S::BM * 128;
-#pragma unroll
-    for (int i = 0; i < S::A_CH; ++i)
-      *reinterpret_cast<uint4*>(sa + swz<128>(r0 + 32 * i, ch)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < S::B_CH; ++i)
-      *reinterpret_cast<uint4*>(sb + swz<128>(r0 + 32 * i, ch)) = rb[i];
+      __builtin_amdgcn_global_load_lds(bp[i] + kt * S::BKE,
+                                       GQE_LDS(st + S::BM * 128 + (4 * i + wave) * 1024), 16, 0, 0);
   };
 
   f32x16 acc[S::TM][S::TN];
@@ -93,12 +139,16 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  gload(0);
-  sstore(0);
-  lds_barrier();
+#pragma unroll
+  for (int st = 0; st < S::NST - 1; ++st)
+    if (st < nk) issue(st);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
-    const char* sa = smem + (kt & 1) * S::STAGE;
+    const int later = min(S::NST - 2, nk - 1 - kt);  // stages issued after kt
+    wait_vm(later * per_stage);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + S::NST - 1 < nk) issue(kt + S::NST - 1);
+    const char* sa = smem + (kt % S::NST) * S::STAGE;
     const char* sb = sa + S::BM * 128;
 #pragma unroll
     for (int ks = 0; ks < S::BKE / 16; ++ks) {
@@ -115,18 +165,30 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
 #pragma unroll
         for (int b = 0; b < S::TN; ++b) mma32(acc[a][b], af[a], bf[b]);
     }
-    if (kt + 1 < nk) sstore((kt + 1) & 1);
-    lds_barrier();
   }
+  lds_barrier();  // every wave is done reading the ring before it holds the tile
 
+  // epilogue: stage the tile, then the problem writes it out in 8-element chunks
+  T* ct = reinterpret_cast<T*>(smem);
 #pragma unroll
   for (int a = 0; a < S::TM; ++a)
 #pragma unroll
     for (int b = 0; b < S::TN; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        prob.store(wm * S::WM + 32 * a + acc_row(i, lane), wn * S::WN + 32 * b + (lane & 31),
-                   acc[a][b][i]);
+        ct[(wm * S::WM + 32 * a + acc_row(i, lane)) * S::LDC + wn * S::WN + 32 * b + (lane & 31)] =
+            from_f32<T>(acc[a][b][i]);
+  lds_barrier();
+  prob.write_tile(ct);
+}
+
+// copy 8 contiguous elements (16 B of bf16, 32 B of fp32)
+template <typename T>
+__device__ __forceinline__ void copy8(T* dst, const T* src) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  d4[0] = s4[0];
+  if constexpr (sizeof(T) == 4) d4[1] = s4[1];
 }
 
 // ---------------------------------------------------------------------------
@@ -160,6 +222,8 @@ struct DenseProb {
     r.transposed = s2 ? a.seg[2].transposed : s1 ? a.seg[1].transposed : a.seg[0].transposed;
     return r;
   }
+  __device__ __forceinline__ const T* a_any() const { return static_cast<const T*>(a.x); }
+  __device__ __forceinline__ const T* b_any() const { return static_cast<const T*>(a.seg[0].w); }
   __device__ __forceinline__ const T* a_row(int r) const {
     const int m = m0 + r;
     return m < a.M ? static_cast<const T*>(a.x) + static_cast<size_t>(m) * a.K : nullptr;
@@ -170,21 +234,45 @@ struct DenseProb {
     const ProjSeg sg = seg_of(col);
     return static_cast<const T*>(sg.w) + static_cast<size_t>(col - sg.n_begin) * a.K;
   }
-  __device__ __forceinline__ void store(int r, int n, float v) const {
-    const int m = m0 + r, col = n0 + n;
-    if (m >= a.M || col >= a.N) return;
-    const ProjSeg sg = seg_of(col);
-    const int c = col - sg.n_begin;
-    const int hh = sg.head_base + c / a.D, dd = c % a.D;
-    const int b = m / a.L, t = m % a.L;
-    T* out = static_cast<T*>(sg.out);
-    size_t o;
-    if (sg.transposed)
-      o = (static_cast<size_t>(b) * sg.heads + hh) * a.D * static_cast<size_t>(a.ld_t) +
-          static_cast<size_t>(dd) * a.ld_t + t;
-    else
-      o = ((static_cast<size_t>(b) * sg.heads + hh) * a.L + t) * a.D + dd;
-    out[o] = from_f32<T>(v);
+  // head-split outputs: 8 consecutive head dims per chunk; the transposed
+  // (V) segment takes 8 consecutive tokens per chunk instead
+  __device__ __forceinline__ void write_tile(const T* ct) const {
+    constexpr int CW = S::BN / 8;
+    for (int c = threadIdx.x; c < S::BM * CW; c += 256) {
+      const int r = c / CW, c8 = c % CW;
+      const int m = m0 + r, col = n0 + 8 * c8;
+      if (m >= a.M || col >= a.N) continue;
+      const ProjSeg sg = seg_of(col);
+      if (sg.transposed) continue;
+      const int cl = col - sg.n_begin;
+      const int hh = sg.head_base + cl / a.D, dd = cl % a.D;
+      const int b = m / a.L, t = m % a.L;
+      T* dst = static_cast<T*>(sg.out) + ((static_cast<size_t>(b) * sg.heads + hh) * a.L + t) * a.D + dd;
+      copy8(dst, ct + r * S::LDC + 8 * c8);
+    }
+    for (int c = threadIdx.x; c < (S::BM / 8) * S::BN; c += 256) {
+      const int nl = c % S::BN, r8 = c / S::BN;
+      const int col = n0 + nl, m = m0 + 8 * r8;
+      if (m >= a.M || col >= a.N) continue;
+      const ProjSeg sg = seg_of(col);
+      if (!sg.transposed) continue;
+      const int cl = col - sg.n_begin;
+      const int hh = sg.head_base + cl / a.D, dd = cl % a.D;
+      const int b = m / a.L, t = m % a.L;
+      T* out = static_cast<T*>(sg.out);
+      if (t + 8 <= a.L && m + 8 <= a.M && (a.L & 7) == 0) {
+        alignas(16) T v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = ct[(8 * r8 + j) * S::LDC + nl];
+        copy8(out + ((static_cast<size_t>(b) * sg.heads + hh) * a.D + dd) * static_cast<size_t>(a.ld_t) + t, v);
+      } else {
+        for (int j = 0; j < 8 && m + j < a.M; ++j) {
+          const int bj = (m + j) / a.L, tj = (m + j) % a.L;
+          out[((static_cast<size_t>(bj) * sg.heads + hh) * a.D + dd) * static_cast<size_t>(a.ld_t) + tj] =
+              ct[(8 * r8 + j) * S::LDC + nl];
+        }
+      }
+    }
   }
 };
 
@@ -214,9 +302,9 @@ template <typename T, class S>
 struct GatherProb {
   const GatherArgs& a;
   int K, m0, cnt, base, b, g, e;
-  __device__ GatherProb(const GatherArgs& args, int tile, int li)
+  __device__ GatherProb(const GatherArgs& args, int tile_in_list, int li)
       : a(args), K(args.d) {
-    m0 = (tile - args.tile_off[li]) * S::BM;
+    m0 = tile_in_list * S::BM;
     cnt = args.counts[li];
     base = args.offsets[li];
     const int GE = args.G * args.E;
@@ -224,6 +312,8 @@ struct GatherProb {
     g = (li / args.E) % args.G;
     e = li % args.E;
   }
+  __device__ __forceinline__ const T* a_any() const { return static_cast<const T*>(a.x); }
+  __device__ __forceinline__ const T* b_any() const { return static_cast<const T*>(a.wq); }
   __device__ __forceinline__ const T* a_row(int r) const {
     if (m0 + r >= cnt) return nullptr;
     const int t = a.pos[base + m0 + r];
@@ -234,26 +324,30 @@ struct GatherProb {
     return static_cast<const T*>(a.wq) +
            (static_cast<size_t>(g * a.E + e) * a.D + n) * static_cast<size_t>(a.d);
   }
-  __device__ __forceinline__ void store(int r, int n, float v) const {
-    if (m0 + r >= cnt || n >= a.D) return;
-    const int entry = base + m0 + r;
-    const int t = a.pos[entry], j = a.slot[entry];
-    T* q = static_cast<T*>(a.q);
-    q[((static_cast<size_t>(b) * a.H + g * a.k + j) * a.L + t) * a.D + n] = from_f32<T>(v);
+  // each routed row lands at (slot-head g*k + slot, position pos): 8 dims per chunk
+  __device__ __forceinline__ void write_tile(const T* ct) const {
+    constexpr int CW = S::BN / 8;
+    for (int c = threadIdx.x; c < S::BM * CW; c += 256) {
+      const int r = c / CW, c8 = c % CW;
+      if (m0 + r >= cnt || 8 * c8 >= a.D) continue;
+      const int entry = base + m0 + r;
+      const int t = a.pos[entry], j = a.slot[entry];
+      T* dst = static_cast<T*>(a.q) + ((static_cast<size_t>(b) * a.H + g * a.k + j) * a.L + t) * a.D + 8 * c8;
+      copy8(dst, ct + r * S::LDC + 8 * c8);
+    }
   }
 };
 
 template <typename T, class S>
 __global__ __launch_bounds__(256) void gather_q_kernel(GatherArgs args) {
   extern __shared__ __align__(16) char smem[];
+  const int bg = blockIdx.y;
   const int tile = blockIdx.x;
-  if (tile >= args.tile_off[args.n_lists]) return;  // whole block leaves together
-  int lo = 0, hi = args.n_lists;                     // last li with tile_off[li] <= tile
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (args.tile_off[mid] <= tile) lo = mid; else hi = mid;
-  }
-  GatherProb<T, S> prob(args, tile, lo);
+  const int* toff = args.tile_off + bg * (args.E + 1);   // tile map of this (b, g)
+  if (tile >= toff[args.E]) return;                      // whole block leaves together
+  int e = 0;                                             // last e with toff[e] <= tile
+  while (e + 1 < args.E && toff[e + 1] <= tile) ++e;
+  GatherProb<T, S> prob(args, tile - toff[e], bg * args.E + e);
   gemm_block<T, S>(prob, smem);
 }
 
@@ -272,6 +366,8 @@ struct OutProb {
   const OutArgs& a;
   int m0, n0, K;
   __device__ OutProb(const OutArgs& args, int m0_, int n0_) : a(args), m0(m0_), n0(n0_), K(args.K) {}
+  __device__ __forceinline__ const T* a_any() const { return static_cast<const T*>(a.a); }
+  __device__ __forceinline__ const T* b_any() const { return static_cast<const T*>(a.w); }
   __device__ __forceinline__ const T* a_row(int r) const {
     const int m = m0 + r;
     return m < a.M ? static_cast<const T*>(a.a) + static_cast<size_t>(m) * a.K : nullptr;
@@ -280,10 +376,14 @@ struct OutProb {
     const int c = n0 + n;
     return c < a.N ? static_cast<const T*>(a.w) + static_cast<size_t>(c) * a.K : nullptr;
   }
-  __device__ __forceinline__ void store(int r, int n, float v) const {
-    const int m = m0 + r, c = n0 + n;
-    if (m < a.M && c < a.N)
-      static_cast<T*>(a.out)[static_cast<size_t>(m) * a.N + c] = from_f32<T>(v);
+  __device__ __forceinline__ void write_tile(const T* ct) const {
+    constexpr int CW = S::BN / 8;
+    for (int c = threadIdx.x; c < S::BM * CW; c += 256) {
+      const int r = c / CW, c8 = c % CW;
+      const int m = m0 + r, n = n0 + 8 * c8;
+      if (m >= a.M || n >= a.N) continue;
+      copy8(static_cast<T*>(a.out) + static_cast<size_t>(m) * a.N + n, ct + r * S::LDC + 8 * c8);
+    }
   }
 };
 
@@ -332,6 +432,18 @@ __global__ __launch_bounds__(256) void weighted_slot_kernel(T* __restrict__ s,
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// launch with S::LDS bytes of dynamic LDS (above 64 KB the kernel must opt in once)
+template <class S, class Kern, class Args>
+static hipError_t launch_gemm(Kern kern, dim3 grid, hipStream_t stream, const Args& a) {
+  if (S::LDS > 65536) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(256), S::LDS, stream, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t ld_t,
                              const ProjSeg* segs, int nseg, hipStream_t stream) {
@@ -352,22 +464,21 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t ld_
   a.N = N;
   if (M == 0 || N == 0) return hipSuccess;
   const dim3 grid((N + S::BN - 1) / S::BN, (M + S::BM - 1) / S::BM);
-  hipLaunchKernelGGL((dense_proj_kernel<T, S>), grid, dim3(256), S::LDS, stream, a);
-  return hipGetLastError();
+  return launch_gemm<S>(dense_proj_kernel<T, S>, grid, stream, a);
 }
 
 template <typename T, int D>
-static hipError_t launch_gather_q_d(const GatherArgs& a, int max_tiles, hipStream_t stream) {
+static hipError_t launch_gather_q_d(const GatherArgs& a, int tiles_per_bg, int n_bg,
+                                    hipStream_t stream) {
   typedef GemmShape<T, kGatherRows, D, (D >= 128 ? 2 : 4), (D >= 128 ? 2 : 1)> S;
-  hipLaunchKernelGGL((gather_q_kernel<T, S>), dim3(max_tiles), dim3(256), S::LDS, stream, a);
-  return hipGetLastError();
+  return launch_gemm<S>(gather_q_kernel<T, S>, dim3(tiles_per_bg, n_bg), stream, a);
 }
 
 template <typename T>
 hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
                            const int32_t* offsets, const int32_t* pos, const int32_t* slot,
                            const int32_t* tile_off, int B, int L, int d, int G, int E, int k,
-                           int D, int max_tiles, hipStream_t stream) {
+                           int D, int tiles_per_bg, hipStream_t stream) {
   GatherArgs a;
   a.x = x;
   a.wq = wq;
@@ -385,11 +496,11 @@ hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
   a.k = k;
   a.D = D;
   a.H = G * k + 1;
-  if (max_tiles == 0) return hipSuccess;
+  if (tiles_per_bg == 0 || B * G == 0) return hipSuccess;
   switch (D) {
-    case 32: return launch_gather_q_d<T, 32>(a, max_tiles, stream);
-    case 64: return launch_gather_q_d<T, 64>(a, max_tiles, stream);
-    case 128: return launch_gather_q_d<T, 128>(a, max_tiles, stream);
+    case 32: return launch_gather_q_d<T, 32>(a, tiles_per_bg, B * G, stream);
+    case 64: return launch_gather_q_d<T, 64>(a, tiles_per_bg, B * G, stream);
+    case 128: return launch_gather_q_d<T, 128>(a, tiles_per_bg, B * G, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -407,8 +518,7 @@ hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K
   a.K = K;
   if (M == 0 || N == 0) return hipSuccess;
   const dim3 grid((N + S::BN - 1) / S::BN, (M + S::BM - 1) / S::BM);
-  hipLaunchKernelGGL((out_proj_kernel<T, S>), grid, dim3(256), S::LDS, stream, a);
-  return hipGetLastError();
+  return launch_gemm<S>(out_proj_kernel<T, S>, grid, stream, a);
 }
 
 template <typename T>

@@ -40,11 +40,13 @@ template <typename T>
 hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t ld_t,
                              const ProjSeg* segs, int nseg, hipStream_t stream);
 
+// Grid: (tiles_per_bg, B*G); tile_off is the per-(b, g) tile map written by
+// the dispatch, tiles_per_bg an upper bound of its totals.
 template <typename T>
 hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
                            const int32_t* offsets, const int32_t* pos, const int32_t* slot,
                            const int32_t* tile_off, int B, int L, int d, int G, int E, int k,
-                           int D, int max_tiles, hipStream_t stream);
+                           int D, int tiles_per_bg, hipStream_t stream);
 
 // ---- K4 attention ------------------------------------------------------------
 struct AttnParams {

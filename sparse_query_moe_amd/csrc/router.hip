@@ -33,28 +33,23 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTok = 16;
 
+// 8 elements of T as raw 16-byte words: one for bf16, two for fp32
+template <typename T> struct U4Count { static constexpr int n = sizeof(T) == 2 ? 1 : 2; };
+
+// widen 8 stored elements to float64 (exact)
 template <typename T>
-__device__ __forceinline__ void load8_f64(const T* p, bool ok, double (&v)[8]) {
-  if (!ok) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = 0.0;
-    return;
-  }
+__device__ __forceinline__ void widen8(const uint4 (&r)[U4Count<T>::n], double (&v)[8]) {
   if constexpr (sizeof(T) == 2) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[2 * j] = static_cast<double>(__uint_as_float(w[j] << 16));
       v[2 * j + 1] = static_cast<double>(__uint_as_float(w[j] & 0xffff0000u));
     }
   } else {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
-    const uint4 b = *reinterpret_cast<const uint4*>(p + 4);
-    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
-    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
-    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = static_cast<double>(__uint_as_float(w[j]));
   }
 }
 
@@ -71,20 +66,37 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   const int tok = t0 + row;
   const int GE = G * E;
   const int nsteps = (d + 31) >> 5;
+  constexpr int kU4 = U4Count<T>::n;
+  constexpr int kBatch = sizeof(T) == 2 ? 8 : 4;  // steps whose loads are issued together
 
   for (int eb = 0; eb < GE; eb += 16) {
     const int e = eb + row;
     const T* xp = x + static_cast<size_t>(tok < n_tokens ? tok : 0) * d;
     const T* wp = wr + static_cast<size_t>(e < GE ? e : 0) * d;
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 2
-    for (int st = wave; st < nsteps; st += 4) {
-      const int d0 = st * 32 + 8 * h;
-      double xv[8], wv[8];
-      load8_f64(xp + d0, tok < n_tokens && d0 < d, xv);
-      load8_f64(wp + d0, e < GE && d0 < d, wv);
+    // batches of 8 steps: every load of a batch is issued before its MFMAs,
+    // so the wave waits for memory once per batch instead of once per step
+    for (int st0 = wave; st0 < nsteps; st0 += 4 * kBatch) {
+      uint4 rx[kBatch][kU4], rw[kBatch][kU4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[j], wv[j], acc, 0, 0, 0);
+      for (int u = 0; u < kBatch; ++u) {
+        const int d0 = (st0 + 4 * u) * 32 + 8 * h;
+        const bool okx = st0 + 4 * u < nsteps && tok < n_tokens && d0 < d;
+        const bool okw = st0 + 4 * u < nsteps && e < GE && d0 < d;
+#pragma unroll
+        for (int q = 0; q < kU4; ++q) {
+          rx[u][q] = okx ? reinterpret_cast<const uint4*>(xp + d0)[q] : make_uint4(0, 0, 0, 0);
+          rw[u][q] = okw ? reinterpret_cast<const uint4*>(wp + d0)[q] : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        double xv[8], wv[8];
+        widen8<T>(rx[u], xv);
+        widen8<T>(rw[u], wv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[j], wv[j], acc, 0, 0, 0);
+      }
     }
     // accumulator of the f64 16x16 MFMA: value i of lane l is C[4i + l/16][l % 16],
     // i.e. token 4i + h, expert eb + row

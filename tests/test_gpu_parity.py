@@ -92,10 +92,12 @@ def test_stage_route_and_dispatch(gqe, name, L, B):
 
 
 @pytest.mark.parametrize("pattern", ["uniform_ties", "one_expert_empty", "all_same", "random"])
-def test_stage_dispatch_patterns(gqe, pattern):
+@pytest.mark.parametrize("B,L", [(3, 1000), (2, 40000)])
+def test_stage_dispatch_patterns(gqe, pattern, B, L):
     """Dispatch alone on seeded idx patterns: ties everywhere, an empty expert,
-    every token picking the same pair, and random selections; B=3, L=1000."""
-    B, L, G, E, k = 3, 1000, 4, 4, 2
+    every token picking the same pair, and random selections; a short batch
+    (one block per (b, g)) and a long one (chunked count / scan / scatter)."""
+    G, E, k = 4, 4, 2
     rng = np.random.default_rng(5)
     if pattern == "uniform_ties":
         idx = np.broadcast_to(np.arange(k), (B, L, G, k)).copy()
@@ -106,7 +108,7 @@ def test_stage_dispatch_patterns(gqe, pattern):
     else:
         idx = np.stack([rng.permutation(E)[:k] for _ in range(B * L * G)]).reshape(B, L, G, k)
     idx = idx.astype(np.int32)
-    log(f"[dispatch] pattern={pattern}")
+    log(f"[dispatch] pattern={pattern} B={B} L={L}")
     cfg = gqe.make_config(B, L, 64, G, E, k, 64)
     ws = gqe.alloc_workspace(cfg)
     v = gqe.workspace_views(cfg, ws)
