@@ -5,10 +5,13 @@
 
 One step = one gqe_forward (router, dispatch, projections, attention, output)
 over one batch of synthetic input already resident in HBM.  The timed region
-is exactly K steps between two device synchronizations; per-stage times come
-from HIP events recorded between the stage calls on the same stream.  The
-dense-GQA baseline (all G*E query heads) is timed the same way, giving the
-GQE-over-GQA prefill speed-up.  Rank 0 prints one JSON line.
+is exactly K back-to-back gqe_forward calls between two device
+synchronizations, bracketed by HIP events on the stream.  Separate passes
+give the per-stage breakdown (events between the stage calls), the average
+duration of the attention kernel over back-to-back launches (the roofline
+figure), and the same step replayed from a HIP graph.  The dense-GQA baseline
+(all G*E query heads) is timed the same way, giving the GQE-over-GQA prefill
+speed-up.  Rank 0 prints one JSON line.
 """
 from __future__ import annotations
 
@@ -102,30 +105,81 @@ class Runner:
             ("output", lambda: g.gqa_output(c, d["wo_dense"], self.out_dense, ws)),
         ]
 
-    def time(self, stages, steps, warmup):
-        """Warm up, then time `steps` full passes; returns (ms per step, {stage: avg ms})."""
+    def gqe_step(self):
+        g, d = self.gqe, self.dev
+        g.gqe_forward(self.cfg, d["x"], d["wq"], d["wk"], d["wv"], d["wr"], d["wo"], self.out,
+                      self.ws)
+
+    def gqa_step(self):
+        g, d = self.gqe, self.dev
+        g.gqa_forward(self.cfg, d["x"], d["wq_dense"], d["wk"], d["wv"], d["wo_dense"],
+                      self.out_dense, self.ws_dense)
+
+    def time_steps(self, step, steps, warmup):
+        """Warm up, then time exactly `steps` back-to-back calls between two
+        synchronizations; returns ms per call (HIP events on the stream)."""
         torch = self.torch
         for _ in range(warmup):
-            for _, fn in stages:
-                fn()
-        torch.cuda.synchronize()
-        n = len(stages)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+            step()
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         start.record()
+        for _ in range(steps):
+            step()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    def time_stages(self, stages, steps):
+        """Per-stage breakdown (a separate pass): events between the stage calls."""
+        torch = self.torch
+        for _, fn in stages:
+            fn()
+        torch.cuda.synchronize()
+        n = len(stages)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
         for s in range(steps):
             ev[s][0].record()
             for i, (_, fn) in enumerate(stages):
                 fn()
                 ev[s][i + 1].record()
-        stop.record()
         torch.cuda.synchronize()
-        total = start.elapsed_time(stop) / steps
-        per = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
-               for i, (name, _) in enumerate(stages)}
-        return total, per
+        return {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+                for i, (name, _) in enumerate(stages)}
+
+    def time_graph(self, step, steps):
+        """The same step captured once in a HIP graph and replayed `steps`
+        times; returns (ms per replay, replay output equals the eager one)."""
+        torch = self.torch
+        out = self.out if step == self.gqe_step else self.out_dense
+        step()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        ms = None
+        ok = True
+        for rep in range(2):
+            out.zero_()
+            torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            start.record()
+            for _ in range(steps):
+                graph.replay()
+            stop.record()
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(stop) / steps
+            ok = ok and bool(torch.equal(out, eager))
+        del graph
+        return ms, ok
 
 
 def rate(kind, amount, ms):
@@ -133,15 +187,21 @@ def rate(kind, amount, ms):
     return v / 1e12  # TFLOP/s or TB/s
 
 
-def measure(wl, gqe, torch, steps, warmup):
+def measure(wl, gqe, torch, steps, warmup, graph=True):
     r = Runner(wl, gqe, torch)
-    t_gqe, st_gqe = r.time(r.gqe_stages(), steps, warmup)
-    t_gqa, st_gqa = r.time(r.gqa_stages(), steps, warmup)
+    t_gqe = r.time_steps(r.gqe_step, steps, warmup)
+    t_gqa = r.time_steps(r.gqa_step, steps, warmup)
+    st_gqe = r.time_stages(r.gqe_stages(), max(2, steps // 2))
+    st_gqa = r.time_stages(r.gqa_stages(), max(2, steps // 2))
+    # the attention kernel alone, launched back to back: its average duration
+    reps = max(3, steps)
+    k_gqe = r.time_steps(lambda: gqe.gqe_attention(r.cfg, r.ws), reps, 1)
+    k_gqa = r.time_steps(lambda: gqe.gqa_attention(r.cfg, r.ws_dense), reps, 1)
     tokens = wl.batch * wl.seq_len
     work = stage_work(wl)
     gwork = gqa_stage_work(wl)
     peak = PEAK_BF16 if wl.dtype == W.BF16 else PEAK_FP32_MFMA
-    att = work["attention"][1] / (st_gqe["attention"] * 1e-3)
+    att = work["attention"][1] / (k_gqe * 1e-3)
     res = {
         "workload": wl.name,
         "tokens": tokens,
@@ -150,33 +210,65 @@ def measure(wl, gqe, torch, steps, warmup):
         "gqe_tokens_per_s": tokens / (t_gqe * 1e-3),
         "gqa_tokens_per_s": tokens / (t_gqa * 1e-3),
         "speedup_vs_gqa": t_gqa / t_gqe,
-        "attention_speedup_vs_gqa": st_gqa["attention"] / st_gqe["attention"],
+        "attention_kernel_ms": k_gqe,
+        "gqa_attention_kernel_ms": k_gqa,
+        "attention_speedup_vs_gqa": k_gqa / k_gqe,
         "gqe_stage_ms": {k: round(v, 5) for k, v in st_gqe.items()},
         "gqa_stage_ms": {k: round(v, 5) for k, v in st_gqa.items()},
         "attention_tflops": att / 1e12,
         "attention_mfma_frac": att / peak,
-        "gqa_attention_mfma_frac": gwork["attention"][1] / (st_gqa["attention"] * 1e-3) / peak,
+        "gqa_attention_mfma_frac": gwork["attention"][1] / (k_gqa * 1e-3) / peak,
     }
+    if graph:
+        g_gqe, ok_gqe = r.time_graph(r.gqe_step, steps)
+        g_gqa, ok_gqa = r.time_graph(r.gqa_step, steps)
+        res.update({"graph_gqe_ms": g_gqe, "graph_gqa_ms": g_gqa,
+                    "graph_speedup_vs_gqa": g_gqa / g_gqe,
+                    "graph_replay_equals_eager": ok_gqe and ok_gqa})
     return r, res
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.txt")
+KERNEL_SOURCES = ("attention.hip", "device_common.h", "kernels.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_query_moe_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(wl_name):
+    """HBM bytes per attention launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the
+    summary is missing, covers another workload or predates the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split("=", 1) for line in f if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    key = f"traffic_bytes_per_launch.{wl_name}"
+    return float(kv[key]) if key in kv else None
+
+
 def roofline_for(wl, res):
-    """Roofline of the dominant kernel of the GQE step (the stage with the most time)."""
-    work = stage_work(wl)
-    stage = max(res["gqe_stage_ms"], key=res["gqe_stage_ms"].get)
-    kind, amount = work[stage]
-    ms = res["gqe_stage_ms"][stage]
-    if kind == "flop":
-        peak = (PEAK_BF16 if wl.dtype == W.BF16 else PEAK_FP32_MFMA) / 1e12
-        bound, unit = "mfma", "TFLOP/s"
-    else:
-        peak, bound, unit = PEAK_HBM / 1e12, "hbm", "TB/s"
+    """Roofline of the dominant kernel of the step, the causal attention kernel
+    (the longest single kernel at every workload), from its average duration
+    over back-to-back launches."""
+    kind, amount = stage_work(wl)["attention"]
+    ms = res["attention_kernel_ms"]
+    peak = (PEAK_BF16 if wl.dtype == W.BF16 else PEAK_FP32_MFMA) / 1e12
     ach = rate(kind, amount, ms)
-    if unit == "TB/s":
-        ach, peak, unit = ach * 1000, peak * 1000, "GB/s"
-    return {"kernel": stage, "bound": bound, "achieved": round(ach, 3), "peak": round(peak, 3),
-            "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
-            "per_launch": {"amount": amount, "kind": kind, "avg_ms": round(ms, 5)}}
+    return {"kernel": "attention_kernel", "bound": "mfma", "achieved": round(ach, 3),
+            "peak": round(peak, 3), "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+            "traffic": measured_traffic(wl.name),
+            "per_launch": {"flop": amount, "avg_ms": round(ms, 5)}}
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -215,6 +307,10 @@ def main():
                     help="other workloads timed for the per-length speed-up (comma list, '' = none)")
     ap.add_argument("--long", action="store_true", help="also time the 1M-token workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB three times (the known-size "
+                         "kernel that calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -225,9 +321,19 @@ def main():
     import torch
     from sparse_query_moe_amd import gqe
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {n} bytes read and written")
+        del src, dst
+
     wl = W.WORKLOADS[args.workload]
     log(f"[bench] {wl.description}: warmup {args.warmup}, steps {args.steps}")
-    _, res = measure(wl, gqe, torch, args.steps, args.warmup)
+    _, res = measure(wl, gqe, torch, args.steps, args.warmup, graph=not args.no_graph)
     log(f"[bench] gqe {res['gqe_ms']:.4f} ms  gqa {res['gqa_ms']:.4f} ms  "
         f"speed-up {res['speedup_vs_gqa']:.3f}  stages {res['gqe_stage_ms']}")
 
@@ -239,7 +345,7 @@ def main():
         w2 = W.WORKLOADS[name]
         steps = max(2, min(args.steps, int(2e12 / max(1, stage_work(w2)["attention"][1]) + 2)))
         log(f"[bench] per-length {w2.description}: steps {steps}")
-        _, r2 = measure(w2, gqe, torch, steps, 1)
+        _, r2 = measure(w2, gqe, torch, steps, 1, graph=not args.no_graph)
         log(f"[bench]   gqe {r2['gqe_ms']:.3f} ms gqa {r2['gqa_ms']:.3f} ms "
             f"speed-up {r2['speedup_vs_gqa']:.3f} attention {r2['attention_mfma_frac']:.3f} of peak")
         per_length.append(r2)
@@ -265,6 +371,8 @@ def main():
         "speedup_vs_gqa": round(res["speedup_vs_gqa"], 4),
         "gqa_tokens_per_s": round(res["gqa_tokens_per_s"], 1),
         "attention_mfma_frac": round(res["attention_mfma_frac"], 4),
+        "graph_tokens_per_s": (round(res["tokens"] / (res["graph_gqe_ms"] * 1e-3), 1)
+                               if "graph_gqe_ms" in res else None),
         "roofline": roofline_for(wl, res),
         "per_length": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
                        for r in per_length],

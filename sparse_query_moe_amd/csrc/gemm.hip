@@ -5,10 +5,12 @@
 // activations are row-major with K contiguous and the weights use the
 // [out, in] layout, also K contiguous, so both MFMA operands are 16-byte
 // vector loads along K.  A block computes a BM x BN tile with 4 waves; K
-// streams through a double-buffered LDS stage of 128-byte rows (64 bf16 or
-// 32 fp32 elements), swizzled per 16-byte chunk.  One barrier per K step: the
-// next stage's global loads are issued before the current stage's MFMAs and
-// written to the other LDS buffer after them.
+// streams through a ring of three LDS stages of 128-byte rows (64 bf16 or
+// 32 fp32 elements), swizzled per 16-byte chunk.  The stages are filled by
+// direct global-to-LDS loads (no register round trip), issued two K steps
+// ahead; one barrier per K step, after a wait that counts only the loads of
+// the stage about to be read.  The finished tile is staged through LDS so
+// that every output row or column is written with 16-byte stores.
 //
 // The three users differ only in where rows come from and where results go:
 //   dense projection  : rows are tokens; output columns are split into
