@@ -93,7 +93,13 @@ typedef struct gqe_config {
  *   q       dtype [B, k*G+1, L, d_h]   queries per slot-head (hard slot g*k+j,
  *                                      then the shared head)
  *   k       dtype [B, G, L, d_h]       keys
- *   vt      dtype [B, G, d_h, vt_ld]   values, transposed; vt_ld >= L
+ *   vt      dtype [B, G, vt_tiles, d_h, 64]  values, transposed per tile of
+ *                                64 keys (vt_tiles = ceil(L/64)); inside
+ *                                every 16-key group, key 8a+4u+r (a, u in
+ *                                {0,1}, r < 4) sits at column 8u+4a+r, the
+ *                                order in which the attention kernel feeds
+ *                                keys to the matrix cores; columns of keys
+ *                                >= L are unspecified
  *   s       dtype [B, L, (k*G+2)*d_h]  slot vectors (input of W_O)
  *   the rest is private scratch (dispatch partial counts, tile maps). */
 typedef struct gqe_ws_layout {
@@ -101,7 +107,7 @@ typedef struct gqe_ws_layout {
   size_t q, k, vt, s;
   size_t scratch;
   size_t total;
-  int64_t vt_ld;
+  int64_t vt_tiles;
 } gqe_ws_layout;
 
 /* Workspace size in bytes for gqe_forward and its stages (0 when cfg is

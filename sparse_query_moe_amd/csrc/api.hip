@@ -66,7 +66,7 @@ struct Layout {
 Layout make_layout(const gqe_config* c, bool dense) {
   const size_t B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts, k = c->top_k;
   const size_t D = c->head_dim, es = elem_bytes(c);
-  const size_t vt_ld = align_up(L, 64);
+  const size_t vt_tiles = (L + 63) / 64;
   Layout l{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -92,11 +92,11 @@ Layout make_layout(const gqe_config* c, bool dense) {
     l.pub.q = take(B * G * E * L * D * es);
   }
   l.pub.k = take(B * G * L * D * es);
-  l.pub.vt = take(B * G * D * vt_ld * es);
+  l.pub.vt = take(B * G * vt_tiles * D * 64 * es);
   l.pub.s = take(B * L * (dense ? G * E : G * k + 2) * D * es);
   if (dense) l.pub.scratch = off;
   l.pub.total = off;
-  l.pub.vt_ld = static_cast<int64_t>(vt_ld);
+  l.pub.vt_tiles = static_cast<int64_t>(vt_tiles);
   return l;
 }
 
@@ -160,7 +160,7 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   seg[2].heads = G;
   seg[2].head_base = 0;
   seg[2].transposed = 1;
-  hipError_t e = launch_dense_proj<T>(static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_ld, seg,
+  hipError_t e = launch_dense_proj<T>(static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_tiles, seg,
                                       3, stream);
   if (e != hipSuccess || dense) return hip_status(e);
   e = launch_gather_q<T>(static_cast<const T*>(x), static_cast<const T*>(wq), at<T>(ws, l.pub.q),
@@ -180,7 +180,7 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
   p.k = at<T>(ws, l.pub.k);
   p.vt = at<T>(ws, l.pub.vt);
   p.o = at<T>(ws, l.pub.s);
-  p.vt_ld = l.pub.vt_ld;
+  p.vt_tiles = l.pub.vt_tiles;
   p.B = c->batch;
   p.G = G;
   p.L = c->seq_len;

@@ -14,8 +14,9 @@
 //   keys of every 32-key block in its accumulator; the row max needs a single
 //   exchange with lane l ^ 32.  The accumulator, converted to bf16, is already
 //   the B operand of O^T = V^T . P^T (keys along K), so probabilities never
-//   leave registers; V^T tiles are staged in LDS with their keys permuted
-//   inside every 16-key group to match that accumulator order, which makes
+//   leave registers; V^T comes from the projection in tiles of 64 keys with
+//   the keys permuted inside every 16-key group to match that accumulator
+//   order, so each V^T tile is one contiguous 8 KB (bf16, d_h 64) read and
 //   each V^T fragment one 16-byte LDS read.  O^T again has one query per lane,
 //   so the online-softmax rescale is lane-local.
 //   K and V^T tiles of 64 keys are double-buffered in LDS (swizzled 16-byte
@@ -38,56 +39,58 @@ namespace {
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 
-template <typename T, int D, int QB = 1>
+// QW query waves of 32*QB rows each share every K/V tile; NS groups of QW
+// waves split the key range of the block (tile jt goes to group jt % NS) and
+// merge their partial softmax states in LDS at the end.
+template <typename T, int D, int QB, int QW, int NS>
 struct AttnShape {
-  static constexpr int BQ = 4 * 32 * QB, BKV = 64;  // 4 waves, QB 32-query blocks each
+  static constexpr int NT = 64 * QW;        // threads of one key group
+  static constexpr int THREADS = NT * NS;
+  static constexpr int BQ = QW * 32 * QB, BKV = 64;
   static constexpr int EPC = 16 / static_cast<int>(sizeof(T));
   static constexpr int KROW = D * static_cast<int>(sizeof(T));    // bytes per K tile row (a key)
   static constexpr int VROW = BKV * static_cast<int>(sizeof(T));  // bytes per V^T tile row (a dim)
   static constexpr int KT = BKV * KROW, VT = D * VROW;
   static constexpr int STAGE = KT + VT;
-  static constexpr int LDS = 2 * STAGE;
   static constexpr int K_CPR = KROW / 16, V_CPR = VROW / 16;  // 16-byte chunks per row
-  static constexpr int K_CH = BKV * K_CPR / 256, V_CH = D * V_CPR / 256;
+  static constexpr int K_CH = BKV * K_CPR / NT, V_CH = D * V_CPR / NT;
   static constexpr int NDB = D / 32;  // 32-row blocks of O^T
   static constexpr int NKS = D / 16;  // K-steps of S^T
+  // partial state of one wave in the merge area: o (NDB*16), m, l per lane
+  static constexpr int PART = (NDB * 16 + 2) * 64;  // floats
+  static constexpr int KV_LDS = NS * 2 * STAGE;
+  static constexpr int MERGE_LDS = (NS - 1) * QW * QB * PART * 4;
+  static constexpr int LDS = KV_LDS > MERGE_LDS ? KV_LDS : MERGE_LDS;
   static_assert(K_CH >= 1 && V_CH >= 1, "tile smaller than one chunk per thread");
+  static_assert(BKV * K_CPR % NT == 0 && D * V_CPR % NT == 0, "uneven tile split");
 };
 
-// Where the 16-byte global chunk cc of a V^T row lands in LDS.  Inside each
-// 16-key group, logical key 8a + 4u + r (a, u in {0,1}, r < 4) is stored at
-// physical position 8u + 4a + r: lane half u then reads its 8 keys contiguously.
-template <typename T, int D> struct VStore;
-template <int D> struct VStore<bf16_t, D> {
-  typedef AttnShape<bf16_t, D> S;
-  // a chunk holds keys 8cc..8cc+7 = (a = cc & 1; u = 0 then u = 1): two 8-byte halves
-  static __device__ __forceinline__ void put(char* vs, int row, int cc, uint4 v) {
-    const int g16 = cc >> 1, a = cc & 1;
-    char* p0 = vs + swz<S::VROW>(row, 2 * g16) + 8 * a;
-    char* p1 = vs + swz<S::VROW>(row, 2 * g16 + 1) + 8 * a;
-    *reinterpret_cast<uint2*>(p0) = make_uint2(v.x, v.y);
-    *reinterpret_cast<uint2*>(p1) = make_uint2(v.z, v.w);
-  }
-};
-template <int D> struct VStore<float, D> {
-  typedef AttnShape<float, D> S;
-  // a chunk holds keys 4cc..4cc+3 = one (a, u) quarter of a 16-key group
-  static __device__ __forceinline__ void put(char* vs, int row, int cc, uint4 v) {
-    const int g16 = cc >> 2, a = (cc >> 1) & 1, u = cc & 1;
-    *reinterpret_cast<uint4*>(vs + swz<S::VROW>(row, 4 * g16 + 2 * u + a)) = v;
-  }
-};
-
-// zero the elements of a chunk whose keys are >= L (chunk starts at key k0)
+// V^T arrives in HBM already in the order the MFMA wants (inside every 16-key
+// group, key 8a+4u+r at column 8u+4a+r), so a 16-byte chunk goes to LDS as is.
+// Logical key of element e of chunk cc (chunk of EPC columns) of a tile:
 template <typename T>
-__device__ __forceinline__ uint4 mask_keys(uint4 v, int k0, int L) {
+__device__ __forceinline__ int vt_key(int cc, int e) {
+  if constexpr (sizeof(T) == 2) {  // 8 columns = half u of a 16-key group
+    const int g16 = cc >> 1, u = cc & 1;
+    return 16 * g16 + 4 * u + (e & 3) + 8 * (e >> 2);
+  } else {  // 4 columns = quarter (u, a) of a 16-key group
+    const int g16 = cc >> 2, u = (cc >> 1) & 1, a = cc & 1;
+    return 16 * g16 + 8 * a + 4 * u + e;
+  }
+}
+
+// zero the elements of V^T chunk cc of the tile starting at key j0 whose keys
+// are >= L (a chunk never leaves its 16-key group)
+template <typename T>
+__device__ __forceinline__ uint4 mask_vt(uint4 v, int j0, int cc, int L) {
   constexpr int EPC = 16 / static_cast<int>(sizeof(T));
-  if (k0 + EPC <= L) return v;
-  if (k0 >= L) return zero4();
+  const int g0 = j0 + 16 * (cc / (16 / EPC));
+  if (g0 + 16 <= L) return v;
+  if (g0 >= L) return zero4();
   T* e = reinterpret_cast<T*>(&v);
 #pragma unroll
   for (int j = 0; j < EPC; ++j)
-    if (k0 + j >= L) e[j] = T(0);
+    if (j0 + vt_key<T>(cc, j) >= L) e[j] = T(0);
   return v;
 }
 
@@ -114,14 +117,18 @@ __device__ __forceinline__ float dot8(const f32x8& a, const f32x8& b) {
   return s;
 }
 
-template <typename T, int D, int QB>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attention_kernel(
+template <typename T, int D, int QB, int QW, int NS, int PF>
+__global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) void attention_kernel(
     AttnParams p) {
-  typedef AttnShape<T, D, QB> S;
+  typedef AttnShape<T, D, QB, QW, NS> S;
   typedef typename Frag<T>::type F;
   extern __shared__ __align__(16) char smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const int grp = NS == 1 ? 0 : (threadIdx.x >> 6) / QW;  // key group
+  const int wave = NS == 1 ? (threadIdx.x >> 6) : (threadIdx.x >> 6) % QW;  // query wave
+  const int tid = threadIdx.x - grp * S::NT;    // thread inside the group
+  char* gsm = smem + grp * 2 * S::STAGE;        // this group's two K/V stages
   const int L = p.L;
   const int nq = (L + S::BQ - 1) / S::BQ;
   const int bh_count = p.B * p.H;
@@ -133,12 +140,66 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attention_kernel(
 
   const T* Q = static_cast<const T*>(p.q) + (static_cast<size_t>(b) * p.H + head) * L * D;
   const T* Kg = static_cast<const T*>(p.k) + (static_cast<size_t>(b) * p.G + g) * L * D;
-  const T* Vg = static_cast<const T*>(p.vt) + (static_cast<size_t>(b) * p.G + g) * D * p.vt_ld;
+  const T* Vg = static_cast<const T*>(p.vt) + (static_cast<size_t>(b) * p.G + g) * p.vt_tiles * D * 64;
 
   const int q0 = qblk * S::BQ;
   const int qw0 = q0 + 32 * QB * wave;                 // first query of this wave
   const int wave_last = min(qw0 + 32 * QB - 1, L - 1);  // last valid query of this wave
   const bool wave_active = qw0 < L;
+
+  const int kv_end = min(q0 + S::BQ, L);
+  const int ntiles = (kv_end + S::BKV - 1) / S::BKV;
+  // group grp takes tiles grp, grp + NS, grp + 2 NS, ...; every group runs
+  // the same number of rounds so that the block-wide barriers pair up
+  const int rounds = (ntiles + NS - 1) / NS;
+  auto tile_of = [&](int it) { return it * NS + grp; };  // tile of round it
+
+  // K/V tile staging: raw 16-byte global loads into registers (addresses
+  // clamped into the sequence, so a load never depends on a branch), then
+  // masked (keys >= L become 0) and stored to LDS.  With PF = 2 two register
+  // sets keep the tiles of the next two rounds in flight.
+  struct Regs {
+    uint4 k[S::K_CH], v[S::V_CH];
+  };
+  Regs rs[PF];
+  auto gload = [&](Regs& r, int jt) {
+    const int j0 = jt * S::BKV;
+#pragma unroll
+    for (int i = 0; i < S::K_CH; ++i) {
+      const int c = tid + S::NT * i;
+      const int row = c / S::K_CPR, cc = c % S::K_CPR;
+      const int key = j0 + row < L ? j0 + row : 0;
+      r.k[i] = *reinterpret_cast<const uint4*>(Kg + static_cast<size_t>(key) * D + cc * S::EPC);
+    }
+#pragma unroll
+    for (int i = 0; i < S::V_CH; ++i) {
+      const int c = tid + S::NT * i;
+      const int row = c / S::V_CPR, cc = c % S::V_CPR;
+      const int jv = j0 < L ? jt : 0;  // tiles past the sequence read tile 0
+      r.v[i] = *reinterpret_cast<const uint4*>(Vg + (static_cast<size_t>(jv) * D + row) * 64 +
+                                               cc * S::EPC);
+    }
+  };
+  auto sstore = [&](const Regs& r, int buf, int jt) {
+    const int j0 = jt * S::BKV;
+    char* ks_ = gsm + buf * S::STAGE;
+    char* vs_ = ks_ + S::KT;
+#pragma unroll
+    for (int i = 0; i < S::K_CH; ++i) {
+      const int c = tid + S::NT * i;
+      const int row = c / S::K_CPR;
+      *reinterpret_cast<uint4*>(ks_ + swz<S::KROW>(row, c % S::K_CPR)) =
+          j0 + row < L ? r.k[i] : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < S::V_CH; ++i) {
+      const int c = tid + S::NT * i;
+      const int cc = c % S::V_CPR;
+      *reinterpret_cast<uint4*>(vs_ + swz<S::VROW>(c / S::V_CPR, cc)) = mask_vt<T>(r.v[i], j0, cc, L);
+    }
+  };
+  gload(rs[0], tile_of(0));
+  if constexpr (PF > 1) gload(rs[PF - 1], tile_of(1));
 
   // queries (pre-scaled) in registers; the running maximum starts at the score
   // against key 0, which every causal row sees, so it is finite from the start
@@ -173,48 +234,6 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attention_kernel(
         for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
     }
   }
-
-  const int kv_end = min(q0 + S::BQ, L);
-  const int ntiles = (kv_end + S::BKV - 1) / S::BKV;
-
-  uint4 rk[S::K_CH], rv[S::V_CH];
-  auto gload = [&](int jt) {
-    const int j0 = jt * S::BKV;
-#pragma unroll
-    for (int i = 0; i < S::K_CH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / S::K_CPR, cc = c % S::K_CPR;
-      const int key = j0 + row;
-      rk[i] = key < L ? *reinterpret_cast<const uint4*>(Kg + static_cast<size_t>(key) * D +
-                                                         cc * S::EPC)
-                      : zero4();
-    }
-#pragma unroll
-    for (int i = 0; i < S::V_CH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / S::V_CPR, cc = c % S::V_CPR;
-      const int k0 = j0 + cc * S::EPC;
-      uint4 v = zero4();
-      if (k0 < L)
-        v = mask_keys<T>(*reinterpret_cast<const uint4*>(Vg + static_cast<size_t>(row) * p.vt_ld + k0),
-                         k0, L);
-      rv[i] = v;
-    }
-  };
-  auto sstore = [&](int buf) {
-    char* ks_ = smem + buf * S::STAGE;
-    char* vs_ = ks_ + S::KT;
-#pragma unroll
-    for (int i = 0; i < S::K_CH; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(ks_ + swz<S::KROW>(c / S::K_CPR, c % S::K_CPR)) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < S::V_CH; ++i) {
-      const int c = tid + 256 * i;
-      VStore<T, D>::put(vs_, c / S::V_CPR, c % S::V_CPR, rv[i]);
-    }
-  };
 
   // one 64-key tile for this wave's QB query blocks
   auto tile = [&](const char* Ks, const char* Vs, int j0, auto masked) {
@@ -297,22 +316,80 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attention_kernel(
     }
   };
 
-  gload(0);
-  sstore(0);
+  if (tile_of(0) < ntiles) sstore(rs[0], 0, tile_of(0));
   lds_barrier();
-  for (int jt = 0; jt < ntiles; ++jt) {
-    if (jt + 1 < ntiles) gload(jt + 1);
-    const char* Ks = smem + (jt & 1) * S::STAGE;
+  // one round: compute tile jt from LDS buffer it & 1 while `fre` (already
+  // stored) takes the load of round it + PF; `nxt` holds round it + 1
+  auto step = [&](int it, Regs& nxt, Regs& fre) {
+    const int jt = tile_of(it);
+    const int jn = it + 1 < rounds ? tile_of(it + 1) : ntiles;  // next round's tile
+    if constexpr (PF > 1) {
+      gload(fre, tile_of(it + 2));
+    } else {
+      if (jn < ntiles) gload(nxt, jn);
+    }
+    const char* Ks = gsm + (it & 1) * S::STAGE;
     const char* Vs = Ks + S::KT;
     const int j0 = jt * S::BKV;
-    if (wave_active && j0 <= wave_last) {
+    if ((NS == 1 || jt < ntiles) && wave_active && j0 <= wave_last) {
       if (j0 + S::BKV - 1 <= qw0)
         tile(Ks, Vs, j0, std::false_type{});
       else
         tile(Ks, Vs, j0, std::true_type{});
     }
-    if (jt + 1 < ntiles) sstore((jt + 1) & 1);
+    if (jn < ntiles) sstore(nxt, (it + 1) & 1, jn);
     lds_barrier();
+  };
+  if constexpr (PF > 1) {
+    for (int it = 0; it < rounds; it += 2) {
+      step(it, rs[1], rs[0]);
+      if (it + 1 < rounds) step(it + 1, rs[0], rs[1]);
+    }
+  } else {
+    for (int it = 0; it < rounds; ++it) step(it, rs[0], rs[0]);
+  }
+
+  if constexpr (NS > 1) {
+    // merge: groups 1.. park (o, m, l) in LDS (the K/V stages are free after
+    // the last barrier), group 0 rescales everything to the common maximum
+    float* part = reinterpret_cast<float*>(smem);
+    auto slot_of = [&](int gsrc, int qb) {
+      return part + (((gsrc - 1) * QW + wave) * QB + qb) * S::PART;
+    };
+    if (grp > 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float* ps = slot_of(grp, qb);
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ps[(db * 16 + i) * 64 + lane] = o[qb][db][i];
+        ps[S::NDB * 16 * 64 + lane] = m_run[qb];
+        ps[(S::NDB * 16 + 1) * 64 + lane] = l_run[qb];
+      }
+    }
+    lds_barrier();
+    if (grp > 0) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mmax = m_run[qb];
+      for (int gs = 1; gs < NS; ++gs) mmax = fmaxf(mmax, slot_of(gs, qb)[S::NDB * 16 * 64 + lane]);
+      const float a0 = __builtin_amdgcn_exp2f(m_run[qb] - mmax);
+      l_run[qb] *= a0;
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[qb][db][i] *= a0;
+      for (int gs = 1; gs < NS; ++gs) {
+        const float* ps = slot_of(gs, qb);
+        const float a = __builtin_amdgcn_exp2f(ps[S::NDB * 16 * 64 + lane] - mmax);
+        l_run[qb] = fmaf(ps[(S::NDB * 16 + 1) * 64 + lane], a, l_run[qb]);
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[qb][db][i] = fmaf(ps[(db * 16 + i) * 64 + lane], a, o[qb][db][i]);
+      }
+    }
   }
 
 #pragma unroll
@@ -339,42 +416,49 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attention_kernel(
   }
 }
 
-template <typename T, int D, int QB>
+template <typename T, int D, int QB, int QW, int NS, int PF>
 hipError_t launch_attention_d(const AttnParams& p, hipStream_t stream) {
-  typedef AttnShape<T, D, QB> S;
+  typedef AttnShape<T, D, QB, QW, NS> S;
   const int nq = (p.L + S::BQ - 1) / S::BQ;
   const long long blocks = static_cast<long long>(nq) * p.B * p.H;
   if (blocks == 0) return hipSuccess;
   if (S::LDS > 65536) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attention_kernel<T, D, QB>),
+        reinterpret_cast<const void*>(&attention_kernel<T, D, QB, QW, NS, PF>),
         hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((attention_kernel<T, D, QB>), dim3(static_cast<unsigned>(blocks)), dim3(256),
-                     S::LDS, stream, p);
+  hipLaunchKernelGGL((attention_kernel<T, D, QB, QW, NS, PF>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(S::THREADS), S::LDS, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Two 32-query blocks per wave halve the LDS traffic per MFMA; short
-// sequences keep one so that the grid still covers the chip.
+// Long launches: 4 query waves per block, two 32-query blocks per wave (half
+// the LDS traffic per MFMA).  Short ones, whose blocks would not cover the
+// chip, take 64-row blocks whose key range is split over NS groups of waves,
+// which shortens the causal critical path NS-fold.
 template <typename T>
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream) {
+  const bool wide = static_cast<long long>(p.L) * p.B * p.H >= 256LL * 256 * 4;
   if constexpr (sizeof(T) == 2) {
-    const bool wide = static_cast<long long>(p.L) * p.B * p.H >= 256LL * 256 * 4;
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 2>(p, stream) : launch_attention_d<T, 32, 1>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 2>(p, stream) : launch_attention_d<T, 64, 1>(p, stream);
-      case 128: return launch_attention_d<T, 128, 1>(p, stream);
+      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1, 1>(p, stream)
+                           : launch_attention_d<T, 32, 1, 2, 4, 2>(p, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1, 1>(p, stream)
+                           : launch_attention_d<T, 64, 1, 2, 4, 2>(p, stream);
+      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1, 1>(p, stream)
+                            : launch_attention_d<T, 128, 1, 2, 2, 2>(p, stream);
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (D) {
-      case 32: return launch_attention_d<T, 32, 1>(p, stream);
-      case 64: return launch_attention_d<T, 64, 1>(p, stream);
-      case 128: return launch_attention_d<T, 128, 1>(p, stream);
+      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1, 1>(p, stream)
+                           : launch_attention_d<T, 32, 1, 2, 4, 2>(p, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1, 1>(p, stream)
+                           : launch_attention_d<T, 64, 1, 2, 2, 1>(p, stream);
+      case 128: return launch_attention_d<T, 128, 1, 4, 1, 1>(p, stream);
       default: return hipErrorInvalidValue;
     }
   }

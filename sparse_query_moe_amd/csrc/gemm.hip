@@ -199,7 +199,7 @@ __device__ __forceinline__ void copy8(T* dst, const T* src) {
 struct DenseArgs {
   const void* x;
   int M, K, N, L, D;
-  int64_t ld_t;
+  int64_t vt_tiles;
   int nseg;
   ProjSeg seg[3];
 };
@@ -252,29 +252,43 @@ struct DenseProb {
       T* dst = static_cast<T*>(sg.out) + ((static_cast<size_t>(b) * sg.heads + hh) * a.L + t) * a.D + dd;
       copy8(dst, ct + r * S::LDC + 8 * c8);
     }
+    // V^T: one 16-byte chunk = 8 keys of one head dim, in the permuted order
+    // (chunk u of a 16-key group holds keys 4u..4u+3 and 8+4u..8+4u+3)
     for (int c = threadIdx.x; c < (S::BM / 8) * S::BN; c += 256) {
       const int nl = c % S::BN, r8 = c / S::BN;
-      const int col = n0 + nl, m = m0 + 8 * r8;
-      if (m >= a.M || col >= a.N) continue;
+      const int g16 = r8 >> 1, u = r8 & 1;
+      const int col = n0 + nl, mg = m0 + 16 * g16;  // first token of the 16-key group
+      if (mg >= a.M || col >= a.N) continue;
       const ProjSeg sg = seg_of(col);
       if (!sg.transposed) continue;
       const int cl = col - sg.n_begin;
       const int hh = sg.head_base + cl / a.D, dd = cl % a.D;
-      const int b = m / a.L, t = m % a.L;
       T* out = static_cast<T*>(sg.out);
-      if (t + 8 <= a.L && m + 8 <= a.M && (a.L & 7) == 0) {
+      auto key_of = [&](int j) { return 16 * g16 + (j < 4 ? 4 * u + j : 8 + 4 * u + (j - 4)); };
+      if ((a.L & 15) == 0 && mg + 16 <= a.M) {
+        const int b = mg / a.L, t = mg % a.L;  // t is a multiple of 16
         alignas(16) T v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = ct[(8 * r8 + j) * S::LDC + nl];
-        copy8(out + ((static_cast<size_t>(b) * sg.heads + hh) * a.D + dd) * static_cast<size_t>(a.ld_t) + t, v);
+        for (int j = 0; j < 8; ++j) v[j] = ct[key_of(j) * S::LDC + nl];
+        copy8(out + vt_index(b, sg.heads, hh, dd, t) + 8 * u, v);
       } else {
-        for (int j = 0; j < 8 && m + j < a.M; ++j) {
-          const int bj = (m + j) / a.L, tj = (m + j) % a.L;
-          out[((static_cast<size_t>(bj) * sg.heads + hh) * a.D + dd) * static_cast<size_t>(a.ld_t) + tj] =
-              ct[(8 * r8 + j) * S::LDC + nl];
+        for (int j = 0; j < 8; ++j) {
+          const int mj = m0 + key_of(j);
+          if (mj >= a.M) continue;
+          const int bj = mj / a.L, tj = mj % a.L;
+          out[vt_index(bj, sg.heads, hh, dd, tj & ~15) + vt_col(tj & 15)] = ct[key_of(j) * S::LDC + nl];
         }
       }
     }
+  }
+  // element offset of (b, head, dim, 16-aligned key t) in [B, heads, tiles, D, 64]
+  __device__ __forceinline__ size_t vt_index(int b, int heads, int hh, int dd, int t) const {
+    return ((static_cast<size_t>(b) * heads + hh) * a.vt_tiles + t / 64) * a.D * 64 +
+           static_cast<size_t>(dd) * 64 + (t & 63);
+  }
+  // column of key position p (< 16) inside its 16-key group
+  static __device__ __forceinline__ int vt_col(int p) {
+    return (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1);
   }
 };
 
@@ -447,7 +461,7 @@ static hipError_t launch_gemm(Kern kern, dim3 grid, hipStream_t stream, const Ar
 }
 
 template <typename T>
-hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t ld_t,
+hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
                              const ProjSeg* segs, int nseg, hipStream_t stream) {
   typedef GemmShape<T, 128, 128, 2, 2> S;
   DenseArgs a;
@@ -456,7 +470,7 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t ld_
   a.K = K;
   a.L = L;
   a.D = D;
-  a.ld_t = ld_t;
+  a.vt_tiles = vt_tiles;
   a.nseg = nseg;
   int N = 0;
   for (int i = 0; i < nseg; ++i) {

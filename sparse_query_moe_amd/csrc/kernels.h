@@ -26,7 +26,8 @@ hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* c
 // ---- K3 projections ----------------------------------------------------------
 // One output segment of a dense projection: columns [n_begin, n_begin + n)
 // of the concatenated output come from `w` (rows of [out, in] layout) and go
-// to head-split tensor `out`, [B, heads, L, D] or, transposed, [B, heads, D, ld_t].
+// to head-split tensor `out`, [B, heads, L, D] or, transposed per 64-key tile
+// with keys permuted inside 16-key groups, [B, heads, vt_tiles, D, 64].
 struct ProjSeg {
   const void* w;
   void* out;
@@ -37,7 +38,7 @@ struct ProjSeg {
   int transposed;
 };
 template <typename T>
-hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t ld_t,
+hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
                              const ProjSeg* segs, int nseg, hipStream_t stream);
 
 // Grid: (tiles_per_bg, B*G); tile_off is the per-(b, g) tile map written by
@@ -52,9 +53,9 @@ hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
 struct AttnParams {
   const void* q;       // [B, H, L, D]
   const void* k;       // [B, G, L, D]
-  const void* vt;      // [B, G, D, vt_ld]
+  const void* vt;      // [B, G, vt_tiles, D, 64], keys permuted in 16-key groups
   void* o;             // o[(b*L + t)*ld_o + head*D + d]
-  int64_t vt_ld;
+  int64_t vt_tiles;
   int64_t ld_o;
   int B, H, G, L;
   int heads_per_group;  // heads h < n_grouped read group h / heads_per_group

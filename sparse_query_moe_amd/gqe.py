@@ -49,7 +49,7 @@ class GqeConfig(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("idx", "w", "counts", "offsets", "pos", "slot", "q", "k", "vt", "s", "scratch",
-                 "total")] + [("vt_ld", ctypes.c_int64)]
+                 "total")] + [("vt_tiles", ctypes.c_int64)]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -218,5 +218,6 @@ def workspace_views(cfg: GqeConfig, ws: torch.Tensor, dense: bool = False) -> di
         out["q"] = view(lay.q, (B, G * E, L, D), dt, es)
         out["s"] = view(lay.s, (B, L, G * E * D), dt, es)
     out["k"] = view(lay.k, (B, G, L, D), dt, es)
-    out["vt"] = view(lay.vt, (B, G, D, int(lay.vt_ld)), dt, es)
+    # V^T per 64-key tile, keys permuted inside 16-key groups (see include/gqe.h)
+    out["vt"] = view(lay.vt, (B, G, int(lay.vt_tiles), D, 64), dt, es)
     return out

@@ -35,6 +35,31 @@ def round_like(a: np.ndarray, dtype: str) -> np.ndarray:
     return W.f32_to_bf16_bits(a32) if dtype == W.BF16 else a32
 
 
+# Column of key position p inside its 16-key group in the tiled V^T workspace
+# layout (include/gqe.h): key 8a+4u+r sits at column 8u+4a+r.
+_VT_COL = np.array([(p & 3) | ((p & 4) << 1) | ((p & 8) >> 1) for p in range(16)])
+
+
+def vt_encode(v: np.ndarray) -> np.ndarray:
+    """V [B, G, L, D] (any dtype) -> tiled V^T [B, G, ceil(L/64), D, 64], zero padded."""
+    B, G, L, D = v.shape
+    nt = (L + 63) // 64
+    pad = np.zeros((B, G, nt * 64, D), dtype=v.dtype)
+    pad[:, :, :L] = v
+    cols = (np.arange(nt * 64) // 16) * 16 + _VT_COL[np.arange(nt * 64) % 16]
+    out = np.zeros_like(pad)
+    out[:, :, cols] = pad
+    return np.ascontiguousarray(out.reshape(B, G, nt, 64, D).transpose(0, 1, 2, 4, 3))
+
+
+def vt_decode(vt: np.ndarray, L: int) -> np.ndarray:
+    """Tiled V^T [B, G, nt, D, 64] -> V [B, G, L, D]."""
+    B, G, nt, D, _ = vt.shape
+    flat = vt.transpose(0, 1, 2, 4, 3).reshape(B, G, nt * 64, D)
+    cols = (np.arange(nt * 64) // 16) * 16 + _VT_COL[np.arange(nt * 64) % 16]
+    return flat[:, :, cols][:, :, :L]
+
+
 def output_gate(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
     """The output tolerances: max-abs 2e-2 and mean-abs 2e-3 for bf16 with fp32
     accumulation; 1e-5 for float32 layers.  Also returns the relative L2 error."""

@@ -14,7 +14,8 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 import workloads as W  # noqa: E402
-from gpu_util import f64_inputs, inputs, log, output_gate, round_like, to_dev, to_f64  # noqa: E402
+from gpu_util import (f64_inputs, inputs, log, output_gate, round_like, to_dev, to_f64,  # noqa: E402
+                      vt_decode, vt_encode)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +69,7 @@ def check_routing(gqe, cfg, ws, ref):
 # stage parity (tiny fp32 layer, the 2k bf16 layer, and a ragged shape)
 # ---------------------------------------------------------------------------
 
-# the last case is long enough (B*L*heads) for the ping-pong attention schedule
+# the last case is long enough (B*L*heads >= 2^18) for the long-launch attention schedule
 STAGE_CASES = [("tiny_fp32", 0, 0), ("l2k", 0, 0), ("l2k", 333, 2), ("l2k", 8269, 4)]
 
 
@@ -138,7 +139,7 @@ def test_stage_project(gqe, name, L, B):
     v = gqe.workspace_views(cfg, ws)
     q = to_f64(v["q"]).transpose(0, 2, 1, 3)            # [B, L, kG+1, D]
     k = to_f64(v["k"])
-    vt = to_f64(v["vt"])[..., :wl.seq_len]
+    vt = vt_decode(to_f64(v["vt"]), wl.seq_len).transpose(0, 1, 3, 2)
     tol = 2.0 ** -8 if wl.dtype == W.BF16 else 1e-6
     for got, want, what in ((q, ref["q"], "q"), (k, ref["k_"], "k"),
                             (vt, ref["v"].transpose(0, 1, 3, 2), "vt")):
@@ -163,7 +164,7 @@ def test_stage_attention(gqe, name, L, B):
     v_st = round_like(ref["v"], wl.dtype)
     v["q"].copy_(to_dev(q_st, wl.dtype))
     v["k"].copy_(to_dev(k_st, wl.dtype))
-    v["vt"][..., :wl.seq_len].copy_(to_dev(np.ascontiguousarray(v_st.transpose(0, 1, 3, 2)), wl.dtype))
+    v["vt"].copy_(to_dev(vt_encode(v_st), wl.dtype))
     gqe.gqe_attention(cfg, ws)
     torch.cuda.synchronize()
     qf = W.to_f64(q_st, wl.dtype)
@@ -177,6 +178,47 @@ def test_stage_attention(gqe, name, L, B):
             g = h // wl.top_k if h < H - 1 else 0
             want = oracle.causal_attention(qf[b, h], t, kf[b, g], vf[b, g], scale)
             output_gate(s[b, :, h], want, wl.dtype, f"attention b={b} h={h}")
+
+
+# every attention schedule the launcher picks: short launches (key range split
+# over wave groups) and long ones (B*L*heads >= 2^18), each head size and type
+ATTN_PATH_CASES = [
+    ("bf16", 32, 1, 2, 1, 700), ("bf16", 32, 1, 4, 2, 32768), ("bf16", 64, 2, 4, 2, 1500),
+    ("bf16", 128, 1, 4, 2, 32768), ("fp32", 32, 1, 4, 2, 32768), ("fp32", 64, 1, 2, 1, 1000),
+    ("fp32", 64, 1, 4, 2, 32768),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,G,k,L", ATTN_PATH_CASES)
+def test_attention_paths(gqe, dtype, D, B, G, k, L):
+    """gqe_attention on seeded random Q/K/V against the oracle's attention on
+    the first 96 rows, the last row and 160 rows drawn at random."""
+    log(f"[attention path] {dtype} D={D} B={B} G={G} k={k} L={L}")
+    wl = W.Workload("attn", B, L, 128, G, k + 1, k, D, dtype, 1.0, 0.05)
+    cfg = cfg_for(gqe, wl)
+    ws = gqe.alloc_workspace(cfg)
+    v = gqe.workspace_views(cfg, ws)
+    H = wl.slot_heads
+    rng = np.random.Generator(np.random.PCG64(11))
+    q = round_like(rng.standard_normal((B, H, L, D)) * 2.0, dtype)
+    kk = round_like(rng.standard_normal((B, G, L, D)), dtype)
+    vv = round_like(rng.standard_normal((B, G, L, D)), dtype)
+    v["q"].copy_(to_dev(q, dtype))
+    v["k"].copy_(to_dev(kk, dtype))
+    v["vt"].copy_(to_dev(vt_encode(vv), dtype))
+    gqe.gqe_attention(cfg, ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(min(L, 96)), [L - 1],
+                                     rng.choice(L, size=min(L, 160), replace=False)]))
+    s = to_f64(v["s"][:, rows]).reshape(B, len(rows), H + 1, D)
+    scale = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for h in range(H):
+            g = h // k if h < H - 1 else 0
+            want = oracle.causal_attention(W.to_f64(q[b, h, rows], dtype), rows,
+                                           W.to_f64(kk[b, g], dtype), W.to_f64(vv[b, g], dtype),
+                                           scale)
+            output_gate(s[b, :, h], want, dtype, f"attention b={b} h={h}")
 
 
 # ---------------------------------------------------------------------------
@@ -256,8 +298,8 @@ def test_determinism(gqe):
     for key in ("idx", "w", "counts", "offsets", "pos", "slot", "q", "k", "s"):
         assert torch.equal(v1[key].view(torch.uint8), v2[key].view(torch.uint8)), key
     L = wl.seq_len
-    assert torch.equal(v1["vt"][..., :L].contiguous().view(torch.uint8),
-                       v2["vt"][..., :L].contiguous().view(torch.uint8))
+    assert np.array_equal(vt_decode(v1["vt"].view(torch.int16).cpu().numpy(), L),
+                          vt_decode(v2["vt"].view(torch.int16).cpu().numpy(), L))
 
 
 @pytest.mark.parametrize("L,B,G,E,k,D,dtype", [
