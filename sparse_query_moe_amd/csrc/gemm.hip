@@ -31,7 +31,7 @@ namespace gqe {
 
 namespace {
 
-template <typename T, int BM_, int BN_, int WGM_, int WGN_, int NST_ = 3>
+template <typename T, int BM_, int BN_, int WGM_, int WGN_, int NST_ = 2>
 struct GemmShape {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, NST = NST_;
   static constexpr int EPC = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
@@ -101,6 +101,7 @@ template <typename T, class S, class P>
 __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
   typedef typename Frag<T>::type F;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int swave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: LDS bases go through M0
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int r0 = tid >> 3;
   const int pc = tid & 7;  // physical 16-byte chunk this lane fills in its row
@@ -126,11 +127,11 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
     char* st = smem + (kt % S::NST) * S::STAGE;
 #pragma unroll
     for (int i = 0; i < S::A_CH; ++i)
-      __builtin_amdgcn_global_load_lds(ap[i] + kt * S::BKE, GQE_LDS(st + (4 * i + wave) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ap[i] + kt * S::BKE, GQE_LDS(st + (4 * i + swave) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < S::B_CH; ++i)
       __builtin_amdgcn_global_load_lds(bp[i] + kt * S::BKE,
-                                       GQE_LDS(st + S::BM * 128 + (4 * i + wave) * 1024), 16, 0, 0);
+                                       GQE_LDS(st + S::BM * 128 + (4 * i + swave) * 1024), 16, 0, 0);
   };
 
   f32x16 acc[S::TM][S::TN];
@@ -141,6 +142,10 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
+  // per K step: wait for this wave's loads of stage kt, barrier (the stage is
+  // complete and every wave is done with stage kt-1), refill stage kt-1's
+  // buffer with stage kt+NST-1, then read the fragments and multiply
+  constexpr int NKS = S::BKE / 16;
 #pragma unroll
   for (int st = 0; st < S::NST - 1; ++st)
     if (st < nk) issue(st);
@@ -153,7 +158,7 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
     const char* sa = smem + (kt % S::NST) * S::STAGE;
     const char* sb = sa + S::BM * 128;
 #pragma unroll
-    for (int ks = 0; ks < S::BKE / 16; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       const int e = ks * 16 + 8 * (lane >> 5);
       F af[S::TM], bf[S::TN];
 #pragma unroll
