@@ -98,8 +98,8 @@ typedef struct gqe_config {
  *                                every 16-key group, key 8a+4u+r (a, u in
  *                                {0,1}, r < 4) sits at column 8u+4a+r, the
  *                                order in which the attention kernel feeds
- *                                keys to the matrix cores; columns of keys
- *                                >= L are unspecified
+ *                                keys to the matrix cores; the columns of
+ *                                keys >= L in the last tile are zero
  *   s       dtype [B, L, (k*G+2)*d_h]  slot vectors (input of W_O)
  *   the rest is private scratch (dispatch partial counts, tile maps). */
 typedef struct gqe_ws_layout {

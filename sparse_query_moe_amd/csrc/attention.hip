@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   struct Regs {
     uint4 k[S::K_CH], v[S::V_CH];
   };
-  Regs rs[PF];
+  Regs rs[PF > 0 ? PF : 1];
   auto gload = [&](Regs& r, int jt) {
     const int j0 = jt * S::BKV;
 #pragma unroll
@@ -198,8 +198,54 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
       *reinterpret_cast<uint4*>(vs_ + swz<S::VROW>(c / S::V_CPR, cc)) = mask_vt<T>(r.v[i], j0, cc, L);
     }
   };
-  gload(rs[0], tile_of(0));
-  if constexpr (PF > 1) gload(rs[PF - 1], tile_of(1));
+
+  // PF == 0: tiles go straight from global memory to LDS.  Wave w fills the
+  // 1 KB runs w, w + QW, ... of each tile (global_load_lds_dwordx4: lane i
+  // writes LDS bytes 16i..16i+15 of the run), each lane fetching the chunk
+  // that belongs there after the swizzle.  Keys past the sequence read row 0
+  // of K (their scores are masked) and the zero padding of the last V^T tile.
+  constexpr bool DL = PF == 0;
+  constexpr int KPW = S::KT / 1024 / QW, VPW = S::VT / 1024 / QW;  // runs per wave
+  static_assert(!DL || (NS == 1 && KPW * QW * 1024 == S::KT && VPW * QW * 1024 == S::VT),
+                "direct staging needs whole 1 KB runs per wave");
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  int k_row[DL ? KPW : 1], k_src[DL ? KPW : 1], v_src[DL ? VPW : 1];
+  if constexpr (DL) {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int off = (wave + QW * i) * 1024 + 16 * lane;
+      const int row = off / S::KROW, pch = (off % S::KROW) / 16;
+      k_row[i] = row;
+      k_src[i] = row * D + (pch ^ swz_xor<S::KROW>(row)) * S::EPC;
+    }
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+      const int off = (wave + QW * i) * 1024 + 16 * lane;
+      const int row = off / S::VROW, pch = (off % S::VROW) / 16;
+      v_src[i] = row * 64 + (pch ^ swz_xor<S::VROW>(row)) * S::EPC;
+    }
+  }
+  auto dl_issue = [&](int jt, int buf) {
+    const int j0 = jt * S::BKV;
+    char* ks_ = gsm + buf * S::STAGE;
+    char* vs_ = ks_ + S::KT;
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const size_t src = j0 + k_row[i] < L ? static_cast<size_t>(j0) * D + k_src[i]
+                                            : static_cast<size_t>(k_src[i] - k_row[i] * D);
+      dma16(Kg + src, ks_ + (swave + QW * i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < VPW; ++i)
+      dma16(Vg + static_cast<size_t>(jt) * D * 64 + v_src[i], vs_ + (swave + QW * i) * 1024);
+  };
+
+  if constexpr (DL) {
+    dl_issue(0, 0);
+  } else {
+    gload(rs[0], tile_of(0));
+    if constexpr (PF > 1) gload(rs[PF - 1], tile_of(1));
+  }
 
   // queries (pre-scaled) in registers; the running maximum starts at the score
   // against key 0, which every causal row sees, so it is finite from the start
@@ -235,47 +281,43 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
     }
   }
 
-  // one 64-key tile for this wave's QB query blocks
+  // one 64-key tile for this wave's QB query blocks.  The query blocks are
+  // staggered: S^T of every block is issued first (the MFMAs run on while the
+  // wave moves on), then block 0's softmax overlaps block 1's S^T, and block
+  // 1's softmax overlaps block 0's O^T update.
   auto tile = [&](const char* Ks, const char* Vs, int j0, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
     // S^T - m: the accumulator starts at -m_run, so exp2 applies directly
+    // (K fragments are read per block too: LDS bandwidth is cheaper than the
+    // registers that would hold them)
     f32x16 s[QB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int ks = 0; ks < S::NKS; ++ks) {
-        const F kf = LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half);
+      for (int kb = 0; kb < 2; ++kb) {
+        s[qb][kb] = splat16(-m_run[qb]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (ks == 0) s[qb][kb] = splat16(-m_run[qb]);  // S^T - m: exp2 applies directly
-          mma32(s[qb][kb], kf, qf[qb][ks]);
-        }
+        for (int ks = 0; ks < S::NKS; ++ks)
+          mma32(s[qb][kb], LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half),
+                qf[qb][ks]);
       }
-    if constexpr (MASK) {  // drop keys after the query
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      if constexpr (MASK) {  // drop keys after the query
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (j0 + 32 * kb + acc_row(i, lane) > qrow[qb]) s[qb][kb][i] = -INFINITY;
-    }
-    float mx[QB];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+      }
       float v = s[qb][0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) v = fmaxf(v, s[qb][kb][i]);
-      mx[qb] = fmaxf(v, __shfl_xor(v, 32, 64));
-      need = need || (mx[qb] > kRescaleThreshold);
-    }
-    if (__any(need)) {  // raise the running maximum (wave-uniform branch)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float sh = fmaxf(mx[qb], 0.f);
+      const float mx = fmaxf(v, __shfl_xor(v, 32, 64));
+      if (__any(mx > kRescaleThreshold)) {  // raise the running maximum (wave-uniform branch)
+        const float sh = fmaxf(mx, 0.f);
         const float alpha = __builtin_amdgcn_exp2f(-sh);
         m_run[qb] += sh;
         l_run[qb] *= alpha;
@@ -288,9 +330,6 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[qb][kb][i] -= sh;
       }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -301,23 +340,22 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
           ls += pv;
         }
       l_run[qb] += ls;
-    }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      F pf[QB];
+      for (int ks = 0; ks < 4; ++ks) {
+        const F pf = FragFromAcc<T>::get(s[qb][ks >> 1], 8 * (ks & 1));
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) pf[qb] = FragFromAcc<T>::get(s[qb][ks >> 1], 8 * (ks & 1));
-#pragma unroll
-      for (int db = 0; db < S::NDB; ++db) {
-        const F vf = LdsFrag<T, S::VROW>::get(Vs, 32 * db + (lane & 31), ks * 16 + 8 * half);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mma32(o[qb][db], vf, pf[qb]);
+        for (int db = 0; db < S::NDB; ++db)
+          mma32(o[qb][db], LdsFrag<T, S::VROW>::get(Vs, 32 * db + (lane & 31), ks * 16 + 8 * half), pf);
       }
     }
   };
 
-  if (tile_of(0) < ntiles) sstore(rs[0], 0, tile_of(0));
-  lds_barrier();
+  if constexpr (DL) {
+    dma_barrier(0);
+  } else {
+    if (tile_of(0) < ntiles) sstore(rs[0], 0, tile_of(0));
+    lds_barrier();
+  }
   // one round: compute tile jt from LDS buffer it & 1 while `fre` (already
   // stored) takes the load of round it + PF; `nxt` holds round it + 1
   auto step = [&](int it, Regs& nxt, Regs& fre) {
@@ -340,7 +378,21 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
     if (jn < ntiles) sstore(nxt, (it + 1) & 1, jn);
     lds_barrier();
   };
-  if constexpr (PF > 1) {
+  if constexpr (DL) {
+    for (int jt = 0; jt < ntiles; ++jt) {
+      if (jt + 1 < ntiles) dl_issue(jt + 1, (jt + 1) & 1);
+      const char* Ks = gsm + (jt & 1) * S::STAGE;
+      const char* Vs = Ks + S::KT;
+      const int j0 = jt * S::BKV;
+      if (wave_active && j0 <= wave_last) {
+        if (j0 + S::BKV - 1 <= qw0)
+          tile(Ks, Vs, j0, std::false_type{});
+        else
+          tile(Ks, Vs, j0, std::true_type{});
+      }
+      dma_barrier(0);
+    }
+  } else if constexpr (PF > 1) {
     for (int it = 0; it < rounds; it += 2) {
       step(it, rs[1], rs[0]);
       if (it + 1 < rounds) step(it + 1, rs[0], rs[1]);
@@ -444,21 +496,21 @@ hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream) {
   const bool wide = static_cast<long long>(p.L) * p.B * p.H >= 256LL * 256 * 4;
   if constexpr (sizeof(T) == 2) {
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1, 1>(p, stream)
+      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1, 0>(p, stream)
                            : launch_attention_d<T, 32, 1, 2, 4, 2>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1, 1>(p, stream)
+      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1, 0>(p, stream)
                            : launch_attention_d<T, 64, 1, 2, 4, 2>(p, stream);
-      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1, 1>(p, stream)
+      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1, 0>(p, stream)
                             : launch_attention_d<T, 128, 1, 2, 2, 2>(p, stream);
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1, 1>(p, stream)
+      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1, 0>(p, stream)
                            : launch_attention_d<T, 32, 1, 2, 4, 2>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1, 1>(p, stream)
+      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1, 0>(p, stream)
                            : launch_attention_d<T, 64, 1, 2, 2, 1>(p, stream);
-      case 128: return launch_attention_d<T, 128, 1, 4, 1, 1>(p, stream);
+      case 128: return launch_attention_d<T, 128, 1, 4, 1, 0>(p, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -123,11 +123,15 @@ template <> struct FragFromAcc<float> {
 // consecutive rows, so the chunk index is XORed with the row's index in units
 // of 256 bytes: any 16 consecutive rows then hit 16 different units.
 template <int ROWB>
-__device__ __forceinline__ int swz(int row, int chunk) {
+__device__ __forceinline__ int swz_xor(int row) {
   constexpr int CPR = ROWB / 16;                       // chunks per row
   constexpr int RP = ROWB >= 256 ? 1 : 256 / ROWB;     // rows per 256 bytes
   constexpr int mask = CPR < 16 ? CPR - 1 : 15;
-  return row * ROWB + ((chunk ^ ((row / RP) & mask)) << 4);
+  return (row / RP) & mask;
+}
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * ROWB + ((chunk ^ swz_xor<ROWB>(row)) << 4);
 }
 
 // 8 K-elements of row `row`, starting at element `elem`, from a swizzled LDS
@@ -165,6 +169,58 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// wait until at most n of this wave's vector-memory operations are in flight
+// (and all its LDS operations are done); n is small and known per call site
+__device__ __forceinline__ void wait_vm(int n) {
+#define GQE_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4))
+  switch (n) {
+    case 0: GQE_VM(0); break;
+    case 1: GQE_VM(1); break;
+    case 2: GQE_VM(2); break;
+    case 3: GQE_VM(3); break;
+    case 4: GQE_VM(4); break;
+    case 5: GQE_VM(5); break;
+    case 6: GQE_VM(6); break;
+    case 7: GQE_VM(7); break;
+    case 8: GQE_VM(8); break;
+    case 9: GQE_VM(9); break;
+    case 10: GQE_VM(10); break;
+    case 11: GQE_VM(11); break;
+    case 12: GQE_VM(12); break;
+    case 13: GQE_VM(13); break;
+    case 14: GQE_VM(14); break;
+    case 15: GQE_VM(15); break;
+    case 16: GQE_VM(16); break;
+    case 17: GQE_VM(17); break;
+    case 18: GQE_VM(18); break;
+    case 19: GQE_VM(19); break;
+    case 20: GQE_VM(20); break;
+    case 21: GQE_VM(21); break;
+    case 22: GQE_VM(22); break;
+    case 23: GQE_VM(23); break;
+    case 24: GQE_VM(24); break;
+    default: GQE_VM(0); break;
+  }
+#undef GQE_VM
+}
+
+// direct global-to-LDS copy of 16 bytes per lane: lane i's src lands at LDS
+// bytes lds + 16 i .. lds + 16 i + 15 (lds must be wave-uniform: it goes
+// through M0).  A plain (non-template) device function, so that kernels whose
+// bodies use it keep their host-side launch stubs.
+__device__ __forceinline__ void dma16(const void* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, GQE_LDS(lds), 16, 0, 0);
+}
+
+// barrier after which every wave's direct global-to-LDS loads issued before
+// it have landed (each wave first waits for its own); no fence, which would
+// also wait for unrelated loads
+__device__ __forceinline__ void dma_barrier(int pending) {
+  wait_vm(pending);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace gqe

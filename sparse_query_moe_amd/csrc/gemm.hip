@@ -50,41 +50,6 @@ struct GemmShape {
   static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
 };
 
-// wait until at most n of this wave's vector-memory operations are in flight
-// (and all its LDS operations are done); n is small and known per call site
-__device__ __forceinline__ void wait_vm(int n) {
-#define GQE_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4))
-  switch (n) {
-    case 0: GQE_VM(0); break;
-    case 1: GQE_VM(1); break;
-    case 2: GQE_VM(2); break;
-    case 3: GQE_VM(3); break;
-    case 4: GQE_VM(4); break;
-    case 5: GQE_VM(5); break;
-    case 6: GQE_VM(6); break;
-    case 7: GQE_VM(7); break;
-    case 8: GQE_VM(8); break;
-    case 9: GQE_VM(9); break;
-    case 10: GQE_VM(10); break;
-    case 11: GQE_VM(11); break;
-    case 12: GQE_VM(12); break;
-    case 13: GQE_VM(13); break;
-    case 14: GQE_VM(14); break;
-    case 15: GQE_VM(15); break;
-    case 16: GQE_VM(16); break;
-    case 17: GQE_VM(17); break;
-    case 18: GQE_VM(18); break;
-    case 19: GQE_VM(19); break;
-    case 20: GQE_VM(20); break;
-    case 21: GQE_VM(21); break;
-    case 22: GQE_VM(22); break;
-    case 23: GQE_VM(23); break;
-    case 24: GQE_VM(24); break;
-    default: GQE_VM(0); break;
-  }
-#undef GQE_VM
-}
-
 // The main loop: P supplies K (a multiple of S::BKE), a_row(r) and b_row(n)
 // (row pointers, or nullptr for rows outside the problem), a_any() (any valid
 // row, loaded in place of missing ones: their results are never written) and
@@ -127,11 +92,10 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
     char* st = smem + (kt % S::NST) * S::STAGE;
 #pragma unroll
     for (int i = 0; i < S::A_CH; ++i)
-      __builtin_amdgcn_global_load_lds(ap[i] + kt * S::BKE, GQE_LDS(st + (4 * i + swave) * 1024), 16, 0, 0);
+      dma16(ap[i] + kt * S::BKE, st + (4 * i + swave) * 1024);
 #pragma unroll
     for (int i = 0; i < S::B_CH; ++i)
-      __builtin_amdgcn_global_load_lds(bp[i] + kt * S::BKE,
-                                       GQE_LDS(st + S::BM * 128 + (4 * i + swave) * 1024), 16, 0, 0);
+      dma16(bp[i] + kt * S::BKE, st + S::BM * 128 + (4 * i + swave) * 1024);
   };
 
   f32x16 acc[S::TM][S::TN];
@@ -282,6 +246,27 @@ struct DenseProb {
           if (mj >= a.M) continue;
           const int bj = mj / a.L, tj = mj % a.L;
           out[vt_index(bj, sg.heads, hh, dd, tj & ~15) + vt_col(tj & 15)] = ct[key_of(j) * S::LDC + nl];
+        }
+      }
+    }
+    // the columns of keys L .. 64*tiles-1 of the last tile are written as
+    // zeros, so that whole tiles can be staged without masking V
+    const int rem = a.L & 63;
+    if (rem != 0) {
+      const int b_hi = min(a.M - 1, m0 + S::BM - 1) / a.L;
+      for (int b = m0 / a.L; b <= b_hi; ++b) {
+        const int last = b * a.L + a.L - 1;  // the block holding a sequence's last token pads it
+        if (last < m0 || last >= m0 + S::BM || last >= a.M) continue;
+        const int t_tile = (a.L - 1) & ~63;
+        for (int c = threadIdx.x; c < (64 - rem) * S::BN; c += 256) {
+          const int nl = c % S::BN, p = rem + c / S::BN;
+          const int col = n0 + nl;
+          if (col >= a.N) continue;
+          const ProjSeg sg = seg_of(col);
+          if (!sg.transposed) continue;
+          const int cl = col - sg.n_begin;
+          const int hh = sg.head_base + cl / a.D, dd = cl % a.D;
+          static_cast<T*>(sg.out)[vt_index(b, sg.heads, hh, dd, t_tile + (p & ~15)) + vt_col(p & 15)] = T(0);
         }
       }
     }
