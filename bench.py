@@ -300,8 +300,8 @@ def cpu_baseline(wl, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="l2k", choices=sorted(W.WORKLOADS))
     ap.add_argument("--lengths", default="b4_l8k,l128k",
                     help="other workloads timed for the per-length speed-up (comma list, '' = none)")

@@ -16,8 +16,9 @@
  * ---------------------------------------
  *  - Every pointer is a DEVICE pointer owned by the caller, except `cfg` and
  *    `layout`, which are host pointers read (or written) before the call
- *    returns.  The library never allocates or frees memory and keeps no
- *    global mutable state: calls are reentrant.
+ *    returns.  The library never allocates or frees device memory.  Its only
+ *    global state is the per-device side stream and events of gqe_forward
+ *    (behind a mutex); every call is thread-safe.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream).  No call synchronizes the host.  The status returned
  *    reports argument errors only (nothing is launched then); a fault inside
@@ -152,8 +153,16 @@ int gqe_attention(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipSt
 int gqe_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace,
                size_t ws_bytes, hipStream_t stream);
 
-/* The whole GQE prefill layer: gqe_route, gqe_dispatch, gqe_project,
- * gqe_attention, gqe_output in that order on `stream`. */
+/* The whole GQE prefill layer: the work of gqe_route, gqe_dispatch,
+ * gqe_project, gqe_attention and gqe_output, ordered on `stream`.  The dense
+ * part of the projection (shared-head Q, K, V^T) does not depend on the
+ * routing; it runs concurrently with routing, dispatch and the gathered Q
+ * projection on a second stream of the same device (created on first use and
+ * kept for the life of the process), forked from and joined back into
+ * `stream` with events, so the call is ordered after all earlier work on
+ * `stream` and later work on `stream` sees all of it.  It works under HIP
+ * graph capture of `stream` once a first call outside capture has created
+ * that stream.  Concurrent calls serialize on a mutex while they enqueue. */
 int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
                 const void* Wv, const void* Wr, const void* Wo, void* out,
                 void* workspace, size_t ws_bytes, hipStream_t stream);

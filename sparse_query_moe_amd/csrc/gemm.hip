@@ -450,10 +450,27 @@ static hipError_t launch_gemm(Kern kern, dim3 grid, hipStream_t stream, const Ar
   return hipGetLastError();
 }
 
+// Launches whose blocks all fit on the chip at once get four LDS stages (three
+// K steps in flight: latency hiding within the block); larger ones get two
+// stages, so that two blocks share a CU and hide each other's prologue and
+// epilogue.
+int cu_count() {
+  static int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return v;
+  }();
+  return n;
+}
+inline bool deep_ring(long long blocks) { return blocks <= cu_count(); }
+
 template <typename T>
 hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
                              const ProjSeg* segs, int nseg, hipStream_t stream) {
   typedef GemmShape<T, 128, 128, 2, 2> S;
+  typedef GemmShape<T, 128, 128, 2, 2, 4> S4;
   DenseArgs a;
   a.x = x;
   a.M = M;
@@ -470,6 +487,8 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_
   a.N = N;
   if (M == 0 || N == 0) return hipSuccess;
   const dim3 grid((N + S::BN - 1) / S::BN, (M + S::BM - 1) / S::BM);
+  if (deep_ring(static_cast<long long>(grid.x) * grid.y))
+    return launch_gemm<S4>(dense_proj_kernel<T, S4>, grid, stream, a);
   return launch_gemm<S>(dense_proj_kernel<T, S>, grid, stream, a);
 }
 
@@ -477,6 +496,9 @@ template <typename T, int D>
 static hipError_t launch_gather_q_d(const GatherArgs& a, int tiles_per_bg, int n_bg,
                                     hipStream_t stream) {
   typedef GemmShape<T, kGatherRows, D, (D >= 128 ? 2 : 4), (D >= 128 ? 2 : 1)> S;
+  typedef GemmShape<T, kGatherRows, D, (D >= 128 ? 2 : 4), (D >= 128 ? 2 : 1), 4> S4;
+  if (deep_ring(static_cast<long long>(tiles_per_bg) * n_bg))
+    return launch_gemm<S4>(gather_q_kernel<T, S4>, dim3(tiles_per_bg, n_bg), stream, a);
   return launch_gemm<S>(gather_q_kernel<T, S>, dim3(tiles_per_bg, n_bg), stream, a);
 }
 
@@ -515,6 +537,7 @@ template <typename T>
 hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream) {
   typedef GemmShape<T, 128, 128, 2, 2> S;
+  typedef GemmShape<T, 128, 128, 2, 2, 4> S4;
   OutArgs a;
   a.a = a_;
   a.w = wo;
@@ -524,6 +547,8 @@ hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K
   a.K = K;
   if (M == 0 || N == 0) return hipSuccess;
   const dim3 grid((N + S::BN - 1) / S::BN, (M + S::BM - 1) / S::BM);
+  if (deep_ring(static_cast<long long>(grid.x) * grid.y))
+    return launch_gemm<S4>(out_proj_kernel<T, S4>, grid, stream, a);
   return launch_gemm<S>(out_proj_kernel<T, S>, grid, stream, a);
 }
 

@@ -302,6 +302,46 @@ def test_determinism(gqe):
                           vt_decode(v2["vt"].view(torch.int16).cpu().numpy(), L))
 
 
+def test_forward_equals_stages_and_graph_replay(gqe):
+    """gqe_forward (dense projection forked to a second stream) gives the same
+    bits as the five stage calls on one stream, and so does every replay of a
+    HIP graph captured from it, with eager work and synchronizations between
+    the replays."""
+    wl, I = inputs("l2k")
+    dev = device_inputs(wl, I)
+    cfg, ws, y_fwd = run_gqe(gqe, wl, I, dev)
+    ws2 = gqe.alloc_workspace(cfg)
+    y_st = torch.empty_like(y_fwd)
+    gqe.gqe_route(cfg, dev["x"], dev["wr"], ws2)
+    gqe.gqe_dispatch(cfg, ws2)
+    gqe.gqe_project(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], ws2)
+    gqe.gqe_attention(cfg, ws2)
+    gqe.gqe_output(cfg, dev["wo"], y_st, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fwd.view(torch.int16), y_st.view(torch.int16))
+
+    ws3 = gqe.alloc_workspace(cfg)
+    y_g = torch.empty_like(y_fwd)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], y_g, ws3)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], y_g, ws3)
+    for rep in range(3):
+        y_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g.view(torch.int16), y_fwd.view(torch.int16)), f"replay {rep}"
+        # eager work in between
+        gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], y_st, ws2)
+        torch.cuda.synchronize()
+    del graph
+
+
 @pytest.mark.parametrize("L,B,G,E,k,D,dtype", [
     (1, 1, 4, 4, 2, 64, "bf16"),
     (65, 2, 4, 4, 2, 64, "bf16"),
