@@ -52,8 +52,6 @@ struct AttnShape {
   static constexpr int VROW = BKV * static_cast<int>(sizeof(T));  // bytes per V^T tile row (a dim)
   static constexpr int KT = BKV * KROW, VT = D * VROW;
   static constexpr int STAGE = KT + VT;
-  static constexpr int K_CPR = KROW / 16, V_CPR = VROW / 16;  // 16-byte chunks per row
-  static constexpr int K_CH = BKV * K_CPR / NT, V_CH = D * V_CPR / NT;
   static constexpr int NDB = D / 32;  // 32-row blocks of O^T
   static constexpr int NKS = D / 16;  // K-steps of S^T
   // partial state of one wave in the merge area: o (NDB*16), m, l per lane
@@ -61,38 +59,7 @@ struct AttnShape {
   static constexpr int KV_LDS = NS * 2 * STAGE;
   static constexpr int MERGE_LDS = (NS - 1) * QW * QB * PART * 4;
   static constexpr int LDS = KV_LDS > MERGE_LDS ? KV_LDS : MERGE_LDS;
-  static_assert(K_CH >= 1 && V_CH >= 1, "tile smaller than one chunk per thread");
-  static_assert(BKV * K_CPR % NT == 0 && D * V_CPR % NT == 0, "uneven tile split");
 };
-
-// V^T arrives in HBM already in the order the MFMA wants (inside every 16-key
-// group, key 8a+4u+r at column 8u+4a+r), so a 16-byte chunk goes to LDS as is.
-// Logical key of element e of chunk cc (chunk of EPC columns) of a tile:
-template <typename T>
-__device__ __forceinline__ int vt_key(int cc, int e) {
-  if constexpr (sizeof(T) == 2) {  // 8 columns = half u of a 16-key group
-    const int g16 = cc >> 1, u = cc & 1;
-    return 16 * g16 + 4 * u + (e & 3) + 8 * (e >> 2);
-  } else {  // 4 columns = quarter (u, a) of a 16-key group
-    const int g16 = cc >> 2, u = (cc >> 1) & 1, a = cc & 1;
-    return 16 * g16 + 8 * a + 4 * u + e;
-  }
-}
-
-// zero the elements of V^T chunk cc of the tile starting at key j0 whose keys
-// are >= L (a chunk never leaves its 16-key group)
-template <typename T>
-__device__ __forceinline__ uint4 mask_vt(uint4 v, int j0, int cc, int L) {
-  constexpr int EPC = 16 / static_cast<int>(sizeof(T));
-  const int g0 = j0 + 16 * (cc / (16 / EPC));
-  if (g0 + 16 <= L) return v;
-  if (g0 >= L) return zero4();
-  T* e = reinterpret_cast<T*>(&v);
-#pragma unroll
-  for (int j = 0; j < EPC; ++j)
-    if (j0 + vt_key<T>(cc, j) >= L) e[j] = T(0);
-  return v;
-}
 
 // q . scale * log2(e), rounded back to the storage type: scores come out of the
 // MFMA already in log2 units.
@@ -117,7 +84,7 @@ __device__ __forceinline__ float dot8(const f32x8& a, const f32x8& b) {
   return s;
 }
 
-template <typename T, int D, int QB, int QW, int NS, int PF>
+template <typename T, int D, int QB, int QW, int NS>
 __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) void attention_kernel(
     AttnParams p) {
   typedef AttnShape<T, D, QB, QW, NS> S;
@@ -154,76 +121,29 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   const int rounds = (ntiles + NS - 1) / NS;
   auto tile_of = [&](int it) { return it * NS + grp; };  // tile of round it
 
-  // K/V tile staging: raw 16-byte global loads into registers (addresses
-  // clamped into the sequence, so a load never depends on a branch), then
-  // masked (keys >= L become 0) and stored to LDS.  With PF = 2 two register
-  // sets keep the tiles of the next two rounds in flight.
-  struct Regs {
-    uint4 k[S::K_CH], v[S::V_CH];
-  };
-  Regs rs[PF > 0 ? PF : 1];
-  auto gload = [&](Regs& r, int jt) {
-    const int j0 = jt * S::BKV;
-#pragma unroll
-    for (int i = 0; i < S::K_CH; ++i) {
-      const int c = tid + S::NT * i;
-      const int row = c / S::K_CPR, cc = c % S::K_CPR;
-      const int key = j0 + row < L ? j0 + row : 0;
-      r.k[i] = *reinterpret_cast<const uint4*>(Kg + static_cast<size_t>(key) * D + cc * S::EPC);
-    }
-#pragma unroll
-    for (int i = 0; i < S::V_CH; ++i) {
-      const int c = tid + S::NT * i;
-      const int row = c / S::V_CPR, cc = c % S::V_CPR;
-      const int jv = j0 < L ? jt : 0;  // tiles past the sequence read tile 0
-      r.v[i] = *reinterpret_cast<const uint4*>(Vg + (static_cast<size_t>(jv) * D + row) * 64 +
-                                               cc * S::EPC);
-    }
-  };
-  auto sstore = [&](const Regs& r, int buf, int jt) {
-    const int j0 = jt * S::BKV;
-    char* ks_ = gsm + buf * S::STAGE;
-    char* vs_ = ks_ + S::KT;
-#pragma unroll
-    for (int i = 0; i < S::K_CH; ++i) {
-      const int c = tid + S::NT * i;
-      const int row = c / S::K_CPR;
-      *reinterpret_cast<uint4*>(ks_ + swz<S::KROW>(row, c % S::K_CPR)) =
-          j0 + row < L ? r.k[i] : zero4();
-    }
-#pragma unroll
-    for (int i = 0; i < S::V_CH; ++i) {
-      const int c = tid + S::NT * i;
-      const int cc = c % S::V_CPR;
-      *reinterpret_cast<uint4*>(vs_ + swz<S::VROW>(c / S::V_CPR, cc)) = mask_vt<T>(r.v[i], j0, cc, L);
-    }
-  };
-
-  // PF == 0: tiles go straight from global memory to LDS.  Wave w fills the
-  // 1 KB runs w, w + QW, ... of each tile (global_load_lds_dwordx4: lane i
-  // writes LDS bytes 16i..16i+15 of the run), each lane fetching the chunk
-  // that belongs there after the swizzle.  Keys past the sequence read row 0
-  // of K (their scores are masked) and the zero padding of the last V^T tile.
-  constexpr bool DL = PF == 0;
+  // K/V^T tiles go straight from global memory to LDS.  Wave w of a group
+  // fills the 1 KB runs w, w + QW, ... of each tile (global_load_lds_dwordx4:
+  // lane i writes LDS bytes 16i..16i+15 of the run), each lane fetching the
+  // chunk that belongs there after the swizzle, so staging costs neither
+  // VGPRs nor VALU work.  Keys past the sequence read row 0 of K (their
+  // scores are masked) and the zero padding of the last V^T tile.
   constexpr int KPW = S::KT / 1024 / QW, VPW = S::VT / 1024 / QW;  // runs per wave
-  static_assert(!DL || (NS == 1 && KPW * QW * 1024 == S::KT && VPW * QW * 1024 == S::VT),
+  static_assert(KPW * QW * 1024 == S::KT && VPW * QW * 1024 == S::VT,
                 "direct staging needs whole 1 KB runs per wave");
   const int swave = __builtin_amdgcn_readfirstlane(wave);
-  int k_row[DL ? KPW : 1], k_src[DL ? KPW : 1], v_src[DL ? VPW : 1];
-  if constexpr (DL) {
+  int k_row[KPW], k_src[KPW], v_src[VPW];
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      const int off = (wave + QW * i) * 1024 + 16 * lane;
-      const int row = off / S::KROW, pch = (off % S::KROW) / 16;
-      k_row[i] = row;
-      k_src[i] = row * D + (pch ^ swz_xor<S::KROW>(row)) * S::EPC;
-    }
+  for (int i = 0; i < KPW; ++i) {
+    const int off = (wave + QW * i) * 1024 + 16 * lane;
+    const int row = off / S::KROW, pch = (off % S::KROW) / 16;
+    k_row[i] = row;
+    k_src[i] = row * D + (pch ^ swz_xor<S::KROW>(row)) * S::EPC;
+  }
 #pragma unroll
-    for (int i = 0; i < VPW; ++i) {
-      const int off = (wave + QW * i) * 1024 + 16 * lane;
-      const int row = off / S::VROW, pch = (off % S::VROW) / 16;
-      v_src[i] = row * 64 + (pch ^ swz_xor<S::VROW>(row)) * S::EPC;
-    }
+  for (int i = 0; i < VPW; ++i) {
+    const int off = (wave + QW * i) * 1024 + 16 * lane;
+    const int row = off / S::VROW, pch = (off % S::VROW) / 16;
+    v_src[i] = row * 64 + (pch ^ swz_xor<S::VROW>(row)) * S::EPC;
   }
   auto dl_issue = [&](int jt, int buf) {
     const int j0 = jt * S::BKV;
@@ -240,12 +160,7 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
       dma16(Vg + static_cast<size_t>(jt) * D * 64 + v_src[i], vs_ + (swave + QW * i) * 1024);
   };
 
-  if constexpr (DL) {
-    dl_issue(0, 0);
-  } else {
-    gload(rs[0], tile_of(0));
-    if constexpr (PF > 1) gload(rs[PF - 1], tile_of(1));
-  }
+  if (tile_of(0) < ntiles) dl_issue(tile_of(0), 0);
 
   // queries (pre-scaled) in registers; the running maximum starts at the score
   // against key 0, which every causal row sees, so it is finite from the start
@@ -350,22 +265,11 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
     }
   };
 
-  if constexpr (DL) {
-    dma_barrier(0);
-  } else {
-    if (tile_of(0) < ntiles) sstore(rs[0], 0, tile_of(0));
-    lds_barrier();
-  }
-  // one round: compute tile jt from LDS buffer it & 1 while `fre` (already
-  // stored) takes the load of round it + PF; `nxt` holds round it + 1
-  auto step = [&](int it, Regs& nxt, Regs& fre) {
+  dma_barrier(0);
+  for (int it = 0; it < rounds; ++it) {
     const int jt = tile_of(it);
     const int jn = it + 1 < rounds ? tile_of(it + 1) : ntiles;  // next round's tile
-    if constexpr (PF > 1) {
-      gload(fre, tile_of(it + 2));
-    } else {
-      if (jn < ntiles) gload(nxt, jn);
-    }
+    if (jn < ntiles) dl_issue(jn, (it + 1) & 1);
     const char* Ks = gsm + (it & 1) * S::STAGE;
     const char* Vs = Ks + S::KT;
     const int j0 = jt * S::BKV;
@@ -375,30 +279,7 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
       else
         tile(Ks, Vs, j0, std::true_type{});
     }
-    if (jn < ntiles) sstore(nxt, (it + 1) & 1, jn);
-    lds_barrier();
-  };
-  if constexpr (DL) {
-    for (int jt = 0; jt < ntiles; ++jt) {
-      if (jt + 1 < ntiles) dl_issue(jt + 1, (jt + 1) & 1);
-      const char* Ks = gsm + (jt & 1) * S::STAGE;
-      const char* Vs = Ks + S::KT;
-      const int j0 = jt * S::BKV;
-      if (wave_active && j0 <= wave_last) {
-        if (j0 + S::BKV - 1 <= qw0)
-          tile(Ks, Vs, j0, std::false_type{});
-        else
-          tile(Ks, Vs, j0, std::true_type{});
-      }
-      dma_barrier(0);
-    }
-  } else if constexpr (PF > 1) {
-    for (int it = 0; it < rounds; it += 2) {
-      step(it, rs[1], rs[0]);
-      if (it + 1 < rounds) step(it + 1, rs[0], rs[1]);
-    }
-  } else {
-    for (int it = 0; it < rounds; ++it) step(it, rs[0], rs[0]);
+    dma_barrier(0);
   }
 
   if constexpr (NS > 1) {
@@ -468,7 +349,7 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   }
 }
 
-template <typename T, int D, int QB, int QW, int NS, int PF>
+template <typename T, int D, int QB, int QW, int NS>
 hipError_t launch_attention_d(const AttnParams& p, hipStream_t stream) {
   typedef AttnShape<T, D, QB, QW, NS> S;
   const int nq = (p.L + S::BQ - 1) / S::BQ;
@@ -476,11 +357,11 @@ hipError_t launch_attention_d(const AttnParams& p, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (S::LDS > 65536) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attention_kernel<T, D, QB, QW, NS, PF>),
+        reinterpret_cast<const void*>(&attention_kernel<T, D, QB, QW, NS>),
         hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((attention_kernel<T, D, QB, QW, NS, PF>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((attention_kernel<T, D, QB, QW, NS>), dim3(static_cast<unsigned>(blocks)),
                      dim3(S::THREADS), S::LDS, stream, p);
   return hipGetLastError();
 }
@@ -496,21 +377,21 @@ hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream) {
   const bool wide = static_cast<long long>(p.L) * p.B * p.H >= 256LL * 256 * 4;
   if constexpr (sizeof(T) == 2) {
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1, 0>(p, stream)
-                           : launch_attention_d<T, 32, 1, 2, 4, 2>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1, 0>(p, stream)
-                           : launch_attention_d<T, 64, 1, 2, 4, 2>(p, stream);
-      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1, 0>(p, stream)
-                            : launch_attention_d<T, 128, 1, 2, 2, 2>(p, stream);
+      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1>(p, stream)
+                           : launch_attention_d<T, 32, 1, 2, 4>(p, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1>(p, stream)
+                           : launch_attention_d<T, 64, 1, 2, 4>(p, stream);
+      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1>(p, stream)
+                            : launch_attention_d<T, 128, 1, 2, 2>(p, stream);
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1, 0>(p, stream)
-                           : launch_attention_d<T, 32, 1, 2, 4, 2>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1, 0>(p, stream)
-                           : launch_attention_d<T, 64, 1, 2, 2, 1>(p, stream);
-      case 128: return launch_attention_d<T, 128, 1, 4, 1, 0>(p, stream);
+      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1>(p, stream)
+                           : launch_attention_d<T, 32, 1, 2, 4>(p, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1>(p, stream)
+                           : launch_attention_d<T, 64, 1, 2, 2>(p, stream);
+      case 128: return launch_attention_d<T, 128, 1, 4, 1>(p, stream);
       default: return hipErrorInvalidValue;
     }
   }
