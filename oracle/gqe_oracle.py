@@ -241,13 +241,48 @@ def output_projection(s: np.ndarray, wo: np.ndarray) -> np.ndarray:
     return s @ wo.T
 
 
+# Output constructions compared in the ablation of [pptc] section 4.3 (Table 1):
+#   "full"            the GQE layer: hard slots, the always-on shared head and the
+#                     renormalized weighted slot; W_O has (k*G+2)*d_h inputs.
+#   "hard"            hard concatenation only: the k*G selected experts' outputs,
+#                     no weighted slot and no shared head (the full layer is
+#                     described as this plus the renormalized slot and the shared
+#                     head); W_O has k*G*d_h inputs.
+#   "weighted_concat" the hard slots, each scaled by its expert's in-group softmax
+#                     probability p (not renormalized over the k), and no further
+#                     slot or shared head; W_O has k*G*d_h inputs.  (The page says
+#                     the weights may be the in-group probabilities; that is the
+#                     reading taken.)
+OUTPUT_MODES = ("full", "hard", "weighted_concat")
+
+
+def slot_width(mode: str, n_groups: int, top_k: int, head_dim: int) -> int:
+    """Width of the slot vector that W_O projects, per output construction."""
+    return (top_k * n_groups + (2 if mode == "full" else 0)) * head_dim
+
+
+def ablation_slots(mode: str, o_hard: np.ndarray, p_sel: np.ndarray) -> np.ndarray:
+    """Slot vector of the "hard" and "weighted_concat" constructions.
+
+    o_hard [n, G, k, d_h]; p_sel [n, G, k] the in-group softmax probability of
+    each selected expert.  Group-major, rank-minor, like the full layer's hard
+    slots.
+    """
+    n = o_hard.shape[0]
+    if mode == "hard":
+        return o_hard.reshape(n, -1)
+    if mode == "weighted_concat":
+        return (p_sel[..., None] * o_hard).reshape(n, -1)
+    raise ValueError(mode)
+
+
 # --------------------------------------------------------------------------
 # full layer
 # --------------------------------------------------------------------------
 
 
 def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
-                shared_kv_group=0, scale=None, positions=None):
+                shared_kv_group=0, scale=None, positions=None, output_mode="full"):
     """GQE prefill forward (steps 1-11) in float64.
 
     x: [B, L, d]; wq [(G*E+1)*d_h, d]; wk, wv [G*d_h, d]; wr [G*E, d];
@@ -259,7 +294,14 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
     (slot-head order: hard slot g*k+j, then the shared head), k_ and v
     ([B,G,upto,d_h]), o [B,n,k*G+1,d_h] (attention outputs), s
     [B,n,(k*G+2)*d_h] (slot vectors) and y [B,n,d].
+
+    ``output_mode`` picks one of OUTPUT_MODES; the "hard" and "weighted_concat"
+    constructions have no shared head (q and o then hold the k*G hard
+    slot-heads only) and a W_O of k*G*d_h inputs.
     """
+    if output_mode not in OUTPUT_MODES:
+        raise ValueError(output_mode)
+    full = output_mode == "full"
     B, L, d = x.shape
     G, E, k, dh = n_groups, n_experts, top_k, head_dim
     scale = 1.0 / math.sqrt(dh) if scale is None else scale
@@ -272,10 +314,10 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
     idx, w = idx.reshape(B, L, G, k), w.reshape(B, L, G, k)
     counts, offsets, pos, slot = dispatch(idx, E)
 
-    S = k * G + 1                                         # attention slot-heads
+    S = k * G + (1 if full else 0)                        # attention slot-heads
     q_all = np.empty((B, n, S, dh))
     o_all = np.empty((B, n, S, dh))
-    s_all = np.empty((B, n, (k * G + 2) * dh))
+    s_all = np.empty((B, n, slot_width(output_mode, G, k, dh)))
     K_all = np.empty((B, G, upto, dh))
     V_all = np.empty((B, G, upto, dh))
     for b in range(B):
@@ -294,11 +336,15 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
                         qh[m] = xq[m] @ head_rows(wq, expert_head(g, e, E), dh).T
                 q_all[b, :, g * k + j] = qh
                 o_hard[:, g, j] = causal_attention(qh, pos_q, K_all[b, g], V_all[b, g], scale)
+        o_all[b, :, :k * G] = o_hard.reshape(n, G * k, dh)
+        if not full:
+            p_sel = np.take_along_axis(p[b, pos_q], idx[b, pos_q].astype(np.int64), axis=-1)
+            s_all[b] = ablation_slots(output_mode, o_hard, p_sel)
+            continue
         q_sh = xq @ head_rows(wq, G * E, dh).T            # step 8: always-on shared head
         o_sh = causal_attention(q_sh, pos_q, K_all[b, shared_kv_group],
                                 V_all[b, shared_kv_group], scale)
         q_all[b, :, k * G] = q_sh
-        o_all[b, :, :k * G] = o_hard.reshape(n, G * k, dh)
         o_all[b, :, k * G] = o_sh
         o_w = weighted_slot(w[b, pos_q], o_hard)
         s_all[b] = slot_vector(o_hard, o_sh, o_w)

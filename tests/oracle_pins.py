@@ -377,6 +377,56 @@ def pin_sampled_rows_match_full(orc):
     assert np.array_equal(full["idx"], part["idx"])
 
 
+
+# ---------------------------------------------------------------------------
+# Ablation output constructions ([pptc] section 4.3)
+# ---------------------------------------------------------------------------
+
+def pin_ablation_constructions(orc):
+    """The "hard" construction is the full layer's hard slots alone: with the
+    shared and weighted columns of W_O zeroed the full layer gives the same y
+    (and the shared head contributes nothing).  With W_r = 0 every in-group
+    probability is 1/E, so "weighted_concat" is "hard" divided by E (not by k,
+    which renormalized weights would give).  At t = 0 both reduce to each
+    group's V[0], scaled by p in "weighted_concat"."""
+    rng = np.random.default_rng(31)
+    t = tiny_layer(rng, B=2, L=6, G=2, E=3, k=2)
+    G, E, k, dh = t["G"], t["E"], t["k"], t["dh"]
+    kG = k * G
+    wo_hard = t["wo"][:, :kG * dh].copy()
+    full_zeroed = dict(t)
+    full_zeroed["wo"] = t["wo"].copy()
+    full_zeroed["wo"][:, kG * dh:] = 0.0
+    y_full = run(orc, full_zeroed)["y"]
+    th = dict(t)
+    th["wo"] = wo_hard
+    hard = run(orc, th, output_mode="hard")
+    assert hard["s"].shape[-1] == kG * dh and hard["q"].shape[2] == kG
+    assert np.allclose(hard["y"], y_full, rtol=0, atol=1e-12)
+
+    t0 = dict(th)
+    t0["wr"] = np.zeros_like(t["wr"])
+    t0["br"] = np.zeros_like(t["br"])
+    y_h = run(orc, t0, output_mode="hard")["y"]
+    y_w = run(orc, t0, output_mode="weighted_concat")["y"]
+    assert np.allclose(y_w, y_h / E, rtol=0, atol=1e-12)
+
+    t1 = dict(th)
+    t1["br"] = rng.standard_normal(t["br"].shape)
+    res = run(orc, t1, output_mode="weighted_concat")
+    for b in range(2):
+        v0 = [t["x"][b, 0] @ t["wv"][g * dh:(g + 1) * dh].T for g in range(G)]
+        r0 = t["x"][b, 0] @ t["wr"].T + t1["br"]
+        slots = []
+        for g in range(G):
+            rg = r0[g * E:(g + 1) * E]
+            pg = np.exp(rg - rg.max()) / np.exp(rg - rg.max()).sum()
+            order = sorted(range(E), key=lambda e: (-rg[e], e))[:k]
+            slots += [pg[e] * v0[g] for e in order]
+        ref = np.concatenate(slots) @ wo_hard.T
+        assert np.allclose(res["y"][b, 0], ref, rtol=0, atol=1e-12), np.abs(res["y"][b, 0] - ref).max()
+
+
 ALL_PINS = [
     pin_k_equals_e_is_dense_gqa,
     pin_weights_sum_to_one,
@@ -394,4 +444,5 @@ ALL_PINS = [
     pin_value_scaling,
     pin_causality,
     pin_sampled_rows_match_full,
+    pin_ablation_constructions,
 ]

@@ -170,6 +170,29 @@ def m_head_rows_shifted(mod):
         if (head + 1) * dh + 1 <= w.shape[0] else w[head * dh:(head + 1) * dh]
 
 
+def m_wconcat_renormalized(mod):
+    """weighted_concat scales by the renormalized weights instead of p."""
+    orig = mod.ablation_slots
+
+    def slots(mode, o_hard, p_sel):
+        if mode == "weighted_concat":
+            p_sel = p_sel / p_sel.sum(axis=-1, keepdims=True)
+        return orig(mode, o_hard, p_sel)
+    mod.ablation_slots = slots
+
+
+def m_wconcat_unscaled(mod):
+    """weighted_concat forgets the scaling (same as hard)."""
+    orig = mod.ablation_slots
+    mod.ablation_slots = lambda mode, o_hard, p_sel: orig("hard", o_hard, p_sel)
+
+
+def m_hard_rank_reversed(mod):
+    """the ablation constructions list the hard slots in reverse rank order."""
+    orig = mod.ablation_slots
+    mod.ablation_slots = lambda mode, o_hard, p_sel: orig(mode, o_hard[:, :, ::-1], p_sel[:, :, ::-1])
+
+
 MUTATIONS = [
     m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
     m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
@@ -178,6 +201,7 @@ MUTATIONS = [
     m_weighted_mean, m_weighted_missing, m_weighted_unweighted, m_slots_rank_major,
     m_shared_weighted_swapped, m_output_untransposed, m_dispatch_descending,
     m_kv_heads_swapped, m_head_rows_shifted,
+    m_wconcat_renormalized, m_wconcat_unscaled, m_hard_rank_reversed,
 ]
 
 
