@@ -60,14 +60,36 @@ typedef enum {
 
 typedef enum { GQE_DTYPE_BF16 = 0, GQE_DTYPE_FP32 = 1 } gqe_dtype;
 
+/* How the attention outputs become W_O's input (pptc.cn review, section 4.3,
+ * Table 1: the output constructions compared in the ablation).
+ *   GQE_OUTPUT_FULL             the GQE layer: k*G hard slots, the always-on
+ *                               shared head's slot and the renormalized
+ *                               weighted slot; W_O [d_model, (k*G+2)*d_h].
+ *   GQE_OUTPUT_HARD             hard concatenation only: the k*G hard slots;
+ *                               no shared head, no weighted slot;
+ *                               W_O [d_model, k*G*d_h].
+ *   GQE_OUTPUT_WEIGHTED_CONCAT  the k*G hard slots, each scaled by its
+ *                               expert's in-group softmax probability p (not
+ *                               renormalized over the k); no shared head, no
+ *                               weighted slot; W_O [d_model, k*G*d_h].  ws.w
+ *                               then holds p instead of the renormalized w. */
+typedef enum {
+  GQE_OUTPUT_FULL = 0,
+  GQE_OUTPUT_HARD = 1,
+  GQE_OUTPUT_WEIGHTED_CONCAT = 2
+} gqe_output_mode;
+
 /* Layer shape.  Limits (GQE_ERR_INVALID_ARG when broken): batch, seq_len >= 0;
  * d_model a positive multiple of 8; 1 <= n_groups; 1 <= n_experts <= 32;
  * 1 <= top_k <= n_experts; n_groups*n_experts <= 64;
- * 0 <= shared_kv_group < n_groups; batch*seq_len*n_groups*n_experts < 2^31.
+ * 0 <= shared_kv_group < n_groups; batch*seq_len*n_groups*n_experts < 2^31;
+ * output_mode a gqe_output_mode.
  * Built subset (GQE_ERR_UNSUPPORTED otherwise): head_dim in {32, 64, 128};
  * the projections stream their reduction dimension in 128-byte steps, so
- * d_model, (top_k*n_groups+2)*head_dim and n_groups*n_experts*head_dim must
- * be multiples of 64 elements for bf16 and of 32 for fp32. */
+ * d_model, the slot width ((top_k*n_groups+2)*head_dim, or
+ * top_k*n_groups*head_dim for the ablation outputs) and
+ * n_groups*n_experts*head_dim must be multiples of 64 elements for bf16 and
+ * of 32 for fp32. */
 typedef struct gqe_config {
   int32_t batch;            /* B                                               */
   int32_t seq_len;          /* L: prefill length, causal, no padding          */
@@ -80,6 +102,7 @@ typedef struct gqe_config {
   int32_t dtype;            /* gqe_dtype                                       */
   float softmax_scale;      /* attention scale; 0 selects 1/sqrt(head_dim)     */
   const float* router_bias; /* device float32 [G*E] added to the logits, or NULL */
+  int32_t output_mode;      /* gqe_output_mode (GQE layer only)                */
 } gqe_config;
 
 /* Byte offsets into the workspace of every intermediate, so that callers can

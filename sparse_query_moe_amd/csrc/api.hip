@@ -32,20 +32,26 @@ bool shape_ok(const gqe_config* c) {
   if (rows >= (1LL << 31)) return false;
   if (static_cast<long long>(c->batch) * c->seq_len * c->n_groups * c->n_experts >= (1LL << 31))
     return false;
+  if (c->output_mode < GQE_OUTPUT_FULL || c->output_mode > GQE_OUTPUT_WEIGHTED_CONCAT) return false;
   return true;
 }
+
+// the full GQE output has the shared head's slot and the weighted slot after
+// the k*G hard slots; the ablation outputs only the hard slots
+bool full_output(const gqe_config* c) { return c->output_mode == GQE_OUTPUT_FULL; }
+int slot_count(const gqe_config* c) { return c->top_k * c->n_groups + (full_output(c) ? 2 : 0); }
 
 bool head_dim_ok(const gqe_config* c) {
   return c->head_dim == 32 || c->head_dim == 64 || c->head_dim == 128;
 }
 
 // The projections stream K in steps of 128 bytes (64 bf16 or 32 fp32
-// elements): d_model, the slot width (k*G+2)*d_h and the dense head width
-// G*E*d_h must be multiples of it.
+// elements): d_model, the slot width and the dense head width G*E*d_h must be
+// multiples of it.
 bool k_steps_ok(const gqe_config* c) {
   const int step = c->dtype == GQE_DTYPE_BF16 ? 64 : 32;
   const int D = c->head_dim;
-  return c->d_model % step == 0 && ((c->top_k * c->n_groups + 2) * D) % step == 0 &&
+  return c->d_model % step == 0 && (slot_count(c) * D) % step == 0 &&
          (c->n_groups * c->n_experts * D) % step == 0;
 }
 
@@ -95,7 +101,7 @@ Layout make_layout(const gqe_config* c, bool dense) {
   }
   l.pub.k = take(B * G * L * D * es);
   l.pub.vt = take(B * G * vt_tiles * D * 64 * es);
-  l.pub.s = take(B * L * (dense ? G * E : G * k + 2) * D * es);
+  l.pub.s = take(B * L * (dense ? G * E : static_cast<size_t>(slot_count(c))) * D * es);
   if (dense) l.pub.scratch = off;
   l.pub.total = off;
   l.pub.vt_tiles = static_cast<int64_t>(vt_tiles);
@@ -142,7 +148,8 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   const int B = c->batch, L = c->seq_len, d = c->d_model, G = c->n_groups, E = c->n_experts;
   const int k = c->top_k, D = c->head_dim;
   ProjSeg seg[3];
-  const int nq_cols = dense ? G * E * D : D;
+  const bool shared = dense || full_output(c);  // the ablation outputs have no shared head
+  const int nq_cols = dense ? G * E * D : shared ? D : 0;
   seg[0].w = dense ? wq : static_cast<const void*>(static_cast<const T*>(wq) +
                                                     static_cast<size_t>(G) * E * D * d);
   seg[0].out = at<T>(ws, l.pub.q);
@@ -167,8 +174,8 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   seg[2].transposed = 1;
   hipError_t e = hipSuccess;
   if (part != kProjGather)
-    e = launch_dense_proj<T>(static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_tiles, seg, 3,
-                             stream);
+    e = launch_dense_proj<T>(static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_tiles,
+                             shared ? seg : seg + 1, shared ? 3 : 2, stream);
   if (e != hipSuccess || dense || part == kProjDense) return hip_status(e);
   e = launch_gather_q<T>(static_cast<const T*>(x), static_cast<const T*>(wq), at<T>(ws, l.pub.q),
                          at<int32_t>(ws, l.pub.counts), at<int32_t>(ws, l.pub.offsets),
@@ -183,6 +190,7 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
   const Layout l = make_layout(c, dense);
   const int G = c->n_groups, E = c->n_experts, k = c->top_k, D = c->head_dim;
   AttnParams p;
+  p.row_scale = nullptr;
   p.q = at<T>(ws, l.pub.q);
   p.k = at<T>(ws, l.pub.k);
   p.vt = at<T>(ws, l.pub.vt);
@@ -198,11 +206,12 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
     p.extra_group = 0;
     p.ld_o = static_cast<int64_t>(G) * E * D;
   } else {
-    p.H = G * k + 1;
+    p.H = G * k + (full_output(c) ? 1 : 0);
     p.heads_per_group = k;
     p.n_grouped = G * k;
     p.extra_group = c->shared_kv_group;
-    p.ld_o = static_cast<int64_t>(G * k + 2) * D;
+    p.ld_o = static_cast<int64_t>(slot_count(c)) * D;
+    if (c->output_mode == GQE_OUTPUT_WEIGHTED_CONCAT) p.row_scale = at<float>(ws, l.pub.w);
   }
   p.scale_log2 = scale_log2(c);
   return hip_status(launch_attention<T>(p, D, stream));
@@ -217,9 +226,11 @@ int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool d
   hipError_t e = hipSuccess;
   int K;
   if (!dense) {
-    e = launch_weighted_slot<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), M, G, k, D, stream);
-    if (e != hipSuccess) return GQE_ERR_HIP;
-    K = (G * k + 2) * D;
+    if (full_output(c)) {
+      e = launch_weighted_slot<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), M, G, k, D, stream);
+      if (e != hipSuccess) return GQE_ERR_HIP;
+    }
+    K = slot_count(c) * D;
   } else {
     K = G * E * D;
   }
@@ -320,17 +331,20 @@ int gqe_route(const gqe_config* cfg, const void* x, const void* Wr, void* worksp
   if (cfg->router_bias && (reinterpret_cast<uintptr_t>(cfg->router_bias) & 3u))
     return GQE_ERR_INVALID_ARG;
   const Layout l = make_layout(cfg, false);
+  const bool renorm = cfg->output_mode != GQE_OUTPUT_WEIGHTED_CONCAT;  // else w = p
   hipError_t e;
   if (cfg->dtype == GQE_DTYPE_BF16)
     e = launch_router<bf16_t>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(Wr),
                               cfg->router_bias, at<int32_t>(workspace, l.pub.idx),
                               at<float>(workspace, l.pub.w), cfg->batch * cfg->seq_len,
-                              cfg->d_model, cfg->n_groups, cfg->n_experts, cfg->top_k, stream);
+                              cfg->d_model, cfg->n_groups, cfg->n_experts, cfg->top_k, renorm,
+                              stream);
   else
     e = launch_router<float>(static_cast<const float*>(x), static_cast<const float*>(Wr),
                              cfg->router_bias, at<int32_t>(workspace, l.pub.idx),
                              at<float>(workspace, l.pub.w), cfg->batch * cfg->seq_len,
-                             cfg->d_model, cfg->n_groups, cfg->n_experts, cfg->top_k, stream);
+                             cfg->d_model, cfg->n_groups, cfg->n_experts, cfg->top_k, renorm,
+                             stream);
   return hip_status(e);
 }
 

@@ -329,7 +329,9 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
     if (qrow[qb] < L) {
-      const float inv = 1.f / l_tot;
+      float inv = 1.f / l_tot;
+      if (p.row_scale != nullptr && head < p.n_grouped)
+        inv *= p.row_scale[(static_cast<size_t>(b) * L + qrow[qb]) * p.n_grouped + head];
       T* out = static_cast<T*>(p.o) + (static_cast<size_t>(b) * L + qrow[qb]) * p.ld_o +
                static_cast<size_t>(head) * D;
 #pragma unroll

@@ -14,8 +14,11 @@ constexpr int kGatherRows = 128;
 
 // ---- K1 router ---------------------------------------------------------------
 template <typename T>
+// renorm: w = p renormalized over the k selected (the GQE layer); otherwise
+// w = p itself, the in-group softmax probability of each selected expert
 hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* idx, float* w,
-                         int n_tokens, int d, int G, int E, int k, hipStream_t stream);
+                         int n_tokens, int d, int G, int E, int k, bool renorm,
+                         hipStream_t stream);
 
 // ---- K2 dispatch -------------------------------------------------------------
 int dispatch_chunks(int L);
@@ -62,6 +65,9 @@ struct AttnParams {
   int n_grouped;
   int extra_group;      // heads h >= n_grouped read this group
   float scale_log2;     // softmax scale * log2(e)
+  // optional per-row factor of the grouped heads' outputs: o[b, t, h] is
+  // multiplied by row_scale[(b*L + t)*n_grouped + h] (h < n_grouped), or NULL
+  const float* row_scale;
 };
 template <typename T>
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream);

@@ -8,7 +8,10 @@
 //                  the largest in-group softmax p), best first, ties to the
 //                  lower index
 //   w[t, g, j]  = exp(r_j - r_0) / sum_j' exp(r_j' - r_0), which equals the
-//                  in-group softmax renormalized over the selected k.
+//                  in-group softmax renormalized over the selected k
+//                  (or, for the weighted-concatenation ablation of section
+//                  4.3, the in-group softmax p itself: the sum runs over
+//                  all E experts).
 //
 // The logits are accumulated in float64 on the fp64 matrix cores
 // (v_mfma_f64_16x16x4: 16 tokens x 16 experts x 4 model dims per
@@ -57,7 +60,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int n_tokens, int d, int G, int E,
-    int k) {
+    int k, int renorm) {
   __shared__ double part[4][kTok][17];
   __shared__ double logit[kTok][65];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     for (int e = 0; e < E; ++e) {
       int rank = 0;
       for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
-      if (rank < k) z += exp(r[e] - rmax);
+      if (rank < k || !renorm) z += exp(r[e] - rmax);
     }
     const size_t o = (static_cast<size_t>(gt) * G + g) * k;
     for (int e = 0; e < E; ++e) {
@@ -147,17 +150,18 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 
 template <typename T>
 hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* idx, float* w,
-                         int n_tokens, int d, int G, int E, int k, hipStream_t stream) {
+                         int n_tokens, int d, int G, int E, int k, bool renorm,
+                         hipStream_t stream) {
   const int blocks = (n_tokens + kTok - 1) / kTok;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(router_topk_kernel<T>, dim3(blocks), dim3(256), 0, stream, x, wr, bias, idx,
-                     w, n_tokens, d, G, E, k);
+                     w, n_tokens, d, G, E, k, renorm ? 1 : 0);
   return hipGetLastError();
 }
 
 template hipError_t launch_router<bf16_t>(const bf16_t*, const bf16_t*, const float*, int32_t*,
-                                          float*, int, int, int, int, int, hipStream_t);
+                                          float*, int, int, int, int, int, bool, hipStream_t);
 template hipError_t launch_router<float>(const float*, const float*, const float*, int32_t*,
-                                         float*, int, int, int, int, int, hipStream_t);
+                                         float*, int, int, int, int, int, bool, hipStream_t);
 
 }  // namespace gqe

@@ -38,7 +38,7 @@ class GqeConfig(ctypes.Structure):
         ("n_groups", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("shared_kv_group", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-        ("router_bias", ctypes.c_void_p),
+        ("router_bias", ctypes.c_void_p), ("output_mode", ctypes.c_int32),
     ]
 
     @property
@@ -93,14 +93,20 @@ def _check(status: int, what: str):
         raise GqeError(f"{what}: {status_string(status)} ({status})")
 
 
+OUTPUT_MODES = {"full": 0, "hard": 1, "weighted_concat": 2}  # gqe_output_mode
+
+
 def make_config(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim, dtype="bf16",
-                shared_kv_group=0, softmax_scale=0.0, router_bias=None) -> GqeConfig:
+                shared_kv_group=0, softmax_scale=0.0, router_bias=None,
+                output_mode="full") -> GqeConfig:
     """Fill a gqe_config.  `router_bias` is a float32 device tensor [G*E] or None;
-    the caller keeps it alive while the config is in use."""
+    the caller keeps it alive while the config is in use.  `output_mode` is
+    "full", "hard" or "weighted_concat" (see gqe_output_mode)."""
     dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}.get(dtype, dtype)
     return GqeConfig(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim,
                      shared_kv_group, dt, float(softmax_scale),
-                     None if router_bias is None else router_bias.data_ptr())
+                     None if router_bias is None else router_bias.data_ptr(),
+                     OUTPUT_MODES.get(output_mode, output_mode))
 
 
 def _ptr(t):
@@ -213,7 +219,8 @@ def workspace_views(cfg: GqeConfig, ws: torch.Tensor, dense: bool = False) -> di
         out["pos"] = view(lay.pos, (rows,), torch.int32, 4)
         out["slot"] = view(lay.slot, (rows,), torch.int32, 4)
         out["q"] = view(lay.q, (B, G * k + 1, L, D), dt, es)
-        out["s"] = view(lay.s, (B, L, (G * k + 2) * D), dt, es)
+        slots = G * k + (2 if cfg.output_mode == OUTPUT_MODES["full"] else 0)
+        out["s"] = view(lay.s, (B, L, slots * D), dt, es)
     else:
         out["q"] = view(lay.q, (B, G * E, L, D), dt, es)
         out["s"] = view(lay.s, (B, L, G * E * D), dt, es)

@@ -51,7 +51,8 @@ def test_config_validation(gqe):
     assert gqe.gqe_workspace_bytes(_cfg(gqe)) > 0
     bad = [dict(top_k=0), dict(top_k=5), dict(d_model=1020), dict(n_groups=0), dict(seq_len=-1),
            dict(n_experts=33), dict(n_groups=9, n_experts=8), dict(shared_kv_group=4),
-           dict(head_dim=0), dict(dtype=7), dict(softmax_scale=-1.0)]
+           dict(head_dim=0), dict(dtype=7), dict(softmax_scale=-1.0), dict(output_mode=3),
+           dict(output_mode=-1)]
     for b in bad:
         assert gqe.gqe_workspace_bytes(_cfg(gqe, **b)) == 0, b
     assert gqe.gqe_workspace_bytes(_cfg(gqe, head_dim=96)) == 0
@@ -59,6 +60,17 @@ def test_config_validation(gqe):
     lay = gqe.WsLayout()
     assert lib.gqe_workspace_layout(ctypes.byref(_cfg(gqe, head_dim=96)), ctypes.byref(lay)) == -2
     assert lib.gqe_workspace_layout(ctypes.byref(_cfg(gqe, top_k=9)), ctypes.byref(lay)) == -1
+    # the ablation outputs: k*G*d_h slot columns must fill whole K steps
+    assert gqe.gqe_workspace_bytes(_cfg(gqe, output_mode="hard")) > 0
+    odd = dict(head_dim=32, n_groups=3, top_k=1, n_experts=2, shared_kv_group=0)
+    assert lib.gqe_workspace_layout(ctypes.byref(_cfg(gqe, output_mode="hard", **odd)),
+                                    ctypes.byref(lay)) == -2
+
+
+def test_ablation_outputs_shrink_the_slot_buffer(gqe):
+    full = gqe.gqe_workspace_layout(_cfg(gqe))
+    hard = gqe.gqe_workspace_layout(_cfg(gqe, output_mode="weighted_concat"))
+    assert hard.total < full.total
 
 
 def test_workspace_monotone_and_aligned(gqe):

@@ -302,6 +302,31 @@ def test_determinism(gqe):
                           vt_decode(v2["vt"].view(torch.int16).cpu().numpy(), L))
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32", "l2k"])
+@pytest.mark.parametrize("mode", ["hard", "weighted_concat"])
+def test_ablation_output_modes(gqe, name, mode):
+    """The two output constructions of the ablation: the k*G hard slots only,
+    or each scaled by its in-group probability; no shared head, W_O of k*G*d_h
+    inputs (its first k*G*d_h columns here)."""
+    wl, I = inputs(name)
+    log(f"[output mode] {name} {mode}")
+    kG, D = wl.top_k * wl.n_groups, wl.head_dim
+    J = dict(I)
+    J["wo"] = np.ascontiguousarray(I["wo"][:, :kG * D])
+    cfg, ws, out = run_gqe(gqe, wl, J, output_mode=mode)
+    F = f64_inputs(wl, J)
+    ref = oracle_gqe(wl, F, output_mode=mode)
+    v = gqe.workspace_views(cfg, ws)
+    assert np.array_equal(v["idx"].cpu().numpy(), ref["idx"])
+    w_ref = ref["w"] if mode == "hard" else np.take_along_axis(
+        ref["p"], ref["idx"].astype(np.int64), axis=-1)
+    assert np.abs(v["w"].cpu().numpy().astype(np.float64) - w_ref).max() <= 2e-7
+    assert v["s"].shape[-1] == kG * D
+    output_gate(to_f64(v["s"]), ref["s"], wl.dtype, f"{name} {mode} s")
+    mx, mean, rel = output_gate(to_f64(out), ref["y"], wl.dtype, f"{name} {mode} y")
+    log(f"  y: max-abs {mx:.3e} mean-abs {mean:.3e} rel-L2 {rel:.3e}")
+
+
 def test_forward_equals_stages_and_graph_replay(gqe):
     """gqe_forward (dense projection forked to a second stream) gives the same
     bits as the five stage calls on one stream, and so does every replay of a
