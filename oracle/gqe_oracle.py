@@ -385,3 +385,87 @@ def gqa_forward(x, wq_dense, wk, wv, wo_dense, n_groups, n_experts, head_dim, sc
 def attention_flops(batch: int, seq_len: int, heads: int, head_dim: int) -> int:
     """Algorithmic flops of causal attention: QK^T and PV, 2*d_h each per pair s <= t."""
     return 2 * 2 * head_dim * heads * batch * seq_len * (seq_len + 1) // 2
+
+
+# --------------------------------------------------------------------------
+# decode: one new token per sequence against a KV cache
+# --------------------------------------------------------------------------
+# The pages analyse prefill only ([pptc] section 6 lists decode as not
+# analysed).  A decode step is the same layer evaluated at one position: the
+# new token of sequence b sits at position pos[b]; it is routed, its K and V
+# are appended to the cache at pos[b], and its queries attend causally to the
+# cached keys 0..pos[b] (steps 1-11 restricted to that row).
+
+
+def gqe_decode_step(x_t, k_cache, v_cache, pos, wq, wk, wv, wr, wo, br, n_groups, n_experts,
+                    top_k, head_dim, shared_kv_group=0, scale=None, output_mode="full"):
+    """x_t [B, d]: the new tokens; k_cache, v_cache [B, G, Lc, d_h]: keys and
+    values of positions < pos[b] (later entries are never read); pos [B].
+
+    Returns idx, w ([B, G, k]), k_new, v_new ([B, G, d_h]), the updated caches
+    (copies), q and o ([B, heads, d_h]: hard slots g*k+j, then the shared head
+    for the full output), s (slot vectors) and y [B, d].
+    """
+    if output_mode not in OUTPUT_MODES:
+        raise ValueError(output_mode)
+    B, d = x_t.shape
+    G, E, k, dh = n_groups, n_experts, top_k, head_dim
+    scale = 1.0 / math.sqrt(dh) if scale is None else scale
+    full = output_mode == "full"
+    r, p, idx, w = route(x_t, wr, br, G, E, k)             # steps 1-4 for the new tokens
+    k_new = (x_t @ wk.T).reshape(B, G, dh)                 # step 6
+    v_new = (x_t @ wv.T).reshape(B, G, dh)
+    kc, vc = k_cache.copy(), v_cache.copy()
+    H = k * G + (1 if full else 0)
+    q_all = np.empty((B, H, dh))
+    o_all = np.empty((B, H, dh))
+    s_all = np.empty((B, slot_width(output_mode, G, k, dh)))
+    for b in range(B):
+        t = int(pos[b])
+        kc[b, :, t] = k_new[b]
+        vc[b, :, t] = v_new[b]
+        tt = np.array([t])
+        o_hard = np.empty((1, G, k, dh))
+        for g in range(G):
+            for j in range(k):                             # step 7: the selected experts
+                qh = x_t[b] @ head_rows(wq, expert_head(g, int(idx[b, g, j]), E), dh).T
+                q_all[b, g * k + j] = qh
+                o_hard[0, g, j] = causal_attention(qh[None], tt, kc[b, g], vc[b, g], scale)[0]
+        o_all[b, :k * G] = o_hard.reshape(G * k, dh)
+        if not full:
+            p_sel = np.take_along_axis(p[b][None], idx[b][None].astype(np.int64), axis=-1)
+            s_all[b] = ablation_slots(output_mode, o_hard, p_sel)[0]
+            continue
+        q_sh = x_t[b] @ head_rows(wq, G * E, dh).T          # step 8
+        o_sh = causal_attention(q_sh[None], tt, kc[b, shared_kv_group], vc[b, shared_kv_group],
+                                scale)
+        q_all[b, k * G] = q_sh
+        o_all[b, k * G] = o_sh[0]
+        o_w = weighted_slot(w[b][None], o_hard)             # step 9
+        s_all[b] = slot_vector(o_hard, o_sh, o_w)[0]        # step 10
+    y = output_projection(s_all, wo)                        # step 11
+    return dict(r=r, p=p, idx=idx, w=w, k_new=k_new, v_new=v_new, k_cache=kc, v_cache=vc,
+                q=q_all, o=o_all, s=s_all, y=y)
+
+
+def gqa_decode_step(x_t, k_cache, v_cache, pos, wq_dense, wk, wv, wo_dense, n_groups, n_experts,
+                    head_dim, scale=None):
+    """Dense GQA decode step: all G*E heads, head h reads KV group h // E."""
+    B, d = x_t.shape
+    G, E, dh = n_groups, n_experts, head_dim
+    H = G * E
+    scale = 1.0 / math.sqrt(dh) if scale is None else scale
+    k_new = (x_t @ wk.T).reshape(B, G, dh)
+    v_new = (x_t @ wv.T).reshape(B, G, dh)
+    kc, vc = k_cache.copy(), v_cache.copy()
+    o_all = np.empty((B, H, dh))
+    for b in range(B):
+        t = int(pos[b])
+        kc[b, :, t] = k_new[b]
+        vc[b, :, t] = v_new[b]
+        for h in range(H):
+            qh = x_t[b] @ head_rows(wq_dense, h, dh).T
+            o_all[b, h] = causal_attention(qh[None], np.array([t]), kc[b, h // E], vc[b, h // E],
+                                           scale)[0]
+    y = output_projection(o_all.reshape(B, H * dh), wo_dense)
+    return dict(k_new=k_new, v_new=v_new, k_cache=kc, v_cache=vc, o=o_all, y=y)

@@ -427,6 +427,49 @@ def pin_ablation_constructions(orc):
         assert np.allclose(res["y"][b, 0], ref, rtol=0, atol=1e-12), np.abs(res["y"][b, 0] - ref).max()
 
 
+
+# ---------------------------------------------------------------------------
+# Decode: one token against a KV cache is the prefill layer's row
+# ---------------------------------------------------------------------------
+
+def pin_decode_step_is_prefill_row(orc):
+    """With the cache holding K/V of positions < t (anything after t), a decode
+    step on x[b, t] gives the prefill layer's y[b, t], its routing, and the
+    prefill K/V row t written into the cache; for every output construction
+    and for dense GQA."""
+    rng = np.random.default_rng(41)
+    t_ = tiny_layer(rng, B=2, L=9, G=2, E=3, k=2)
+    G, E, k, dh = t_["G"], t_["E"], t_["k"], t_["dh"]
+    B, L = t_["x"].shape[:2]
+    pos = np.array([8, 3])
+    K = np.stack([orc.kv_project(t_["x"][b], t_["wk"], G, dh, L) for b in range(B)])
+    V = np.stack([orc.kv_project(t_["x"][b], t_["wv"], G, dh, L) for b in range(B)])
+    kc = rng.standard_normal((B, G, 12, dh))
+    vc = rng.standard_normal((B, G, 12, dh))
+    for b in range(B):
+        kc[b, :, :pos[b]] = K[b, :, :pos[b]]
+        vc[b, :, :pos[b]] = V[b, :, :pos[b]]
+    x_t = np.stack([t_["x"][b, pos[b]] for b in range(B)])
+    for mode in ("full", "hard", "weighted_concat"):
+        tm = dict(t_)
+        if mode != "full":
+            tm["wo"] = t_["wo"][:, :k * G * dh]
+        pre = run(orc, tm, output_mode=mode)
+        dec = orc.gqe_decode_step(x_t, kc, vc, pos, tm["wq"], tm["wk"], tm["wv"], tm["wr"], tm["wo"],
+                                  tm["br"], G, E, k, dh, output_mode=mode)
+        for b in range(B):
+            assert np.array_equal(dec["idx"][b], pre["idx"][b, pos[b]])
+            assert np.allclose(dec["y"][b], pre["y"][b, pos[b]], rtol=0, atol=1e-12), mode
+            assert np.allclose(dec["k_cache"][b, :, pos[b]], K[b, :, pos[b]], rtol=0, atol=1e-12)
+            assert np.allclose(dec["v_cache"][b, :, :pos[b] + 1], V[b, :, :pos[b] + 1], rtol=0, atol=1e-12)
+    wq_d = t_["wq"][:G * E * dh]
+    wo_d = rng.standard_normal((t_["x"].shape[2], G * E * dh))
+    pre = orc.gqa_forward(t_["x"], wq_d, t_["wk"], t_["wv"], wo_d, G, E, dh)
+    dec = orc.gqa_decode_step(x_t, kc, vc, pos, wq_d, t_["wk"], t_["wv"], wo_d, G, E, dh)
+    for b in range(B):
+        assert np.allclose(dec["y"][b], pre["y"][b, pos[b]], rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_k_equals_e_is_dense_gqa,
     pin_weights_sum_to_one,
@@ -445,4 +488,5 @@ ALL_PINS = [
     pin_causality,
     pin_sampled_rows_match_full,
     pin_ablation_constructions,
+    pin_decode_step_is_prefill_row,
 ]

@@ -193,6 +193,16 @@ def m_hard_rank_reversed(mod):
     mod.ablation_slots = lambda mode, o_hard, p_sel: orig(mode, o_hard[:, :, ::-1], p_sel[:, :, ::-1])
 
 
+def m_decode_stale_cache(mod):
+    """the decode step attends before its own K/V reach the cache."""
+    orig = mod.gqe_decode_step
+
+    def step(x_t, k_cache, v_cache, pos, *a, **kw):
+        res = orig(x_t, k_cache, v_cache, pos - 1, *a, **kw)
+        return res
+    mod.gqe_decode_step = step
+
+
 MUTATIONS = [
     m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
     m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
@@ -201,7 +211,7 @@ MUTATIONS = [
     m_weighted_mean, m_weighted_missing, m_weighted_unweighted, m_slots_rank_major,
     m_shared_weighted_swapped, m_output_untransposed, m_dispatch_descending,
     m_kv_heads_swapped, m_head_rows_shifted,
-    m_wconcat_renormalized, m_wconcat_unscaled, m_hard_rank_reversed,
+    m_wconcat_renormalized, m_wconcat_unscaled, m_hard_rank_reversed, m_decode_stale_cache,
 ]
 
 
