@@ -206,6 +206,53 @@ int gqa_forward(const gqe_config* cfg, const void* x, const void* Wq, const void
                 const void* Wv, const void* Wo, void* out, void* workspace, size_t ws_bytes,
                 hipStream_t stream);
 
+/* ---- Decode: one new token per sequence against a KV cache -----------------
+ *
+ * The pages analyse prefill only (pptc.cn, section 6: decode is named as not
+ * analysed).  A decode step is the same layer evaluated at one position: the
+ * row t = pos[b] of the prefill layer over the sequence whose keys and values
+ * for positions < t are those in the cache.  For decode, cfg->batch is the
+ * number of sequences B (one new token each) and cfg->seq_len the cache
+ * capacity Lc >= 1; every other field means what it means for prefill, and
+ * the same limits and built subset apply, plus d_model <= 16384
+ * (GQE_ERR_UNSUPPORTED otherwise).
+ *
+ *   x         dtype [B, d_model]              the new tokens
+ *   Wq..Wo    as for gqe_forward / gqa_forward
+ *   k_cache   dtype [B, G, Lc, d_h]           keys, read for positions
+ *                                             <= pos[b]
+ *   vt_cache  dtype [B, G, ceil(Lc/64), d_h, 64]  values in the layout of
+ *                                             gqe_ws_layout.vt (64-key tiles,
+ *                                             keys permuted in 16-key groups);
+ *                                             columns past pos[b] are never
+ *                                             read (no zero fill needed)
+ *   pos       device int32 [B]                position of each new token
+ *   out       dtype [B, d_model]
+ *
+ * The step writes the new token's key and value into both caches at pos[b]
+ * (caller-owned, updated in place), routes the tokens exactly as gqe_route
+ * does (renormalized weights, or p for GQE_OUTPUT_WEIGHTED_CONCAT), lets
+ * every active query head attend to cache positions 0..pos[b] of its group,
+ * and projects the slot vectors through Wo as gqe_output does.  pos is read
+ * on the device only: a pos[b] outside [0, Lc) touches no cache entry and
+ * yields zero head outputs for that sequence (out = 0 . Wo).  The workspace
+ * (size from the *_decode_workspace_bytes call, 16-byte aligned) is private
+ * scratch; a call may overlap nothing else that uses the same workspace or
+ * caches.  Returns GQE_ERR_INVALID_ARG for a NULL or misaligned pointer
+ * (16 bytes; 4 for pos), GQE_ERR_WORKSPACE when ws_bytes is too small, and
+ * GQE_OK with nothing enqueued when B == 0. */
+size_t gqe_decode_workspace_bytes(const gqe_config* cfg);
+int gqe_decode(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+               const void* Wv, const void* Wr, const void* Wo, void* k_cache, void* vt_cache,
+               const int32_t* pos, void* out, void* workspace, size_t ws_bytes,
+               hipStream_t stream);
+
+/* Dense GQA decode step (all G*E heads; head h reads group h / E). */
+size_t gqa_decode_workspace_bytes(const gqe_config* cfg);
+int gqa_decode(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+               const void* Wv, const void* Wo, void* k_cache, void* vt_cache, const int32_t* pos,
+               void* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Static text for a gqe_status value; never NULL. */
 const char* gqe_status_string(int status);
 

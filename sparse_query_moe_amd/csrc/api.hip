@@ -108,10 +108,10 @@ Layout make_layout(const gqe_config* c, bool dense) {
   return l;
 }
 
-float scale_log2(const gqe_config* c) {
-  const float s = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / sqrtf(static_cast<float>(c->head_dim));
-  return s * 1.4426950408889634f;
+float softmax_scale(const gqe_config* c) {
+  return c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / sqrtf(static_cast<float>(c->head_dim));
 }
+float scale_log2(const gqe_config* c) { return softmax_scale(c) * 1.4426950408889634f; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GQE_OK : GQE_ERR_HIP; }
 
@@ -237,6 +237,126 @@ int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool d
   e = launch_out_proj<T>(at<T>(ws, l.pub.s), static_cast<const T*>(wo), static_cast<T*>(out), M,
                          c->d_model, K, stream);
   return hip_status(e);
+}
+
+// ---- decode ------------------------------------------------------------------
+
+// Decode takes batch = B sequences of one new token each and seq_len = the
+// cache capacity Lc.  The dynamic LDS of its row products holds d_model floats.
+constexpr int kDecodeMaxDModel = 16384;
+
+int decode_heads(const gqe_config* c, bool dense) {
+  return dense ? c->n_groups * c->n_experts
+               : c->top_k * c->n_groups + (full_output(c) ? 1 : 0);
+}
+int decode_ld_s(const gqe_config* c, bool dense) {
+  return (dense ? c->n_groups * c->n_experts : slot_count(c)) * c->head_dim;
+}
+
+struct DecodeLayout {
+  size_t idx, w, q, part, s, total;
+  int chunk, n_chunks;
+};
+
+DecodeLayout make_decode_layout(const gqe_config* c, bool dense) {
+  const size_t B = c->batch, G = c->n_groups, k = c->top_k, D = c->head_dim;
+  const size_t H = decode_heads(c, dense);
+  DecodeLayout l{};
+  l.chunk = decode_chunk(c->batch, c->n_groups, c->seq_len);
+  l.n_chunks = (c->seq_len + l.chunk - 1) / l.chunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  if (!dense) {
+    l.idx = take(B * G * k * 4);
+    l.w = take(B * G * k * 4);
+  }
+  l.q = take(B * H * D * 4);
+  l.part = take(B * H * static_cast<size_t>(l.n_chunks) * (D + 2) * 4);
+  l.s = take(B * static_cast<size_t>(decode_ld_s(c, dense)) * elem_bytes(c));
+  l.total = off;
+  return l;
+}
+
+int check_decode_cfg(const gqe_config* c) {
+  const int st = check_cfg(c);
+  if (st != GQE_OK) return st;
+  if (c->batch > 0 && c->seq_len < 1) return GQE_ERR_INVALID_ARG;  // no room for the token
+  if (c->d_model > kDecodeMaxDModel) return GQE_ERR_UNSUPPORTED;
+  return GQE_OK;
+}
+
+template <typename T>
+int decode_impl(const gqe_config* c, bool dense, const void* x, const void* wq, const void* wk,
+                const void* wv, const void* wr, const void* wo, void* k_cache, void* vt_cache,
+                const int32_t* pos, void* out, void* ws, hipStream_t stream) {
+  const DecodeLayout l = make_decode_layout(c, dense);
+  const int G = c->n_groups, E = c->n_experts, k = c->top_k;
+  DecodeParams p;
+  p.x = x;
+  p.wq = wq;
+  p.wk = wk;
+  p.wv = wv;
+  p.wo = wo;
+  p.idx = dense ? nullptr : at<int32_t>(ws, l.idx);
+  p.w = dense ? nullptr : at<float>(ws, l.w);
+  p.pos = pos;
+  p.q = at<float>(ws, l.q);
+  p.k_cache = k_cache;
+  p.vt_cache = vt_cache;
+  p.part = at<float>(ws, l.part);
+  p.s = at<T>(ws, l.s);
+  p.row_scale = !dense && c->output_mode == GQE_OUTPUT_WEIGHTED_CONCAT ? p.w : nullptr;
+  p.out = out;
+  p.B = c->batch;
+  p.d = c->d_model;
+  p.G = G;
+  p.E = E;
+  p.k = k;
+  p.D = c->head_dim;
+  p.Lc = c->seq_len;
+  p.Hq = decode_heads(c, dense);
+  p.n_routed = dense ? G * E : G * k;
+  p.shared_head = !dense && full_output(c) ? 1 : 0;
+  p.shared_kv_group = c->shared_kv_group;
+  p.heads_per_group = dense ? E : k;
+  p.chunk = l.chunk;
+  p.scale = softmax_scale(c);
+  p.ld_s = decode_ld_s(c, dense);
+  p.K_out = p.ld_s;
+  p.weighted_slot = p.shared_head;
+  if (!dense) {
+    const bool renorm = c->output_mode != GQE_OUTPUT_WEIGHTED_CONCAT;
+    const hipError_t e =
+        launch_router<T>(static_cast<const T*>(x), static_cast<const T*>(wr), c->router_bias,
+                         at<int32_t>(ws, l.idx), at<float>(ws, l.w), c->batch, c->d_model, G, E,
+                         k, renorm, stream);
+    if (e != hipSuccess) return GQE_ERR_HIP;
+  }
+  return hip_status(launch_decode<T>(p, stream));
+}
+
+int decode_entry(const gqe_config* cfg, bool dense, const void* x, const void* Wq, const void* Wk,
+                 const void* Wv, const void* Wr, const void* Wo, void* k_cache, void* vt_cache,
+                 const int32_t* pos, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_decode_cfg(cfg);
+  if (st != GQE_OK || cfg->batch == 0) return st;
+  if (!aligned16(x) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(Wo) ||
+      !aligned16(k_cache) || !aligned16(vt_cache) || !aligned16(out) || !aligned16(ws) ||
+      pos == nullptr || (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return GQE_ERR_INVALID_ARG;
+  if (!dense && (!aligned16(Wr) ||
+                 (cfg->router_bias && (reinterpret_cast<uintptr_t>(cfg->router_bias) & 3u))))
+    return GQE_ERR_INVALID_ARG;
+  if (ws_bytes < make_decode_layout(cfg, dense).total) return GQE_ERR_WORKSPACE;
+  return cfg->dtype == GQE_DTYPE_BF16
+             ? decode_impl<bf16_t>(cfg, dense, x, Wq, Wk, Wv, Wr, Wo, k_cache, vt_cache, pos,
+                                   out, ws, stream)
+             : decode_impl<float>(cfg, dense, x, Wq, Wk, Wv, Wr, Wo, k_cache, vt_cache, pos, out,
+                                  ws, stream);
 }
 
 }  // namespace
@@ -454,6 +574,31 @@ int gqa_forward(const gqe_config* cfg, const void* x, const void* Wq, const void
   if ((st = gqa_project(cfg, x, Wq, Wk, Wv, workspace, ws_bytes, stream)) != GQE_OK) return st;
   if ((st = gqa_attention(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
   return gqa_output(cfg, Wo, out, workspace, ws_bytes, stream);
+}
+
+size_t gqe_decode_workspace_bytes(const gqe_config* cfg) {
+  if (check_decode_cfg(cfg) != GQE_OK) return 0;
+  return make_decode_layout(cfg, false).total;
+}
+
+size_t gqa_decode_workspace_bytes(const gqe_config* cfg) {
+  if (check_decode_cfg(cfg) != GQE_OK) return 0;
+  return make_decode_layout(cfg, true).total;
+}
+
+int gqe_decode(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+               const void* Wv, const void* Wr, const void* Wo, void* k_cache, void* vt_cache,
+               const int32_t* pos, void* out, void* workspace, size_t ws_bytes,
+               hipStream_t stream) {
+  return decode_entry(cfg, false, x, Wq, Wk, Wv, Wr, Wo, k_cache, vt_cache, pos, out, workspace,
+                      ws_bytes, stream);
+}
+
+int gqa_decode(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+               const void* Wv, const void* Wo, void* k_cache, void* vt_cache, const int32_t* pos,
+               void* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return decode_entry(cfg, true, x, Wq, Wk, Wv, nullptr, Wo, k_cache, vt_cache, pos, out,
+                      workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

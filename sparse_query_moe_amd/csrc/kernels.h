@@ -80,4 +80,41 @@ template <typename T>
 hipError_t launch_out_proj(const T* a, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream);
 
+// ---- decode: one token per sequence against a KV cache --------------------------
+// query heads of one KV group that one decode attention block holds (E <= 32
+// dense heads, or k routed heads plus the shared one)
+constexpr int kMaxDecodeHeads = 33;
+
+struct DecodeParams {
+  const void* x;          // [B, d] the new tokens
+  const void* wq;         // query rows, [(G*E + 1)*D, d] (GQE) or [G*E*D, d] (GQA)
+  const void* wk;         // [G*D, d]
+  const void* wv;         // [G*D, d]
+  const void* wo;         // [d, K_out]
+  const int32_t* idx;     // [B, G, k] routed experts, or NULL (GQA: every head)
+  const float* w;         // [B, G, k] routing weights (GQE) or NULL
+  const int32_t* pos;     // [B] position of each new token in its cache
+  float* q;               // [B, Hq, D] scratch
+  void* k_cache;          // [B, G, Lc, D]
+  void* vt_cache;         // [B, G, ceil(Lc/64), D, 64], keys permuted in 16-key groups
+  float* part;            // [B, Hq, ceil(Lc/chunk), D + 2] scratch
+  void* s;                // [B, ld_s] slot vectors (concatenated head outputs)
+  const float* row_scale; // [B, n_routed] factor of the routed heads' outputs, or NULL
+  void* out;              // [B, d]
+  int B, d, G, E, k, D, Lc;
+  int Hq;                 // query heads per sequence
+  int n_routed;           // heads before the shared one (the routed heads)
+  int shared_head;        // 1: head n_routed is the shared head
+  int shared_kv_group;
+  int heads_per_group;    // head h < n_routed reads group h / heads_per_group
+  int chunk;              // keys per attention block (decode_chunk)
+  float scale;            // softmax scale
+  int ld_s, K_out;
+  int weighted_slot;      // 1: build the weighted slot after the heads
+};
+// keys per decode attention block for B sequences of G groups in a cache of Lc
+int decode_chunk(int B, int G, int Lc);
+template <typename T>
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
 }  // namespace gqe

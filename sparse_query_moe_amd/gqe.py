@@ -24,7 +24,8 @@ _TORCH_DTYPE = {DTYPE_BF16: torch.bfloat16, DTYPE_FP32: torch.float32}
 EXPORTS = (
     "gqe_workspace_bytes", "gqe_workspace_layout", "gqe_route", "gqe_dispatch", "gqe_project",
     "gqe_attention", "gqe_output", "gqe_forward", "gqa_workspace_bytes", "gqa_workspace_layout",
-    "gqa_project", "gqa_attention", "gqa_output", "gqa_forward", "gqe_status_string",
+    "gqa_project", "gqa_attention", "gqa_output", "gqa_forward", "gqe_decode_workspace_bytes",
+    "gqe_decode", "gqa_decode_workspace_bytes", "gqa_decode", "gqe_status_string",
 )
 
 
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqa_attention": (ctypes.c_int, [cfgp, vp, sz, vp]),
         "gqa_output": (ctypes.c_int, [cfgp, vp, vp, vp, sz, vp]),
         "gqa_forward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "gqe_decode_workspace_bytes": (sz, [cfgp]),
+        "gqa_decode_workspace_bytes": (sz, [cfgp]),
+        "gqe_decode": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "gqa_decode": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "gqe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -193,6 +198,33 @@ def gqa_output(cfg, wo, out, ws, stream=None):
 def gqa_forward(cfg, x, wq, wk, wv, wo, out, ws, stream=None):
     _check(_lib.gqa_forward(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
                             _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "gqa_forward")
+
+
+def gqe_decode_workspace_bytes(cfg: GqeConfig) -> int:
+    return int(_lib.gqe_decode_workspace_bytes(ctypes.byref(cfg)))
+
+
+def gqa_decode_workspace_bytes(cfg: GqeConfig) -> int:
+    return int(_lib.gqa_decode_workspace_bytes(ctypes.byref(cfg)))
+
+
+def alloc_decode_workspace(cfg: GqeConfig, dense: bool = False, device="cuda") -> torch.Tensor:
+    n = gqa_decode_workspace_bytes(cfg) if dense else gqe_decode_workspace_bytes(cfg)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def gqe_decode(cfg, x, wq, wk, wv, wr, wo, k_cache, vt_cache, pos, out, ws, stream=None):
+    """One decode step: cfg.batch sequences, cfg.seq_len the cache capacity;
+    pos is a device int32 tensor [B]; the caches are updated in place."""
+    _check(_lib.gqe_decode(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wr),
+                           _ptr(wo), _ptr(k_cache), _ptr(vt_cache), _ptr(pos), _ptr(out),
+                           _ptr(ws), ws.numel(), _stream(stream)), "gqe_decode")
+
+
+def gqa_decode(cfg, x, wq, wk, wv, wo, k_cache, vt_cache, pos, out, ws, stream=None):
+    _check(_lib.gqa_decode(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+                           _ptr(k_cache), _ptr(vt_cache), _ptr(pos), _ptr(out), _ptr(ws),
+                           ws.numel(), _stream(stream)), "gqa_decode")
 
 
 def workspace_views(cfg: GqeConfig, ws: torch.Tensor, dense: bool = False) -> dict:

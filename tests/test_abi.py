@@ -108,3 +108,40 @@ def test_host_errors_before_any_launch(gqe):
                          None, None, 0, None)
     assert st == 0
     assert gqe.status_string(-3).startswith("GQE_ERR_WORKSPACE")
+
+
+def test_decode_workspace_and_validation(gqe):
+    """Decode: batch = sequences, seq_len = cache capacity."""
+    cfg = _cfg(gqe, batch=4, seq_len=8192)
+    n = gqe.gqe_decode_workspace_bytes(cfg)
+    assert n > 0 and gqe.gqa_decode_workspace_bytes(cfg) > 0
+    # split-K partials grow with the cache; the workspace never shrinks
+    assert gqe.gqe_decode_workspace_bytes(_cfg(gqe, batch=4, seq_len=65536)) >= n
+    assert gqe.gqe_decode_workspace_bytes(_cfg(gqe, batch=8, seq_len=8192)) >= n
+    assert gqe.gqe_decode_workspace_bytes(_cfg(gqe, batch=4, seq_len=0)) == 0  # no room
+    assert gqe.gqe_decode_workspace_bytes(_cfg(gqe, d_model=32768)) == 0
+    assert gqe.gqe_decode_workspace_bytes(_cfg(gqe, top_k=0)) == 0
+    # the ablation outputs have fewer heads and slots
+    assert gqe.gqe_decode_workspace_bytes(_cfg(gqe, batch=4, seq_len=8192, output_mode="hard")) < n
+
+
+def test_decode_host_errors_before_any_launch(gqe):
+    lib = gqe._lib
+    cfg = _cfg(gqe, batch=2, seq_len=4096)
+    n = gqe.gqe_decode_workspace_bytes(cfg)
+    a = ctypes.c_void_p(256)
+    nulls = [None] * 11
+    assert lib.gqe_decode(ctypes.byref(cfg), *nulls, n, None) == -1
+    assert lib.gqa_decode(ctypes.byref(cfg), *nulls[:10], n, None) == -1
+    # misaligned pos
+    args = [a] * 11
+    args[8] = ctypes.c_void_p(258)
+    assert lib.gqe_decode(ctypes.byref(cfg), *args, n, None) == -1
+    # workspace too small
+    assert lib.gqe_decode(ctypes.byref(cfg), *([a] * 11), n - 1, None) == -3
+    m = gqe.gqa_decode_workspace_bytes(cfg)
+    assert lib.gqa_decode(ctypes.byref(cfg), *([a] * 10), m - 1, None) == -3
+    # unsupported head size
+    assert lib.gqe_decode(ctypes.byref(_cfg(gqe, head_dim=96)), *([a] * 11), n, None) == -2
+    # no sequences: nothing to do
+    assert lib.gqe_decode(ctypes.byref(_cfg(gqe, batch=0)), *nulls, 0, None) == 0

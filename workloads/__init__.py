@@ -189,3 +189,43 @@ def sample_rows(wl: Workload, seed: int = 0) -> np.ndarray:
         chosen.update(int(v) for v in rng.choice(rest, size=need, replace=False))
     rows = np.array(sorted(chosen), dtype=np.int64)
     return rows[:n] if len(rows) > n else rows
+
+
+# ---------------------------------------------------------------------------
+# decode: one new token per sequence against a KV cache
+# ---------------------------------------------------------------------------
+
+DECODE_WORKLOADS = {
+    "dec_tiny_fp32": Workload(
+        "dec_tiny_fp32", 3, 200, 256, 2, 2, 1, 32, FP32, 1.0, 1.0 / math.sqrt(256.0),
+        description="tiny fp32 decode: 3 sequences, cache 200, d256 G2 E2 k1 d_h32"),
+    "dec_b64_c8k": Workload(
+        "dec_b64_c8k", 64, 8192, 1024, 4, 4, 2, 64, BF16, 1.0, 0.02,
+        description="250M-scale layer decode bf16: 64 sequences, cache 8192"),
+}
+
+
+def make_decode_inputs(wl: Workload, seed: int = 0, with_gqa: bool = False) -> dict:
+    """Inputs of one decode step: wl.batch sequences, wl.seq_len the cache capacity.
+
+    Layer weights and the new tokens come from ``make_inputs`` of the same
+    shape at one position (x is [B, d]).  A second generator (seed + 2) then
+    draws, in order, the key cache and the value cache ([B, G, Lc, d_h], the
+    standard deviation of a projection of x, x_std * w_std * sqrt(d)), and the
+    positions pos [B] uniform in [0, Lc), after which pos[0] = Lc - 1 (a full
+    cache) and, for B > 1, pos[1] = 0 (an empty one).  Entries at positions
+    >= pos[b] hold random values that a correct step never reads.
+    """
+    I = make_inputs(wl.with_(seq_len=1), seed, with_gqa)
+    I["x"] = np.ascontiguousarray(I["x"][:, 0])
+    rng = np.random.Generator(np.random.PCG64(seed + 2))
+    B, G, Lc, dh = wl.batch, wl.n_groups, wl.seq_len, wl.head_dim
+    kv_std = wl.x_std * wl.w_std * math.sqrt(wl.d_model)
+    I["k_cache"] = _draw(rng, (B, G, Lc, dh), kv_std, wl.dtype)
+    I["v_cache"] = _draw(rng, (B, G, Lc, dh), kv_std, wl.dtype)
+    pos = rng.integers(0, Lc, size=B).astype(np.int32)
+    pos[0] = Lc - 1
+    if B > 1:
+        pos[1] = 0
+    I["pos"] = pos
+    return I
