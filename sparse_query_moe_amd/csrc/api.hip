@@ -239,12 +239,75 @@ int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool d
   return hip_status(e);
 }
 
+}  // namespace
+
+namespace {
+
+// gqe_forward overlaps the dense projection (shared-head Q, K, V^T), which
+// does not depend on the routing, with routing, dispatch and the gathered Q
+// projection: it runs on a second stream of the same device between a fork
+// and a join event.  One side stream and two events per device, created on
+// first use; the whole enqueue sequence holds a mutex so that concurrent
+// callers cannot interleave their event records.
+struct Fork {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;
+};
+constexpr int kMaxDevices = 64;
+Fork g_forks[kMaxDevices];
+std::mutex g_fork_mutex;
+
+// the fork resources of the stream's device, or nullptr (then everything runs
+// on the caller's stream)
+Fork* fork_for(hipStream_t stream) {
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return nullptr;
+  Fork& f = g_forks[dev];
+  if (!f.tried) {
+    f.tried = true;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    bool ok = hipSetDevice(dev) == hipSuccess;
+    ok = ok && hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&f.join, hipEventDisableTiming) == hipSuccess;
+    (void)hipSetDevice(cur);
+    if (!ok) {
+      (void)hipGetLastError();
+      f.side = nullptr;
+    }
+  }
+  return f.side != nullptr ? &f : nullptr;
+}
+
+// work enqueued on *side after this is ordered after everything on `stream`
+hipError_t fork_begin(Fork* f, hipStream_t stream, hipStream_t* side) {
+  hipError_t e = hipEventRecord(f->fork, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(f->side, f->fork, 0);
+  *side = f->side;
+  return e;
+}
+
+// later work on `stream` is ordered after everything enqueued on the side stream
+hipError_t fork_end(Fork* f, hipStream_t stream) {
+  hipError_t e = hipEventRecord(f->join, f->side);
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, f->join, 0);
+  return e;
+}
+
 // ---- decode ------------------------------------------------------------------
 
 // Decode takes batch = B sequences of one new token each and seq_len = the
 // cache capacity Lc.  The dynamic LDS of its row products holds d_model floats.
 constexpr int kDecodeMaxDModel = 16384;
 
+// query heads projected per token: every routed expert, plus the shared head
+// for the full output
+int decode_q_heads(const gqe_config* c, bool dense) {
+  return c->n_groups * c->n_experts + (!dense && full_output(c) ? 1 : 0);
+}
 int decode_heads(const gqe_config* c, bool dense) {
   return dense ? c->n_groups * c->n_experts
                : c->top_k * c->n_groups + (full_output(c) ? 1 : 0);
@@ -274,7 +337,7 @@ DecodeLayout make_decode_layout(const gqe_config* c, bool dense) {
     l.idx = take(B * G * k * 4);
     l.w = take(B * G * k * 4);
   }
-  l.q = take(B * H * D * 4);
+  l.q = take(B * static_cast<size_t>(decode_q_heads(c, dense)) * D * 4);
   l.part = take(B * H * static_cast<size_t>(l.n_chunks) * (D + 2) * 4);
   l.s = take(B * static_cast<size_t>(decode_ld_s(c, dense)) * elem_bytes(c));
   l.total = off;
@@ -318,6 +381,7 @@ int decode_impl(const gqe_config* c, bool dense, const void* x, const void* wq, 
   p.k = k;
   p.D = c->head_dim;
   p.Lc = c->seq_len;
+  p.q_heads = decode_q_heads(c, dense);
   p.Hq = decode_heads(c, dense);
   p.n_routed = dense ? G * E : G * k;
   p.shared_head = !dense && full_output(c) ? 1 : 0;
@@ -328,15 +392,26 @@ int decode_impl(const gqe_config* c, bool dense, const void* x, const void* wq, 
   p.ld_s = decode_ld_s(c, dense);
   p.K_out = p.ld_s;
   p.weighted_slot = p.shared_head;
-  if (!dense) {
-    const bool renorm = c->output_mode != GQE_OUTPUT_WEIGHTED_CONCAT;
-    const hipError_t e =
-        launch_router<T>(static_cast<const T*>(x), static_cast<const T*>(wr), c->router_bias,
-                         at<int32_t>(ws, l.idx), at<float>(ws, l.w), c->batch, c->d_model, G, E,
-                         k, renorm, stream);
-    if (e != hipSuccess) return GQE_ERR_HIP;
+  if (dense) {
+    hipError_t e = launch_decode_qkv<T>(p, stream);
+    if (e == hipSuccess) e = launch_decode_attend<T>(p, stream);
+    return hip_status(e);
   }
-  return hip_status(launch_decode<T>(p, stream));
+  // the routing does not depend on the projections: it runs on the side
+  // stream of the device while the projections run on `stream`
+  std::lock_guard<std::mutex> lock(g_fork_mutex);
+  Fork* f = fork_for(stream);
+  hipStream_t rs = stream;
+  if (f != nullptr && fork_begin(f, stream, &rs) != hipSuccess) return GQE_ERR_HIP;
+  const bool renorm = c->output_mode != GQE_OUTPUT_WEIGHTED_CONCAT;
+  hipError_t e = launch_router_tokens<T>(static_cast<const T*>(x), static_cast<const T*>(wr),
+                                         c->router_bias, at<int32_t>(ws, l.idx),
+                                         at<float>(ws, l.w), c->batch, c->d_model, G, E, k,
+                                         renorm, rs);
+  if (e != hipSuccess) return GQE_ERR_HIP;
+  if ((e = launch_decode_qkv<T>(p, stream)) != hipSuccess) return GQE_ERR_HIP;
+  if (f != nullptr && fork_end(f, stream) != hipSuccess) return GQE_ERR_HIP;
+  return hip_status(launch_decode_attend<T>(p, stream));
 }
 
 int decode_entry(const gqe_config* cfg, bool dense, const void* x, const void* Wq, const void* Wk,
@@ -359,48 +434,6 @@ int decode_entry(const gqe_config* cfg, bool dense, const void* x, const void* W
                                   ws, stream);
 }
 
-}  // namespace
-
-namespace {
-
-// gqe_forward overlaps the dense projection (shared-head Q, K, V^T), which
-// does not depend on the routing, with routing, dispatch and the gathered Q
-// projection: it runs on a second stream of the same device between a fork
-// and a join event.  One side stream and two events per device, created on
-// first use; the whole enqueue sequence holds a mutex so that concurrent
-// callers cannot interleave their event records.
-struct Fork {
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool tried = false;
-};
-constexpr int kMaxDevices = 64;
-Fork g_forks[kMaxDevices];
-std::mutex g_fork_mutex;
-
-// the fork resources of the stream's device, or nullptr (then everything runs
-// on the caller's stream)
-Fork* fork_for(hipStream_t stream) {
-  hipDevice_t dev = 0;
-  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return nullptr;
-  Fork& f = g_forks[dev];
-  if (!f.tried) {
-    f.tried = true;
-    int cur = 0;
-    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
-    bool ok = hipSetDevice(dev) == hipSuccess;
-    ok = ok && hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&f.join, hipEventDisableTiming) == hipSuccess;
-    (void)hipSetDevice(cur);
-    if (!ok) {
-      (void)hipGetLastError();
-      f.side = nullptr;
-    }
-  }
-  return f.side != nullptr ? &f : nullptr;
-}
 
 }  // namespace
 

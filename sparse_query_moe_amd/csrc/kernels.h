@@ -20,6 +20,13 @@ hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* id
                          int n_tokens, int d, int G, int E, int k, bool renorm,
                          hipStream_t stream);
 
+// The same routing for a few tokens (decode): one block per token, logits
+// summed over the model dimension in a different (fixed) float64 order.
+template <typename T>
+hipError_t launch_router_tokens(const T* x, const T* wr, const float* bias, int32_t* idx,
+                                float* w, int n_tokens, int d, int G, int E, int k, bool renorm,
+                                hipStream_t stream);
+
 // ---- K2 dispatch -------------------------------------------------------------
 int dispatch_chunks(int L);
 hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* counts,
@@ -94,7 +101,7 @@ struct DecodeParams {
   const int32_t* idx;     // [B, G, k] routed experts, or NULL (GQA: every head)
   const float* w;         // [B, G, k] routing weights (GQE) or NULL
   const int32_t* pos;     // [B] position of each new token in its cache
-  float* q;               // [B, Hq, D] scratch
+  float* q;               // [B, q_heads, D] scratch: every query head's projection
   void* k_cache;          // [B, G, Lc, D]
   void* vt_cache;         // [B, G, ceil(Lc/64), D, 64], keys permuted in 16-key groups
   float* part;            // [B, Hq, ceil(Lc/chunk), D + 2] scratch
@@ -102,7 +109,8 @@ struct DecodeParams {
   const float* row_scale; // [B, n_routed] factor of the routed heads' outputs, or NULL
   void* out;              // [B, d]
   int B, d, G, E, k, D, Lc;
-  int Hq;                 // query heads per sequence
+  int q_heads;            // query heads projected per token (G*E, plus the shared head)
+  int Hq;                 // slot heads per token (heads that attend)
   int n_routed;           // heads before the shared one (the routed heads)
   int shared_head;        // 1: head n_routed is the shared head
   int shared_kv_group;
@@ -114,7 +122,12 @@ struct DecodeParams {
 };
 // keys per decode attention block for B sequences of G groups in a cache of Lc
 int decode_chunk(int B, int G, int Lc);
+// the projections (query heads into q, K and V^T into the caches at pos) ...
 template <typename T>
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t stream);
+// ... then, once the routing (idx, w) is there too, attention, slot vectors
+// and the output projection
+template <typename T>
+hipError_t launch_decode_attend(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace gqe
