@@ -282,16 +282,25 @@ constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16 (i ^ 15)
 // total of partial c.  Each step pairs lanes that differ in the step's bit
 // (and possibly lower ones): a lane keeps the half of the partials whose
 // index has its own bit and sends the other half.
+// The two-way choices go through v_perm_b32 with a per-lane selector: as
+// plain selects the compiler folds them into an indexed array access, which
+// it then expands into compare-and-select chains over every partial.
+__device__ __forceinline__ float pick(float lo, float hi, uint32_t sel) {
+  return __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), sel));
+}
+constexpr uint32_t kPickLo = 0x03020100u, kPickHi = 0x07060504u;
+
 template <int N>
 __device__ __forceinline__ float reduce_scatter(float (&v)[N], int c) {
 #pragma unroll
   for (int n = N; n > 1; n >>= 1) {
     const int half = n / 2;
     const bool hi = (c & half) != 0;
+    const uint32_t sel_keep = hi ? kPickHi : kPickLo, sel_send = hi ? kPickLo : kPickHi;
 #pragma unroll
     for (int j = 0; j < half; ++j) {
-      const float keep = hi ? v[j + half] : v[j];
-      const float send = hi ? v[j] : v[j + half];
+      const float keep = pick(v[j], v[j + half], sel_keep);
+      const float send = pick(v[j], v[j + half], sel_send);
       float recv;
       if (half == 8) recv = dpp<kDppMirror>(send);
       else if (half == 4) recv = dpp<kDppHalfMirror>(send);
@@ -310,13 +319,26 @@ __device__ __forceinline__ float sum8(float v) {
   return v + dpp<kDppHalfMirror>(v);
 }
 
+// v moved by a row broadcast to the rows in ROW_MASK; the other rows keep old
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+
+// maximum over the wave (all 64 lanes active), without the LDS unit: the
+// rows of 16 reduce by lane moves, rows 1 and 3 take in rows 0 and 2, rows 2
+// and 3 take in row 1, and lane 63 then holds the maximum of all four rows
 __device__ __forceinline__ float wave_max_fast(float v) {
   v = fmaxf(v, dpp<kDppXor1>(v));
   v = fmaxf(v, dpp<kDppXor2>(v));
   v = fmaxf(v, dpp<kDppHalfMirror>(v));
   v = fmaxf(v, dpp<kDppMirror>(v));
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  v = fmaxf(v, dpp_rows<kDppRowBcast15, 0xa>(v, v));
+  v = fmaxf(v, dpp_rows<kDppRowBcast31, 0xc>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -392,9 +414,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecAttnAr
   const char* Vg = static_cast<const char*>(a.vt_cache) +
                    (static_cast<size_t>(b) * a.G + g) * tiles * D * 64 * sizeof(bf16_t);
 
-  for (int j0 = k0 + 64 * wave; j0 < k1; j0 += 64 * NW) {
-    const int live = min(64, k1 - j0);  // valid keys of this tile
-    uint4 kf[NL], vf[NL];
+  // 16 bytes per lane per load: the K rows and V^T columns of one tile
+  auto load_tile = [&](int j0, uint4 (&kf)[NL], uint4 (&vf)[NL]) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int key = min(j0 + i * KPI + lane / LPK, a.Lc - 1);  // rows past the cache: any valid row
@@ -403,6 +424,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecAttnAr
     const char* vt = Vg + static_cast<size_t>(j0 / 64) * D * 64 * sizeof(bf16_t);
 #pragma unroll
     for (int j = 0; j < NL; ++j) vf[j] = *reinterpret_cast<const uint4*>(vt + j * 1024 + lane * 16);
+  };
+  auto do_tile = [&](int j0, uint4 (&kf)[NL], uint4 (&vf)[NL]) {
+    const int live = min(64, k1 - j0);  // valid keys of this tile
     if (live < 64) {  // columns of keys past the end may hold anything: zero them
       uint32_t keep[4];
 #pragma unroll
@@ -452,6 +476,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecAttnAr
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // two register buffers: the next tile's loads are in flight while this
+  // tile is computed
+  constexpr int kStep = 64 * NW;
+  uint4 ka[NL], va[NL], kb[NL], vb[NL];
+  int j0 = k0 + 64 * wave;
+  if (j0 < k1) load_tile(j0, ka, va);
+  while (j0 < k1) {
+    if (j0 + kStep < k1) load_tile(j0 + kStep, kb, vb);
+    do_tile(j0, ka, va);
+    j0 += kStep;
+    if (j0 >= k1) break;
+    if (j0 + kStep < k1) load_tile(j0 + kStep, ka, va);
+    do_tile(j0, kb, vb);
+    j0 += kStep;
   }
   // this wave's state per head: o over the 8 lanes of a V^T row, l over all lanes
 #pragma unroll
