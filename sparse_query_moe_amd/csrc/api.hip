@@ -282,21 +282,6 @@ Fork* fork_for(hipStream_t stream) {
   return f.side != nullptr ? &f : nullptr;
 }
 
-// work enqueued on *side after this is ordered after everything on `stream`
-hipError_t fork_begin(Fork* f, hipStream_t stream, hipStream_t* side) {
-  hipError_t e = hipEventRecord(f->fork, stream);
-  if (e == hipSuccess) e = hipStreamWaitEvent(f->side, f->fork, 0);
-  *side = f->side;
-  return e;
-}
-
-// later work on `stream` is ordered after everything enqueued on the side stream
-hipError_t fork_end(Fork* f, hipStream_t stream) {
-  hipError_t e = hipEventRecord(f->join, f->side);
-  if (e == hipSuccess) e = hipStreamWaitEvent(stream, f->join, 0);
-  return e;
-}
-
 // ---- decode ------------------------------------------------------------------
 
 // Decode takes batch = B sequences of one new token each and seq_len = the
@@ -364,6 +349,9 @@ int decode_impl(const gqe_config* c, bool dense, const void* x, const void* wq, 
   p.wk = wk;
   p.wv = wv;
   p.wo = wo;
+  p.wr = dense ? nullptr : wr;
+  p.router_bias = dense ? nullptr : c->router_bias;
+  p.renorm = c->output_mode != GQE_OUTPUT_WEIGHTED_CONCAT;
   p.idx = dense ? nullptr : at<int32_t>(ws, l.idx);
   p.w = dense ? nullptr : at<float>(ws, l.w);
   p.pos = pos;
@@ -392,26 +380,9 @@ int decode_impl(const gqe_config* c, bool dense, const void* x, const void* wq, 
   p.ld_s = decode_ld_s(c, dense);
   p.K_out = p.ld_s;
   p.weighted_slot = p.shared_head;
-  if (dense) {
-    hipError_t e = launch_decode_qkv<T>(p, stream);
-    if (e == hipSuccess) e = launch_decode_attend<T>(p, stream);
-    return hip_status(e);
-  }
-  // the routing does not depend on the projections: it runs on the side
-  // stream of the device while the projections run on `stream`
-  std::lock_guard<std::mutex> lock(g_fork_mutex);
-  Fork* f = fork_for(stream);
-  hipStream_t rs = stream;
-  if (f != nullptr && fork_begin(f, stream, &rs) != hipSuccess) return GQE_ERR_HIP;
-  const bool renorm = c->output_mode != GQE_OUTPUT_WEIGHTED_CONCAT;
-  hipError_t e = launch_router_tokens<T>(static_cast<const T*>(x), static_cast<const T*>(wr),
-                                         c->router_bias, at<int32_t>(ws, l.idx),
-                                         at<float>(ws, l.w), c->batch, c->d_model, G, E, k,
-                                         renorm, rs);
-  if (e != hipSuccess) return GQE_ERR_HIP;
-  if ((e = launch_decode_qkv<T>(p, stream)) != hipSuccess) return GQE_ERR_HIP;
-  if (f != nullptr && fork_end(f, stream) != hipSuccess) return GQE_ERR_HIP;
-  return hip_status(launch_decode_attend<T>(p, stream));
+  hipError_t e = launch_decode_front<T>(p, stream);
+  if (e == hipSuccess) e = launch_decode_attend<T>(p, stream);
+  return hip_status(e);
 }
 
 int decode_entry(const gqe_config* cfg, bool dense, const void* x, const void* Wq, const void* Wk,

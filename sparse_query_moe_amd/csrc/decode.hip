@@ -8,24 +8,26 @@
 // through W_O.
 //
 // Decode moves the whole cache once per step and does O(1) work per byte:
-//   rows_gemm_kernel    the two projections of the B new tokens, C = A . W^T
-//                       with B (a few) rows: 32x32 output tiles on the matrix
+//   decode_front_kernel the projections of the B new tokens, C = A . W^T with
+//                       B (a few) rows: 32x32 output tiles on the matrix
 //                       cores, the reduction dimension split over 4 waves.
 //                       Every query head of every token is projected (the
 //                       weight bytes are read once whatever k is); the
-//                       epilogue writes K and V^T into the caches.  For W_O
-//                       the operand loads form the weighted slot.
+//                       epilogue writes K and V^T into the caches.  Further
+//                       blocks of the same launch route the tokens.
 //   decode_attn_*       split-K attention ("flash decoding"): one block per
 //                       (sequence, KV group, chunk of keys); the slot heads of
 //                       the group share every K / V^T tile read.
 //   decode_combine_kernel  one wave per (sequence, slot head) merges the
 //                       chunk partials into the slot vector.
+//   rows_gemm_kernel    W_O; its operand loads form the weighted slot.
 #include <math.h>
 
 #include <algorithm>
 
 #include "device_common.h"
 #include "kernels.h"
+#include "routing.h"
 
 namespace gqe {
 
@@ -96,7 +98,69 @@ struct DecAttnArgs {
   int extra_head;         // a further head (the shared one) or -1
   int extra_group;        // the group it reads
   float scale_log2;
+  // merge of the partials into slot vectors
+  const float* row_scale; // [B, n_scaled] or NULL: output of head h < n_scaled times this
+  void* s;                // [B, ld_s] slot vectors; head h at columns h*D
+  int ld_s, n_scaled;
 };
+
+// One wave merges the chunk partials of (sequence b, slot head h): the chunk
+// maxima, then the partial outputs weighted by 2^(m_c - max), 64 chunks at a
+// time (lane = chunk for the weights, lane = head dimension for the sums);
+// sw is the wave's 64-float LDS row.
+template <typename T>
+__device__ __forceinline__ void combine_head(const DecAttnArgs& a, int b, int h, int lane,
+                                             float* sw) {
+  const int stride = a.D + 2;
+  const float* pp = a.part + (static_cast<size_t>(b) * a.Hq + h) * a.n_chunks * stride;
+  float mm = -INFINITY;
+  for (int c = lane; c < a.n_chunks; c += 64) mm = fmaxf(mm, pp[c * stride + a.D]);
+  mm = wave_max(mm);
+  float ll = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int c0 = 0; c0 < a.n_chunks; c0 += 64) {
+    const int c = c0 + lane;
+    float sc = 0.f;
+    if (c < a.n_chunks) {
+      const float mc = pp[c * stride + a.D];
+      if (mc != -INFINITY) {
+        sc = __builtin_amdgcn_exp2f(mc - mm);
+        ll = fmaf(pp[c * stride + a.D + 1], sc, ll);
+      }
+    }
+    sw[lane] = sc;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n = min(64, a.n_chunks - c0);
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) {
+      const float* pc = pp + (c0 + j) * stride;
+      const float sj = sw[j];
+      if (lane < a.D) o0 = fmaf(pc[lane], sj, o0);
+      if (lane + 64 < a.D) o1 = fmaf(pc[lane + 64], sj, o1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  ll = wave_sum(ll);
+  float f = ll > 0.f ? 1.f / ll : 0.f;  // no key (position outside the cache): zero output
+  if (a.row_scale != nullptr && h < a.n_scaled)
+    f *= a.row_scale[static_cast<size_t>(b) * a.n_scaled + h];
+  T* out = static_cast<T*>(a.s) + static_cast<size_t>(b) * a.ld_s + static_cast<size_t>(h) * a.D;
+  if (lane < a.D) out[lane] = from_f32<T>(o0 * f);
+  if (lane + 64 < a.D) out[lane + 64] = from_f32<T>(o1 * f);
+}
+
+// One wave per (sequence, slot head).
+template <typename T>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecAttnArgs a) {
+  __shared__ float sw[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pair = blockIdx.x * 4 + wave;
+  if (pair >= a.B * a.Hq) return;
+  combine_head<T>(a, pair / a.Hq, pair % a.Hq, lane, sw[wave]);
+}
 
 // query head read by slot head h of sequence b: routed slot g*k + j uses
 // expert idx[b, g, j] of group g (head g*E + e); the next slot is the shared
@@ -529,63 +593,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecAttnAr
   }
 }
 
-struct DecCombineArgs {
-  const float* part;      // [B, Hq, n_chunks, D + 2]
-  const float* row_scale; // [B, n_scaled] or NULL: output of head h < n_scaled times this
-  void* s;                // [B, ld_s] slot vectors; head h at columns h*D
-  int B, Hq, n_chunks, D, ld_s, n_scaled;
-};
-
-// One wave per (sequence, slot head): the chunk maxima, then the partial
-// outputs weighted by 2^(m_c - max), 64 chunks at a time (lane = chunk for
-// the weights, lane = head dimension for the sums).
-template <typename T>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecCombineArgs a) {
-  __shared__ float sw[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int pair = blockIdx.x * 4 + wave;
-  if (pair >= a.B * a.Hq) return;
-  const int b = pair / a.Hq, h = pair % a.Hq;
-  const int stride = a.D + 2;
-  const float* pp = a.part + static_cast<size_t>(pair) * a.n_chunks * stride;
-  float mm = -INFINITY;
-  for (int c = lane; c < a.n_chunks; c += 64) mm = fmaxf(mm, pp[c * stride + a.D]);
-  mm = wave_max(mm);
-  float ll = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int c0 = 0; c0 < a.n_chunks; c0 += 64) {
-    const int c = c0 + lane;
-    float sc = 0.f;
-    if (c < a.n_chunks) {
-      const float mc = pp[c * stride + a.D];
-      if (mc != -INFINITY) {
-        sc = __builtin_amdgcn_exp2f(mc - mm);
-        ll = fmaf(pp[c * stride + a.D + 1], sc, ll);
-      }
-    }
-    sw[wave][lane] = sc;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int n = min(64, a.n_chunks - c0);
-#pragma unroll 8
-    for (int j = 0; j < n; ++j) {
-      const float* pc = pp + (c0 + j) * stride;
-      const float s = sw[wave][j];
-      if (lane < a.D) o0 = fmaf(pc[lane], s, o0);
-      if (lane + 64 < a.D) o1 = fmaf(pc[lane + 64], s, o1);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-  ll = wave_sum(ll);
-  float f = ll > 0.f ? 1.f / ll : 0.f;  // no key (position outside the cache): zero output
-  if (a.row_scale != nullptr && h < a.n_scaled) f *= a.row_scale[static_cast<size_t>(b) * a.n_scaled + h];
-  T* out = static_cast<T*>(a.s) + static_cast<size_t>(b) * a.ld_s + static_cast<size_t>(h) * a.D;
-  if (lane < a.D) out[lane] = from_f32<T>(o0 * f);
-  if (lane + 64 < a.D) out[lane + 64] = from_f32<T>(o1 * f);
-}
-
 // ---------------------------------------------------------------------------
 // projections of the new tokens: C[M, N] = A[M, K] . W[N, K]^T
 // ---------------------------------------------------------------------------
@@ -629,15 +636,14 @@ __device__ __forceinline__ typename Frag<T>::type weighted_frag(const T* arow, c
   return load_frag(r);
 }
 
-// Grid (N/32, ceil(M/32)); 4 waves, wave w takes the w-th quarter of the K
-// steps (16 elements each) of the block's 32x32 tile; the four partial tiles
-// are added in LDS and each wave stores a quarter of the result.
+// One 32x32 output tile (rows m0.., columns n0..) per block of 4 waves: wave w
+// takes the w-th quarter of the K steps (16 elements each); the four partial
+// tiles are added in LDS and each wave stores a quarter of the result.
 template <typename T>
-__global__ __launch_bounds__(256) void rows_gemm_kernel(RowsGemmArgs a) {
+__device__ __forceinline__ void gemm_tile(const RowsGemmArgs& a, int n0, int m0) {
   constexpr int U = sizeof(T) == 2 ? 8 : 4;  // K steps whose loads are issued together
   __shared__ float red[4][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
   int seg = 0;
   while (seg < 2 && n0 >= a.n_end[seg]) ++seg;
   const int nb = seg == 0 ? 0 : a.n_end[seg - 1];
@@ -700,6 +706,34 @@ __global__ __launch_bounds__(256) void rows_gemm_kernel(RowsGemmArgs a) {
   }
 }
 
+// grid (N/32, ceil(M/32))
+template <typename T>
+__global__ __launch_bounds__(256) void rows_gemm_kernel(RowsGemmArgs a) {
+  gemm_tile<T>(a, blockIdx.x * 32, blockIdx.y * 32);
+}
+
+struct FrontArgs {
+  const void* x;          // [B, d] the new tokens
+  const void* wr;         // [G*E, d] router rows, or NULL (no routing)
+  const float* bias;      // [G*E] or NULL
+  int32_t* idx;           // [B, G, k]
+  float* w;               // [B, G, k]
+  int d, G, E, k, renorm;
+  int n_gemm_blocks, gemm_nbx;
+};
+
+// The first launch of a decode step: the projection tiles, then (GQE) one
+// routing block per token.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_front_kernel(RowsGemmArgs g, FrontArgs f) {
+  const int id = blockIdx.x;
+  if (id < f.n_gemm_blocks)
+    gemm_tile<T>(g, (id % f.gemm_nbx) * 32, (id / f.gemm_nbx) * 32);
+  else
+    route_token_block<T>(static_cast<const T*>(f.x), static_cast<const T*>(f.wr), f.bias, f.idx,
+                         f.w, id - f.n_gemm_blocks, f.d, f.G, f.E, f.k, f.renorm);
+}
+
 template <typename T>
 hipError_t launch_rows_gemm(const RowsGemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
@@ -748,7 +782,7 @@ int decode_chunk(int B, int G, int Lc) {
 }
 
 template <typename T>
-hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode_front(const DecodeParams& p, hipStream_t stream) {
   RowsGemmArgs ga = {};
   ga.a = p.x;
   ga.lda = p.d;
@@ -770,7 +804,23 @@ hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t stream) {
   ga.G = p.G;
   ga.D = p.D;
   ga.Lc = p.Lc;
-  return launch_rows_gemm<T>(ga, stream);
+  if (ga.N % 32 != 0 || ga.K % 16 != 0) return hipErrorInvalidValue;
+  FrontArgs f = {};
+  f.x = p.x;
+  f.wr = p.wr;
+  f.bias = p.router_bias;
+  f.idx = const_cast<int32_t*>(p.idx);
+  f.w = const_cast<float*>(p.w);
+  f.d = p.d;
+  f.G = p.G;
+  f.E = p.E;
+  f.k = p.k;
+  f.renorm = p.renorm;
+  f.gemm_nbx = ga.N / 32;
+  f.n_gemm_blocks = f.gemm_nbx * ((p.B + 31) / 32);
+  const int blocks = f.n_gemm_blocks + (p.wr != nullptr ? p.B : 0);
+  hipLaunchKernelGGL(decode_front_kernel<T>, dim3(blocks), dim3(256), 0, stream, ga, f);
+  return hipGetLastError();
 }
 
 template <typename T>
@@ -796,6 +846,10 @@ hipError_t launch_decode_attend(const DecodeParams& p, hipStream_t stream) {
   aa.extra_head = p.shared_head ? p.n_routed : -1;
   aa.extra_group = p.shared_kv_group;
   aa.scale_log2 = p.scale * kLog2e;
+  aa.row_scale = p.row_scale;
+  aa.s = p.s;
+  aa.ld_s = p.ld_s;
+  aa.n_scaled = p.n_routed;
   hipError_t e;
   switch (p.D) {
     case 32: e = launch_decode_attn_d<T, 32>(aa, stream); break;
@@ -804,21 +858,9 @@ hipError_t launch_decode_attend(const DecodeParams& p, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-
-  DecCombineArgs ca;
-  ca.part = p.part;
-  ca.row_scale = p.row_scale;
-  ca.s = p.s;
-  ca.B = p.B;
-  ca.Hq = p.Hq;
-  ca.n_chunks = aa.n_chunks;
-  ca.D = p.D;
-  ca.ld_s = p.ld_s;
-  ca.n_scaled = p.n_routed;
   hipLaunchKernelGGL(decode_combine_kernel<T>, dim3((p.B * p.Hq + 3) / 4), dim3(256), 0, stream,
-                     ca);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                     aa);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
 
   RowsGemmArgs ga = {};
   ga.a = p.s;
@@ -838,8 +880,8 @@ hipError_t launch_decode_attend(const DecodeParams& p, hipStream_t stream) {
   return launch_rows_gemm<T>(ga, stream);
 }
 
-template hipError_t launch_decode_qkv<bf16_t>(const DecodeParams&, hipStream_t);
-template hipError_t launch_decode_qkv<float>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_front<bf16_t>(const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_front<float>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_attend<bf16_t>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_attend<float>(const DecodeParams&, hipStream_t);
 

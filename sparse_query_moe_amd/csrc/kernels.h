@@ -20,13 +20,6 @@ hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* id
                          int n_tokens, int d, int G, int E, int k, bool renorm,
                          hipStream_t stream);
 
-// The same routing for a few tokens (decode): one block per token, logits
-// summed over the model dimension in a different (fixed) float64 order.
-template <typename T>
-hipError_t launch_router_tokens(const T* x, const T* wr, const float* bias, int32_t* idx,
-                                float* w, int n_tokens, int d, int G, int E, int k, bool renorm,
-                                hipStream_t stream);
-
 // ---- K2 dispatch -------------------------------------------------------------
 int dispatch_chunks(int L);
 hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* counts,
@@ -98,8 +91,11 @@ struct DecodeParams {
   const void* wk;         // [G*D, d]
   const void* wv;         // [G*D, d]
   const void* wo;         // [d, K_out]
-  const int32_t* idx;     // [B, G, k] routed experts, or NULL (GQA: every head)
-  const float* w;         // [B, G, k] routing weights (GQE) or NULL
+  const void* wr;         // [G*E, d] router rows (GQE) or NULL (GQA: no routing)
+  const float* router_bias;  // [G*E] or NULL
+  int renorm;             // routing weights renormalized over the k selected
+  int32_t* idx;           // [B, G, k] routed experts, or NULL (GQA: every head)
+  float* w;               // [B, G, k] routing weights (GQE) or NULL
   const int32_t* pos;     // [B] position of each new token in its cache
   float* q;               // [B, q_heads, D] scratch: every query head's projection
   void* k_cache;          // [B, G, Lc, D]
@@ -122,11 +118,12 @@ struct DecodeParams {
 };
 // keys per decode attention block for B sequences of G groups in a cache of Lc
 int decode_chunk(int B, int G, int Lc);
-// the projections (query heads into q, K and V^T into the caches at pos) ...
+// routing and projections (query heads into q, K and V^T into the caches at
+// pos) in one launch ...
 template <typename T>
-hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t stream);
-// ... then, once the routing (idx, w) is there too, attention, slot vectors
-// and the output projection
+hipError_t launch_decode_front(const DecodeParams& p, hipStream_t stream);
+// ... then attention, the merge of its partials into slot vectors, and the
+// output projection
 template <typename T>
 hipError_t launch_decode_attend(const DecodeParams& p, hipStream_t stream);
 

@@ -27,6 +27,7 @@
 // experts ahead of it), which needs no per-thread arrays.
 #include "device_common.h"
 #include "kernels.h"
+#include "routing.h"
 
 namespace gqe {
 
@@ -35,50 +36,6 @@ namespace {
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTok = 16;
-
-// 8 elements of T as raw 16-byte words: one for bf16, two for fp32
-template <typename T> struct U4Count { static constexpr int n = sizeof(T) == 2 ? 1 : 2; };
-
-// widen 8 stored elements to float64 (exact)
-template <typename T>
-__device__ __forceinline__ void widen8(const uint4 (&r)[U4Count<T>::n], double (&v)[8]) {
-  if constexpr (sizeof(T) == 2) {
-    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = static_cast<double>(__uint_as_float(w[j] << 16));
-      v[2 * j + 1] = static_cast<double>(__uint_as_float(w[j] & 0xffff0000u));
-    }
-  } else {
-    const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = static_cast<double>(__uint_as_float(w[j]));
-  }
-}
-
-// In-group selection from the E float64 logits r of one (token, group): the k
-// largest, best first (rank of e = experts with a larger logit, or an equal
-// one and a lower index), and their weights exp(r_e - max) / z with z summed
-// over the selected k (renormalized) or over all E (the softmax itself).
-__device__ __forceinline__ void select_group(const double* r, int E, int k, int renorm,
-                                             int32_t* idx_out, float* w_out, size_t o) {
-  double rmax = r[0];
-  for (int e = 1; e < E; ++e) rmax = fmax(rmax, r[e]);
-  double z = 0.0;
-  for (int e = 0; e < E; ++e) {
-    int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
-    if (rank < k || !renorm) z += exp(r[e] - rmax);
-  }
-  for (int e = 0; e < E; ++e) {
-    int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
-    if (rank < k) {
-      idx_out[o + rank] = e;
-      w_out[o + rank] = static_cast<float>(exp(r[e] - rmax) / z);
-    }
-  }
-}
 
 template <typename T>
 __global__ __launch_bounds__(256) void router_topk_kernel(
@@ -153,47 +110,6 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
 }
 
-// One token per block (the decode step's few tokens): wave w forms the
-// logits of experts w, w+4, ...; lane l accumulates model dims 8l + 512i in
-// float64 (exact products of bf16/fp32 inputs) and the wave sums the lanes in
-// a fixed butterfly order.
-template <typename T>
-__global__ __launch_bounds__(256) void router_token_kernel(
-    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int d, int G, int E, int k,
-    int renorm) {
-  __shared__ double logit[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = blockIdx.x;
-  const int GE = G * E;
-  constexpr int kU4 = U4Count<T>::n;
-  const T* xp = x + static_cast<size_t>(t) * d;
-  for (int e = wave; e < GE; e += 4) {
-    const T* wp = wr + static_cast<size_t>(e) * d;
-    double acc = 0.0;
-    for (int d0 = 8 * lane; d0 < d; d0 += 512) {
-      uint4 rx[kU4], rw[kU4];
-#pragma unroll
-      for (int q = 0; q < kU4; ++q) {
-        rx[q] = reinterpret_cast<const uint4*>(xp + d0)[q];
-        rw[q] = reinterpret_cast<const uint4*>(wp + d0)[q];
-      }
-      double xv[8], wv[8];
-      widen8<T>(rx, xv);
-      widen8<T>(rw, wv);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fma(xv[j], wv[j], acc);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0) logit[e] = acc + (bias ? static_cast<double>(bias[e]) : 0.0);
-  }
-  __syncthreads();
-  if (tid < G)
-    select_group(&logit[tid * E], E, k, renorm, idx_out, w_out,
-                 (static_cast<size_t>(t) * G + tid) * k);
-}
-
 }  // namespace
 
 template <typename T>
@@ -207,22 +123,6 @@ hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* id
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_router_tokens(const T* x, const T* wr, const float* bias, int32_t* idx,
-                                float* w, int n_tokens, int d, int G, int E, int k, bool renorm,
-                                hipStream_t stream) {
-  if (n_tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_token_kernel<T>, dim3(n_tokens), dim3(256), 0, stream, x, wr, bias,
-                     idx, w, d, G, E, k, renorm ? 1 : 0);
-  return hipGetLastError();
-}
-
-template hipError_t launch_router_tokens<bf16_t>(const bf16_t*, const bf16_t*, const float*,
-                                                 int32_t*, float*, int, int, int, int, int, bool,
-                                                 hipStream_t);
-template hipError_t launch_router_tokens<float>(const float*, const float*, const float*,
-                                                int32_t*, float*, int, int, int, int, int, bool,
-                                                hipStream_t);
 template hipError_t launch_router<bf16_t>(const bf16_t*, const bf16_t*, const float*, int32_t*,
                                           float*, int, int, int, int, int, bool, hipStream_t);
 template hipError_t launch_router<float>(const float*, const float*, const float*, int32_t*,
