@@ -228,6 +228,67 @@ def measure(wl, gqe, torch, steps, warmup, graph=True):
     return r, res
 
 
+def measure_decode(gqe, torch, steps, warmup, name="dec_b64_c8k"):
+    """One decode step (gqe_decode / gqa_decode): every sequence's new token
+    at the last cache position, so each step reads the whole cache.  Returns
+    step times, tokens/s and the HBM rate over the algorithmic bytes (the K
+    and V^T cache once, every weight once)."""
+    wl = W.DECODE_WORKLOADS[name]
+    I = W.make_decode_inputs(wl, with_gqa=True)
+    I["pos"][:] = wl.seq_len - 1
+    B, Lc, d, G, E, k, D = (wl.batch, wl.seq_len, wl.d_model, wl.n_groups, wl.n_experts,
+                            wl.top_k, wl.head_dim)
+    cfg = gqe.make_config(B, Lc, d, G, E, k, D, dtype=wl.dtype)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to("cuda")
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    # timing only: the V^T cache holds the drawn values in its own tiled shape
+    assert Lc % 64 == 0
+    vt = I["v_cache"].reshape(B, G, Lc // 64, D, 64)
+    x, wq, wk, wv, wr, wo = (dev(I[n]) for n in ("x", "wq", "wk", "wv", "wr", "wo"))
+    wqd, wod = dev(I["wq_dense"]), dev(I["wo_dense"])
+    kc, vtc = dev(I["k_cache"]), dev(vt)
+    pos = torch.from_numpy(I["pos"].astype(np.int32)).cuda()
+    out = torch.empty((B, d), dtype=cfg.torch_dtype, device="cuda")
+    ws = gqe.alloc_decode_workspace(cfg)
+    ws_d = gqe.alloc_decode_workspace(cfg, dense=True)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    t_gqe = timed(lambda: gqe.gqe_decode(cfg, x, wq, wk, wv, wr, wo, kc, vtc, pos, out, ws))
+    t_gqa = timed(lambda: gqe.gqa_decode(cfg, x, wqd, wk, wv, wod, kc, vtc, pos, out, ws_d))
+    es = 2 if wl.dtype == W.BF16 else 4
+    kv = B * G * Lc * D * 2 * es
+    w_gqe = ((G * E + 1) * D + 2 * G * D + G * E) * d * es + d * (k * G + 2) * D * es
+    w_gqa = (G * E * D + 2 * G * D) * d * es + d * G * E * D * es
+    del kc, vtc, ws, ws_d
+    torch.cuda.empty_cache()
+    return {
+        "workload": wl.description, "batch": B, "cache_len": Lc,
+        "gqe_step_ms": round(t_gqe, 5), "gqa_step_ms": round(t_gqa, 5),
+        "gqe_tokens_per_s": round(B / (t_gqe * 1e-3), 1),
+        "gqa_tokens_per_s": round(B / (t_gqa * 1e-3), 1),
+        "speedup_vs_gqa": round(t_gqa / t_gqe, 4),
+        "gqe_hbm_tb_per_s": round((kv + w_gqe) / (t_gqe * 1e-3) / 1e12, 3),
+        "gqa_hbm_tb_per_s": round((kv + w_gqa) / (t_gqa * 1e-3) / 1e12, 3),
+        "bytes_per_step": {"kv_cache": kv, "gqe_weights": w_gqe, "gqa_weights": w_gqa},
+    }
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.txt")
 KERNEL_SOURCES = ("attention.hip", "device_common.h", "kernels.h")
 
@@ -308,6 +369,7 @@ def main():
     ap.add_argument("--long", action="store_true", help="also time the 1M-token workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB three times (the known-size "
                          "kernel that calibrates HBM byte counters)")
@@ -377,6 +439,10 @@ def main():
         "per_length": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
                        for r in per_length],
     }
+    if not args.no_decode:
+        log("[bench] decode step ...")
+        line["decode"] = measure_decode(gqe, torch, args.steps, args.warmup)
+        log(f"[bench]   decode {line['decode']}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(wl)
