@@ -230,8 +230,9 @@ int gqa_forward(const gqe_config* cfg, const void* x, const void* Wq, const void
  *   out       dtype [B, d_model]
  *
  * The step writes the new token's key and value into both caches at pos[b]
- * (caller-owned, updated in place), routes the tokens exactly as gqe_route
- * does (renormalized weights, or p for GQE_OUTPUT_WEIGHTED_CONCAT), lets
+ * (caller-owned, updated in place), routes the tokens as gqe_route does
+ * (float64 logits, summed in another fixed order; renormalized weights, or p
+ * for GQE_OUTPUT_WEIGHTED_CONCAT), lets
  * every active query head attend to cache positions 0..pos[b] of its group,
  * and projects the slot vectors through Wo as gqe_output does.  pos is read
  * on the device only: a pos[b] outside [0, Lc) touches no cache entry and
