@@ -1,4 +1,5 @@
-"""CPU float64 oracle for the Grouped Query Experts (GQE) attention layer, prefill forward.
+"""CPU float64 oracle for the Grouped Query Experts (GQE) attention layer: prefill
+forward, decode step and backward.
 
 TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg
 of the benchmark may import or run this module; the product path never does.
@@ -469,3 +470,188 @@ def gqa_decode_step(x_t, k_cache, v_cache, pos, wq_dense, wk, wv, wo_dense, n_gr
                                            scale)[0]
     y = output_projection(o_all.reshape(B, H * dh), wo_dense)
     return dict(k_new=k_new, v_new=v_new, k_cache=kc, v_cache=vc, o=o_all, y=y)
+
+
+# --------------------------------------------------------------------------
+# backward: gradients of  <y, dy> + aux_weight * L_aux
+# --------------------------------------------------------------------------
+# [gist-nl] "Architectuur en Routing" and "Training en Loss": the discrete
+# top-k choice has no gradient; the language-model loss reaches the router
+# only through the weighted slot (step 9), and an auxiliary load-balancing
+# loss pushes every group's router to spread its tokens over the experts.
+# The pages give no formula for that loss.  The reading taken is the usual
+# product of the routed fraction and the mean router probability, per group,
+# averaged over groups and scaled by E (1 at a perfectly even load):
+#     L_aux = (E / G) * sum_g sum_e f[g, e] * P[g, e]
+#     f[g, e] = (routed slots of group g that chose e) / (B * L * k)
+#     P[g, e] = mean over all tokens of p[t, g, e]
+# f is a count and carries no gradient; P carries it through p.
+
+
+def load_balance_loss(p: np.ndarray, idx: np.ndarray, n_experts: int):
+    """L_aux, f [G, E] and P [G, E] from p [..., G, E] and idx [..., G, k]."""
+    G, E = p.shape[-2], n_experts
+    k = idx.shape[-1]
+    pt = p.reshape(-1, G, E)
+    it = idx.reshape(-1, G, k)
+    T = pt.shape[0]
+    f = np.zeros((G, E))
+    for g in range(G):
+        f[g] = np.bincount(it[:, g, :].reshape(-1), minlength=E)[:E] / (T * k)
+    P = pt.mean(axis=0)
+    return (E / G) * float((f * P).sum()), f, P
+
+
+def softmax_backward(prob: np.ndarray, dprob: np.ndarray) -> np.ndarray:
+    """Gradient on the logits of prob = softmax(logits) over the last axis."""
+    return prob * (dprob - (prob * dprob).sum(axis=-1, keepdims=True))
+
+
+def attention_backward(q, t, K, V, do, scale):
+    """Gradients of o = causal_attention(q, t, K, V, scale) given do.
+
+    q, do [n, d_h] at positions t; K, V [upto, d_h].  Returns dq [n, d_h],
+    dK and dV [upto, d_h].  The probabilities P are formed again, exactly;
+    with dP = do . V^T, the score gradient is P * (dP - rowsum(dP * P)).
+    """
+    upto = K.shape[0]
+    s = scale * (q @ K.T)
+    s[np.arange(upto)[None, :] > t[:, None]] = -np.inf
+    P = np.exp(s - s.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    dV = P.T @ do
+    dP = do @ V.T
+    dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
+    return scale * (dS @ K), scale * (dS.T @ q), dV
+
+
+def gqe_backward(x, wq, wk, wv, wr, wo, br, dy, n_groups, n_experts, top_k, head_dim,
+                 shared_kv_group=0, scale=None, output_mode="full", aux_weight=0.0):
+    """Gradients of <y, dy> + aux_weight * L_aux for the GQE layer (float64).
+
+    Returns dx [B, L, d], dwq, dwk, dwv, dwr, dbr, dwo (the shapes of the
+    weights), aux_loss, and the intermediates: ds (slot-vector gradient),
+    do [B, L, S, d_h] (attention-output gradient per slot-head), dq
+    [B, L, S, d_h], dk and dv [B, G, L, d_h], dw [B, L, G, k] (routing-weight
+    gradient; the in-group probability of the selected experts for
+    "weighted_concat"), dr [B, L, G, E] (logit gradient), and the forward
+    dict under "fwd".
+    """
+    if output_mode not in OUTPUT_MODES:
+        raise ValueError(output_mode)
+    full = output_mode == "full"
+    B, L, d = x.shape
+    G, E, k, dh = n_groups, n_experts, top_k, head_dim
+    kG = k * G
+    sc = 1.0 / math.sqrt(dh) if scale is None else scale
+    fwd = gqe_forward(x, wq, wk, wv, wr, wo, br, G, E, k, dh, shared_kv_group=shared_kv_group,
+                      scale=scale, output_mode=output_mode)
+    p, idx, w, s_all, o_all = fwd["p"], fwd["idx"], fwd["w"], fwd["s"], fwd["o"]
+    Sh = o_all.shape[2]
+    dwo = np.einsum("bln,blc->nc", dy, s_all)             # y = s . W_O^T
+    ds = dy @ wo
+    dx = np.zeros_like(x)
+    dwq, dwk, dwv = np.zeros_like(wq), np.zeros_like(wk), np.zeros_like(wv)
+    dr = np.zeros((B, L, G, E))
+    dw_all = np.zeros((B, L, G, k))
+    do_all = np.zeros((B, L, Sh, dh))
+    dq_all = np.zeros((B, L, Sh, dh))
+    dk_all = np.zeros((B, G, L, dh))
+    dv_all = np.zeros((B, G, L, dh))
+    tpos = np.arange(L)
+    for b in range(B):
+        o_hard = o_all[b, :, :kG].reshape(L, G, k, dh)
+        ds_h = ds[b, :, :kG * dh].reshape(L, G, k, dh)
+        if full:                                          # steps 9-10 backwards
+            ds_w = ds[b, :, (kG + 1) * dh:]
+            do_hard = ds_h + w[b][..., None] * ds_w[:, None, None, :]
+            dw = np.einsum("lgjd,ld->lgj", o_hard, ds_w)
+            dr_sel = softmax_backward(w[b], dw)          # w = softmax of the selected logits
+            np.put_along_axis(dr[b], idx[b].astype(np.int64), dr_sel, axis=-1)
+        elif output_mode == "weighted_concat":
+            p_sel = np.take_along_axis(p[b], idx[b].astype(np.int64), axis=-1)
+            do_hard = p_sel[..., None] * ds_h
+            dw = np.einsum("lgjd,lgjd->lgj", o_hard, ds_h)
+            dp = np.zeros((L, G, E))
+            np.put_along_axis(dp, idx[b].astype(np.int64), dw, axis=-1)
+            dr[b] += softmax_backward(p[b], dp)          # p = softmax over all E
+        else:
+            do_hard = ds_h
+            dw = np.zeros((L, G, k))
+        dw_all[b] = dw
+        do_all[b, :, :kG] = do_hard.reshape(L, kG, dh)
+        xb = x[b]
+        K = fwd["k_"][b]
+        V = fwd["v"][b]
+        heads = [(g * k + j, g) for g in range(G) for j in range(k)]
+        if full:
+            do_all[b, :, kG] = ds[b, :, kG * dh:(kG + 1) * dh]
+            heads.append((kG, shared_kv_group))
+        for h, g in heads:
+            dq, dKg, dVg = attention_backward(fwd["q"][b, :, h], tpos, K[g], V[g],
+                                              do_all[b, :, h], sc)
+            dq_all[b, :, h] = dq
+            dk_all[b, g] += dKg
+            dv_all[b, g] += dVg
+            if h == kG:                                   # the shared head's own W_q rows
+                rows = slice(G * E * dh, (G * E + 1) * dh)
+                dwq[rows] += dq.T @ xb
+                dx[b] += dq @ wq[rows]
+                continue
+            j = h % k
+            for e in range(E):
+                m = idx[b, :, g, j] == e
+                if m.any():
+                    rows = slice(expert_head(g, e, E) * dh, (expert_head(g, e, E) + 1) * dh)
+                    dwq[rows] += dq[m].T @ xb[m]
+                    dx[b][m] += dq[m] @ wq[rows]
+        for g in range(G):                                # K, V = x . W_k^T, x . W_v^T
+            rows = slice(g * dh, (g + 1) * dh)
+            dwk[rows] += dk_all[b, g].T @ xb
+            dwv[rows] += dv_all[b, g].T @ xb
+            dx[b] += dk_all[b, g] @ wk[rows] + dv_all[b, g] @ wv[rows]
+    aux_loss, f, _ = load_balance_loss(p, idx, E)
+    if aux_weight:
+        dp_aux = np.broadcast_to(aux_weight * (E / G) * f / (B * L), p.shape)
+        dr += softmax_backward(p, dp_aux)
+    drf = dr.reshape(B * L, G * E)
+    dwr = drf.T @ x.reshape(B * L, d)                     # r = x . W_r^T + b_r
+    dbr = drf.sum(axis=0)
+    dx += (drf @ wr).reshape(B, L, d)
+    return dict(dx=dx, dwq=dwq, dwk=dwk, dwv=dwv, dwr=dwr, dbr=dbr, dwo=dwo, aux_loss=aux_loss,
+                ds=ds, do=do_all, dq=dq_all, dk=dk_all, dv=dv_all, dw=dw_all, dr=dr, fwd=fwd)
+
+
+def gqa_backward(x, wq_dense, wk, wv, wo_dense, dy, n_groups, n_experts, head_dim, scale=None):
+    """Gradients of <y, dy> for the dense GQA baseline: dx, dwq, dwk, dwv, dwo."""
+    B, L, d = x.shape
+    G, E, dh = n_groups, n_experts, head_dim
+    H = G * E
+    sc = 1.0 / math.sqrt(dh) if scale is None else scale
+    fwd = gqa_forward(x, wq_dense, wk, wv, wo_dense, G, E, dh, scale=scale)
+    o = fwd["o"].reshape(B, L, H * dh)
+    dwo = np.einsum("bln,blc->nc", dy, o)
+    do = (dy @ wo_dense).reshape(B, L, H, dh)
+    dx = np.zeros_like(x)
+    dwq, dwk, dwv = np.zeros_like(wq_dense), np.zeros_like(wk), np.zeros_like(wv)
+    tpos = np.arange(L)
+    for b in range(B):
+        xb = x[b]
+        K = kv_project(xb, wk, G, dh, L)
+        V = kv_project(xb, wv, G, dh, L)
+        dK = np.zeros((G, L, dh))
+        dV = np.zeros((G, L, dh))
+        for h in range(H):
+            g = h // E
+            dq, dKg, dVg = attention_backward(fwd["q"][b, :, h], tpos, K[g], V[g], do[b, :, h], sc)
+            dK[g] += dKg
+            dV[g] += dVg
+            rows = slice(h * dh, (h + 1) * dh)
+            dwq[rows] += dq.T @ xb
+            dx[b] += dq @ wq_dense[rows]
+        for g in range(G):
+            rows = slice(g * dh, (g + 1) * dh)
+            dwk[rows] += dK[g].T @ xb
+            dwv[rows] += dV[g].T @ xb
+            dx[b] += dK[g] @ wk[rows] + dV[g] @ wv[rows]
+    return dict(dx=dx, dwq=dwq, dwk=dwk, dwv=dwv, dwo=dwo, do=do, fwd=fwd)

@@ -470,6 +470,100 @@ def pin_decode_step_is_prefill_row(orc):
         assert np.allclose(dec["y"][b], pre["y"][b, pos[b]], rtol=0, atol=1e-12)
 
 
+
+# ---------------------------------------------------------------------------
+# backward: the gradients are those of the forward (finite differences), and
+# they respect the invariances of the layer
+# ---------------------------------------------------------------------------
+
+def _total_loss(orc, t, dy, alpha, **kw):
+    """<y, dy> + alpha * L_aux, the scalar whose gradients the backward returns."""
+    f = run(orc, t, **kw)
+    aux = orc.load_balance_loss(f["p"], f["idx"], t["E"])[0]
+    return float((f["y"] * dy).sum()) + alpha * aux
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of <y, dy> + alpha * L_aux agree with the backward on
+    every parameter tensor and on x, for every output construction (the
+    weighted slot is the router's differentiable path, gist.science Training
+    en Loss), with a non-default shared group and scale; and for dense GQA."""
+    rng = np.random.default_rng(57)
+    h = 1e-6
+    for mode, kw in (("full", dict(shared_kv_group=1, scale=0.7)), ("hard", {}),
+                     ("weighted_concat", {})):
+        t = tiny_layer(rng, B=2, L=5, d=6, G=2, E=3, k=2, dh=4)
+        t["br"] = rng.standard_normal(t["G"] * t["E"]) * 0.3
+        if mode != "full":
+            t["wo"] = np.ascontiguousarray(t["wo"][:, :t["k"] * t["G"] * t["dh"]])
+        f0 = run(orc, t, output_mode=mode, **kw)
+        srt = -np.sort(-f0["r"], axis=-1)
+        assert (srt[..., :-1] - srt[..., 1:]).min() > 1e-3, "seed too close to a routing tie"
+        dy = rng.standard_normal(f0["y"].shape)
+        alpha = 0.3
+        g = orc.gqe_backward(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"], dy,
+                             t["G"], t["E"], t["k"], t["dh"], output_mode=mode,
+                             aux_weight=alpha, **kw)
+        for name, key in (("x", "dx"), ("wq", "dwq"), ("wk", "dwk"), ("wv", "dwv"),
+                          ("wr", "dwr"), ("br", "dbr"), ("wo", "dwo")):
+            arr = t[name]
+            flat = arr.reshape(-1)
+            for i in rng.choice(flat.size, size=min(flat.size, 24), replace=False):
+                old = flat[i]
+                flat[i] = old + h
+                lp = _total_loss(orc, t, dy, alpha, output_mode=mode, **kw)
+                flat[i] = old - h
+                lm = _total_loss(orc, t, dy, alpha, output_mode=mode, **kw)
+                flat[i] = old
+                num = (lp - lm) / (2 * h)
+                ana = g[key].reshape(-1)[i]
+                assert abs(num - ana) <= 1e-6 * (1.0 + abs(num)), (mode, name, i, num, ana)
+    # dense GQA
+    t = tiny_layer(rng, B=1, L=6, d=6, G=2, E=2, k=1, dh=4)
+    wq_d = t["wq"][:4 * 4].copy()
+    wo_d = rng.standard_normal((6, 4 * 4))
+    dy = rng.standard_normal((1, 6, 6))
+    g = orc.gqa_backward(t["x"], wq_d, t["wk"], t["wv"], wo_d, dy, 2, 2, 4)
+    for arr, key in ((t["x"], "dx"), (wq_d, "dwq"), (t["wk"], "dwk"), (t["wv"], "dwv"),
+                     (wo_d, "dwo")):
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(flat.size, 16), replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp = float((orc.gqa_forward(t["x"], wq_d, t["wk"], t["wv"], wo_d, 2, 2, 4)["y"] * dy).sum())
+            flat[i] = old - h
+            lm = float((orc.gqa_forward(t["x"], wq_d, t["wk"], t["wv"], wo_d, 2, 2, 4)["y"] * dy).sum())
+            flat[i] = old
+            num = (lp - lm) / (2 * h)
+            assert abs(num - g[key].reshape(-1)[i]) <= 1e-6 * (1.0 + abs(num)), ("gqa", key, i)
+
+
+def pin_backward_invariances(orc):
+    """Shifting every key of a group by one vector, or every logit of a (token,
+    group) by one constant, leaves y unchanged, so the key gradient of each
+    group sums to zero over positions and the logit gradient of each (token,
+    group) sums to zero over experts.  With dy = 0 and a uniform router
+    (ties to the lower index: experts 0..k-1), the auxiliary loss alone gives
+    the logit gradient alpha / (G T) * (f_e - 1/E) with f_e = 1/k for e < k."""
+    rng = np.random.default_rng(61)
+    t = tiny_layer(rng, B=2, L=9, d=8, G=2, E=4, k=2, dh=4)
+    f = run(orc, t)
+    dy = rng.standard_normal(f["y"].shape)
+    g = orc.gqe_backward(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"], dy,
+                         t["G"], t["E"], t["k"], t["dh"], aux_weight=0.2)
+    assert np.abs(g["dk"].sum(axis=2)).max() < 1e-9
+    assert np.abs(g["dr"].sum(axis=-1)).max() < 1e-12
+    assert np.abs(g["dr"]).max() > 1e-3                      # the router does get a gradient
+    t["wr"] = np.zeros_like(t["wr"])
+    alpha, G, E, k = 0.5, t["G"], t["E"], t["k"]
+    T = t["x"].shape[0] * t["x"].shape[1]
+    g = orc.gqe_backward(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"],
+                         np.zeros_like(dy), G, E, k, t["dh"], aux_weight=alpha)
+    f_e = np.array([1.0 / k if e < k else 0.0 for e in range(E)])
+    want = alpha / (G * T) * (f_e - 1.0 / E)
+    assert np.allclose(g["dr"], np.broadcast_to(want, g["dr"].shape), rtol=0, atol=1e-15)
+    assert abs(g["aux_loss"] - (E / G) * G * sum(f_e / E)) < 1e-12   # = 1 at uniform p
+
 ALL_PINS = [
     pin_k_equals_e_is_dense_gqa,
     pin_weights_sum_to_one,
@@ -489,4 +583,6 @@ ALL_PINS = [
     pin_sampled_rows_match_full,
     pin_ablation_constructions,
     pin_decode_step_is_prefill_row,
+    pin_backward_finite_differences,
+    pin_backward_invariances,
 ]

@@ -203,6 +203,51 @@ def m_decode_stale_cache(mod):
     mod.gqe_decode_step = step
 
 
+def _patch_source(mod, old, new):
+    """Re-execute the oracle's source with one passage replaced (in place)."""
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, old
+    exec(compile(src.replace(old, new), ORACLE_SRC, "exec"), mod.__dict__)
+
+
+def m_bwd_no_rowsum_term(mod):
+    """attention backward without the -rowsum(dP * P) term of the softmax."""
+    _patch_source(mod, "dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))", "dS = P * dP")
+
+
+def m_bwd_dk_unscaled(mod):
+    """key gradient without the attention scale."""
+    _patch_source(mod, "return scale * (dS @ K), scale * (dS.T @ q), dV",
+                  "return scale * (dS @ K), dS.T @ q, dV")
+
+
+def m_bwd_weighted_slot_dropped(mod):
+    """the weighted slot's gradient does not reach the experts' outputs."""
+    _patch_source(mod, "do_hard = ds_h + w[b][..., None] * ds_w[:, None, None, :]",
+                  "do_hard = ds_h")
+
+
+def m_bwd_softmax_jacobian_diagonal(mod):
+    """the router's softmax backward keeps only the diagonal of the Jacobian."""
+    _patch_source(mod, "return prob * (dprob - (prob * dprob).sum(axis=-1, keepdims=True))",
+                  "return prob * dprob")
+
+
+def m_bwd_aux_sign(mod):
+    """the load-balancing gradient with the wrong sign."""
+    _patch_source(mod, "dr += softmax_backward(p, dp_aux)", "dr -= softmax_backward(p, dp_aux)")
+
+
+def m_aux_fraction_per_token(mod):
+    """routed fraction counted per token instead of per routed slot."""
+    _patch_source(mod, "minlength=E)[:E] / (T * k)", "minlength=E)[:E] / T")
+
+
+def m_bwd_shared_head_group0(mod):
+    """the shared head's gradient goes to group 0 whatever shared_kv_group is."""
+    _patch_source(mod, "heads.append((kG, shared_kv_group))", "heads.append((kG, 0))")
+
+
 MUTATIONS = [
     m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
     m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
@@ -212,6 +257,9 @@ MUTATIONS = [
     m_shared_weighted_swapped, m_output_untransposed, m_dispatch_descending,
     m_kv_heads_swapped, m_head_rows_shifted,
     m_wconcat_renormalized, m_wconcat_unscaled, m_hard_rank_reversed, m_decode_stale_cache,
+    m_bwd_no_rowsum_term, m_bwd_dk_unscaled, m_bwd_weighted_slot_dropped,
+    m_bwd_softmax_jacobian_diagonal, m_bwd_aux_sign, m_aux_fraction_per_token,
+    m_bwd_shared_head_group0,
 ]
 
 
