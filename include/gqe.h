@@ -125,10 +125,14 @@ typedef struct gqe_config {
  *                                keys to the matrix cores; the columns of
  *                                keys >= L in the last tile are zero
  *   s       dtype [B, L, (k*G+2)*d_h]  slot vectors (input of W_O)
+ *   lse     float [B, k*G+1, L]  per slot-head row: log2 of the softmax
+ *                                normalizer of its scores scaled by
+ *                                softmax_scale*log2(e) (max + log2 of the sum
+ *                                of 2^(score - max)); read by the backward
  *   the rest is private scratch (dispatch partial counts, tile maps). */
 typedef struct gqe_ws_layout {
   size_t idx, w, counts, offsets, pos, slot;
-  size_t q, k, vt, s;
+  size_t q, k, vt, s, lse;
   size_t scratch;
   size_t total;
   int64_t vt_tiles;
@@ -253,6 +257,46 @@ size_t gqa_decode_workspace_bytes(const gqe_config* cfg);
 int gqa_decode(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
                const void* Wv, const void* Wo, void* k_cache, void* vt_cache, const int32_t* pos,
                void* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Backward: gradients of <y, dy> + aux_weight * L_aux ----------------------
+ *
+ * gist.science, Architectuur en Routing and Training en Loss: the top-k choice
+ * has no gradient; the loss reaches the router through the weighted slot
+ * (through the scaled slots for GQE_OUTPUT_WEIGHTED_CONCAT), and a
+ * load-balancing auxiliary loss spreads each group's tokens over its experts.
+ * The pages give no formula for that loss; L_aux here is
+ *     (E / G) * sum_g sum_e f[g, e] * P[g, e],
+ * f[g, e] = (routed slots of group g that chose e) / (B * L * k), which is a
+ * count and carries no gradient, and P[g, e] = the mean over all tokens of
+ * the in-group softmax p[t, g, e].
+ *
+ * fwd_workspace is the workspace of a gqe_forward (gqa_forward) call on the
+ * same cfg and inputs, unchanged since: the backward reads the routing, the
+ * queries, K, V^T, the slot vectors and the per-row log-sum-exp from it.
+ * dy has the dtype of the layer, [B, L, d_model].  Every gradient is float32,
+ * caller-owned, and overwritten:
+ *   dx [B, L, d_model]; dWq, dWk, dWv, dWr, dWo with the shapes of Wq, Wk,
+ *   Wv, Wr, Wo; dbr [G*E] (gradient of a router bias, whether or not
+ *   cfg->router_bias is set); aux_loss: one float, the value of L_aux.
+ * For the ablation outputs the shared head's rows of dWq are zero.  The
+ * workspace (size from *_backward_workspace_bytes, 16-byte aligned) is
+ * private scratch.  Returns GQE_ERR_INVALID_ARG for a NULL or misaligned
+ * pointer (16 bytes; 4 for dbr and aux_loss) or a negative or infinite
+ * aux_weight, GQE_ERR_WORKSPACE when either workspace is too small, and
+ * GQE_OK with nothing enqueued when B*L == 0. */
+size_t gqe_backward_workspace_bytes(const gqe_config* cfg);
+int gqe_backward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                 const void* Wv, const void* Wr, const void* Wo, const void* dy, float aux_weight,
+                 const void* fwd_workspace, size_t fwd_ws_bytes, float* dx, float* dWq, float* dWk,
+                 float* dWv, float* dWr, float* dbr, float* dWo, float* aux_loss, void* workspace,
+                 size_t ws_bytes, hipStream_t stream);
+
+/* Dense GQA backward (gradients of <y, dy>; no router, no auxiliary loss). */
+size_t gqa_backward_workspace_bytes(const gqe_config* cfg);
+int gqa_backward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                 const void* Wv, const void* Wo, const void* dy, const void* fwd_workspace,
+                 size_t fwd_ws_bytes, float* dx, float* dWq, float* dWk, float* dWv, float* dWo,
+                 void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Static text for a gqe_status value; never NULL. */
 const char* gqe_status_string(int status);

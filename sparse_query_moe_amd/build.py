@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgqe.so")
-SOURCES = ["router.hip", "dispatch.hip", "gemm.hip", "attention.hip", "decode.hip", "api.hip"]
+SOURCES = ["router.hip", "dispatch.hip", "gemm.hip", "attention.hip", "decode.hip", "backward.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

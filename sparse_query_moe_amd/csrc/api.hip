@@ -70,6 +70,13 @@ struct Layout {
   size_t chunk_counts, tile_off;
 };
 
+// slot-heads that attend: every routed slot and the shared head (full
+// output), or all G*E dense heads
+int attn_heads(const gqe_config* c, bool dense) {
+  return dense ? c->n_groups * c->n_experts
+               : c->top_k * c->n_groups + (full_output(c) ? 1 : 0);
+}
+
 // Workspace of gqe_forward (dense == false) or gqa_forward (dense == true).
 Layout make_layout(const gqe_config* c, bool dense) {
   const size_t B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts, k = c->top_k;
@@ -102,6 +109,7 @@ Layout make_layout(const gqe_config* c, bool dense) {
   l.pub.k = take(B * G * L * D * es);
   l.pub.vt = take(B * G * vt_tiles * D * 64 * es);
   l.pub.s = take(B * L * (dense ? G * E : static_cast<size_t>(slot_count(c))) * D * es);
+  l.pub.lse = take(B * L * static_cast<size_t>(attn_heads(c, dense)) * 4);
   if (dense) l.pub.scratch = off;
   l.pub.total = off;
   l.pub.vt_tiles = static_cast<int64_t>(vt_tiles);
@@ -191,6 +199,7 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
   const int G = c->n_groups, E = c->n_experts, k = c->top_k, D = c->head_dim;
   AttnParams p;
   p.row_scale = nullptr;
+  p.lse = at<float>(ws, l.pub.lse);
   p.q = at<T>(ws, l.pub.q);
   p.k = at<T>(ws, l.pub.k);
   p.vt = at<T>(ws, l.pub.vt);
@@ -408,6 +417,166 @@ int decode_entry(const gqe_config* cfg, bool dense, const void* x, const void* W
 
 }  // namespace
 
+namespace {
+
+// ---- backward ------------------------------------------------------------------
+
+struct BwdLayout {
+  size_t gall, w_t, wo_t, ds, dO, dOt, qt, kt, vr, dsum, dw, dr, p_all, psum, gall_t, x_t, dy_t,
+      s_t, total;
+  int tpad, ws, qcols, kcol, vcol, rcol, kcols, kpad, H, q_heads;
+};
+
+BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
+  const size_t B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts, k = c->top_k;
+  const size_t D = c->head_dim, d = c->d_model, es = elem_bytes(c), T = B * L;
+  const size_t tiles = (L + 63) / 64;
+  BwdLayout l{};
+  l.tpad = static_cast<int>((T + 63) / 64 * 64);
+  l.H = attn_heads(c, dense);
+  l.q_heads = dense ? static_cast<int>(G * E) : static_cast<int>(G * k + 1);
+  l.ws = static_cast<int>((dense ? G * E : static_cast<size_t>(slot_count(c))) * D);
+  l.qcols = static_cast<int>((G * E + (dense ? 0 : 1)) * D);
+  l.kcol = l.qcols;
+  l.vcol = l.kcol + static_cast<int>(G * D);
+  l.rcol = l.vcol + static_cast<int>(G * D);
+  l.kcols = l.rcol + (dense ? 0 : static_cast<int>(G * E));
+  l.kpad = (l.kcols + 63) / 64 * 64;
+  const size_t H = l.H, tp = l.tpad, kp = l.kpad, ws = l.ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  l.gall = take(T * kp * es);
+  l.w_t = take(d * kp * es);
+  l.wo_t = take(ws * d * es);
+  l.ds = take(T * ws * 4);
+  l.dO = take(B * H * L * D * es);
+  l.dOt = take(B * H * tiles * D * 64 * es);
+  l.qt = take(B * H * tiles * D * 64 * es);
+  l.kt = take(B * G * tiles * D * 64 * es);
+  l.vr = take(B * G * L * D * es);
+  l.dsum = take(B * H * L * 4);
+  l.dw = take(dense ? 0 : T * G * k * 4);
+  l.dr = take(dense ? 0 : T * G * E * 4);
+  l.p_all = take(dense ? 0 : T * G * E * 4);
+  l.psum = take(dense ? 0 : G * E * 8);
+  l.gall_t = take(kp * tp * es);
+  l.x_t = take(d * tp * es);
+  l.dy_t = take(d * tp * es);
+  l.s_t = take(ws * tp * es);
+  l.total = off;
+  return l;
+}
+
+template <typename T>
+int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq, const void* wk,
+                  const void* wv, const void* wr, const void* wo, const void* dy, float aux_weight,
+                  const void* fws, float* dx, float* dwq, float* dwk, float* dwv, float* dwr,
+                  float* dbr, float* dwo, float* aux_loss, void* ws, hipStream_t stream) {
+  const Layout fl = make_layout(c, dense);
+  const BwdLayout l = make_bwd_layout(c, dense);
+  void* f = const_cast<void*>(fws);
+  const int G = c->n_groups, E = c->n_experts, k = c->top_k;
+  BwdParams p;
+  p.x = x;
+  p.wq = wq;
+  p.wk = wk;
+  p.wv = wv;
+  p.wr = dense ? nullptr : wr;
+  p.router_bias = dense ? nullptr : c->router_bias;
+  p.wo = wo;
+  p.dy = dy;
+  p.idx = dense ? nullptr : at<int32_t>(f, fl.pub.idx);
+  p.w = dense ? nullptr : at<float>(f, fl.pub.w);
+  p.counts = dense ? nullptr : at<int32_t>(f, fl.pub.counts);
+  p.q = at<T>(f, fl.pub.q);
+  p.keys = at<T>(f, fl.pub.k);
+  p.vt = at<T>(f, fl.pub.vt);
+  p.vt_tiles = fl.pub.vt_tiles;
+  p.s = at<T>(f, fl.pub.s);
+  p.lse = at<float>(f, fl.pub.lse);
+  p.dx = dx;
+  p.dwq = dwq;
+  p.dwk = dwk;
+  p.dwv = dwv;
+  p.dwr = dwr;
+  p.dbr = dbr;
+  p.dwo = dwo;
+  p.aux_loss = aux_loss;
+  p.gall = at<T>(ws, l.gall);
+  p.w_t = at<T>(ws, l.w_t);
+  p.wo_t = at<T>(ws, l.wo_t);
+  p.dO = at<T>(ws, l.dO);
+  p.dOt = at<T>(ws, l.dOt);
+  p.qt = at<T>(ws, l.qt);
+  p.kt = at<T>(ws, l.kt);
+  p.vr = at<T>(ws, l.vr);
+  p.gall_t = at<T>(ws, l.gall_t);
+  p.x_t = at<T>(ws, l.x_t);
+  p.dy_t = at<T>(ws, l.dy_t);
+  p.s_t = at<T>(ws, l.s_t);
+  p.ds = at<float>(ws, l.ds);
+  p.dsum = at<float>(ws, l.dsum);
+  p.dw = dense ? nullptr : at<float>(ws, l.dw);
+  p.dr = dense ? nullptr : at<float>(ws, l.dr);
+  p.p_all = dense ? nullptr : at<float>(ws, l.p_all);
+  p.psum = dense ? nullptr : at<double>(ws, l.psum);
+  p.B = c->batch;
+  p.L = c->seq_len;
+  p.d = c->d_model;
+  p.G = G;
+  p.E = E;
+  p.k = k;
+  p.D = c->head_dim;
+  p.H = l.H;
+  p.q_heads = l.q_heads;
+  p.n_routed = dense ? 0 : G * k;
+  p.heads_per_group = dense ? E : k;
+  p.n_grouped = dense ? G * E : G * k;
+  p.extra_group = c->shared_kv_group;
+  p.mode = dense ? 3 : c->output_mode == GQE_OUTPUT_FULL ? 0 : c->output_mode == GQE_OUTPUT_HARD ? 1 : 2;
+  p.ws = l.ws;
+  p.qcols = l.qcols;
+  p.kcol = l.kcol;
+  p.vcol = l.vcol;
+  p.rcol = l.rcol;
+  p.kcols = l.kcols;
+  p.kpad = l.kpad;
+  p.tpad = l.tpad;
+  p.scale = softmax_scale(c);
+  p.aux_weight = dense ? 0.f : aux_weight;
+  return hip_status(launch_backward<T>(p, stream));
+}
+
+int backward_entry(const gqe_config* cfg, bool dense, const void* x, const void* Wq,
+                   const void* Wk, const void* Wv, const void* Wr, const void* Wo, const void* dy,
+                   float aux_weight, const void* fws, size_t fws_bytes, float* dx, float* dWq,
+                   float* dWk, float* dWv, float* dWr, float* dbr, float* dWo, float* aux_loss,
+                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_cfg(cfg);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if (!(aux_weight >= 0.f) || isinf(aux_weight)) return GQE_ERR_INVALID_ARG;
+  const void* need[] = {x, Wq, Wk, Wv, Wo, dy, fws, dx, dWq, dWk, dWv, dWo, ws};
+  for (const void* q : need)
+    if (!aligned16(q)) return GQE_ERR_INVALID_ARG;
+  if (!dense && (!aligned16(Wr) || !aligned16(dWr) || dbr == nullptr || aux_loss == nullptr ||
+                 (reinterpret_cast<uintptr_t>(dbr) & 3u) || (reinterpret_cast<uintptr_t>(aux_loss) & 3u) ||
+                 (cfg->router_bias && (reinterpret_cast<uintptr_t>(cfg->router_bias) & 3u))))
+    return GQE_ERR_INVALID_ARG;
+  if (fws_bytes < make_layout(cfg, dense).pub.total) return GQE_ERR_WORKSPACE;
+  if (ws_bytes < make_bwd_layout(cfg, dense).total) return GQE_ERR_WORKSPACE;
+  return cfg->dtype == GQE_DTYPE_BF16
+             ? backward_impl<bf16_t>(cfg, dense, x, Wq, Wk, Wv, Wr, Wo, dy, aux_weight, fws, dx,
+                                     dWq, dWk, dWv, dWr, dbr, dWo, aux_loss, ws, stream)
+             : backward_impl<float>(cfg, dense, x, Wq, Wk, Wv, Wr, Wo, dy, aux_weight, fws, dx,
+                                    dWq, dWk, dWv, dWr, dbr, dWo, aux_loss, ws, stream);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* gqe_status_string(int status) {
@@ -603,6 +772,35 @@ int gqa_decode(const gqe_config* cfg, const void* x, const void* Wq, const void*
                void* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return decode_entry(cfg, true, x, Wq, Wk, Wv, nullptr, Wo, k_cache, vt_cache, pos, out,
                       workspace, ws_bytes, stream);
+}
+
+size_t gqe_backward_workspace_bytes(const gqe_config* cfg) {
+  if (check_cfg(cfg) != GQE_OK) return 0;
+  return make_bwd_layout(cfg, false).total;
+}
+
+size_t gqa_backward_workspace_bytes(const gqe_config* cfg) {
+  if (check_cfg(cfg) != GQE_OK) return 0;
+  return make_bwd_layout(cfg, true).total;
+}
+
+int gqe_backward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                 const void* Wv, const void* Wr, const void* Wo, const void* dy, float aux_weight,
+                 const void* fwd_workspace, size_t fwd_ws_bytes, float* dx, float* dWq, float* dWk,
+                 float* dWv, float* dWr, float* dbr, float* dWo, float* aux_loss, void* workspace,
+                 size_t ws_bytes, hipStream_t stream) {
+  return backward_entry(cfg, false, x, Wq, Wk, Wv, Wr, Wo, dy, aux_weight, fwd_workspace,
+                        fwd_ws_bytes, dx, dWq, dWk, dWv, dWr, dbr, dWo, aux_loss, workspace,
+                        ws_bytes, stream);
+}
+
+int gqa_backward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                 const void* Wv, const void* Wo, const void* dy, const void* fwd_workspace,
+                 size_t fwd_ws_bytes, float* dx, float* dWq, float* dWk, float* dWv, float* dWo,
+                 void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return backward_entry(cfg, true, x, Wq, Wk, Wv, nullptr, Wo, dy, 0.f, fwd_workspace,
+                        fwd_ws_bytes, dx, dWq, dWk, dWv, nullptr, nullptr, dWo, nullptr, workspace,
+                        ws_bytes, stream);
 }
 
 }  // extern "C"

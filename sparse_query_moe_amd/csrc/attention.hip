@@ -308,6 +308,7 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
       float mmax = m_run[qb];
       for (int gs = 1; gs < NS; ++gs) mmax = fmaxf(mmax, slot_of(gs, qb)[S::NDB * 16 * 64 + lane]);
       const float a0 = __builtin_amdgcn_exp2f(m_run[qb] - mmax);
+      m_run[qb] = mmax;
       l_run[qb] *= a0;
 #pragma unroll
       for (int db = 0; db < S::NDB; ++db)
@@ -328,6 +329,10 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    // log-sum-exp of the row's scores (log2 units, as the pre-scaled scores)
+    // for the backward pass; both lanes of a row hold the same m_run
+    if (p.lse != nullptr && half == 0 && qrow[qb] < L)
+      p.lse[(static_cast<size_t>(b) * p.H + head) * L + qrow[qb]] = m_run[qb] + log2f(l_tot);
     if (qrow[qb] < L) {
       float inv = 1.f / l_tot;
       if (p.row_scale != nullptr && head < p.n_grouped)

@@ -1,0 +1,865 @@
+// Backward pass of the GQE layer (and of dense GQA): the gradients of
+// <y, dy> + aux_weight * L_aux with respect to x and every weight.
+//
+// gist.science, Architectuur en Routing and Training en Loss: the discrete
+// top-k choice has no gradient, the language-model loss reaches the router
+// through the weighted slot, and a load-balancing auxiliary loss spreads each
+// group's tokens over its experts.  The pages give no formula for that loss;
+// this implements L_aux = (E / G) * sum_g sum_e f[g, e] * P[g, e], with f the
+// fraction of the group's routed slots that chose e (a count: no gradient) and
+// P the mean in-group router probability.
+//
+// The forward pass leaves in its workspace what the backward reads: the
+// routing (idx, w, counts), the slot-major queries, K, V^T, the slot vectors
+// s and the per-row log-sum-exp of the attention scores.  The pass:
+//   1. dS = dy . W_O                      (NT GEMM against W_O^T)
+//   2. slot backward: per slot head the attention-output gradient dO (the
+//      hard slot's own gradient plus w times the weighted slot's), the row
+//      sums D = <dO, O>, and the routing-weight gradient dw
+//   3. attention backward, FlashAttention-2 style with P formed again from
+//      the saved log-sum-exp:
+//        attn_bwd_dkdv_kernel  one wave per 32 keys of a group: for every
+//                              slot head of the group and every later query
+//                              block, dV^T += dO^T P and dK^T += Q^T dS
+//        attn_bwd_dq_kernel    one wave per 32 queries of a slot head: for
+//                              every earlier key block, dQ^T += K^T dS^T
+//      on 32x32x16 MFMA.  P and dS leave the accumulators as B operands
+//      directly: their k order (the accumulator's row order) is the key
+//      permutation of the V^T tiles, so Q^T, K^T and dO^T are laid out in the
+//      same permuted tiles and every A operand is one 16-byte load.
+//   4. router backward: logits again in float64; the routing-weight gradient
+//      through the softmax over the selected experts (renormalized weights)
+//      or over all E (the weighted-concatenation ablation), plus the
+//      auxiliary loss's gradient through the in-group softmax
+//   5. the gradients of every projection input are laid side by side in one
+//      matrix Gall[token, :] = [dQ by expert head | dK | dV | dr], so that
+//        dx = Gall . [W_q; W_k; W_v; W_r]      (NT GEMM against the stacked
+//                                              weights transposed)
+//        dW = Gall^T . x                      (NT GEMM of transposed copies)
+//        dW_O = dy^T . s
+//      The routed query gradient sits in the column block of the expert the
+//      token chose; the other experts' blocks are zero.
+#include <math.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "routing.h"
+
+namespace gqe {
+
+namespace {
+
+// column of key position p (< 64) in a permuted tile (keys permuted in
+// 16-key groups; the map is its own inverse)
+__device__ __forceinline__ int tile_col(int p) {
+  return (p & ~15) | (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// layout helpers
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// dst[c * ldd + dcol + r] = src[r * lds + c] for r < R, c < C, and zero for
+// R <= r < Rpad.  64 x 64 tiles through LDS; grid (ceil(C/64), ceil(Rpad/64)).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int lds_,
+                                                        int R, int C, T* __restrict__ dst,
+                                                        int ldd, int dcol, int Rpad) {
+  __shared__ T tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i / 64, c = i % 64;
+    tile[r][c] = (r0 + r < R && c0 + c < C) ? src[static_cast<size_t>(r0 + r) * lds_ + c0 + c]
+                                            : from_f32<T>(0.f);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int c = i / 64, r = i % 64;
+    if (c0 + c < C && r0 + r < Rpad) dst[static_cast<size_t>(c0 + c) * ldd + dcol + r0 + r] = tile[r][c];
+  }
+}
+
+// Row-major slabs [R, D] -> permuted tiles [tiles, D, 64] (zero past R).
+// Destination slab s reads source slab (s / dst_heads) * src_heads + s % dst_heads.
+// Grid (tiles, slabs).
+template <typename T>
+__global__ __launch_bounds__(256) void to_tiles_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                       int R, int D, int tiles, int src_heads,
+                                                       int dst_heads) {
+  extern __shared__ float tsm[];
+  T* tile = reinterpret_cast<T*>(tsm);  // [64][D + 1]
+  const int j = blockIdx.x, s = blockIdx.y;
+  const size_t ss = static_cast<size_t>(s / dst_heads) * src_heads + s % dst_heads;
+  const T* sp = src + ss * R * D;
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    const int r = i / D, d = i % D;
+    const int key = 64 * j + r;
+    tile[r * (D + 1) + d] = key < R ? sp[static_cast<size_t>(key) * D + d] : from_f32<T>(0.f);
+  }
+  __syncthreads();
+  T* dp = dst + (static_cast<size_t>(s) * tiles + j) * D * 64;
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    const int d = i / 64, c = i % 64;
+    dp[d * 64 + c] = tile[tile_col(c) * (D + 1) + d];
+  }
+}
+
+// Permuted tiles [tiles, D, 64] -> row-major [R, D].  Grid (tiles, slabs).
+template <typename T>
+__global__ __launch_bounds__(256) void from_tiles_kernel(const T* __restrict__ src,
+                                                         T* __restrict__ dst, int R, int D,
+                                                         int tiles) {
+  extern __shared__ float tsm[];
+  T* tile = reinterpret_cast<T*>(tsm);  // [D][65]
+  const int j = blockIdx.x, s = blockIdx.y;
+  const T* sp = src + (static_cast<size_t>(s) * tiles + j) * D * 64;
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    const int d = i / 64, c = i % 64;
+    tile[d * 65 + c] = sp[d * 64 + c];
+  }
+  __syncthreads();
+  T* dp = dst + static_cast<size_t>(s) * R * D;
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    const int r = i / D, d = i % D;
+    const int key = 64 * j + r;
+    if (key < R) dp[static_cast<size_t>(key) * D + d] = tile[d * 65 + tile_col(r)];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// slot backward: one wave per token
+// ---------------------------------------------------------------------------
+struct SlotBwdArgs {
+  const float* ds;   // [T, Ws] gradient of the slot vectors
+  const void* s;     // [T, Ws] slot vectors (forward)
+  const float* w;    // [T, n_routed] routing weights (p for the weighted concatenation), or NULL
+  void* dO;          // [B, H, L, D]
+  float* dsum;       // [B, H, L]
+  float* dw;         // [T, n_routed] or NULL
+  int B, L, H, D, Ws;
+  int n_routed;      // slot heads with a routing weight
+  int mode;          // 0 full (weighted slot after the shared one), 1 hard, 2 weighted concat, 3 dense
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void slot_bwd_kernel(SlotBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= a.B * a.L) return;
+  const int b = tok / a.L, t = tok % a.L;
+  const float* ds = a.ds + static_cast<size_t>(tok) * a.Ws;
+  const T* s = static_cast<const T*>(a.s) + static_cast<size_t>(tok) * a.Ws;
+  const int D = a.D;
+  const int d0 = lane, d1 = lane + 64;
+  float dsw0 = 0.f, dsw1 = 0.f;  // weighted slot's gradient
+  if (a.mode == 0) {
+    const int wc = (a.n_routed + 1) * D;
+    if (d0 < D) dsw0 = ds[wc + d0];
+    if (d1 < D) dsw1 = ds[wc + d1];
+  }
+  for (int h = 0; h < a.H; ++h) {
+    const bool routed = h < a.n_routed && a.mode != 3;
+    const float wh = routed && a.w != nullptr ? a.w[static_cast<size_t>(tok) * a.n_routed + h] : 1.f;
+    float o0 = 0.f, o1 = 0.f, g0 = 0.f, g1 = 0.f;
+    if (d0 < D) {
+      o0 = to_f32(s[h * D + d0]);
+      g0 = ds[h * D + d0];
+    }
+    if (d1 < D) {
+      o1 = to_f32(s[h * D + d1]);
+      g1 = ds[h * D + d1];
+    }
+    float dwv = 0.f;
+    if (routed && a.mode == 0) {
+      g0 = fmaf(wh, dsw0, g0);
+      g1 = fmaf(wh, dsw1, g1);
+      dwv = wsum(dsw0 * o0 + dsw1 * o1);
+    } else if (routed && a.mode == 2) {
+      // the slot holds p * o: the attention output is s / p
+      o0 /= wh;
+      o1 /= wh;
+      dwv = wsum(g0 * o0 + g1 * o1);
+      g0 *= wh;
+      g1 *= wh;
+    }
+    // dO in the storage type; the row sum uses the stored values
+    T* dO = static_cast<T*>(a.dO) + ((static_cast<size_t>(b) * a.H + h) * a.L + t) * D;
+    const T q0 = from_f32<T>(g0), q1 = from_f32<T>(g1);
+    if (d0 < D) dO[d0] = q0;
+    if (d1 < D) dO[d1] = q1;
+    const float dsum = wsum((d0 < D ? to_f32(q0) * o0 : 0.f) + (d1 < D ? to_f32(q1) * o1 : 0.f));
+    if (lane == 0) {
+      a.dsum[(static_cast<size_t>(b) * a.H + h) * a.L + t] = dsum;
+      if (routed && a.dw != nullptr) a.dw[static_cast<size_t>(tok) * a.n_routed + h] = dwv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention backward
+// ---------------------------------------------------------------------------
+struct AttnBwdArgs {
+  const void* q;       // [B, q_heads, L, D] forward queries (unscaled), slot-major
+  int q_heads;
+  const void* keys;    // [B, G, L, D]
+  const void* vr;      // [B, G, L, D] V row-major
+  const void* qt;      // [B, H, tiles, D, 64] Q^T, permuted tiles
+  const void* kt;      // [B, G, tiles, D, 64] K^T, permuted tiles
+  const void* dO;      // [B, H, L, D]
+  const void* dOt;     // [B, H, tiles, D, 64]
+  const float* lse;    // [B, H, L] (log2 units of the scaled scores)
+  const float* dsum;   // [B, H, L]
+  void* gall;          // [T, ldg]
+  int ldg, kcol, vcol; // dK and dV column blocks (group g at + g*D)
+  const int32_t* idx;  // [B, L, G, k] or NULL (dense: head h's dQ at column h*D)
+  int E, k;
+  int B, G, L, H, tiles;
+  int heads_per_group, n_grouped, extra_group;
+  float scale, scale_log2;
+};
+
+// queries scaled by softmax_scale * log2(e) and rounded to the storage type,
+// exactly as the forward kernel forms its scores
+__device__ __forceinline__ bf16x8 scaled_frag(const bf16_t* p, float sl) {
+  const bf16x8 f = load_frag(p);
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = static_cast<__bf16>(static_cast<float>(f[j]) * sl);
+  return r;
+}
+__device__ __forceinline__ f32x8 scaled_frag(const float* p, float sl) { return load_frag(p) * sl; }
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type frag_or_zero(const T* p, bool ok) {
+  if (ok) return load_frag(p);
+  typename Frag<T>::type f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = 0;
+  return f;
+}
+
+__device__ __forceinline__ int group_of(const AttnBwdArgs& a, int h) {
+  return h < a.n_grouped ? h / a.heads_per_group : a.extra_group;
+}
+
+// 32 rows x D (float) in LDS -> rows of Gall, 16 bytes per store
+template <typename T, int D>
+__device__ __forceinline__ void store_rows(const float* buf, T* gall, int ldg, int lane,
+                                           const int* row_of, const int* col_of) {
+  constexpr int EPC = 16 / static_cast<int>(sizeof(T));
+  for (int c = lane; c < 32 * (D / EPC); c += 64) {
+    const int r = c / (D / EPC), e0 = (c % (D / EPC)) * EPC;
+    if (row_of[r] < 0) continue;
+    T v[EPC];
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) v[j] = from_f32<T>(buf[r * (D + 1) + e0 + j]);
+    *reinterpret_cast<uint4*>(gall + static_cast<size_t>(row_of[r]) * ldg + col_of[r] + e0) =
+        *reinterpret_cast<const uint4*>(v);
+  }
+}
+
+// grid (ceil(L/128), B*G); wave w of a block takes keys 128x + 32w .. +31
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  typedef typename Frag<T>::type F;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  __shared__ float stat[4][2][32];
+  __shared__ float obuf[4][32 * (D + 1)];
+  __shared__ int rows[4][32], cols[4][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int b = blockIdx.y / a.G, g = blockIdx.y % a.G;
+  const int key0 = blockIdx.x * 128 + 32 * wave;
+  if (key0 >= a.L) return;
+  const int L = a.L;
+  const int my_key = key0 + (lane & 31);
+  const int krow = min(my_key, L - 1);
+  const T* Kg = static_cast<const T*>(a.keys) + (static_cast<size_t>(b) * a.G + g) * L * D;
+  const T* Vg = static_cast<const T*>(a.vr) + (static_cast<size_t>(b) * a.G + g) * L * D;
+  F kf[NKS], vf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    kf[ks] = load_frag(Kg + static_cast<size_t>(krow) * D + 16 * ks + 8 * half);
+    vf[ks] = load_frag(Vg + static_cast<size_t>(krow) * D + 16 * ks + 8 * half);
+  }
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+
+  const int nh = a.heads_per_group + (g == a.extra_group && a.n_grouped < a.H ? 1 : 0);
+  for (int hi = 0; hi < nh; ++hi) {
+    const int h = hi < a.heads_per_group ? g * a.heads_per_group + hi : a.n_grouped;
+    const size_t bh = static_cast<size_t>(b) * a.H + h;
+    const T* Q = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.q_heads + h) * L * D;
+    const T* dO = static_cast<const T*>(a.dO) + bh * L * D;
+    const T* Qt = static_cast<const T*>(a.qt) + bh * a.tiles * D * 64;
+    const T* dOt = static_cast<const T*>(a.dOt) + bh * a.tiles * D * 64;
+    const float* lse = a.lse + bh * L;
+    const float* dsm = a.dsum + bh * L;
+    for (int q0 = key0; q0 < L; q0 += 32) {
+      {
+        const int qq = q0 + (lane & 31);
+        stat[wave][half][lane & 31] = qq < L ? (half == 0 ? lse[qq] : dsm[qq]) : 0.f;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int my_q = q0 + (lane & 31);
+      const bool qok = my_q < L;
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const size_t off = static_cast<size_t>(qok ? my_q : 0) * D + 16 * ks + 8 * half;
+        F qa = scaled_frag(Q + off, a.scale_log2);
+        if (!qok) qa = frag_or_zero<T>(Q, false);
+        mma32(s, qa, kf[ks]);
+        mma32(dp, frag_or_zero(dO + off, qok), vf[ks]);
+      }
+      // rows of s/dp: queries q0 + acc_row(i); column: this lane's key
+      f32x16 P, dS;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = acc_row(i, lane);
+        const int qq = q0 + r;
+        const bool keep = qq < L && my_key <= qq;
+        const float pv = keep ? __builtin_amdgcn_exp2f(s[i] - stat[wave][0][r]) : 0.f;
+        P[i] = pv;
+        dS[i] = pv * (dp[i] - stat[wave][1][r]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const size_t tb = static_cast<size_t>(q0 / 64) * D * 64 + (q0 % 64);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const F bp = FragFromAcc<T>::get(P, 8 * m);
+        const F bs = FragFromAcc<T>::get(dS, 8 * m);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const size_t toff = tb + static_cast<size_t>(32 * db + (lane & 31)) * 64 + 16 * m + 8 * half;
+          mma32(dv[db], load_frag(dOt + toff), bp);
+          mma32(dk[db], load_frag(Qt + toff), bs);
+        }
+      }
+    }
+  }
+  // dK^T, dV^T accumulators: row = dim 32 db + acc_row(i), column = key -> rows of Gall
+  float* buf = obuf[wave];
+  if (lane < 32) {
+    rows[wave][lane] = key0 + lane < L ? b * L + key0 + lane : -1;
+    cols[wave][lane] = a.kcol + g * D;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[(lane & 31) * (D + 1) + 32 * db + acc_row(i, lane)] = dk[db][i] * a.scale;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  store_rows<T, D>(buf, static_cast<T*>(a.gall), a.ldg, lane, rows[wave], cols[wave]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < 32) cols[wave][lane] = a.vcol + g * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[(lane & 31) * (D + 1) + 32 * db + acc_row(i, lane)] = dv[db][i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  store_rows<T, D>(buf, static_cast<T*>(a.gall), a.ldg, lane, rows[wave], cols[wave]);
+}
+
+// grid (ceil(L/128), B*H); wave w of a block takes queries 128x + 32w .. +31
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+  typedef typename Frag<T>::type F;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  __shared__ float obuf[4][32 * (D + 1)];
+  __shared__ int rows[4][32], cols[4][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int b = blockIdx.y / a.H, h = blockIdx.y % a.H;
+  const int q0 = blockIdx.x * 128 + 32 * wave;
+  if (q0 >= a.L) return;
+  const int L = a.L;
+  const int g = group_of(a, h);
+  const size_t bh = static_cast<size_t>(b) * a.H + h;
+  const int my_q = q0 + (lane & 31);
+  const bool qok = my_q < L;
+  const T* Q = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.q_heads + h) * L * D;
+  const T* dO = static_cast<const T*>(a.dO) + bh * L * D;
+  const T* Kg = static_cast<const T*>(a.keys) + (static_cast<size_t>(b) * a.G + g) * L * D;
+  const T* Vg = static_cast<const T*>(a.vr) + (static_cast<size_t>(b) * a.G + g) * L * D;
+  const T* Kt = static_cast<const T*>(a.kt) + (static_cast<size_t>(b) * a.G + g) * a.tiles * D * 64;
+  const float lse = qok ? a.lse[bh * L + my_q] : 0.f;
+  const float dsm = qok ? a.dsum[bh * L + my_q] : 0.f;
+  F qf[NKS], df[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const size_t off = static_cast<size_t>(qok ? my_q : 0) * D + 16 * ks + 8 * half;
+    qf[ks] = qok ? scaled_frag(Q + off, a.scale_log2) : frag_or_zero<T>(Q, false);
+    df[ks] = frag_or_zero(dO + off, qok);
+  }
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+  const int q_last = min(q0 + 31, L - 1);
+  for (int k0 = 0; k0 <= q_last; k0 += 32) {
+    const int krow = min(k0 + (lane & 31), L - 1);
+    f32x16 st, dpt;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[i] = dpt[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const size_t off = static_cast<size_t>(krow) * D + 16 * ks + 8 * half;
+      mma32(st, load_frag(Kg + off), qf[ks]);
+      mma32(dpt, load_frag(Vg + off), df[ks]);
+    }
+    // rows: keys k0 + acc_row(i); column: this lane's query
+    f32x16 dS;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = k0 + acc_row(i, lane);
+      const bool keep = qok && kk <= my_q;
+      const float pv = keep ? __builtin_amdgcn_exp2f(st[i] - lse) : 0.f;
+      dS[i] = pv * (dpt[i] - dsm);
+    }
+    const size_t tb = static_cast<size_t>(k0 / 64) * D * 64 + (k0 % 64);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const F bs = FragFromAcc<T>::get(dS, 8 * m);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        mma32(dq[db], load_frag(Kt + tb + static_cast<size_t>(32 * db + (lane & 31)) * 64 + 16 * m + 8 * half), bs);
+    }
+  }
+  // dQ^T: row = dim, column = query -> the query's expert column block of Gall
+  float* buf = obuf[wave];
+  if (lane < 32) {
+    const int qq = q0 + lane;
+    rows[wave][lane] = qq < L ? b * L + qq : -1;
+    int col = h * D;
+    if (a.idx != nullptr) {
+      if (h < a.n_grouped) {
+        const int j = h % a.k;
+        const int e = qq < L ? a.idx[((static_cast<size_t>(b) * L + qq) * a.G + g) * a.k + j] : 0;
+        col = (g * a.E + e) * D;
+      } else {
+        col = a.G * a.E * D;  // the shared head's own W_q rows follow the routed ones
+      }
+    }
+    cols[wave][lane] = col;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[(lane & 31) * (D + 1) + 32 * db + acc_row(i, lane)] = dq[db][i] * a.scale;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  store_rows<T, D>(buf, static_cast<T*>(a.gall), a.ldg, lane, rows[wave], cols[wave]);
+}
+
+// ---------------------------------------------------------------------------
+// router backward: one block per token
+// ---------------------------------------------------------------------------
+struct RouterBwdArgs {
+  const void* x;
+  const void* wr;
+  const float* bias;
+  const int32_t* idx;     // [T, G, k]
+  const float* dw;        // [T, G*k] routing-weight gradient (NULL: none)
+  const int32_t* counts;  // [B, G, E] forward dispatch counts
+  void* gall;             // dr at columns rcol + g*E + e
+  int ldg, rcol;
+  float* dr;              // [T, G*E] float copy
+  float* p_out;           // [T, G*E] in-group probabilities
+  int B, T, d, G, E, k;
+  int mode;               // 0 full (renormalized weights), 1 hard, 2 weighted concatenation
+  float aux_weight;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
+  __shared__ double logit[64], pr[64], dpv[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+  const int GE = a.G * a.E;
+  constexpr int kU4 = U4Count<T>::n;
+  const T* xp = static_cast<const T*>(a.x) + static_cast<size_t>(t) * a.d;
+  for (int e = wave; e < GE; e += 4) {
+    const T* wp = static_cast<const T*>(a.wr) + static_cast<size_t>(e) * a.d;
+    double acc = 0.0;
+    for (int d0 = 8 * lane; d0 < a.d; d0 += 512) {
+      uint4 rx[kU4], rw[kU4];
+#pragma unroll
+      for (int q = 0; q < kU4; ++q) {
+        rx[q] = reinterpret_cast<const uint4*>(xp + d0)[q];
+        rw[q] = reinterpret_cast<const uint4*>(wp + d0)[q];
+      }
+      double xv[8], wv[8];
+      widen8<T>(rx, xv);
+      widen8<T>(rw, wv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = fma(xv[j], wv[j], acc);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) logit[e] = acc + (a.bias ? static_cast<double>(a.bias[e]) : 0.0);
+  }
+  __syncthreads();
+  if (tid < GE) {  // in-group softmax p over all E
+    const int g = tid / a.E;
+    const double* r = &logit[g * a.E];
+    double rmax = r[0];
+    for (int f = 1; f < a.E; ++f) rmax = fmax(rmax, r[f]);
+    double z = 0.0;
+    for (int f = 0; f < a.E; ++f) z += exp(r[f] - rmax);
+    pr[tid] = exp(logit[tid] - rmax) / z;
+    dpv[tid] = 0.0;
+  }
+  __syncthreads();
+  // gradient on p (aux) and on the selected weights
+  if (tid < a.G) {
+    const int g = tid;
+    const int32_t* id = a.idx + (static_cast<size_t>(t) * a.G + g) * a.k;
+    double* dp = &dpv[g * a.E];
+    const double* p = &pr[g * a.E];
+    double grad[64];
+    for (int e = 0; e < a.E; ++e) grad[e] = 0.0;
+    if (a.aux_weight != 0.f) {
+      // dL/dp[t, g, e] = aux_weight * (E / G) * f[g, e] / T
+      for (int e = 0; e < a.E; ++e) {
+        long long c = 0;
+        for (int bb = 0; bb < a.B; ++bb) c += a.counts[(static_cast<size_t>(bb) * a.G + g) * a.E + e];
+        const double f = static_cast<double>(c) / (static_cast<double>(a.T) * a.k);
+        dp[e] = static_cast<double>(a.aux_weight) * a.E / a.G * f / a.T;
+      }
+      double sdp = 0.0;
+      for (int e = 0; e < a.E; ++e) sdp += p[e] * dp[e];
+      for (int e = 0; e < a.E; ++e) grad[e] += p[e] * (dp[e] - sdp);
+    }
+    if (a.dw != nullptr && a.mode == 0) {
+      // w = softmax over the selected logits: dr_j = w_j (dw_j - sum w dw)
+      double ws[64], z = 0.0, rmax = logit[g * a.E + id[0]];
+      for (int j = 0; j < a.k; ++j) rmax = fmax(rmax, logit[g * a.E + id[j]]);
+      for (int j = 0; j < a.k; ++j) z += (ws[j] = exp(logit[g * a.E + id[j]] - rmax));
+      double s = 0.0;
+      for (int j = 0; j < a.k; ++j) {
+        ws[j] /= z;
+        s += ws[j] * a.dw[(static_cast<size_t>(t) * a.G + g) * a.k + j];
+      }
+      for (int j = 0; j < a.k; ++j)
+        grad[id[j]] += ws[j] * (a.dw[(static_cast<size_t>(t) * a.G + g) * a.k + j] - s);
+    } else if (a.dw != nullptr && a.mode == 2) {
+      // the selected experts' p scale their slots: softmax over all E
+      double dps[64];
+      for (int e = 0; e < a.E; ++e) dps[e] = 0.0;
+      for (int j = 0; j < a.k; ++j) dps[id[j]] = a.dw[(static_cast<size_t>(t) * a.G + g) * a.k + j];
+      double s = 0.0;
+      for (int e = 0; e < a.E; ++e) s += p[e] * dps[e];
+      for (int e = 0; e < a.E; ++e) grad[e] += p[e] * (dps[e] - s);
+    }
+    for (int e = 0; e < a.E; ++e) {
+      const size_t o = static_cast<size_t>(t) * GE + g * a.E + e;
+      a.dr[o] = static_cast<float>(grad[e]);
+      a.p_out[o] = static_cast<float>(p[e]);
+      static_cast<T*>(a.gall)[static_cast<size_t>(t) * a.ldg + a.rcol + g * a.E + e] =
+          from_f32<T>(static_cast<float>(grad[e]));
+    }
+  }
+}
+
+// Column sums over T rows in a fixed order: block c sums column c of dr (into
+// dbr) and of p (into psum, for the auxiliary loss).
+__global__ __launch_bounds__(256) void column_sums_kernel(const float* dr, const float* p, int T,
+                                                          int C, float* dbr, double* psum) {
+  __shared__ double s1[256], s2[256];
+  const int c = blockIdx.x;
+  double a = 0.0, q = 0.0;
+  for (int t = threadIdx.x; t < T; t += 256) {
+    a += dr[static_cast<size_t>(t) * C + c];
+    q += p[static_cast<size_t>(t) * C + c];
+  }
+  s1[threadIdx.x] = a;
+  s2[threadIdx.x] = q;
+  __syncthreads();
+  for (int n = 128; n >= 1; n >>= 1) {
+    if (threadIdx.x < n) {
+      s1[threadIdx.x] += s1[threadIdx.x + n];
+      s2[threadIdx.x] += s2[threadIdx.x + n];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    dbr[c] = static_cast<float>(s1[0]);
+    psum[c] = s2[0];
+  }
+}
+
+// L_aux = (E / G) * sum_{g,e} f[g, e] * P[g, e]
+__global__ void aux_loss_kernel(const double* psum, const int32_t* counts, int B, int T, int G,
+                                int E, int k, float* out) {
+  if (threadIdx.x != 0) return;
+  double acc = 0.0;
+  for (int g = 0; g < G; ++g)
+    for (int e = 0; e < E; ++e) {
+      long long c = 0;
+      for (int bb = 0; bb < B; ++bb) c += counts[(static_cast<size_t>(bb) * G + g) * E + e];
+      acc += (static_cast<double>(c) / (static_cast<double>(T) * k)) * (psum[g * E + e] / T);
+    }
+  *out = static_cast<float>(acc * E / G);
+}
+
+template <typename T>
+hipError_t launch_transpose(const T* src, int lds_, int R, int C, T* dst, int ldd, int dcol,
+                            int Rpad, hipStream_t stream) {
+  if (C == 0 || Rpad == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel<T>, dim3((C + 63) / 64, (Rpad + 63) / 64), dim3(256), 0,
+                     stream, src, lds_, R, C, dst, ldd, dcol, Rpad);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n16 + 255) / 256, 8192));
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint4*>(p),
+                     n16);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_attn_bwd_d(const AttnBwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3((a.L + 127) / 128, a.B * a.G), dim3(256),
+                     0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3((a.L + 127) / 128, a.B * a.H), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
+  const int B = p.B, L = p.L, T_ = p.B * p.L, d = p.d, G = p.G, E = p.E, k = p.k, D = p.D;
+  const int H = p.H;
+  hipError_t e;
+#define GQE_TRY(x)                     \
+  do {                                 \
+    if ((e = (x)) != hipSuccess) return e; \
+  } while (0)
+  const size_t es = sizeof(T);
+  // layouts: Gall and the stacked weights transposed (zero outside the
+  // blocks), W_O transposed
+  GQE_TRY(launch_fill(p.gall, static_cast<size_t>(T_) * p.kpad * es, stream));
+  GQE_TRY(launch_fill(p.w_t, static_cast<size_t>(d) * p.kpad * es, stream));
+  GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.wq), d, p.qcols, d, static_cast<T*>(p.w_t),
+                              p.kpad, 0, p.qcols, stream));
+  GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.wk), d, G * D, d, static_cast<T*>(p.w_t),
+                              p.kpad, p.kcol, G * D, stream));
+  GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.wv), d, G * D, d, static_cast<T*>(p.w_t),
+                              p.kpad, p.vcol, G * D, stream));
+  if (p.wr != nullptr)
+    GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.wr), d, G * E, d, static_cast<T*>(p.w_t),
+                                p.kpad, p.rcol, G * E, stream));
+  GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.wo), p.ws, d, p.ws, static_cast<T*>(p.wo_t),
+                              d, 0, d, stream));
+
+  // 1. dS = dy . W_O
+  {
+    NtArgs g = {};
+    g.a = p.dy;
+    g.lda = d;
+    g.b = p.wo_t;
+    g.ldb = d;
+    g.M = T_;
+    g.N = p.ws;
+    g.K = d;
+    g.nseg = 1;
+    g.seg[0] = NtSeg{p.ds, 0, T_, p.ws, 0};
+    GQE_TRY(launch_nt_gemm<T>(g, stream));
+  }
+  // 2. slot backward
+  {
+    SlotBwdArgs s;
+    s.ds = p.ds;
+    s.s = p.s;
+    s.w = p.w;
+    s.dO = p.dO;
+    s.dsum = p.dsum;
+    s.dw = p.dw;
+    s.B = B;
+    s.L = L;
+    s.H = H;
+    s.D = D;
+    s.Ws = p.ws;
+    s.n_routed = p.n_routed;
+    s.mode = p.mode;
+    hipLaunchKernelGGL(slot_bwd_kernel<T>, dim3((T_ + 3) / 4), dim3(256), 0, stream, s);
+    GQE_TRY(hipGetLastError());
+  }
+  // 3. attention backward
+  const int tiles = (L + 63) / 64;
+  {
+    const size_t tl = 64 * (D + 1) * es;
+    hipLaunchKernelGGL(to_tiles_kernel<T>, dim3(tiles, B * H), dim3(256), tl, stream,
+                       static_cast<const T*>(p.q), static_cast<T*>(p.qt), L, D, tiles, p.q_heads, H);
+    GQE_TRY(hipGetLastError());
+    hipLaunchKernelGGL(to_tiles_kernel<T>, dim3(tiles, B * G), dim3(256), tl, stream,
+                       static_cast<const T*>(p.keys), static_cast<T*>(p.kt), L, D, tiles, G, G);
+    GQE_TRY(hipGetLastError());
+    hipLaunchKernelGGL(to_tiles_kernel<T>, dim3(tiles, B * H), dim3(256), tl, stream,
+                       static_cast<const T*>(p.dO), static_cast<T*>(p.dOt), L, D, tiles, H, H);
+    GQE_TRY(hipGetLastError());
+    hipLaunchKernelGGL(from_tiles_kernel<T>, dim3(tiles, B * G), dim3(256), D * 65 * es, stream,
+                       static_cast<const T*>(p.vt), static_cast<T*>(p.vr), L, D,
+                       static_cast<int>(p.vt_tiles));
+    GQE_TRY(hipGetLastError());
+    AttnBwdArgs a;
+    a.q = p.q;
+    a.q_heads = p.q_heads;
+    a.keys = p.keys;
+    a.vr = p.vr;
+    a.qt = p.qt;
+    a.kt = p.kt;
+    a.dO = p.dO;
+    a.dOt = p.dOt;
+    a.lse = p.lse;
+    a.dsum = p.dsum;
+    a.gall = p.gall;
+    a.ldg = p.kpad;
+    a.kcol = p.kcol;
+    a.vcol = p.vcol;
+    a.idx = p.idx;
+    a.E = E;
+    a.k = k;
+    a.B = B;
+    a.G = G;
+    a.L = L;
+    a.H = H;
+    a.tiles = tiles;
+    a.heads_per_group = p.heads_per_group;
+    a.n_grouped = p.n_grouped;
+    a.extra_group = p.extra_group;
+    a.scale = p.scale;
+    a.scale_log2 = p.scale * 1.4426950408889634f;
+    switch (D) {
+      case 32: GQE_TRY((launch_attn_bwd_d<T, 32>(a, stream))); break;
+      case 64: GQE_TRY((launch_attn_bwd_d<T, 64>(a, stream))); break;
+      case 128: GQE_TRY((launch_attn_bwd_d<T, 128>(a, stream))); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  // 4. router backward and the auxiliary loss
+  if (p.wr != nullptr) {
+    RouterBwdArgs r;
+    r.x = p.x;
+    r.wr = p.wr;
+    r.bias = p.router_bias;
+    r.idx = p.idx;
+    r.dw = p.mode == 1 ? nullptr : p.dw;
+    r.counts = p.counts;
+    r.gall = p.gall;
+    r.ldg = p.kpad;
+    r.rcol = p.rcol;
+    r.dr = p.dr;
+    r.p_out = p.p_all;
+    r.B = B;
+    r.T = T_;
+    r.d = d;
+    r.G = G;
+    r.E = E;
+    r.k = k;
+    r.mode = p.mode;
+    r.aux_weight = p.aux_weight;
+    hipLaunchKernelGGL(router_bwd_kernel<T>, dim3(T_), dim3(256), 0, stream, r);
+    GQE_TRY(hipGetLastError());
+    hipLaunchKernelGGL(column_sums_kernel, dim3(G * E), dim3(256), 0, stream, p.dr, p.p_all, T_,
+                       G * E, p.dbr, p.psum);
+    GQE_TRY(hipGetLastError());
+    hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(64), 0, stream, p.psum, p.counts, B, T_, G,
+                       E, k, p.aux_loss);
+    GQE_TRY(hipGetLastError());
+  }
+  // 5. transposed copies over tokens (zero past T), then the weight and input gradients
+  const int tp = p.tpad;
+  GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.gall), p.kpad, T_, p.kpad,
+                              static_cast<T*>(p.gall_t), tp, 0, tp, stream));
+  GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.x), d, T_, d, static_cast<T*>(p.x_t), tp, 0,
+                              tp, stream));
+  GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.dy), d, T_, d, static_cast<T*>(p.dy_t), tp, 0,
+                              tp, stream));
+  GQE_TRY(launch_transpose<T>(static_cast<const T*>(p.s), p.ws, T_, p.ws, static_cast<T*>(p.s_t),
+                              tp, 0, tp, stream));
+  {
+    NtArgs g = {};  // dW_O = dy^T . s
+    g.a = p.dy_t;
+    g.lda = tp;
+    g.b = p.s_t;
+    g.ldb = tp;
+    g.M = d;
+    g.N = p.ws;
+    g.K = tp;
+    g.nseg = 1;
+    g.seg[0] = NtSeg{p.dwo, 0, d, p.ws, 0};
+    GQE_TRY(launch_nt_gemm<T>(g, stream));
+  }
+  {
+    NtArgs g = {};  // dx = Gall . W_all
+    g.a = p.gall;
+    g.lda = p.kpad;
+    g.b = p.w_t;
+    g.ldb = p.kpad;
+    g.M = T_;
+    g.N = d;
+    g.K = p.kpad;
+    g.nseg = 1;
+    g.seg[0] = NtSeg{p.dx, 0, T_, d, 0};
+    GQE_TRY(launch_nt_gemm<T>(g, stream));
+  }
+  {
+    NtArgs g = {};  // [dW_q; dW_k; dW_v; dW_r] = Gall^T . x
+    g.a = p.gall_t;
+    g.lda = tp;
+    g.b = p.x_t;
+    g.ldb = tp;
+    g.M = p.kcols;
+    g.N = d;
+    g.K = tp;
+    g.nseg = p.wr != nullptr ? 4 : 3;
+    g.seg[0] = NtSeg{p.dwq, 0, p.qcols, d, 0};
+    g.seg[1] = NtSeg{p.dwk, p.kcol, G * D, d, 0};
+    g.seg[2] = NtSeg{p.dwv, p.vcol, G * D, d, 0};
+    if (p.wr != nullptr) g.seg[3] = NtSeg{p.dwr, p.rcol, G * E, d, 0};
+    GQE_TRY(launch_nt_gemm<T>(g, stream));
+  }
+#undef GQE_TRY
+  return hipSuccess;
+}
+
+template hipError_t launch_backward<bf16_t>(const BwdParams&, hipStream_t);
+template hipError_t launch_backward<float>(const BwdParams&, hipStream_t);
+
+}  // namespace gqe

@@ -24,12 +24,22 @@
 //                       sparsity of pptc.cn section 5).
 //   output projection : slot vectors times W_O (hotpaper.ai: W_O of k*G+2
 //                       slots), row-major.
+#include <type_traits>
+#include <utility>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace gqe {
 
 namespace {
+
+// A problem that defines store_acc(row, col, value) (tile-relative) receives
+// the float32 accumulators directly instead of a tile staged in LDS as T.
+template <class P, class = void> struct HasStoreAcc : std::false_type {};
+template <class P>
+struct HasStoreAcc<P, std::void_t<decltype(std::declval<const P&>().store_acc(0, 0, 0.f))>>
+    : std::true_type {};
 
 template <typename T, int BM_, int BN_, int WGM_, int WGN_, int NST_ = 2>
 struct GemmShape {
@@ -137,20 +147,31 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
         for (int b = 0; b < S::TN; ++b) mma32(acc[a][b], af[a], bf[b]);
     }
   }
-  lds_barrier();  // every wave is done reading the ring before it holds the tile
+  if constexpr (HasStoreAcc<P>::value) {
+#pragma unroll
+    for (int a = 0; a < S::TM; ++a)
+#pragma unroll
+      for (int b = 0; b < S::TN; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          prob.store_acc(wm * S::WM + 32 * a + acc_row(i, lane), wn * S::WN + 32 * b + (lane & 31),
+                         acc[a][b][i]);
+  } else {
+    lds_barrier();  // every wave is done reading the ring before it holds the tile
 
-  // epilogue: stage the tile, then the problem writes it out in 8-element chunks
-  T* ct = reinterpret_cast<T*>(smem);
+    // epilogue: stage the tile, then the problem writes it out in 8-element chunks
+    T* ct = reinterpret_cast<T*>(smem);
 #pragma unroll
-  for (int a = 0; a < S::TM; ++a)
+    for (int a = 0; a < S::TM; ++a)
 #pragma unroll
-    for (int b = 0; b < S::TN; ++b)
+      for (int b = 0; b < S::TN; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        ct[(wm * S::WM + 32 * a + acc_row(i, lane)) * S::LDC + wn * S::WN + 32 * b + (lane & 31)] =
-            from_f32<T>(acc[a][b][i]);
-  lds_barrier();
-  prob.write_tile(ct);
+        for (int i = 0; i < 16; ++i)
+          ct[(wm * S::WM + 32 * a + acc_row(i, lane)) * S::LDC + wn * S::WN + 32 * b + (lane & 31)] =
+              from_f32<T>(acc[a][b][i]);
+    lds_barrier();
+    prob.write_tile(ct);
+  }
 }
 
 // copy 8 contiguous elements (16 B of bf16, 32 B of fp32)
@@ -401,6 +422,45 @@ __global__ __launch_bounds__(256) void out_proj_kernel(OutArgs args) {
 }
 
 // ---------------------------------------------------------------------------
+// general NT product with float32 results (the backward pass)
+// ---------------------------------------------------------------------------
+template <typename T, class S>
+struct NtProb {
+  const NtArgs& a;
+  int m0, n0, K;
+  __device__ NtProb(const NtArgs& args, int m0_, int n0_) : a(args), m0(m0_), n0(n0_), K(args.K) {}
+  __device__ __forceinline__ const T* a_any() const { return static_cast<const T*>(a.a); }
+  __device__ __forceinline__ const T* b_any() const { return static_cast<const T*>(a.b); }
+  __device__ __forceinline__ const T* a_row(int r) const {
+    const int m = m0 + r;
+    return m < a.M ? static_cast<const T*>(a.a) + static_cast<size_t>(m) * a.lda : nullptr;
+  }
+  __device__ __forceinline__ const T* b_row(int n) const {
+    const int c = n0 + n;
+    return c < a.N ? static_cast<const T*>(a.b) + static_cast<size_t>(c) * a.ldb : nullptr;
+  }
+  __device__ __forceinline__ void store_acc(int r, int c, float v) const {
+    const int m = m0 + r, n = n0 + c;
+    if (m >= a.M || n >= a.N) return;
+    for (int i = 0; i < a.nseg; ++i) {
+      const NtSeg& sg = a.seg[i];
+      if (m >= sg.row_begin && m < sg.row_begin + sg.rows) {
+        float* o = sg.out + static_cast<size_t>(m - sg.row_begin) * sg.ldo + n;
+        *o = sg.accumulate ? *o + v : v;
+        return;
+      }
+    }
+  }
+};
+
+template <typename T, class S>
+__global__ __launch_bounds__(256) void nt_gemm_kernel(NtArgs args) {
+  extern __shared__ __align__(16) char smem[];
+  NtProb<T, S> prob(args, blockIdx.y * S::BM, blockIdx.x * S::BN);
+  gemm_block<T, S>(prob, smem);
+}
+
+// ---------------------------------------------------------------------------
 // weighted slot: s[t, (kG+1)D + c] = sum_{g,j} w[t, g, j] * s[t, (g k + j) D + c]
 // (gist.science, Architectuur en Routing: weighted sum of the selected
 // experts' outputs with the router weights; a plain sum over groups)
@@ -553,6 +613,18 @@ hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K
 }
 
 template <typename T>
+hipError_t launch_nt_gemm(const NtArgs& a, hipStream_t stream) {
+  typedef GemmShape<T, 128, 128, 2, 2> S;
+  typedef GemmShape<T, 128, 128, 2, 2, 4> S4;
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (a.K % S::BKE != 0 || a.nseg < 1 || a.nseg > 4) return hipErrorInvalidValue;
+  const dim3 grid((a.N + S::BN - 1) / S::BN, (a.M + S::BM - 1) / S::BM);
+  if (deep_ring(static_cast<long long>(grid.x) * grid.y))
+    return launch_gemm<S4>(nt_gemm_kernel<T, S4>, grid, stream, a);
+  return launch_gemm<S>(nt_gemm_kernel<T, S>, grid, stream, a);
+}
+
+template <typename T>
 hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int G, int k, int D,
                                 hipStream_t stream) {
   const size_t n = static_cast<size_t>(n_tokens) * (D / 4);
@@ -570,7 +642,8 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int G, int k
                                          const int32_t*, const int32_t*, const int32_t*, int, int, \
                                          int, int, int, int, int, int, hipStream_t);             \
   template hipError_t launch_out_proj<T>(const T*, const T*, T*, int, int, int, hipStream_t);    \
-  template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, int, hipStream_t);
+  template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, int, hipStream_t); \
+  template hipError_t launch_nt_gemm<T>(const NtArgs&, hipStream_t);
 GQE_INST(bf16_t)
 GQE_INST(float)
 #undef GQE_INST

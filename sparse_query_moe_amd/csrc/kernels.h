@@ -68,6 +68,9 @@ struct AttnParams {
   // optional per-row factor of the grouped heads' outputs: o[b, t, h] is
   // multiplied by row_scale[(b*L + t)*n_grouped + h] (h < n_grouped), or NULL
   const float* row_scale;
+  // optional [B, H, L]: log2 of each row's softmax normalizer in the units of
+  // the scaled scores (max + log2(sum of 2^(s - max))), or NULL
+  float* lse;
 };
 template <typename T>
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream);
@@ -79,6 +82,69 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int G, int k
 template <typename T>
 hipError_t launch_out_proj(const T* a, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream);
+
+// ---- backward: C[M, N] = A[M, K] . B[N, K]^T in float32 ------------------------
+// Rows of C go to up to four segments: row m in [row_begin, row_begin + rows)
+// is stored (or added, when accumulate) at out[(m - row_begin)*ldo + n];
+// rows in no segment are dropped.  K must be a multiple of 64 (bf16) or 32
+// (fp32) elements.
+struct NtSeg {
+  float* out;
+  int row_begin, rows, ldo, accumulate;
+};
+struct NtArgs {
+  const void* a;
+  int lda;
+  const void* b;
+  int ldb;
+  int M, N, K;
+  int nseg;
+  NtSeg seg[4];
+};
+template <typename T>
+hipError_t launch_nt_gemm(const NtArgs& a, hipStream_t stream);
+
+// ---- backward of the layer -----------------------------------------------------
+struct BwdParams {
+  // inputs of the forward pass and the output gradient
+  const void* x;            // [T, d]
+  const void* wq;           // query rows, [q_rows, d] (the first qcols are used)
+  const void* wk;           // [G*D, d]
+  const void* wv;           // [G*D, d]
+  const void* wr;           // [G*E, d] or NULL (dense GQA: no router)
+  const float* router_bias; // [G*E] or NULL
+  const void* wo;           // [d, ws]
+  const void* dy;           // [T, d]
+  // the forward workspace
+  const int32_t* idx;       // [T, G, k] or NULL
+  const float* w;           // [T, n_routed] routing weights (p for weighted concatenation) or NULL
+  const int32_t* counts;    // [B, G, E] or NULL
+  const void* q;            // [B, q_heads, L, D]
+  const void* keys;         // [B, G, L, D]
+  const void* vt;           // [B, G, vt_tiles, D, 64]
+  int64_t vt_tiles;
+  const void* s;            // [T, ws]
+  const float* lse;         // [B, H, L]
+  // gradients (float32, caller-owned)
+  float *dx, *dwq, *dwk, *dwv, *dwr, *dbr, *dwo, *aux_loss;
+  // scratch
+  void *gall, *w_t, *wo_t, *dO, *dOt, *qt, *kt, *vr, *gall_t, *x_t, *dy_t, *s_t;
+  float *ds, *dsum, *dw, *dr, *p_all;
+  double* psum;
+  // shapes
+  int B, L, d, G, E, k, D;
+  int H;                    // attending slot heads
+  int q_heads;              // heads allocated in q
+  int n_routed;             // slot heads with a routing weight
+  int heads_per_group, n_grouped, extra_group;
+  int mode;                 // 0 full, 1 hard, 2 weighted concatenation, 3 dense GQA
+  int ws;                   // slot width
+  int qcols, kcol, vcol, rcol, kcols, kpad;  // column blocks of Gall
+  int tpad;                 // tokens rounded up to 64
+  float scale, aux_weight;
+};
+template <typename T>
+hipError_t launch_backward(const BwdParams& p, hipStream_t stream);
 
 // ---- decode: one token per sequence against a KV cache --------------------------
 // query heads of one KV group that one decode attention block holds (E <= 32

@@ -25,7 +25,8 @@ EXPORTS = (
     "gqe_workspace_bytes", "gqe_workspace_layout", "gqe_route", "gqe_dispatch", "gqe_project",
     "gqe_attention", "gqe_output", "gqe_forward", "gqa_workspace_bytes", "gqa_workspace_layout",
     "gqa_project", "gqa_attention", "gqa_output", "gqa_forward", "gqe_decode_workspace_bytes",
-    "gqe_decode", "gqa_decode_workspace_bytes", "gqa_decode", "gqe_status_string",
+    "gqe_decode", "gqa_decode_workspace_bytes", "gqa_decode", "gqe_backward_workspace_bytes",
+    "gqe_backward", "gqa_backward_workspace_bytes", "gqa_backward", "gqe_status_string",
 )
 
 
@@ -49,8 +50,8 @@ class GqeConfig(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("idx", "w", "counts", "offsets", "pos", "slot", "q", "k", "vt", "s", "scratch",
-                 "total")] + [("vt_tiles", ctypes.c_int64)]
+                ("idx", "w", "counts", "offsets", "pos", "slot", "q", "k", "vt", "s", "lse",
+                 "scratch", "total")] + [("vt_tiles", ctypes.c_int64)]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -77,6 +78,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqa_decode_workspace_bytes": (sz, [cfgp]),
         "gqe_decode": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "gqa_decode": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "gqe_backward_workspace_bytes": (sz, [cfgp]),
+        "gqa_backward_workspace_bytes": (sz, [cfgp]),
+        "gqe_backward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz,
+                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "gqa_backward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp,
+                                        vp, sz, vp]),
         "gqe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -227,6 +234,37 @@ def gqa_decode(cfg, x, wq, wk, wv, wo, k_cache, vt_cache, pos, out, ws, stream=N
                            ws.numel(), _stream(stream)), "gqa_decode")
 
 
+def gqe_backward_workspace_bytes(cfg: GqeConfig) -> int:
+    return int(_lib.gqe_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
+def gqa_backward_workspace_bytes(cfg: GqeConfig) -> int:
+    return int(_lib.gqa_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
+def alloc_backward_workspace(cfg: GqeConfig, dense: bool = False, device="cuda") -> torch.Tensor:
+    n = gqa_backward_workspace_bytes(cfg) if dense else gqe_backward_workspace_bytes(cfg)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def gqe_backward(cfg, x, wq, wk, wv, wr, wo, dy, aux_weight, fwd_ws, dx, dwq, dwk, dwv, dwr, dbr,
+                 dwo, aux_loss, ws, stream=None):
+    """Gradients of <y, dy> + aux_weight * L_aux (float32 tensors, overwritten);
+    fwd_ws is the workspace of a gqe_forward on the same inputs."""
+    _check(_lib.gqe_backward(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wr),
+                             _ptr(wo), _ptr(dy), float(aux_weight), _ptr(fwd_ws), fwd_ws.numel(),
+                             _ptr(dx), _ptr(dwq), _ptr(dwk), _ptr(dwv), _ptr(dwr), _ptr(dbr),
+                             _ptr(dwo), _ptr(aux_loss), _ptr(ws), ws.numel(), _stream(stream)),
+           "gqe_backward")
+
+
+def gqa_backward(cfg, x, wq, wk, wv, wo, dy, fwd_ws, dx, dwq, dwk, dwv, dwo, ws, stream=None):
+    _check(_lib.gqa_backward(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+                             _ptr(dy), _ptr(fwd_ws), fwd_ws.numel(), _ptr(dx), _ptr(dwq),
+                             _ptr(dwk), _ptr(dwv), _ptr(dwo), _ptr(ws), ws.numel(),
+                             _stream(stream)), "gqa_backward")
+
+
 def workspace_views(cfg: GqeConfig, ws: torch.Tensor, dense: bool = False) -> dict:
     """Typed views of the intermediates inside a workspace (see gqe_ws_layout)."""
     lay = gqa_workspace_layout(cfg) if dense else gqe_workspace_layout(cfg)
@@ -251,11 +289,14 @@ def workspace_views(cfg: GqeConfig, ws: torch.Tensor, dense: bool = False) -> di
         out["pos"] = view(lay.pos, (rows,), torch.int32, 4)
         out["slot"] = view(lay.slot, (rows,), torch.int32, 4)
         out["q"] = view(lay.q, (B, G * k + 1, L, D), dt, es)
-        slots = G * k + (2 if cfg.output_mode == OUTPUT_MODES["full"] else 0)
+        full = cfg.output_mode == OUTPUT_MODES["full"]
+        slots = G * k + (2 if full else 0)
         out["s"] = view(lay.s, (B, L, slots * D), dt, es)
+        out["lse"] = view(lay.lse, (B, G * k + (1 if full else 0), L), torch.float32, 4)
     else:
         out["q"] = view(lay.q, (B, G * E, L, D), dt, es)
         out["s"] = view(lay.s, (B, L, G * E * D), dt, es)
+        out["lse"] = view(lay.lse, (B, G * E, L), torch.float32, 4)
     out["k"] = view(lay.k, (B, G, L, D), dt, es)
     # V^T per 64-key tile, keys permuted inside 16-key groups (see include/gqe.h)
     out["vt"] = view(lay.vt, (B, G, int(lay.vt_tiles), D, 64), dt, es)
