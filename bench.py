@@ -289,6 +289,52 @@ def measure_decode(gqe, torch, steps, warmup, name="dec_b64_c8k"):
     }
 
 
+def measure_training(wl, gqe, torch, steps, warmup):
+    """One training step of the layer: gqe_forward then gqe_backward (dy of
+    the output's shape, load-balancing weight 0.01), and the same for dense
+    GQA; the backward alone is timed too.  Returns ms per step and tokens/s."""
+    r = Runner(wl, gqe, torch)
+    G, E, D, d = wl.n_groups, wl.n_experts, wl.head_dim, wl.d_model
+    f32 = dict(dtype=torch.float32, device="cuda")
+    rng = np.random.Generator(np.random.PCG64(12))
+    dy = W._draw(rng, (wl.batch, wl.seq_len, d), 1.0, wl.dtype)
+    if dy.dtype == np.uint16:
+        dy = torch.from_numpy(dy.view(np.int16)).view(torch.bfloat16).to("cuda")
+    else:
+        dy = torch.from_numpy(dy).to("cuda")
+    I = r.I
+    g = {k: torch.empty(v, **f32) for k, v in dict(
+        dx=(wl.batch, wl.seq_len, d), dwq=I["wq"].shape, dwk=I["wk"].shape, dwv=I["wv"].shape,
+        dwr=(G * E, d), dbr=(G * E,), dwo=I["wo"].shape, aux=(1,), dwqd=I["wq_dense"].shape,
+        dwod=I["wo_dense"].shape).items()}
+    bws = gqe.alloc_backward_workspace(r.cfg)
+    bws_d = gqe.alloc_backward_workspace(r.cfg, dense=True)
+    dv = r.dev
+
+    def gqe_bwd():
+        gqe.gqe_backward(r.cfg, dv["x"], dv["wq"], dv["wk"], dv["wv"], dv["wr"], dv["wo"], dy, 0.01,
+                         r.ws, g["dx"], g["dwq"], g["dwk"], g["dwv"], g["dwr"], g["dbr"], g["dwo"],
+                         g["aux"], bws)
+
+    def gqa_bwd():
+        gqe.gqa_backward(r.cfg, dv["x"], dv["wq_dense"], dv["wk"], dv["wv"], dv["wo_dense"], dy,
+                         r.ws_dense, g["dx"], g["dwqd"], g["dwk"], g["dwv"], g["dwod"], bws_d)
+
+    t_gqe = r.time_steps(lambda: (r.gqe_step(), gqe_bwd()), steps, warmup)
+    t_gqa = r.time_steps(lambda: (r.gqa_step(), gqa_bwd()), steps, warmup)
+    b_gqe = r.time_steps(gqe_bwd, steps, 1)
+    b_gqa = r.time_steps(gqa_bwd, steps, 1)
+    tokens = wl.batch * wl.seq_len
+    del bws, bws_d, g, r
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "gqe_step_ms": round(t_gqe, 5), "gqa_step_ms": round(t_gqa, 5),
+            "gqe_backward_ms": round(b_gqe, 5), "gqa_backward_ms": round(b_gqa, 5),
+            "gqe_tokens_per_s": round(tokens / (t_gqe * 1e-3), 1),
+            "gqa_tokens_per_s": round(tokens / (t_gqa * 1e-3), 1),
+            "speedup_vs_gqa": round(t_gqa / t_gqe, 4),
+            "backward_speedup_vs_gqa": round(b_gqa / b_gqe, 4)}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.txt")
 KERNEL_SOURCES = ("attention.hip", "device_common.h", "kernels.h")
 
@@ -370,6 +416,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
+    ap.add_argument("--training", default="l2k,b4_l8k",
+                    help="workloads whose training step (forward + backward) is timed "
+                         "(comma list, '' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB three times (the known-size "
                          "kernel that calibrates HBM byte counters)")
@@ -439,6 +488,16 @@ def main():
         "per_length": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
                        for r in per_length],
     }
+    train = []
+    for name in [n for n in args.training.split(",") if n]:
+        w2 = W.WORKLOADS[name]
+        steps = max(2, min(args.steps, int(2e12 / max(1, stage_work(w2)["attention"][1]) + 2)))
+        log(f"[bench] training step {w2.description}: steps {steps}")
+        t = measure_training(w2, gqe, torch, steps, 2)
+        log(f"[bench]   {t}")
+        train.append(t)
+    if train:
+        line["training"] = train
     if not args.no_decode:
         log("[bench] decode step ...")
         line["decode"] = measure_decode(gqe, torch, args.steps, args.warmup)

@@ -145,3 +145,33 @@ def test_decode_host_errors_before_any_launch(gqe):
     assert lib.gqe_decode(ctypes.byref(_cfg(gqe, head_dim=96)), *([a] * 11), n, None) == -2
     # no sequences: nothing to do
     assert lib.gqe_decode(ctypes.byref(_cfg(gqe, batch=0)), *nulls, 0, None) == 0
+
+
+def test_backward_workspace_and_host_errors(gqe):
+    lib = gqe._lib
+    cfg = _cfg(gqe)
+    n = gqe.gqe_backward_workspace_bytes(cfg)
+    assert n > 0 and gqe.gqa_backward_workspace_bytes(cfg) > 0
+    assert gqe.gqe_backward_workspace_bytes(_cfg(gqe, seq_len=4096)) > n
+    assert gqe.gqe_backward_workspace_bytes(_cfg(gqe, top_k=0)) == 0
+    f = gqe.gqe_workspace_bytes(cfg)
+    a = ctypes.c_void_p(256)
+    # null pointers
+    st = lib.gqe_backward(ctypes.byref(cfg), *([None] * 7), 0.0, None, f, *([None] * 8), None, n,
+                          None)
+    assert st == -1
+    # negative or infinite auxiliary weight
+    for aux in (-1.0, float("inf")):
+        st = lib.gqe_backward(ctypes.byref(cfg), *([a] * 7), aux, a, f, *([a] * 8), a, n, None)
+        assert st == -1
+    # forward workspace or backward workspace too small
+    assert lib.gqe_backward(ctypes.byref(cfg), *([a] * 7), 0.0, a, f - 1, *([a] * 8), a, n,
+                            None) == -3
+    assert lib.gqe_backward(ctypes.byref(cfg), *([a] * 7), 0.0, a, f, *([a] * 8), a, n - 1,
+                            None) == -3
+    m = gqe.gqa_backward_workspace_bytes(cfg)
+    fd = gqe.gqa_workspace_bytes(cfg)
+    assert lib.gqa_backward(ctypes.byref(cfg), *([a] * 6), a, fd, *([a] * 5), a, m - 1, None) == -3
+    # empty input: nothing to do
+    assert lib.gqe_backward(ctypes.byref(_cfg(gqe, seq_len=0)), *([None] * 7), 0.0, None, 0,
+                            *([None] * 8), None, 0, None) == 0
