@@ -422,8 +422,8 @@ namespace {
 // ---- backward ------------------------------------------------------------------
 
 struct BwdLayout {
-  size_t gall, w_t, wo_t, ds, dO, dOt, qt, kt, vr, dsum, dw, dr, p_all, psum, gall_t, x_t, dy_t,
-      s_t, total;
+  size_t gall, w_t, wo_t, ds, dO, dOt, qt, qs, kt, vr, dsum, dw, dr, p_all, psum, gall_t, x_t,
+      dy_t, s_t, total;
   int tpad, ws, qcols, kcol, vcol, rcol, kcols, kpad, H, q_heads;
 };
 
@@ -456,6 +456,7 @@ BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
   l.dO = take(B * H * L * D * es);
   l.dOt = take(B * H * tiles * D * 64 * es);
   l.qt = take(B * H * tiles * D * 64 * es);
+  l.qs = take(B * H * L * D * es);
   l.kt = take(B * G * tiles * D * 64 * es);
   l.vr = take(B * G * L * D * es);
   l.dsum = take(B * H * L * 4);
@@ -512,6 +513,7 @@ int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq
   p.dO = at<T>(ws, l.dO);
   p.dOt = at<T>(ws, l.dOt);
   p.qt = at<T>(ws, l.qt);
+  p.qs = at<T>(ws, l.qs);
   p.kt = at<T>(ws, l.kt);
   p.vr = at<T>(ws, l.vr);
   p.gall_t = at<T>(ws, l.gall_t);

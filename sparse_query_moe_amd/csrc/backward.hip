@@ -480,6 +480,353 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// attention backward, bf16: operand tiles shared by the block through LDS
+// ---------------------------------------------------------------------------
+// The four waves of a block need the same 64-row tiles (the dK/dV kernel: Q,
+// dO, Q^T and dO^T of a query block; the dQ kernel: K, V and K^T of a key
+// block).  The tiles go straight from global memory into a two-stage LDS
+// ring (global_load_lds_dwordx4, swizzled as in the forward kernel), one
+// stage ahead of the MFMAs.
+template <int D>
+struct BwdTiles {
+  static constexpr int ROWB = D * 2;              // bytes per row of a row-major tile
+  static constexpr int RT = 64 * ROWB;            // 64 rows
+  static constexpr int TT = D * 128;              // a [D][64] permuted tile
+  static constexpr int RRUNS = RT / 1024, TRUNS = TT / 1024;
+  static_assert(RRUNS % 4 == 0 && TRUNS % 4 == 0, "whole runs per wave");
+};
+
+// wave w copies runs w, w + 4, ... of a 64-row row-major tile (rows past
+// row_lim repeat the last valid row: their results are masked)
+template <int D>
+__device__ __forceinline__ void dma_rows(const bf16_t* src, int row_lim, char* lds, int wave,
+                                         int lane) {
+  typedef BwdTiles<D> S;
+#pragma unroll
+  for (int i = 0; i < S::RRUNS / 4; ++i) {
+    const int run = wave + 4 * i;
+    const int off = run * 1024 + 16 * lane;
+    const int row = off / S::ROWB, pc = (off % S::ROWB) / 16;
+    const int lc = pc ^ swz_xor<S::ROWB>(row);
+    dma16(src + static_cast<size_t>(min(row, row_lim - 1)) * D + lc * 8, lds + run * 1024);
+  }
+}
+template <int D>
+__device__ __forceinline__ void dma_tile(const bf16_t* src, char* lds, int wave, int lane) {
+  typedef BwdTiles<D> S;
+#pragma unroll
+  for (int i = 0; i < S::TRUNS / 4; ++i) {
+    const int run = wave + 4 * i;
+    const int off = run * 1024 + 16 * lane;
+    const int row = off / 128, pc = (off % 128) / 16;
+    const int lc = pc ^ swz_xor<128>(row);
+    dma16(src + row * 64 + lc * 8, lds + run * 1024);
+  }
+}
+
+// grid (ceil(L/128), B*G); wave w owns keys 128x + 32w .. +31; the block
+// walks (slot head, 64-query block) pairs from the block's first query on.
+// qs: the queries scaled by softmax_scale*log2(e), rounded to bf16, [B, H, L, D].
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_lds_kernel(AttnBwdArgs a, const bf16_t* qs) {
+  typedef bf16_t T;
+  typedef bf16x8 F;
+  typedef BwdTiles<D> S;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int STAGE = 2 * S::RT + 2 * S::TT;
+  constexpr int DMA_OPS = 2 * (S::RRUNS / 4) + 2 * (S::TRUNS / 4);  // per wave per stage
+  extern __shared__ __align__(16) char smem[];
+  __shared__ float stat[4][2][64];
+  __shared__ int rows[4][32], cols[4][32];
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.y / a.G, g = blockIdx.y % a.G;
+  const int L = a.L;
+  const int kb0 = blockIdx.x * 128, kw0 = kb0 + 32 * wave;
+  const int my_key = kw0 + (lane & 31);
+  const int krow = min(my_key, L - 1);
+  const T* Kg = static_cast<const T*>(a.keys) + (static_cast<size_t>(b) * a.G + g) * L * D;
+  const T* Vg = static_cast<const T*>(a.vr) + (static_cast<size_t>(b) * a.G + g) * L * D;
+  F kf[NKS], vf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    kf[ks] = load_frag(Kg + static_cast<size_t>(krow) * D + 16 * ks + 8 * half);
+    vf[ks] = load_frag(Vg + static_cast<size_t>(krow) * D + 16 * ks + 8 * half);
+  }
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+
+  const int nh = a.heads_per_group + (g == a.extra_group && a.n_grouped < a.H ? 1 : 0);
+  const int q_begin = (kb0 / 64) * 64;
+  const int nqb = (L - q_begin + 63) / 64;
+  const int n_iter = nh * nqb;
+  auto head_of = [&](int hi) { return hi < a.heads_per_group ? g * a.heads_per_group + hi : a.n_grouped; };
+  // stage it: (head, query block) and its sources
+  auto issue = [&](int it) {
+    const int h = head_of(it / nqb), q0 = q_begin + 64 * (it % nqb);
+    const size_t bh = static_cast<size_t>(b) * a.H + h;
+    char* st = smem + (it & 1) * STAGE;
+    dma_rows<D>(qs + (bh * L + q0) * D, L - q0, st, wave, lane);
+    dma_rows<D>(static_cast<const T*>(a.dO) + (bh * L + q0) * D, L - q0, st + S::RT, wave, lane);
+    const size_t tb = (bh * a.tiles + q0 / 64) * D * 64;
+    dma_tile<D>(static_cast<const T*>(a.qt) + tb, st + 2 * S::RT, wave, lane);
+    dma_tile<D>(static_cast<const T*>(a.dOt) + tb, st + 2 * S::RT + S::TT, wave, lane);
+  };
+  auto load_stats = [&](int it, float& ls, float& ds_) {
+    const int h = head_of(it / nqb), q = q_begin + 64 * (it % nqb) + lane;
+    const size_t bh = static_cast<size_t>(b) * a.H + h;
+    ls = q < L ? a.lse[bh * L + q] : 0.f;
+    ds_ = q < L ? a.dsum[bh * L + q] : 0.f;
+  };
+
+  float ls_cur = 0.f, ds_cur = 0.f;
+  if (n_iter > 0) {
+    issue(0);
+    load_stats(0, ls_cur, ds_cur);
+  }
+  for (int it = 0; it < n_iter; ++it) {
+    float ls_nxt = 0.f, ds_nxt = 0.f;
+    const bool more = it + 1 < n_iter;
+    if (more) {
+      issue(it + 1);
+      load_stats(it + 1, ls_nxt, ds_nxt);
+    }
+    // this stage's copies and statistics are in; the next stage's are in flight
+    wait_vm(more ? DMA_OPS + 2 : 0);
+    stat[wave][0][lane] = ls_cur;
+    stat[wave][1][lane] = ds_cur;
+    __builtin_amdgcn_s_barrier();  // every wave's copies of this stage have landed
+    __builtin_amdgcn_sched_barrier(0);
+    const char* st = smem + (it & 1) * STAGE;
+    const char* sQ = st;
+    const char* sdO = st + S::RT;
+    const char* sQt = st + 2 * S::RT;
+    const char* sdOt = sQt + S::TT;
+    const int q0 = q_begin + 64 * (it % nqb);
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const int qs0 = q0 + 32 * m2;
+      if (kw0 >= L || qs0 + 31 < kw0 || qs0 >= L) continue;  // wave-uniform: all masked
+      f32x16 sc, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        mma32(sc, LdsFrag<T, S::ROWB>::get(sQ, 32 * m2 + (lane & 31), 16 * ks + 8 * half), kf[ks]);
+        mma32(dp, LdsFrag<T, S::ROWB>::get(sdO, 32 * m2 + (lane & 31), 16 * ks + 8 * half), vf[ks]);
+      }
+      f32x16 P, dS;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * m2 + acc_row(i, lane);
+        const int qq = q0 + r;
+        const bool keep = qq < L && my_key <= qq;
+        const float pv = keep ? __builtin_amdgcn_exp2f(sc[i] - stat[wave][0][r]) : 0.f;
+        P[i] = pv;
+        dS[i] = pv * (dp[i] - stat[wave][1][r]);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const F bp = FragFromAcc<T>::get(P, 8 * m);
+        const F bs = FragFromAcc<T>::get(dS, 8 * m);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int row = 32 * db + (lane & 31), col = 32 * m2 + 16 * m + 8 * half;
+          mma32(dv[db], LdsFrag<T, 128>::get(sdOt, row, col), bp);
+          mma32(dk[db], LdsFrag<T, 128>::get(sQt, row, col), bs);
+        }
+      }
+    }
+    ls_cur = ls_nxt;
+    ds_cur = ds_nxt;
+    lds_barrier();  // every wave is done with this stage before it is refilled
+  }
+  if (kw0 >= L) return;
+  // dK^T, dV^T: row = dim, column = key -> rows of Gall, through this wave's
+  // part of the (now free) ring
+  float* buf = reinterpret_cast<float*>(smem) + wave * 32 * (D + 1);
+  if (lane < 32) {
+    rows[wave][lane] = kw0 + lane < L ? b * L + kw0 + lane : -1;
+    cols[wave][lane] = a.kcol + g * D;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[(lane & 31) * (D + 1) + 32 * db + acc_row(i, lane)] = dk[db][i] * a.scale;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  store_rows<T, D>(buf, static_cast<T*>(a.gall), a.ldg, lane, rows[wave], cols[wave]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < 32) cols[wave][lane] = a.vcol + g * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[(lane & 31) * (D + 1) + 32 * db + acc_row(i, lane)] = dv[db][i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  store_rows<T, D>(buf, static_cast<T*>(a.gall), a.ldg, lane, rows[wave], cols[wave]);
+}
+
+// grid (ceil(L/128), B*H); wave w owns queries 128x + 32w .. +31; the block
+// walks the 64-key blocks up to its last query.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(AttnBwdArgs a, const bf16_t* qs) {
+  typedef bf16_t T;
+  typedef bf16x8 F;
+  typedef BwdTiles<D> S;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int STAGE = 2 * S::RT + S::TT;
+  constexpr int DMA_OPS = 2 * (S::RRUNS / 4) + S::TRUNS / 4;
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int rows[4][32], cols[4][32];
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.y / a.H, h = blockIdx.y % a.H;
+  const int L = a.L;
+  const int g = group_of(a, h);
+  const size_t bh = static_cast<size_t>(b) * a.H + h;
+  const int qb0 = blockIdx.x * 128, qw0 = qb0 + 32 * wave;
+  const int my_q = qw0 + (lane & 31);
+  const bool qok = my_q < L;
+  const T* dO = static_cast<const T*>(a.dO) + bh * L * D;
+  const T* Kg = static_cast<const T*>(a.keys) + (static_cast<size_t>(b) * a.G + g) * L * D;
+  const T* Vg = static_cast<const T*>(a.vr) + (static_cast<size_t>(b) * a.G + g) * L * D;
+  const T* Kt = static_cast<const T*>(a.kt) + (static_cast<size_t>(b) * a.G + g) * a.tiles * D * 64;
+  const float lse = qok ? a.lse[bh * L + my_q] : 0.f;
+  const float dsm = qok ? a.dsum[bh * L + my_q] : 0.f;
+  F qf[NKS], df[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const size_t off = static_cast<size_t>(qok ? my_q : 0) * D + 16 * ks + 8 * half;
+    qf[ks] = frag_or_zero(qs + bh * L * D + off, qok);
+    df[ks] = frag_or_zero(dO + off, qok);
+  }
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+  const int n_iter = (min(qb0 + 128, L) + 63) / 64;  // key blocks up to the block's last query
+  const int w_last = min(qw0 + 31, L - 1);
+  auto issue = [&](int it) {
+    const int k0 = 64 * it;
+    char* st = smem + (it & 1) * STAGE;
+    dma_rows<D>(Kg + static_cast<size_t>(k0) * D, L - k0, st, wave, lane);
+    dma_rows<D>(Vg + static_cast<size_t>(k0) * D, L - k0, st + S::RT, wave, lane);
+    dma_tile<D>(Kt + static_cast<size_t>(it) * D * 64, st + 2 * S::RT, wave, lane);
+  };
+  issue(0);
+  for (int it = 0; it < n_iter; ++it) {
+    const bool more = it + 1 < n_iter;
+    if (more) issue(it + 1);
+    dma_barrier(more ? DMA_OPS : 0);
+    const char* st = smem + (it & 1) * STAGE;
+    const char* sK = st;
+    const char* sV = st + S::RT;
+    const char* sKt = st + 2 * S::RT;
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const int ks0 = 64 * it + 32 * m2;
+      if (qw0 >= L || ks0 > w_last) continue;  // wave-uniform: every key after every query
+      f32x16 stt, dpt;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) stt[i] = dpt[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        mma32(stt, LdsFrag<T, S::ROWB>::get(sK, 32 * m2 + (lane & 31), 16 * ks + 8 * half), qf[ks]);
+        mma32(dpt, LdsFrag<T, S::ROWB>::get(sV, 32 * m2 + (lane & 31), 16 * ks + 8 * half), df[ks]);
+      }
+      f32x16 dS;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = ks0 + acc_row(i, lane);
+        const bool keep = qok && kk <= my_q;
+        const float pv = keep ? __builtin_amdgcn_exp2f(stt[i] - lse) : 0.f;
+        dS[i] = pv * (dpt[i] - dsm);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const F bs = FragFromAcc<T>::get(dS, 8 * m);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          mma32(dq[db], LdsFrag<T, 128>::get(sKt, 32 * db + (lane & 31), 32 * m2 + 16 * m + 8 * half), bs);
+      }
+    }
+    lds_barrier();  // every wave is done with this stage before it is refilled
+  }
+  if (qw0 >= L) return;
+  float* buf = reinterpret_cast<float*>(smem) + wave * 32 * (D + 1);
+  if (lane < 32) {
+    const int qq = qw0 + lane;
+    rows[wave][lane] = qq < L ? b * L + qq : -1;
+    int col = h * D;
+    if (a.idx != nullptr) {
+      if (h < a.n_grouped) {
+        const int j = h % a.k;
+        const int e = qq < L ? a.idx[((static_cast<size_t>(b) * L + qq) * a.G + g) * a.k + j] : 0;
+        col = (g * a.E + e) * D;
+      } else {
+        col = a.G * a.E * D;
+      }
+    }
+    cols[wave][lane] = col;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buf[(lane & 31) * (D + 1) + 32 * db + acc_row(i, lane)] = dq[db][i] * a.scale;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  store_rows<T, D>(buf, static_cast<T*>(a.gall), a.ldg, lane, rows[wave], cols[wave]);
+}
+
+// queries scaled by softmax_scale * log2(e), rounded to bf16: dst slab s reads
+// source slab (s / H) * q_heads + s % H
+__global__ __launch_bounds__(256) void scale_rows_kernel(const bf16_t* __restrict__ src,
+                                                         bf16_t* __restrict__ dst, size_t n,
+                                                         size_t slab, int H, int q_heads,
+                                                         float sl) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * 256) {
+    const size_t s = i / slab, e = i % slab;
+    const size_t src_s = (s / H) * q_heads + s % H;
+    dst[i] = from_f32<bf16_t>(to_f32(src[src_s * slab + e]) * sl);
+  }
+}
+
+template <int D>
+hipError_t launch_attn_bwd_lds(const AttnBwdArgs& a, const bf16_t* qs, hipStream_t stream) {
+  typedef BwdTiles<D> S;
+  constexpr int lds_kv = 2 * (2 * S::RT + 2 * S::TT);
+  constexpr int lds_q = 2 * (2 * S::RT + S::TT);
+  static_assert(lds_kv >= 4 * 32 * (D + 1) * 4 && lds_q >= 4 * 32 * (D + 1) * 4,
+                "the ring holds the epilogue's transposes");
+  static const hipError_t attr1 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&attn_bwd_dkdv_lds_kernel<D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+  static const hipError_t attr2 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&attn_bwd_dq_lds_kernel<D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds_q);
+  if (attr1 != hipSuccess) return attr1;
+  if (attr2 != hipSuccess) return attr2;
+  hipLaunchKernelGGL((attn_bwd_dkdv_lds_kernel<D>), dim3((a.L + 127) / 128, a.B * a.G), dim3(256),
+                     lds_kv, stream, a, qs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_lds_kernel<D>), dim3((a.L + 127) / 128, a.B * a.H), dim3(256),
+                     lds_q, stream, a, qs);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // router backward: one block per token
 // ---------------------------------------------------------------------------
 struct RouterBwdArgs {
@@ -765,11 +1112,28 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     a.extra_group = p.extra_group;
     a.scale = p.scale;
     a.scale_log2 = p.scale * 1.4426950408889634f;
-    switch (D) {
-      case 32: GQE_TRY((launch_attn_bwd_d<T, 32>(a, stream))); break;
-      case 64: GQE_TRY((launch_attn_bwd_d<T, 64>(a, stream))); break;
-      case 128: GQE_TRY((launch_attn_bwd_d<T, 128>(a, stream))); break;
-      default: return hipErrorInvalidValue;
+    if constexpr (sizeof(T) == 2) {
+      // queries pre-scaled as the forward kernel scores them
+      const size_t n = static_cast<size_t>(B) * H * L * D;
+      const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 16384));
+      hipLaunchKernelGGL(scale_rows_kernel, dim3(blocks), dim3(256), 0, stream,
+                         static_cast<const bf16_t*>(p.q), static_cast<bf16_t*>(p.qs), n,
+                         static_cast<size_t>(L) * D, H, p.q_heads, a.scale_log2);
+      GQE_TRY(hipGetLastError());
+      const bf16_t* qs = static_cast<const bf16_t*>(p.qs);
+      switch (D) {
+        case 32: GQE_TRY(launch_attn_bwd_lds<32>(a, qs, stream)); break;
+        case 64: GQE_TRY(launch_attn_bwd_lds<64>(a, qs, stream)); break;
+        case 128: GQE_TRY(launch_attn_bwd_lds<128>(a, qs, stream)); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (D) {
+        case 32: GQE_TRY((launch_attn_bwd_d<T, 32>(a, stream))); break;
+        case 64: GQE_TRY((launch_attn_bwd_d<T, 64>(a, stream))); break;
+        case 128: GQE_TRY((launch_attn_bwd_d<T, 128>(a, stream))); break;
+        default: return hipErrorInvalidValue;
+      }
     }
   }
   // 4. router backward and the auxiliary loss

@@ -128,7 +128,7 @@ struct BwdParams {
   // gradients (float32, caller-owned)
   float *dx, *dwq, *dwk, *dwv, *dwr, *dbr, *dwo, *aux_loss;
   // scratch
-  void *gall, *w_t, *wo_t, *dO, *dOt, *qt, *kt, *vr, *gall_t, *x_t, *dy_t, *s_t;
+  void *gall, *w_t, *wo_t, *dO, *dOt, *qt, *qs, *kt, *vr, *gall_t, *x_t, *dy_t, *s_t;
   float *ds, *dsum, *dw, *dr, *p_all;
   double* psum;
   // shapes
