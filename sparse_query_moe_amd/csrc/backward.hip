@@ -524,25 +524,36 @@ __device__ __forceinline__ void dma_tile(const bf16_t* src, char* lds, int wave,
   }
 }
 
-// grid (ceil(L/128), B*G); wave w owns keys 128x + 32w .. +31; the block
-// walks (slot head, 64-query block) pairs from the block's first query on.
+// The dK/dV kernel's blocks are 8 waves (256 keys; 4 waves at d_h 128, whose
+// accumulators need all 256 VGPRs): every query tile a block streams serves
+// all of them.  Run r of a stage (1 KB) is copied by wave r % waves.
+template <int D> struct DkvWaves { static constexpr int n = D >= 128 ? 4 : 8; };
+
+// grid (ceil(L/256), B*G); wave w owns keys 256x + 32w .. +31.  The block
+// walks its 64-query blocks from the last one down, and the group's slot heads
+// inside each: concurrent blocks of a group then read the same query tiles at
+// the same time, which the caches serve once.
 // qs: the queries scaled by softmax_scale*log2(e), rounded to bf16, [B, H, L, D].
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_lds_kernel(AttnBwdArgs a, const bf16_t* qs) {
+__global__ __launch_bounds__(64 * DkvWaves<D>::n, 1) void attn_bwd_dkdv_lds_kernel(
+    AttnBwdArgs a, const bf16_t* qs) {
   typedef bf16_t T;
   typedef bf16x8 F;
   typedef BwdTiles<D> S;
+  constexpr int NW = DkvWaves<D>::n;
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int STAGE = 2 * S::RT + 2 * S::TT;
-  constexpr int DMA_OPS = 2 * (S::RRUNS / 4) + 2 * (S::TRUNS / 4);  // per wave per stage
+  constexpr int NRUNS = STAGE / 1024;
+  static_assert(NRUNS % NW == 0, "whole runs per wave");
+  constexpr int DMA_OPS = NRUNS / NW;  // per wave per stage
   extern __shared__ __align__(16) char smem[];
-  __shared__ float stat[4][2][64];
-  __shared__ int rows[4][32], cols[4][32];
+  __shared__ float stat[NW][2][64];
+  __shared__ int rows[NW][32], cols[NW][32];
   const int lane = threadIdx.x & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y / a.G, g = blockIdx.y % a.G;
   const int L = a.L;
-  const int kb0 = blockIdx.x * 128, kw0 = kb0 + 32 * wave;
+  const int kb0 = blockIdx.x * 32 * NW, kw0 = kb0 + 32 * wave;
   const int my_key = kw0 + (lane & 31);
   const int krow = min(my_key, L - 1);
   const T* Kg = static_cast<const T*>(a.keys) + (static_cast<size_t>(b) * a.G + g) * L * D;
@@ -562,21 +573,39 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_lds_kernel(AttnBwdArgs a
   const int nh = a.heads_per_group + (g == a.extra_group && a.n_grouped < a.H ? 1 : 0);
   const int q_begin = (kb0 / 64) * 64;
   const int nqb = (L - q_begin + 63) / 64;
+  const int last_qb = (L - 1) / 64;
   const int n_iter = nh * nqb;
   auto head_of = [&](int hi) { return hi < a.heads_per_group ? g * a.heads_per_group + hi : a.n_grouped; };
-  // stage it: (head, query block) and its sources
+  // stage it: query block last_qb - it / nh, slot head it % nh
+  auto qblk_of = [&](int it) { return 64 * (last_qb - it / nh); };
   auto issue = [&](int it) {
-    const int h = head_of(it / nqb), q0 = q_begin + 64 * (it % nqb);
+    const int h = head_of(it % nh), q0 = qblk_of(it);
     const size_t bh = static_cast<size_t>(b) * a.H + h;
     char* st = smem + (it & 1) * STAGE;
-    dma_rows<D>(qs + (bh * L + q0) * D, L - q0, st, wave, lane);
-    dma_rows<D>(static_cast<const T*>(a.dO) + (bh * L + q0) * D, L - q0, st + S::RT, wave, lane);
+    const T* qsrc = qs + (bh * L + q0) * D;
+    const T* dsrc = static_cast<const T*>(a.dO) + (bh * L + q0) * D;
     const size_t tb = (bh * a.tiles + q0 / 64) * D * 64;
-    dma_tile<D>(static_cast<const T*>(a.qt) + tb, st + 2 * S::RT, wave, lane);
-    dma_tile<D>(static_cast<const T*>(a.dOt) + tb, st + 2 * S::RT + S::TT, wave, lane);
+    const T* tq = static_cast<const T*>(a.qt) + tb;
+    const T* td = static_cast<const T*>(a.dOt) + tb;
+#pragma unroll
+    for (int i = 0; i < DMA_OPS; ++i) {
+      const int run = wave + NW * i;  // wave-uniform
+      const int off = run * 1024 + 16 * lane;
+      const T* src;
+      if (run < 2 * S::RRUNS) {  // Q or dO rows
+        const int o = off % S::RT;
+        const int row = o / S::ROWB, lc = ((o % S::ROWB) / 16) ^ swz_xor<S::ROWB>(row);
+        src = (run < S::RRUNS ? qsrc : dsrc) + static_cast<size_t>(min(row, L - q0 - 1)) * D + lc * 8;
+      } else {  // Q^T or dO^T tile
+        const int o = (off - 2 * S::RT) % S::TT;
+        const int row = o / 128, lc = ((o % 128) / 16) ^ swz_xor<128>(row);
+        src = (run < 2 * S::RRUNS + S::TRUNS ? tq : td) + row * 64 + lc * 8;
+      }
+      dma16(src, st + run * 1024);
+    }
   };
   auto load_stats = [&](int it, float& ls, float& ds_) {
-    const int h = head_of(it / nqb), q = q_begin + 64 * (it % nqb) + lane;
+    const int h = head_of(it % nh), q = qblk_of(it) + lane;
     const size_t bh = static_cast<size_t>(b) * a.H + h;
     ls = q < L ? a.lse[bh * L + q] : 0.f;
     ds_ = q < L ? a.dsum[bh * L + q] : 0.f;
@@ -605,7 +634,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_lds_kernel(AttnBwdArgs a
     const char* sdO = st + S::RT;
     const char* sQt = st + 2 * S::RT;
     const char* sdOt = sQt + S::TT;
-    const int q0 = q_begin + 64 * (it % nqb);
+    const int q0 = qblk_of(it);
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
       const int qs0 = q0 + 32 * m2;
@@ -805,10 +834,13 @@ __global__ __launch_bounds__(256) void scale_rows_kernel(const bf16_t* __restric
 template <int D>
 hipError_t launch_attn_bwd_lds(const AttnBwdArgs& a, const bf16_t* qs, hipStream_t stream) {
   typedef BwdTiles<D> S;
-  constexpr int lds_kv = 2 * (2 * S::RT + 2 * S::TT);
+  // the ring, or the epilogue's per-wave transposes if they need more
+  constexpr int NW = DkvWaves<D>::n;
+  constexpr int ring_kv = 2 * (2 * S::RT + 2 * S::TT), tr_kv = NW * 32 * (D + 1) * 4;
+  constexpr int lds_kv = ring_kv > tr_kv ? ring_kv : tr_kv;
   constexpr int lds_q = 2 * (2 * S::RT + S::TT);
-  static_assert(lds_kv >= 4 * 32 * (D + 1) * 4 && lds_q >= 4 * 32 * (D + 1) * 4,
-                "the ring holds the epilogue's transposes");
+  static_assert(lds_q >= 4 * 32 * (D + 1) * 4, "the ring holds the epilogue's transposes");
+  static_assert(lds_kv <= 160 * 1024 - 8 * 1024, "LDS of one CU");
   static const hipError_t attr1 = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&attn_bwd_dkdv_lds_kernel<D>),
       hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
@@ -817,8 +849,9 @@ hipError_t launch_attn_bwd_lds(const AttnBwdArgs& a, const bf16_t* qs, hipStream
       hipFuncAttributeMaxDynamicSharedMemorySize, lds_q);
   if (attr1 != hipSuccess) return attr1;
   if (attr2 != hipSuccess) return attr2;
-  hipLaunchKernelGGL((attn_bwd_dkdv_lds_kernel<D>), dim3((a.L + 127) / 128, a.B * a.G), dim3(256),
-                     lds_kv, stream, a, qs);
+  hipLaunchKernelGGL((attn_bwd_dkdv_lds_kernel<D>),
+                     dim3((a.L + 32 * NW - 1) / (32 * NW), a.B * a.G), dim3(64 * NW), lds_kv,
+                     stream, a, qs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dq_lds_kernel<D>), dim3((a.L + 127) / 128, a.B * a.H), dim3(256),
