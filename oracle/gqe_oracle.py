@@ -655,3 +655,118 @@ def gqa_backward(x, wq_dense, wk, wv, wo_dense, dy, n_groups, n_experts, head_di
             dwv[rows] += dV[g].T @ xb
             dx[b] += dK[g] @ wk[rows] + dV[g] @ wv[rows]
     return dict(dx=dx, dwq=dwq, dwk=dwk, dwv=dwv, dwo=dwo, do=do, fwd=fwd)
+
+
+# --------------------------------------------------------------------------
+# non-uniform k: group g selects k_g experts
+# --------------------------------------------------------------------------
+# [pptc] section 6 lists a non-uniform k ("each group selects a different
+# number of experts") as future work.  Everything else is the layer above:
+# the top-k_g of every group by the same rule, weights renormalized over the
+# k_g of the group, hard slots group-major (group g's k_g slots in rank
+# order), then the shared slot and the weighted slot; W_O has (K+2)*d_h
+# inputs with K = sum of k_g.
+
+
+def group_offsets(group_top_k):
+    """koff[g]: first hard slot of group g; koff[G] = K."""
+    koff = [0]
+    for kg in group_top_k:
+        koff.append(koff[-1] + int(kg))
+    return koff
+
+
+def route_group_k(x, wr, br, n_groups, n_experts, group_top_k):
+    """Steps 1-4 with k_g experts in group g.  Returns r, p [T, G, E] and idx,
+    w [T, K] (group g at koff[g] .. koff[g]+k_g-1, rank order)."""
+    r, p, _, _ = route(x, wr, br, n_groups, n_experts, max(group_top_k))
+    koff = group_offsets(group_top_k)
+    T = x.shape[0]
+    idx = np.empty((T, koff[-1]), dtype=np.int32)
+    w = np.empty((T, koff[-1]))
+    for g, kg in enumerate(group_top_k):
+        sel = topk_in_group(r[:, g], kg)                  # [T, k_g]
+        idx[:, koff[g]:koff[g + 1]] = sel
+        w[:, koff[g]:koff[g + 1]] = renormalize(p[:, g], sel)
+    return r, p, idx, w
+
+
+def dispatch_group_k(idx, n_groups, n_experts, group_top_k):
+    """Per-(b, g, e) lists for idx [B, L, K]: counts [B, G, E]; offsets, the
+    exclusive prefix of counts in (b, g, e) order; pos and slot (ascending t,
+    rank j) per list."""
+    B, L, _ = idx.shape
+    koff = group_offsets(group_top_k)
+    counts = np.zeros((B, n_groups, n_experts), dtype=np.int32)
+    pos_l, slot_l = [], []
+    for b in range(B):
+        for g in range(n_groups):
+            ids = idx[b, :, koff[g]:koff[g + 1]]           # [L, k_g]
+            for e in range(n_experts):
+                t_sel, j_sel = np.nonzero(ids == e)
+                counts[b, g, e] = t_sel.size
+                pos_l.append(t_sel)
+                slot_l.append(j_sel)
+    offsets = np.zeros(B * n_groups * n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts.reshape(-1))
+    return (counts, offsets.astype(np.int32), np.concatenate(pos_l).astype(np.int32),
+            np.concatenate(slot_l).astype(np.int32))
+
+
+def gqe_forward_group_k(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, group_top_k, head_dim,
+                        shared_kv_group=0, scale=None, output_mode="full"):
+    """The GQE layer with k_g experts selected in group g (float64).
+
+    Returns r, p [B,L,G,E]; idx, w [B,L,K]; counts, offsets, pos, slot; q, o
+    [B,L,S,d_h] (slot-heads: group g's k_g hard slots from koff[g], then the
+    shared head for the full output); s [B,L,width]; y [B,L,d].
+    """
+    if output_mode not in OUTPUT_MODES:
+        raise ValueError(output_mode)
+    full = output_mode == "full"
+    B, L, d = x.shape
+    G, E, dh = n_groups, n_experts, head_dim
+    koff = group_offsets(group_top_k)
+    K = koff[-1]
+    scale = 1.0 / math.sqrt(dh) if scale is None else scale
+    r, p, idx, w = route_group_k(x.reshape(B * L, d), wr, br, G, E, group_top_k)
+    r, p = r.reshape(B, L, G, E), p.reshape(B, L, G, E)
+    idx, w = idx.reshape(B, L, K), w.reshape(B, L, K)
+    counts, offsets, pos, slot = dispatch_group_k(idx, G, E, group_top_k)
+    S = K + (1 if full else 0)
+    q_all = np.empty((B, L, S, dh))
+    o_all = np.empty((B, L, S, dh))
+    s_all = np.empty((B, L, (K + (2 if full else 0)) * dh))
+    tpos = np.arange(L)
+    for b in range(B):
+        K_b = kv_project(x[b], wk, G, dh, L)
+        V_b = kv_project(x[b], wv, G, dh, L)
+        for g in range(G):
+            for j in range(group_top_k[g]):
+                h = koff[g] + j
+                qh = np.empty((L, dh))
+                for e in range(E):
+                    m = idx[b, :, h] == e
+                    if m.any():
+                        qh[m] = x[b][m] @ head_rows(wq, expert_head(g, e, E), dh).T
+                q_all[b, :, h] = qh
+                o_all[b, :, h] = causal_attention(qh, tpos, K_b[g], V_b[g], scale)
+        o_hard = o_all[b, :, :K]                          # [L, K, d_h]
+        if output_mode == "hard":
+            s_all[b] = o_hard.reshape(L, -1)
+            continue
+        if output_mode == "weighted_concat":
+            p_sel = np.concatenate([np.take_along_axis(p[b, :, g], idx[b, :, koff[g]:koff[g + 1]]
+                                                       .astype(np.int64), axis=-1)
+                                    for g in range(G)], axis=1)
+            s_all[b] = (p_sel[..., None] * o_hard).reshape(L, -1)
+            continue
+        q_sh = x[b] @ head_rows(wq, G * E, dh).T
+        o_sh = causal_attention(q_sh, tpos, K_b[shared_kv_group], V_b[shared_kv_group], scale)
+        q_all[b, :, K] = q_sh
+        o_all[b, :, K] = o_sh
+        o_w = np.einsum("lh,lhd->ld", w[b], o_hard)       # sum over groups and ranks
+        s_all[b] = np.concatenate([o_hard.reshape(L, -1), o_sh, o_w], axis=1)
+    y = output_projection(s_all, wo)
+    return dict(r=r, p=p, idx=idx, w=w, counts=counts, offsets=offsets, pos=pos, slot=slot,
+                q=q_all, o=o_all, s=s_all, y=y)

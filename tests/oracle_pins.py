@@ -564,6 +564,69 @@ def pin_backward_invariances(orc):
     assert np.allclose(g["dr"], np.broadcast_to(want, g["dr"].shape), rtol=0, atol=1e-15)
     assert abs(g["aux_loss"] - (E / G) * G * sum(f_e / E)) < 1e-12   # = 1 at uniform p
 
+
+# ---------------------------------------------------------------------------
+# non-uniform k per group
+# ---------------------------------------------------------------------------
+
+def _run_gk(orc, t, ks, **kw):
+    return orc.gqe_forward_group_k(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"],
+                                   t["G"], t["E"], ks, t["dh"], **kw)
+
+
+def pin_group_k_uniform_is_the_layer(orc):
+    """With the same k in every group the per-group layer is the pages' layer:
+    routing, dispatch lists and outputs, for every output construction."""
+    rng = np.random.default_rng(71)
+    for mode in orc.OUTPUT_MODES:
+        t = tiny_layer(rng, B=2, L=8, G=3, E=3, k=2)
+        if mode != "full":
+            t["wo"] = np.ascontiguousarray(t["wo"][:, :t["k"] * t["G"] * t["dh"]])
+        a = run(orc, t, output_mode=mode)
+        b = _run_gk(orc, t, [t["k"]] * t["G"], output_mode=mode)
+        B, L = t["x"].shape[:2]
+        assert np.array_equal(b["idx"], a["idx"].reshape(B, L, -1))
+        assert np.allclose(b["w"], a["w"].reshape(B, L, -1), rtol=0, atol=1e-15)
+        for key in ("counts", "offsets", "pos", "slot"):
+            assert np.array_equal(b[key], a[key]), key
+        assert np.allclose(b["y"], a["y"], rtol=0, atol=1e-12), mode
+
+
+def pin_group_k_selection_brute_force(orc):
+    """Group g's selection is the best k_g-subset by logit (ties to the lower
+    index), in rank order; its weights renormalize over that subset only."""
+    rng = np.random.default_rng(73)
+    ks = [1, 3, 2]
+    t = tiny_layer(rng, B=1, L=6, G=3, E=4, k=2)
+    t["wo"] = rng.standard_normal((t["x"].shape[2], (sum(ks) + 2) * t["dh"]))
+    f = _run_gk(orc, t, ks)
+    koff = [0, 1, 4, 6]
+    for tt in range(6):
+        for g, kg in enumerate(ks):
+            r = f["r"][0, tt, g]
+            best = max(itertools.combinations(range(4), kg), key=lambda c: (sum(r[list(c)]), [-i for i in c]))
+            got = f["idx"][0, tt, koff[g]:koff[g + 1]]
+            assert sorted(got.tolist()) == sorted(best)
+            assert all(r[got[i]] >= r[got[i + 1]] for i in range(kg - 1))
+            ps = f["p"][0, tt, g][got]
+            assert np.allclose(f["w"][0, tt, koff[g]:koff[g + 1]], ps / ps.sum(), rtol=0, atol=1e-15)
+
+
+def pin_group_k_first_position(orc):
+    """At t = 0 every head sees one key: y[0] = [v_g repeated k_g times per
+    group | v_shared | sum_g v_g] . W_O^T (the weights of a group sum to 1)."""
+    rng = np.random.default_rng(79)
+    ks = [3, 1, 2]
+    t = tiny_layer(rng, B=1, L=5, G=3, E=3, k=1)
+    dh = t["dh"]
+    t["wo"] = rng.standard_normal((t["x"].shape[2], (sum(ks) + 2) * dh))
+    f = _run_gk(orc, t, ks, shared_kv_group=2)
+    x0 = t["x"][0, 0]
+    v = (t["wv"] @ x0).reshape(3, dh)
+    slots = [v[g] for g in range(3) for _ in range(ks[g])] + [v[2], v.sum(axis=0)]
+    want = np.concatenate(slots) @ t["wo"].T
+    assert np.allclose(f["y"][0, 0], want, rtol=0, atol=1e-12)
+
 ALL_PINS = [
     pin_k_equals_e_is_dense_gqa,
     pin_weights_sum_to_one,
@@ -585,4 +648,7 @@ ALL_PINS = [
     pin_decode_step_is_prefill_row,
     pin_backward_finite_differences,
     pin_backward_invariances,
+    pin_group_k_uniform_is_the_layer,
+    pin_group_k_selection_brute_force,
+    pin_group_k_first_position,
 ]

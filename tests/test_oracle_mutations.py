@@ -248,6 +248,18 @@ def m_bwd_shared_head_group0(mod):
     _patch_source(mod, "heads.append((kG, shared_kv_group))", "heads.append((kG, 0))")
 
 
+def m_group_k_first_groups_k(mod):
+    """every group selects as many experts as group 0."""
+    _patch_source(mod, "        sel = topk_in_group(r[:, g], kg)                  # [T, k_g]",
+                  "        sel = topk_in_group(r[:, g], group_top_k[0])[:, :kg]")
+
+
+def m_group_k_weights_over_all(mod):
+    """per-group weights renormalized over the largest k instead of k_g."""
+    _patch_source(mod, "        w[:, koff[g]:koff[g + 1]] = renormalize(p[:, g], sel)",
+                  "        w[:, koff[g]:koff[g + 1]] = renormalize(p[:, g], topk_in_group(r[:, g], max(group_top_k)))[:, :kg]")
+
+
 MUTATIONS = [
     m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
     m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
@@ -259,7 +271,7 @@ MUTATIONS = [
     m_wconcat_renormalized, m_wconcat_unscaled, m_hard_rank_reversed, m_decode_stale_cache,
     m_bwd_no_rowsum_term, m_bwd_dk_unscaled, m_bwd_weighted_slot_dropped,
     m_bwd_softmax_jacobian_diagonal, m_bwd_aux_sign, m_aux_fraction_per_token,
-    m_bwd_shared_head_group0,
+    m_bwd_shared_head_group0, m_group_k_first_groups_k, m_group_k_weights_over_all,
 ]
 
 
