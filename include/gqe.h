@@ -83,8 +83,12 @@ typedef enum {
  * d_model a positive multiple of 8; 1 <= n_groups; 1 <= n_experts <= 32;
  * 1 <= top_k <= n_experts; n_groups*n_experts <= 64;
  * 0 <= shared_kv_group < n_groups; batch*seq_len*n_groups*n_experts < 2^31;
- * output_mode a gqe_output_mode.
+ * output_mode a gqe_output_mode; every group_top_k[g] (when set) in
+ * [1, n_experts].  Below, k*G stands for the total K of selected experts
+ * (sum of group_top_k, or top_k*G): the hard slots are group-major, group g's
+ * k_g slots in rank order, and batch*seq_len*K < 2^31.
  * Built subset (GQE_ERR_UNSUPPORTED otherwise): head_dim in {32, 64, 128};
+ * group_top_k only for the prefill calls (not decode or backward);
  * the projections stream their reduction dimension in 128-byte steps, so
  * d_model, the slot width ((top_k*n_groups+2)*head_dim, or
  * top_k*n_groups*head_dim for the ablation outputs) and
@@ -103,12 +107,17 @@ typedef struct gqe_config {
   float softmax_scale;      /* attention scale; 0 selects 1/sqrt(head_dim)     */
   const float* router_bias; /* device float32 [G*E] added to the logits, or NULL */
   int32_t output_mode;      /* gqe_output_mode (GQE layer only)                */
+  const int32_t* group_top_k; /* host int32 [G]: experts selected in group g (the
+                               * non-uniform k the pages list as future work,
+                               * pptc.cn section 6), or NULL for top_k in every
+                               * group.  Read during each call. */
 } gqe_config;
 
 /* Byte offsets into the workspace of every intermediate, so that callers can
  * read (or seed) them.  All offsets are 256-byte aligned.
- *   idx     int32 [B, L, G, k]   selected experts, best first
- *   w       float [B, L, G, k]   renormalized router weights
+ *   idx     int32 [B, L, G, k]   selected experts, best first (per-group k:
+ *                                [B, L, K], group g at its slot offset)
+ *   w       float [B, L, G, k]   renormalized router weights (same layout)
  *   counts  int32 [B*G*E]        tokens routed to expert e of (b, g)
  *   offsets int32 [B*G*E+1]      exclusive prefix sum of counts, (b,g,e) order
  *   pos     int32 [B*L*G*k]      list (b,g,e) at offsets[(b*G+g)*E+e]: the

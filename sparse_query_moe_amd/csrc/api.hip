@@ -28,7 +28,12 @@ bool shape_ok(const gqe_config* c) {
   if (c->shared_kv_group < 0 || c->shared_kv_group >= c->n_groups) return false;
   if (c->dtype != GQE_DTYPE_BF16 && c->dtype != GQE_DTYPE_FP32) return false;
   if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return false;
-  const long long rows = static_cast<long long>(c->batch) * c->seq_len * c->n_groups * c->top_k;
+  if (c->group_top_k != nullptr)  // n_groups <= 64 here
+    for (int g = 0; g < c->n_groups; ++g)
+      if (c->group_top_k[g] < 1 || c->group_top_k[g] > c->n_experts) return false;
+  long long K = 0;
+  for (int g = 0; g < c->n_groups; ++g) K += c->group_top_k ? c->group_top_k[g] : c->top_k;
+  const long long rows = static_cast<long long>(c->batch) * c->seq_len * K;
   if (rows >= (1LL << 31)) return false;
   if (static_cast<long long>(c->batch) * c->seq_len * c->n_groups * c->n_experts >= (1LL << 31))
     return false;
@@ -36,10 +41,34 @@ bool shape_ok(const gqe_config* c) {
   return true;
 }
 
+// experts selected in group g, and their sum over the groups (the hard slots)
+int group_k(const gqe_config* c, int g) { return c->group_top_k ? c->group_top_k[g] : c->top_k; }
+int total_k(const gqe_config* c) {
+  int K = 0;
+  for (int g = 0; g < c->n_groups; ++g) K += group_k(c, g);
+  return K;
+}
+int max_k(const gqe_config* c) {
+  int m = 0;
+  for (int g = 0; g < c->n_groups; ++g) m = group_k(c, g) > m ? group_k(c, g) : m;
+  return m;
+}
+GroupK make_group_k(const gqe_config* c) {
+  GroupK gk{};
+  gk.koff[0] = 0;
+  for (int g = 0; g < c->n_groups; ++g) {
+    gk.kg[g] = group_k(c, g);
+    gk.koff[g + 1] = gk.koff[g] + gk.kg[g];
+  }
+  gk.K = gk.koff[c->n_groups];
+  gk.kmax = max_k(c);
+  return gk;
+}
+
 // the full GQE output has the shared head's slot and the weighted slot after
 // the k*G hard slots; the ablation outputs only the hard slots
 bool full_output(const gqe_config* c) { return c->output_mode == GQE_OUTPUT_FULL; }
-int slot_count(const gqe_config* c) { return c->top_k * c->n_groups + (full_output(c) ? 2 : 0); }
+int slot_count(const gqe_config* c) { return total_k(c) + (full_output(c) ? 2 : 0); }
 
 bool head_dim_ok(const gqe_config* c) {
   return c->head_dim == 32 || c->head_dim == 64 || c->head_dim == 128;
@@ -74,12 +103,12 @@ struct Layout {
 // output), or all G*E dense heads
 int attn_heads(const gqe_config* c, bool dense) {
   return dense ? c->n_groups * c->n_experts
-               : c->top_k * c->n_groups + (full_output(c) ? 1 : 0);
+               : total_k(c) + (full_output(c) ? 1 : 0);
 }
 
 // Workspace of gqe_forward (dense == false) or gqa_forward (dense == true).
 Layout make_layout(const gqe_config* c, bool dense) {
-  const size_t B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts, k = c->top_k;
+  const size_t B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts;
   const size_t D = c->head_dim, es = elem_bytes(c);
   const size_t vt_tiles = (L + 63) / 64;
   Layout l{};
@@ -90,7 +119,7 @@ Layout make_layout(const gqe_config* c, bool dense) {
     return o;
   };
   if (!dense) {
-    const size_t rows = B * L * G * k;
+    const size_t rows = B * L * static_cast<size_t>(total_k(c));
     const size_t lists = B * G * E;
     l.pub.idx = take(rows * 4);
     l.pub.w = take(rows * 4);
@@ -101,7 +130,7 @@ Layout make_layout(const gqe_config* c, bool dense) {
     l.pub.scratch = off;
     l.chunk_counts = take(B * static_cast<size_t>(dispatch_chunks(static_cast<int>(L))) * G * E * 4);
     l.tile_off = take(B * G * (E + 1) * 4);
-    l.pub.q = take(B * (G * k + 1) * L * D * es);
+    l.pub.q = take(B * (static_cast<size_t>(total_k(c)) + 1) * L * D * es);
     l.pub.s = 0;
   } else {
     l.pub.q = take(B * G * E * L * D * es);
@@ -142,7 +171,7 @@ bool empty(const gqe_config* c) { return static_cast<long long>(c->batch) * c->s
 // Upper bound of the gathered-projection tiles of one (b, g): its lists hold
 // L*k rows in E lists.
 int gather_tiles_per_bg(const gqe_config* c) {
-  const long long rows = static_cast<long long>(c->seq_len) * c->top_k;
+  const long long rows = static_cast<long long>(c->seq_len) * max_k(c);
   return static_cast<int>((rows + kGatherRows - 1) / kGatherRows) + c->n_experts;
 }
 
@@ -154,7 +183,7 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
                  ProjPart part = kProjAll) {
   const Layout l = make_layout(c, dense);
   const int B = c->batch, L = c->seq_len, d = c->d_model, G = c->n_groups, E = c->n_experts;
-  const int k = c->top_k, D = c->head_dim;
+  const int D = c->head_dim;
   ProjSeg seg[3];
   const bool shared = dense || full_output(c);  // the ablation outputs have no shared head
   const int nq_cols = dense ? G * E * D : shared ? D : 0;
@@ -163,8 +192,9 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   seg[0].out = at<T>(ws, l.pub.q);
   seg[0].n_begin = 0;
   seg[0].n = nq_cols;
-  seg[0].heads = dense ? G * E : G * k + 1;
-  seg[0].head_base = dense ? 0 : G * k;
+  const int K = total_k(c);
+  seg[0].heads = dense ? G * E : K + 1;
+  seg[0].head_base = dense ? 0 : K;
   seg[0].transposed = 0;
   seg[1].w = wk;
   seg[1].out = at<T>(ws, l.pub.k);
@@ -188,7 +218,8 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   e = launch_gather_q<T>(static_cast<const T*>(x), static_cast<const T*>(wq), at<T>(ws, l.pub.q),
                          at<int32_t>(ws, l.pub.counts), at<int32_t>(ws, l.pub.offsets),
                          at<int32_t>(ws, l.pub.pos), at<int32_t>(ws, l.pub.slot),
-                         at<int32_t>(ws, l.tile_off), B, L, d, G, E, k, D, gather_tiles_per_bg(c),
+                         at<int32_t>(ws, l.tile_off), B, L, d, G, E, make_group_k(c), D,
+                         gather_tiles_per_bg(c),
                          stream);
   return hip_status(e);
 }
@@ -196,7 +227,7 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
 template <typename T>
 int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream) {
   const Layout l = make_layout(c, dense);
-  const int G = c->n_groups, E = c->n_experts, k = c->top_k, D = c->head_dim;
+  const int G = c->n_groups, E = c->n_experts, D = c->head_dim;
   AttnParams p;
   p.row_scale = nullptr;
   p.lse = at<float>(ws, l.pub.lse);
@@ -210,14 +241,17 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
   p.L = c->seq_len;
   if (dense) {
     p.H = G * E;
-    p.heads_per_group = E;
+    p.q_heads = G * E;
     p.n_grouped = G * E;
+    for (int g = 0; g <= G; ++g) p.koff[g] = g * E;
     p.extra_group = 0;
     p.ld_o = static_cast<int64_t>(G) * E * D;
   } else {
-    p.H = G * k + (full_output(c) ? 1 : 0);
-    p.heads_per_group = k;
-    p.n_grouped = G * k;
+    const GroupK gk = make_group_k(c);
+    p.H = gk.K + (full_output(c) ? 1 : 0);
+    p.q_heads = gk.K + 1;  // q always has room for the shared head
+    p.n_grouped = gk.K;
+    for (int g = 0; g <= G; ++g) p.koff[g] = gk.koff[g];
     p.extra_group = c->shared_kv_group;
     p.ld_o = static_cast<int64_t>(slot_count(c)) * D;
     if (c->output_mode == GQE_OUTPUT_WEIGHTED_CONCAT) p.row_scale = at<float>(ws, l.pub.w);
@@ -230,13 +264,14 @@ template <typename T>
 int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool dense,
                 hipStream_t stream) {
   const Layout l = make_layout(c, dense);
-  const int G = c->n_groups, E = c->n_experts, k = c->top_k, D = c->head_dim;
+  const int G = c->n_groups, E = c->n_experts, D = c->head_dim;
   const int M = c->batch * c->seq_len;
   hipError_t e = hipSuccess;
   int K;
   if (!dense) {
     if (full_output(c)) {
-      e = launch_weighted_slot<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), M, G, k, D, stream);
+      e = launch_weighted_slot<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), M, total_k(c), D,
+                                  stream);
       if (e != hipSuccess) return GQE_ERR_HIP;
     }
     K = slot_count(c) * D;
@@ -343,6 +378,7 @@ int check_decode_cfg(const gqe_config* c) {
   if (st != GQE_OK) return st;
   if (c->batch > 0 && c->seq_len < 1) return GQE_ERR_INVALID_ARG;  // no room for the token
   if (c->d_model > kDecodeMaxDModel) return GQE_ERR_UNSUPPORTED;
+  if (c->group_top_k != nullptr) return GQE_ERR_UNSUPPORTED;  // uniform top_k only
   return GQE_OK;
 }
 
@@ -560,6 +596,7 @@ int backward_entry(const gqe_config* cfg, bool dense, const void* x, const void*
                    void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_cfg(cfg);
   if (st != GQE_OK || empty(cfg)) return st;
+  if (cfg->group_top_k != nullptr) return GQE_ERR_UNSUPPORTED;  // uniform top_k only
   if (!(aux_weight >= 0.f) || isinf(aux_weight)) return GQE_ERR_INVALID_ARG;
   const void* need[] = {x, Wq, Wk, Wv, Wo, dy, fws, dx, dWq, dWk, dWv, dWo, ws};
   for (const void* q : need)
@@ -632,13 +669,13 @@ int gqe_route(const gqe_config* cfg, const void* x, const void* Wr, void* worksp
     e = launch_router<bf16_t>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(Wr),
                               cfg->router_bias, at<int32_t>(workspace, l.pub.idx),
                               at<float>(workspace, l.pub.w), cfg->batch * cfg->seq_len,
-                              cfg->d_model, cfg->n_groups, cfg->n_experts, cfg->top_k, renorm,
+                              cfg->d_model, cfg->n_groups, cfg->n_experts, make_group_k(cfg), renorm,
                               stream);
   else
     e = launch_router<float>(static_cast<const float*>(x), static_cast<const float*>(Wr),
                              cfg->router_bias, at<int32_t>(workspace, l.pub.idx),
                              at<float>(workspace, l.pub.w), cfg->batch * cfg->seq_len,
-                             cfg->d_model, cfg->n_groups, cfg->n_experts, cfg->top_k, renorm,
+                             cfg->d_model, cfg->n_groups, cfg->n_experts, make_group_k(cfg), renorm,
                              stream);
   return hip_status(e);
 }
@@ -652,7 +689,7 @@ int gqe_dispatch(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStr
       at<int32_t>(workspace, l.pub.counts), at<int32_t>(workspace, l.pub.offsets),
       at<int32_t>(workspace, l.tile_off), at<int32_t>(workspace, l.pub.pos),
       at<int32_t>(workspace, l.pub.slot), cfg->batch, cfg->seq_len, cfg->n_groups,
-      cfg->n_experts, cfg->top_k, kGatherRows, stream));
+      cfg->n_experts, make_group_k(cfg), kGatherRows, stream));
 }
 
 int gqe_project(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,

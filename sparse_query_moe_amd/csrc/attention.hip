@@ -103,9 +103,13 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   const int bh = blockIdx.x % bh_count;
   const int qblk = nq - 1 - qi;  // heaviest first
   const int b = bh / p.H, head = bh % p.H;
-  const int g = head < p.n_grouped ? head / p.heads_per_group : p.extra_group;
+  int g = p.extra_group;
+  if (head < p.n_grouped) {  // the group whose slot-heads include this one
+    g = 0;
+    while (p.koff[g + 1] <= head) ++g;
+  }
 
-  const T* Q = static_cast<const T*>(p.q) + (static_cast<size_t>(b) * p.H + head) * L * D;
+  const T* Q = static_cast<const T*>(p.q) + (static_cast<size_t>(b) * p.q_heads + head) * L * D;
   const T* Kg = static_cast<const T*>(p.k) + (static_cast<size_t>(b) * p.G + g) * L * D;
   const T* Vg = static_cast<const T*>(p.vt) + (static_cast<size_t>(b) * p.G + g) * p.vt_tiles * D * 64;
 

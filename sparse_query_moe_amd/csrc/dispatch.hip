@@ -7,10 +7,11 @@
 // row-major order; pos = those t in ascending order; slot = the rank j at
 // which t chose e.
 //
-// Every token picks exactly k distinct experts in every group, so the lists
-// of one (b, g) always hold L*k entries together: they start at
-// (b*G + g)*L*k whatever the routing, and each (b, g) is dispatched
-// independently of the others.  The same holds for the tile map of the
+// Every token picks exactly k_g distinct experts in group g (k_g = k for the
+// pages' layer), so the lists of one (b, g) always hold L*k_g entries
+// together: they start at b*L*K + koff[g]*L (K = sum of k_g, koff the prefix
+// of k_g) whatever the routing, and each (b, g) is dispatched independently of
+// the others.  idx[b, t] holds group g's experts at koff[g] .. koff[g]+k_g-1.  The same holds for the tile map of the
 // gathered query projection, which is kept per (b, g):
 //   tile_off[(b*G+g)*(E+1) + e] = sum over e' < e of ceil(counts / tile_rows).
 //
@@ -39,10 +40,15 @@ __device__ __forceinline__ int chosen_rank(const int32_t* ids, int k, int e) {
 }
 
 __device__ __forceinline__ void load_ids(const int32_t* idx, int32_t* ids, int b, int t, int g,
-                                         int L, int G, int k) {
+                                         int L, const GroupK& gk) {
   const bool valid = t < L;
-  for (int j = 0; j < k; ++j)
-    ids[j] = valid ? idx[((static_cast<size_t>(b) * L + t) * G + g) * k + j] : -1;
+  const size_t row = (static_cast<size_t>(b) * L + t) * gk.K + gk.koff[g];
+  for (int j = 0; j < gk.kg[g]; ++j) ids[j] = valid ? idx[row + j] : -1;
+}
+
+// first entry of the lists of (b, g)
+__device__ __forceinline__ int list_base(const GroupK& gk, int b, int g, int L) {
+  return b * L * gk.K + gk.koff[g] * L;
 }
 
 // Exclusive scan of 64 values across a wave; returns the exclusive prefix and
@@ -61,7 +67,7 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
 // counts -> offsets and the per-(b, g) tile map for the lists of one (b, g);
 // run by all lanes of one wave (lane e < E owns list e)
 __device__ __forceinline__ void finish_lists(const int* cnt, int32_t* counts, int32_t* offsets,
-                                             int32_t* tile_off, int bg, int E, int L, int k,
+                                             int32_t* tile_off, int bg, int E, int base, int rows,
                                              int tile_rows, int lane, int n_lists) {
   const int v = lane < E ? cnt[lane] : 0;
   const int tv = (v + tile_rows - 1) / tile_rows;
@@ -70,12 +76,12 @@ __device__ __forceinline__ void finish_lists(const int* cnt, int32_t* counts, in
   const int tex = wave_excl_scan(tv, lane, &ttot);
   if (lane < E) {
     counts[bg * E + lane] = v;
-    offsets[bg * E + lane] = bg * L * k + ex;
+    offsets[bg * E + lane] = base + ex;
     tile_off[bg * (E + 1) + lane] = tex;
   }
   if (lane == 0) {
     tile_off[bg * (E + 1) + E] = ttot;
-    if (bg * E + E == n_lists) offsets[n_lists] = (bg + 1) * L * k;
+    if (bg * E + E == n_lists) offsets[n_lists] = base + rows;
   }
 }
 
@@ -89,22 +95,23 @@ __device__ __forceinline__ void finish_lists(const int* cnt, int32_t* counts, in
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_off, int32_t* __restrict__ pos, int32_t* __restrict__ slot, int L,
-    int G, int E, int k, int tile_rows, int n_lists) {
+    int G, int E, GroupK gk, int tile_rows, int n_lists) {
   __shared__ int wcnt[kSmallRounds][kSmallWaves][32];  // count, then first entry, per (r, w, e)
   __shared__ int total[32];
   const int bg = blockIdx.x, b = bg / G, g = bg % G;
+  const int k = gk.kg[g];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int rounds = (L + 64 * kSmallWaves - 1) / (64 * kSmallWaves);
 
-  // expert ids of this thread's tokens, packed 8 bits each (E <= 32, k <= 4 here)
+  // expert ids of this thread's tokens, packed 8 bits each (E <= 32, k_g <= 4 here)
   uint32_t packed[kSmallRounds];
 #pragma unroll
   for (int r = 0; r < kSmallRounds; ++r) {
     const int t = r * 64 * kSmallWaves + wave * 64 + lane;
     uint32_t v = 0xffffffffu;
     if (r < rounds && t < L) {
-      const int32_t* p = idx + ((static_cast<size_t>(b) * L + t) * G + g) * k;
+      const int32_t* p = idx + (static_cast<size_t>(b) * L + t) * gk.K + gk.koff[g];
       v = 0u;
       for (int j = 0; j < 4; ++j) v |= static_cast<uint32_t>(j < k ? p[j] : 0xff) << (8 * j);
     }
@@ -137,11 +144,13 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     total[e] = e < E ? tot : 0;
   }
   __syncthreads();
-  if (wave == 0) finish_lists(total, counts, offsets, tile_off, bg, E, L, k, tile_rows, lane, n_lists);
+  if (wave == 0)
+    finish_lists(total, counts, offsets, tile_off, bg, E, list_base(gk, b, g, L), L * k, tile_rows,
+                 lane, n_lists);
   if (threadIdx.x < 32) {
     const int e = threadIdx.x;
     if (e < E) {
-      int run = bg * L * k;
+      int run = list_base(gk, b, g, L);
       for (int f = 0; f < e; ++f) run += total[f];
       for (int r = 0; r < rounds; ++r)
         for (int w = 0; w < kSmallWaves; ++w) {
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx,
                                                              int32_t* __restrict__ chunk_counts,
-                                                             int L, int G, int E, int k,
+                                                             int L, int G, int E, GroupK gk,
                                                              int n_chunks) {
   __shared__ int cnt[4][64];
   const int c = blockIdx.x, b = blockIdx.y;
@@ -182,9 +191,9 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   const int t = c * kChunk + wave * 64 + lane;
   int32_t ids[32];
   for (int g = 0; g < G; ++g) {
-    load_ids(idx, ids, b, t, g, L, G, k);
+    load_ids(idx, ids, b, t, g, L, gk);
     for (int e = 0; e < E; ++e) {
-      const uint64_t m = __ballot(chosen_rank(ids, k, e) >= 0);
+      const uint64_t m = __ballot(chosen_rank(ids, gk.kg[g], e) >= 0);
       if (lane == 0) cnt[wave][g * E + e] = popc64(m);
     }
   }
@@ -200,7 +209,7 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
 // chunk bases in place; counts, offsets and the tile map come out on the way
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     int32_t* __restrict__ chunk_counts, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int L, int G, int E, int k,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int L, int G, int E, GroupK gk,
     int n_chunks, int tile_rows, int n_lists) {
   __shared__ int total[32];
   __shared__ int base[32];
@@ -223,9 +232,11 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     if (lane == 0) total[e] = runv;
   }
   __syncthreads();
-  if (wave == 0) finish_lists(total, counts, offsets, tile_off, bg, E, L, k, tile_rows, lane, n_lists);
+  if (wave == 0)
+    finish_lists(total, counts, offsets, tile_off, bg, E, list_base(gk, b, g, L), L * gk.kg[g],
+                 tile_rows, lane, n_lists);
   if (threadIdx.x < 32) {
-    int s = bg * L * k;
+    int s = list_base(gk, b, g, L);
     for (int e = 0; e < static_cast<int>(threadIdx.x) && e < E; ++e) s += total[e];
     base[threadIdx.x] = s;
   }
@@ -239,7 +250,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ chunk_base,
-    int32_t* __restrict__ pos, int32_t* __restrict__ slot, int L, int G, int E, int k,
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot, int L, int G, int E, GroupK gk,
     int n_chunks) {
   __shared__ int cnt[4][64];
   const int c = blockIdx.x, b = blockIdx.y;
@@ -249,17 +260,17 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t ids[32];
   for (int g = 0; g < G; ++g) {
-    load_ids(idx, ids, b, t, g, L, G, k);
+    load_ids(idx, ids, b, t, g, L, gk);
     for (int e = 0; e < E; ++e) {
-      const uint64_t m = __ballot(chosen_rank(ids, k, e) >= 0);
+      const uint64_t m = __ballot(chosen_rank(ids, gk.kg[g], e) >= 0);
       if (lane == 0) cnt[wave][g * E + e] = popc64(m);
     }
   }
   __syncthreads();
   for (int g = 0; g < G; ++g) {
-    load_ids(idx, ids, b, t, g, L, G, k);
+    load_ids(idx, ids, b, t, g, L, gk);
     for (int e = 0; e < E; ++e) {
-      const int r = chosen_rank(ids, k, e);
+      const int r = chosen_rank(ids, gk.kg[g], e);
       const uint64_t m = __ballot(r >= 0);
       if (r >= 0) {
         int wbase = 0;
@@ -279,26 +290,26 @@ int dispatch_chunks(int L) { return (L + kChunk - 1) / kChunk; }
 
 hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int32_t* pos, int32_t* slot,
-                           int B, int L, int G, int E, int k, int tile_rows,
+                           int B, int L, int G, int E, const GroupK& gk, int tile_rows,
                            hipStream_t stream) {
   const int n_lists = B * G * E;
-  if (L <= kSmallRounds * 64 * kSmallWaves && k <= 4) {
+  if (L <= kSmallRounds * 64 * kSmallWaves && gk.kmax <= 4) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(B * G), dim3(64 * kSmallWaves), 0, stream, idx,
-                       counts, offsets, tile_off, pos, slot, L, G, E, k, tile_rows, n_lists);
+                       counts, offsets, tile_off, pos, slot, L, G, E, gk, tile_rows, n_lists);
     return hipGetLastError();
   }
   const int n_chunks = dispatch_chunks(L);
   const dim3 grid(n_chunks, B);
   hipLaunchKernelGGL(dispatch_count_kernel, grid, dim3(256), 0, stream, idx, chunk_counts, L, G,
-                     E, k, n_chunks);
+                     E, gk, n_chunks);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(B * G), dim3(1024), 0, stream, chunk_counts,
-                     counts, offsets, tile_off, L, G, E, k, n_chunks, tile_rows, n_lists);
+                     counts, offsets, tile_off, L, G, E, gk, n_chunks, tile_rows, n_lists);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, grid, dim3(256), 0, stream, idx, chunk_counts, pos,
-                     slot, L, G, E, k, n_chunks);
+                     slot, L, G, E, gk, n_chunks);
   return hipGetLastError();
 }
 

@@ -322,7 +322,8 @@ struct GatherArgs {
   const int32_t* pos;
   const int32_t* slot;
   const int32_t* tile_off;
-  int n_lists, L, d, G, E, k, D, H;
+  int n_lists, L, d, G, E, D, H;
+  int koff[kMaxGroups + 1];  // group g's slot-heads start at koff[g]
 };
 
 template <typename T, class S>
@@ -351,7 +352,7 @@ struct GatherProb {
     return static_cast<const T*>(a.wq) +
            (static_cast<size_t>(g * a.E + e) * a.D + n) * static_cast<size_t>(a.d);
   }
-  // each routed row lands at (slot-head g*k + slot, position pos): 8 dims per chunk
+  // each routed row lands at (slot-head koff[g] + slot, position pos): 8 dims per chunk
   __device__ __forceinline__ void write_tile(const T* ct) const {
     constexpr int CW = S::BN / 8;
     for (int c = threadIdx.x; c < S::BM * CW; c += 256) {
@@ -359,7 +360,7 @@ struct GatherProb {
       if (m0 + r >= cnt || 8 * c8 >= a.D) continue;
       const int entry = base + m0 + r;
       const int t = a.pos[entry], j = a.slot[entry];
-      T* dst = static_cast<T*>(a.q) + ((static_cast<size_t>(b) * a.H + g * a.k + j) * a.L + t) * a.D + 8 * c8;
+      T* dst = static_cast<T*>(a.q) + ((static_cast<size_t>(b) * a.H + a.koff[g] + j) * a.L + t) * a.D + 8 * c8;
       copy8(dst, ct + r * S::LDC + 8 * c8);
     }
   }
@@ -468,13 +469,13 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(NtArgs args) {
 template <typename T>
 __global__ __launch_bounds__(256) void weighted_slot_kernel(T* __restrict__ s,
                                                             const float* __restrict__ w,
-                                                            int n_tokens, int G, int k, int D) {
+                                                            int n_tokens, int K, int D) {
   const int per_tok = D / 4;
   const size_t gid = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= static_cast<size_t>(n_tokens) * per_tok) return;
   const int t = static_cast<int>(gid / per_tok);
   const int c = static_cast<int>(gid % per_tok) * 4;
-  const int slots = G * k;
+  const int slots = K;
   T* row = s + static_cast<size_t>(t) * (slots + 2) * D;
   const float* wt = w + static_cast<size_t>(t) * slots;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
@@ -565,8 +566,8 @@ static hipError_t launch_gather_q_d(const GatherArgs& a, int tiles_per_bg, int n
 template <typename T>
 hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
                            const int32_t* offsets, const int32_t* pos, const int32_t* slot,
-                           const int32_t* tile_off, int B, int L, int d, int G, int E, int k,
-                           int D, int tiles_per_bg, hipStream_t stream) {
+                           const int32_t* tile_off, int B, int L, int d, int G, int E,
+                           const GroupK& gk, int D, int tiles_per_bg, hipStream_t stream) {
   GatherArgs a;
   a.x = x;
   a.wq = wq;
@@ -581,9 +582,9 @@ hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
   a.d = d;
   a.G = G;
   a.E = E;
-  a.k = k;
+  for (int g = 0; g <= G; ++g) a.koff[g] = gk.koff[g];
   a.D = D;
-  a.H = G * k + 1;
+  a.H = gk.K + 1;
   if (tiles_per_bg == 0 || B * G == 0) return hipSuccess;
   switch (D) {
     case 32: return launch_gather_q_d<T, 32>(a, tiles_per_bg, B * G, stream);
@@ -625,13 +626,13 @@ hipError_t launch_nt_gemm(const NtArgs& a, hipStream_t stream) {
 }
 
 template <typename T>
-hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int G, int k, int D,
+hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D,
                                 hipStream_t stream) {
   const size_t n = static_cast<size_t>(n_tokens) * (D / 4);
   if (n == 0) return hipSuccess;
   const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
   hipLaunchKernelGGL(weighted_slot_kernel<T>, dim3(blocks), dim3(256), 0, stream, s, w, n_tokens,
-                     G, k, D);
+                     K, D);
   return hipGetLastError();
 }
 
@@ -640,9 +641,9 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int G, int k
                                            int, hipStream_t);                                    \
   template hipError_t launch_gather_q<T>(const T*, const T*, T*, const int32_t*, const int32_t*, \
                                          const int32_t*, const int32_t*, const int32_t*, int, int, \
-                                         int, int, int, int, int, int, hipStream_t);             \
+                                         int, int, int, const GroupK&, int, int, hipStream_t);    \
   template hipError_t launch_out_proj<T>(const T*, const T*, T*, int, int, int, hipStream_t);    \
-  template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, int, hipStream_t); \
+  template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, hipStream_t);      \
   template hipError_t launch_nt_gemm<T>(const NtArgs&, hipStream_t);
 GQE_INST(bf16_t)
 GQE_INST(float)

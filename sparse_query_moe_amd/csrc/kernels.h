@@ -12,19 +12,33 @@ typedef uint16_t bf16_t;
 // rows of one gathered query-projection tile (the dispatch tile map unit)
 constexpr int kGatherRows = 128;
 
+// Experts selected per group: group g owns hard slots koff[g] .. koff[g] +
+// kg[g] - 1 of every token, in rank order; K = koff[G] hard slots in all.  A
+// uniform top-k is kg[g] = k, koff[g] = g*k (the pages' layer); a per-group k
+// is the non-uniform variant the pages list as future work (pptc.cn,
+// section 6).
+constexpr int kMaxGroups = 64;
+struct GroupK {
+  int K;
+  int kmax;
+  int kg[kMaxGroups];
+  int koff[kMaxGroups + 1];
+};
+
 // ---- K1 router ---------------------------------------------------------------
 template <typename T>
 // renorm: w = p renormalized over the k selected (the GQE layer); otherwise
 // w = p itself, the in-group softmax probability of each selected expert
 hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* idx, float* w,
-                         int n_tokens, int d, int G, int E, int k, bool renorm,
+                         int n_tokens, int d, int G, int E, const GroupK& gk, bool renorm,
                          hipStream_t stream);
 
 // ---- K2 dispatch -------------------------------------------------------------
 int dispatch_chunks(int L);
 hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int32_t* pos, int32_t* slot,
-                           int B, int L, int G, int E, int k, int tile_rows, hipStream_t stream);
+                           int B, int L, int G, int E, const GroupK& gk, int tile_rows,
+                           hipStream_t stream);
 
 // ---- K3 projections ----------------------------------------------------------
 // One output segment of a dense projection: columns [n_begin, n_begin + n)
@@ -49,20 +63,21 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_
 template <typename T>
 hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
                            const int32_t* offsets, const int32_t* pos, const int32_t* slot,
-                           const int32_t* tile_off, int B, int L, int d, int G, int E, int k,
-                           int D, int tiles_per_bg, hipStream_t stream);
+                           const int32_t* tile_off, int B, int L, int d, int G, int E,
+                           const GroupK& gk, int D, int tiles_per_bg, hipStream_t stream);
 
 // ---- K4 attention ------------------------------------------------------------
 struct AttnParams {
-  const void* q;       // [B, H, L, D]
+  const void* q;       // [B, q_heads, L, D]: heads 0 .. H-1 attend
   const void* k;       // [B, G, L, D]
   const void* vt;      // [B, G, vt_tiles, D, 64], keys permuted in 16-key groups
   void* o;             // o[(b*L + t)*ld_o + head*D + d]
   int64_t vt_tiles;
   int64_t ld_o;
   int B, H, G, L;
-  int heads_per_group;  // heads h < n_grouped read group h / heads_per_group
-  int n_grouped;
+  int q_heads;          // heads per sequence in q (H, or one more when the shared head is absent)
+  int n_grouped;        // heads h < n_grouped read group g with koff[g] <= h < koff[g + 1]
+  int koff[kMaxGroups + 1];
   int extra_group;      // heads h >= n_grouped read this group
   float scale_log2;     // softmax scale * log2(e)
   // optional per-row factor of the grouped heads' outputs: o[b, t, h] is
@@ -76,8 +91,9 @@ template <typename T>
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream);
 
 // ---- K5 output -----------------------------------------------------------------
+// s[t] holds K hard slots, the shared slot and the weighted slot; w is [T, K]
 template <typename T>
-hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int G, int k, int D,
+hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D,
                                 hipStream_t stream);
 template <typename T>
 hipError_t launch_out_proj(const T* a, const T* wo, T* out, int M, int N, int K,

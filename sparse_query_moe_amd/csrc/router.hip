@@ -41,7 +41,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int n_tokens, int d, int G, int E,
-    int k, int renorm) {
+    GroupK gk, int renorm) {
   __shared__ double part[4][kTok][17];
   __shared__ double logit[kTok][65];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -105,8 +105,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     const int tt = task / G, g = task % G;
     const int gt = t0 + tt;
     if (gt >= n_tokens) continue;
-    select_group(&logit[tt][g * E], E, k, renorm, idx_out, w_out,
-                 (static_cast<size_t>(gt) * G + g) * k);
+    select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out, w_out,
+                 static_cast<size_t>(gt) * gk.K + gk.koff[g]);
   }
 }
 
@@ -114,18 +114,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 
 template <typename T>
 hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* idx, float* w,
-                         int n_tokens, int d, int G, int E, int k, bool renorm,
+                         int n_tokens, int d, int G, int E, const GroupK& gk, bool renorm,
                          hipStream_t stream) {
   const int blocks = (n_tokens + kTok - 1) / kTok;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(router_topk_kernel<T>, dim3(blocks), dim3(256), 0, stream, x, wr, bias, idx,
-                     w, n_tokens, d, G, E, k, renorm ? 1 : 0);
+                     w, n_tokens, d, G, E, gk, renorm ? 1 : 0);
   return hipGetLastError();
 }
 
 template hipError_t launch_router<bf16_t>(const bf16_t*, const bf16_t*, const float*, int32_t*,
-                                          float*, int, int, int, int, int, bool, hipStream_t);
+                                          float*, int, int, int, int, const GroupK&, bool,
+                                          hipStream_t);
 template hipError_t launch_router<float>(const float*, const float*, const float*, int32_t*,
-                                         float*, int, int, int, int, int, bool, hipStream_t);
+                                         float*, int, int, int, int, const GroupK&, bool,
+                                         hipStream_t);
 
 }  // namespace gqe

@@ -41,6 +41,7 @@ class GqeConfig(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("shared_kv_group", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("router_bias", ctypes.c_void_p), ("output_mode", ctypes.c_int32),
+        ("group_top_k", ctypes.c_void_p),
     ]
 
     @property
@@ -110,15 +111,30 @@ OUTPUT_MODES = {"full": 0, "hard": 1, "weighted_concat": 2}  # gqe_output_mode
 
 def make_config(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim, dtype="bf16",
                 shared_kv_group=0, softmax_scale=0.0, router_bias=None,
-                output_mode="full") -> GqeConfig:
+                output_mode="full", group_top_k=None) -> GqeConfig:
     """Fill a gqe_config.  `router_bias` is a float32 device tensor [G*E] or None;
     the caller keeps it alive while the config is in use.  `output_mode` is
-    "full", "hard" or "weighted_concat" (see gqe_output_mode)."""
+    "full", "hard" or "weighted_concat" (see gqe_output_mode).  `group_top_k`
+    is a list of G per-group expert counts or None (top_k in every group)."""
     dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}.get(dtype, dtype)
-    return GqeConfig(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim,
-                     shared_kv_group, dt, float(softmax_scale),
-                     None if router_bias is None else router_bias.data_ptr(),
-                     OUTPUT_MODES.get(output_mode, output_mode))
+    gk = None
+    if group_top_k is not None:
+        gk = (ctypes.c_int32 * len(group_top_k))(*[int(v) for v in group_top_k])
+    cfg = GqeConfig(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim,
+                    shared_kv_group, dt, float(softmax_scale),
+                    None if router_bias is None else router_bias.data_ptr(),
+                    OUTPUT_MODES.get(output_mode, output_mode),
+                    None if gk is None else ctypes.cast(gk, ctypes.c_void_p))
+    cfg._group_top_k = gk  # kept alive with the config
+    return cfg
+
+
+def total_k(cfg: GqeConfig) -> int:
+    """Hard slots per token: the sum of the per-group expert counts."""
+    if cfg.group_top_k:
+        arr = ctypes.cast(cfg.group_top_k, ctypes.POINTER(ctypes.c_int32))
+        return sum(arr[g] for g in range(cfg.n_groups))
+    return cfg.top_k * cfg.n_groups
 
 
 def _ptr(t):
@@ -281,18 +297,21 @@ def workspace_views(cfg: GqeConfig, ws: torch.Tensor, dense: bool = False) -> di
 
     out = {}
     if not dense:
-        rows = B * L * G * k
-        out["idx"] = view(lay.idx, (B, L, G, k), torch.int32, 4)
-        out["w"] = view(lay.w, (B, L, G, k), torch.float32, 4)
+        K = total_k(cfg)
+        rows = B * L * K
+        # [B, L, G, k] for a uniform k, [B, L, K] for per-group counts
+        shp = (B, L, G, k) if not cfg.group_top_k else (B, L, K)
+        out["idx"] = view(lay.idx, shp, torch.int32, 4)
+        out["w"] = view(lay.w, shp, torch.float32, 4)
         out["counts"] = view(lay.counts, (B, G, E), torch.int32, 4)
         out["offsets"] = view(lay.offsets, (B * G * E + 1,), torch.int32, 4)
         out["pos"] = view(lay.pos, (rows,), torch.int32, 4)
         out["slot"] = view(lay.slot, (rows,), torch.int32, 4)
-        out["q"] = view(lay.q, (B, G * k + 1, L, D), dt, es)
+        out["q"] = view(lay.q, (B, K + 1, L, D), dt, es)
         full = cfg.output_mode == OUTPUT_MODES["full"]
-        slots = G * k + (2 if full else 0)
+        slots = K + (2 if full else 0)
         out["s"] = view(lay.s, (B, L, slots * D), dt, es)
-        out["lse"] = view(lay.lse, (B, G * k + (1 if full else 0), L), torch.float32, 4)
+        out["lse"] = view(lay.lse, (B, K + (1 if full else 0), L), torch.float32, 4)
     else:
         out["q"] = view(lay.q, (B, G * E, L, D), dt, es)
         out["s"] = view(lay.s, (B, L, G * E * D), dt, es)

@@ -302,13 +302,15 @@ def test_determinism(gqe):
                           vt_decode(v2["vt"].view(torch.int16).cpu().numpy(), L))
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "l2k"])
+@pytest.mark.parametrize("name,L,B", [("tiny_fp32", 0, 0), ("l2k", 0, 0), ("l2k", 600, 2)])
 @pytest.mark.parametrize("mode", ["hard", "weighted_concat"])
-def test_ablation_output_modes(gqe, name, mode):
+def test_ablation_output_modes(gqe, name, L, B, mode):
     """The two output constructions of the ablation: the k*G hard slots only,
     or each scaled by its in-group probability; no shared head, W_O of k*G*d_h
-    inputs (its first k*G*d_h columns here)."""
-    wl, I = inputs(name)
+    inputs (its first k*G*d_h columns here).  Two sequences check that the
+    attention steps through the query buffer, which keeps room for the shared
+    head, by its own head count."""
+    wl, I = inputs(name, L, B)
     log(f"[output mode] {name} {mode}")
     kG, D = wl.top_k * wl.n_groups, wl.head_dim
     J = dict(I)
