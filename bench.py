@@ -335,6 +335,61 @@ def measure_training(wl, gqe, torch, steps, warmup):
             "backward_speedup_vs_gqa": round(b_gqa / b_gqe, 4)}
 
 
+def measure_sweep(gqe, torch, steps, warmup, batch=4, seq_len=8192):
+    """The pages leave two knobs unexplored (pptc.cn section 6): the expert
+    pool E per group and a per-group k.  GQE against dense GQA (all G*E heads)
+    at B4 x L8192 of the 250M layer for E = 2, 4, 8, 16 with half of each
+    group's experts active, and for two per-group splits of k = 8 slots."""
+    base = W.WORKLOADS["b4_l8k"].with_(batch=batch, seq_len=seq_len)
+    configs = [(E, E // 2, None) for E in (2, 4, 8, 16)] + [(4, 2, [1, 2, 3, 2]),
+                                                              (4, 2, [4, 2, 1, 1])]
+    out = []
+    for E, k, ks in configs:
+        wl = base.with_(n_experts=E, top_k=k)
+        I = W.make_inputs(wl, with_gqa=True)
+        K = sum(ks) if ks else k * wl.n_groups
+        if ks:
+            rng = np.random.Generator(np.random.PCG64(22))
+            I["wo"] = W._draw(rng, (wl.d_model, (K + 2) * wl.head_dim), wl.w_std, wl.dtype)
+
+        def dev(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                    torch.bfloat16).to("cuda")
+            return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+        d = {n: dev(v) for n, v in I.items()}
+        cfg = gqe.make_config(wl.batch, wl.seq_len, wl.d_model, wl.n_groups, E, k, wl.head_dim,
+                              dtype=wl.dtype, router_bias=d["br"], group_top_k=ks)
+        ws, ws_d = gqe.alloc_workspace(cfg), gqe.alloc_workspace(cfg, dense=True)
+        y = torch.empty((wl.batch, wl.seq_len, wl.d_model), dtype=cfg.torch_dtype, device="cuda")
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / steps
+
+        t_gqe = timed(lambda: gqe.gqe_forward(cfg, d["x"], d["wq"], d["wk"], d["wv"], d["wr"],
+                                              d["wo"], y, ws))
+        t_gqa = timed(lambda: gqe.gqa_forward(cfg, d["x"], d["wq_dense"], d["wk"], d["wv"],
+                                              d["wo_dense"], y, ws_d))
+        out.append({"n_experts": E, "top_k": k if ks is None else None, "group_top_k": ks,
+                    "active_query_heads": f"{K + 1}/{wl.n_groups * E}",
+                    "gqe_ms": round(t_gqe, 5), "gqa_ms": round(t_gqa, 5),
+                    "speedup_vs_gqa": round(t_gqa / t_gqe, 4)})
+        log(f"[bench]   sweep {out[-1]}")
+        del ws, ws_d, d, y
+        torch.cuda.empty_cache()
+    return {"workload": base.description, "points": out}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.txt")
 KERNEL_SOURCES = ("attention.hip", "device_common.h", "kernels.h")
 
@@ -416,6 +471,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the expert-pool and per-group-k sweep")
     ap.add_argument("--training", default="l2k,b4_l8k",
                     help="workloads whose training step (forward + backward) is timed "
                          "(comma list, '' = none)")
@@ -498,6 +555,9 @@ def main():
         train.append(t)
     if train:
         line["training"] = train
+    if not args.no_sweep:
+        log("[bench] expert-pool and per-group-k sweep ...")
+        line["sweep"] = measure_sweep(gqe, torch, min(args.steps, 20), 3)
     if not args.no_decode:
         log("[bench] decode step ...")
         line["decode"] = measure_decode(gqe, torch, args.steps, args.warmup)
