@@ -229,13 +229,15 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
           for (int i = 0; i < 16; ++i)
             if (j0 + 32 * kb + acc_row(i, lane) > qrow[qb]) s[qb][kb][i] = -INFINITY;
       }
+      // the half-row maximum decides (any lane over the threshold), so the
+      // exchange with lane l ^ 32 is only paid when the maximum is raised
       float v = s[qb][0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) v = fmaxf(v, s[qb][kb][i]);
-      const float mx = fmaxf(v, __shfl_xor(v, 32, 64));
-      if (__any(mx > kRescaleThreshold)) {  // raise the running maximum (wave-uniform branch)
+      if (__any(v > kRescaleThreshold)) {  // raise the running maximum (wave-uniform branch)
+        const float mx = fmaxf(v, __shfl_xor(v, 32, 64));  // both halves of a row agree
         const float sh = fmaxf(mx, 0.f);
         const float alpha = __builtin_amdgcn_exp2f(-sh);
         m_run[qb] += sh;

@@ -90,14 +90,15 @@ __device__ __forceinline__ void finish_lists(const int* cnt, int32_t* counts, in
 // t = r*1024 + 64*w + lane for rounds r < kSmallRounds; all their expert ids
 // are loaded at once.  Pass 1 ballots every (round, wave, expert) count into
 // LDS; one prefix over (expert, round, wave) gives every wave its list bases;
-// pass 2 scatters.  Two barriers in all.
+// pass 2 scatters.  Three barriers in all.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_off, int32_t* __restrict__ pos, int32_t* __restrict__ slot, int L,
     int G, int E, GroupK gk, int tile_rows, int n_lists) {
-  __shared__ int wcnt[kSmallRounds][kSmallWaves][32];  // count, then first entry, per (r, w, e)
+  __shared__ int wcnt[kSmallRounds][kSmallWaves][32];  // count, then offset in the list, per (r, w, e)
   __shared__ int total[32];
+  __shared__ int start[32];
   const int bg = blockIdx.x, b = bg / G, g = bg % G;
   const int k = gk.kg[g];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -134,31 +135,32 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     }
   }
   __syncthreads();
-  // prefix in (expert, round, wave) order: list e first, tokens ascending
-  if (threadIdx.x < 32) {
-    const int e = threadIdx.x;
-    int tot = 0;
-    if (e < E)
-      for (int r = 0; r < rounds; ++r)
-        for (int w = 0; w < kSmallWaves; ++w) tot += wcnt[r][w][e];
-    total[e] = e < E ? tot : 0;
+  // prefix of every expert's counts in (round, wave) order, i.e. tokens
+  // ascending: wave e scans list e, each lane owning two consecutive
+  // (round, wave) entries; the entries become offsets inside the list
+  static_assert(kSmallRounds * kSmallWaves == 128, "two (round, wave) entries per lane");
+  for (int e = wave; e < E; e += kSmallWaves) {
+    const int n = rounds * kSmallWaves;
+    const int i0 = 2 * lane, i1 = 2 * lane + 1;
+    int* c0p = &wcnt[i0 / kSmallWaves][i0 % kSmallWaves][e];
+    int* c1p = &wcnt[i1 / kSmallWaves][i1 % kSmallWaves][e];
+    const int c0 = i0 < n ? *c0p : 0;
+    const int c1 = i1 < n ? *c1p : 0;
+    int tot;
+    const int ex = wave_excl_scan(c0 + c1, lane, &tot);
+    if (i0 < n) *c0p = ex;
+    if (i1 < n) *c1p = ex + c0;
+    if (lane == 0) total[e] = tot;
   }
   __syncthreads();
   if (wave == 0)
     finish_lists(total, counts, offsets, tile_off, bg, E, list_base(gk, b, g, L), L * k, tile_rows,
                  lane, n_lists);
-  if (threadIdx.x < 32) {
+  if (threadIdx.x < 32) {  // first entry of every list
     const int e = threadIdx.x;
-    if (e < E) {
-      int run = list_base(gk, b, g, L);
-      for (int f = 0; f < e; ++f) run += total[f];
-      for (int r = 0; r < rounds; ++r)
-        for (int w = 0; w < kSmallWaves; ++w) {
-          const int c = wcnt[r][w][e];
-          wcnt[r][w][e] = run;
-          run += c;
-        }
-    }
+    int run = list_base(gk, b, g, L);
+    for (int f = 0; f < e && f < E; ++f) run += total[f];
+    start[e] = run;
   }
   __syncthreads();
   // pass 2: scatter
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
       const int rk = rank_of(packed[r], e);
       const uint64_t m = __ballot(rk >= 0);
       if (rk >= 0) {
-        const int entry = wcnt[r][wave][e] + __popcll(m & below);
+        const int entry = start[e] + wcnt[r][wave][e] + __popcll(m & below);
         pos[entry] = t;
         slot[entry] = rk;
       }

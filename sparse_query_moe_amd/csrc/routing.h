@@ -35,7 +35,7 @@ __device__ __forceinline__ void widen8(const uint4 (&r)[U4Count<T>::n], double (
 // largest, best first (rank of e = experts with a larger logit, or an equal
 // one and a lower index), and their weights exp(r_e - max) / z with z summed
 // over the selected k (renormalized) or over all E (the softmax itself).
-inline __device__ __forceinline__ void select_group(const double* r, int E, int k, int renorm,
+__device__ __forceinline__ void select_group(const double* r, int E, int k, int renorm,
                                              int32_t* idx_out, float* w_out, size_t o) {
   double rmax = r[0];
   for (int e = 1; e < E; ++e) rmax = fmax(rmax, r[e]);
