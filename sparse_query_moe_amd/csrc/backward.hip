@@ -547,7 +547,7 @@ __global__ __launch_bounds__(64 * DkvWaves<D>::n, 1) void attn_bwd_dkdv_lds_kern
   static_assert(NRUNS % NW == 0, "whole runs per wave");
   constexpr int DMA_OPS = NRUNS / NW;  // per wave per stage
   extern __shared__ __align__(16) char smem[];
-  __shared__ float stat[NW][2][64];
+  __shared__ __align__(16) float stat[NW][2][64];
   __shared__ int rows[NW][32], cols[NW][32];
   const int lane = threadIdx.x & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -647,15 +647,26 @@ __global__ __launch_bounds__(64 * DkvWaves<D>::n, 1) void attn_bwd_dkdv_lds_kern
         mma32(sc, LdsFrag<T, S::ROWB>::get(sQ, 32 * m2 + (lane & 31), 16 * ks + 8 * half), kf[ks]);
         mma32(dp, LdsFrag<T, S::ROWB>::get(sdO, 32 * m2 + (lane & 31), 16 * ks + 8 * half), vf[ks]);
       }
+      // the rows' statistics, four consecutive rows per read; P is formed for
+      // every entry and the masked ones are selected away afterwards, so the
+      // loop has no branches (a masked entry's exp2 may overflow: it is dropped)
+      float lsr[16], dsr[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 32 * m2 + 8 * q4 + 4 * half;
+        const float4 l4 = *reinterpret_cast<const float4*>(&stat[wave][0][r0]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&stat[wave][1][r0]);
+        lsr[4 * q4 + 0] = l4.x; lsr[4 * q4 + 1] = l4.y; lsr[4 * q4 + 2] = l4.z; lsr[4 * q4 + 3] = l4.w;
+        dsr[4 * q4 + 0] = d4.x; dsr[4 * q4 + 1] = d4.y; dsr[4 * q4 + 2] = d4.z; dsr[4 * q4 + 3] = d4.w;
+      }
       f32x16 P, dS;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = 32 * m2 + acc_row(i, lane);
-        const int qq = q0 + r;
+        const int qq = q0 + 32 * m2 + acc_row(i, lane);
         const bool keep = qq < L && my_key <= qq;
-        const float pv = keep ? __builtin_amdgcn_exp2f(sc[i] - stat[wave][0][r]) : 0.f;
-        P[i] = pv;
-        dS[i] = pv * (dp[i] - stat[wave][1][r]);
+        const float pv = __builtin_amdgcn_exp2f(sc[i] - lsr[i]);
+        P[i] = keep ? pv : 0.f;
+        dS[i] = P[i] * (dp[i] - dsr[i]);
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
