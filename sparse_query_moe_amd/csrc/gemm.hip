@@ -527,11 +527,51 @@ int cu_count() {
 }
 inline bool deep_ring(long long blocks) { return blocks <= cu_count(); }
 
+// Tile shapes of an M x N output: 128 x 128 tiles while they fill the chip;
+// below one tile per compute unit, 64-row tiles (twice the blocks; every
+// output element still takes the same K steps in the same order, so the
+// results are the same).  A launch that fits the chip at once gets the
+// four-stage LDS ring.
+enum class Tiles { k128, k128Deep, k64, k64Deep };
+inline Tiles choose_tiles(int M, int N) {
+  const long long b128 = static_cast<long long>((N + 127) / 128) * ((M + 127) / 128);
+  if (b128 < cu_count()) {
+    const long long b64 = static_cast<long long>((N + 127) / 128) * ((M + 63) / 64);
+    return deep_ring(b64) ? Tiles::k64Deep : Tiles::k64;
+  }
+  return deep_ring(b128) ? Tiles::k128Deep : Tiles::k128;
+}
+inline dim3 tile_grid(Tiles t, int M, int N) {
+  const int bm = (t == Tiles::k64 || t == Tiles::k64Deep) ? 64 : 128;
+  return dim3((N + 127) / 128, (M + bm - 1) / bm);
+}
+#define GQE_LAUNCH_TILED(KERNEL, T, M, N, stream, args)                                        \
+  do {                                                                                       \
+    const Tiles t_ = choose_tiles(M, N);                                                     \
+    const dim3 g_ = tile_grid(t_, M, N);                                                     \
+    switch (t_) {                                                                            \
+      case Tiles::k64: {                                                                     \
+        typedef GemmShape<T, 64, 128, 2, 2> S_;                                              \
+        return launch_gemm<S_>(KERNEL<T, S_>, g_, stream, args);                             \
+      }                                                                                      \
+      case Tiles::k64Deep: {                                                                 \
+        typedef GemmShape<T, 64, 128, 2, 2, 4> S_;                                           \
+        return launch_gemm<S_>(KERNEL<T, S_>, g_, stream, args);                             \
+      }                                                                                      \
+      case Tiles::k128Deep: {                                                                \
+        typedef GemmShape<T, 128, 128, 2, 2, 4> S_;                                          \
+        return launch_gemm<S_>(KERNEL<T, S_>, g_, stream, args);                             \
+      }                                                                                      \
+      default: {                                                                             \
+        typedef GemmShape<T, 128, 128, 2, 2> S_;                                             \
+        return launch_gemm<S_>(KERNEL<T, S_>, g_, stream, args);                             \
+      }                                                                                      \
+    }                                                                                        \
+  } while (0)
+
 template <typename T>
 hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
                              const ProjSeg* segs, int nseg, hipStream_t stream) {
-  typedef GemmShape<T, 128, 128, 2, 2> S;
-  typedef GemmShape<T, 128, 128, 2, 2, 4> S4;
   DenseArgs a;
   a.x = x;
   a.M = M;
@@ -547,10 +587,7 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_
   }
   a.N = N;
   if (M == 0 || N == 0) return hipSuccess;
-  const dim3 grid((N + S::BN - 1) / S::BN, (M + S::BM - 1) / S::BM);
-  if (deep_ring(static_cast<long long>(grid.x) * grid.y))
-    return launch_gemm<S4>(dense_proj_kernel<T, S4>, grid, stream, a);
-  return launch_gemm<S>(dense_proj_kernel<T, S>, grid, stream, a);
+  GQE_LAUNCH_TILED(dense_proj_kernel, T, M, N, stream, a);
 }
 
 template <typename T, int D>
@@ -597,8 +634,6 @@ hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
 template <typename T>
 hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream) {
-  typedef GemmShape<T, 128, 128, 2, 2> S;
-  typedef GemmShape<T, 128, 128, 2, 2, 4> S4;
   OutArgs a;
   a.a = a_;
   a.w = wo;
@@ -607,22 +642,15 @@ hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K
   a.N = N;
   a.K = K;
   if (M == 0 || N == 0) return hipSuccess;
-  const dim3 grid((N + S::BN - 1) / S::BN, (M + S::BM - 1) / S::BM);
-  if (deep_ring(static_cast<long long>(grid.x) * grid.y))
-    return launch_gemm<S4>(out_proj_kernel<T, S4>, grid, stream, a);
-  return launch_gemm<S>(out_proj_kernel<T, S>, grid, stream, a);
+  GQE_LAUNCH_TILED(out_proj_kernel, T, M, N, stream, a);
 }
 
 template <typename T>
 hipError_t launch_nt_gemm(const NtArgs& a, hipStream_t stream) {
   typedef GemmShape<T, 128, 128, 2, 2> S;
-  typedef GemmShape<T, 128, 128, 2, 2, 4> S4;
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.K % S::BKE != 0 || a.nseg < 1 || a.nseg > 4) return hipErrorInvalidValue;
-  const dim3 grid((a.N + S::BN - 1) / S::BN, (a.M + S::BM - 1) / S::BM);
-  if (deep_ring(static_cast<long long>(grid.x) * grid.y))
-    return launch_gemm<S4>(nt_gemm_kernel<T, S4>, grid, stream, a);
-  return launch_gemm<S>(nt_gemm_kernel<T, S>, grid, stream, a);
+  GQE_LAUNCH_TILED(nt_gemm_kernel, T, a.M, a.N, stream, a);
 }
 
 template <typename T>
