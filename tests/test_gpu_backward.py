@@ -166,9 +166,13 @@ def test_gqa_backward(gqe, name):
     (333, 2, 2, 3, 2, 32, "fp32"),
     (200, 1, 2, 2, 1, 128, "fp32"),
     (97, 2, 4, 4, 2, 64, "bf16"),
+    (333, 2, 2, 3, 2, 32, "bf16"),
+    (200, 1, 2, 2, 1, 128, "bf16"),
+    (600, 1, 4, 4, 2, 64, "bf16"),     # several 256-key blocks, a ragged last one
 ])
 def test_backward_edge_shapes(gqe, L, B, G, E, k, D, dtype):
-    """Ragged lengths (tails of every tile), head sizes 32 and 128, k = 1."""
+    """Ragged lengths (tails of every tile), every head size in both
+    precisions, k = 1, and key blocks past the first."""
     wl = W.Workload("edge", B, L, 128, G, E, k, D, dtype, 1.0, 0.05)
     log(f"[backward edge] {wl}")
     I = W.make_inputs(wl, seed=4, with_gqa=True)
