@@ -770,3 +770,58 @@ def gqe_forward_group_k(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, group_to
     y = output_projection(s_all, wo)
     return dict(r=r, p=p, idx=idx, w=w, counts=counts, offsets=offsets, pos=pos, slot=slot,
                 q=q_all, o=o_all, s=s_all, y=y)
+
+
+def gqe_decode_step_group_k(x_t, k_cache, v_cache, pos, wq, wk, wv, wr, wo, br, n_groups,
+                            n_experts, group_top_k, head_dim, shared_kv_group=0, scale=None,
+                            output_mode="full"):
+    """One decode step (as gqe_decode_step) with k_g experts selected in group
+    g: idx, w [B, K]; q, o [B, S, d_h] with group g's hard slots from koff[g]
+    and then the shared head for the full output; s, y as in the prefill layer
+    with per-group counts."""
+    if output_mode not in OUTPUT_MODES:
+        raise ValueError(output_mode)
+    B, d = x_t.shape
+    G, E, dh = n_groups, n_experts, head_dim
+    koff = group_offsets(group_top_k)
+    K = koff[-1]
+    scale = 1.0 / math.sqrt(dh) if scale is None else scale
+    full = output_mode == "full"
+    r, p, idx, w = route_group_k(x_t, wr, br, G, E, group_top_k)     # steps 1-4
+    k_new = (x_t @ wk.T).reshape(B, G, dh)                            # step 6
+    v_new = (x_t @ wv.T).reshape(B, G, dh)
+    kc, vc = k_cache.copy(), v_cache.copy()
+    S = K + (1 if full else 0)
+    q_all = np.empty((B, S, dh))
+    o_all = np.empty((B, S, dh))
+    s_all = np.empty((B, (K + (2 if full else 0)) * dh))
+    for b in range(B):
+        t = int(pos[b])
+        kc[b, :, t] = k_new[b]
+        vc[b, :, t] = v_new[b]
+        tt = np.array([t])
+        for g in range(G):
+            for j in range(group_top_k[g]):                           # step 7
+                h = koff[g] + j
+                qh = x_t[b] @ head_rows(wq, expert_head(g, int(idx[b, h]), E), dh).T
+                q_all[b, h] = qh
+                o_all[b, h] = causal_attention(qh[None], tt, kc[b, g], vc[b, g], scale)[0]
+        o_hard = o_all[b, :K]
+        if output_mode == "hard":
+            s_all[b] = o_hard.reshape(-1)
+            continue
+        if output_mode == "weighted_concat":
+            p_sel = np.concatenate([p[b, g, idx[b, koff[g]:koff[g + 1]].astype(np.int64)]
+                                    for g in range(G)])
+            s_all[b] = (p_sel[:, None] * o_hard).reshape(-1)
+            continue
+        q_sh = x_t[b] @ head_rows(wq, G * E, dh).T                    # step 8
+        o_sh = causal_attention(q_sh[None], tt, kc[b, shared_kv_group], vc[b, shared_kv_group],
+                                scale)[0]
+        q_all[b, K] = q_sh
+        o_all[b, K] = o_sh
+        o_w = w[b] @ o_hard                                           # step 9
+        s_all[b] = np.concatenate([o_hard.reshape(-1), o_sh, o_w])    # step 10
+    y = output_projection(s_all, wo)                                  # step 11
+    return dict(r=r, p=p, idx=idx, w=w, k_new=k_new, v_new=v_new, k_cache=kc, v_cache=vc,
+                q=q_all, o=o_all, s=s_all, y=y)

@@ -627,6 +627,47 @@ def pin_group_k_first_position(orc):
     want = np.concatenate(slots) @ t["wo"].T
     assert np.allclose(f["y"][0, 0], want, rtol=0, atol=1e-12)
 
+def pin_group_k_decode_step(orc):
+    """The per-group decode step is the per-group prefill layer's row t (cache
+    holding the prefill K/V of positions < t, anything after), for every output
+    construction; with the same k in every group it is the uniform decode step."""
+    rng = np.random.default_rng(83)
+    ks = [1, 3, 2]
+    t_ = tiny_layer(rng, B=2, L=9, G=3, E=3, k=2)
+    G, E, dh = t_["G"], t_["E"], t_["dh"]
+    B, L, d = t_["x"].shape
+    pos = np.array([8, 2])
+    K = np.stack([orc.kv_project(t_["x"][b], t_["wk"], G, dh, L) for b in range(B)])
+    V = np.stack([orc.kv_project(t_["x"][b], t_["wv"], G, dh, L) for b in range(B)])
+    kc = rng.standard_normal((B, G, 12, dh))
+    vc = rng.standard_normal((B, G, 12, dh))
+    for b in range(B):
+        kc[b, :, :pos[b]] = K[b, :, :pos[b]]
+        vc[b, :, :pos[b]] = V[b, :, :pos[b]]
+    x_t = np.stack([t_["x"][b, pos[b]] for b in range(B)])
+    for mode in orc.OUTPUT_MODES:
+        width = (sum(ks) + (2 if mode == "full" else 0)) * dh
+        wo = rng.standard_normal((d, width))
+        pre = orc.gqe_forward_group_k(t_["x"], t_["wq"], t_["wk"], t_["wv"], t_["wr"], wo, t_["br"],
+                                      G, E, ks, dh, output_mode=mode)
+        dec = orc.gqe_decode_step_group_k(x_t, kc, vc, pos, t_["wq"], t_["wk"], t_["wv"], t_["wr"],
+                                          wo, t_["br"], G, E, ks, dh, output_mode=mode)
+        for b in range(B):
+            assert np.array_equal(dec["idx"][b], pre["idx"][b, pos[b]])
+            assert np.allclose(dec["w"][b], pre["w"][b, pos[b]], rtol=0, atol=1e-15)
+            assert np.allclose(dec["y"][b], pre["y"][b, pos[b]], rtol=0, atol=1e-12), mode
+            assert np.allclose(dec["k_cache"][b, :, pos[b]], K[b, :, pos[b]], rtol=0, atol=1e-12)
+    # uniform counts: the pages' decode step
+    k = 2
+    wo = rng.standard_normal((d, (k * G + 2) * dh))
+    a = orc.gqe_decode_step(x_t, kc, vc, pos, t_["wq"], t_["wk"], t_["wv"], t_["wr"], wo, t_["br"],
+                            G, E, k, dh)
+    g = orc.gqe_decode_step_group_k(x_t, kc, vc, pos, t_["wq"], t_["wk"], t_["wv"], t_["wr"], wo,
+                                    t_["br"], G, E, [k] * G, dh)
+    assert np.array_equal(g["idx"], a["idx"].reshape(B, -1))
+    assert np.allclose(g["y"], a["y"], rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_k_equals_e_is_dense_gqa,
     pin_weights_sum_to_one,
@@ -651,4 +692,5 @@ ALL_PINS = [
     pin_group_k_uniform_is_the_layer,
     pin_group_k_selection_brute_force,
     pin_group_k_first_position,
+    pin_group_k_decode_step,
 ]

@@ -260,6 +260,18 @@ def m_group_k_weights_over_all(mod):
                   "        w[:, koff[g]:koff[g + 1]] = renormalize(p[:, g], topk_in_group(r[:, g], max(group_top_k)))[:, :kg]")
 
 
+def m_group_k_decode_group_zero_keys(mod):
+    """the per-group decode step's hard slots all read group 0's cache."""
+    _patch_source(mod, "                o_all[b, h] = causal_attention(qh[None], tt, kc[b, g], vc[b, g], scale)[0]",
+                  "                o_all[b, h] = causal_attention(qh[None], tt, kc[b, 0], vc[b, 0], scale)[0]")
+
+
+def m_group_k_decode_rank_as_slot(mod):
+    """the per-group decode step looks its experts up by rank j, not by slot."""
+    _patch_source(mod, "qh = x_t[b] @ head_rows(wq, expert_head(g, int(idx[b, h]), E), dh).T",
+                  "qh = x_t[b] @ head_rows(wq, expert_head(g, int(idx[b, j]), E), dh).T")
+
+
 MUTATIONS = [
     m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
     m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
@@ -272,6 +284,7 @@ MUTATIONS = [
     m_bwd_no_rowsum_term, m_bwd_dk_unscaled, m_bwd_weighted_slot_dropped,
     m_bwd_softmax_jacobian_diagonal, m_bwd_aux_sign, m_aux_fraction_per_token,
     m_bwd_shared_head_group0, m_group_k_first_groups_k, m_group_k_weights_over_all,
+    m_group_k_decode_group_zero_keys, m_group_k_decode_rank_as_slot,
 ]
 
 
