@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/gqe.h"
@@ -338,8 +339,7 @@ int decode_q_heads(const gqe_config* c, bool dense) {
   return c->n_groups * c->n_experts + (!dense && full_output(c) ? 1 : 0);
 }
 int decode_heads(const gqe_config* c, bool dense) {
-  return dense ? c->n_groups * c->n_experts
-               : c->top_k * c->n_groups + (full_output(c) ? 1 : 0);
+  return dense ? c->n_groups * c->n_experts : total_k(c) + (full_output(c) ? 1 : 0);
 }
 int decode_ld_s(const gqe_config* c, bool dense) {
   return (dense ? c->n_groups * c->n_experts : slot_count(c)) * c->head_dim;
@@ -351,7 +351,7 @@ struct DecodeLayout {
 };
 
 DecodeLayout make_decode_layout(const gqe_config* c, bool dense) {
-  const size_t B = c->batch, G = c->n_groups, k = c->top_k, D = c->head_dim;
+  const size_t B = c->batch, K = total_k(c), D = c->head_dim;
   const size_t H = decode_heads(c, dense);
   DecodeLayout l{};
   l.chunk = decode_chunk(c->batch, c->n_groups, c->seq_len);
@@ -363,8 +363,8 @@ DecodeLayout make_decode_layout(const gqe_config* c, bool dense) {
     return o;
   };
   if (!dense) {
-    l.idx = take(B * G * k * 4);
-    l.w = take(B * G * k * 4);
+    l.idx = take(B * K * 4);
+    l.w = take(B * K * 4);
   }
   l.q = take(B * static_cast<size_t>(decode_q_heads(c, dense)) * D * 4);
   l.part = take(B * H * static_cast<size_t>(l.n_chunks) * (D + 2) * 4);
@@ -378,7 +378,6 @@ int check_decode_cfg(const gqe_config* c) {
   if (st != GQE_OK) return st;
   if (c->batch > 0 && c->seq_len < 1) return GQE_ERR_INVALID_ARG;  // no room for the token
   if (c->d_model > kDecodeMaxDModel) return GQE_ERR_UNSUPPORTED;
-  if (c->group_top_k != nullptr) return GQE_ERR_UNSUPPORTED;  // uniform top_k only
   return GQE_OK;
 }
 
@@ -387,7 +386,7 @@ int decode_impl(const gqe_config* c, bool dense, const void* x, const void* wq, 
                 const void* wv, const void* wr, const void* wo, void* k_cache, void* vt_cache,
                 const int32_t* pos, void* out, void* ws, hipStream_t stream) {
   const DecodeLayout l = make_decode_layout(c, dense);
-  const int G = c->n_groups, E = c->n_experts, k = c->top_k;
+  const int G = c->n_groups, E = c->n_experts;
   DecodeParams p;
   p.x = x;
   p.wq = wq;
@@ -411,15 +410,19 @@ int decode_impl(const gqe_config* c, bool dense, const void* x, const void* wq, 
   p.d = c->d_model;
   p.G = G;
   p.E = E;
-  p.k = k;
+  p.gk = make_group_k(c);
   p.D = c->head_dim;
   p.Lc = c->seq_len;
   p.q_heads = decode_q_heads(c, dense);
   p.Hq = decode_heads(c, dense);
-  p.n_routed = dense ? G * E : G * k;
+  p.n_routed = dense ? G * E : p.gk.K;
   p.shared_head = !dense && full_output(c) ? 1 : 0;
   p.shared_kv_group = c->shared_kv_group;
-  p.heads_per_group = dense ? E : k;
+  p.max_heads = 0;
+  for (int g = 0; g <= G; ++g) p.hbeg[g] = dense ? g * E : p.gk.koff[g];
+  for (int g = 0; g < G; ++g)
+    p.max_heads = std::max(p.max_heads, p.hbeg[g + 1] - p.hbeg[g] +
+                                            (p.shared_head && g == c->shared_kv_group ? 1 : 0));
   p.chunk = l.chunk;
   p.scale = softmax_scale(c);
   p.ld_s = decode_ld_s(c, dense);

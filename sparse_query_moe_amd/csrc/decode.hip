@@ -87,14 +87,15 @@ __device__ __forceinline__ int vt_column(int p) {
 // ---------------------------------------------------------------------------
 struct DecAttnArgs {
   const float* q;         // [B, q_heads, D] every query head's projection (unscaled)
-  const int32_t* idx;     // [B, G, k] routed experts, or NULL (slot h uses query head h)
-  int E, k, q_heads;
+  const int32_t* idx;     // [B, K] routed experts by slot, or NULL (slot h uses query head h)
+  int E, q_heads;
   const void* k_cache;    // [B, G, Lc, D]
   const void* vt_cache;   // [B, G, Lc/64, D, 64]
   const int32_t* pos;     // [B]
   float* part;            // [B, Hq, n_chunks, D + 2]: o (unnormalized), m, l
   int B, G, Lc, D, Hq, chunk, n_chunks;
-  int heads_per_group;    // query heads g*hpg .. g*hpg+hpg-1 read group g
+  int hbeg[kMaxGroups + 1];  // slot heads hbeg[g] .. hbeg[g+1]-1 read group g
+  int max_heads;          // most slot heads of one group, the extra one included
   int extra_head;         // a further head (the shared one) or -1
   int extra_group;        // the group it reads
   float scale_log2;
@@ -162,20 +163,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecAttnArgs a) {
   combine_head<T>(a, pair / a.Hq, pair % a.Hq, lane, sw[wave]);
 }
 
-// query head read by slot head h of sequence b: routed slot g*k + j uses
-// expert idx[b, g, j] of group g (head g*E + e); the next slot is the shared
-// head (the last query head); without idx slot h is query head h
-__device__ __forceinline__ const float* q_row(const DecAttnArgs& a, int b, int h, int n_routed,
-                                             int D) {
+// query head read by slot head h (of group g) of sequence b: routed slot h
+// uses expert idx[b, h] of its group (head g*E + e); the next slot is the
+// shared head (the last query head); without idx slot h is query head h
+__device__ __forceinline__ const float* q_row(const DecAttnArgs& a, int b, int g, int h,
+                                             int n_routed, int D) {
   int qh = h;
-  if (a.idx != nullptr) {
-    if (h < n_routed) {
-      const int g = h / a.k;
-      qh = g * a.E + a.idx[(static_cast<size_t>(b) * a.G + g) * a.k + h % a.k];
-    } else {
-      qh = a.q_heads - 1;
-    }
-  }
+  if (a.idx != nullptr)
+    qh = h < n_routed ? g * a.E + a.idx[static_cast<size_t>(b) * n_routed + h] : a.q_heads - 1;
   return a.q + (static_cast<size_t>(b) * a.q_heads + qh) * D;
 }
 
@@ -196,8 +191,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecAttnArgs a)
   const int kv_end = (t >= 0 && t < a.Lc) ? t + 1 : 0;  // a position outside the cache reads nothing
   const int k0 = c * a.chunk, k1 = min(k0 + a.chunk, kv_end);
   const bool extra = a.extra_head >= 0 && g == a.extra_group;
-  const int nh = a.heads_per_group + (extra ? 1 : 0);
-  auto head_of = [&](int i) { return i < a.heads_per_group ? g * a.heads_per_group + i : a.extra_head; };
+  const int nh0 = a.hbeg[g + 1] - a.hbeg[g];  // this group's routed slot heads
+  const int nh = nh0 + (extra ? 1 : 0);
+  auto head_of = [&](int i) { return i < nh0 ? a.hbeg[g] + i : a.extra_head; };
   auto part_of = [&](int i) {
     return a.part + ((static_cast<size_t>(b) * a.Hq + head_of(i)) * a.n_chunks + c) * (D + 2);
   };
@@ -209,7 +205,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(DecAttnArgs a)
     return;
   }
   for (int i = threadIdx.x; i < nh * D; i += kDecThreads)
-    qs[i / D][i % D] = q_row(a, b, head_of(i / D), a.G * a.heads_per_group, D)[i % D] * a.scale_log2;
+    qs[i / D][i % D] = q_row(a, b, g, head_of(i / D), a.hbeg[a.G], D)[i % D] * a.scale_log2;
   __syncthreads();
 
   const T* Kg = static_cast<const T*>(a.k_cache) + (static_cast<size_t>(b) * a.G + g) * a.Lc * D;
@@ -433,8 +429,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecAttnAr
   const int kv_end = (t >= 0 && t < a.Lc) ? t + 1 : 0;
   const int k0 = c * a.chunk, k1 = min(k0 + a.chunk, kv_end);
   const bool extra = a.extra_head >= 0 && g == a.extra_group;
-  const int nh = a.heads_per_group + (extra ? 1 : 0);
-  auto head_of = [&](int i) { return i < a.heads_per_group ? g * a.heads_per_group + i : a.extra_head; };
+  const int nh0 = a.hbeg[g + 1] - a.hbeg[g];  // this group's routed slot heads
+  const int nh = nh0 + (extra ? 1 : 0);
+  auto head_of = [&](int i) { return i < nh0 ? a.hbeg[g] + i : a.extra_head; };
   auto part_of = [&](int i) {
     return a.part + ((static_cast<size_t>(b) * a.Hq + head_of(i)) * a.n_chunks + c) * (D + 2);
   };
@@ -454,7 +451,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_bf16_kernel(DecAttnAr
 #pragma unroll
   for (int h = 0; h < MAXH; ++h) {
     if (h < nh) {
-      const float* qp = q_row(a, b, head_of(h), a.G * a.heads_per_group, D) + 8 * kc;
+      const float* qp = q_row(a, b, g, head_of(h), a.hbeg[a.G], D) + 8 * kc;
       const float4 q0 = reinterpret_cast<const float4*>(qp)[0];
       const float4 q1 = reinterpret_cast<const float4*>(qp)[1];
       const float sl = a.scale_log2;
@@ -716,9 +713,10 @@ struct FrontArgs {
   const void* x;          // [B, d] the new tokens
   const void* wr;         // [G*E, d] router rows, or NULL (no routing)
   const float* bias;      // [G*E] or NULL
-  int32_t* idx;           // [B, G, k]
-  float* w;               // [B, G, k]
-  int d, G, E, k, renorm;
+  int32_t* idx;           // [B, K]
+  float* w;               // [B, K]
+  int d, G, E, renorm;
+  GroupK gk;              // experts selected per group and their slot offsets
   int n_gemm_blocks, gemm_nbx;
 };
 
@@ -731,7 +729,7 @@ __global__ __launch_bounds__(256) void decode_front_kernel(RowsGemmArgs g, Front
     gemm_tile<T>(g, (id % f.gemm_nbx) * 32, (id / f.gemm_nbx) * 32);
   else
     route_token_block<T>(static_cast<const T*>(f.x), static_cast<const T*>(f.wr), f.bias, f.idx,
-                         f.w, id - f.n_gemm_blocks, f.d, f.G, f.E, f.k, f.renorm);
+                         f.w, id - f.n_gemm_blocks, f.d, f.G, f.E, f.gk, f.renorm);
 }
 
 template <typename T>
@@ -745,7 +743,7 @@ hipError_t launch_rows_gemm(const RowsGemmArgs& a, hipStream_t stream) {
 
 template <typename T, int D>
 hipError_t launch_decode_attn_d(const DecAttnArgs& a, hipStream_t stream) {
-  const int nh = a.heads_per_group + (a.extra_head >= 0 ? 1 : 0);
+  const int nh = a.max_heads;
   const dim3 grid(a.n_chunks, a.B * a.G);
   if (sizeof(T) == 2) {  // coalesced bf16 kernel while the head accumulators fit
     if (nh <= 4) {
@@ -814,7 +812,7 @@ hipError_t launch_decode_front(const DecodeParams& p, hipStream_t stream) {
   f.d = p.d;
   f.G = p.G;
   f.E = p.E;
-  f.k = p.k;
+  f.gk = p.gk;
   f.renorm = p.renorm;
   f.gemm_nbx = ga.N / 32;
   f.n_gemm_blocks = f.gemm_nbx * ((p.B + 31) / 32);
@@ -829,7 +827,6 @@ hipError_t launch_decode_attend(const DecodeParams& p, hipStream_t stream) {
   aa.q = p.q;
   aa.idx = p.idx;
   aa.E = p.E;
-  aa.k = p.k;
   aa.q_heads = p.q_heads;
   aa.k_cache = p.k_cache;
   aa.vt_cache = p.vt_cache;
@@ -842,7 +839,8 @@ hipError_t launch_decode_attend(const DecodeParams& p, hipStream_t stream) {
   aa.Hq = p.Hq;
   aa.chunk = p.chunk;
   aa.n_chunks = (p.Lc + p.chunk - 1) / p.chunk;
-  aa.heads_per_group = p.heads_per_group;
+  for (int g = 0; g <= p.G; ++g) aa.hbeg[g] = p.hbeg[g];
+  aa.max_heads = p.max_heads;
   aa.extra_head = p.shared_head ? p.n_routed : -1;
   aa.extra_group = p.shared_kv_group;
   aa.scale_log2 = p.scale * kLog2e;

@@ -176,8 +176,8 @@ struct DecodeParams {
   const void* wr;         // [G*E, d] router rows (GQE) or NULL (GQA: no routing)
   const float* router_bias;  // [G*E] or NULL
   int renorm;             // routing weights renormalized over the k selected
-  int32_t* idx;           // [B, G, k] routed experts, or NULL (GQA: every head)
-  float* w;               // [B, G, k] routing weights (GQE) or NULL
+  int32_t* idx;           // [B, K] routed experts by slot, or NULL (GQA: every head)
+  float* w;               // [B, K] routing weights (GQE) or NULL
   const int32_t* pos;     // [B] position of each new token in its cache
   float* q;               // [B, q_heads, D] scratch: every query head's projection
   void* k_cache;          // [B, G, Lc, D]
@@ -186,13 +186,15 @@ struct DecodeParams {
   void* s;                // [B, ld_s] slot vectors (concatenated head outputs)
   const float* row_scale; // [B, n_routed] factor of the routed heads' outputs, or NULL
   void* out;              // [B, d]
-  int B, d, G, E, k, D, Lc;
+  int B, d, G, E, D, Lc;
+  GroupK gk;              // GQE: experts per group and their slot offsets
   int q_heads;            // query heads projected per token (G*E, plus the shared head)
   int Hq;                 // slot heads per token (heads that attend)
   int n_routed;           // heads before the shared one (the routed heads)
   int shared_head;        // 1: head n_routed is the shared head
   int shared_kv_group;
-  int heads_per_group;    // head h < n_routed reads group h / heads_per_group
+  int hbeg[kMaxGroups + 1];  // slot heads hbeg[g] .. hbeg[g+1]-1 read group g (hbeg[G] = n_routed)
+  int max_heads;          // most slot heads of one group, the shared one included
   int chunk;              // keys per attention block (decode_chunk)
   float scale;            // softmax scale
   int ld_s, K_out;

@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include "device_common.h"
+#include "kernels.h"
 
 namespace gqe {
 
@@ -66,7 +67,7 @@ __device__ __forceinline__ void route_token_block(const T* __restrict__ x, const
                                                   const float* __restrict__ bias,
                                                   int32_t* __restrict__ idx_out,
                                                   float* __restrict__ w_out, int t, int d, int G,
-                                                  int E, int k, int renorm) {
+                                                  int E, const GroupK& gk, int renorm) {
   __shared__ double logit[64], ex[64];
   __shared__ int rank_of[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -108,11 +109,12 @@ __device__ __forceinline__ void route_token_block(const T* __restrict__ x, const
   if (tid < GE) {
     const int g = tid / E, e = tid % E;
     const int rank = rank_of[tid];
+    const int k = gk.kg[g];
     if (rank < k) {
       double z = 0.0;
       for (int f = 0; f < E; ++f)
         if (rank_of[g * E + f] < k || !renorm) z += ex[g * E + f];
-      const size_t o = (static_cast<size_t>(t) * G + g) * k;
+      const size_t o = static_cast<size_t>(t) * gk.K + gk.koff[g];  // group g's slots of token t
       idx_out[o + rank] = e;
       w_out[o + rank] = static_cast<float>(ex[tid] / z);
     }

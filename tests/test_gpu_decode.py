@@ -215,3 +215,37 @@ def test_decode_graph_replay(gqe):
         pos_g += 1
         pos_e += 1
     del graph
+
+
+GROUP_K_DECODE_CASES = [
+    # name, overrides, per-group counts, output mode
+    ("dec_tiny_fp32", dict(n_groups=3, n_experts=3, batch=3), [1, 3, 2], "full"),
+    ("dec_tiny_fp32", dict(n_groups=3, n_experts=3, batch=3), [2, 1, 3], "hard"),
+    ("dec_tiny_fp32", dict(n_groups=3, n_experts=3, batch=3), [3, 2, 1], "weighted_concat"),
+    ("dec_b64_c8k", dict(batch=6, seq_len=1000), [1, 2, 3, 2], "full"),
+    ("dec_b64_c8k", dict(batch=4, seq_len=700, n_experts=8), [6, 1, 1, 2], "full"),  # 7 heads on group 0
+]
+
+
+@pytest.mark.parametrize("name,over,ks,mode", GROUP_K_DECODE_CASES)
+def test_gqe_decode_group_k(gqe, name, over, ks, mode):
+    """Per-group expert counts in decode: routing bit for bit, caches, output."""
+    wl = W.DECODE_WORKLOADS[name].with_(**over)
+    K = sum(ks)
+    log(f"[decode group k] {wl} ks={ks} {mode}")
+    I = W.make_decode_inputs(wl.with_(top_k=max(ks)), seed=9, with_gqa=True)
+    rng = np.random.Generator(np.random.PCG64(10))
+    width = (K + (2 if mode == "full" else 0)) * wl.head_dim
+    I["wo"] = W._draw(rng, (wl.d_model, width), wl.w_std, wl.dtype)
+    dev = _device(wl, I)
+    cfg, ws, out = _run(gqe, wl.with_(top_k=max(ks)), dev, output_mode=mode, group_top_k=ks)
+    F = f64_inputs(wl, I)
+    kc, vc = W.to_f64(I["k_cache"], wl.dtype), W.to_f64(I["v_cache"], wl.dtype)
+    ref = oracle.gqe_decode_step_group_k(F["x"], kc, vc, I["pos"], F["wq"], F["wk"], F["wv"],
+                                         F["wr"], F["wo"], F["br"], wl.n_groups, wl.n_experts, ks,
+                                         wl.head_dim, output_mode=mode)
+    idx = ws[:4 * wl.batch * K].view(torch.int32).cpu().numpy().reshape(ref["idx"].shape)
+    assert np.array_equal(idx, ref["idx"]), f"idx mismatches: {(idx != ref['idx']).sum()}"
+    _check_caches(wl, I, dev, ref, name)
+    mx, mean, rel = output_gate(to_f64(out), ref["y"], wl.dtype, f"{name} {ks} {mode} y")
+    log(f"  y: max-abs {mx:.3e} mean-abs {mean:.3e} rel-L2 {rel:.3e}")
