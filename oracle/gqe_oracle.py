@@ -825,3 +825,117 @@ def gqe_decode_step_group_k(x_t, k_cache, v_cache, pos, wq, wk, wv, wr, wo, br, 
     y = output_projection(s_all, wo)                                  # step 11
     return dict(r=r, p=p, idx=idx, w=w, k_new=k_new, v_new=v_new, k_cache=kc, v_cache=vc,
                 q=q_all, o=o_all, s=s_all, y=y)
+
+
+def load_balance_loss_group_k(p, idx, n_experts, group_top_k):
+    """L_aux, f [G, E] and P [G, E] with k_g experts in group g: f[g, e] is
+    expert e's share of group g's T*k_g routed slots (idx [..., K])."""
+    G, E = p.shape[-2], n_experts
+    koff = group_offsets(group_top_k)
+    pt = p.reshape(-1, G, E)
+    it = idx.reshape(-1, koff[-1])
+    T = pt.shape[0]
+    f = np.zeros((G, E))
+    for g in range(G):
+        f[g] = np.bincount(it[:, koff[g]:koff[g + 1]].reshape(-1), minlength=E)[:E] / (
+            T * group_top_k[g])
+    P = pt.mean(axis=0)
+    return (E / G) * float((f * P).sum()), f, P
+
+
+def gqe_backward_group_k(x, wq, wk, wv, wr, wo, br, dy, n_groups, n_experts, group_top_k,
+                         head_dim, shared_kv_group=0, scale=None, output_mode="full",
+                         aux_weight=0.0):
+    """Gradients of <y, dy> + aux_weight * L_aux for the layer with k_g experts
+    in group g (float64): the same returns as gqe_backward, with dw [B, L, K]
+    and the slot-heads of gqe_forward_group_k."""
+    if output_mode not in OUTPUT_MODES:
+        raise ValueError(output_mode)
+    full = output_mode == "full"
+    B, L, d = x.shape
+    G, E, dh = n_groups, n_experts, head_dim
+    koff = group_offsets(group_top_k)
+    K = koff[-1]
+    sc = 1.0 / math.sqrt(dh) if scale is None else scale
+    fwd = gqe_forward_group_k(x, wq, wk, wv, wr, wo, br, G, E, group_top_k, dh,
+                              shared_kv_group=shared_kv_group, scale=scale,
+                              output_mode=output_mode)
+    p, idx, w, s_all, o_all = fwd["p"], fwd["idx"], fwd["w"], fwd["s"], fwd["o"]
+    Sh = o_all.shape[2]
+    dwo = np.einsum("bln,blc->nc", dy, s_all)             # y = s . W_O^T
+    ds = dy @ wo
+    dx = np.zeros_like(x)
+    dwq, dwk, dwv = np.zeros_like(wq), np.zeros_like(wk), np.zeros_like(wv)
+    dr = np.zeros((B, L, G, E))
+    dw_all = np.zeros((B, L, K))
+    do_all = np.zeros((B, L, Sh, dh))
+    dq_all = np.zeros((B, L, Sh, dh))
+    dk_all = np.zeros((B, G, L, dh))
+    dv_all = np.zeros((B, G, L, dh))
+    tpos = np.arange(L)
+    for b in range(B):
+        o_hard = o_all[b, :, :K]                          # [L, K, d_h]
+        ds_h = ds[b, :, :K * dh].reshape(L, K, dh)
+        if full:                                          # steps 9-10 backwards
+            ds_w = ds[b, :, (K + 1) * dh:]
+            do_hard = ds_h + w[b][..., None] * ds_w[:, None, :]
+            dw = np.einsum("lhd,ld->lh", o_hard, ds_w)
+            for g in range(G):                            # w = softmax of group g's selected logits
+                sl = slice(koff[g], koff[g + 1])
+                dr_sel = softmax_backward(w[b][:, sl], dw[:, sl])
+                np.put_along_axis(dr[b][:, g], idx[b][:, sl].astype(np.int64), dr_sel, axis=-1)
+        elif output_mode == "weighted_concat":
+            p_sel = np.concatenate([np.take_along_axis(p[b][:, g], idx[b][:, koff[g]:koff[g + 1]]
+                                                       .astype(np.int64), axis=-1)
+                                    for g in range(G)], axis=1)
+            do_hard = p_sel[..., None] * ds_h
+            dw = np.einsum("lhd,lhd->lh", o_hard, ds_h)
+            for g in range(G):                            # p = softmax over all E
+                sl = slice(koff[g], koff[g + 1])
+                dp = np.zeros((L, E))
+                np.put_along_axis(dp, idx[b][:, sl].astype(np.int64), dw[:, sl], axis=-1)
+                dr[b][:, g] += softmax_backward(p[b][:, g], dp)
+        else:
+            do_hard = ds_h
+            dw = np.zeros((L, K))
+        dw_all[b] = dw
+        do_all[b, :, :K] = do_hard
+        xb = x[b]
+        K_b = kv_project(xb, wk, G, dh, L)
+        V_b = kv_project(xb, wv, G, dh, L)
+        heads = [(koff[g] + j, g) for g in range(G) for j in range(group_top_k[g])]
+        if full:
+            do_all[b, :, K] = ds[b, :, K * dh:(K + 1) * dh]
+            heads.append((K, shared_kv_group))
+        for h, g in heads:
+            dq, dKg, dVg = attention_backward(fwd["q"][b, :, h], tpos, K_b[g], V_b[g],
+                                              do_all[b, :, h], sc)
+            dq_all[b, :, h] = dq
+            dk_all[b, g] += dKg
+            dv_all[b, g] += dVg
+            if h == K:                                    # the shared head's own W_q rows
+                rows = slice(G * E * dh, (G * E + 1) * dh)
+                dwq[rows] += dq.T @ xb
+                dx[b] += dq @ wq[rows]
+                continue
+            for e in range(E):
+                m = idx[b, :, h] == e
+                if m.any():
+                    rows = slice(expert_head(g, e, E) * dh, (expert_head(g, e, E) + 1) * dh)
+                    dwq[rows] += dq[m].T @ xb[m]
+                    dx[b][m] += dq[m] @ wq[rows]
+        for g in range(G):                                # K, V = x . W_k^T, x . W_v^T
+            rows = slice(g * dh, (g + 1) * dh)
+            dwk[rows] += dk_all[b, g].T @ xb
+            dwv[rows] += dv_all[b, g].T @ xb
+            dx[b] += dk_all[b, g] @ wk[rows] + dv_all[b, g] @ wv[rows]
+    aux_loss, f, _ = load_balance_loss_group_k(p, idx, E, group_top_k)
+    if aux_weight:
+        dp_aux = np.broadcast_to(aux_weight * (E / G) * f / (B * L), p.shape)
+        dr += softmax_backward(p, dp_aux)
+    drf = dr.reshape(B * L, G * E)
+    dwr = drf.T @ x.reshape(B * L, d)                     # r = x . W_r^T + b_r
+    dbr = drf.sum(axis=0)
+    dx += (drf @ wr).reshape(B, L, d)
+    return dict(dx=dx, dwq=dwq, dwk=dwk, dwv=dwv, dwr=dwr, dbr=dbr, dwo=dwo, aux_loss=aux_loss,
+                ds=ds, do=do_all, dq=dq_all, dk=dk_all, dv=dv_all, dw=dw_all, dr=dr, fwd=fwd)

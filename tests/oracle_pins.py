@@ -668,6 +668,65 @@ def pin_group_k_decode_step(orc):
     assert np.allclose(g["y"], a["y"], rtol=0, atol=1e-12)
 
 
+def pin_group_k_backward(orc):
+    """The per-group backward: central differences of <y, dy> + alpha * L_aux
+    (f per group over its T*k_g slots) on every parameter tensor and on x, for
+    every output construction; with the same k in every group it is the
+    pages' backward."""
+    rng = np.random.default_rng(89)
+    h = 1e-6
+    ks = [1, 3, 2]
+    for mode, kw in (("full", dict(shared_kv_group=2, scale=0.6)), ("hard", {}),
+                     ("weighted_concat", {})):
+        t = tiny_layer(rng, B=2, L=5, d=6, G=3, E=3, k=1, dh=4)
+        t["br"] = rng.standard_normal(t["G"] * t["E"]) * 0.3
+        t["wo"] = rng.standard_normal((6, (sum(ks) + (2 if mode == "full" else 0)) * t["dh"]))
+        f0 = _run_gk(orc, t, ks, output_mode=mode, **kw)
+        srt = -np.sort(-f0["r"], axis=-1)
+        assert (srt[..., :-1] - srt[..., 1:]).min() > 1e-3, "seed too close to a routing tie"
+        # f[g] is a share of group g's slots: it sums to one over the experts
+        _, fsh, Psh = orc.load_balance_loss_group_k(f0["p"], f0["idx"], t["E"], ks)
+        assert np.allclose(fsh.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+        assert np.allclose(Psh.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        dy = rng.standard_normal(f0["y"].shape)
+        alpha = 0.3
+        g = orc.gqe_backward_group_k(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"],
+                                     dy, t["G"], t["E"], ks, t["dh"], output_mode=mode,
+                                     aux_weight=alpha, **kw)
+
+        def loss():
+            f = _run_gk(orc, t, ks, output_mode=mode, **kw)
+            aux = orc.load_balance_loss_group_k(f["p"], f["idx"], t["E"], ks)[0]
+            return float((f["y"] * dy).sum()) + alpha * aux
+        for name, key in (("x", "dx"), ("wq", "dwq"), ("wk", "dwk"), ("wv", "dwv"),
+                          ("wr", "dwr"), ("br", "dbr"), ("wo", "dwo")):
+            flat = t[name].reshape(-1)
+            for i in rng.choice(flat.size, size=min(flat.size, 16), replace=False):
+                old = flat[i]
+                flat[i] = old + h
+                lp = loss()
+                flat[i] = old - h
+                lm = loss()
+                flat[i] = old
+                num = (lp - lm) / (2 * h)
+                ana = g[key].reshape(-1)[i]
+                assert abs(num - ana) <= 1e-6 * (1.0 + abs(num)), (mode, name, i, num, ana)
+    # the same k everywhere: the pages' backward, for every output construction
+    for mode in orc.OUTPUT_MODES:
+        t = tiny_layer(rng, B=2, L=6, d=6, G=2, E=3, k=2, dh=4)
+        if mode != "full":
+            t["wo"] = np.ascontiguousarray(t["wo"][:, :t["k"] * t["G"] * t["dh"]])
+        dy = rng.standard_normal((2, 6, 6))
+        a = orc.gqe_backward(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"], dy,
+                             t["G"], t["E"], t["k"], t["dh"], output_mode=mode, aux_weight=0.2)
+        b = orc.gqe_backward_group_k(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"],
+                                     dy, t["G"], t["E"], [t["k"]] * t["G"], t["dh"],
+                                     output_mode=mode, aux_weight=0.2)
+        for key in ("dx", "dwq", "dwk", "dwv", "dwr", "dbr", "dwo"):
+            assert np.allclose(b[key], a[key], rtol=0, atol=1e-12), (mode, key)
+        assert abs(b["aux_loss"] - a["aux_loss"]) <= 1e-15
+
+
 ALL_PINS = [
     pin_k_equals_e_is_dense_gqa,
     pin_weights_sum_to_one,
@@ -693,4 +752,5 @@ ALL_PINS = [
     pin_group_k_selection_brute_force,
     pin_group_k_first_position,
     pin_group_k_decode_step,
+    pin_group_k_backward,
 ]

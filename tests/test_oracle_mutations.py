@@ -235,7 +235,13 @@ def m_bwd_softmax_jacobian_diagonal(mod):
 
 def m_bwd_aux_sign(mod):
     """the load-balancing gradient with the wrong sign."""
-    _patch_source(mod, "dr += softmax_backward(p, dp_aux)", "dr -= softmax_backward(p, dp_aux)")
+    _patch_source(mod, """    aux_loss, f, _ = load_balance_loss(p, idx, E)
+    if aux_weight:
+        dp_aux = np.broadcast_to(aux_weight * (E / G) * f / (B * L), p.shape)
+        dr += softmax_backward(p, dp_aux)""", """    aux_loss, f, _ = load_balance_loss(p, idx, E)
+    if aux_weight:
+        dp_aux = np.broadcast_to(aux_weight * (E / G) * f / (B * L), p.shape)
+        dr -= softmax_backward(p, dp_aux)""")
 
 
 def m_aux_fraction_per_token(mod):
@@ -272,6 +278,17 @@ def m_group_k_decode_rank_as_slot(mod):
                   "qh = x_t[b] @ head_rows(wq, expert_head(g, int(idx[b, j]), E), dh).T")
 
 
+def m_group_k_aux_over_largest_k(mod):
+    """the per-group load fraction divides by the largest k, not by k_g."""
+    _patch_source(mod, "            T * group_top_k[g])", "            T * max(group_top_k))")
+
+
+def m_group_k_bwd_softmax_over_all_slots(mod):
+    """the per-group weight gradient treats all K slots as one softmax."""
+    _patch_source(mod, "                dr_sel = softmax_backward(w[b][:, sl], dw[:, sl])",
+                  "                dr_sel = softmax_backward(w[b], dw)[:, sl]")
+
+
 MUTATIONS = [
     m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
     m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
@@ -285,6 +302,7 @@ MUTATIONS = [
     m_bwd_softmax_jacobian_diagonal, m_bwd_aux_sign, m_aux_fraction_per_token,
     m_bwd_shared_head_group0, m_group_k_first_groups_k, m_group_k_weights_over_all,
     m_group_k_decode_group_zero_keys, m_group_k_decode_rank_as_slot,
+    m_group_k_aux_over_largest_k, m_group_k_bwd_softmax_over_all_slots,
 ]
 
 
