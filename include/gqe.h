@@ -88,7 +88,7 @@ typedef enum {
  * (sum of group_top_k, or top_k*G): the hard slots are group-major, group g's
  * k_g slots in rank order, and batch*seq_len*K < 2^31.
  * Built subset (GQE_ERR_UNSUPPORTED otherwise): head_dim in {32, 64, 128};
- * group_top_k for the prefill and decode calls (not the backward);
+ * group_top_k on every call (prefill, decode and backward);
  * the projections stream their reduction dimension in 128-byte steps, so
  * d_model, the slot width ((top_k*n_groups+2)*head_dim, or
  * top_k*n_groups*head_dim for the ablation outputs) and

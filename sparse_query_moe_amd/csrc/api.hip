@@ -467,13 +467,14 @@ struct BwdLayout {
 };
 
 BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
-  const size_t B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts, k = c->top_k;
+  const size_t B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts;
+  const size_t K = total_k(c);
   const size_t D = c->head_dim, d = c->d_model, es = elem_bytes(c), T = B * L;
   const size_t tiles = (L + 63) / 64;
   BwdLayout l{};
   l.tpad = static_cast<int>((T + 63) / 64 * 64);
   l.H = attn_heads(c, dense);
-  l.q_heads = dense ? static_cast<int>(G * E) : static_cast<int>(G * k + 1);
+  l.q_heads = dense ? static_cast<int>(G * E) : static_cast<int>(K + 1);
   l.ws = static_cast<int>((dense ? G * E : static_cast<size_t>(slot_count(c))) * D);
   l.qcols = static_cast<int>((G * E + (dense ? 0 : 1)) * D);
   l.kcol = l.qcols;
@@ -499,7 +500,7 @@ BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
   l.kt = take(B * G * tiles * D * 64 * es);
   l.vr = take(B * G * L * D * es);
   l.dsum = take(B * H * L * 4);
-  l.dw = take(dense ? 0 : T * G * k * 4);
+  l.dw = take(dense ? 0 : T * K * 4);
   l.dr = take(dense ? 0 : T * G * E * 4);
   l.p_all = take(dense ? 0 : T * G * E * 4);
   l.psum = take(dense ? 0 : G * E * 8);
@@ -519,7 +520,7 @@ int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq
   const Layout fl = make_layout(c, dense);
   const BwdLayout l = make_bwd_layout(c, dense);
   void* f = const_cast<void*>(fws);
-  const int G = c->n_groups, E = c->n_experts, k = c->top_k;
+  const int G = c->n_groups, E = c->n_experts;
   BwdParams p;
   p.x = x;
   p.wq = wq;
@@ -570,13 +571,13 @@ int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq
   p.d = c->d_model;
   p.G = G;
   p.E = E;
-  p.k = k;
+  p.gk = make_group_k(c);
   p.D = c->head_dim;
   p.H = l.H;
   p.q_heads = l.q_heads;
-  p.n_routed = dense ? 0 : G * k;
-  p.heads_per_group = dense ? E : k;
-  p.n_grouped = dense ? G * E : G * k;
+  p.n_routed = dense ? 0 : p.gk.K;
+  for (int g = 0; g <= G; ++g) p.hbeg[g] = dense ? g * E : p.gk.koff[g];
+  p.n_grouped = p.hbeg[G];
   p.extra_group = c->shared_kv_group;
   p.mode = dense ? 3 : c->output_mode == GQE_OUTPUT_FULL ? 0 : c->output_mode == GQE_OUTPUT_HARD ? 1 : 2;
   p.ws = l.ws;
@@ -599,7 +600,6 @@ int backward_entry(const gqe_config* cfg, bool dense, const void* x, const void*
                    void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_cfg(cfg);
   if (st != GQE_OK || empty(cfg)) return st;
-  if (cfg->group_top_k != nullptr) return GQE_ERR_UNSUPPORTED;  // uniform top_k only
   if (!(aux_weight >= 0.f) || isinf(aux_weight)) return GQE_ERR_INVALID_ARG;
   const void* need[] = {x, Wq, Wk, Wv, Wo, dy, fws, dx, dWq, dWk, dWv, dWo, ws};
   for (const void* q : need)

@@ -224,10 +224,11 @@ struct AttnBwdArgs {
   const float* dsum;   // [B, H, L]
   void* gall;          // [T, ldg]
   int ldg, kcol, vcol; // dK and dV column blocks (group g at + g*D)
-  const int32_t* idx;  // [B, L, G, k] or NULL (dense: head h's dQ at column h*D)
-  int E, k;
+  const int32_t* idx;  // [B*L, n_grouped] experts by slot, or NULL (dense: head h's dQ at column h*D)
+  int E;
   int B, G, L, H, tiles;
-  int heads_per_group, n_grouped, extra_group;
+  int hbeg[kMaxGroups + 1];  // slot heads hbeg[g] .. hbeg[g+1]-1 read group g (hbeg[G] = n_grouped)
+  int n_grouped, extra_group;
   float scale, scale_log2;
 };
 
@@ -252,7 +253,10 @@ __device__ __forceinline__ typename Frag<T>::type frag_or_zero(const T* p, bool 
 }
 
 __device__ __forceinline__ int group_of(const AttnBwdArgs& a, int h) {
-  return h < a.n_grouped ? h / a.heads_per_group : a.extra_group;
+  if (h >= a.n_grouped) return a.extra_group;
+  int g = 0;
+  while (a.hbeg[g + 1] <= h) ++g;
+  return g;
 }
 
 // 32 rows x D (float) in LDS -> rows of Gall, 16 bytes per store
@@ -300,9 +304,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
-  const int nh = a.heads_per_group + (g == a.extra_group && a.n_grouped < a.H ? 1 : 0);
+  const int nh0 = a.hbeg[g + 1] - a.hbeg[g];  // this group's routed (or dense) slot heads
+  const int nh = nh0 + (g == a.extra_group && a.n_grouped < a.H ? 1 : 0);
   for (int hi = 0; hi < nh; ++hi) {
-    const int h = hi < a.heads_per_group ? g * a.heads_per_group + hi : a.n_grouped;
+    const int h = hi < nh0 ? a.hbeg[g] + hi : a.n_grouped;
     const size_t bh = static_cast<size_t>(b) * a.H + h;
     const T* Q = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.q_heads + h) * L * D;
     const T* dO = static_cast<const T*>(a.dO) + bh * L * D;
@@ -460,8 +465,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     int col = h * D;
     if (a.idx != nullptr) {
       if (h < a.n_grouped) {
-        const int j = h % a.k;
-        const int e = qq < L ? a.idx[((static_cast<size_t>(b) * L + qq) * a.G + g) * a.k + j] : 0;
+        const int e = qq < L ? a.idx[(static_cast<size_t>(b) * L + qq) * a.n_grouped + h] : 0;
         col = (g * a.E + e) * D;
       } else {
         col = a.G * a.E * D;  // the shared head's own W_q rows follow the routed ones
@@ -570,12 +574,13 @@ __global__ __launch_bounds__(64 * DkvWaves<D>::n, 1) void attn_bwd_dkdv_lds_kern
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
-  const int nh = a.heads_per_group + (g == a.extra_group && a.n_grouped < a.H ? 1 : 0);
+  const int nh0 = a.hbeg[g + 1] - a.hbeg[g];  // this group's routed (or dense) slot heads
+  const int nh = nh0 + (g == a.extra_group && a.n_grouped < a.H ? 1 : 0);
   const int q_begin = (kb0 / 64) * 64;
   const int nqb = (L - q_begin + 63) / 64;
   const int last_qb = (L - 1) / 64;
   const int n_iter = nh * nqb;
-  auto head_of = [&](int hi) { return hi < a.heads_per_group ? g * a.heads_per_group + hi : a.n_grouped; };
+  auto head_of = [&](int hi) { return hi < nh0 ? a.hbeg[g] + hi : a.n_grouped; };
   // stage it: query block last_qb - it / nh, slot head it % nh
   auto qblk_of = [&](int it) { return 64 * (last_qb - it / nh); };
   auto issue = [&](int it) {
@@ -809,8 +814,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(AttnBwdArgs a, 
     int col = h * D;
     if (a.idx != nullptr) {
       if (h < a.n_grouped) {
-        const int j = h % a.k;
-        const int e = qq < L ? a.idx[((static_cast<size_t>(b) * L + qq) * a.G + g) * a.k + j] : 0;
+        const int e = qq < L ? a.idx[(static_cast<size_t>(b) * L + qq) * a.n_grouped + h] : 0;
         col = (g * a.E + e) * D;
       } else {
         col = a.G * a.E * D;
@@ -877,14 +881,15 @@ struct RouterBwdArgs {
   const void* x;
   const void* wr;
   const float* bias;
-  const int32_t* idx;     // [T, G, k]
-  const float* dw;        // [T, G*k] routing-weight gradient (NULL: none)
+  const int32_t* idx;     // [T, K] experts by slot (group g at koff[g])
+  const float* dw;        // [T, K] routing-weight gradient (NULL: none)
   const int32_t* counts;  // [B, G, E] forward dispatch counts
   void* gall;             // dr at columns rcol + g*E + e
   int ldg, rcol;
   float* dr;              // [T, G*E] float copy
   float* p_out;           // [T, G*E] in-group probabilities
-  int B, T, d, G, E, k;
+  int B, T, d, G, E;
+  GroupK gk;              // experts selected per group and their slot offsets
   int mode;               // 0 full (renormalized weights), 1 hard, 2 weighted concatenation
   float aux_weight;
 };
@@ -932,7 +937,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
   // gradient on p (aux) and on the selected weights
   if (tid < a.G) {
     const int g = tid;
-    const int32_t* id = a.idx + (static_cast<size_t>(t) * a.G + g) * a.k;
+    const int k = a.gk.kg[g];
+    const size_t so = static_cast<size_t>(t) * a.gk.K + a.gk.koff[g];  // group g's slots of token t
+    const int32_t* id = a.idx + so;
     double* dp = &dpv[g * a.E];
     const double* p = &pr[g * a.E];
     double grad[64];
@@ -942,7 +949,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
       for (int e = 0; e < a.E; ++e) {
         long long c = 0;
         for (int bb = 0; bb < a.B; ++bb) c += a.counts[(static_cast<size_t>(bb) * a.G + g) * a.E + e];
-        const double f = static_cast<double>(c) / (static_cast<double>(a.T) * a.k);
+        const double f = static_cast<double>(c) / (static_cast<double>(a.T) * k);
         dp[e] = static_cast<double>(a.aux_weight) * a.E / a.G * f / a.T;
       }
       double sdp = 0.0;
@@ -952,20 +959,19 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
     if (a.dw != nullptr && a.mode == 0) {
       // w = softmax over the selected logits: dr_j = w_j (dw_j - sum w dw)
       double ws[64], z = 0.0, rmax = logit[g * a.E + id[0]];
-      for (int j = 0; j < a.k; ++j) rmax = fmax(rmax, logit[g * a.E + id[j]]);
-      for (int j = 0; j < a.k; ++j) z += (ws[j] = exp(logit[g * a.E + id[j]] - rmax));
+      for (int j = 0; j < k; ++j) rmax = fmax(rmax, logit[g * a.E + id[j]]);
+      for (int j = 0; j < k; ++j) z += (ws[j] = exp(logit[g * a.E + id[j]] - rmax));
       double s = 0.0;
-      for (int j = 0; j < a.k; ++j) {
+      for (int j = 0; j < k; ++j) {
         ws[j] /= z;
-        s += ws[j] * a.dw[(static_cast<size_t>(t) * a.G + g) * a.k + j];
+        s += ws[j] * a.dw[so + j];
       }
-      for (int j = 0; j < a.k; ++j)
-        grad[id[j]] += ws[j] * (a.dw[(static_cast<size_t>(t) * a.G + g) * a.k + j] - s);
+      for (int j = 0; j < k; ++j) grad[id[j]] += ws[j] * (a.dw[so + j] - s);
     } else if (a.dw != nullptr && a.mode == 2) {
       // the selected experts' p scale their slots: softmax over all E
       double dps[64];
       for (int e = 0; e < a.E; ++e) dps[e] = 0.0;
-      for (int j = 0; j < a.k; ++j) dps[id[j]] = a.dw[(static_cast<size_t>(t) * a.G + g) * a.k + j];
+      for (int j = 0; j < k; ++j) dps[id[j]] = a.dw[so + j];
       double s = 0.0;
       for (int e = 0; e < a.E; ++e) s += p[e] * dps[e];
       for (int e = 0; e < a.E; ++e) grad[e] += p[e] * (dps[e] - s);
@@ -1007,16 +1013,17 @@ __global__ __launch_bounds__(256) void column_sums_kernel(const float* dr, const
   }
 }
 
-// L_aux = (E / G) * sum_{g,e} f[g, e] * P[g, e]
+// L_aux = (E / G) * sum_{g,e} f[g, e] * P[g, e], f[g, e] the share of group
+// g's T*k_g routed slots that went to expert e
 __global__ void aux_loss_kernel(const double* psum, const int32_t* counts, int B, int T, int G,
-                                int E, int k, float* out) {
+                                int E, GroupK gk, float* out) {
   if (threadIdx.x != 0) return;
   double acc = 0.0;
   for (int g = 0; g < G; ++g)
     for (int e = 0; e < E; ++e) {
       long long c = 0;
       for (int bb = 0; bb < B; ++bb) c += counts[(static_cast<size_t>(bb) * G + g) * E + e];
-      acc += (static_cast<double>(c) / (static_cast<double>(T) * k)) * (psum[g * E + e] / T);
+      acc += (static_cast<double>(c) / (static_cast<double>(T) * gk.kg[g])) * (psum[g * E + e] / T);
     }
   *out = static_cast<float>(acc * E / G);
 }
@@ -1054,7 +1061,7 @@ hipError_t launch_attn_bwd_d(const AttnBwdArgs& a, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
-  const int B = p.B, L = p.L, T_ = p.B * p.L, d = p.d, G = p.G, E = p.E, k = p.k, D = p.D;
+  const int B = p.B, L = p.L, T_ = p.B * p.L, d = p.d, G = p.G, E = p.E, D = p.D;
   const int H = p.H;
   hipError_t e;
 #define GQE_TRY(x)                     \
@@ -1145,13 +1152,12 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     a.vcol = p.vcol;
     a.idx = p.idx;
     a.E = E;
-    a.k = k;
     a.B = B;
     a.G = G;
     a.L = L;
     a.H = H;
     a.tiles = tiles;
-    a.heads_per_group = p.heads_per_group;
+    for (int g = 0; g <= G; ++g) a.hbeg[g] = p.hbeg[g];
     a.n_grouped = p.n_grouped;
     a.extra_group = p.extra_group;
     a.scale = p.scale;
@@ -1199,7 +1205,7 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     r.d = d;
     r.G = G;
     r.E = E;
-    r.k = k;
+    r.gk = p.gk;
     r.mode = p.mode;
     r.aux_weight = p.aux_weight;
     hipLaunchKernelGGL(router_bwd_kernel<T>, dim3(T_), dim3(256), 0, stream, r);
@@ -1208,7 +1214,7 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
                        G * E, p.dbr, p.psum);
     GQE_TRY(hipGetLastError());
     hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(64), 0, stream, p.psum, p.counts, B, T_, G,
-                       E, k, p.aux_loss);
+                       E, p.gk, p.aux_loss);
     GQE_TRY(hipGetLastError());
   }
   // 5. transposed copies over tokens (zero past T), then the weight and input gradients

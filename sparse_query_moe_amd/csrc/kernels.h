@@ -132,7 +132,7 @@ struct BwdParams {
   const void* wo;           // [d, ws]
   const void* dy;           // [T, d]
   // the forward workspace
-  const int32_t* idx;       // [T, G, k] or NULL
+  const int32_t* idx;       // [T, K] experts by slot or NULL
   const float* w;           // [T, n_routed] routing weights (p for weighted concatenation) or NULL
   const int32_t* counts;    // [B, G, E] or NULL
   const void* q;            // [B, q_heads, L, D]
@@ -148,11 +148,13 @@ struct BwdParams {
   float *ds, *dsum, *dw, *dr, *p_all;
   double* psum;
   // shapes
-  int B, L, d, G, E, k, D;
+  int B, L, d, G, E, D;
+  GroupK gk;                // experts selected per group and their slot offsets
   int H;                    // attending slot heads
   int q_heads;              // heads allocated in q
   int n_routed;             // slot heads with a routing weight
-  int heads_per_group, n_grouped, extra_group;
+  int hbeg[kMaxGroups + 1];  // slot heads hbeg[g] .. hbeg[g+1]-1 read group g
+  int n_grouped, extra_group;
   int mode;                 // 0 full, 1 hard, 2 weighted concatenation, 3 dense GQA
   int ws;                   // slot width
   int qcols, kcol, vcol, rcol, kcols, kpad;  // column blocks of Gall

@@ -183,3 +183,38 @@ def test_backward_edge_shapes(gqe, L, B, G, E, k, D, dtype):
                               W.to_f64(dy, wl.dtype), G, E, k, D, aux_weight=0.2)
     for key in ("dwo", "dx", "dwq", "dwk", "dwv", "dwr", "dbr"):
         grad_gate(g[key], ref[key], wl.dtype, f"edge {key}")
+
+
+GROUP_K_BWD_CASES = [
+    # L, B, G, E, per-group counts, D, dtype, output mode, aux weight, extra config
+    (150, 2, 3, 3, [1, 3, 2], 32, "fp32", "full", 0.3, dict(shared_kv_group=2)),
+    (150, 2, 3, 3, [2, 1, 3], 32, "fp32", "hard", 0.0, {}),
+    (150, 1, 3, 3, [3, 2, 1], 32, "fp32", "weighted_concat", 0.2, {}),
+    (700, 1, 4, 4, [1, 2, 3, 2], 64, "bf16", "full", 0.01, {}),
+    (333, 2, 4, 8, [6, 1, 1, 2], 64, "bf16", "full", 0.01, {}),   # 7 slot heads on group 0
+]
+
+
+@pytest.mark.parametrize("L,B,G,E,ks,D,dtype,mode,aux,kw", GROUP_K_BWD_CASES)
+def test_gqe_backward_group_k(gqe, L, B, G, E, ks, D, dtype, mode, aux, kw):
+    """Per-group expert counts: every gradient and the auxiliary loss against
+    the oracle's per-group backward."""
+    K = sum(ks)
+    wl = W.Workload("bwd_group_k", B, L, 128, G, E, max(ks), D, dtype, 1.0, 0.05)
+    log(f"[backward group k] {wl} ks={ks} {mode} aux={aux} {kw}")
+    I = W.make_inputs(wl, seed=15, with_gqa=True)
+    rng = np.random.Generator(np.random.PCG64(16))
+    I["wo"] = W._draw(rng, (wl.d_model, (K + (2 if mode == "full" else 0)) * D), 0.05, dtype)
+    dy = draw_dy(wl, seed=17)
+    cfg, fws, g = run_backward(gqe, wl, I, dy, mode=mode, aux_weight=aux, group_top_k=ks, **kw)
+    F = f64_inputs(wl, I)
+    ref = oracle.gqe_backward_group_k(F["x"], F["wq"], F["wk"], F["wv"], F["wr"], F["wo"], F["br"],
+                                      W.to_f64(dy, dtype), G, E, ks, D, output_mode=mode,
+                                      aux_weight=aux, **kw)
+    for key in ("dwo", "dx", "dwq", "dwk", "dwv", "dwr", "dbr"):
+        if mode == "hard" and aux == 0.0 and key in ("dwr", "dbr"):
+            assert np.abs(g[key]).max() == 0.0
+            continue
+        rel, mx = grad_gate(g[key], ref[key], dtype, f"group k {ks} {mode} {key}")
+        log(f"  {key}: rel-L2 {rel:.2e} max/max {mx:.2e}")
+    assert abs(float(g["aux"][0]) - ref["aux_loss"]) <= 1e-5 * max(1.0, abs(ref["aux_loss"]))
