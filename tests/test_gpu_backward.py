@@ -218,3 +218,52 @@ def test_gqe_backward_group_k(gqe, L, B, G, E, ks, D, dtype, mode, aux, kw):
         rel, mx = grad_gate(g[key], ref[key], dtype, f"group k {ks} {mode} {key}")
         log(f"  {key}: rel-L2 {rel:.2e} max/max {mx:.2e}")
     assert abs(float(g["aux"][0]) - ref["aux_loss"]) <= 1e-5 * max(1.0, abs(ref["aux_loss"]))
+
+
+def test_backward_is_deterministic_and_replays_from_a_graph(gqe):
+    """Two gqe_backward calls give the same bits (no atomics anywhere), and so
+    does every replay of a HIP graph captured from one, with eager work and
+    synchronizations between the replays."""
+    wl, I = inputs("l2k")
+    dy = draw_dy(wl)
+    _, _, g1 = run_backward(gqe, wl, I, dy, aux_weight=0.01)
+    _, _, g2 = run_backward(gqe, wl, I, dy, aux_weight=0.01)
+    for key in g1:
+        assert np.array_equal(g1[key], g2[key]), key
+
+    dev = {k: to_dev(v, wl.dtype) for k, v in I.items()}
+    cfg = _cfg(gqe, wl, dev)
+    fws = gqe.alloc_workspace(cfg)
+    y = torch.empty((wl.batch, wl.seq_len, wl.d_model), dtype=cfg.torch_dtype, device="cuda")
+    gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], y, fws)
+    G, E, d = wl.n_groups, wl.n_experts, wl.d_model
+    g = dict(dx=_zeros(wl.batch, wl.seq_len, d), dwq=_zeros(*I["wq"].shape),
+             dwk=_zeros(*I["wk"].shape), dwv=_zeros(*I["wv"].shape), dwr=_zeros(G * E, d),
+             dbr=_zeros(G * E), dwo=_zeros(*I["wo"].shape), aux=_zeros(1))
+    bws = gqe.alloc_backward_workspace(cfg)
+    dyd = to_dev(dy, wl.dtype)
+
+    def bwd():
+        gqe.gqe_backward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], dyd,
+                         0.01, fws, g["dx"], g["dwq"], g["dwk"], g["dwv"], g["dwr"], g["dbr"],
+                         g["dwo"], g["aux"], bws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bwd()
+    for rep in range(3):
+        for t in g.values():
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key, t in g.items():
+            assert np.array_equal(t.cpu().numpy(), g1[key]), f"replay {rep}: {key}"
+        # eager work in between
+        _, _, _ = run_backward(gqe, wl, I, dy, aux_weight=0.01)
+    del graph
