@@ -39,6 +39,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def route_bytes(wl):
+    """Algorithmic HBM bytes of the router: x and W_r read once, idx and w
+    (int32 and float32 per routed slot) written once."""
+    T, es = wl.batch * wl.seq_len, 2 if wl.dtype == W.BF16 else 4
+    return T * wl.d_model * es + wl.n_groups * wl.n_experts * wl.d_model * es + \
+        T * wl.n_groups * wl.top_k * 8
+
+
+def dispatch_bytes(wl):
+    """Algorithmic HBM bytes of the dispatch: idx read once, pos and slot
+    (int32 each) written once per routed row."""
+    rows = wl.batch * wl.seq_len * wl.n_groups * wl.top_k
+    return rows * 4 + rows * 8
+
+
 def stage_work(wl):
     """Algorithmic work of every stage for one step: (kind, amount) with kind
     'flop' (MFMA) or 'byte' (HBM)."""
@@ -217,6 +232,9 @@ def measure(wl, gqe, torch, steps, warmup, graph=True):
         "gqa_stage_ms": {k: round(v, 5) for k, v in st_gqa.items()},
         "attention_tflops": att / 1e12,
         "attention_mfma_frac": att / peak,
+        # the routing kernels against HBM: algorithmic bytes / stage time
+        "route_hbm_tb_per_s": route_bytes(wl) / (st_gqe["route"] * 1e-3) / 1e12,
+        "dispatch_hbm_tb_per_s": dispatch_bytes(wl) / (st_gqe["dispatch"] * 1e-3) / 1e12,
         "gqa_attention_mfma_frac": gwork["attention"][1] / (k_gqa * 1e-3) / peak,
     }
     if graph:
