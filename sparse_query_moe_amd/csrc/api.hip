@@ -462,8 +462,8 @@ namespace {
 
 struct BwdLayout {
   size_t gall, w_t, wo_t, ds, dO, dOt, qt, qs, kt, vr, dsum, dw, dr, p_all, psum, gall_t, x_t,
-      dy_t, s_t, total;
-  int tpad, ws, qcols, kcol, vcol, rcol, kcols, kpad, H, q_heads;
+      dy_t, s_t, dkv_part, total;
+  int tpad, ws, qcols, kcol, vcol, rcol, kcols, kpad, H, q_heads, dkv_split;
 };
 
 BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
@@ -508,6 +508,11 @@ BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
   l.x_t = take(d * tp * es);
   l.dy_t = take(d * tp * es);
   l.s_t = take(ws * tp * es);
+  // float partials of the split dK/dV walk (bf16 short launches only)
+  l.dkv_split = c->dtype == GQE_DTYPE_BF16
+                    ? dkdv_splits(c->batch, c->n_groups, c->seq_len, c->head_dim)
+                    : 1;
+  l.dkv_part = take(l.dkv_split > 1 ? static_cast<size_t>(l.dkv_split) * B * G * L * 2 * D * 4 : 0);
   l.total = off;
   return l;
 }
@@ -588,6 +593,8 @@ int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq
   p.kcols = l.kcols;
   p.kpad = l.kpad;
   p.tpad = l.tpad;
+  p.dkv_split = l.dkv_split;
+  p.dkv_part = at<float>(ws, l.dkv_part);
   p.scale = softmax_scale(c);
   p.aux_weight = dense ? 0.f : aux_weight;
   return hip_status(launch_backward<T>(p, stream));

@@ -230,6 +230,10 @@ struct AttnBwdArgs {
   int hbeg[kMaxGroups + 1];  // slot heads hbeg[g] .. hbeg[g+1]-1 read group g (hbeg[G] = n_grouped)
   int n_grouped, extra_group;
   float scale, scale_log2;
+  // dK/dV with the query walk split over n_split blocks per key block: float
+  // partials [n_split, B, G, L, 2*D] (dK unscaled, then dV), summed afterwards
+  int n_split;
+  float* dkv_part;
 };
 
 // queries scaled by softmax_scale * log2(e) and rounded to the storage type,
@@ -579,12 +583,15 @@ __global__ __launch_bounds__(64 * DkvWaves<D>::n, 1) void attn_bwd_dkdv_lds_kern
   const int q_begin = (kb0 / 64) * 64;
   const int nqb = (L - q_begin + 63) / 64;
   const int last_qb = (L - 1) / 64;
-  const int n_iter = nh * nqb;
+  // this block's part of the walk: stages it_beg .. it_beg + n_iter - 1 of nh*nqb
+  const int n_all = nh * nqb;
+  const int it_beg = static_cast<int>(static_cast<long long>(n_all) * blockIdx.z / a.n_split);
+  const int n_iter = static_cast<int>(static_cast<long long>(n_all) * (blockIdx.z + 1) / a.n_split) - it_beg;
   auto head_of = [&](int hi) { return hi < nh0 ? a.hbeg[g] + hi : a.n_grouped; };
-  // stage it: query block last_qb - it / nh, slot head it % nh
-  auto qblk_of = [&](int it) { return 64 * (last_qb - it / nh); };
+  // stage it: query block last_qb - (it_beg + it) / nh, slot head (it_beg + it) % nh
+  auto qblk_of = [&](int it) { return 64 * (last_qb - (it_beg + it) / nh); };
   auto issue = [&](int it) {
-    const int h = head_of(it % nh), q0 = qblk_of(it);
+    const int h = head_of((it_beg + it) % nh), q0 = qblk_of(it);
     const size_t bh = static_cast<size_t>(b) * a.H + h;
     char* st = smem + (it & 1) * STAGE;
     const T* qsrc = qs + (bh * L + q0) * D;
@@ -610,7 +617,7 @@ __global__ __launch_bounds__(64 * DkvWaves<D>::n, 1) void attn_bwd_dkdv_lds_kern
     }
   };
   auto load_stats = [&](int it, float& ls, float& ds_) {
-    const int h = head_of(it % nh), q = qblk_of(it) + lane;
+    const int h = head_of((it_beg + it) % nh), q = qblk_of(it) + lane;
     const size_t bh = static_cast<size_t>(b) * a.H + h;
     ls = q < L ? a.lse[bh * L + q] : 0.f;
     ds_ = q < L ? a.dsum[bh * L + q] : 0.f;
@@ -690,6 +697,20 @@ __global__ __launch_bounds__(64 * DkvWaves<D>::n, 1) void attn_bwd_dkdv_lds_kern
     lds_barrier();  // every wave is done with this stage before it is refilled
   }
   if (kw0 >= L) return;
+  if (a.n_split > 1) {  // float partials of this part of the walk: key (lane & 31), dims by acc_row
+    if (my_key < L) {
+      float* pp = a.dkv_part +
+                  ((static_cast<size_t>(blockIdx.z) * a.B * a.G + blockIdx.y) * L + my_key) * (2 * D);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          pp[32 * db + acc_row(i, lane)] = dk[db][i];
+          pp[D + 32 * db + acc_row(i, lane)] = dv[db][i];
+        }
+    }
+    return;
+  }
   // dK^T, dV^T: row = dim, column = key -> rows of Gall, through this wave's
   // part of the (now free) ring
   float* buf = reinterpret_cast<float*>(smem) + wave * 32 * (D + 1);
@@ -717,6 +738,41 @@ __global__ __launch_bounds__(64 * DkvWaves<D>::n, 1) void attn_bwd_dkdv_lds_kern
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   store_rows<T, D>(buf, static_cast<T*>(a.gall), a.ldg, lane, rows[wave], cols[wave]);
+}
+
+// dK, dV of the split walk: the n_split float partials of (b, g, key) summed
+// in split order, dK scaled, both rounded once into Gall.  One thread per
+// 8 consecutive dims of one key.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(AttnBwdArgs a) {
+  constexpr int C8 = 2 * D / 8;  // 8-column chunks of a key's [dK | dV] row
+  const size_t n = static_cast<size_t>(a.B) * a.G * a.L * C8;
+  const size_t id = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= n) return;
+  const int c8 = static_cast<int>(id % C8);
+  const size_t bgk = id / C8;  // (b*G + g)*L + key
+  const int key = static_cast<int>(bgk % a.L);
+  const int bg = static_cast<int>(bgk / a.L);
+  const int b = bg / a.G, g = bg % a.G;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  const size_t stride = static_cast<size_t>(a.B) * a.G * a.L * 2 * D;
+  const float* src = a.dkv_part + bgk * 2 * D + 8 * c8;
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const float4 lo = *reinterpret_cast<const float4*>(src + sp * stride);
+    const float4 hi = *reinterpret_cast<const float4*>(src + sp * stride + 4);
+    acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+    acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+  }
+  const bool is_k = 8 * c8 < D;
+  const float f = is_k ? a.scale : 1.f;
+  T v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = from_f32<T>(acc[j] * f);
+  const int col = (is_k ? a.kcol : a.vcol) + g * D + (8 * c8) % D;
+  T* dst = static_cast<T*>(a.gall) + (static_cast<size_t>(b) * a.L + key) * a.ldg + col;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
 }
 
 // grid (ceil(L/128), B*H); wave w owns queries 128x + 32w .. +31; the block
@@ -865,10 +921,16 @@ hipError_t launch_attn_bwd_lds(const AttnBwdArgs& a, const bf16_t* qs, hipStream
   if (attr1 != hipSuccess) return attr1;
   if (attr2 != hipSuccess) return attr2;
   hipLaunchKernelGGL((attn_bwd_dkdv_lds_kernel<D>),
-                     dim3((a.L + 32 * NW - 1) / (32 * NW), a.B * a.G), dim3(64 * NW), lds_kv,
-                     stream, a, qs);
+                     dim3((a.L + 32 * NW - 1) / (32 * NW), a.B * a.G, a.n_split), dim3(64 * NW),
+                     lds_kv, stream, a, qs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.n_split > 1) {
+    const size_t n = static_cast<size_t>(a.B) * a.G * a.L * (2 * D / 8);
+    hipLaunchKernelGGL((dkv_reduce_kernel<bf16_t, D>), dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((attn_bwd_dq_lds_kernel<D>), dim3((a.L + 127) / 128, a.B * a.H), dim3(256),
                      lds_q, stream, a, qs);
   return hipGetLastError();
@@ -1059,6 +1121,16 @@ hipError_t launch_attn_bwd_d(const AttnBwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+int dkdv_splits(int B, int G, int L, int D) {
+  // bf16 dK/dV blocks of 256 keys (128 at d_h 128): below one block per
+  // compute unit, the query walk of each key block is split so that the
+  // blocks cover the chip
+  const int keys = D >= 128 ? 128 : 256;
+  const long long blocks = static_cast<long long>((L + keys - 1) / keys) * B * G;
+  if (blocks <= 0 || blocks >= cu_count()) return 1;
+  return static_cast<int>(std::min<long long>(8, (cu_count() + blocks - 1) / blocks));
+}
+
 template <typename T>
 hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
   const int B = p.B, L = p.L, T_ = p.B * p.L, d = p.d, G = p.G, E = p.E, D = p.D;
@@ -1159,6 +1231,8 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     a.tiles = tiles;
     for (int g = 0; g <= G; ++g) a.hbeg[g] = p.hbeg[g];
     a.n_grouped = p.n_grouped;
+    a.n_split = sizeof(T) == 2 ? p.dkv_split : 1;
+    a.dkv_part = p.dkv_part;
     a.extra_group = p.extra_group;
     a.scale = p.scale;
     a.scale_log2 = p.scale * 1.4426950408889634f;

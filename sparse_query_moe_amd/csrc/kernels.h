@@ -18,6 +18,8 @@ constexpr int kGatherRows = 128;
 // is the non-uniform variant the pages list as future work (pptc.cn,
 // section 6).
 constexpr int kMaxGroups = 64;
+// compute units of the device (read once)
+int cu_count();
 struct GroupK {
   int K;
   int kmax;
@@ -159,8 +161,12 @@ struct BwdParams {
   int ws;                   // slot width
   int qcols, kcol, vcol, rcol, kcols, kpad;  // column blocks of Gall
   int tpad;                 // tokens rounded up to 64
+  int dkv_split;            // dK/dV query-walk splits (dkdv_splits), 1: none
+  float* dkv_part;          // [dkv_split, B, G, L, 2*D] float partials when split
   float scale, aux_weight;
 };
+// dK/dV query-walk splits for a bf16 backward of B x L tokens, G groups, d_h D
+int dkdv_splits(int B, int G, int L, int D);
 template <typename T>
 hipError_t launch_backward(const BwdParams& p, hipStream_t stream);
 
