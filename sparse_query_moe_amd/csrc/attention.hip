@@ -23,7 +23,9 @@
 //   chunks, one barrier per tile).  The running maximum is only raised when a
 //   tile exceeds it by more than 2^8: the stale maximum keeps every
 //   probability <= 256, and since the same maximum scales numerator and
-//   denominator the result is unchanged.
+//   denominator the result is unchanged.  It is subtracted inside the score
+//   MFMA chain (one extra K step of a unit key column against -m), so it is
+//   held as an operand-type value, rounded up.
 //   Blocks are issued heaviest query block first to shorten the causal tail.
 #include <math.h>
 
@@ -37,6 +39,36 @@ namespace gqe {
 namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+// The running maximum enters the score MFMA as one more K step: a unit column
+// of K against -m in the query's row, so the accumulator starts from zero and
+// S^T - m costs no VALU work.  The maximum is kept representable in the
+// operand type (rounded up, so probabilities never exceed the bound).
+template <typename T> struct ShiftOp;
+template <> struct ShiftOp<bf16_t> {
+  typedef bf16x8 type;
+  static __device__ __forceinline__ type make(float v, int half) {
+    type r = {};
+    r[0] = static_cast<__bf16>(half == 0 ? v : 0.f);
+    return r;
+  }
+  static __device__ __forceinline__ f32x16 mma(const type& unit, const type& nm) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(unit, nm, f32x16{}, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float round_up(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (!(u >> 31)) u += 0xffffu;
+    return __uint_as_float(u & 0xffff0000u);
+  }
+};
+template <> struct ShiftOp<float> {
+  typedef float type;
+  static __device__ __forceinline__ type make(float v, int half) { return half == 0 ? v : 0.f; }
+  static __device__ __forceinline__ f32x16 mma(type unit, type nm) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(unit, nm, f32x16{}, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float round_up(float x) { return x; }
+};
 
 
 // QW query waves of 32*QB rows each share every K/V tile; NS groups of QW
@@ -171,6 +203,8 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   int qrow[QB];
   F qf[QB][S::NKS];
   float m_run[QB], l_run[QB];
+  typename ShiftOp<T>::type nm[QB];
+  const typename ShiftOp<T>::type unit = ShiftOp<T>::make(1.f, half);
   f32x16 o[QB][S::NDB];
   {
     F k0[S::NKS];
@@ -191,7 +225,8 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
         }
         dot += dot8(qf[qb][ks], k0[ks]);
       }
-      m_run[qb] = dot + __shfl_xor(dot, 32, 64);
+      m_run[qb] = ShiftOp<T>::round_up(dot + __shfl_xor(dot, 32, 64));
+      nm[qb] = ShiftOp<T>::make(-m_run[qb], half);
       l_run[qb] = 0.f;
 #pragma unroll
       for (int db = 0; db < S::NDB; ++db)
@@ -206,29 +241,30 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   // 1's softmax overlaps block 0's O^T update.
   auto tile = [&](const char* Ks, const char* Vs, int j0, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    // S^T - m: the accumulator starts at -m_run, so exp2 applies directly
-    // (K fragments are read per block too: LDS bandwidth is cheaper than the
-    // registers that would hold them)
-    f32x16 s[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    // S^T - m of one query block (K fragments are read per block: LDS
+    // bandwidth is cheaper than the registers that would hold them)
+    auto scores = [&](int qb, f32x16 (&sq)[2]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[qb][kb] = splat16(-m_run[qb]);
+        sq[kb] = ShiftOp<T>::mma(unit, nm[qb]);
 #pragma unroll
         for (int ks = 0; ks < S::NKS; ++ks)
-          mma32(s[qb][kb], LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half),
+          mma32(sq[kb], LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half),
                 qf[qb][ks]);
       }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
       if constexpr (MASK) {  // drop keys after the query
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (j0 + 32 * kb + acc_row(i, lane) > qrow[qb]) s[qb][kb][i] = -INFINITY;
+            if (j0 + 32 * kb + acc_row(i, lane) > qrow[qb]) sq[kb][i] = -INFINITY;
       }
+    };
+    f32x16 s[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) scores(qb, s[qb]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       // the half-row maximum decides (any lane over the threshold), so the
       // exchange with lane l ^ 32 is only paid when the maximum is raised
       float v = s[qb][0][0];
@@ -237,10 +273,12 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
 #pragma unroll
         for (int i = 0; i < 16; ++i) v = fmaxf(v, s[qb][kb][i]);
       if (__any(v > kRescaleThreshold)) {  // raise the running maximum (wave-uniform branch)
-        const float mx = fmaxf(v, __shfl_xor(v, 32, 64));  // both halves of a row agree
-        const float sh = fmaxf(mx, 0.f);
+        const float mx = fmaxf(fmaxf(v, __shfl_xor(v, 32, 64)), 0.f);
+        const float m_new = ShiftOp<T>::round_up(m_run[qb] + mx);
+        const float sh = m_new - m_run[qb];
         const float alpha = __builtin_amdgcn_exp2f(-sh);
-        m_run[qb] += sh;
+        m_run[qb] = m_new;
+        nm[qb] = ShiftOp<T>::make(-m_new, half);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < S::NDB; ++db)
