@@ -462,8 +462,9 @@ namespace {
 
 struct BwdLayout {
   size_t gall, w_t, wo_t, ds, dO, dOt, qt, qs, kt, vr, dsum, dw, dr, p_all, psum, gall_t, x_t,
-      dy_t, s_t, dkv_part, total;
+      dy_t, s_t, dkv_part, gemm_part, total;
   int tpad, ws, qcols, kcol, vcol, rcol, kcols, kpad, H, q_heads, dkv_split;
+  bool has_gemm_part;
 };
 
 BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
@@ -513,6 +514,17 @@ BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
                     ? dkdv_splits(c->batch, c->n_groups, c->seq_len, c->head_dim)
                     : 1;
   l.dkv_part = take(l.dkv_split > 1 ? static_cast<size_t>(l.dkv_split) * B * G * L * 2 * D * 4 : 0);
+  // float partials of the split-K weight-gradient products (dW_O = dy^T s and
+  // [dW_q; dW_k; dW_v; dW_r] = Gall^T x), when their tiles alone leave
+  // compute units idle
+  {
+    const int dd = static_cast<int>(d), tpi = l.tpad;
+    const int s_o = nt_gemm_splits(dd, l.ws, tpi), s_w = nt_gemm_splits(l.kcols, dd, tpi);
+    const size_t part = std::max(s_o > 1 ? static_cast<size_t>(s_o) * d * ws : 0,
+                                 s_w > 1 ? static_cast<size_t>(s_w) * l.kcols * d : 0);
+    l.gemm_part = part > 0 ? take(part * 4) : 0;
+    l.has_gemm_part = part > 0;
+  }
   l.total = off;
   return l;
 }
@@ -595,6 +607,7 @@ int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq
   p.tpad = l.tpad;
   p.dkv_split = l.dkv_split;
   p.dkv_part = at<float>(ws, l.dkv_part);
+  p.gemm_part = l.has_gemm_part ? at<float>(ws, l.gemm_part) : nullptr;
   p.scale = softmax_scale(c);
   p.aux_weight = dense ? 0.f : aux_weight;
   return hip_status(launch_backward<T>(p, stream));

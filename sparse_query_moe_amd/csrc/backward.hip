@@ -1312,6 +1312,8 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     g.K = tp;
     g.nseg = 1;
     g.seg[0] = NtSeg{p.dwo, 0, d, p.ws, 0};
+    g.part = p.gemm_part;
+    g.splits = p.gemm_part != nullptr ? nt_gemm_splits(g.M, g.N, g.K) : 1;
     GQE_TRY(launch_nt_gemm<T>(g, stream));
   }
   {
@@ -1341,6 +1343,8 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     g.seg[1] = NtSeg{p.dwk, p.kcol, G * D, d, 0};
     g.seg[2] = NtSeg{p.dwv, p.vcol, G * D, d, 0};
     if (p.wr != nullptr) g.seg[3] = NtSeg{p.dwr, p.rcol, G * E, d, 0};
+    g.part = p.gemm_part;
+    g.splits = p.gemm_part != nullptr ? nt_gemm_splits(g.M, g.N, g.K) : 1;
     GQE_TRY(launch_nt_gemm<T>(g, stream));
   }
 #undef GQE_TRY

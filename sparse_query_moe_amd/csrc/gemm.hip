@@ -24,10 +24,12 @@
 //                       sparsity of pptc.cn section 5).
 //   output projection : slot vectors times W_O (hotpaper.ai: W_O of k*G+2
 //                       slots), row-major.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
 #include "device_common.h"
+
 #include "kernels.h"
 
 namespace gqe {
@@ -428,21 +430,28 @@ __global__ __launch_bounds__(256) void out_proj_kernel(OutArgs args) {
 template <typename T, class S>
 struct NtProb {
   const NtArgs& a;
-  int m0, n0, K;
-  __device__ NtProb(const NtArgs& args, int m0_, int n0_) : a(args), m0(m0_), n0(n0_), K(args.K) {}
+  int m0, n0, K, z, k0;
+  __device__ NtProb(const NtArgs& args, int m0_, int n0_, int z_)
+      : a(args), m0(m0_), n0(n0_), z(z_), k0(args.splits > 1 ? z_ * args.kchunk : 0) {
+    K = args.splits > 1 ? min(args.kchunk, args.K - k0) : args.K;
+  }
   __device__ __forceinline__ const T* a_any() const { return static_cast<const T*>(a.a); }
   __device__ __forceinline__ const T* b_any() const { return static_cast<const T*>(a.b); }
   __device__ __forceinline__ const T* a_row(int r) const {
     const int m = m0 + r;
-    return m < a.M ? static_cast<const T*>(a.a) + static_cast<size_t>(m) * a.lda : nullptr;
+    return m < a.M ? static_cast<const T*>(a.a) + static_cast<size_t>(m) * a.lda + k0 : nullptr;
   }
   __device__ __forceinline__ const T* b_row(int n) const {
     const int c = n0 + n;
-    return c < a.N ? static_cast<const T*>(a.b) + static_cast<size_t>(c) * a.ldb : nullptr;
+    return c < a.N ? static_cast<const T*>(a.b) + static_cast<size_t>(c) * a.ldb + k0 : nullptr;
   }
   __device__ __forceinline__ void store_acc(int r, int c, float v) const {
     const int m = m0 + r, n = n0 + c;
     if (m >= a.M || n >= a.N) return;
+    if (a.splits > 1) {
+      a.part[(static_cast<size_t>(z) * a.M + m) * a.N + n] = v;
+      return;
+    }
     for (int i = 0; i < a.nseg; ++i) {
       const NtSeg& sg = a.seg[i];
       if (m >= sg.row_begin && m < sg.row_begin + sg.rows) {
@@ -457,8 +466,26 @@ struct NtProb {
 template <typename T, class S>
 __global__ __launch_bounds__(256) void nt_gemm_kernel(NtArgs args) {
   extern __shared__ __align__(16) char smem[];
-  NtProb<T, S> prob(args, blockIdx.y * S::BM, blockIdx.x * S::BN);
+  NtProb<T, S> prob(args, blockIdx.y * S::BM, blockIdx.x * S::BN, blockIdx.z);
   gemm_block<T, S>(prob, smem);
+}
+
+// the split-K partials summed in split order, then stored like store_acc
+__global__ __launch_bounds__(256) void nt_split_reduce_kernel(NtArgs a, int zs) {
+  const size_t mn = static_cast<size_t>(a.M) * a.N;
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= mn) return;
+  float v = a.part[i];
+  for (int z = 1; z < zs; ++z) v += a.part[z * mn + i];
+  const int m = static_cast<int>(i / a.N), n = static_cast<int>(i % a.N);
+  for (int s = 0; s < a.nseg; ++s) {
+    const NtSeg& sg = a.seg[s];
+    if (m >= sg.row_begin && m < sg.row_begin + sg.rows) {
+      float* o = sg.out + static_cast<size_t>(m - sg.row_begin) * sg.ldo + n;
+      *o = sg.accumulate ? *o + v : v;
+      return;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -545,10 +572,13 @@ inline dim3 tile_grid(Tiles t, int M, int N) {
   const int bm = (t == Tiles::k64 || t == Tiles::k64Deep) ? 64 : 128;
   return dim3((N + 127) / 128, (M + bm - 1) / bm);
 }
-#define GQE_LAUNCH_TILED(KERNEL, T, M, N, stream, args)                                        \
+#define GQE_LAUNCH_TILED(KERNEL, T, M, N, stream, args) \
+  GQE_LAUNCH_TILED_Z(KERNEL, T, M, N, 1, stream, args)
+#define GQE_LAUNCH_TILED_Z(KERNEL, T, M, N, Z, stream, args)                                   \
   do {                                                                                       \
     const Tiles t_ = choose_tiles(M, N);                                                     \
-    const dim3 g_ = tile_grid(t_, M, N);                                                     \
+    dim3 g_ = tile_grid(t_, M, N);                                                           \
+    g_.z = (Z);                                                                              \
     switch (t_) {                                                                            \
       case Tiles::k64: {                                                                     \
         typedef GemmShape<T, 64, 128, 2, 2> S_;                                              \
@@ -645,12 +675,54 @@ hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K
   GQE_LAUNCH_TILED(out_proj_kernel, T, M, N, stream, a);
 }
 
+// The split count s minimizes the rounds of blocks over the compute units per
+// unit of work, ceil(tiles * s / cu) / s, plus a small charge per split for
+// writing and summing the partials; every split keeps at least 1024 of K.
+int nt_gemm_splits(int M, int N, int K) {
+  const dim3 g = tile_grid(choose_tiles(M, N), M, N);
+  const long long tiles = static_cast<long long>(g.x) * g.y;
+  const long long cu = cu_count();
+  if (tiles == 0 || tiles >= cu || K < 2048) return 1;
+  int best = 1;
+  double best_cost = 1.0 + 0.02;
+  for (int s = 2; s <= 8 && K / s >= 1024; ++s) {
+    const double cost = static_cast<double>((tiles * s + cu - 1) / cu) / s + 0.02 * s;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
 template <typename T>
-hipError_t launch_nt_gemm(const NtArgs& a, hipStream_t stream) {
+static hipError_t launch_nt_tiles(const NtArgs& a, int zs, hipStream_t stream) {
+  GQE_LAUNCH_TILED_Z(nt_gemm_kernel, T, a.M, a.N, zs, stream, a);
+}
+
+// An NT product with float32 results.  With a.splits > 1 (and a.part), K is
+// cut into chunks of whole LDS steps, one per grid layer, and a second kernel
+// sums the partials in chunk order (deterministic).
+template <typename T>
+hipError_t launch_nt_gemm(const NtArgs& args, hipStream_t stream) {
   typedef GemmShape<T, 128, 128, 2, 2> S;
-  if (a.M == 0 || a.N == 0) return hipSuccess;
-  if (a.K % S::BKE != 0 || a.nseg < 1 || a.nseg > 4) return hipErrorInvalidValue;
-  GQE_LAUNCH_TILED(nt_gemm_kernel, T, a.M, a.N, stream, a);
+  if (args.M == 0 || args.N == 0) return hipSuccess;
+  if (args.K % S::BKE != 0 || args.nseg < 1 || args.nseg > 4) return hipErrorInvalidValue;
+  NtArgs a = args;
+  if (a.splits <= 1 || a.part == nullptr || a.K == 0) {
+    a.splits = 1;
+    return launch_nt_tiles<T>(a, 1, stream);
+  }
+  a.kchunk = ((a.K + a.splits - 1) / a.splits + S::BKE - 1) / S::BKE * S::BKE;
+  const int zs = (a.K + a.kchunk - 1) / a.kchunk;
+  a.splits = zs;
+  if (zs <= 1) return launch_nt_tiles<T>(a, 1, stream);
+  const hipError_t e = launch_nt_tiles<T>(a, zs, stream);
+  if (e != hipSuccess) return e;
+  const size_t mn = static_cast<size_t>(a.M) * a.N;
+  hipLaunchKernelGGL(nt_split_reduce_kernel, dim3(static_cast<unsigned>((mn + 255) / 256)),
+                     dim3(256), 0, stream, a, zs);
+  return hipGetLastError();
 }
 
 template <typename T>

@@ -118,7 +118,15 @@ struct NtArgs {
   int M, N, K;
   int nseg;
   NtSeg seg[4];
+  // split K: with splits > 1, block z multiplies K elements z*kchunk .. and
+  // writes float partials part[z][M][N], which are then summed in z order
+  // into the segments (launch_nt_gemm sets kchunk)
+  float* part;
+  int splits, kchunk;
 };
+// K splits for an NT product whose output tiles alone would leave compute
+// units idle (1: no split); part must then hold splits * M * N floats
+int nt_gemm_splits(int M, int N, int K);
 template <typename T>
 hipError_t launch_nt_gemm(const NtArgs& a, hipStream_t stream);
 
@@ -163,6 +171,7 @@ struct BwdParams {
   int tpad;                 // tokens rounded up to 64
   int dkv_split;            // dK/dV query-walk splits (dkdv_splits), 1: none
   float* dkv_part;          // [dkv_split, B, G, L, 2*D] float partials when split
+  float* gemm_part;         // split-K partials of the weight-gradient products
   float scale, aux_weight;
 };
 // dK/dV query-walk splits for a bf16 backward of B x L tokens, G groups, d_h D
