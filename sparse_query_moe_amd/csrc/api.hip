@@ -462,8 +462,8 @@ namespace {
 
 struct BwdLayout {
   size_t gall, w_t, wo_t, ds, dO, dOt, qt, qs, kt, vr, dsum, dw, dr, p_all, psum, gall_t, x_t,
-      dy_t, s_t, dkv_part, gemm_part, total;
-  int tpad, ws, qcols, kcol, vcol, rcol, kcols, kpad, H, q_heads, dkv_split;
+      dy_t, s_t, dkv_part, gemm_part, dq_part, total;
+  int tpad, ws, qcols, kcol, vcol, rcol, kcols, kpad, H, q_heads, dkv_split, dq_split;
   bool has_gemm_part;
 };
 
@@ -525,6 +525,9 @@ BwdLayout make_bwd_layout(const gqe_config* c, bool dense) {
     l.gemm_part = part > 0 ? take(part * 4) : 0;
     l.has_gemm_part = part > 0;
   }
+  // float partials of the split dQ walk (bf16 short launches only)
+  l.dq_split = c->dtype == GQE_DTYPE_BF16 ? dq_splits(c->batch, l.H, c->seq_len) : 1;
+  l.dq_part = take(l.dq_split > 1 ? static_cast<size_t>(l.dq_split) * B * H * L * D * 4 : 0);
   l.total = off;
   return l;
 }
@@ -608,6 +611,8 @@ int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq
   p.dkv_split = l.dkv_split;
   p.dkv_part = at<float>(ws, l.dkv_part);
   p.gemm_part = l.has_gemm_part ? at<float>(ws, l.gemm_part) : nullptr;
+  p.dq_split = l.dq_split;
+  p.dq_part = at<float>(ws, l.dq_part);
   p.scale = softmax_scale(c);
   p.aux_weight = dense ? 0.f : aux_weight;
   return hip_status(launch_backward<T>(p, stream));

@@ -234,6 +234,10 @@ struct AttnBwdArgs {
   // partials [n_split, B, G, L, 2*D] (dK unscaled, then dV), summed afterwards
   int n_split;
   float* dkv_part;
+  // dQ with the key walk split over n_qsplit blocks per query block: float
+  // partials [n_qsplit, B, H, L, D], already scaled, summed afterwards
+  int n_qsplit;
+  float* dq_part;
 };
 
 // queries scaled by softmax_scale * log2(e) and rounded to the storage type,
@@ -775,8 +779,49 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(AttnBwdArgs a) {
   *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
 }
 
-// grid (ceil(L/128), B*H); wave w owns queries 128x + 32w .. +31; the block
-// walks the 64-key blocks up to its last query.
+// dQ of the split walk: the n_qsplit float partials of (b, h, query) summed
+// in split order and rounded once into the query's column block of Gall.
+// One thread per 8 consecutive dims of one query.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(AttnBwdArgs a) {
+  constexpr int C8 = D / 8;
+  const size_t n = static_cast<size_t>(a.B) * a.H * a.L * C8;
+  const size_t id = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= n) return;
+  const int c8 = static_cast<int>(id % C8);
+  const size_t bhq = id / C8;  // (b*H + h)*L + query
+  const int q = static_cast<int>(bhq % a.L);
+  const int bh = static_cast<int>(bhq / a.L);
+  const int b = bh / a.H, h = bh % a.H;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  const size_t stride = static_cast<size_t>(a.B) * a.H * a.L * D;
+  const float* src = a.dq_part + bhq * D + 8 * c8;
+  for (int sp = 0; sp < a.n_qsplit; ++sp) {
+    const float4 lo = *reinterpret_cast<const float4*>(src + sp * stride);
+    const float4 hi = *reinterpret_cast<const float4*>(src + sp * stride + 4);
+    acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+    acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+  }
+  int col = h * D;  // the dense baseline: head h's own block
+  if (a.idx != nullptr) {
+    if (h < a.n_grouped) {
+      const int e = a.idx[(static_cast<size_t>(b) * a.L + q) * a.n_grouped + h];
+      col = (group_of(a, h) * a.E + e) * D;
+    } else {
+      col = a.G * a.E * D;
+    }
+  }
+  T v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = from_f32<T>(acc[j]);
+  T* dst = static_cast<T*>(a.gall) + (static_cast<size_t>(b) * a.L + q) * a.ldg + col + 8 * c8;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
+}
+
+// grid (ceil(L/128), B*H, n_qsplit); wave w owns queries 128x + 32w .. +31;
+// the block walks (its share of) the 64-key blocks up to its last query.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(AttnBwdArgs a, const bf16_t* qs) {
   typedef bf16_t T;
@@ -814,7 +859,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(AttnBwdArgs a, 
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
-  const int n_iter = (min(qb0 + 128, L) + 63) / 64;  // key blocks up to the block's last query
+  // key blocks up to the block's last query; split z of n_qsplit walks its
+  // contiguous share of them
+  const int n_all = (min(qb0 + 128, L) + 63) / 64;
+  const int it_beg = n_all * static_cast<int>(blockIdx.z) / a.n_qsplit;
+  const int it_end = n_all * (static_cast<int>(blockIdx.z) + 1) / a.n_qsplit;
   const int w_last = min(qw0 + 31, L - 1);
   auto issue = [&](int it) {
     const int k0 = 64 * it;
@@ -823,9 +872,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(AttnBwdArgs a, 
     dma_rows<D>(Vg + static_cast<size_t>(k0) * D, L - k0, st + S::RT, wave, lane);
     dma_tile<D>(Kt + static_cast<size_t>(it) * D * 64, st + 2 * S::RT, wave, lane);
   };
-  issue(0);
-  for (int it = 0; it < n_iter; ++it) {
-    const bool more = it + 1 < n_iter;
+  if (it_beg < it_end) issue(it_beg);
+  for (int it = it_beg; it < it_end; ++it) {
+    const bool more = it + 1 < it_end;
     if (more) issue(it + 1);
     dma_barrier(more ? DMA_OPS : 0);
     const char* st = smem + (it & 1) * STAGE;
@@ -863,6 +912,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(AttnBwdArgs a, 
     lds_barrier();  // every wave is done with this stage before it is refilled
   }
   if (qw0 >= L) return;
+  if (a.n_qsplit > 1) {  // float partials: query (lane & 31), 4 consecutive dims per store
+    if (!qok) return;
+    float* pp = a.dq_part + ((static_cast<size_t>(blockIdx.z) * a.B * a.H + bh) * L + my_q) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; i += 4)
+        *reinterpret_cast<float4*>(pp + 32 * db + acc_row(i, lane)) =
+            make_float4(dq[db][i] * a.scale, dq[db][i + 1] * a.scale, dq[db][i + 2] * a.scale,
+                        dq[db][i + 3] * a.scale);
+    return;
+  }
   float* buf = reinterpret_cast<float*>(smem) + wave * 32 * (D + 1);
   if (lane < 32) {
     const int qq = qw0 + lane;
@@ -931,9 +992,16 @@ hipError_t launch_attn_bwd_lds(const AttnBwdArgs& a, const bf16_t* qs, hipStream
                        dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((attn_bwd_dq_lds_kernel<D>), dim3((a.L + 127) / 128, a.B * a.H), dim3(256),
-                     lds_q, stream, a, qs);
-  return hipGetLastError();
+  hipLaunchKernelGGL((attn_bwd_dq_lds_kernel<D>), dim3((a.L + 127) / 128, a.B * a.H, a.n_qsplit),
+                     dim3(256), lds_q, stream, a, qs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.n_qsplit > 1) {
+    const size_t n = static_cast<size_t>(a.B) * a.H * a.L * (D / 8);
+    hipLaunchKernelGGL((dq_reduce_kernel<bf16_t, D>), dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, stream, a);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 // ---------------------------------------------------------------------------
@@ -1131,6 +1199,16 @@ int dkdv_splits(int B, int G, int L, int D) {
   return static_cast<int>(std::min<long long>(8, (cu_count() + blocks - 1) / blocks));
 }
 
+int dq_splits(int B, int H, int L) {
+  // bf16 dQ blocks of 128 queries, two per compute unit: below one block per
+  // compute unit, each block's key walk is split so that the blocks fill
+  // both slots of every unit (the longest walk, the last query block's,
+  // shrinks by the same factor)
+  const long long blocks = static_cast<long long>((L + 127) / 128) * B * H;
+  if (blocks <= 0 || blocks >= cu_count()) return 1;
+  return static_cast<int>(std::max<long long>(1, std::min<long long>(4, 2LL * cu_count() / blocks)));
+}
+
 template <typename T>
 hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
   const int B = p.B, L = p.L, T_ = p.B * p.L, d = p.d, G = p.G, E = p.E, D = p.D;
@@ -1233,6 +1311,8 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     a.n_grouped = p.n_grouped;
     a.n_split = sizeof(T) == 2 ? p.dkv_split : 1;
     a.dkv_part = p.dkv_part;
+    a.n_qsplit = sizeof(T) == 2 ? p.dq_split : 1;
+    a.dq_part = p.dq_part;
     a.extra_group = p.extra_group;
     a.scale = p.scale;
     a.scale_log2 = p.scale * 1.4426950408889634f;

@@ -172,10 +172,14 @@ struct BwdParams {
   int dkv_split;            // dK/dV query-walk splits (dkdv_splits), 1: none
   float* dkv_part;          // [dkv_split, B, G, L, 2*D] float partials when split
   float* gemm_part;         // split-K partials of the weight-gradient products
+  int dq_split;             // dQ key-walk splits (dq_splits), 1: none
+  float* dq_part;           // [dq_split, B, H, L, D] float partials when split
   float scale, aux_weight;
 };
 // dK/dV query-walk splits for a bf16 backward of B x L tokens, G groups, d_h D
 int dkdv_splits(int B, int G, int L, int D);
+// dQ key-walk splits for a bf16 backward of B x L tokens over H slot heads
+int dq_splits(int B, int H, int L);
 template <typename T>
 hipError_t launch_backward(const BwdParams& p, hipStream_t stream);
 
