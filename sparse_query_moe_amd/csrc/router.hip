@@ -100,13 +100,33 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     __syncthreads();
   }
 
-  // selection: one thread per (token, group)
-  for (int task = tid; task < kTok * G; task += 256) {
-    const int tt = task / G, g = task % G;
-    const int gt = t0 + tt;
-    if (gt >= n_tokens) continue;
-    select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out, w_out,
-                 static_cast<size_t>(gt) * gk.K + gk.koff[g]);
+  // selection, one thread per (token, expert): the expert's rank inside its
+  // group (experts with a larger logit, or an equal one and a lower index)
+  // and exp(r - max) once; then each selected expert's weight divides by the
+  // sum over its group's selected experts (all E when !renorm) in expert order
+  __shared__ double ex[kTok][65];
+  __shared__ int rk[kTok][65];
+  for (int task = tid; task < kTok * GE; task += 256) {
+    const int tt = task / GE, ge = task % GE, g = ge / E, e = ge % E;
+    const double* r = &logit[tt][g * E];
+    double rmax = r[0];
+    for (int f = 1; f < E; ++f) rmax = fmax(rmax, r[f]);
+    int rank = 0;
+    for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
+    ex[tt][ge] = exp(r[e] - rmax);
+    rk[tt][ge] = rank;
+  }
+  __syncthreads();
+  for (int task = tid; task < kTok * GE; task += 256) {
+    const int tt = task / GE, ge = task % GE, g = ge / E, e = ge % E;
+    const int gt = t0 + tt, k = gk.kg[g], rank = rk[tt][ge];
+    if (gt >= n_tokens || rank >= k) continue;
+    double z = 0.0;
+    for (int f = 0; f < E; ++f)
+      if (rk[tt][g * E + f] < k || !renorm) z += ex[tt][g * E + f];
+    const size_t o = static_cast<size_t>(gt) * gk.K + gk.koff[g];  // group g's slots of token gt
+    idx_out[o + rank] = e;
+    w_out[o + rank] = static_cast<float>(ex[tt][ge] / z);
   }
 }
 

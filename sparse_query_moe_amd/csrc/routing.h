@@ -1,5 +1,6 @@
-// Device-side routing helpers shared by the prefill router and the decode
-// step's router blocks (pptc.cn review, section 7: softmax inside the group
+// Device-side routing helpers: float64 widening shared by the prefill router
+// and the decode step's router blocks, and the decode step's per-token
+// routing (pptc.cn review, section 7: softmax inside the group
 // first, then top-k; section 5: every group takes part; hotpaper.ai,
 // technical approach: renormalized scoring).  Logits are float64: products of
 // bf16/fp32 inputs are exact in float64, so the only rounding is in the sums.
@@ -32,36 +33,13 @@ __device__ __forceinline__ void widen8(const uint4 (&r)[U4Count<T>::n], double (
   }
 }
 
-// In-group selection from the E float64 logits r of one (token, group): the k
-// largest, best first (rank of e = experts with a larger logit, or an equal
-// one and a lower index), and their weights exp(r_e - max) / z with z summed
-// over the selected k (renormalized) or over all E (the softmax itself).
-__device__ __forceinline__ void select_group(const double* r, int E, int k, int renorm,
-                                             int32_t* idx_out, float* w_out, size_t o) {
-  double rmax = r[0];
-  for (int e = 1; e < E; ++e) rmax = fmax(rmax, r[e]);
-  double z = 0.0;
-  for (int e = 0; e < E; ++e) {
-    int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
-    if (rank < k || !renorm) z += exp(r[e] - rmax);
-  }
-  for (int e = 0; e < E; ++e) {
-    int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
-    if (rank < k) {
-      idx_out[o + rank] = e;
-      w_out[o + rank] = static_cast<float>(exp(r[e] - rmax) / z);
-    }
-  }
-}
-
 // One token per block of 256 threads (the decode step's few tokens): wave w
 // forms the logits of experts w, w+4, ...; lane l accumulates model dims
 // 8l + 512i in float64 and the wave sums its lanes in a fixed butterfly
 // order.  Then one thread per expert takes its rank and exp(r - max); the
 // weights divide by the sum over the group's selected experts (all E when
-// !renorm) in expert order, the same operations as select_group.
+// !renorm) in expert order, the same operations as the prefill router's
+// selection.
 template <typename T>
 __device__ __forceinline__ void route_token_block(const T* __restrict__ x, const T* __restrict__ wr,
                                                   const float* __restrict__ bias,
