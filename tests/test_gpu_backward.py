@@ -169,6 +169,11 @@ def test_gqa_backward(gqe, name):
     (333, 2, 2, 3, 2, 32, "bf16"),
     (200, 1, 2, 2, 1, 128, "bf16"),
     (600, 1, 4, 4, 2, 64, "bf16"),     # several 256-key blocks, a ragged last one
+    # few output tiles and a long token axis: the weight-gradient products
+    # split K (dW_O and the stacked projection gradients), and in bf16 the
+    # dK/dV query walk and the dQ key walk are split too
+    (4100, 1, 2, 2, 1, 32, "fp32"),
+    (4100, 1, 2, 2, 1, 32, "bf16"),
 ])
 def test_backward_edge_shapes(gqe, L, B, G, E, k, D, dtype):
     """Ragged lengths (tails of every tile), every head size in both
