@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the GQE prefill layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload l2k] [--long]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload l1m_zipf]
 
 One step = one gqe_forward (router, dispatch, projections, attention, output)
-over one batch of synthetic input already resident in HBM.  The timed region
-is exactly K back-to-back gqe_forward calls between two device
-synchronizations, bracketed by HIP events on the stream.  Separate passes
-give the per-stage breakdown (events between the stage calls), the average
-duration of the attention kernel over back-to-back launches (the roofline
-figure), and the same step replayed from a HIP graph.  The dense-GQA baseline
-(all G*E query heads) is timed the same way, giving the GQE-over-GQA prefill
-speed-up.  Rank 0 prints one JSON line.
+over one batch of synthetic input already resident in HBM.  The headline
+workload is the largest one, B1 x L1048576 with a Zipf(1.2) router prior.
+The timed region is exactly K back-to-back gqe_forward calls between two
+device synchronizations, bracketed by HIP events on the stream.  Separate
+passes give the per-stage breakdown (events between the stage calls), the
+average duration of the attention kernel over back-to-back launches (the
+roofline figure) and, for the short workloads, the same step replayed from a
+HIP graph.  The dense-GQA baseline (all G*E query heads) is timed the same
+way, giving the GQE-over-GQA prefill speed-up at every length.  The CPU
+oracle is timed beside it on the host cores (sampled query rows at the long
+workloads, which also check the GPU step).  Rank 0 prints one JSON line.
 """
 from __future__ import annotations
 
@@ -202,16 +205,20 @@ def rate(kind, amount, ms):
     return v / 1e12  # TFLOP/s or TB/s
 
 
-def measure(wl, gqe, torch, steps, warmup, graph=True):
+def measure(wl, gqe, torch, steps, warmup, graph=True, side_steps=None):
+    """GQE and dense-GQA step times of one workload.  The GQE step is timed
+    over exactly `steps` calls after `warmup`; the dense baseline, the
+    per-stage breakdown and the attention kernel alone use `side_steps`
+    calls (default: `steps`; at least 3)."""
     r = Runner(wl, gqe, torch)
+    side = max(3, steps if side_steps is None else side_steps)
     t_gqe = r.time_steps(r.gqe_step, steps, warmup)
-    t_gqa = r.time_steps(r.gqa_step, steps, warmup)
-    st_gqe = r.time_stages(r.gqe_stages(), max(2, steps // 2))
-    st_gqa = r.time_stages(r.gqa_stages(), max(2, steps // 2))
+    t_gqa = r.time_steps(r.gqa_step, side, min(warmup, 1 if side_steps else warmup))
+    st_gqe = r.time_stages(r.gqe_stages(), max(2, side // 2))
+    st_gqa = r.time_stages(r.gqa_stages(), max(2, side // 2))
     # the attention kernel alone, launched back to back: its average duration
-    reps = max(3, steps)
-    k_gqe = r.time_steps(lambda: gqe.gqe_attention(r.cfg, r.ws), reps, 1)
-    k_gqa = r.time_steps(lambda: gqe.gqa_attention(r.cfg, r.ws_dense), reps, 1)
+    k_gqe = r.time_steps(lambda: gqe.gqe_attention(r.cfg, r.ws), side, 1)
+    k_gqa = r.time_steps(lambda: gqe.gqa_attention(r.cfg, r.ws_dense), side, 1)
     tokens = wl.batch * wl.seq_len
     work = stage_work(wl)
     gwork = gqa_stage_work(wl)
@@ -451,15 +458,18 @@ def roofline_for(wl, res):
             "per_launch": {"flop": amount, "avg_ms": round(ms, 5)}}
 
 
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The CPU oracle, as it stands, on full layers of the same workload until
     about `budget_s` seconds have passed; tokens/s over the layers it finished."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
     I = W.make_inputs(wl)
     f = lambda a: W.to_f64(a, wl.dtype)  # noqa: E731
     args = (f(I["x"]), f(I["wq"]), f(I["wk"]), f(I["wv"]), f(I["wr"]), f(I["wo"]),
@@ -472,20 +482,71 @@ def cpu_baseline(wl, budget_s=12.0):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": round(n * wl.tokens / el, 2), "unit": "tokens/s", "cores": int(threads),
+    return {"value": round(n * wl.tokens / el, 2), "unit": "tokens/s", "cores": int(_oracle_threads()),
             "kind": "oracle",
             "sample": f"{n} full layers of {wl.name} (B={wl.batch}, L={wl.seq_len}) in {el:.1f} s, float64 numpy"}
+
+
+def cpu_baseline_sampled(wl, runner, gqe):
+    """The CPU oracle on the long workloads: routing and dispatch of every
+    token, K and V of every position, then the attention and output of the
+    workload's sampled query rows only.  Each phase is timed.  The full-layer
+    oracle time is extrapolated from the sampled rows (attention in proportion
+    to the causal span sum of (t+1), the output projection to the row count)
+    and is labelled as such; `value` is tokens / that extrapolated time.
+
+    The same call checks the GPU step that `runner` last ran: the routing and
+    dispatch lists bit for bit over all tokens, and the sampled output rows
+    against the output gate (max-abs 2e-2, mean-abs 2e-3 for bf16)."""
+    import oracle
+    I = runner.I
+    rows = W.sample_rows(wl)
+    f = lambda a: W.to_f64(a, wl.dtype)  # noqa: E731
+    x = W.bf16_bits_to_f32(I["x"]) if wl.dtype == W.BF16 else I["x"]
+    phases = {}
+    t0 = time.perf_counter()
+    ref = oracle.gqe_forward(x, f(I["wq"]), f(I["wk"]), f(I["wv"]), f(I["wr"]), f(I["wo"]),
+                             I["br"].astype(np.float64), wl.n_groups, wl.n_experts, wl.top_k,
+                             wl.head_dim, positions=rows, phase_times=phases)
+    el = time.perf_counter() - t0
+    L, B = wl.seq_len, wl.batch
+    span_all = B * L * (L + 1) / 2.0
+    span_sampled = B * float((rows + 1).sum())
+    extrap = (phases["route"] + phases["dispatch"] + phases["kv"] +
+              phases["attention"] * span_all / span_sampled +
+              phases["output"] * (B * L) / (B * len(rows)))
+    # the GPU's results of the last timed step
+    v = gqe.workspace_views(runner.cfg, runner.ws)
+    routing_ok = all(np.array_equal(v[key].cpu().numpy(), ref[key])
+                     for key in ("idx", "counts", "offsets", "pos", "slot"))
+    sel = runner.torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(runner.out.device)
+    y = runner.out[:, sel].float().cpu().double().numpy()
+    err = np.abs(y - ref["y"])
+    rel = float(np.linalg.norm(y - ref["y"]) / max(np.linalg.norm(ref["y"]), 1e-300))
+    tol = (2e-2, 2e-3) if wl.dtype == W.BF16 else (1e-5, 1e-5)
+    check = {"rows": int(len(rows)), "routing_bit_exact": bool(routing_ok),
+             "max_abs": float(err.max()), "mean_abs": float(err.mean()), "rel_l2": rel,
+             "within_gate": bool(routing_ok and err.max() <= tol[0] and err.mean() <= tol[1])}
+    return {"value": round(B * L / extrap, 2), "unit": "tokens/s", "cores": int(_oracle_threads()),
+            "kind": "oracle",
+            "sample": (f"{wl.name}: routing, dispatch and K/V of all {B * L} tokens, then "
+                       f"{len(rows)} sampled query rows (seeded, log-spaced position bands) in "
+                       f"{el:.1f} s, float64 numpy; value = tokens / extrapolated full-layer "
+                       f"oracle time {extrap:.0f} s"),
+            "phase_s": {k: round(t, 3) for k, t in phases.items()},
+            "sampled_rows_per_s": round(len(rows) * B / (phases["attention"] + phases["output"]), 2),
+            "extrapolated_full_layer_s": round(extrap, 1),
+            "gpu_check": check}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="l2k", choices=sorted(W.WORKLOADS))
-    ap.add_argument("--lengths", default="b4_l8k,l128k",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="l1m_zipf", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--lengths", default="l2k,b4_l8k,l128k",
                     help="other workloads timed for the per-length speed-up (comma list, '' = none)")
-    ap.add_argument("--long", action="store_true", help="also time the 1M-token workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
@@ -518,24 +579,35 @@ def main():
         del src, dst
 
     wl = W.WORKLOADS[args.workload]
+    long_step = stage_work(wl)["attention"][1] > 1e14   # a step of 40 ms or more
     log(f"[bench] {wl.description}: warmup {args.warmup}, steps {args.steps}")
-    _, res = measure(wl, gqe, torch, args.steps, args.warmup, graph=not args.no_graph)
+    runner, res = measure(wl, gqe, torch, args.steps, args.warmup,
+                          graph=not args.no_graph and not long_step,
+                          side_steps=3 if long_step else None)
     log(f"[bench] gqe {res['gqe_ms']:.4f} ms  gqa {res['gqa_ms']:.4f} ms  "
-        f"speed-up {res['speedup_vs_gqa']:.3f}  stages {res['gqe_stage_ms']}")
+        f"speed-up {res['speedup_vs_gqa']:.3f}  attention {res['attention_mfma_frac']:.3f} of peak  "
+        f"stages {res['gqe_stage_ms']}")
+    cpu = None
+    if not args.no_cpu_baseline and wl.sample_rows:
+        log("[bench] cpu baseline (oracle, sampled rows) and check of the GPU step ...")
+        cpu = cpu_baseline_sampled(wl, runner, gqe)
+        log(f"[bench]   {cpu}")
+    del runner
+    torch.cuda.empty_cache()
 
-    per_length = [res]
-    extra = [n for n in args.lengths.split(",") if n] + (["l1m_zipf"] if args.long else [])
-    for name in extra:
+    per_length = []
+    for name in [n for n in args.lengths.split(",") if n]:
         if name == wl.name:
             continue
         w2 = W.WORKLOADS[name]
-        steps = max(2, min(args.steps, int(2e12 / max(1, stage_work(w2)["attention"][1]) + 2)))
+        steps = max(2, min(200, int(2e12 / max(1, stage_work(w2)["attention"][1]) + 2)))
         log(f"[bench] per-length {w2.description}: steps {steps}")
-        _, r2 = measure(w2, gqe, torch, steps, 1, graph=not args.no_graph)
-        log(f"[bench]   gqe {r2['gqe_ms']:.3f} ms gqa {r2['gqa_ms']:.3f} ms "
+        _, r2 = measure(w2, gqe, torch, steps, min(10, steps), graph=not args.no_graph)
+        log(f"[bench]   gqe {r2['gqe_ms']:.4f} ms gqa {r2['gqa_ms']:.4f} ms "
             f"speed-up {r2['speedup_vs_gqa']:.3f} attention {r2['attention_mfma_frac']:.3f} of peak")
         per_length.append(r2)
         torch.cuda.empty_cache()
+    per_length.append(res)
 
     line = {
         "metric": METRIC,
@@ -550,7 +622,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == W.BF16 else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.description, "batch": wl.batch, "seq_len": wl.seq_len,
+        "config": {"workload": wl.description, "name": wl.name, "batch": wl.batch,
+                   "seq_len": wl.seq_len, "router_bias": (f"-{wl.zipf_s} ln(e+1) per group"
+                                                          if wl.zipf_s else "zero"),
                    "d_model": wl.d_model, "n_groups": wl.n_groups, "n_experts": wl.n_experts,
                    "top_k": wl.top_k, "head_dim": wl.head_dim, "shared_heads": 1,
                    "parallelism": "single GPU"},
@@ -580,7 +654,9 @@ def main():
         log("[bench] decode step ...")
         line["decode"] = measure_decode(gqe, torch, args.steps, args.warmup)
         log(f"[bench]   decode {line['decode']}")
-    if not args.no_cpu_baseline:
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    elif not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

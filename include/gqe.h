@@ -16,13 +16,19 @@
  * ---------------------------------------
  *  - Every pointer is a DEVICE pointer owned by the caller, except `cfg` and
  *    `layout`, which are host pointers read (or written) before the call
- *    returns.  The library never allocates or frees device memory.  Its only
- *    global state is the per-device side stream and events of gqe_forward
- *    (behind a mutex); every call is thread-safe.
+ *    returns.  The library never allocates or frees device memory and holds
+ *    no global mutable state.  Every call is thread-safe; calls that share a
+ *    workspace must not overlap.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
- *    default stream).  No call synchronizes the host.  The status returned
- *    reports argument errors only (nothing is launched then); a fault inside
- *    a kernel surfaces at the caller's next synchronization of `stream`.
+ *    default stream), and only on `stream`.  No call synchronizes the host.
+ *    An argument error is returned before anything is enqueued.  A call that
+ *    returns GQE_ERR_HIP (a launch the runtime rejected) may have enqueued
+ *    the stages before the failing launch.  A fault inside a kernel surfaces
+ *    at the caller's next synchronization of `stream`.
+ *  - Weights use the [out, in] layout of nn.Linear (below), not the [in, out]
+ *    layout of a plain x.W product: with it both operands of every projection
+ *    are contiguous along the reduction dimension, which is how the matrix
+ *    cores take them (16-byte vector loads along K for both).
  *  - Tensors are contiguous and row-major.  Element type `cfg->dtype`:
  *    bfloat16 (GQE_DTYPE_BF16) or float32 (GQE_DTYPE_FP32) for x, every
  *    weight and `out`; router bias and weights w are float32; indices int32.
@@ -190,15 +196,9 @@ int gqe_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace
                size_t ws_bytes, hipStream_t stream);
 
 /* The whole GQE prefill layer: the work of gqe_route, gqe_dispatch,
- * gqe_project, gqe_attention and gqe_output, ordered on `stream`.  The dense
- * part of the projection (shared-head Q, K, V^T) does not depend on the
- * routing; it runs concurrently with routing, dispatch and the gathered Q
- * projection on a second stream of the same device (created on first use and
- * kept for the life of the process), forked from and joined back into
- * `stream` with events, so the call is ordered after all earlier work on
- * `stream` and later work on `stream` sees all of it.  It works under HIP
- * graph capture of `stream` once a first call outside capture has created
- * that stream.  Concurrent calls serialize on a mutex while they enqueue. */
+ * gqe_project, gqe_attention and gqe_output, in that order on `stream` (the
+ * dense and the gathered projections share one launch).  Works under HIP
+ * graph capture of `stream`, first call included. */
 int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
                 const void* Wv, const void* Wr, const void* Wo, void* out,
                 void* workspace, size_t ws_bytes, hipStream_t stream);

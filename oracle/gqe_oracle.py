@@ -60,6 +60,7 @@ recomputed with an exactly rounded sum (math.fsum of the exact products).
 from __future__ import annotations
 
 import math
+import time
 
 import numpy as np
 
@@ -283,7 +284,8 @@ def ablation_slots(mode: str, o_hard: np.ndarray, p_sel: np.ndarray) -> np.ndarr
 
 
 def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
-                shared_kv_group=0, scale=None, positions=None, output_mode="full"):
+                shared_kv_group=0, scale=None, positions=None, output_mode="full",
+                phase_times=None):
     """GQE prefill forward (steps 1-11) in float64.
 
     x: [B, L, d]; wq [(G*E+1)*d_h, d]; wk, wv [G*d_h, d]; wr [G*E, d];
@@ -299,6 +301,11 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
     ``output_mode`` picks one of OUTPUT_MODES; the "hard" and "weighted_concat"
     constructions have no shared head (q and o then hold the k*G hard
     slot-heads only) and a W_O of k*G*d_h inputs.
+
+    ``phase_times``, when a dict, receives the wall time in seconds of each
+    phase: "route" (steps 1-4), "dispatch" (5), "kv" (6), "attention"
+    (7-8, query projections included) and "output" (9-11).  Timing only: it
+    changes nothing that is computed.
     """
     if output_mode not in OUTPUT_MODES:
         raise ValueError(output_mode)
@@ -310,10 +317,20 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
     n = len(pos_q)
     upto = int(pos_q.max()) + 1
 
+    clock = [time.perf_counter()]
+
+    def tick(phase):
+        now = time.perf_counter()
+        if phase_times is not None:
+            phase_times[phase] = phase_times.get(phase, 0.0) + now - clock[0]
+        clock[0] = now
+
     r, p, idx, w = route(x.reshape(B * L, d), wr, br, G, E, k)
     r, p = r.reshape(B, L, G, E), p.reshape(B, L, G, E)
     idx, w = idx.reshape(B, L, G, k), w.reshape(B, L, G, k)
+    tick("route")
     counts, offsets, pos, slot = dispatch(idx, E)
+    tick("dispatch")
 
     S = k * G + (1 if full else 0)                        # attention slot-heads
     q_all = np.empty((B, n, S, dh))
@@ -325,6 +342,7 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
         xb = x[b]
         K_all[b] = kv_project(xb, wk, G, dh, upto)
         V_all[b] = kv_project(xb, wv, G, dh, upto)
+        tick("kv")
         xq = xb[pos_q]                                    # [n, d]
         o_hard = np.empty((n, G, k, dh))
         for g in range(G):
@@ -339,17 +357,22 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
                 o_hard[:, g, j] = causal_attention(qh, pos_q, K_all[b, g], V_all[b, g], scale)
         o_all[b, :, :k * G] = o_hard.reshape(n, G * k, dh)
         if not full:
+            tick("attention")
             p_sel = np.take_along_axis(p[b, pos_q], idx[b, pos_q].astype(np.int64), axis=-1)
             s_all[b] = ablation_slots(output_mode, o_hard, p_sel)
+            tick("output")
             continue
         q_sh = xq @ head_rows(wq, G * E, dh).T            # step 8: always-on shared head
         o_sh = causal_attention(q_sh, pos_q, K_all[b, shared_kv_group],
                                 V_all[b, shared_kv_group], scale)
         q_all[b, :, k * G] = q_sh
         o_all[b, :, k * G] = o_sh
+        tick("attention")
         o_w = weighted_slot(w[b, pos_q], o_hard)
         s_all[b] = slot_vector(o_hard, o_sh, o_w)
+        tick("output")
     y = output_projection(s_all, wo)
+    tick("output")
     return dict(r=r, p=p, idx=idx, w=w, counts=counts, offsets=offsets, pos=pos, slot=slot,
                 q=q_all, k_=K_all, v=V_all, o=o_all, s=s_all, y=y, positions=pos_q)
 

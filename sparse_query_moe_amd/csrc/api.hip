@@ -4,7 +4,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <mutex>
 
 #include "../../include/gqe.h"
 #include "kernels.h"
@@ -176,12 +175,9 @@ int gather_tiles_per_bg(const gqe_config* c) {
   return static_cast<int>((rows + kGatherRows - 1) / kGatherRows) + c->n_experts;
 }
 
-enum ProjPart { kProjAll, kProjDense, kProjGather };
-
 template <typename T>
 int project_impl(const gqe_config* c, const void* x, const void* wq, const void* wk,
-                 const void* wv, void* ws, bool dense, hipStream_t stream,
-                 ProjPart part = kProjAll) {
+                 const void* wv, void* ws, bool dense, hipStream_t stream) {
   const Layout l = make_layout(c, dense);
   const int B = c->batch, L = c->seq_len, d = c->d_model, G = c->n_groups, E = c->n_experts;
   const int D = c->head_dim;
@@ -211,18 +207,15 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   seg[2].heads = G;
   seg[2].head_base = 0;
   seg[2].transposed = 1;
-  hipError_t e = hipSuccess;
-  if (part != kProjGather)
-    e = launch_dense_proj<T>(static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_tiles,
-                             shared ? seg : seg + 1, shared ? 3 : 2, stream);
-  if (e != hipSuccess || dense || part == kProjDense) return hip_status(e);
-  e = launch_gather_q<T>(static_cast<const T*>(x), static_cast<const T*>(wq), at<T>(ws, l.pub.q),
-                         at<int32_t>(ws, l.pub.counts), at<int32_t>(ws, l.pub.offsets),
-                         at<int32_t>(ws, l.pub.pos), at<int32_t>(ws, l.pub.slot),
-                         at<int32_t>(ws, l.tile_off), B, L, d, G, E, make_group_k(c), D,
-                         gather_tiles_per_bg(c),
-                         stream);
-  return hip_status(e);
+  if (dense)
+    return hip_status(launch_dense_proj<T>(static_cast<const T*>(x), B * L, d, L, D,
+                                           l.pub.vt_tiles, seg, 3, stream));
+  // dense tiles and gathered routed-query tiles in one launch
+  return hip_status(launch_project<T>(
+      static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_tiles, shared ? seg : seg + 1,
+      shared ? 3 : 2, static_cast<const T*>(wq), at<T>(ws, l.pub.q), at<int32_t>(ws, l.pub.counts),
+      at<int32_t>(ws, l.pub.offsets), at<int32_t>(ws, l.pub.pos), at<int32_t>(ws, l.pub.slot),
+      at<int32_t>(ws, l.tile_off), B, G, E, make_group_k(c), gather_tiles_per_bg(c), stream));
 }
 
 template <typename T>
@@ -287,45 +280,6 @@ int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool d
 }  // namespace
 
 namespace {
-
-// gqe_forward overlaps the dense projection (shared-head Q, K, V^T), which
-// does not depend on the routing, with routing, dispatch and the gathered Q
-// projection: it runs on a second stream of the same device between a fork
-// and a join event.  One side stream and two events per device, created on
-// first use; the whole enqueue sequence holds a mutex so that concurrent
-// callers cannot interleave their event records.
-struct Fork {
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool tried = false;
-};
-constexpr int kMaxDevices = 64;
-Fork g_forks[kMaxDevices];
-std::mutex g_fork_mutex;
-
-// the fork resources of the stream's device, or nullptr (then everything runs
-// on the caller's stream)
-Fork* fork_for(hipStream_t stream) {
-  hipDevice_t dev = 0;
-  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return nullptr;
-  Fork& f = g_forks[dev];
-  if (!f.tried) {
-    f.tried = true;
-    int cur = 0;
-    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
-    bool ok = hipSetDevice(dev) == hipSuccess;
-    ok = ok && hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&f.join, hipEventDisableTiming) == hipSuccess;
-    (void)hipSetDevice(cur);
-    if (!ok) {
-      (void)hipGetLastError();
-      f.side = nullptr;
-    }
-  }
-  return f.side != nullptr ? &f : nullptr;
-}
 
 // ---- decode ------------------------------------------------------------------
 
@@ -756,24 +710,9 @@ int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void
   if (!aligned16(x) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(Wr) ||
       !aligned16(Wo) || !aligned16(out))
     return GQE_ERR_INVALID_ARG;
-  const bool bf16 = cfg->dtype == GQE_DTYPE_BF16;
-  auto project = [&](hipStream_t s_, ProjPart part) {
-    return bf16 ? project_impl<bf16_t>(cfg, x, Wq, Wk, Wv, workspace, false, s_, part)
-                : project_impl<float>(cfg, x, Wq, Wk, Wv, workspace, false, s_, part);
-  };
-  std::lock_guard<std::mutex> lock(g_fork_mutex);
-  Fork* f = fork_for(stream);
-  if (f != nullptr) {  // dense projection on the side stream, after everything before the call
-    if (hipEventRecord(f->fork, stream) != hipSuccess ||
-        hipStreamWaitEvent(f->side, f->fork, 0) != hipSuccess)
-      return GQE_ERR_HIP;
-    if ((st = project(f->side, kProjDense)) != GQE_OK) return st;
-    if (hipEventRecord(f->join, f->side) != hipSuccess) return GQE_ERR_HIP;
-  }
   if ((st = gqe_route(cfg, x, Wr, workspace, ws_bytes, stream)) != GQE_OK) return st;
   if ((st = gqe_dispatch(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
-  if ((st = project(stream, f != nullptr ? kProjGather : kProjAll)) != GQE_OK) return st;
-  if (f != nullptr && hipStreamWaitEvent(stream, f->join, 0) != hipSuccess) return GQE_ERR_HIP;
+  if ((st = gqe_project(cfg, x, Wq, Wk, Wv, workspace, ws_bytes, stream)) != GQE_OK) return st;
   if ((st = gqe_attention(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
   return gqe_output(cfg, Wo, out, workspace, ws_bytes, stream);
 }

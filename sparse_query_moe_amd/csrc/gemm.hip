@@ -368,17 +368,31 @@ struct GatherProb {
   }
 };
 
-template <typename T, class S>
-__global__ __launch_bounds__(256) void gather_q_kernel(GatherArgs args) {
+// ---------------------------------------------------------------------------
+// the whole GQE projection in one launch: the dense tiles (shared-head Q, K,
+// V^T) first, then the gathered routed-query tiles.  Neither depends on the
+// other, so one grid covers both and the gathered tiles fill the compute
+// units the dense ones leave idle.
+// ---------------------------------------------------------------------------
+template <typename T, class SD, class SG>
+__global__ __launch_bounds__(256) void project_kernel(DenseArgs dargs, GatherArgs gargs,
+                                                      int dense_nx, int dense_blocks,
+                                                      int tiles_per_bg) {
   extern __shared__ __align__(16) char smem[];
-  const int bg = blockIdx.y;
-  const int tile = blockIdx.x;
-  const int* toff = args.tile_off + bg * (args.E + 1);   // tile map of this (b, g)
-  if (tile >= toff[args.E]) return;                      // whole block leaves together
-  int e = 0;                                             // last e with toff[e] <= tile
-  while (e + 1 < args.E && toff[e + 1] <= tile) ++e;
-  GatherProb<T, S> prob(args, tile - toff[e], bg * args.E + e);
-  gemm_block<T, S>(prob, smem);
+  const int bid = blockIdx.x;
+  if (bid < dense_blocks) {
+    DenseProb<T, SD> prob(dargs, (bid / dense_nx) * SD::BM, (bid % dense_nx) * SD::BN);
+    gemm_block<T, SD>(prob, smem);
+    return;
+  }
+  const int gb = bid - dense_blocks;
+  const int tile = gb % tiles_per_bg, bg = gb / tiles_per_bg;
+  const int* toff = gargs.tile_off + bg * (gargs.E + 1);  // tile map of this (b, g)
+  if (tile >= toff[gargs.E]) return;                      // whole block leaves together
+  int e = 0;                                              // last e with toff[e] <= tile
+  while (e + 1 < gargs.E && toff[e + 1] <= tile) ++e;
+  GatherProb<T, SG> prob(gargs, tile - toff[e], bg * gargs.E + e);
+  gemm_block<T, SG>(prob, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -620,43 +634,89 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_
   GQE_LAUNCH_TILED(dense_proj_kernel, T, M, N, stream, a);
 }
 
+template <typename T, class SD, class SG>
+static hipError_t launch_project_s(const DenseArgs& d, const GatherArgs& g, int tiles_per_bg,
+                                   int n_bg, hipStream_t stream) {
+  const int nx = (d.N + SD::BN - 1) / SD::BN;
+  const int dense_blocks = d.N == 0 || d.M == 0 ? 0 : nx * ((d.M + SD::BM - 1) / SD::BM);
+  const long long blocks = dense_blocks + static_cast<long long>(tiles_per_bg) * n_bg;
+  if (blocks == 0) return hipSuccess;
+  constexpr int lds = SD::LDS > SG::LDS ? SD::LDS : SG::LDS;
+  auto kern = project_kernel<T, SD, SG>;
+  if (lds > 65536) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream, d, g,
+                     nx > 0 ? nx : 1, dense_blocks, tiles_per_bg);
+  return hipGetLastError();
+}
+
+// Dense tiles: 128 x 128 while the whole launch fills the chip, else 64-row
+// tiles (the same K steps in the same order per output element); the
+// four-stage ring when every block of the launch is resident at once.
 template <typename T, int D>
-static hipError_t launch_gather_q_d(const GatherArgs& a, int tiles_per_bg, int n_bg,
-                                    hipStream_t stream) {
-  typedef GemmShape<T, kGatherRows, D, (D >= 128 ? 2 : 4), (D >= 128 ? 2 : 1)> S;
-  typedef GemmShape<T, kGatherRows, D, (D >= 128 ? 2 : 4), (D >= 128 ? 2 : 1), 4> S4;
-  if (deep_ring(static_cast<long long>(tiles_per_bg) * n_bg))
-    return launch_gemm<S4>(gather_q_kernel<T, S4>, dim3(tiles_per_bg, n_bg), stream, a);
-  return launch_gemm<S>(gather_q_kernel<T, S>, dim3(tiles_per_bg, n_bg), stream, a);
+static hipError_t launch_project_d(const DenseArgs& d, const GatherArgs& g, int tiles_per_bg,
+                                   int n_bg, hipStream_t stream) {
+  constexpr int WGM = D >= 128 ? 2 : 4, WGN = D >= 128 ? 2 : 1;
+  const long long gblocks = static_cast<long long>(tiles_per_bg) * n_bg;
+  const long long nx = (d.N + 127) / 128;
+  const long long b128 = nx * ((d.M + 127) / 128) + gblocks;
+  const bool small = b128 < cu_count();
+  const long long total = small ? nx * ((d.M + 63) / 64) + gblocks : b128;
+  if (deep_ring(total)) {
+    typedef GemmShape<T, kGatherRows, D, WGM, WGN, 4> SG;
+    return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2, 4>, SG>(d, g, tiles_per_bg, n_bg, stream)
+                 : launch_project_s<T, GemmShape<T, 128, 128, 2, 2, 4>, SG>(d, g, tiles_per_bg, n_bg, stream);
+  }
+  typedef GemmShape<T, kGatherRows, D, WGM, WGN> SG;
+  return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2>, SG>(d, g, tiles_per_bg, n_bg, stream)
+               : launch_project_s<T, GemmShape<T, 128, 128, 2, 2>, SG>(d, g, tiles_per_bg, n_bg, stream);
 }
 
 template <typename T>
-hipError_t launch_gather_q(const T* x, const T* wq, T* q, const int32_t* counts,
-                           const int32_t* offsets, const int32_t* pos, const int32_t* slot,
-                           const int32_t* tile_off, int B, int L, int d, int G, int E,
-                           const GroupK& gk, int D, int tiles_per_bg, hipStream_t stream) {
-  GatherArgs a;
-  a.x = x;
-  a.wq = wq;
-  a.q = q;
-  a.counts = counts;
-  a.offsets = offsets;
-  a.pos = pos;
-  a.slot = slot;
-  a.tile_off = tile_off;
-  a.n_lists = B * G * E;
-  a.L = L;
-  a.d = d;
-  a.G = G;
-  a.E = E;
-  for (int g = 0; g <= G; ++g) a.koff[g] = gk.koff[g];
-  a.D = D;
-  a.H = gk.K + 1;
-  if (tiles_per_bg == 0 || B * G == 0) return hipSuccess;
+hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
+                          const ProjSeg* segs, int nseg, const T* wq, T* q,
+                          const int32_t* counts, const int32_t* offsets, const int32_t* pos,
+                          const int32_t* slot, const int32_t* tile_off, int B, int G, int E,
+                          const GroupK& gk, int tiles_per_bg, hipStream_t stream) {
+  DenseArgs d;
+  d.x = x;
+  d.M = M;
+  d.K = K;
+  d.L = L;
+  d.D = D;
+  d.vt_tiles = vt_tiles;
+  d.nseg = nseg;
+  int N = 0;
+  for (int i = 0; i < nseg; ++i) {
+    d.seg[i] = segs[i];
+    N = segs[i].n_begin + segs[i].n;
+  }
+  d.N = N;
+  GatherArgs g;
+  g.x = x;
+  g.wq = wq;
+  g.q = q;
+  g.counts = counts;
+  g.offsets = offsets;
+  g.pos = pos;
+  g.slot = slot;
+  g.tile_off = tile_off;
+  g.n_lists = B * G * E;
+  g.L = L;
+  g.d = K;
+  g.G = G;
+  g.E = E;
+  for (int i = 0; i <= G; ++i) g.koff[i] = gk.koff[i];
+  g.D = D;
+  g.H = gk.K + 1;
+  if (B * G == 0) tiles_per_bg = 0;
   switch (D) {
-    case 32: return launch_gather_q_d<T, 32>(a, tiles_per_bg, B * G, stream);
-    case 64: return launch_gather_q_d<T, 64>(a, tiles_per_bg, B * G, stream);
-    case 128: return launch_gather_q_d<T, 128>(a, tiles_per_bg, B * G, stream);
+    case 32: return launch_project_d<T, 32>(d, g, tiles_per_bg, B * G, stream);
+    case 64: return launch_project_d<T, 64>(d, g, tiles_per_bg, B * G, stream);
+    case 128: return launch_project_d<T, 128>(d, g, tiles_per_bg, B * G, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -739,9 +799,10 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
 #define GQE_INST(T)                                                                              \
   template hipError_t launch_dense_proj<T>(const T*, int, int, int, int, int64_t, const ProjSeg*, \
                                            int, hipStream_t);                                    \
-  template hipError_t launch_gather_q<T>(const T*, const T*, T*, const int32_t*, const int32_t*, \
-                                         const int32_t*, const int32_t*, const int32_t*, int, int, \
-                                         int, int, int, const GroupK&, int, int, hipStream_t);    \
+  template hipError_t launch_project<T>(const T*, int, int, int, int, int64_t, const ProjSeg*,   \
+                                        int, const T*, T*, const int32_t*, const int32_t*,       \
+                                        const int32_t*, const int32_t*, const int32_t*, int, int, \
+                                        int, const GroupK&, int, hipStream_t);                   \
   template hipError_t launch_out_proj<T>(const T*, const T*, T*, int, int, int, hipStream_t);    \
   template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, hipStream_t);      \
   template hipError_t launch_nt_gemm<T>(const NtArgs&, hipStream_t);

@@ -23,7 +23,8 @@ _TORCH_DTYPE = {DTYPE_BF16: torch.bfloat16, DTYPE_FP32: torch.float32}
 # every entry point include/gqe.h declares
 EXPORTS = (
     "gqe_workspace_bytes", "gqe_workspace_layout", "gqe_route", "gqe_dispatch", "gqe_project",
-    "gqe_attention", "gqe_output", "gqe_forward", "gqa_workspace_bytes", "gqa_workspace_layout",
+    "gqe_attention", "gqe_output", "gqe_forward", "gqa_workspace_bytes",
+    "gqa_workspace_layout",
     "gqa_project", "gqa_attention", "gqa_output", "gqa_forward", "gqe_decode_workspace_bytes",
     "gqe_decode", "gqa_decode_workspace_bytes", "gqa_decode", "gqe_backward_workspace_bytes",
     "gqe_backward", "gqa_backward_workspace_bytes", "gqa_backward", "gqe_status_string",
