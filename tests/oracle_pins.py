@@ -176,6 +176,32 @@ def pin_tie_rule(orc):
     assert (idx[:, :, 1, 0] == 0).all() and (idx[:, :, 1, 1] == 2).all()
 
 
+def pin_exact_logits_keep_the_bias(orc):
+    """Near-ties are decided on exactly rounded logits, and those include the
+    router bias.  Experts 1 and 2 of group 0 have identical router rows, so
+    their products with x tie exactly; a bias of 2^-44 on expert 2 (a gap far
+    below the 1e-12 margin that sends the token to the exact path) must rank
+    it first, and expert 1 second.  In group 1 the two rows differ by one
+    element so that expert 1's dot product is larger by exactly 2^-40, and a
+    bias of 2^-39 on expert 2 overturns it.  Inputs are dyadic, so every
+    product and every sum here is exact."""
+    rng = np.random.default_rng(19)
+    t = tiny_layer(rng, B=1, L=5, d=12, G=2, E=4, k=2)
+    E = t["E"]
+    x = rng.integers(1, 4, t["x"].shape).astype(np.float64)         # positive integers
+    wr = rng.integers(-8, -3, t["wr"].shape).astype(np.float64) / 8.0
+    wr[0 * E + 1] = wr[0 * E + 2] = 0.5                              # group 0: exact tie
+    wr[1 * E + 1] = wr[1 * E + 2] = 0.5                              # group 1 ...
+    wr[1 * E + 1, 0] += 2.0 ** -40 / x[0, 0, 0]                      # ... expert 1 ahead by 2^-40 at t=0
+    br = np.zeros(t["G"] * E)
+    br[0 * E + 2] = 2.0 ** -44
+    br[1 * E + 2] = 2.0 ** -39
+    t.update(x=x, wr=wr, br=br)
+    idx = run(orc, t)["idx"]
+    assert (idx[0, :, 0, 0] == 2).all() and (idx[0, :, 0, 1] == 1).all(), idx[0, :, 0]
+    assert idx[0, 0, 1, 0] == 2 and idx[0, 0, 1, 1] == 1, idx[0, 0, 1]
+
+
 # ---------------------------------------------------------------------------
 # P5, P10: dispatch lists
 # ---------------------------------------------------------------------------
@@ -735,6 +761,7 @@ ALL_PINS = [
     pin_bias_selects,
     pin_topk_brute_force,
     pin_tie_rule,
+    pin_exact_logits_keep_the_bias,
     pin_dispatch_lists,
     pin_active_query_ratio,
     pin_attention_brute_force,

@@ -101,6 +101,13 @@ def m_router_bias_dropped(mod):
     mod.router_logits = logits
 
 
+def m_exact_logits_bias_dropped(mod):
+    """the exactly rounded logits of near-tie tokens leave out the router bias."""
+    def exact_logits(x_row, wr, br):
+        return np.array([math.fsum(list(x_row * wr[c])) for c in range(wr.shape[0])])
+    mod.exact_logits = exact_logits
+
+
 def m_expert_head_transposed(mod):
     mod.expert_head = lambda g, e, E: e * E + g          # group and expert swapped
 
@@ -292,7 +299,8 @@ def m_group_k_bwd_softmax_over_all_slots(mod):
 MUTATIONS = [
     m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
     m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
-    m_router_group_transposed, m_router_bias_dropped, m_expert_head_transposed,
+    m_router_group_transposed, m_router_bias_dropped, m_exact_logits_bias_dropped,
+    m_expert_head_transposed,
     m_expert_head_reversed,
     m_weighted_mean, m_weighted_missing, m_weighted_unweighted, m_slots_rank_major,
     m_shared_weighted_swapped, m_output_untransposed, m_dispatch_descending,
