@@ -96,7 +96,7 @@ bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr
 
 struct Layout {
   gqe_ws_layout pub;
-  size_t chunk_counts, tile_off;
+  size_t chunk_counts, tile_off, redo;
 };
 
 // slot-heads that attend: every routed slot and the shared head (full
@@ -140,6 +140,8 @@ Layout make_layout(const gqe_config* c, bool dense) {
   l.pub.s = take(B * L * (dense ? G * E : static_cast<size_t>(slot_count(c))) * D * es);
   l.pub.lse = take(B * L * static_cast<size_t>(attn_heads(c, dense)) * 4);
   if (dense) l.pub.scratch = off;
+  l.redo = take(static_cast<size_t>(attention_redo_ints(c->batch, attn_heads(c, dense),
+                                                        c->seq_len)) * 4);
   l.pub.total = off;
   l.pub.vt_tiles = static_cast<int64_t>(vt_tiles);
   return l;
@@ -225,6 +227,7 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
   AttnParams p;
   p.row_scale = nullptr;
   p.lse = at<float>(ws, l.pub.lse);
+  p.redo = at<int>(ws, l.redo);
   p.q = at<T>(ws, l.pub.q);
   p.k = at<T>(ws, l.pub.k);
   p.vt = at<T>(ws, l.pub.vt);

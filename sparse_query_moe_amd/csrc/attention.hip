@@ -20,12 +20,21 @@
 //   each V^T fragment one 16-byte LDS read.  O^T again has one query per lane,
 //   so the online-softmax rescale is lane-local.
 //   K and V^T tiles of 64 keys are double-buffered in LDS (swizzled 16-byte
-//   chunks, one barrier per tile).  The running maximum is only raised when a
-//   tile exceeds it by more than 2^8: the stale maximum keeps every
-//   probability <= 256, and since the same maximum scales numerator and
-//   denominator the result is unchanged.  It is subtracted inside the score
-//   MFMA chain (one extra K step of a unit key column against -m), so it is
-//   held as an operand-type value, rounded up.
+//   chunks, one barrier per tile).
+//
+// Softmax without a running maximum (the fast path).  Scores come out of the
+// MFMA in log2 units and are exponentiated as they are: the subtraction of a
+// maximum only guards the range of exp2, and the same shift cancels between
+// numerator and denominator.  A row takes this path when its score against
+// key 0 (which every causal row sees) lies in [-60, 60]; the block checks at
+// the end that every row's sum stays in [2^-60, 2^100] and its output is
+// finite.  Otherwise -- scores far outside the range of ordinary inputs --
+// the whole block is recomputed with the running maximum (the fallback):
+// the maximum is raised only when a tile exceeds it by more than 2^8, so the
+// stale maximum keeps every probability <= 256, and it is subtracted inside
+// the score MFMA chain as one more K step: unit key columns against -m split
+// exactly into three operand-type parts, so no VALU work is spent on it and
+// any float32 maximum is represented exactly.
 //   Blocks are issued heaviest query block first to shorten the causal tail.
 #include <math.h>
 
@@ -40,35 +49,47 @@ namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-// The running maximum enters the score MFMA as one more K step: a unit column
-// of K against -m in the query's row, so the accumulator starts from zero and
-// S^T - m costs no VALU work.  The maximum is kept representable in the
-// operand type (rounded up, so probabilities never exceed the bound).
+// The running maximum enters the score MFMA of the fallback as one more K
+// step: unit key columns against -m in the query's column, so the
+// accumulator starts from zero and S^T - m costs no VALU work.  For bf16
+// operands -m is split into three bf16 parts whose sum is exactly the
+// float32 value (8 + 8 + 8 significant bits), against three unit columns.
 template <typename T> struct ShiftOp;
 template <> struct ShiftOp<bf16_t> {
   typedef bf16x8 type;
+  static __device__ __forceinline__ type unit(int half) {
+    type r = {};
+    if (half == 0) r[0] = r[1] = r[2] = static_cast<__bf16>(1.f);
+    return r;
+  }
   static __device__ __forceinline__ type make(float v, int half) {
     type r = {};
-    r[0] = static_cast<__bf16>(half == 0 ? v : 0.f);
+    if (half == 0) {
+      const __bf16 hi = static_cast<__bf16>(v);
+      const float r1 = v - static_cast<float>(hi);  // exact
+      const __bf16 mid = static_cast<__bf16>(r1);
+      r[0] = hi;
+      r[1] = mid;
+      r[2] = static_cast<__bf16>(r1 - static_cast<float>(mid));  // exact
+    }
     return r;
   }
   static __device__ __forceinline__ f32x16 mma(const type& unit, const type& nm) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(unit, nm, f32x16{}, 0, 0, 0);
   }
-  static __device__ __forceinline__ float round_up(float x) {
-    uint32_t u = __float_as_uint(x);
-    if (!(u >> 31)) u += 0xffffu;
-    return __uint_as_float(u & 0xffff0000u);
-  }
 };
 template <> struct ShiftOp<float> {
   typedef float type;
+  static __device__ __forceinline__ type unit(int half) { return half == 0 ? 1.f : 0.f; }
   static __device__ __forceinline__ type make(float v, int half) { return half == 0 ? v : 0.f; }
   static __device__ __forceinline__ f32x16 mma(type unit, type nm) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(unit, nm, f32x16{}, 0, 0, 0);
   }
-  static __device__ __forceinline__ float round_up(float x) { return x; }
 };
+
+// the fast path's acceptance bounds (log2 units / row sums)
+constexpr float kFastScore = 60.f;
+constexpr float kFastSumMin = 0x1p-60f, kFastSumMax = 0x1p100f;
 
 
 // QW query waves of 32*QB rows each share every K/V tile; NS groups of QW
@@ -116,10 +137,20 @@ __device__ __forceinline__ float dot8(const f32x8& a, const f32x8& b) {
   return s;
 }
 
-template <typename T, int D, int QB, int QW, int NS>
+// How a launch treats the fallback: inline (a block that needs it runs it
+// at once), or split over two launches of the same grid, the first running
+// the fast path only and flagging the blocks that need the fallback in
+// p.redo, the second running the fallback for the flagged blocks only.  The
+// split keeps the fallback's registers out of the fast path's allocation.
+enum { kInline = 0, kFastOnly = 1, kFallbackOnly = 2 };
+
+template <typename T, int D, int QB, int QW, int NS, int MODE>
 __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) void attention_kernel(
     AttnParams p) {
   typedef AttnShape<T, D, QB, QW, NS> S;
+  if constexpr (MODE == kFallbackOnly) {
+    if (p.redo[blockIdx.x] == 0) return;  // the fast path's result stands
+  }
   typedef typename Frag<T>::type F;
   extern __shared__ __align__(16) char smem[];
 
@@ -198,14 +229,16 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
 
   if (tile_of(0) < ntiles) dl_issue(tile_of(0), 0);
 
-  // queries (pre-scaled) in registers; the running maximum starts at the score
-  // against key 0, which every causal row sees, so it is finite from the start
+  // queries (pre-scaled) in registers, and each row's score against key 0,
+  // which every causal row sees: the fallback's first running maximum, and
+  // the test that admits the row to the fast path
   int qrow[QB];
   F qf[QB][S::NKS];
-  float m_run[QB], l_run[QB];
+  float m_run[QB], l_run[QB], score0[QB];
   typename ShiftOp<T>::type nm[QB];
-  const typename ShiftOp<T>::type unit = ShiftOp<T>::make(1.f, half);
+  const typename ShiftOp<T>::type unit = ShiftOp<T>::unit(half);
   f32x16 o[QB][S::NDB];
+  bool fast = true;
   {
     F k0[S::NKS];
 #pragma unroll
@@ -225,7 +258,14 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
         }
         dot += dot8(qf[qb][ks], k0[ks]);
       }
-      m_run[qb] = ShiftOp<T>::round_up(dot + __shfl_xor(dot, 32, 64));
+      score0[qb] = dot + __shfl_xor(dot, 32, 64);
+      fast = fast && score0[qb] >= -kFastScore && score0[qb] <= kFastScore;
+    }
+  }
+  auto reset = [&](bool shifted) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m_run[qb] = shifted ? score0[qb] : 0.f;
       nm[qb] = ShiftOp<T>::make(-m_run[qb], half);
       l_run[qb] = 0.f;
 #pragma unroll
@@ -233,48 +273,86 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
     }
-  }
+  };
 
-  // one 64-key tile for this wave's QB query blocks.  The query blocks are
-  // staggered: S^T of every block is issued first (the MFMAs run on while the
-  // wave moves on), then block 0's softmax overlaps block 1's S^T, and block
-  // 1's softmax overlaps block 0's O^T update.
-  auto tile = [&](const char* Ks, const char* Vs, int j0, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    // S^T - m of one query block (K fragments are read per block: LDS
-    // bandwidth is cheaper than the registers that would hold them)
-    auto scores = [&](int qb, f32x16 (&sq)[2]) {
+  // S^T of one query block and one 32-key half of the tile, minus the running
+  // maximum when SHIFT (K fragments are read per block: LDS bandwidth is
+  // cheaper than the registers that would hold them)
+  auto scores = [&](const char* Ks, int j0, int qb, auto shift_tag, auto mask_tag, f32x16 (&sq)[2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (decltype(shift_tag)::value) {
         sq[kb] = ShiftOp<T>::mma(unit, nm[qb]);
-#pragma unroll
-        for (int ks = 0; ks < S::NKS; ++ks)
-          mma32(sq[kb], LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half),
-                qf[qb][ks]);
+        mma32(sq[kb], LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), 8 * half), qf[qb][0]);
+      } else {
+        sq[kb] = mma32c(LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), 8 * half), qf[qb][0],
+                        f32x16{});
       }
-      if constexpr (MASK) {  // drop keys after the query
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (j0 + 32 * kb + acc_row(i, lane) > qrow[qb]) sq[kb][i] = -INFINITY;
-      }
-    };
-    f32x16 s[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) scores(qb, s[qb]);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // the half-row maximum decides (any lane over the threshold), so the
-      // exchange with lane l ^ 32 is only paid when the maximum is raised
-      float v = s[qb][0][0];
+      for (int ks = 1; ks < S::NKS; ++ks)
+        mma32(sq[kb], LdsFrag<T, S::KROW>::get(Ks, 32 * kb + (lane & 31), ks * 16 + 8 * half),
+              qf[qb][ks]);
+    }
+    if constexpr (decltype(mask_tag)::value) {  // drop keys after the query
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v = fmaxf(v, s[qb][kb][i]);
-      if (__any(v > kRescaleThreshold)) {  // raise the running maximum (wave-uniform branch)
+        for (int i = 0; i < 16; ++i)
+          if (j0 + 32 * kb + acc_row(i, lane) > qrow[qb]) sq[kb][i] = -INFINITY;
+    }
+  };
+  // probabilities (in place), their lane sum into l_run, and O^T += V^T . P^T
+  auto accumulate = [&](const char* Vs, int qb, f32x16 (&sq)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sq[kb][i] = __builtin_amdgcn_exp2f(sq[kb][i]);
+    F pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pf[ks] = FragFromAcc<T>::get(sq[ks >> 1], 8 * (ks & 1));
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      l0 += sq[0][i];
+      l1 += sq[1][i];
+    }
+    l_run[qb] += l0 + l1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+        mma32(o[qb][db], LdsFrag<T, S::VROW>::get(Vs, 32 * db + (lane & 31), ks * 16 + 8 * half),
+              pf[ks]);
+  };
+
+  // one 64-key tile for this wave's QB query blocks: S^T of every block is
+  // issued first (the MFMAs run on while the wave moves on), then each
+  // block's softmax overlaps the next block's S^T or the previous block's
+  // O^T update
+  auto tile_fast = [&](const char* Ks, const char* Vs, int j0, auto masked) {
+    f32x16 sq[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) scores(Ks, j0, qb, std::false_type{}, masked, sq[qb]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) accumulate(Vs, qb, sq[qb]);
+  };
+  // the fallback: the maximum is raised when a tile's (half-row) maximum
+  // exceeds it by more than the threshold; the exchange with lane l ^ 32 is
+  // only paid then
+  auto tile_shifted = [&](const char* Ks, const char* Vs, int j0, auto masked) {
+    f32x16 sq[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) scores(Ks, j0, qb, std::true_type{}, masked, sq[qb]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float v = sq[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v = fmaxf(v, sq[qb][kb][i]);
+      if (__any(v > kRescaleThreshold)) {  // wave-uniform branch
         const float mx = fmaxf(fmaxf(v, __shfl_xor(v, 32, 64)), 0.f);
-        const float m_new = ShiftOp<T>::round_up(m_run[qb] + mx);
+        const float m_new = m_run[qb] + mx;
         const float sh = m_new - m_run[qb];
         const float alpha = __builtin_amdgcn_exp2f(-sh);
         m_run[qb] = m_new;
@@ -287,43 +365,70 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[qb][kb][i] -= sh;
+          for (int i = 0; i < 16; ++i) sq[qb][kb][i] -= sh;
       }
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(s[qb][kb][i]);
-          s[qb][kb][i] = pv;
-          ls += pv;
-        }
-      l_run[qb] += ls;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const F pf = FragFromAcc<T>::get(s[qb][ks >> 1], 8 * (ks & 1));
-#pragma unroll
-        for (int db = 0; db < S::NDB; ++db)
-          mma32(o[qb][db], LdsFrag<T, S::VROW>::get(Vs, 32 * db + (lane & 31), ks * 16 + 8 * half), pf);
-      }
+      accumulate(Vs, qb, sq[qb]);
     }
   };
 
-  dma_barrier(0);
-  for (int it = 0; it < rounds; ++it) {
-    const int jt = tile_of(it);
-    const int jn = it + 1 < rounds ? tile_of(it + 1) : ntiles;  // next round's tile
-    if (jn < ntiles) dl_issue(jn, (it + 1) & 1);
-    const char* Ks = gsm + (it & 1) * S::STAGE;
-    const char* Vs = Ks + S::KT;
-    const int j0 = jt * S::BKV;
-    if ((NS == 1 || jt < ntiles) && wave_active && j0 <= wave_last) {
-      if (j0 + S::BKV - 1 <= qw0)
-        tile(Ks, Vs, j0, std::false_type{});
-      else
-        tile(Ks, Vs, j0, std::true_type{});
-    }
+  // the key walk of this group; the first tile's copy is already in flight
+  // on the first walk
+  auto walk = [&](auto tilef, bool first_issued) {
+    if (!first_issued && tile_of(0) < ntiles) dl_issue(tile_of(0), 0);
     dma_barrier(0);
+    for (int it = 0; it < rounds; ++it) {
+      const int jt = tile_of(it);
+      const int jn = it + 1 < rounds ? tile_of(it + 1) : ntiles;  // next round's tile
+      if (jn < ntiles) dl_issue(jn, (it + 1) & 1);
+      const char* Ks = gsm + (it & 1) * S::STAGE;
+      const char* Vs = Ks + S::KT;
+      const int j0 = jt * S::BKV;
+      if ((NS == 1 || jt < ntiles) && wave_active && j0 <= wave_last) {
+        if (j0 + S::BKV - 1 <= qw0)
+          tilef(Ks, Vs, j0, std::false_type{});
+        else
+          tilef(Ks, Vs, j0, std::true_type{});
+      }
+      dma_barrier(0);
+    }
+  };
+
+  // the fast path for the whole block, or the fallback; a block whose fast
+  // result fails the range checks is recomputed with the fallback
+  if constexpr (MODE == kFallbackOnly) {
+    reset(true);
+    walk(tile_shifted, true);
+  } else if (__syncthreads_or(fast ? 0 : 1) == 0) {
+    reset(false);
+    walk(tile_fast, true);
+    bool ok = true;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+      float os = 0.f;
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) os += o[qb][db][i];
+      if (qrow[qb] < L) ok = ok && lt >= kFastSumMin && lt <= kFastSumMax && fabsf(os) <= kFastSumMax;
+    }
+    const int redo = __syncthreads_or(ok ? 0 : 1);
+    if constexpr (MODE == kFastOnly) {
+      if (threadIdx.x == 0) p.redo[blockIdx.x] = redo;
+      if (redo) return;
+    } else if (redo) {
+      reset(true);
+      walk(tile_shifted, false);
+    }
+  } else {
+    if constexpr (MODE == kFastOnly) {
+      if (threadIdx.x == 0) p.redo[blockIdx.x] = 1;
+      wait_vm(0);  // the first tile's copy lands before the block's LDS is released
+      return;
+    } else {
+      reset(true);
+      walk(tile_shifted, true);
+    }
   }
 
   if constexpr (NS > 1) {
@@ -400,21 +505,33 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   }
 }
 
-template <typename T, int D, int QB, int QW, int NS>
+template <typename T, int D, int QB, int QW, int NS, int MODE>
+hipError_t launch_attention_mode(const AttnParams& p, long long blocks, hipStream_t stream) {
+  typedef AttnShape<T, D, QB, QW, NS> S;
+  if (S::LDS > 65536) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attention_kernel<T, D, QB, QW, NS, MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL((attention_kernel<T, D, QB, QW, NS, MODE>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(S::THREADS), S::LDS, stream, p);
+  return hipGetLastError();
+}
+
+// SPLIT: the fast path and the fallback in two launches (p.redo must hold one
+// int per block); otherwise one launch with the fallback inline
+template <typename T, int D, int QB, int QW, int NS, bool SPLIT>
 hipError_t launch_attention_d(const AttnParams& p, hipStream_t stream) {
   typedef AttnShape<T, D, QB, QW, NS> S;
   const int nq = (p.L + S::BQ - 1) / S::BQ;
   const long long blocks = static_cast<long long>(nq) * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  if (S::LDS > 65536) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attention_kernel<T, D, QB, QW, NS>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
-    if (attr != hipSuccess) return attr;
-  }
-  hipLaunchKernelGGL((attention_kernel<T, D, QB, QW, NS>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(S::THREADS), S::LDS, stream, p);
-  return hipGetLastError();
+  if (!SPLIT || p.redo == nullptr)
+    return launch_attention_mode<T, D, QB, QW, NS, kInline>(p, blocks, stream);
+  const hipError_t e = launch_attention_mode<T, D, QB, QW, NS, kFastOnly>(p, blocks, stream);
+  if (e != hipSuccess) return e;
+  return launch_attention_mode<T, D, QB, QW, NS, kFallbackOnly>(p, blocks, stream);
 }
 
 }  // namespace
@@ -428,21 +545,21 @@ hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream) {
   const bool wide = static_cast<long long>(p.L) * p.B * p.H >= 256LL * 256 * 4;
   if constexpr (sizeof(T) == 2) {
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1>(p, stream)
-                           : launch_attention_d<T, 32, 1, 2, 4>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1>(p, stream)
-                           : launch_attention_d<T, 64, 1, 2, 4>(p, stream);
-      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1>(p, stream)
-                            : launch_attention_d<T, 128, 1, 2, 2>(p, stream);
+      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1, true>(p, stream)
+                           : launch_attention_d<T, 32, 1, 2, 4, false>(p, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1, true>(p, stream)
+                           : launch_attention_d<T, 64, 1, 2, 4, false>(p, stream);
+      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1, true>(p, stream)
+                            : launch_attention_d<T, 128, 1, 2, 2, false>(p, stream);
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1>(p, stream)
-                           : launch_attention_d<T, 32, 1, 2, 4>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1>(p, stream)
-                           : launch_attention_d<T, 64, 1, 2, 2>(p, stream);
-      case 128: return launch_attention_d<T, 128, 1, 4, 1>(p, stream);
+      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1, false>(p, stream)
+                           : launch_attention_d<T, 32, 1, 2, 4, false>(p, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1, false>(p, stream)
+                           : launch_attention_d<T, 64, 1, 2, 2, false>(p, stream);
+      case 128: return launch_attention_d<T, 128, 1, 4, 1, false>(p, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -92,7 +92,14 @@ struct AttnParams {
   // optional [B, H, L]: log2 of each row's softmax normalizer in the units of
   // the scaled scores (max + log2(sum of 2^(s - max))), or NULL
   float* lse;
+  // scratch of attention_redo_ints(B, H, L) ints, or NULL: long launches then
+  // run the fast path and the fallback as two launches (one flag per block)
+  int* redo;
 };
+// ints of the per-block flag array of a launch over B x H heads of L rows
+inline long long attention_redo_ints(int B, int H, int L) {
+  return static_cast<long long>(B) * H * ((L + 31) / 32);
+}
 template <typename T>
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream);
 
