@@ -17,7 +17,8 @@
  *  - Every pointer is a DEVICE pointer owned by the caller, except `cfg` and
  *    `layout`, which are host pointers read (or written) before the call
  *    returns.  The library never allocates or frees device memory and holds
- *    no global mutable state.  Every call is thread-safe; calls that share a
+ *    no global mutable state, except gqe_forward_noalloc's per-device scratch
+ *    array (described there).  Every call is thread-safe; calls that share a
  *    workspace must not overlap.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream), and only on `stream`.  No call synchronizes the host.
@@ -202,6 +203,23 @@ int gqe_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace
 int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
                 const void* Wv, const void* Wr, const void* Wo, void* out,
                 void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* gqe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace is a library-owned array of GQE_NOALLOC_SCRATCH_BYTES in device
+ * memory, one per device, which the device holds from the first use of the
+ * library on it until the process ends.  The call allocates and frees
+ * nothing.  Every call on a device shares that device's array, so calls that
+ * overlap on one device (other streams, other threads) race; the routing
+ * and other intermediates of the last call stay in it and are not exposed.
+ * Returns GQE_ERR_WORKSPACE when the layer's workspace
+ * (gqe_workspace_bytes(cfg)) exceeds GQE_NOALLOC_SCRATCH_BYTES (32 MiB:
+ * e.g. B*L <= 8192 tokens of the d_model 1024, G 4, E 4, k 2, d_h 64 layer),
+ * and otherwise what gqe_forward returns. */
+#define GQE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int gqe_forward_noalloc(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                        const void* Wv, const void* Wr, const void* Wo, void* out,
+                        hipStream_t stream);
 
 /* Dense GQA baseline, all G*E query heads active (pptc.cn section 4.2: the
  * all-active comparison model).  Wq [G*E*d_h, d_model], Wo [d_model, G*E*d_h];

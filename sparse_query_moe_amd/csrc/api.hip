@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/gqe.h"
 #include "kernels.h"
@@ -282,7 +283,45 @@ int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool d
 
 }  // namespace
 
+// the workspace of gqe_forward_noalloc (see below)
+static __device__ __align__(256) unsigned char scratch[GQE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// ---- the workspace of gqe_forward_noalloc ------------------------------------
+// One array per device, part of the library's code object: it exists from the
+// moment the runtime loads that object on a device until the process ends.
+// Host code never uses its name as an address (on the host the name stands
+// for a host-side shadow); the device address comes from hipGetSymbolAddress,
+// once per device with that device current, and is kept per device.
+constexpr size_t kNoAllocBytes = GQE_NOALLOC_SCRATCH_BYTES;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];  // device address of `scratch` per device, once resolved
+
+int noalloc_scratch(hipStream_t stream, void** addr) {
+  int dev = -1;
+  const hipError_t e = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return GQE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GQE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_addr[dev] == nullptr) {  // first call on this device (retried after a failure)
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return GQE_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return GQE_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t ge = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (ge != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return GQE_ERR_HIP;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return GQE_OK;
+}
 
 // ---- decode ------------------------------------------------------------------
 
@@ -718,6 +757,17 @@ int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void
   if ((st = gqe_project(cfg, x, Wq, Wk, Wv, workspace, ws_bytes, stream)) != GQE_OK) return st;
   if ((st = gqe_attention(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
   return gqe_output(cfg, Wo, out, workspace, ws_bytes, stream);
+}
+
+int gqe_forward_noalloc(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
+                        const void* Wv, const void* Wr, const void* Wo, void* out,
+                        hipStream_t stream) {
+  int st = check_cfg(cfg);
+  if (st != GQE_OK || empty(cfg)) return st;
+  if (make_layout(cfg, false).pub.total > kNoAllocBytes) return GQE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(stream, &ws)) != GQE_OK) return st;
+  return gqe_forward(cfg, x, Wq, Wk, Wv, Wr, Wo, out, ws, kNoAllocBytes, stream);
 }
 
 int gqa_project(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
