@@ -13,17 +13,34 @@
 //                  4.3, the in-group softmax p itself: the sum runs over
 //                  all E experts).
 //
-// The logits are accumulated in float64 on the fp64 matrix cores
-// (v_mfma_f64_16x16x4: 16 tokens x 16 experts x 4 model dims per
-// instruction): bf16 or fp32 inputs are exact in float64, so the only rounding
-// is in the sums, far below the gaps that decide the selection.
+// Two kernels compute the logits.
 //
-// A block of 4 waves takes 16 tokens; each wave accumulates a quarter of the
-// model dimension and the four partial 16x16 tiles are added in LDS in a fixed
-// order (deterministic).  Every lane loads 8 consecutive elements of x and of
-// Wr per 32-dimension step and feeds them to 8 MFMAs; the K index each
+// bf16 layers (router_bf16_kernel): the products of two bf16 values are
+// exact in float32, so the bf16 matrix cores (v_mfma_f32_16x16x32_bf16: 16
+// tokens x 16 experts x 32 model dims) form every 32-dim partial sum with
+// float32 rounding only, and each partial is added into float64
+// accumulators.  The result is within
+//     31 * 2^-24 * sum_i |x_i| |w_i|  <=  31 * 2^-24 * ||x_t|| * ||w_e||
+// of the exact logit (a sequential float32 sum of 32 products at worst,
+// then float64 sums).  Wherever a gap that decides the selection or the rank
+// order of a (token, group) is within twice that bound, the group's logits
+// are recomputed from the products in float64 in a fixed order (the same
+// accuracy as the float64 kernel below), so every decision is the one the
+// float64 logits make.  One wave takes 16 tokens and all experts; x is read
+// once, W_r once per wave (from L2), and the kernel is bound by HBM.
+//
+// fp32 layers, and model widths that are not a multiple of 32
+// (router_f64_kernel): the logits are accumulated in float64 on the fp64
+// matrix cores (v_mfma_f64_16x16x4: 16 tokens x 16 experts x 4 model dims);
+// fp32 inputs are exact in float64, so the only rounding is in the sums.  A
+// block of 4 waves takes 16 tokens; each wave accumulates a quarter of the
+// model dimension and the four partial 16x16 tiles are added in LDS in a
+// fixed order (deterministic).  Every lane loads 8 consecutive elements of x
+// and of Wr per 32-dimension step and feeds them to 8 MFMAs; the K index each
 // (lane, step) pair covers is the same for both operands, so the products
-// pair up correctly.  The selection computes each expert's rank (number of
+// pair up correctly.
+//
+// The selection (both kernels) computes each expert's rank (number of
 // experts ahead of it), which needs no per-thread arrays.
 #include "device_common.h"
 #include "kernels.h"
@@ -38,7 +55,7 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kTok = 16;
 
 template <typename T>
-__global__ __launch_bounds__(256) void router_topk_kernel(
+__global__ __launch_bounds__(256) void router_f64_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int n_tokens, int d, int G, int E,
     GroupK gk, int renorm) {
@@ -130,15 +147,263 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 router: 4 waves x 16 tokens; NE tiles of 16 experts
+// ---------------------------------------------------------------------------
+// the selection of one (token, group) from its E logits r: ranks (larger
+// logit first, ties to the lower index), then w = exp(r - max) / z with z the
+// sum over the selected experts (all E when !renorm) in expert order.  Returns
+// the smallest gap between consecutive ranks that decides the selection or
+// its order (ranks 0 .. min(k, E-1)), and writes idx/w when `write`.
+__device__ __forceinline__ double select_group(const double* r, int E, int k, int renorm,
+                                               int32_t* idx_out, float* w_out, bool write) {
+  double rmax = r[0];
+  for (int f = 1; f < E; ++f) rmax = fmax(rmax, r[f]);
+  const int kk = k < E - 1 ? k : E - 1;
+  double z = 0.0, mingap = INFINITY;
+  for (int e = 0; e < E; ++e) {
+    int rank = 0;
+    for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
+    if (rank < k || !renorm) z += exp(r[e] - rmax);
+    if (rank < kk) {  // the gap to the next rank: the largest logit ranked after e
+      double nxt = -INFINITY;
+      for (int f = 0; f < E; ++f)
+        if (r[f] < r[e] || (r[f] == r[e] && f > e)) nxt = fmax(nxt, r[f]);
+      mingap = fmin(mingap, r[e] - nxt);
+    }
+  }
+  if (write) {
+    for (int e = 0; e < E; ++e) {
+      int rank = 0;
+      for (int f = 0; f < E; ++f) rank += (r[f] > r[e]) || (r[f] == r[e] && f < e);
+      if (rank < k) {
+        idx_out[rank] = e;
+        w_out[rank] = static_cast<float>(exp(r[e] - rmax) / z);
+      }
+    }
+  }
+  return mingap;
+}
+
+// KS: waves that split the model dimension of one 16-token tile (4 for short
+// launches, so that enough blocks exist; 1 for long ones, where every wave
+// takes its own tile and W_r is read once per 64 tokens).  Their float64
+// partial sums are added in LDS in a fixed order.
+template <int NE, int KS>
+__global__ __launch_bounds__(256) void router_bf16_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int n_tokens, int d, int G, int E,
+    GroupK gk, int renorm) {
+  constexpr int TB = 16 * (4 / KS);  // tokens per block
+  __shared__ double logit[TB][65];
+  __shared__ double part[KS > 1 ? KS : 1][TB][KS > 1 ? 64 : 1];
+  __shared__ float xpart[KS][TB], wpart[KS][64];
+  __shared__ float xnorm[TB], wnorm[64];
+  __shared__ unsigned char redo[TB * 64];  // (token, group) pairs recomputed exactly
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, kq = lane >> 4;
+  const int tile = wave / KS, ksp = wave % KS;
+  const int blk0 = blockIdx.x * TB;
+  const int t0 = blk0 + tile * 16;
+  const int GE = G * E;
+  const int tok = t0 + row;
+  const int nsteps = d / 32 / KS;  // steps of this wave
+  const int kbase = ksp * nsteps * 32;
+  const bf16_t* xp = x + static_cast<size_t>(tok < n_tokens ? tok : 0) * d + kbase + 8 * kq;
+  const bf16_t* wp[NE];
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+    const int e = 16 * n + row;
+    wp[n] = wr + static_cast<size_t>(e < GE ? e : 0) * d + kbase + 8 * kq;
+  }
+  double acc[NE][4];
+  float wsq[NE];
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+    wsq[n] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[n][i] = 0.0;
+  }
+  float xsq = 0.f;
+  // 32 model dims per MFMA; U steps of loads are issued before their MFMAs
+  constexpr int U = NE <= 2 ? 8 : 4;
+  auto sq8 = [](const bf16x8& v) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = fmaf(static_cast<float>(v[j]), static_cast<float>(v[j]), s);
+    return s;
+  };
+  for (int st = 0; st < nsteps; st += U) {
+    bf16x8 a[U], b[U][NE];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int o = (st + u < nsteps ? st + u : 0) * 32;
+      a[u] = load_frag(xp + o);
+#pragma unroll
+      for (int n = 0; n < NE; ++n) b[u][n] = load_frag(wp[n] + o);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (st + u >= nsteps) break;
+      xsq += sq8(a[u]);
+#pragma unroll
+      for (int n = 0; n < NE; ++n) {
+        wsq[n] += sq8(b[u][n]);
+        const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][n], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                               0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[n][i] += static_cast<double>(c[i]);
+      }
+    }
+  }
+  // lanes row, row+16, row+32, row+48 hold disjoint dims of token / expert `row`
+  xsq += __shfl_xor(xsq, 16, 64);
+  xsq += __shfl_xor(xsq, 32, 64);
+  if (kq == 0) xpart[ksp][tile * 16 + row] = xsq;
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+    float v = wsq[n];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (tile == 0 && kq == 0 && 16 * n + row < 64) wpart[ksp][16 * n + row] = v;
+  }
+  // accumulator of the 16x16 MFMA: value i of lane l is D[4*(l/16) + i][l % 16],
+  // i.e. token 4*kq + i of the wave's tile, expert 16*n + row
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+    const int e = 16 * n + row;
+    if (e < GE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = tile * 16 + 4 * kq + i;
+        if constexpr (KS == 1)
+          logit[tt][e] = acc[n][i] + (bias ? static_cast<double>(bias[e]) : 0.0);
+        else
+          part[ksp][tt][e] = acc[n][i];
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (KS > 1) {  // the split sums, in a fixed order
+    for (int i = tid; i < TB * GE; i += 256) {
+      const int tt = i / GE, e = i % GE;
+      double v = part[0][tt][e];
+#pragma unroll
+      for (int k = 1; k < KS; ++k) v += part[k][tt][e];
+      logit[tt][e] = v + (bias ? static_cast<double>(bias[e]) : 0.0);
+    }
+  }
+  for (int i = tid; i < TB + 64; i += 256) {
+    float v = 0.f;
+    if (i < TB) {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) v += xpart[k][i];
+      xnorm[i] = sqrtf(v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) v += wpart[k][i - TB];
+      wnorm[i - TB] = sqrtf(v);
+    }
+  }
+  __syncthreads();
+
+  // selection per (token, group); a pair whose deciding gap is within twice
+  // the error bound of its logits is flagged for the exact recomputation
+  constexpr float kErr = 32.f * 0x1p-23f;  // per unit of ||x|| ||w||, with margin
+  const int tasks = TB * G;
+  for (int task = tid; task < tasks; task += 256) {
+    const int tt = task / G, g = task % G;
+    const int gt = blk0 + tt;
+    float wmax = 0.f;
+    for (int e = 0; e < E; ++e) wmax = fmaxf(wmax, wnorm[g * E + e]);
+    const double tol = 2.0 * static_cast<double>(kErr) * xnorm[tt] * wmax;
+    const bool valid = gt < n_tokens;
+    const size_t o = static_cast<size_t>(valid ? gt : 0) * gk.K + gk.koff[g];
+    const double gap = select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, false);
+    const bool fix = valid && !(gap > tol);
+    redo[task] = fix ? 1 : 0;
+    if (valid && !fix) select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, true);
+  }
+  __syncthreads();
+
+  // exact recomputation of the flagged pairs: one wave per pair, 16 lanes per
+  // expert (4 experts at a time), each lane 8 dims per 16-byte load at a
+  // stride of 128 dims; float64 products summed lane-sequentially, then over
+  // the 16 lanes in a fixed butterfly
+  for (int c0 = wave * 64; c0 < tasks; c0 += 256) {
+    uint64_t m = __ballot(c0 + lane < tasks && redo[c0 + lane] != 0);
+    while (m) {
+      const int task = c0 + __builtin_ctzll(m);
+      m &= m - 1;
+      const int tt = task / G, g = task % G;
+      const bf16_t* xr = x + static_cast<size_t>(blk0 + tt) * d;
+      const int eg = lane >> 4, sl = lane & 15;
+      for (int e0 = 0; e0 < E; e0 += 4) {
+        const int e = e0 + eg;
+        const bf16_t* wrow = wr + static_cast<size_t>(g * E + (e < E ? e : 0)) * d;
+        double sacc = 0.0;
+#pragma unroll 8
+        for (int c = 8 * sl; c < d; c += 128) {
+          const bf16x8 xv = load_frag(xr + c), wv = load_frag(wrow + c);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            sacc = fma(static_cast<double>(static_cast<float>(xv[j])),
+                       static_cast<double>(static_cast<float>(wv[j])), sacc);
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) sacc += __shfl_xor(sacc, off, 64);
+        if (e < E && sl == 0)
+          logit[tt][g * E + e] = sacc + (bias ? static_cast<double>(bias[g * E + e]) : 0.0);
+      }
+    }
+  }
+  __syncthreads();
+  for (int task = tid; task < tasks; task += 256) {
+    if (!redo[task]) continue;
+    const int tt = task / G, g = task % G;
+    const size_t o = static_cast<size_t>(blk0 + tt) * gk.K + gk.koff[g];
+    select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, true);
+  }
+}
+
+template <int NE>
+void launch_router_bf16(bool split, dim3 grid, const bf16_t* x, const bf16_t* wr, const float* bias,
+                        int32_t* idx, float* w, int n_tokens, int d, int G, int E, const GroupK& gk,
+                        int renorm, hipStream_t stream) {
+  if (split)
+    hipLaunchKernelGGL((router_bf16_kernel<NE, 4>), grid, dim3(256), 0, stream, x, wr, bias, idx, w,
+                       n_tokens, d, G, E, gk, renorm);
+  else
+    hipLaunchKernelGGL((router_bf16_kernel<NE, 1>), grid, dim3(256), 0, stream, x, wr, bias, idx, w,
+                       n_tokens, d, G, E, gk, renorm);
+}
+
 }  // namespace
 
 template <typename T>
 hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* idx, float* w,
                          int n_tokens, int d, int G, int E, const GroupK& gk, bool renorm,
                          hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2) {
+    const int GE = G * E;
+    if (d % 32 == 0 && GE <= 64) {
+      // short launches split every 16-token tile's model dims over 4 waves
+      const bool split = n_tokens <= 32768 && d % 128 == 0;
+      const int tb = split ? 16 : 64;
+      const dim3 grid((n_tokens + tb - 1) / tb);
+      const int r = renorm ? 1 : 0;
+      switch ((GE + 15) / 16) {
+        case 1: launch_router_bf16<1>(split, grid, x, wr, bias, idx, w, n_tokens, d, G, E, gk, r, stream); break;
+        case 2: launch_router_bf16<2>(split, grid, x, wr, bias, idx, w, n_tokens, d, G, E, gk, r, stream); break;
+        case 3: launch_router_bf16<3>(split, grid, x, wr, bias, idx, w, n_tokens, d, G, E, gk, r, stream); break;
+        default: launch_router_bf16<4>(split, grid, x, wr, bias, idx, w, n_tokens, d, G, E, gk, r, stream); break;
+      }
+      return hipGetLastError();
+    }
+  }
   const int blocks = (n_tokens + kTok - 1) / kTok;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_topk_kernel<T>, dim3(blocks), dim3(256), 0, stream, x, wr, bias, idx,
+  hipLaunchKernelGGL(router_f64_kernel<T>, dim3(blocks), dim3(256), 0, stream, x, wr, bias, idx,
                      w, n_tokens, d, G, E, gk, renorm ? 1 : 0);
   return hipGetLastError();
 }

@@ -413,3 +413,109 @@ def test_empty_and_errors(gqe):
                         small)
     with pytest.raises(gqe.GqeError, match="UNSUPPORTED"):
         gqe.gqe_workspace_layout(gqe.make_config(1, 64, wl.d_model, 4, 4, 2, 80))
+
+
+# ---------------------------------------------------------------------------
+# routing ties against the oracle
+# ---------------------------------------------------------------------------
+
+def _route_case(kind, rng):
+    """Inputs whose routing hinges on exact ties or on a bias far below any
+    rounding of the logits (the tie rule: lower expert index first)."""
+    wl = W.WORKLOADS["l2k"].with_(seq_len=512)
+    I = dict(W.make_inputs(wl, seed=7, with_gqa=True))
+    G, E, d = wl.n_groups, wl.n_experts, wl.d_model
+    if kind == "zero_router":            # every logit 0: experts 0 and 1 everywhere
+        I["wr"] = np.zeros_like(I["wr"])
+    elif kind == "duplicate_rows":       # experts 1 and 3 of every group share a router row
+        wr = I["wr"].copy()
+        for g in range(G):
+            wr[g * E + 3] = wr[g * E + 1]
+        I["wr"] = wr
+    elif kind == "integer_ties":         # small integers: every sum exact, many exact ties
+        x = rng.integers(1, 4, I["x"].shape).astype(np.float32)
+        wr = rng.integers(-3, 1, I["wr"].shape).astype(np.float32)
+        wr[0 * E + 1] = wr[0 * E + 3] = 2.0
+        wr[1 * E + 0] = wr[1 * E + 2] = 1.0
+        I["x"] = W.f32_to_bf16_bits(x)
+        I["wr"] = W.f32_to_bf16_bits(wr)
+    elif kind == "bias_decides":         # identical rows; a 2^-44 bias ranks expert 2 first
+        wr = I["wr"].copy()
+        for g in range(G):
+            wr[g * E + 2] = wr[g * E + 1]
+        I["wr"] = wr
+        br = np.zeros(G * E, dtype=np.float32)
+        br[[g * E + 2 for g in range(G)]] = np.float32(2.0 ** -44)
+        I["br"] = br
+    return wl, I
+
+
+@pytest.mark.parametrize("kind", ["zero_router", "duplicate_rows", "integer_ties", "bias_decides"])
+def test_routing_ties_match_oracle(gqe, kind):
+    """idx (and w, and the dispatch lists) from gqe_route/gqe_dispatch equal
+    the oracle's on inputs where the tie rule or a bias of 2^-44 decides."""
+    rng = np.random.default_rng(31)
+    wl, I = _route_case(kind, rng)
+    log(f"[route ties] {kind}")
+    F = f64_inputs(wl, I)
+    r, p, idx, w = oracle.route(F["x"].reshape(-1, wl.d_model), F["wr"], F["br"], wl.n_groups,
+                                wl.n_experts, wl.top_k)
+    idx = idx.reshape(wl.batch, wl.seq_len, wl.n_groups, wl.top_k)
+    counts, offsets, pos, slot = oracle.dispatch(idx, wl.n_experts)
+    dev = device_inputs(wl, I)
+    cfg = cfg_for(gqe, wl, dev["br"])
+    ws = gqe.alloc_workspace(cfg)
+    gqe.gqe_route(cfg, dev["x"], dev["wr"], ws)
+    gqe.gqe_dispatch(cfg, ws)
+    torch.cuda.synchronize()
+    check_routing(gqe, cfg, ws, dict(idx=idx, w=w.reshape(idx.shape), counts=counts,
+                                     offsets=offsets, pos=pos, slot=slot))
+    if kind == "zero_router":
+        assert (idx == np.arange(wl.top_k)).all()
+    if kind == "bias_decides":   # expert 2 always beats its twin by 2^-44
+        assert (idx[..., 0] != 1).all()
+
+
+# ---------------------------------------------------------------------------
+# negative controls: the gates reject plausible wrong answers
+# ---------------------------------------------------------------------------
+
+def test_gates_reject_wrong_layers(gqe):
+    """The GPU layer passes the output gate against the oracle, and fails it
+    against the oracle's slot vectors rearranged the way plausible mistakes
+    would: the two hard slots of every group in index order instead of rank
+    order, the weighted slot dropped, the shared and weighted slots swapped,
+    and an all-zero output."""
+    wl, I = inputs("l2k", 1024)
+    cfg, ws, out = run_gqe(gqe, wl, I)
+    F = f64_inputs(wl, I)
+    ref = oracle_gqe(wl, F)
+    y = to_f64(out)
+
+    def layer_gate(got, want, what):   # the gate of test_gqe_forward
+        _, _, rel = output_gate(got, want, wl.dtype, what)
+        assert rel <= 2e-2, f"{what}: rel-L2 {rel:.3e}"
+
+    layer_gate(y, ref["y"], "the layer")
+    G, k, D = wl.n_groups, wl.top_k, wl.head_dim
+    s = ref["s"]
+    wrong = {}
+    s1 = s.copy()                                   # index order within each group
+    for g in range(G):
+        swap = ref["idx"][..., g, 0] > ref["idx"][..., g, 1]
+        a, b = (g * k) * D, (g * k + 1) * D
+        s1[swap, a:a + D], s1[swap, b:b + D] = s[swap, b:b + D], s[swap, a:a + D]
+    wrong["index-order slots"] = s1
+    s2 = s.copy()
+    s2[..., (k * G + 1) * D:] = 0.0
+    wrong["no weighted slot"] = s2
+    s3 = s.copy()
+    s3[..., k * G * D:(k * G + 1) * D], s3[..., (k * G + 1) * D:] = (s[..., (k * G + 1) * D:],
+                                                                     s[..., k * G * D:(k * G + 1) * D])
+    wrong["shared and weighted swapped"] = s3
+    for what, sw in wrong.items():
+        y_wrong = oracle.output_projection(sw, F["wo"])
+        with pytest.raises(AssertionError):
+            layer_gate(y, y_wrong, what)
+    with pytest.raises(AssertionError):
+        layer_gate(np.zeros_like(y), ref["y"], "zero output")
