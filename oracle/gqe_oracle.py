@@ -189,6 +189,34 @@ def kv_project(x_b: np.ndarray, w: np.ndarray, n_groups: int, head_dim: int,
     return out
 
 
+# Rotary position embedding, an option the pages do not name (they are silent
+# on position encoding; a model of this size would normally use one).  The
+# form is that of RoFormer (Su et al., 2021) with interleaved pairs: in every
+# query head and every key head, the pair of dims (2i, 2i+1) of the vector at
+# position t is rotated by the angle t * theta_i, theta_i = base^(-2i/d_h).
+# It is applied to the projected queries and keys, never to the values, so
+# every score depends on positions only through their difference.  base 0
+# means no rotation (the layer of the pages).
+
+
+def rope(v: np.ndarray, t, base: float, inverse: bool = False) -> np.ndarray:
+    """v [..., d_h] at positions t (broadcast against v's leading axes)
+    rotated pairwise by t * theta_i; inverse rotates back (the transpose)."""
+    if not base:
+        return v
+    dh = v.shape[-1]
+    theta = float(base) ** (-2.0 * np.arange(dh // 2) / dh)
+    ang = np.asarray(t, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    if inverse:
+        s = -s
+    x0, x1 = v[..., 0::2], v[..., 1::2]
+    out = np.empty(np.broadcast_shapes(v.shape, c.shape[:-1] + (dh,)))
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
 def causal_attention(q: np.ndarray, t: np.ndarray, K: np.ndarray, V: np.ndarray,
                      scale: float) -> np.ndarray:
     """o[i] = sum_{s <= t[i]} softmax_s(scale * q[i] . K[s]) V[s]  (step 7).
@@ -285,7 +313,7 @@ def ablation_slots(mode: str, o_hard: np.ndarray, p_sel: np.ndarray) -> np.ndarr
 
 def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
                 shared_kv_group=0, scale=None, positions=None, output_mode="full",
-                phase_times=None):
+                phase_times=None, rope_base=0.0):
     """GQE prefill forward (steps 1-11) in float64.
 
     x: [B, L, d]; wq [(G*E+1)*d_h, d]; wk, wv [G*d_h, d]; wr [G*E, d];
@@ -306,6 +334,9 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
     phase: "route" (steps 1-4), "dispatch" (5), "kv" (6), "attention"
     (7-8, query projections included) and "output" (9-11).  Timing only: it
     changes nothing that is computed.
+
+    ``rope_base`` > 0 rotates every query row and K (``rope``) after the
+    projections; q and k_ are then the rotated values.
     """
     if output_mode not in OUTPUT_MODES:
         raise ValueError(output_mode)
@@ -340,7 +371,7 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
     V_all = np.empty((B, G, upto, dh))
     for b in range(B):
         xb = x[b]
-        K_all[b] = kv_project(xb, wk, G, dh, upto)
+        K_all[b] = rope(kv_project(xb, wk, G, dh, upto), np.arange(upto), rope_base)
         V_all[b] = kv_project(xb, wv, G, dh, upto)
         tick("kv")
         xq = xb[pos_q]                                    # [n, d]
@@ -353,6 +384,7 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
                     m = e_sel == e
                     if m.any():
                         qh[m] = xq[m] @ head_rows(wq, expert_head(g, e, E), dh).T
+                qh = rope(qh, pos_q, rope_base)
                 q_all[b, :, g * k + j] = qh
                 o_hard[:, g, j] = causal_attention(qh, pos_q, K_all[b, g], V_all[b, g], scale)
         o_all[b, :, :k * G] = o_hard.reshape(n, G * k, dh)
@@ -362,7 +394,7 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
             s_all[b] = ablation_slots(output_mode, o_hard, p_sel)
             tick("output")
             continue
-        q_sh = xq @ head_rows(wq, G * E, dh).T            # step 8: always-on shared head
+        q_sh = rope(xq @ head_rows(wq, G * E, dh).T, pos_q, rope_base)  # step 8: shared head
         o_sh = causal_attention(q_sh, pos_q, K_all[b, shared_kv_group],
                                 V_all[b, shared_kv_group], scale)
         q_all[b, :, k * G] = q_sh
@@ -378,7 +410,7 @@ def gqe_forward(x, wq, wk, wv, wr, wo, br, n_groups, n_experts, top_k, head_dim,
 
 
 def gqa_forward(x, wq_dense, wk, wv, wo_dense, n_groups, n_experts, head_dim, scale=None,
-                positions=None):
+                positions=None, rope_base=0.0):
     """Dense GQA baseline: all G*E query heads active, head h reads KV group h // E.
 
     wq_dense [G*E*d_h, d]; wo_dense [d, G*E*d_h].  Returns q, o [B,n,G*E,d_h] and
@@ -395,11 +427,11 @@ def gqa_forward(x, wq_dense, wk, wv, wo_dense, n_groups, n_experts, head_dim, sc
     q_all = np.empty((B, n, H, dh))
     o_all = np.empty((B, n, H, dh))
     for b in range(B):
-        K = kv_project(x[b], wk, G, dh, upto)
+        K = rope(kv_project(x[b], wk, G, dh, upto), np.arange(upto), rope_base)
         V = kv_project(x[b], wv, G, dh, upto)
         xq = x[b][pos_q]
         for h in range(H):
-            qh = xq @ head_rows(wq_dense, h, dh).T
+            qh = rope(xq @ head_rows(wq_dense, h, dh).T, pos_q, rope_base)
             q_all[b, :, h] = qh
             o_all[b, :, h] = causal_attention(qh, pos_q, K[h // E], V[h // E], scale)
     y = output_projection(o_all.reshape(B, n, H * dh), wo_dense)
@@ -422,7 +454,8 @@ def attention_flops(batch: int, seq_len: int, heads: int, head_dim: int) -> int:
 
 
 def gqe_decode_step(x_t, k_cache, v_cache, pos, wq, wk, wv, wr, wo, br, n_groups, n_experts,
-                    top_k, head_dim, shared_kv_group=0, scale=None, output_mode="full"):
+                    top_k, head_dim, shared_kv_group=0, scale=None, output_mode="full",
+                    rope_base=0.0):
     """x_t [B, d]: the new tokens; k_cache, v_cache [B, G, Lc, d_h]: keys and
     values of positions < pos[b] (later entries are never read); pos [B].
 
@@ -437,7 +470,8 @@ def gqe_decode_step(x_t, k_cache, v_cache, pos, wq, wk, wv, wr, wo, br, n_groups
     scale = 1.0 / math.sqrt(dh) if scale is None else scale
     full = output_mode == "full"
     r, p, idx, w = route(x_t, wr, br, G, E, k)             # steps 1-4 for the new tokens
-    k_new = (x_t @ wk.T).reshape(B, G, dh)                 # step 6
+    posf = np.asarray(pos, dtype=np.int64)
+    k_new = rope((x_t @ wk.T).reshape(B, G, dh), posf[:, None], rope_base)  # step 6
     v_new = (x_t @ wv.T).reshape(B, G, dh)
     kc, vc = k_cache.copy(), v_cache.copy()
     H = k * G + (1 if full else 0)
@@ -452,7 +486,8 @@ def gqe_decode_step(x_t, k_cache, v_cache, pos, wq, wk, wv, wr, wo, br, n_groups
         o_hard = np.empty((1, G, k, dh))
         for g in range(G):
             for j in range(k):                             # step 7: the selected experts
-                qh = x_t[b] @ head_rows(wq, expert_head(g, int(idx[b, g, j]), E), dh).T
+                qh = rope(x_t[b] @ head_rows(wq, expert_head(g, int(idx[b, g, j]), E), dh).T,
+                          t, rope_base)
                 q_all[b, g * k + j] = qh
                 o_hard[0, g, j] = causal_attention(qh[None], tt, kc[b, g], vc[b, g], scale)[0]
         o_all[b, :k * G] = o_hard.reshape(G * k, dh)
@@ -460,7 +495,7 @@ def gqe_decode_step(x_t, k_cache, v_cache, pos, wq, wk, wv, wr, wo, br, n_groups
             p_sel = np.take_along_axis(p[b][None], idx[b][None].astype(np.int64), axis=-1)
             s_all[b] = ablation_slots(output_mode, o_hard, p_sel)[0]
             continue
-        q_sh = x_t[b] @ head_rows(wq, G * E, dh).T          # step 8
+        q_sh = rope(x_t[b] @ head_rows(wq, G * E, dh).T, t, rope_base)  # step 8
         o_sh = causal_attention(q_sh[None], tt, kc[b, shared_kv_group], vc[b, shared_kv_group],
                                 scale)
         q_all[b, k * G] = q_sh
@@ -473,13 +508,14 @@ def gqe_decode_step(x_t, k_cache, v_cache, pos, wq, wk, wv, wr, wo, br, n_groups
 
 
 def gqa_decode_step(x_t, k_cache, v_cache, pos, wq_dense, wk, wv, wo_dense, n_groups, n_experts,
-                    head_dim, scale=None):
+                    head_dim, scale=None, rope_base=0.0):
     """Dense GQA decode step: all G*E heads, head h reads KV group h // E."""
     B, d = x_t.shape
     G, E, dh = n_groups, n_experts, head_dim
     H = G * E
     scale = 1.0 / math.sqrt(dh) if scale is None else scale
-    k_new = (x_t @ wk.T).reshape(B, G, dh)
+    posf = np.asarray(pos, dtype=np.int64)
+    k_new = rope((x_t @ wk.T).reshape(B, G, dh), posf[:, None], rope_base)
     v_new = (x_t @ wv.T).reshape(B, G, dh)
     kc, vc = k_cache.copy(), v_cache.copy()
     o_all = np.empty((B, H, dh))
@@ -488,7 +524,7 @@ def gqa_decode_step(x_t, k_cache, v_cache, pos, wq_dense, wk, wv, wo_dense, n_gr
         kc[b, :, t] = k_new[b]
         vc[b, :, t] = v_new[b]
         for h in range(H):
-            qh = x_t[b] @ head_rows(wq_dense, h, dh).T
+            qh = rope(x_t[b] @ head_rows(wq_dense, h, dh).T, t, rope_base)
             o_all[b, h] = causal_attention(qh[None], np.array([t]), kc[b, h // E], vc[b, h // E],
                                            scale)[0]
     y = output_projection(o_all.reshape(B, H * dh), wo_dense)
@@ -549,7 +585,8 @@ def attention_backward(q, t, K, V, do, scale):
 
 
 def gqe_backward(x, wq, wk, wv, wr, wo, br, dy, n_groups, n_experts, top_k, head_dim,
-                 shared_kv_group=0, scale=None, output_mode="full", aux_weight=0.0):
+                 shared_kv_group=0, scale=None, output_mode="full", aux_weight=0.0,
+                 rope_base=0.0):
     """Gradients of <y, dy> + aux_weight * L_aux for the GQE layer (float64).
 
     Returns dx [B, L, d], dwq, dwk, dwv, dwr, dbr, dwo (the shapes of the
@@ -568,7 +605,7 @@ def gqe_backward(x, wq, wk, wv, wr, wo, br, dy, n_groups, n_experts, top_k, head
     kG = k * G
     sc = 1.0 / math.sqrt(dh) if scale is None else scale
     fwd = gqe_forward(x, wq, wk, wv, wr, wo, br, G, E, k, dh, shared_kv_group=shared_kv_group,
-                      scale=scale, output_mode=output_mode)
+                      scale=scale, output_mode=output_mode, rope_base=rope_base)
     p, idx, w, s_all, o_all = fwd["p"], fwd["idx"], fwd["w"], fwd["s"], fwd["o"]
     Sh = o_all.shape[2]
     dwo = np.einsum("bln,blc->nc", dy, s_all)             # y = s . W_O^T
@@ -613,8 +650,9 @@ def gqe_backward(x, wq, wk, wv, wr, wo, br, dy, n_groups, n_experts, top_k, head
         for h, g in heads:
             dq, dKg, dVg = attention_backward(fwd["q"][b, :, h], tpos, K[g], V[g],
                                               do_all[b, :, h], sc)
+            dq = rope(dq, tpos, rope_base, inverse=True)  # through the rotation (its transpose)
             dq_all[b, :, h] = dq
-            dk_all[b, g] += dKg
+            dk_all[b, g] += rope(dKg, tpos, rope_base, inverse=True)
             dv_all[b, g] += dVg
             if h == kG:                                   # the shared head's own W_q rows
                 rows = slice(G * E * dh, (G * E + 1) * dh)
@@ -645,13 +683,14 @@ def gqe_backward(x, wq, wk, wv, wr, wo, br, dy, n_groups, n_experts, top_k, head
                 ds=ds, do=do_all, dq=dq_all, dk=dk_all, dv=dv_all, dw=dw_all, dr=dr, fwd=fwd)
 
 
-def gqa_backward(x, wq_dense, wk, wv, wo_dense, dy, n_groups, n_experts, head_dim, scale=None):
+def gqa_backward(x, wq_dense, wk, wv, wo_dense, dy, n_groups, n_experts, head_dim, scale=None,
+                 rope_base=0.0):
     """Gradients of <y, dy> for the dense GQA baseline: dx, dwq, dwk, dwv, dwo."""
     B, L, d = x.shape
     G, E, dh = n_groups, n_experts, head_dim
     H = G * E
     sc = 1.0 / math.sqrt(dh) if scale is None else scale
-    fwd = gqa_forward(x, wq_dense, wk, wv, wo_dense, G, E, dh, scale=scale)
+    fwd = gqa_forward(x, wq_dense, wk, wv, wo_dense, G, E, dh, scale=scale, rope_base=rope_base)
     o = fwd["o"].reshape(B, L, H * dh)
     dwo = np.einsum("bln,blc->nc", dy, o)
     do = (dy @ wo_dense).reshape(B, L, H, dh)
@@ -660,13 +699,15 @@ def gqa_backward(x, wq_dense, wk, wv, wo_dense, dy, n_groups, n_experts, head_di
     tpos = np.arange(L)
     for b in range(B):
         xb = x[b]
-        K = kv_project(xb, wk, G, dh, L)
+        K = rope(kv_project(xb, wk, G, dh, L), tpos, rope_base)
         V = kv_project(xb, wv, G, dh, L)
         dK = np.zeros((G, L, dh))
         dV = np.zeros((G, L, dh))
         for h in range(H):
             g = h // E
             dq, dKg, dVg = attention_backward(fwd["q"][b, :, h], tpos, K[g], V[g], do[b, :, h], sc)
+            dq = rope(dq, tpos, rope_base, inverse=True)
+            dKg = rope(dKg, tpos, rope_base, inverse=True)
             dK[g] += dKg
             dV[g] += dVg
             rows = slice(h * dh, (h + 1) * dh)

@@ -498,6 +498,141 @@ def pin_decode_step_is_prefill_row(orc):
 
 
 # ---------------------------------------------------------------------------
+# RoPE option (RoFormer, Su et al. 2021; the pages are silent on positions)
+# ---------------------------------------------------------------------------
+
+def pin_rope_closed_forms(orc):
+    """The rotation itself: each pair (2i, 2i+1) read as a complex number is
+    multiplied by exp(i t theta_i), theta_i = base^(-2i/d_h) (so the first
+    pair turns by t radians at any base); it keeps the norm, is the identity
+    at t = 0, and the inverse undoes it."""
+    rng = np.random.default_rng(81)
+    dh, base = 8, 50.0
+    v = rng.standard_normal((5, dh))
+    t = np.array([0, 1, 7, 1000, 123457])
+    got = orc.rope(v, t, base)
+    z = (v[:, 0::2] + 1j * v[:, 1::2]) * np.exp(
+        1j * t[:, None] * base ** (-np.arange(dh // 2) * 2.0 / dh))
+    assert np.allclose(got[:, 0::2], z.real, rtol=0, atol=1e-12)
+    assert np.allclose(got[:, 1::2], z.imag, rtol=0, atol=1e-12)
+    assert np.allclose(np.linalg.norm(got, axis=1), np.linalg.norm(v, axis=1), rtol=1e-13)
+    assert np.array_equal(got[0], v[0])
+    assert np.allclose(orc.rope(got, t, base, inverse=True), v, rtol=0, atol=1e-9)
+    assert orc.rope(v, t, 0.0) is v
+
+
+def pin_rope_relative_positions(orc):
+    """With RoPE a score depends on positions only through their difference,
+    so a layer whose positions all move by the same offset is unchanged: here
+    the attention of the shifted rotations equals the original's, and the
+    layer at t = 0 (one key, rotated by 0) equals the layer without RoPE."""
+    rng = np.random.default_rng(82)
+    dh, base = 8, 30.0
+    q = rng.standard_normal((6, dh))
+    kk = rng.standard_normal((9, dh))
+    v = rng.standard_normal((9, dh))
+    tq = np.array([0, 2, 3, 5, 8, 8])
+    for shift in (1, 17, 4096):
+        a = orc.causal_attention(orc.rope(q, tq, base), tq, orc.rope(kk, np.arange(9), base), v, 0.5)
+        b = orc.causal_attention(orc.rope(q, tq + shift, base), tq,
+                                 orc.rope(kk, np.arange(9) + shift, base), v, 0.5)
+        assert np.allclose(a, b, rtol=0, atol=1e-10)
+    t = tiny_layer(rng, B=1, L=6, G=2, E=3, k=2)
+    plain = run(orc, t)
+    rot = run(orc, t, rope_base=30.0)
+    assert np.array_equal(plain["idx"], rot["idx"])
+    assert np.allclose(rot["y"][:, 0], plain["y"][:, 0], rtol=0, atol=1e-12)
+    assert not np.allclose(rot["y"][:, 1:], plain["y"][:, 1:], rtol=0, atol=1e-6)
+
+
+def pin_rope_layer_reductions(orc):
+    """k = E with a uniform router and the extra W_O rows zeroed is dense GQA
+    with RoPE too, and a decode step with RoPE is the RoPE prefill row."""
+    rng = np.random.default_rng(83)
+    base = 25.0
+    G, E = 2, 3
+    t = tiny_layer(rng, G=G, E=E, k=E)
+    t["wr"] = np.zeros_like(t["wr"])
+    dh = t["dh"]
+    wo = t["wo"].copy()
+    wo[:, G * E * dh:] = 0.0
+    t["wo"] = wo
+    a = run(orc, t, rope_base=base)
+    b = orc.gqa_forward(t["x"], t["wq"][:G * E * dh], t["wk"], t["wv"], wo[:, :G * E * dh], G, E,
+                        dh, rope_base=base)
+    assert np.allclose(a["y"], b["y"], rtol=0, atol=1e-12)
+    t_ = tiny_layer(rng, B=2, L=9, G=2, E=3, k=2)
+    G, E, k, dh = t_["G"], t_["E"], t_["k"], t_["dh"]
+    B, L = t_["x"].shape[:2]
+    pos = np.array([8, 3])
+    pre = run(orc, t_, rope_base=base)
+    K = pre["k_"]
+    V = np.stack([orc.kv_project(t_["x"][b], t_["wv"], G, dh, L) for b in range(B)])
+    kc = rng.standard_normal((B, G, 12, dh))
+    vc = rng.standard_normal((B, G, 12, dh))
+    for b in range(B):
+        kc[b, :, :pos[b]] = K[b, :, :pos[b]]
+        vc[b, :, :pos[b]] = V[b, :, :pos[b]]
+    x_t = np.stack([t_["x"][b, pos[b]] for b in range(B)])
+    dec = orc.gqe_decode_step(x_t, kc, vc, pos, t_["wq"], t_["wk"], t_["wv"], t_["wr"], t_["wo"],
+                              t_["br"], G, E, k, dh, rope_base=base)
+    for b in range(B):
+        assert np.allclose(dec["y"][b], pre["y"][b, pos[b]], rtol=0, atol=1e-12)
+        assert np.allclose(dec["k_cache"][b, :, pos[b]], K[b, :, pos[b]], rtol=0, atol=1e-12)
+    wq_d = t_["wq"][:G * E * dh]
+    wo_d = rng.standard_normal((t_["x"].shape[2], G * E * dh))
+    pre = orc.gqa_forward(t_["x"], wq_d, t_["wk"], t_["wv"], wo_d, G, E, dh, rope_base=base)
+    dec = orc.gqa_decode_step(x_t, kc, vc, pos, wq_d, t_["wk"], t_["wv"], wo_d, G, E, dh,
+                              rope_base=base)
+    for b in range(B):
+        assert np.allclose(dec["y"][b], pre["y"][b, pos[b]], rtol=0, atol=1e-12)
+
+
+def pin_rope_backward_finite_differences(orc):
+    """Central differences of <y, dy> + alpha * L_aux agree with the RoPE
+    backward on x, W_q and W_k (the inputs the rotation's transpose reaches)
+    and W_O, for GQE and dense GQA."""
+    rng = np.random.default_rng(84)
+    h, base, alpha = 1e-6, 20.0, 0.3
+    t = tiny_layer(rng, B=1, L=6, d=6, G=2, E=3, k=2, dh=4)
+    t["br"] = rng.standard_normal(t["G"] * t["E"]) * 0.3
+    f0 = run(orc, t, rope_base=base)
+    srt = -np.sort(-f0["r"], axis=-1)
+    assert (srt[..., :-1] - srt[..., 1:]).min() > 1e-3, "seed too close to a routing tie"
+    dy = rng.standard_normal(f0["y"].shape)
+    g = orc.gqe_backward(t["x"], t["wq"], t["wk"], t["wv"], t["wr"], t["wo"], t["br"], dy,
+                         t["G"], t["E"], t["k"], t["dh"], aux_weight=alpha, rope_base=base)
+    for name, key in (("x", "dx"), ("wq", "dwq"), ("wk", "dwk"), ("wo", "dwo")):
+        flat = t[name].reshape(-1)
+        for i in rng.choice(flat.size, size=min(flat.size, 20), replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp = _total_loss(orc, t, dy, alpha, rope_base=base)
+            flat[i] = old - h
+            lm = _total_loss(orc, t, dy, alpha, rope_base=base)
+            flat[i] = old
+            num = (lp - lm) / (2 * h)
+            assert abs(num - g[key].reshape(-1)[i]) <= 1e-6 * (1.0 + abs(num)), (name, i)
+    wq_d = t["wq"][:6 * 4].copy()
+    wo_d = rng.standard_normal((6, 6 * 4))
+    dy = rng.standard_normal((1, 6, 6))
+    g = orc.gqa_backward(t["x"], wq_d, t["wk"], t["wv"], wo_d, dy, 2, 3, 4, rope_base=base)
+    for arr, key in ((t["x"], "dx"), (wq_d, "dwq"), (t["wk"], "dwk")):
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(flat.size, 12), replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp = float((orc.gqa_forward(t["x"], wq_d, t["wk"], t["wv"], wo_d, 2, 3, 4,
+                                        rope_base=base)["y"] * dy).sum())
+            flat[i] = old - h
+            lm = float((orc.gqa_forward(t["x"], wq_d, t["wk"], t["wv"], wo_d, 2, 3, 4,
+                                        rope_base=base)["y"] * dy).sum())
+            flat[i] = old
+            num = (lp - lm) / (2 * h)
+            assert abs(num - g[key].reshape(-1)[i]) <= 1e-6 * (1.0 + abs(num)), ("gqa", key, i)
+
+
+# ---------------------------------------------------------------------------
 # backward: the gradients are those of the forward (finite differences), and
 # they respect the invariances of the layer
 # ---------------------------------------------------------------------------
@@ -773,6 +908,10 @@ ALL_PINS = [
     pin_sampled_rows_match_full,
     pin_ablation_constructions,
     pin_decode_step_is_prefill_row,
+    pin_rope_closed_forms,
+    pin_rope_relative_positions,
+    pin_rope_layer_reductions,
+    pin_rope_backward_finite_differences,
     pin_backward_finite_differences,
     pin_backward_invariances,
     pin_group_k_uniform_is_the_layer,

@@ -296,7 +296,39 @@ def m_group_k_bwd_softmax_over_all_slots(mod):
                   "                dr_sel = softmax_backward(w[b], dw)[:, sl]")
 
 
+def m_rope_on_values(mod):
+    """the rotation is applied to V as well."""
+    _patch_source(mod, "        V_all[b] = kv_project(xb, wv, G, dh, upto)\n",
+                  "        V_all[b] = rope(kv_project(xb, wv, G, dh, upto), np.arange(upto), rope_base)\n")
+
+
+def m_rope_off_by_one(mod):
+    """positions counted from 1."""
+    _patch_source(mod, "    ang = np.asarray(t, dtype=np.float64)[..., None] * theta",
+                  "    ang = (np.asarray(t, dtype=np.float64)[..., None] + 1.0) * theta")
+
+
+def m_rope_half_split(mod):
+    """dims i and i + d_h/2 paired instead of 2i and 2i+1."""
+    _patch_source(mod, "    x0, x1 = v[..., 0::2], v[..., 1::2]",
+                  "    x0, x1 = v[..., :dh // 2], v[..., dh // 2:]")
+
+
+def m_rope_backward_not_inverted(mod):
+    """the query gradient is rotated forward instead of back."""
+    _patch_source(mod, "            dq = rope(dq, tpos, rope_base, inverse=True)  # through the rotation (its transpose)",
+                  "            dq = rope(dq, tpos, rope_base)")
+
+
+def m_rope_queries_only(mod):
+    """keys left unrotated."""
+    _patch_source(mod, "        K_all[b] = rope(kv_project(xb, wk, G, dh, upto), np.arange(upto), rope_base)",
+                  "        K_all[b] = kv_project(xb, wk, G, dh, upto)")
+
+
 MUTATIONS = [
+    m_rope_on_values, m_rope_off_by_one, m_rope_half_split, m_rope_backward_not_inverted,
+    m_rope_queries_only,
     m_no_scale, m_strict_causal, m_no_causal_mask, m_topk_lowest, m_tie_to_highest,
     m_index_order_slots, m_renorm_over_all_groups, m_no_renorm, m_softmax_over_groups,
     m_router_group_transposed, m_router_bias_dropped, m_exact_logits_bias_dropped,
