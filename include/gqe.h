@@ -118,6 +118,14 @@ typedef struct gqe_config {
                                * non-uniform k the pages list as future work,
                                * pptc.cn section 6), or NULL for top_k in every
                                * group.  Read during each call. */
+  float rope_base;          /* rotary position embedding of queries and keys, an
+                             * option the pages do not name: 0 = none (the
+                             * layer of the pages); b > 0 turns dims (2j, 2j+1)
+                             * of every query head and key head at position t
+                             * by t * b^(-2j/head_dim) after the projections
+                             * (RoFormer's interleaved form); values are never
+                             * turned.  Prefill, decode and backward; not with
+                             * group_top_k (GQE_ERR_UNSUPPORTED). */
 } gqe_config;
 
 /* Byte offsets into the workspace of every intermediate, so that callers can

@@ -39,6 +39,7 @@ bool shape_ok(const gqe_config* c) {
   if (static_cast<long long>(c->batch) * c->seq_len * c->n_groups * c->n_experts >= (1LL << 31))
     return false;
   if (c->output_mode < GQE_OUTPUT_FULL || c->output_mode > GQE_OUTPUT_WEIGHTED_CONCAT) return false;
+  if (!(c->rope_base >= 0.f) || isinf(c->rope_base)) return false;
   return true;
 }
 
@@ -90,7 +91,18 @@ int check_cfg(const gqe_config* c) {
   if (c->head_dim < 1) return GQE_ERR_INVALID_ARG;
   if (!shape_ok(c)) return GQE_ERR_INVALID_ARG;
   if (!head_dim_ok(c) || !k_steps_ok(c)) return GQE_ERR_UNSUPPORTED;
+  if (c->rope_base > 0.f && c->group_top_k != nullptr) return GQE_ERR_UNSUPPORTED;
   return GQE_OK;
+}
+
+// theta_j = base^(-2j/d_h) of the rotary embedding, in float64
+RopeTable make_rope(const gqe_config* c) {
+  RopeTable r{};
+  r.on = c->rope_base > 0.f ? 1 : 0;
+  if (r.on)
+    for (int j = 0; j < c->head_dim / 2 && j < 64; ++j)
+      r.theta[j] = pow(static_cast<double>(c->rope_base), -2.0 * j / c->head_dim);
+  return r;
 }
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -196,6 +208,7 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   seg[0].heads = dense ? G * E : K + 1;
   seg[0].head_base = dense ? 0 : K;
   seg[0].transposed = 0;
+  seg[0].rope = 1;
   seg[1].w = wk;
   seg[1].out = at<T>(ws, l.pub.k);
   seg[1].n_begin = nq_cols;
@@ -203,6 +216,7 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   seg[1].heads = G;
   seg[1].head_base = 0;
   seg[1].transposed = 0;
+  seg[1].rope = 1;
   seg[2].w = wv;
   seg[2].out = at<T>(ws, l.pub.vt);
   seg[2].n_begin = nq_cols + G * D;
@@ -210,15 +224,17 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
   seg[2].heads = G;
   seg[2].head_base = 0;
   seg[2].transposed = 1;
+  seg[2].rope = 0;
   if (dense)
     return hip_status(launch_dense_proj<T>(static_cast<const T*>(x), B * L, d, L, D,
-                                           l.pub.vt_tiles, seg, 3, stream));
+                                           l.pub.vt_tiles, seg, 3, make_rope(c), stream));
   // dense tiles and gathered routed-query tiles in one launch
   return hip_status(launch_project<T>(
       static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_tiles, shared ? seg : seg + 1,
       shared ? 3 : 2, static_cast<const T*>(wq), at<T>(ws, l.pub.q), at<int32_t>(ws, l.pub.counts),
       at<int32_t>(ws, l.pub.offsets), at<int32_t>(ws, l.pub.pos), at<int32_t>(ws, l.pub.slot),
-      at<int32_t>(ws, l.tile_off), B, G, E, make_group_k(c), gather_tiles_per_bg(c), stream));
+      at<int32_t>(ws, l.tile_off), B, G, E, make_group_k(c), gather_tiles_per_bg(c),
+      make_rope(c), stream));
 }
 
 template <typename T>
@@ -424,6 +440,7 @@ int decode_impl(const gqe_config* c, bool dense, const void* x, const void* wq, 
   p.ld_s = decode_ld_s(c, dense);
   p.K_out = p.ld_s;
   p.weighted_slot = p.shared_head;
+  p.rope = make_rope(c);
   hipError_t e = launch_decode_front<T>(p, stream);
   if (e == hipSuccess) e = launch_decode_attend<T>(p, stream);
   return hip_status(e);
@@ -611,6 +628,7 @@ int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq
   p.dq_part = at<float>(ws, l.dq_part);
   p.scale = softmax_scale(c);
   p.aux_weight = dense ? 0.f : aux_weight;
+  p.rope = make_rope(c);
   return hip_status(launch_backward<T>(p, stream));
 }
 

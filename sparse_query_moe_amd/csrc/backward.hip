@@ -66,6 +66,28 @@ __device__ __forceinline__ float wsum(float v) {
 // ---------------------------------------------------------------------------
 // layout helpers
 // ---------------------------------------------------------------------------
+// Rotary embedding backward: the attention backward leaves in Gall the
+// gradients of the turned queries and keys; the projections need them turned
+// back (the transpose of the rotation) at each row's position.  One thread
+// per (row, pair of dims) of the query and key column blocks.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_back_kernel(T* __restrict__ gall, int rows, int ldg,
+                                                        int qcols, int kcol, int kcols, int L,
+                                                        int D, RopeTable rope) {
+  const int pq = qcols / 2, pairs = pq + kcols / 2;
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<size_t>(rows) * pairs) return;
+  const int row = static_cast<int>(i / pairs), pr = static_cast<int>(i % pairs);
+  const int c = pr < pq ? 2 * pr : 2 * (pr - pq);  // column inside the block
+  const int dim = c % D;
+  T* gp = gall + static_cast<size_t>(row) * ldg + (pr < pq ? c : kcol + c);
+  const float v0 = to_f32(gp[0]), v1 = to_f32(gp[1]);
+  float cs, sn;
+  rope_cs(row % L, rope.theta[dim >> 1], cs, sn);
+  gp[0] = from_f32<T>(rope_apply(v0, v1, dim, cs, sn, true));
+  gp[1] = from_f32<T>(rope_apply(v1, v0, dim + 1, cs, sn, true));
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
   for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
        i += static_cast<size_t>(gridDim.x) * 256)
@@ -1339,6 +1361,14 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
         default: return hipErrorInvalidValue;
       }
     }
+  }
+  // the query and key gradients turned back by position (rotary embedding)
+  if (p.rope.on) {
+    const size_t n = static_cast<size_t>(T_) * (p.qcols / 2 + G * D / 2);
+    hipLaunchKernelGGL(rope_back_kernel<T>, dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, stream, static_cast<T*>(p.gall), T_, p.kpad, p.qcols, p.kcol,
+                       G * D, L, D, p.rope);
+    GQE_TRY(hipGetLastError());
   }
   // 4. router backward and the auxiliary loss
   if (p.wr != nullptr) {

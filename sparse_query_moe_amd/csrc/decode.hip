@@ -613,6 +613,8 @@ struct RowsGemmArgs {
   // are sum_h w[m, h] * A[m, h*D + c] over h < ws_heads, rounded to T
   const float* ws_w;
   int ws_col, ws_heads;
+  // rotary embedding of the query and key columns of the decode projection
+  RopeTable rope;
 };
 
 template <typename T>
@@ -677,8 +679,19 @@ __device__ __forceinline__ void gemm_tile(const RowsGemmArgs& a, int n0, int m0)
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int i = 4 * wave + ii;
-    const float v = red[0][i][lane] + red[1][i][lane] + red[2][i][lane] + red[3][i][lane];
+    float v = red[0][i][lane] + red[1][i][lane] + red[2][i][lane] + red[3][i][lane];
     const int row = m0 + acc_row(i, lane);
+    if (a.out == nullptr && a.rope.on) {  // queries and keys turn by the token's position
+      const float partner = __shfl_xor(v, 1, 64);  // column col ^ 1, the pair partner
+      const bool qk = col < a.nq || col - a.nq < a.G * a.D;
+      const int t = row < a.M ? a.pos[row] : -1;
+      if (qk && t >= 0 && t < a.Lc) {
+        const int dim = (col < a.nq ? col : col - a.nq) % a.D;
+        float cs, sn;
+        rope_cs(t, a.rope.theta[dim >> 1], cs, sn);
+        v = rope_apply(v, partner, dim, cs, sn);
+      }
+    }
     if (row >= a.M) continue;
     if (a.out != nullptr) {
       static_cast<T*>(a.out)[static_cast<size_t>(row) * a.N + col] = from_f32<T>(v);
@@ -802,6 +815,7 @@ hipError_t launch_decode_front(const DecodeParams& p, hipStream_t stream) {
   ga.G = p.G;
   ga.D = p.D;
   ga.Lc = p.Lc;
+  ga.rope = p.rope;
   if (ga.N % 32 != 0 || ga.K % 16 != 0) return hipErrorInvalidValue;
   FrontArgs f = {};
   f.x = p.x;

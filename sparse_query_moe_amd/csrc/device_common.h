@@ -158,6 +158,30 @@ template <int ROWB> struct LdsFrag<float, ROWB> {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Rotary position embedding (RoFormer, Su et al. 2021, interleaved pairs):
+// dims (2j, 2j+1) of a query or key head at position t turn by t * theta_j,
+// theta_j = base^(-2j/d_h) (float64, from the host; on == 0: no rotation).
+// The angle is formed and reduced modulo 2 pi in float64 (positions reach
+// 2^20), then its cosine and sine are taken in float32.
+struct RopeTable {
+  double theta[64];
+  int on;
+};
+__device__ __forceinline__ void rope_cs(int t, double theta, float& c, float& s) {
+  const double a = static_cast<double>(t) * theta;
+  const double k = rint(a * 0.15915494309189533577);              // a / (2 pi)
+  double r = fma(-k, 6.28318530717958623200, a);                   // 2 pi, high part
+  r = fma(-k, 2.44929359829470635445e-16, r);                      // 2 pi, low part
+  sincosf(static_cast<float>(r), &s, &c);
+}
+// v (dim d of a head) turned together with its pair partner p (dim d ^ 1);
+// inverse turns back (the transpose of the rotation)
+__device__ __forceinline__ float rope_apply(float v, float p, int d, float c, float s,
+                                            bool inverse = false) {
+  const float sn = inverse ? -s : s;
+  return (d & 1) ? fmaf(p, sn, v * c) : fmaf(-p, sn, v * c);
+}
+
 // an LDS address as the direct-load builtins want it
 #define GQE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 

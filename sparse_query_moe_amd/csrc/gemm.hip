@@ -42,6 +42,13 @@ template <class P, class = void> struct HasStoreAcc : std::false_type {};
 template <class P>
 struct HasStoreAcc<P, std::void_t<decltype(std::declval<const P&>().store_acc(0, 0, 0.f))>>
     : std::true_type {};
+// A problem that defines rotating() and rotate(row, col, v, partner) turns its
+// float32 results by position before they are stored (the rotary embedding:
+// the partner of column c is column c ^ 1, held by lane l ^ 1).
+template <class P, class = void> struct HasRotate : std::false_type {};
+template <class P>
+struct HasRotate<P, std::void_t<decltype(std::declval<const P&>().rotate(0, 0, 0.f, 0.f))>>
+    : std::true_type {};
 
 template <typename T, int BM_, int BN_, int WGM_, int WGN_, int NST_ = 2>
 struct GemmShape {
@@ -149,6 +156,21 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
         for (int b = 0; b < S::TN; ++b) mma32(acc[a][b], af[a], bf[b]);
     }
   }
+  if constexpr (HasRotate<P>::value) {
+    if (prob.rotating()) {
+#pragma unroll
+      for (int a = 0; a < S::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < S::TN; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float v = acc[a][b][i];
+            const float partner = __shfl_xor(v, 1, 64);
+            acc[a][b][i] = prob.rotate(wm * S::WM + 32 * a + acc_row(i, lane),
+                                       wn * S::WN + 32 * b + (lane & 31), v, partner);
+          }
+    }
+  }
   if constexpr (HasStoreAcc<P>::value) {
 #pragma unroll
     for (int a = 0; a < S::TM; ++a)
@@ -194,6 +216,7 @@ struct DenseArgs {
   int64_t vt_tiles;
   int nseg;
   ProjSeg seg[3];
+  RopeTable rope;
 };
 
 template <typename T, class S>
@@ -214,7 +237,21 @@ struct DenseProb {
     r.heads = s2 ? a.seg[2].heads : s1 ? a.seg[1].heads : a.seg[0].heads;
     r.head_base = s2 ? a.seg[2].head_base : s1 ? a.seg[1].head_base : a.seg[0].head_base;
     r.transposed = s2 ? a.seg[2].transposed : s1 ? a.seg[1].transposed : a.seg[0].transposed;
+    r.rope = s2 ? a.seg[2].rope : s1 ? a.seg[1].rope : a.seg[0].rope;
     return r;
+  }
+  // rows are tokens (position m % L); the rotated segments' columns are
+  // head-split, dim (col - n_begin) % D
+  __device__ __forceinline__ bool rotating() const { return a.rope.on != 0; }
+  __device__ __forceinline__ float rotate(int r, int c, float v, float partner) const {
+    const int m = m0 + r, col = n0 + c;
+    if (m >= a.M || col >= a.N) return v;
+    const ProjSeg sg = seg_of(col);
+    if (!sg.rope) return v;
+    const int dd = (col - sg.n_begin) % a.D;
+    float cs, sn;
+    rope_cs(m % a.L, a.rope.theta[dd >> 1], cs, sn);
+    return rope_apply(v, partner, dd, cs, sn);
   }
   __device__ __forceinline__ const T* a_any() const { return static_cast<const T*>(a.x); }
   __device__ __forceinline__ const T* b_any() const { return static_cast<const T*>(a.seg[0].w); }
@@ -326,6 +363,7 @@ struct GatherArgs {
   const int32_t* tile_off;
   int n_lists, L, d, G, E, D, H;
   int koff[kMaxGroups + 1];  // group g's slot-heads start at koff[g]
+  RopeTable rope;
 };
 
 template <typename T, class S>
@@ -353,6 +391,14 @@ struct GatherProb {
     if (n >= a.D) return nullptr;
     return static_cast<const T*>(a.wq) +
            (static_cast<size_t>(g * a.E + e) * a.D + n) * static_cast<size_t>(a.d);
+  }
+  // a routed row is turned by its position pos; its columns are the head's dims
+  __device__ __forceinline__ bool rotating() const { return a.rope.on != 0; }
+  __device__ __forceinline__ float rotate(int r, int c, float v, float partner) const {
+    if (m0 + r >= cnt || c >= a.D) return v;
+    float cs, sn;
+    rope_cs(a.pos[base + m0 + r], a.rope.theta[c >> 1], cs, sn);
+    return rope_apply(v, partner, c, cs, sn);
   }
   // each routed row lands at (slot-head koff[g] + slot, position pos): 8 dims per chunk
   __device__ __forceinline__ void write_tile(const T* ct) const {
@@ -615,8 +661,10 @@ inline dim3 tile_grid(Tiles t, int M, int N) {
 
 template <typename T>
 hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
-                             const ProjSeg* segs, int nseg, hipStream_t stream) {
+                             const ProjSeg* segs, int nseg, const RopeTable& rope,
+                             hipStream_t stream) {
   DenseArgs a;
+  a.rope = rope;
   a.x = x;
   a.M = M;
   a.K = K;
@@ -680,8 +728,10 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
                           const ProjSeg* segs, int nseg, const T* wq, T* q,
                           const int32_t* counts, const int32_t* offsets, const int32_t* pos,
                           const int32_t* slot, const int32_t* tile_off, int B, int G, int E,
-                          const GroupK& gk, int tiles_per_bg, hipStream_t stream) {
+                          const GroupK& gk, int tiles_per_bg, const RopeTable& rope,
+                          hipStream_t stream) {
   DenseArgs d;
+  d.rope = rope;
   d.x = x;
   d.M = M;
   d.K = K;
@@ -696,6 +746,7 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
   }
   d.N = N;
   GatherArgs g;
+  g.rope = rope;
   g.x = x;
   g.wq = wq;
   g.q = q;
@@ -798,11 +849,11 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
 
 #define GQE_INST(T)                                                                              \
   template hipError_t launch_dense_proj<T>(const T*, int, int, int, int, int64_t, const ProjSeg*, \
-                                           int, hipStream_t);                                    \
+                                           int, const RopeTable&, hipStream_t);                  \
   template hipError_t launch_project<T>(const T*, int, int, int, int, int64_t, const ProjSeg*,   \
                                         int, const T*, T*, const int32_t*, const int32_t*,       \
                                         const int32_t*, const int32_t*, const int32_t*, int, int, \
-                                        int, const GroupK&, int, hipStream_t);                   \
+                                        int, const GroupK&, int, const RopeTable&, hipStream_t); \
   template hipError_t launch_out_proj<T>(const T*, const T*, T*, int, int, int, hipStream_t);    \
   template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, hipStream_t);      \
   template hipError_t launch_nt_gemm<T>(const NtArgs&, hipStream_t);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
+
 namespace gqe {
 
 typedef uint16_t bf16_t;
@@ -55,10 +57,13 @@ struct ProjSeg {
   int heads;
   int head_base;
   int transposed;
+  int rope;        // rotate by position (rope.on): queries and keys
 };
+// rope: the rotary embedding of the rotated segments (rope.on == 0: none)
 template <typename T>
 hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
-                             const ProjSeg* segs, int nseg, hipStream_t stream);
+                             const ProjSeg* segs, int nseg, const RopeTable& rope,
+                             hipStream_t stream);
 
 // The dense projection (segments as for launch_dense_proj) and the gathered
 // routed-query projection in one launch: for every dispatch list (b, g, e),
@@ -70,7 +75,8 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
                           const ProjSeg* segs, int nseg, const T* wq, T* q,
                           const int32_t* counts, const int32_t* offsets, const int32_t* pos,
                           const int32_t* slot, const int32_t* tile_off, int B, int G, int E,
-                          const GroupK& gk, int tiles_per_bg, hipStream_t stream);
+                          const GroupK& gk, int tiles_per_bg, const RopeTable& rope,
+                          hipStream_t stream);
 
 // ---- K4 attention ------------------------------------------------------------
 struct AttnParams {
@@ -186,6 +192,7 @@ struct BwdParams {
   int dq_split;             // dQ key-walk splits (dq_splits), 1: none
   float* dq_part;           // [dq_split, B, H, L, D] float partials when split
   float scale, aux_weight;
+  RopeTable rope;           // rotary embedding of the forward (on == 0: none)
 };
 // dK/dV query-walk splits for a bf16 backward of B x L tokens, G groups, d_h D
 int dkdv_splits(int B, int G, int L, int D);
@@ -231,6 +238,7 @@ struct DecodeParams {
   float scale;            // softmax scale
   int ld_s, K_out;
   int weighted_slot;      // 1: build the weighted slot after the heads
+  RopeTable rope;         // rotary embedding of the new queries and keys (on == 0: none)
 };
 // keys per decode attention block for B sequences of G groups in a cache of Lc
 int decode_chunk(int B, int G, int Lc);

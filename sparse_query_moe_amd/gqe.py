@@ -42,7 +42,7 @@ class GqeConfig(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("shared_kv_group", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("router_bias", ctypes.c_void_p), ("output_mode", ctypes.c_int32),
-        ("group_top_k", ctypes.c_void_p),
+        ("group_top_k", ctypes.c_void_p), ("rope_base", ctypes.c_float),
     ]
 
     @property
@@ -113,11 +113,12 @@ OUTPUT_MODES = {"full": 0, "hard": 1, "weighted_concat": 2}  # gqe_output_mode
 
 def make_config(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim, dtype="bf16",
                 shared_kv_group=0, softmax_scale=0.0, router_bias=None,
-                output_mode="full", group_top_k=None) -> GqeConfig:
+                output_mode="full", group_top_k=None, rope_base=0.0) -> GqeConfig:
     """Fill a gqe_config.  `router_bias` is a float32 device tensor [G*E] or None;
     the caller keeps it alive while the config is in use.  `output_mode` is
     "full", "hard" or "weighted_concat" (see gqe_output_mode).  `group_top_k`
-    is a list of G per-group expert counts or None (top_k in every group)."""
+    is a list of G per-group expert counts or None (top_k in every group).
+    `rope_base` > 0 turns queries and keys by position (see gqe_config)."""
     dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}.get(dtype, dtype)
     gk = None
     if group_top_k is not None:
@@ -126,7 +127,7 @@ def make_config(batch, seq_len, d_model, n_groups, n_experts, top_k, head_dim, d
                     shared_kv_group, dt, float(softmax_scale),
                     None if router_bias is None else router_bias.data_ptr(),
                     OUTPUT_MODES.get(output_mode, output_mode),
-                    None if gk is None else ctypes.cast(gk, ctypes.c_void_p))
+                    None if gk is None else ctypes.cast(gk, ctypes.c_void_p), float(rope_base))
     cfg._group_top_k = gk  # kept alive with the config
     return cfg
 
