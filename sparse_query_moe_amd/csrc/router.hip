@@ -307,22 +307,86 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   }
   __syncthreads();
 
-  // selection per (token, group); a pair whose deciding gap is within twice
-  // the error bound of its logits is flagged for the exact recomputation
+  // selection, with every (token, group) whose deciding gap is within twice
+  // the error bound of its logits flagged for the exact recomputation.
+  // Short launches take one lane per (token, expert): the expert's rank in
+  // its group (larger logit first, ties to the lower index), its
+  // exp(r - max), and whether the gap from it to the best expert ranked after
+  // it decides the selection or its order and is too small.
   constexpr float kErr = 32.f * 0x1p-23f;  // per unit of ||x|| ||w||, with margin
   const int tasks = TB * G;
-  for (int task = tid; task < tasks; task += 256) {
-    const int tt = task / G, g = task % G;
-    const int gt = blk0 + tt;
-    float wmax = 0.f;
-    for (int e = 0; e < E; ++e) wmax = fmaxf(wmax, wnorm[g * E + e]);
-    const double tol = 2.0 * static_cast<double>(kErr) * xnorm[tt] * wmax;
-    const bool valid = gt < n_tokens;
-    const size_t o = static_cast<size_t>(valid ? gt : 0) * gk.K + gk.koff[g];
-    const double gap = select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, false);
-    const bool fix = valid && !(gap > tol);
-    redo[task] = fix ? 1 : 0;
-    if (valid && !fix) select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, true);
+  if constexpr (KS > 1) {
+    constexpr int PER = TB * 64 / 256;        // lane-tasks per thread, at most
+    __shared__ unsigned char rkb[TB * 64];    // rank | 0x80 when a deciding gap is too small
+    double ex[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + 256 * j;
+      ex[j] = 0.0;
+      if (i >= TB * GE) continue;
+      const int tt = i / GE, ge = i % GE, g = ge / E, e = ge % E;
+      const double* r = &logit[tt][g * E];
+      const double re = r[e];
+      double rmax = r[0], nxt = -INFINITY;
+      int rank = 0;
+      for (int f = 0; f < E; ++f) {
+        const double rf = r[f];
+        rmax = fmax(rmax, rf);
+        rank += (rf > re) || (rf == re && f < e);
+        if (rf < re || (rf == re && f > e)) nxt = fmax(nxt, rf);
+      }
+      const int k = gk.kg[g], kk = k < E - 1 ? k : E - 1;
+      float wmax = 0.f;
+      for (int f = 0; f < E; ++f) wmax = fmaxf(wmax, wnorm[g * E + f]);
+      const double tol = 2.0 * static_cast<double>(kErr) * xnorm[tt] * wmax;
+      const bool bad = rank < kk && !(re - nxt > tol);
+      rkb[i] = static_cast<unsigned char>(rank | (bad ? 0x80 : 0));
+      if (rank < k || !renorm) ex[j] = exp(re - rmax);
+    }
+    __syncthreads();
+    // every lane has read its group's logits: replace them by the terms of the
+    // normalizer (0 for experts outside it)
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + 256 * j;
+      if (i < TB * GE) logit[i / GE][i % GE] = ex[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + 256 * j;
+      if (i >= TB * GE) continue;
+      const int tt = i / GE, ge = i % GE, g = ge / E, e = ge % E;
+      const int rank = rkb[i] & 0x7f, k = gk.kg[g];
+      const int gt = blk0 + tt;
+      const bool valid = gt < n_tokens;
+      bool fix = false;
+      for (int f = 0; f < E; ++f) fix = fix || (rkb[tt * GE + g * E + f] & 0x80);
+      fix = fix && valid;
+      if (rank == 0) redo[tt * G + g] = fix ? 1 : 0;
+      if (!valid || fix || rank >= k) continue;
+      double z = 0.0;  // in expert order
+      for (int f = 0; f < E; ++f) z += logit[tt][g * E + f];
+      const size_t o = static_cast<size_t>(gt) * gk.K + gk.koff[g] + rank;
+      idx_out[o] = e;
+      w_out[o] = static_cast<float>(ex[j] / z);
+    }
+  } else {
+    // long launches: one thread per (token, group), which keeps the block's
+    // barriers few while other blocks stream their tokens
+    for (int task = tid; task < tasks; task += 256) {
+      const int tt = task / G, g = task % G;
+      const int gt = blk0 + tt;
+      float wmax = 0.f;
+      for (int e = 0; e < E; ++e) wmax = fmaxf(wmax, wnorm[g * E + e]);
+      const double tol = 2.0 * static_cast<double>(kErr) * xnorm[tt] * wmax;
+      const bool valid = gt < n_tokens;
+      const size_t o = static_cast<size_t>(valid ? gt : 0) * gk.K + gk.koff[g];
+      const double gap = select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, false);
+      const bool fix = valid && !(gap > tol);
+      redo[task] = fix ? 1 : 0;
+      if (valid && !fix) select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, true);
+    }
   }
   __syncthreads();
 
