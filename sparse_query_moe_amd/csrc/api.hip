@@ -185,11 +185,6 @@ bool empty(const gqe_config* c) { return static_cast<long long>(c->batch) * c->s
 
 // Upper bound of the gathered-projection tiles of one (b, g): its lists hold
 // L*k rows in E lists.
-int gather_tiles_per_bg(const gqe_config* c) {
-  const long long rows = static_cast<long long>(c->seq_len) * max_k(c);
-  return static_cast<int>((rows + kGatherRows - 1) / kGatherRows) + c->n_experts;
-}
-
 template <typename T>
 int project_impl(const gqe_config* c, const void* x, const void* wq, const void* wk,
                  const void* wv, void* ws, bool dense, hipStream_t stream) {
@@ -233,8 +228,7 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
       static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_tiles, shared ? seg : seg + 1,
       shared ? 3 : 2, static_cast<const T*>(wq), at<T>(ws, l.pub.q), at<int32_t>(ws, l.pub.counts),
       at<int32_t>(ws, l.pub.offsets), at<int32_t>(ws, l.pub.pos), at<int32_t>(ws, l.pub.slot),
-      at<int32_t>(ws, l.tile_off), B, G, E, make_group_k(c), gather_tiles_per_bg(c),
-      make_rope(c), stream));
+      at<int32_t>(ws, l.tile_off), B, G, E, make_group_k(c), make_rope(c), stream));
 }
 
 template <typename T>

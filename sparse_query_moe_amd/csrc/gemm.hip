@@ -419,11 +419,22 @@ struct GatherProb {
 // V^T) first, then the gathered routed-query tiles.  Neither depends on the
 // other, so one grid covers both and the gathered tiles fill the compute
 // units the dense ones leave idle.
+//
+// Gathered tiles come in one of two orders.  Launches of more blocks than
+// the chip holds at once order them tile index first, then list: block i of
+// every (b, g, e) list runs at about the same time, and with loads near k/E
+// of the tokens the i-th tiles of all lists cover about the same token
+// window, so each token's x row, which k*G lists read, is fetched from HBM
+// once and found in L2 by the other lists.  Every list then gets
+// `per` = ceil(L / rows) slots (a list holds at most L entries); slots past
+// its length exit at once.  Smaller launches, where all blocks run at once
+// anyway, pack the tiles of each (b, g) one list after another in `per`
+// slots (an upper bound of the (b, g)'s total), which needs fewer blocks.
 // ---------------------------------------------------------------------------
 template <typename T, class SD, class SG>
 __global__ __launch_bounds__(256) void project_kernel(DenseArgs dargs, GatherArgs gargs,
-                                                      int dense_nx, int dense_blocks,
-                                                      int tiles_per_bg) {
+                                                      int dense_nx, int dense_blocks, int per,
+                                                      int by_tile) {
   extern __shared__ __align__(16) char smem[];
   const int bid = blockIdx.x;
   if (bid < dense_blocks) {
@@ -432,12 +443,24 @@ __global__ __launch_bounds__(256) void project_kernel(DenseArgs dargs, GatherArg
     return;
   }
   const int gb = bid - dense_blocks;
-  const int tile = gb % tiles_per_bg, bg = gb / tiles_per_bg;
-  const int* toff = gargs.tile_off + bg * (gargs.E + 1);  // tile map of this (b, g)
-  if (tile >= toff[gargs.E]) return;                      // whole block leaves together
-  int e = 0;                                              // last e with toff[e] <= tile
-  while (e + 1 < gargs.E && toff[e + 1] <= tile) ++e;
-  GatherProb<T, SG> prob(gargs, tile - toff[e], bg * gargs.E + e);
+  int tile, bg, e;
+  if (by_tile) {
+    tile = gb / gargs.n_lists;
+    const int li = gb % gargs.n_lists;
+    bg = li / gargs.E;
+    e = li % gargs.E;
+    const int* toff = gargs.tile_off + bg * (gargs.E + 1);  // tile map of this (b, g)
+    if (tile >= toff[e + 1] - toff[e]) return;              // whole block leaves together
+  } else {
+    const int slot = gb % per;
+    bg = gb / per;
+    const int* toff = gargs.tile_off + bg * (gargs.E + 1);
+    if (slot >= toff[gargs.E]) return;
+    e = 0;  // last e with toff[e] <= slot
+    while (e + 1 < gargs.E && toff[e + 1] <= slot) ++e;
+    tile = slot - toff[e];
+  }
+  GatherProb<T, SG> prob(gargs, tile, bg * gargs.E + e);
   gemm_block<T, SG>(prob, smem);
 }
 
@@ -683,11 +706,12 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_
 }
 
 template <typename T, class SD, class SG>
-static hipError_t launch_project_s(const DenseArgs& d, const GatherArgs& g, int tiles_per_bg,
-                                   int n_bg, hipStream_t stream) {
+static hipError_t launch_project_s(const DenseArgs& d, const GatherArgs& g, int per,
+                                   bool by_tile, hipStream_t stream) {
   const int nx = (d.N + SD::BN - 1) / SD::BN;
   const int dense_blocks = d.N == 0 || d.M == 0 ? 0 : nx * ((d.M + SD::BM - 1) / SD::BM);
-  const long long blocks = dense_blocks + static_cast<long long>(tiles_per_bg) * n_bg;
+  const long long blocks =
+      dense_blocks + static_cast<long long>(per) * (by_tile ? g.n_lists : g.n_lists / g.E);
   if (blocks == 0) return hipSuccess;
   constexpr int lds = SD::LDS > SG::LDS ? SD::LDS : SG::LDS;
   auto kern = project_kernel<T, SD, SG>;
@@ -697,7 +721,7 @@ static hipError_t launch_project_s(const DenseArgs& d, const GatherArgs& g, int 
     if (attr != hipSuccess) return attr;
   }
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream, d, g,
-                     nx > 0 ? nx : 1, dense_blocks, tiles_per_bg);
+                     nx > 0 ? nx : 1, dense_blocks, per, by_tile ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -705,22 +729,32 @@ static hipError_t launch_project_s(const DenseArgs& d, const GatherArgs& g, int 
 // tiles (the same K steps in the same order per output element); the
 // four-stage ring when every block of the launch is resident at once.
 template <typename T, int D>
-static hipError_t launch_project_d(const DenseArgs& d, const GatherArgs& g, int tiles_per_bg,
-                                   int n_bg, hipStream_t stream) {
+static hipError_t launch_project_d(const DenseArgs& d, const GatherArgs& g, int kmax,
+                                   hipStream_t stream) {
   constexpr int WGM = D >= 128 ? 2 : 4, WGN = D >= 128 ? 2 : 1;
-  const long long gblocks = static_cast<long long>(tiles_per_bg) * n_bg;
+  const int n_bg = g.E == 0 ? 0 : g.n_lists / g.E;
+  // packed: a (b, g) has at most L*kmax routed rows, in at most E partial tiles
+  const int packed = static_cast<int>((static_cast<long long>(g.L) * kmax + kGatherRows - 1) / kGatherRows) + g.E;
+  const int per_list = (g.L + kGatherRows - 1) / kGatherRows;
   const long long nx = (d.N + 127) / 128;
+  long long gblocks = static_cast<long long>(packed) * n_bg;
+  const bool by_tile = nx * ((d.M + 127) / 128) + gblocks > 2LL * cu_count();
+  int per = packed;
+  if (by_tile) {
+    per = per_list;
+    gblocks = static_cast<long long>(per_list) * g.n_lists;
+  }
   const long long b128 = nx * ((d.M + 127) / 128) + gblocks;
   const bool small = b128 < cu_count();
   const long long total = small ? nx * ((d.M + 63) / 64) + gblocks : b128;
   if (deep_ring(total)) {
     typedef GemmShape<T, kGatherRows, D, WGM, WGN, 4> SG;
-    return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2, 4>, SG>(d, g, tiles_per_bg, n_bg, stream)
-                 : launch_project_s<T, GemmShape<T, 128, 128, 2, 2, 4>, SG>(d, g, tiles_per_bg, n_bg, stream);
+    return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2, 4>, SG>(d, g, per, by_tile, stream)
+                 : launch_project_s<T, GemmShape<T, 128, 128, 2, 2, 4>, SG>(d, g, per, by_tile, stream);
   }
   typedef GemmShape<T, kGatherRows, D, WGM, WGN> SG;
-  return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2>, SG>(d, g, tiles_per_bg, n_bg, stream)
-               : launch_project_s<T, GemmShape<T, 128, 128, 2, 2>, SG>(d, g, tiles_per_bg, n_bg, stream);
+  return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2>, SG>(d, g, per, by_tile, stream)
+               : launch_project_s<T, GemmShape<T, 128, 128, 2, 2>, SG>(d, g, per, by_tile, stream);
 }
 
 template <typename T>
@@ -728,8 +762,7 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
                           const ProjSeg* segs, int nseg, const T* wq, T* q,
                           const int32_t* counts, const int32_t* offsets, const int32_t* pos,
                           const int32_t* slot, const int32_t* tile_off, int B, int G, int E,
-                          const GroupK& gk, int tiles_per_bg, const RopeTable& rope,
-                          hipStream_t stream) {
+                          const GroupK& gk, const RopeTable& rope, hipStream_t stream) {
   DenseArgs d;
   d.rope = rope;
   d.x = x;
@@ -763,11 +796,11 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
   for (int i = 0; i <= G; ++i) g.koff[i] = gk.koff[i];
   g.D = D;
   g.H = gk.K + 1;
-  if (B * G == 0) tiles_per_bg = 0;
+  if (B * G == 0) g.n_lists = 0;
   switch (D) {
-    case 32: return launch_project_d<T, 32>(d, g, tiles_per_bg, B * G, stream);
-    case 64: return launch_project_d<T, 64>(d, g, tiles_per_bg, B * G, stream);
-    case 128: return launch_project_d<T, 128>(d, g, tiles_per_bg, B * G, stream);
+    case 32: return launch_project_d<T, 32>(d, g, gk.kmax, stream);
+    case 64: return launch_project_d<T, 64>(d, g, gk.kmax, stream);
+    case 128: return launch_project_d<T, 128>(d, g, gk.kmax, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -853,7 +886,7 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
   template hipError_t launch_project<T>(const T*, int, int, int, int, int64_t, const ProjSeg*,   \
                                         int, const T*, T*, const int32_t*, const int32_t*,       \
                                         const int32_t*, const int32_t*, const int32_t*, int, int, \
-                                        int, const GroupK&, int, const RopeTable&, hipStream_t); \
+                                        int, const GroupK&, const RopeTable&, hipStream_t);      \
   template hipError_t launch_out_proj<T>(const T*, const T*, T*, int, int, int, hipStream_t);    \
   template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, hipStream_t);      \
   template hipError_t launch_nt_gemm<T>(const NtArgs&, hipStream_t);

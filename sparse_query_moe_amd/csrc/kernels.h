@@ -69,14 +69,13 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_
 // routed-query projection in one launch: for every dispatch list (b, g, e),
 // the rows x[b, pos] . Wq[head g*E+e]^T land in slot-head koff[g] + slot at
 // their positions.  tile_off is the per-(b, g) tile map written by the
-// dispatch, tiles_per_bg an upper bound of its totals.
+// dispatch.
 template <typename T>
 hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
                           const ProjSeg* segs, int nseg, const T* wq, T* q,
                           const int32_t* counts, const int32_t* offsets, const int32_t* pos,
                           const int32_t* slot, const int32_t* tile_off, int B, int G, int E,
-                          const GroupK& gk, int tiles_per_bg, const RopeTable& rope,
-                          hipStream_t stream);
+                          const GroupK& gk, const RopeTable& rope, hipStream_t stream);
 
 // ---- K4 attention ------------------------------------------------------------
 struct AttnParams {
