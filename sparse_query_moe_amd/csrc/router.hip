@@ -185,21 +185,25 @@ __device__ __forceinline__ double select_group(const double* r, int E, int k, in
   return mingap;
 }
 
-// KS: waves that split the model dimension of one 16-token tile (4 for short
-// launches, so that enough blocks exist; 1 for long ones, where every wave
-// takes its own tile and W_r is read once per 64 tokens).  Their float64
-// partial sums are added in LDS in a fixed order.
+// KS: waves that split the model dimension of one 16-token tile (4 up to
+// 2^19 tokens, so that many blocks exist and their phases overlap; 1 for the
+// longest launches, where every wave takes its own tile, W_r is read once
+// per 64 tokens and 8 waves share each SIMD).  Their float64 partial sums are
+// added in LDS in a fixed order.
 template <int NE, int KS>
-__global__ __launch_bounds__(256) void router_bf16_kernel(
+__global__ __launch_bounds__(256, KS == 1 ? 6 : 2) void router_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int n_tokens, int d, int G, int E,
     GroupK gk, int renorm) {
   constexpr int TB = 16 * (4 / KS);  // tokens per block
-  __shared__ double logit[TB][65];
-  __shared__ double part[KS > 1 ? KS : 1][TB][KS > 1 ? 64 : 1];
-  __shared__ float xpart[KS][TB], wpart[KS][64];
-  __shared__ float xnorm[TB], wnorm[64];
-  __shared__ unsigned char redo[TB * 64];  // (token, group) pairs recomputed exactly
+  constexpr int GEP = 16 * NE;        // experts of all groups, at most
+  // LDS sized by the expert count, so that long launches keep several blocks
+  // per compute unit and enough of x in flight
+  __shared__ double logit[TB][GEP + 1];
+  __shared__ double part[KS > 1 ? KS : 1][TB][KS > 1 ? GEP : 1];
+  __shared__ float xpart[KS][TB], wpart[KS][GEP];
+  __shared__ float xnorm[TB], wnorm[GEP];
+  __shared__ unsigned char redo[TB * GEP];  // (token, group) pairs recomputed exactly
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, kq = lane >> 4;
   const int tile = wave / KS, ksp = wave % KS;
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     float v = wsq[n];
     v += __shfl_xor(v, 16, 64);
     v += __shfl_xor(v, 32, 64);
-    if (tile == 0 && kq == 0 && 16 * n + row < 64) wpart[ksp][16 * n + row] = v;
+    if (tile == 0 && kq == 0) wpart[ksp][16 * n + row] = v;
   }
   // accumulator of the 16x16 MFMA: value i of lane l is D[4*(l/16) + i][l % 16],
   // i.e. token 4*kq + i of the wave's tile, expert 16*n + row
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
       logit[tt][e] = v + (bias ? static_cast<double>(bias[e]) : 0.0);
     }
   }
-  for (int i = tid; i < TB + 64; i += 256) {
+  for (int i = tid; i < TB + GEP; i += 256) {
     float v = 0.f;
     if (i < TB) {
 #pragma unroll
@@ -316,8 +320,8 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   constexpr float kErr = 32.f * 0x1p-23f;  // per unit of ||x|| ||w||, with margin
   const int tasks = TB * G;
   if constexpr (KS > 1) {
-    constexpr int PER = TB * 64 / 256;        // lane-tasks per thread, at most
-    __shared__ unsigned char rkb[TB * 64];    // rank | 0x80 when a deciding gap is too small
+    constexpr int PER = (TB * GEP + 255) / 256;  // lane-tasks per thread, at most
+    __shared__ unsigned char rkb[TB * GEP];      // rank | 0x80 when a deciding gap is too small
     double ex[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -452,8 +456,10 @@ hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* id
   if constexpr (sizeof(T) == 2) {
     const int GE = G * E;
     if (d % 32 == 0 && GE <= 64) {
-      // short launches split every 16-token tile's model dims over 4 waves
-      const bool split = n_tokens <= 32768 && d % 128 == 0;
+      // up to 2^19 tokens, 4 waves split the model dims of every 16-token
+      // tile (more blocks, whose load and selection phases then overlap);
+      // beyond that, a wave owns 16 tokens and 8 waves share each SIMD
+      const bool split = n_tokens <= (1 << 19) && d % 128 == 0;
       const int tb = split ? 16 : 64;
       const dim3 grid((n_tokens + tb - 1) / tb);
       const int r = renorm ? 1 : 0;
