@@ -88,3 +88,31 @@ def f64_inputs(wl, I):
     x = W.bf16_bits_to_f32(I["x"]) if wl.dtype == W.BF16 else I["x"]   # exact, float32 storage
     return dict(x=x, wq=f(I["wq"]), wk=f(I["wk"]), wv=f(I["wv"]), wr=f(I["wr"]), wo=f(I["wo"]),
                 br=I["br"].astype(np.float64), wq_dense=f(I["wq_dense"]), wo_dense=f(I["wo_dense"]))
+
+
+# Gates of the bf16 gradients, per tensor: (relative L2, max-abs over the
+# tensor's largest magnitude).  Every product takes bf16 operands (dO, P, dS
+# and the stacked gradient matrix) with float32 accumulation; the gates sit
+# at about twice the largest error measured over the backward tests.  The
+# router's gradients sum the logit gradients of every token, with
+# cancellation, and carry the largest errors.
+BF16_GRAD_GATE = {"dx": (1e-2, 1.5e-2), "dwq": (1e-2, 1.5e-2), "dwk": (1e-2, 1.5e-2),
+                  "dwv": (1e-2, 1.5e-2), "dwo": (1e-2, 1.5e-2), "dwr": (2e-2, 3e-2),
+                  "dbr": (2e-2, 3e-2)}
+
+
+def grad_gate(gpu, ref, dtype, what, key):
+    """Relative L2 and max-abs (over the largest magnitude) error of one
+    gradient tensor against the oracle's, asserted against its gate: the
+    bf16 table above, or relative L2 1e-5 for float32 layers."""
+    gpu = np.asarray(gpu, dtype=np.float64).reshape(ref.shape)
+    scale = max(np.abs(ref).max(), 1e-30)
+    rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
+    mx = float(np.abs(gpu - ref).max() / scale)
+    log(f"  {what}: rel-L2 {rel:.2e} max/max {mx:.2e}")
+    if dtype == W.BF16:
+        g_rel, g_max = BF16_GRAD_GATE[key]
+        assert rel <= g_rel and mx <= g_max, f"{what}: rel-L2 {rel:.3e}, max-abs/max {mx:.3e}"
+    else:
+        assert rel <= 1e-5, f"{what}: rel-L2 {rel:.3e}, max-abs/max {mx:.3e}"
+    return rel, mx

@@ -3,10 +3,12 @@
 
 gqe_forward runs first; gqe_backward then reads its workspace.  Every
 gradient (dx, dW_q, dW_k, dW_v, dW_r, db_r, dW_O) and the auxiliary loss are
-compared with the float64 oracle.  Gate, per gradient tensor: relative L2
-error <= 2e-2 and max-abs error <= 5e-2 of the tensor's largest magnitude for
-bf16 layers (bf16 operands of every product, float32 accumulation), and
-relative L2 <= 1e-5 for float32 layers.
+compared with the float64 oracle.  Gate, per gradient tensor (gpu_util's
+BF16_GRAD_GATE): for bf16 layers (bf16 operands of every product, float32
+accumulation) relative L2 <= 1e-2 and max-abs <= 1.5e-2 of the tensor's
+largest magnitude for dx and the projection weights, 2e-2 and 3e-2 for the
+router's weight and bias (sums over every token's logit gradient); relative
+L2 <= 1e-5 for float32 layers.
 """
 import math
 
@@ -17,7 +19,7 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 import workloads as W  # noqa: E402
-from gpu_util import f64_inputs, inputs, log, to_dev, to_f64  # noqa: E402
+from gpu_util import f64_inputs, grad_gate, inputs, log, to_dev, to_f64  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -28,18 +30,6 @@ def gqe():
         pytest.skip("no GPU")
     from sparse_query_moe_amd import gqe as mod
     return mod
-
-
-def grad_gate(gpu, ref, dtype, what):
-    gpu = np.asarray(gpu, dtype=np.float64).reshape(ref.shape)
-    scale = max(np.abs(ref).max(), 1e-30)
-    rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
-    mx = float(np.abs(gpu - ref).max() / scale)
-    if dtype == W.BF16:
-        assert rel <= 2e-2 and mx <= 5e-2, f"{what}: rel-L2 {rel:.3e}, max-abs/max {mx:.3e}"
-    else:
-        assert rel <= 1e-5, f"{what}: rel-L2 {rel:.3e}, max-abs/max {mx:.3e}"
-    return rel, mx
 
 
 def _cfg(gqe, wl, dev, **kw):
@@ -134,7 +124,7 @@ def test_gqe_backward(gqe, name, mode, aux, kw):
         if mode == "hard" and aux == 0.0 and rk in ("dwr", "dbr"):
             assert np.abs(g[key]).max() == 0.0
             continue
-        rel, mx = grad_gate(g[key], ref[rk], wl.dtype, f"{name} {mode} {key}")
+        rel, mx = grad_gate(g[key], ref[rk], wl.dtype, f"{name} {mode} {key}", key)
         log(f"  {key}: rel-L2 {rel:.2e} max/max {mx:.2e}")
     assert abs(float(g["aux"][0]) - ref["aux_loss"]) <= 1e-5 * max(1.0, abs(ref["aux_loss"]))
 
@@ -159,7 +149,7 @@ def test_gqa_backward(gqe, name):
     ref = oracle.gqa_backward(F["x"], F["wq_dense"], F["wk"], F["wv"], F["wo_dense"],
                               W.to_f64(dy, wl.dtype), wl.n_groups, wl.n_experts, wl.head_dim)
     for key in ("dwo", "dx", "dwq", "dwk", "dwv"):
-        grad_gate(g[key].cpu().numpy(), ref[key], wl.dtype, f"gqa {name} {key}")
+        grad_gate(g[key].cpu().numpy(), ref[key], wl.dtype, f"gqa {name} {key}", key)
 
 
 @pytest.mark.parametrize("L,B,G,E,k,D,dtype", [
@@ -187,7 +177,7 @@ def test_backward_edge_shapes(gqe, L, B, G, E, k, D, dtype):
     ref = oracle.gqe_backward(F["x"], F["wq"], F["wk"], F["wv"], F["wr"], F["wo"], F["br"],
                               W.to_f64(dy, wl.dtype), G, E, k, D, aux_weight=0.2)
     for key in ("dwo", "dx", "dwq", "dwk", "dwv", "dwr", "dbr"):
-        grad_gate(g[key], ref[key], wl.dtype, f"edge {key}")
+        grad_gate(g[key], ref[key], wl.dtype, f"edge {key}", key)
 
 
 GROUP_K_BWD_CASES = [
@@ -220,7 +210,7 @@ def test_gqe_backward_group_k(gqe, L, B, G, E, ks, D, dtype, mode, aux, kw):
         if mode == "hard" and aux == 0.0 and key in ("dwr", "dbr"):
             assert np.abs(g[key]).max() == 0.0
             continue
-        rel, mx = grad_gate(g[key], ref[key], dtype, f"group k {ks} {mode} {key}")
+        rel, mx = grad_gate(g[key], ref[key], dtype, f"group k {ks} {mode} {key}", key)
         log(f"  {key}: rel-L2 {rel:.2e} max/max {mx:.2e}")
     assert abs(float(g["aux"][0]) - ref["aux_loss"]) <= 1e-5 * max(1.0, abs(ref["aux_loss"]))
 
