@@ -319,14 +319,14 @@ __global__ __launch_bounds__(256, KS == 1 ? 6 : 2) void router_bf16_kernel(
   // it decides the selection or its order and is too small.
   constexpr float kErr = 32.f * 0x1p-23f;  // per unit of ||x|| ||w||, with margin
   const int tasks = TB * G;
+  bool any_fix = false;  // this thread flagged a (token, group)
   if constexpr (KS > 1) {
     constexpr int PER = (TB * GEP + 255) / 256;  // lane-tasks per thread, at most
     __shared__ unsigned char rkb[TB * GEP];      // rank | 0x80 when a deciding gap is too small
-    double ex[PER];
+    __shared__ double exs[TB][GEP];              // terms of the normalizer (0 outside it)
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int i = tid + 256 * j;
-      ex[j] = 0.0;
       if (i >= TB * GE) continue;
       const int tt = i / GE, ge = i % GE, g = ge / E, e = ge % E;
       const double* r = &logit[tt][g * E];
@@ -345,15 +345,7 @@ __global__ __launch_bounds__(256, KS == 1 ? 6 : 2) void router_bf16_kernel(
       const double tol = 2.0 * static_cast<double>(kErr) * xnorm[tt] * wmax;
       const bool bad = rank < kk && !(re - nxt > tol);
       rkb[i] = static_cast<unsigned char>(rank | (bad ? 0x80 : 0));
-      if (rank < k || !renorm) ex[j] = exp(re - rmax);
-    }
-    __syncthreads();
-    // every lane has read its group's logits: replace them by the terms of the
-    // normalizer (0 for experts outside it)
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = tid + 256 * j;
-      if (i < TB * GE) logit[i / GE][i % GE] = ex[j];
+      exs[tt][ge] = (rank < k || !renorm) ? exp(re - rmax) : 0.0;
     }
     __syncthreads();
 #pragma unroll
@@ -368,12 +360,13 @@ __global__ __launch_bounds__(256, KS == 1 ? 6 : 2) void router_bf16_kernel(
       for (int f = 0; f < E; ++f) fix = fix || (rkb[tt * GE + g * E + f] & 0x80);
       fix = fix && valid;
       if (rank == 0) redo[tt * G + g] = fix ? 1 : 0;
+      any_fix = any_fix || fix;
       if (!valid || fix || rank >= k) continue;
       double z = 0.0;  // in expert order
-      for (int f = 0; f < E; ++f) z += logit[tt][g * E + f];
+      for (int f = 0; f < E; ++f) z += exs[tt][g * E + f];
       const size_t o = static_cast<size_t>(gt) * gk.K + gk.koff[g] + rank;
       idx_out[o] = e;
-      w_out[o] = static_cast<float>(ex[j] / z);
+      w_out[o] = static_cast<float>(exs[tt][ge] / z);
     }
   } else {
     // long launches: one thread per (token, group), which keeps the block's
@@ -389,10 +382,12 @@ __global__ __launch_bounds__(256, KS == 1 ? 6 : 2) void router_bf16_kernel(
       const double gap = select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, false);
       const bool fix = valid && !(gap > tol);
       redo[task] = fix ? 1 : 0;
+      any_fix = any_fix || fix;
       if (valid && !fix) select_group(&logit[tt][g * E], E, gk.kg[g], renorm, idx_out + o, w_out + o, true);
     }
   }
-  __syncthreads();
+  // most blocks have no flagged pair and end here
+  if (__syncthreads_or(any_fix ? 1 : 0) == 0) return;
 
   // exact recomputation of the flagged pairs: one wave per pair, 16 lanes per
   // expert (4 experts at a time), each lane 8 dims per 16-byte load at a
