@@ -421,15 +421,18 @@ struct GatherProb {
 // units the dense ones leave idle.
 //
 // Gathered tiles come in one of two orders.  Launches of more blocks than
-// the chip holds at once order them tile index first, then list: block i of
+// the chip holds at once, on sequences up to 2^18 tokens, order them tile
+// index first, then list: block i of
 // every (b, g, e) list runs at about the same time, and with loads near k/E
 // of the tokens the i-th tiles of all lists cover about the same token
 // window, so each token's x row, which k*G lists read, is fetched from HBM
 // once and found in L2 by the other lists.  Every list then gets
 // `per` = ceil(L / rows) slots (a list holds at most L entries); slots past
-// its length exit at once.  Smaller launches, where all blocks run at once
-// anyway, pack the tiles of each (b, g) one list after another in `per`
-// slots (an upper bound of the (b, g)'s total), which needs fewer blocks.
+// its length exit at once.  Other launches pack the tiles of each (b, g)
+// one list after another in `per` slots (an upper bound of the (b, g)'s
+// total): small ones run all blocks at once anyway, and on the longest
+// sequences a skewed expert load puts the lists' i-th tiles far apart, so a
+// list read in order is the more local walk over x.
 // ---------------------------------------------------------------------------
 template <typename T, class SD, class SG>
 __global__ __launch_bounds__(256) void project_kernel(DenseArgs dargs, GatherArgs gargs,
@@ -738,7 +741,10 @@ static hipError_t launch_project_d(const DenseArgs& d, const GatherArgs& g, int 
   const int per_list = (g.L + kGatherRows - 1) / kGatherRows;
   const long long nx = (d.N + 127) / 128;
   long long gblocks = static_cast<long long>(packed) * n_bg;
-  const bool by_tile = nx * ((d.M + 127) / 128) + gblocks > 2LL * cu_count();
+  // tile-index order where the launch exceeds what the chip holds, up to
+  // L = 2^18 (beyond that, under a skewed load the lists' i-th tiles lie far
+  // apart in the sequence and the packed order reads x more locally)
+  const bool by_tile = nx * ((d.M + 127) / 128) + gblocks > 2LL * cu_count() && g.L <= (1 << 18);
   int per = packed;
   if (by_tile) {
     per = per_list;
