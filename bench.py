@@ -416,7 +416,7 @@ def measure_sweep(gqe, torch, steps, warmup, batch=4, seq_len=8192):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.txt")
-KERNEL_SOURCES = ("attention.hip", "device_common.h", "kernels.h")
+KERNEL_SOURCES = ("attention.hip", "attention.h", "device_common.h")
 
 
 def kernel_source_hash():

@@ -40,8 +40,8 @@
 
 #include <type_traits>
 
+#include "attention.h"
 #include "device_common.h"
-#include "kernels.h"
 
 namespace gqe {
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attention.h"
 #include "device_common.h"
 
 namespace gqe {
@@ -18,8 +19,7 @@ constexpr int kGatherRows = 128;
 // kg[g] - 1 of every token, in rank order; K = koff[G] hard slots in all.  A
 // uniform top-k is kg[g] = k, koff[g] = g*k (the pages' layer); a per-group k
 // is the non-uniform variant the pages list as future work (pptc.cn,
-// section 6).
-constexpr int kMaxGroups = 64;
+// section 6).  kMaxGroups (attention.h) bounds G.
 // compute units of the device (read once)
 int cu_count();
 struct GroupK {
@@ -76,37 +76,6 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
                           const int32_t* counts, const int32_t* offsets, const int32_t* pos,
                           const int32_t* slot, const int32_t* tile_off, int B, int G, int E,
                           const GroupK& gk, const RopeTable& rope, hipStream_t stream);
-
-// ---- K4 attention ------------------------------------------------------------
-struct AttnParams {
-  const void* q;       // [B, q_heads, L, D]: heads 0 .. H-1 attend
-  const void* k;       // [B, G, L, D]
-  const void* vt;      // [B, G, vt_tiles, D, 64], keys permuted in 16-key groups
-  void* o;             // o[(b*L + t)*ld_o + head*D + d]
-  int64_t vt_tiles;
-  int64_t ld_o;
-  int B, H, G, L;
-  int q_heads;          // heads per sequence in q (H, or one more when the shared head is absent)
-  int n_grouped;        // heads h < n_grouped read group g with koff[g] <= h < koff[g + 1]
-  int koff[kMaxGroups + 1];
-  int extra_group;      // heads h >= n_grouped read this group
-  float scale_log2;     // softmax scale * log2(e)
-  // optional per-row factor of the grouped heads' outputs: o[b, t, h] is
-  // multiplied by row_scale[(b*L + t)*n_grouped + h] (h < n_grouped), or NULL
-  const float* row_scale;
-  // optional [B, H, L]: log2 of each row's softmax normalizer in the units of
-  // the scaled scores (max + log2(sum of 2^(s - max))), or NULL
-  float* lse;
-  // scratch of attention_redo_ints(B, H, L) ints, or NULL: long launches then
-  // run the fast path and the fallback as two launches (one flag per block)
-  int* redo;
-};
-// ints of the per-block flag array of a launch over B x H heads of L rows
-inline long long attention_redo_ints(int B, int H, int L) {
-  return static_cast<long long>(B) * H * ((L + 31) / 32);
-}
-template <typename T>
-hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream);
 
 // ---- K5 output -----------------------------------------------------------------
 // s[t] holds K hard slots, the shared slot and the weighted slot; w is [T, K]
