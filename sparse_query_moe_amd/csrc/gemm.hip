@@ -342,10 +342,29 @@ struct DenseProb {
   }
 };
 
+
+// Tile of a 2-D grid of (N tiles) x (M tiles).  Blocks go to the 8 XCDs
+// round-robin in launch order; when the row tiles come in whole groups of 8,
+// the tiles are renumbered so that every column tile of a row block runs on
+// the same XCD and its L2 serves the A rows to all of them.
+__device__ __forceinline__ void xcd_tile(int& row_tile, int& col_tile) {
+  const int nx = gridDim.x;
+  row_tile = blockIdx.y;
+  col_tile = blockIdx.x;
+  if ((gridDim.y & 7) == 0) {
+    const int lin = blockIdx.x + blockIdx.y * nx;
+    const int sx = lin >> 3;
+    row_tile = (sx / nx) * 8 + (lin & 7);
+    col_tile = sx % nx;
+  }
+}
+
 template <typename T, class S>
 __global__ __launch_bounds__(256) void dense_proj_kernel(DenseArgs args) {
   extern __shared__ __align__(16) char smem[];
-  DenseProb<T, S> prob(args, blockIdx.y * S::BM, blockIdx.x * S::BN);
+  int rt, ct;
+  xcd_tile(rt, ct);
+  DenseProb<T, S> prob(args, rt * S::BM, ct * S::BN);
   gemm_block<T, S>(prob, smem);
 }
 
@@ -441,7 +460,13 @@ __global__ __launch_bounds__(256) void project_kernel(DenseArgs dargs, GatherArg
   extern __shared__ __align__(16) char smem[];
   const int bid = blockIdx.x;
   if (bid < dense_blocks) {
-    DenseProb<T, SD> prob(dargs, (bid / dense_nx) * SD::BM, (bid % dense_nx) * SD::BN);
+    int rb = bid / dense_nx, c = bid % dense_nx;
+    if (by_tile == 2) {  // all column tiles of a row block on one XCD
+      const int sx = bid >> 3;
+      rb = (sx / dense_nx) * 8 + (bid & 7);
+      c = sx % dense_nx;
+    }
+    DenseProb<T, SD> prob(dargs, rb * SD::BM, c * SD::BN);
     gemm_block<T, SD>(prob, smem);
     return;
   }
@@ -449,7 +474,12 @@ __global__ __launch_bounds__(256) void project_kernel(DenseArgs dargs, GatherArg
   int tile, bg, e;
   if (by_tile) {
     tile = gb / gargs.n_lists;
-    const int li = gb % gargs.n_lists;
+    int li = gb % gargs.n_lists;
+    if (by_tile == 2) {  // tile i of every list on XCD i % 8
+      const int sx = gb >> 3;
+      tile = (sx / gargs.n_lists) * 8 + (gb & 7);
+      li = sx % gargs.n_lists;
+    }
     bg = li / gargs.E;
     e = li % gargs.E;
     const int* toff = gargs.tile_off + bg * (gargs.E + 1);  // tile map of this (b, g)
@@ -506,7 +536,9 @@ struct OutProb {
 template <typename T, class S>
 __global__ __launch_bounds__(256) void out_proj_kernel(OutArgs args) {
   extern __shared__ __align__(16) char smem[];
-  OutProb<T, S> prob(args, blockIdx.y * S::BM, blockIdx.x * S::BN);
+  int rt, ct;
+  xcd_tile(rt, ct);
+  OutProb<T, S> prob(args, rt * S::BM, ct * S::BN);
   gemm_block<T, S>(prob, smem);
 }
 
@@ -552,7 +584,9 @@ struct NtProb {
 template <typename T, class S>
 __global__ __launch_bounds__(256) void nt_gemm_kernel(NtArgs args) {
   extern __shared__ __align__(16) char smem[];
-  NtProb<T, S> prob(args, blockIdx.y * S::BM, blockIdx.x * S::BN, blockIdx.z);
+  int rt, ct;
+  xcd_tile(rt, ct);  // each z layer is a whole number of 8-block rounds when it remaps
+  NtProb<T, S> prob(args, rt * S::BM, ct * S::BN, blockIdx.z);
   gemm_block<T, S>(prob, smem);
 }
 
@@ -710,7 +744,7 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_
 
 template <typename T, class SD, class SG>
 static hipError_t launch_project_s(const DenseArgs& d, const GatherArgs& g, int per,
-                                   bool by_tile, hipStream_t stream) {
+                                   int by_tile, hipStream_t stream) {
   const int nx = (d.N + SD::BN - 1) / SD::BN;
   const int dense_blocks = d.N == 0 || d.M == 0 ? 0 : nx * ((d.M + SD::BM - 1) / SD::BM);
   const long long blocks =
@@ -724,7 +758,7 @@ static hipError_t launch_project_s(const DenseArgs& d, const GatherArgs& g, int 
     if (attr != hipSuccess) return attr;
   }
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream, d, g,
-                     nx > 0 ? nx : 1, dense_blocks, per, by_tile ? 1 : 0);
+                     nx > 0 ? nx : 1, dense_blocks, per, by_tile);
   return hipGetLastError();
 }
 
@@ -750,17 +784,21 @@ static hipError_t launch_project_d(const DenseArgs& d, const GatherArgs& g, int 
     per = per_list;
     gblocks = static_cast<long long>(per_list) * g.n_lists;
   }
+  // blocks go to the XCDs round-robin: with whole groups of 8 row blocks and
+  // 8 tiles per list, the mapping can keep the blocks that read the same x
+  // rows on one XCD's L2
+  const int xcd = by_tile && ((d.M + 127) / 128) % 8 == 0 && per_list % 8 == 0 ? 2 : (by_tile ? 1 : 0);
   const long long b128 = nx * ((d.M + 127) / 128) + gblocks;
   const bool small = b128 < cu_count();
   const long long total = small ? nx * ((d.M + 63) / 64) + gblocks : b128;
   if (deep_ring(total)) {
     typedef GemmShape<T, kGatherRows, D, WGM, WGN, 4> SG;
-    return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2, 4>, SG>(d, g, per, by_tile, stream)
-                 : launch_project_s<T, GemmShape<T, 128, 128, 2, 2, 4>, SG>(d, g, per, by_tile, stream);
+    return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2, 4>, SG>(d, g, per, by_tile ? 1 : 0, stream)
+                 : launch_project_s<T, GemmShape<T, 128, 128, 2, 2, 4>, SG>(d, g, per, xcd, stream);
   }
   typedef GemmShape<T, kGatherRows, D, WGM, WGN> SG;
-  return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2>, SG>(d, g, per, by_tile, stream)
-               : launch_project_s<T, GemmShape<T, 128, 128, 2, 2>, SG>(d, g, per, by_tile, stream);
+  return small ? launch_project_s<T, GemmShape<T, 64, 128, 2, 2>, SG>(d, g, per, by_tile ? 1 : 0, stream)
+               : launch_project_s<T, GemmShape<T, 128, 128, 2, 2>, SG>(d, g, per, xcd, stream);
 }
 
 template <typename T>
