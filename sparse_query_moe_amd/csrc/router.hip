@@ -26,8 +26,9 @@
 // order of a (token, group) is within twice that bound, the group's logits
 // are recomputed from the products in float64 in a fixed order (the same
 // accuracy as the float64 kernel below), so every decision is the one the
-// float64 logits make.  One wave takes 16 tokens and all experts; x is read
-// once, W_r once per wave (from L2), and the kernel is bound by HBM.
+// float64 logits make.  A 16-token tile takes all experts, its model
+// dimension split over 4 waves (up to 2^19 tokens) or held by one wave
+// (longer launches); x is read once, W_r once per tile (from L2).
 //
 // fp32 layers, and model widths that are not a multiple of 32
 // (router_f64_kernel): the logits are accumulated in float64 on the fp64
@@ -190,6 +191,8 @@ __device__ __forceinline__ double select_group(const double* r, int E, int k, in
 // longest launches, where every wave takes its own tile, W_r is read once
 // per 64 tokens and 8 waves share each SIMD).  Their float64 partial sums are
 // added in LDS in a fixed order.
+// (The long-launch form asks for 6 blocks per compute unit, which holds it to
+// 64 VGPRs: 8 waves per SIMD, and enough of x in flight.)
 template <int NE, int KS>
 __global__ __launch_bounds__(256, KS == 1 ? 6 : 2) void router_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
