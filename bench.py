@@ -444,18 +444,65 @@ def measured_traffic(wl_name):
     return float(kv[key]) if key in kv else None
 
 
-def roofline_for(wl, res):
+def roofline_for(wl, res, peaks=None):
     """Roofline of the dominant kernel of the step, the causal attention kernel
     (the longest single kernel at every workload), from its average duration
-    over back-to-back launches."""
+    over back-to-back launches; with `peaks` (measured_peaks) also against the
+    matrix-core rate the probe sustains on the same device."""
     kind, amount = stage_work(wl)["attention"]
     ms = res["attention_kernel_ms"]
     peak = (PEAK_BF16 if wl.dtype == W.BF16 else PEAK_FP32_MFMA) / 1e12
     ach = rate(kind, amount, ms)
-    return {"kernel": "attention_kernel", "bound": "mfma", "achieved": round(ach, 3),
-            "peak": round(peak, 3), "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-            "traffic": measured_traffic(wl.name),
-            "per_launch": {"flop": amount, "avg_ms": round(ms, 5)}}
+    out = {"kernel": "attention_kernel", "bound": "mfma", "achieved": round(ach, 3),
+           "peak": round(peak, 3), "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+           "traffic": measured_traffic(wl.name),
+           "per_launch": {"flop": amount, "avg_ms": round(ms, 5)}}
+    if peaks is not None and wl.dtype == W.BF16:
+        out["peak_measured"] = peaks["mfma_bf16_tflops"]
+        out["frac_of_measured"] = round(ach / peaks["mfma_bf16_tflops"], 4)
+    return out
+
+
+def measured_peaks(gqe, torch, mfma_ms=200.0, copy_bytes=2 << 30):
+    """What this device sustains, as the second reference beside the published
+    peaks: the bf16 matrix-core probe (four independent 32x32x16 MFMA chains
+    per wave, two waves per SIMD, nothing else) run for about `mfma_ms` per
+    launch, and the HBM copy probe over `copy_bytes` (eight times the 256 MB
+    last-level cache), each the best of its timed launches after a warm-up."""
+    def time_launch(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    blocks = gqe.peak_blocks()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    iters = 4000
+    time_launch(lambda: gqe.peak_mfma_bf16(out, blocks, iters))
+    ms = time_launch(lambda: gqe.peak_mfma_bf16(out, blocks, iters))
+    iters = max(iters, int(iters * mfma_ms / max(ms, 1e-3)))
+    best = min(time_launch(lambda: gqe.peak_mfma_bf16(out, blocks, iters)) for _ in range(3))
+    flop = blocks * 4 * iters * 4 * 32768
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("matrix-core probe produced a non-finite value")
+    del out
+    src = torch.ones(copy_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    time_launch(lambda: gqe.peak_copy(dst, src))
+    best_c = min(time_launch(lambda: gqe.peak_copy(dst, src)) for _ in range(5))
+    if not bool(torch.equal(dst, src)):
+        raise RuntimeError("copy probe result differs from its source")
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(flop / (best * 1e-3) / 1e12, 1),
+            "hbm_copy_tb_per_s": round(2 * copy_bytes / (best_c * 1e-3) / 1e12, 3),
+            "mfma_probe": f"{blocks} blocks x 4 waves x {iters} rounds of 4 chained "
+                          f"v_mfma_f32_32x32x16_bf16, best of 3 ({best:.1f} ms)",
+            "copy_probe": f"{copy_bytes} B read + {copy_bytes} B written, 16 B per access, "
+                          f"best of 5 ({best_c:.3f} ms)"}
 
 
 def _oracle_threads():
@@ -609,6 +656,10 @@ def main():
         torch.cuda.empty_cache()
     per_length.append(res)
 
+    log("[bench] measured peaks (matrix-core and HBM copy probes) ...")
+    peaks = measured_peaks(gqe, torch)
+    log(f"[bench]   {peaks}")
+
     line = {
         "metric": METRIC,
         "value": round(res["gqe_tokens_per_s"], 1),
@@ -633,7 +684,8 @@ def main():
         "attention_mfma_frac": round(res["attention_mfma_frac"], 4),
         "graph_tokens_per_s": (round(res["tokens"] / (res["graph_gqe_ms"] * 1e-3), 1)
                                if "graph_gqe_ms" in res else None),
-        "roofline": roofline_for(wl, res),
+        "roofline": roofline_for(wl, res, peaks),
+        "measured_peaks": peaks,
         "per_length": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
                        for r in per_length],
     }

@@ -18,7 +18,8 @@
  *    `layout`, which are host pointers read (or written) before the call
  *    returns.  The library never allocates or frees device memory and holds
  *    no global mutable state, except gqe_forward_noalloc's per-device scratch
- *    array (described there).  Every call is thread-safe; calls that share a
+ *    array (described there) and, in a debug build, the per-device debug
+ *    word (below).  Every call is thread-safe; calls that share a
  *    workspace must not overlap.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream), and only on `stream`.  No call synchronizes the host.
@@ -44,6 +45,15 @@
  *    input or the workspace.  Device pointers must be 16-byte aligned
  *    (router_bias: 4-byte).
  *  - B*L == 0 is valid: nothing is launched and GQE_OK is returned.
+ *  - Debug build (libgqe_debug.so, compiled with -DGQE_DEBUG): the kernels
+ *    check every index they take from the routing (expert ids in [0, E),
+ *    distinct within a group) and from the dispatch lists (each list inside
+ *    its (b, g) range, positions in [0, L), slots in [0, k_g)), and skip the
+ *    access a failed check guards.  gqe_dispatch, gqe_project, gqe_forward,
+ *    gqe_forward_noalloc and gqe_backward then synchronize `stream`, read and
+ *    clear a per-device debug word, and return GQE_ERR_DEBUG if a check
+ *    failed (the outputs are then unspecified).  Release builds compile the
+ *    checks out, never synchronize and never return GQE_ERR_DEBUG.
  */
 #ifndef GQE_H_
 #define GQE_H_
@@ -62,7 +72,8 @@ typedef enum {
   GQE_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or field  */
   GQE_ERR_UNSUPPORTED = -2,   /* valid but not built: e.g. head_dim 96       */
   GQE_ERR_WORKSPACE = -3,     /* ws_bytes smaller than gqe_workspace_bytes() */
-  GQE_ERR_HIP = -4            /* a launch was rejected by the HIP runtime    */
+  GQE_ERR_HIP = -4,           /* a launch was rejected by the HIP runtime    */
+  GQE_ERR_DEBUG = -5          /* debug builds only: an index check failed    */
 } gqe_status;
 
 typedef enum { GQE_DTYPE_BF16 = 0, GQE_DTYPE_FP32 = 1 } gqe_dtype;
@@ -332,6 +343,30 @@ int gqa_backward(const gqe_config* cfg, const void* x, const void* Wq, const voi
                  const void* Wv, const void* Wo, const void* dy, const void* fwd_workspace,
                  size_t fwd_ws_bytes, float* dx, float* dWq, float* dWk, float* dWv, float* dWo,
                  void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Measurement probes (diagnostics, not steps of the layer): what this device
+ * sustains, as the second reference beside the published peaks (bf16 matrix
+ * cores 2.5166 PFLOP/s at the nominal 2.4 GHz, HBM 8 TB/s).  Both enqueue one
+ * kernel on `stream` and return at once; the caller times them.
+ *
+ * gqe_peak_blocks: the grid gqe_peak_mfma_bf16 should get to load every SIMD
+ * with two waves (2 blocks of 256 threads per compute unit, all resident).
+ *
+ * gqe_peak_mfma_bf16: blocks x 256 threads, each wave running `iters` rounds
+ * of four independent v_mfma_f32_32x32x16_bf16 chains and nothing else:
+ * blocks * 4 * iters * 4 * 32768 flop in all.  out (device, blocks * 256
+ * floats, caller-owned) receives one finite sum per thread.  Returns
+ * GQE_ERR_INVALID_ARG for a NULL out, blocks < 1 or iters < 0.
+ *
+ * gqe_peak_copy: copies `bytes` from src to dst (device, 16-byte aligned,
+ * not overlapping, bytes a multiple of 16) in 16-byte loads and stores:
+ * `bytes` read and `bytes` written.  Returns GQE_OK with nothing enqueued
+ * when bytes == 0 (the pointers are then not looked at), and
+ * GQE_ERR_INVALID_ARG for a NULL, misaligned or overlapping pair or a size
+ * that is not a multiple of 16. */
+int gqe_peak_blocks(void);
+int gqe_peak_mfma_bf16(float* out, int blocks, int iters, hipStream_t stream);
+int gqe_peak_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 /* Static text for a gqe_status value; never NULL. */
 const char* gqe_status_string(int status);

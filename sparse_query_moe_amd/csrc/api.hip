@@ -11,7 +11,71 @@
 
 using namespace gqe;
 
+#ifdef GQE_DEBUG
+// the debug word of the index checks of a debug build (see debug_check.h)
+static __device__ uint32_t debug_word[1];
+#endif
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// The device address of a file-scope __device__ array on the device of
+// `stream`, resolved with hipGetSymbolAddress once per device (with that
+// device current) and kept in `table`.  Host code never uses such a name as
+// an address: on the host it stands for a host-side shadow.
+int symbol_on_device(const void* symbol, void** table, std::mutex& mu, hipStream_t stream,
+                     void** addr) {
+  int dev = -1;
+  const hipError_t e = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return GQE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GQE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (table[dev] == nullptr) {  // first call on this device (retried after a failure)
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return GQE_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return GQE_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t ge = hipGetSymbolAddress(&p, symbol);
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (ge != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return GQE_ERR_HIP;
+    }
+    table[dev] = p;
+  }
+  *addr = table[dev];
+  return GQE_OK;
+}
+
+// Debug builds: the kernels that take indices from the routing or the
+// dispatch lists get the device's debug word; after its launches an entry
+// point waits for them, reads and clears the word, and returns GQE_ERR_DEBUG
+// when a check failed.  Release builds pass NULL and return at once.
+#ifdef GQE_DEBUG
+std::mutex g_debug_mutex;
+void* g_debug_addr[kMaxDevices];
+uint32_t* debug_word_of(hipStream_t stream) {
+  void* p = nullptr;
+  return symbol_on_device(HIP_SYMBOL(debug_word), g_debug_addr, g_debug_mutex, stream, &p) == GQE_OK
+             ? static_cast<uint32_t*>(p)
+             : nullptr;
+}
+int debug_collect(hipStream_t stream, int st) {
+  if (st != GQE_OK) return st;
+  uint32_t* p = debug_word_of(stream);
+  if (p == nullptr || hipStreamSynchronize(stream) != hipSuccess) return GQE_ERR_HIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, p, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return GQE_ERR_HIP;
+  if (v == 0) return GQE_OK;
+  const uint32_t zero = 0;
+  if (hipMemcpy(p, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return GQE_ERR_HIP;
+  return GQE_ERR_DEBUG;
+}
+#else
+uint32_t* debug_word_of(hipStream_t) { return nullptr; }
+int debug_collect(hipStream_t, int st) { return st; }
+#endif
 
 constexpr size_t kAlign = 256;
 
@@ -228,7 +292,8 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
       static_cast<const T*>(x), B * L, d, L, D, l.pub.vt_tiles, shared ? seg : seg + 1,
       shared ? 3 : 2, static_cast<const T*>(wq), at<T>(ws, l.pub.q), at<int32_t>(ws, l.pub.counts),
       at<int32_t>(ws, l.pub.offsets), at<int32_t>(ws, l.pub.pos), at<int32_t>(ws, l.pub.slot),
-      at<int32_t>(ws, l.tile_off), B, G, E, make_group_k(c), make_rope(c), stream));
+      at<int32_t>(ws, l.tile_off), B, G, E, make_group_k(c), make_rope(c), debug_word_of(stream),
+      stream));
 }
 
 template <typename T>
@@ -301,36 +366,14 @@ namespace {
 // ---- the workspace of gqe_forward_noalloc ------------------------------------
 // One array per device, part of the library's code object: it exists from the
 // moment the runtime loads that object on a device until the process ends.
-// Host code never uses its name as an address (on the host the name stands
-// for a host-side shadow); the device address comes from hipGetSymbolAddress,
-// once per device with that device current, and is kept per device.
+// Its device address is resolved once per device (symbol_on_device).
 constexpr size_t kNoAllocBytes = GQE_NOALLOC_SCRATCH_BYTES;
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 void* g_scratch_addr[kMaxDevices];  // device address of `scratch` per device, once resolved
 
 int noalloc_scratch(hipStream_t stream, void** addr) {
-  int dev = -1;
-  const hipError_t e = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
-  if (e != hipSuccess) return GQE_ERR_HIP;
-  if (dev < 0 || dev >= kMaxDevices) return GQE_ERR_UNSUPPORTED;
-  std::lock_guard<std::mutex> lock(g_scratch_mutex);
-  if (g_scratch_addr[dev] == nullptr) {  // first call on this device (retried after a failure)
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess) return GQE_ERR_HIP;
-    if (cur != dev && hipSetDevice(dev) != hipSuccess) return GQE_ERR_HIP;
-    void* p = nullptr;
-    const hipError_t ge = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (cur != dev) (void)hipSetDevice(cur);
-    if (ge != hipSuccess || p == nullptr) {
-      (void)hipGetLastError();
-      return GQE_ERR_HIP;
-    }
-    g_scratch_addr[dev] = p;
-  }
-  *addr = g_scratch_addr[dev];
-  return GQE_OK;
+  return symbol_on_device(HIP_SYMBOL(scratch), g_scratch_addr, g_scratch_mutex, stream, addr);
 }
 
 // ---- decode ------------------------------------------------------------------
@@ -623,7 +666,8 @@ int backward_impl(const gqe_config* c, bool dense, const void* x, const void* wq
   p.scale = softmax_scale(c);
   p.aux_weight = dense ? 0.f : aux_weight;
   p.rope = make_rope(c);
-  return hip_status(launch_backward<T>(p, stream));
+  p.dbg = dense ? nullptr : debug_word_of(stream);
+  return debug_collect(stream, hip_status(launch_backward<T>(p, stream)));
 }
 
 int backward_entry(const gqe_config* cfg, bool dense, const void* x, const void* Wq,
@@ -661,6 +705,7 @@ const char* gqe_status_string(int status) {
     case GQE_ERR_UNSUPPORTED: return "GQE_ERR_UNSUPPORTED: configuration not built";
     case GQE_ERR_WORKSPACE: return "GQE_ERR_WORKSPACE: workspace too small";
     case GQE_ERR_HIP: return "GQE_ERR_HIP: the HIP runtime rejected a launch";
+    case GQE_ERR_DEBUG: return "GQE_ERR_DEBUG: an index check of the debug build failed";
     default: return "unknown gqe status";
   }
 }
@@ -720,12 +765,12 @@ int gqe_dispatch(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStr
   int st = check_common(cfg, workspace, ws_bytes, false);
   if (st != GQE_OK || empty(cfg)) return st;
   const Layout l = make_layout(cfg, false);
-  return hip_status(launch_dispatch(
+  return debug_collect(stream, hip_status(launch_dispatch(
       at<int32_t>(workspace, l.pub.idx), at<int32_t>(workspace, l.chunk_counts),
       at<int32_t>(workspace, l.pub.counts), at<int32_t>(workspace, l.pub.offsets),
       at<int32_t>(workspace, l.tile_off), at<int32_t>(workspace, l.pub.pos),
       at<int32_t>(workspace, l.pub.slot), cfg->batch, cfg->seq_len, cfg->n_groups,
-      cfg->n_experts, make_group_k(cfg), kGatherRows, stream));
+      cfg->n_experts, make_group_k(cfg), kGatherRows, debug_word_of(stream), stream)));
 }
 
 int gqe_project(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
@@ -734,9 +779,9 @@ int gqe_project(const gqe_config* cfg, const void* x, const void* Wq, const void
   if (st != GQE_OK || empty(cfg)) return st;
   if (!aligned16(x) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv))
     return GQE_ERR_INVALID_ARG;
-  return cfg->dtype == GQE_DTYPE_BF16
-             ? project_impl<bf16_t>(cfg, x, Wq, Wk, Wv, workspace, false, stream)
-             : project_impl<float>(cfg, x, Wq, Wk, Wv, workspace, false, stream);
+  return debug_collect(stream, cfg->dtype == GQE_DTYPE_BF16
+                                  ? project_impl<bf16_t>(cfg, x, Wq, Wk, Wv, workspace, false, stream)
+                                  : project_impl<float>(cfg, x, Wq, Wk, Wv, workspace, false, stream));
 }
 
 int gqe_attention(const gqe_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream) {

@@ -43,6 +43,7 @@
 
 #include <algorithm>
 
+#include "debug_check.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "routing.h"
@@ -260,6 +261,7 @@ struct AttnBwdArgs {
   // partials [n_qsplit, B, H, L, D], already scaled, summed afterwards
   int n_qsplit;
   float* dq_part;
+  uint32_t* dbg;       // debug word of a debug build's expert-id checks (else unused)
 };
 
 // queries scaled by softmax_scale * log2(e) and rounded to the storage type,
@@ -496,6 +498,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     if (a.idx != nullptr) {
       if (h < a.n_grouped) {
         const int e = qq < L ? a.idx[(static_cast<size_t>(b) * L + qq) * a.n_grouped + h] : 0;
+        if (!dbg_ok(e >= 0 && e < a.E, a.dbg, kDbgExpert)) rows[wave][lane] = -1;
         col = (g * a.E + e) * D;
       } else {
         col = a.G * a.E * D;  // the shared head's own W_q rows follow the routed ones
@@ -830,6 +833,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(AttnBwdArgs a) {
   if (a.idx != nullptr) {
     if (h < a.n_grouped) {
       const int e = a.idx[(static_cast<size_t>(b) * a.L + q) * a.n_grouped + h];
+      if (!dbg_ok(e >= 0 && e < a.E, a.dbg, kDbgExpert)) return;
       col = (group_of(a, h) * a.E + e) * D;
     } else {
       col = a.G * a.E * D;
@@ -954,6 +958,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(AttnBwdArgs a, 
     if (a.idx != nullptr) {
       if (h < a.n_grouped) {
         const int e = qq < L ? a.idx[(static_cast<size_t>(b) * L + qq) * a.n_grouped + h] : 0;
+        if (!dbg_ok(e >= 0 && e < a.E, a.dbg, kDbgExpert)) rows[wave][lane] = -1;
         col = (g * a.E + e) * D;
       } else {
         col = a.G * a.E * D;
@@ -1044,6 +1049,7 @@ struct RouterBwdArgs {
   GroupK gk;              // experts selected per group and their slot offsets
   int mode;               // 0 full (renormalized weights), 1 hard, 2 weighted concatenation
   float aux_weight;
+  uint32_t* dbg;          // debug word of a debug build's expert-id checks (else unused)
 };
 
 template <typename T>
@@ -1108,7 +1114,12 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
       for (int e = 0; e < a.E; ++e) sdp += p[e] * dp[e];
       for (int e = 0; e < a.E; ++e) grad[e] += p[e] * (dp[e] - sdp);
     }
-    if (a.dw != nullptr && a.mode == 0) {
+    bool ids_ok = true;
+#ifdef GQE_DEBUG
+    for (int j = 0; j < k; ++j) ids_ok = ids_ok && id[j] >= 0 && id[j] < a.E;
+    ids_ok = dbg_ok(ids_ok, a.dbg, kDbgExpert);
+#endif
+    if (a.dw != nullptr && a.mode == 0 && ids_ok) {
       // w = softmax over the selected logits: dr_j = w_j (dw_j - sum w dw)
       double ws[64], z = 0.0, rmax = logit[g * a.E + id[0]];
       for (int j = 0; j < k; ++j) rmax = fmax(rmax, logit[g * a.E + id[j]]);
@@ -1119,7 +1130,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
         s += ws[j] * a.dw[so + j];
       }
       for (int j = 0; j < k; ++j) grad[id[j]] += ws[j] * (a.dw[so + j] - s);
-    } else if (a.dw != nullptr && a.mode == 2) {
+    } else if (a.dw != nullptr && a.mode == 2 && ids_ok) {
       // the selected experts' p scale their slots: softmax over all E
       double dps[64];
       for (int e = 0; e < a.E; ++e) dps[e] = 0.0;
@@ -1323,6 +1334,7 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     a.kcol = p.kcol;
     a.vcol = p.vcol;
     a.idx = p.idx;
+    a.dbg = p.dbg;
     a.E = E;
     a.B = B;
     a.G = G;
@@ -1377,6 +1389,7 @@ hipError_t launch_backward(const BwdParams& p, hipStream_t stream) {
     r.wr = p.wr;
     r.bias = p.router_bias;
     r.idx = p.idx;
+    r.dbg = p.dbg;
     r.dw = p.mode == 1 ? nullptr : p.dw;
     r.counts = p.counts;
     r.gall = p.gall;

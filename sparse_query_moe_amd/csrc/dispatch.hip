@@ -19,6 +19,7 @@
 // atomics.  Sequences up to 8192 tokens use one block per (b, g) that counts,
 // then scatters; longer ones split the tokens into 256-token chunks (count
 // kernel, per-(b, g) scan over chunks, scatter kernel).
+#include "debug_check.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -44,6 +45,17 @@ __device__ __forceinline__ void load_ids(const int32_t* idx, int32_t* ids, int b
   const bool valid = t < L;
   const size_t row = (static_cast<size_t>(b) * L + t) * gk.K + gk.koff[g];
   for (int j = 0; j < gk.kg[g]; ++j) ids[j] = valid ? idx[row + j] : -1;
+}
+
+// debug builds: the k expert ids of one (token, group) lie in [0, E) and
+// differ from each other (a token picks k distinct experts)
+__device__ __forceinline__ void check_ids(const int32_t* ids, int k, int E, uint32_t* dbg) {
+  bool ok = true;
+  for (int j = 0; j < k; ++j) {
+    ok = ok && ids[j] >= 0 && ids[j] < E;
+    for (int i = 0; i < j; ++i) ok = ok && ids[i] != ids[j];
+  }
+  dbg_ok(ok, dbg, kDbgExpert);
 }
 
 // first entry of the lists of (b, g)
@@ -95,7 +107,7 @@ __device__ __forceinline__ void finish_lists(const int* cnt, int32_t* counts, in
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_off, int32_t* __restrict__ pos, int32_t* __restrict__ slot, int L,
-    int G, int E, GroupK gk, int tile_rows, int n_lists) {
+    int G, int E, GroupK gk, int tile_rows, int n_lists, uint32_t* dbg) {
   __shared__ int wcnt[kSmallRounds][kSmallWaves][32];  // count, then offset in the list, per (r, w, e)
   __shared__ int total[32];
   __shared__ int start[32];
@@ -113,6 +125,9 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     uint32_t v = 0xffffffffu;
     if (r < rounds && t < L) {
       const int32_t* p = idx + (static_cast<size_t>(b) * L + t) * gk.K + gk.koff[g];
+#ifdef GQE_DEBUG
+      check_ids(p, k, E, dbg);
+#endif
       v = 0u;
       for (int j = 0; j < 4; ++j) v |= static_cast<uint32_t>(j < k ? p[j] : 0xff) << (8 * j);
     }
@@ -186,7 +201,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx,
                                                              int32_t* __restrict__ chunk_counts,
                                                              int L, int G, int E, GroupK gk,
-                                                             int n_chunks) {
+                                                             int n_chunks, uint32_t* dbg) {
   __shared__ int cnt[4][64];
   const int c = blockIdx.x, b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -194,6 +209,9 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   int32_t ids[32];
   for (int g = 0; g < G; ++g) {
     load_ids(idx, ids, b, t, g, L, gk);
+#ifdef GQE_DEBUG
+    if (t < L) check_ids(ids, gk.kg[g], E, dbg);
+#endif
     for (int e = 0; e < E; ++e) {
       const uint64_t m = __ballot(chosen_rank(ids, gk.kg[g], e) >= 0);
       if (lane == 0) cnt[wave][g * E + e] = popc64(m);
@@ -293,17 +311,17 @@ int dispatch_chunks(int L) { return (L + kChunk - 1) / kChunk; }
 hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int32_t* pos, int32_t* slot,
                            int B, int L, int G, int E, const GroupK& gk, int tile_rows,
-                           hipStream_t stream) {
+                           uint32_t* dbg, hipStream_t stream) {
   const int n_lists = B * G * E;
   if (L <= kSmallRounds * 64 * kSmallWaves && gk.kmax <= 4) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(B * G), dim3(64 * kSmallWaves), 0, stream, idx,
-                       counts, offsets, tile_off, pos, slot, L, G, E, gk, tile_rows, n_lists);
+                       counts, offsets, tile_off, pos, slot, L, G, E, gk, tile_rows, n_lists, dbg);
     return hipGetLastError();
   }
   const int n_chunks = dispatch_chunks(L);
   const dim3 grid(n_chunks, B);
   hipLaunchKernelGGL(dispatch_count_kernel, grid, dim3(256), 0, stream, idx, chunk_counts, L, G,
-                     E, gk, n_chunks);
+                     E, gk, n_chunks, dbg);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(B * G), dim3(1024), 0, stream, chunk_counts,

@@ -28,6 +28,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "debug_check.h"
 #include "device_common.h"
 
 #include "kernels.h"
@@ -383,6 +384,7 @@ struct GatherArgs {
   int n_lists, L, d, G, E, D, H;
   int koff[kMaxGroups + 1];  // group g's slot-heads start at koff[g]
   RopeTable rope;
+  uint32_t* dbg;             // debug word (index checks of debug builds)
 };
 
 template <typename T, class S>
@@ -398,12 +400,19 @@ struct GatherProb {
     b = li / GE;
     g = (li / args.E) % args.G;
     e = li % args.E;
+    // the lists of (b, g) fill entries lb .. lb + L*k_g - 1
+    const long long lb = (static_cast<long long>(b) * args.koff[args.G] + args.koff[g]) * args.L;
+    const long long rows = static_cast<long long>(args.L) * (args.koff[g + 1] - args.koff[g]);
+    if (!dbg_ok(m0 >= 0 && cnt >= 0 && cnt <= args.L && base >= lb && base + cnt <= lb + rows,
+                args.dbg, kDbgListRange))
+      cnt = 0;  // the block computes nothing and writes nothing
   }
   __device__ __forceinline__ const T* a_any() const { return static_cast<const T*>(a.x); }
   __device__ __forceinline__ const T* b_any() const { return static_cast<const T*>(a.wq); }
   __device__ __forceinline__ const T* a_row(int r) const {
     if (m0 + r >= cnt) return nullptr;
     const int t = a.pos[base + m0 + r];
+    if (!dbg_ok(t >= 0 && t < a.L, a.dbg, kDbgPos)) return nullptr;
     return static_cast<const T*>(a.x) + (static_cast<size_t>(b) * a.L + t) * a.d;
   }
   __device__ __forceinline__ const T* b_row(int n) const {
@@ -427,6 +436,9 @@ struct GatherProb {
       if (m0 + r >= cnt || 8 * c8 >= a.D) continue;
       const int entry = base + m0 + r;
       const int t = a.pos[entry], j = a.slot[entry];
+      if (!dbg_ok(t >= 0 && t < a.L, a.dbg, kDbgPos) ||
+          !dbg_ok(j >= 0 && j < a.koff[g + 1] - a.koff[g], a.dbg, kDbgSlot))
+        continue;
       T* dst = static_cast<T*>(a.q) + ((static_cast<size_t>(b) * a.H + a.koff[g] + j) * a.L + t) * a.D + 8 * c8;
       copy8(dst, ct + r * S::LDC + 8 * c8);
     }
@@ -806,7 +818,8 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
                           const ProjSeg* segs, int nseg, const T* wq, T* q,
                           const int32_t* counts, const int32_t* offsets, const int32_t* pos,
                           const int32_t* slot, const int32_t* tile_off, int B, int G, int E,
-                          const GroupK& gk, const RopeTable& rope, hipStream_t stream) {
+                          const GroupK& gk, const RopeTable& rope, uint32_t* dbg,
+                          hipStream_t stream) {
   DenseArgs d;
   d.rope = rope;
   d.x = x;
@@ -832,6 +845,7 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
   g.pos = pos;
   g.slot = slot;
   g.tile_off = tile_off;
+  g.dbg = dbg;
   g.n_lists = B * G * E;
   g.L = L;
   g.d = K;
@@ -930,7 +944,8 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
   template hipError_t launch_project<T>(const T*, int, int, int, int, int64_t, const ProjSeg*,   \
                                         int, const T*, T*, const int32_t*, const int32_t*,       \
                                         const int32_t*, const int32_t*, const int32_t*, int, int, \
-                                        int, const GroupK&, const RopeTable&, hipStream_t);      \
+                                        int, const GroupK&, const RopeTable&, uint32_t*,         \
+                                        hipStream_t);                                            \
   template hipError_t launch_out_proj<T>(const T*, const T*, T*, int, int, int, hipStream_t);    \
   template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, hipStream_t);      \
   template hipError_t launch_nt_gemm<T>(const NtArgs&, hipStream_t);

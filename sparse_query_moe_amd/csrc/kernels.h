@@ -39,10 +39,11 @@ hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* id
 
 // ---- K2 dispatch -------------------------------------------------------------
 int dispatch_chunks(int L);
+// dbg: the debug word of a debug build's expert-id checks (see launch_project)
 hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int32_t* pos, int32_t* slot,
                            int B, int L, int G, int E, const GroupK& gk, int tile_rows,
-                           hipStream_t stream);
+                           uint32_t* dbg, hipStream_t stream);
 
 // ---- K3 projections ----------------------------------------------------------
 // One output segment of a dense projection: columns [n_begin, n_begin + n)
@@ -69,13 +70,15 @@ hipError_t launch_dense_proj(const T* x, int M, int K, int L, int D, int64_t vt_
 // routed-query projection in one launch: for every dispatch list (b, g, e),
 // the rows x[b, pos] . Wq[head g*E+e]^T land in slot-head koff[g] + slot at
 // their positions.  tile_off is the per-(b, g) tile map written by the
-// dispatch.
+// dispatch.  dbg: the debug word of a debug build's index checks (unused, and
+// may be NULL, otherwise).
 template <typename T>
 hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_tiles,
                           const ProjSeg* segs, int nseg, const T* wq, T* q,
                           const int32_t* counts, const int32_t* offsets, const int32_t* pos,
                           const int32_t* slot, const int32_t* tile_off, int B, int G, int E,
-                          const GroupK& gk, const RopeTable& rope, hipStream_t stream);
+                          const GroupK& gk, const RopeTable& rope, uint32_t* dbg,
+                          hipStream_t stream);
 
 // ---- K5 output -----------------------------------------------------------------
 // s[t] holds K hard slots, the shared slot and the weighted slot; w is [T, K]
@@ -161,6 +164,7 @@ struct BwdParams {
   float* dq_part;           // [dq_split, B, H, L, D] float partials when split
   float scale, aux_weight;
   RopeTable rope;           // rotary embedding of the forward (on == 0: none)
+  uint32_t* dbg;            // debug word of a debug build's expert-id checks (else unused)
 };
 // dK/dV query-walk splits for a bf16 backward of B x L tokens, G groups, d_h D
 int dkdv_splits(int B, int G, int L, int D);

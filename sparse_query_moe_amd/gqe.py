@@ -27,7 +27,8 @@ EXPORTS = (
     "gqa_workspace_layout",
     "gqa_project", "gqa_attention", "gqa_output", "gqa_forward", "gqe_decode_workspace_bytes",
     "gqe_decode", "gqa_decode_workspace_bytes", "gqa_decode", "gqe_backward_workspace_bytes",
-    "gqe_backward", "gqa_backward_workspace_bytes", "gqa_backward", "gqe_status_string",
+    "gqe_backward", "gqa_backward_workspace_bytes", "gqa_backward", "gqe_peak_blocks",
+    "gqe_peak_mfma_bf16", "gqe_peak_copy", "gqe_status_string",
 )
 
 
@@ -87,6 +88,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "gqa_backward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp,
                                         vp, sz, vp]),
+        "gqe_peak_blocks": (ctypes.c_int, []),
+        "gqe_peak_mfma_bf16": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, vp]),
+        "gqe_peak_copy": (ctypes.c_int, [vp, vp, sz, vp]),
         "gqe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -294,6 +298,24 @@ def gqa_backward(cfg, x, wq, wk, wv, wo, dy, fwd_ws, dx, dwq, dwk, dwv, dwo, ws,
                              _ptr(dy), _ptr(fwd_ws), fwd_ws.numel(), _ptr(dx), _ptr(dwq),
                              _ptr(dwk), _ptr(dwv), _ptr(dwo), _ptr(ws), ws.numel(),
                              _stream(stream)), "gqa_backward")
+
+
+def peak_blocks() -> int:
+    return int(_lib.gqe_peak_blocks())
+
+
+def peak_mfma_bf16(out, blocks, iters, stream=None):
+    """Enqueue the matrix-core probe: blocks*4*iters*4*32768 flop; out holds
+    blocks*256 float32 values."""
+    _check(_lib.gqe_peak_mfma_bf16(_ptr(out), blocks, iters, _stream(stream)), "gqe_peak_mfma_bf16")
+
+
+def peak_copy(dst, src, stream=None):
+    """Enqueue the HBM copy probe: src's bytes into dst (same size)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise GqeError("gqe_peak_copy: dst and src sizes differ")
+    _check(_lib.gqe_peak_copy(_ptr(dst), _ptr(src), n, _stream(stream)), "gqe_peak_copy")
 
 
 def workspace_views(cfg: GqeConfig, ws: torch.Tensor, dense: bool = False) -> dict:

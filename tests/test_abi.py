@@ -23,6 +23,10 @@ def gqe():
         from sparse_query_moe_amd import build
         build.build()
     from sparse_query_moe_amd import gqe as mod
+    # test_asan.py runs this file against the host-ASan build of the library
+    other = os.environ.get("GQE_TEST_LIBRARY")
+    if other:
+        mod._lib = mod.load_library(other)
     return mod
 
 
@@ -32,6 +36,10 @@ def test_header_declares_the_boundary():
               "gqe_route", "gqe_dispatch", "gqe_project", "gqe_attention", "gqe_output",
               "gqe_status_string"):
         assert n in names
+
+
+def test_binding_uses_the_library_under_test(gqe):
+    assert gqe._lib._name == os.environ.get("GQE_TEST_LIBRARY", LIB)
 
 
 def test_library_exports_every_declared_symbol(gqe):
@@ -192,3 +200,33 @@ def test_group_top_k_validation_and_reach(gqe):
     for bad in ([0, 2], [1, 3]):
         assert gqe.gqe_workspace_bytes(
             gqe.make_config(1, 64, 256, 2, 2, 1, 32, dtype="fp32", group_top_k=bad)) == 0
+
+
+def test_probe_host_errors_before_any_launch(gqe):
+    """The measurement probes reject bad arguments on the host."""
+    lib = gqe._lib
+    assert lib.gqe_peak_mfma_bf16(None, 1, 1, None) == -1
+    assert lib.gqe_peak_mfma_bf16(ctypes.c_void_p(256), 0, 1, None) == -1
+    assert lib.gqe_peak_mfma_bf16(ctypes.c_void_p(256), 1, -1, None) == -1
+    assert lib.gqe_peak_copy(None, ctypes.c_void_p(256), 16, None) == -1
+    assert lib.gqe_peak_copy(ctypes.c_void_p(8), ctypes.c_void_p(4096), 16, None) == -1   # misaligned
+    assert lib.gqe_peak_copy(ctypes.c_void_p(4096), ctypes.c_void_p(256), 24, None) == -1  # not 16 B steps
+    assert lib.gqe_peak_copy(ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 1024), 2048, None) == -1  # overlap
+    assert lib.gqe_peak_copy(ctypes.c_void_p(4096), ctypes.c_void_p(256), 0, None) == 0  # nothing to do
+    assert lib.gqe_peak_copy(None, None, 0, None) == 0
+
+
+def test_debug_library_exports_every_declared_symbol():
+    """The index-checked debug build has the same boundary."""
+    from sparse_query_moe_amd import build
+    if not os.path.exists(build.DEBUG_LIB):
+        build.build(variant="debug")
+    lib = ctypes.CDLL(build.DEBUG_LIB)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(gqe):
+    for st, name in ((0, "GQE_OK"), (-1, "GQE_ERR_INVALID_ARG"), (-2, "GQE_ERR_UNSUPPORTED"),
+                     (-3, "GQE_ERR_WORKSPACE"), (-4, "GQE_ERR_HIP"), (-5, "GQE_ERR_DEBUG")):
+        assert gqe.status_string(st).startswith(name)
