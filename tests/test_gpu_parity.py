@@ -330,10 +330,9 @@ def test_ablation_output_modes(gqe, name, L, B, mode):
 
 
 def test_forward_equals_stages_and_graph_replay(gqe):
-    """gqe_forward (dense projection forked to a second stream) gives the same
-    bits as the five stage calls on one stream, and so does every replay of a
-    HIP graph captured from it, with eager work and synchronizations between
-    the replays."""
+    """gqe_forward gives the same bits as the five stage calls, and so does
+    every replay of a HIP graph captured from it, with eager work and
+    synchronizations between the replays."""
     wl, I = inputs("l2k")
     dev = device_inputs(wl, I)
     cfg, ws, y_fwd = run_gqe(gqe, wl, I, dev)
@@ -367,6 +366,23 @@ def test_forward_equals_stages_and_graph_replay(gqe):
         gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], y_st, ws2)
         torch.cuda.synchronize()
     del graph
+
+
+def test_graph_capture_of_the_first_call():
+    """A fresh process whose first gqe_forward calls are made under HIP graph
+    capture (short and long launch forms: 2k, 8k x 4, 128k) replays them
+    exactly (tests/graph_first_call.py)."""
+    import os
+    import subprocess
+    import sys
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    here = os.path.dirname(os.path.abspath(__file__))
+    log("[graph] first calls under capture in a child process: l2k b4_l8k l128k")
+    res = subprocess.run([sys.executable, os.path.join(here, "graph_first_call.py"), "l2k", "b4_l8k",
+                          "l128k"], capture_output=True, text=True, timeout=300)
+    log(res.stdout[-2000:])
+    assert res.returncode == 0 and "graph first call ok" in res.stdout, res.stderr[-3000:]
 
 
 @pytest.mark.parametrize("L,B,G,E,k,D,dtype", [
