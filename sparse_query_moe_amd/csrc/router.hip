@@ -392,15 +392,20 @@ __global__ __launch_bounds__(256, KS == 1 ? 6 : 2) void router_bf16_kernel(
   // most blocks have no flagged pair and end here
   if (__syncthreads_or(any_fix ? 1 : 0) == 0) return;
 
-  // exact recomputation of the flagged pairs: one wave per pair, 16 lanes per
-  // expert (4 experts at a time), each lane 8 dims per 16-byte load at a
-  // stride of 128 dims; float64 products summed lane-sequentially, then over
-  // the 16 lanes in a fixed butterfly
-  for (int c0 = wave * 64; c0 < tasks; c0 += 256) {
+  // exact recomputation of the flagged pairs: the block's waves take them in
+  // turn (the n-th flagged pair goes to wave n mod 4), one wave per pair, 16
+  // lanes per expert (4 experts at a time), each lane 8 dims per 16-byte load
+  // at a stride of 128 dims, FB loads of each operand issued before their
+  // products; float64 products summed lane-sequentially in dimension order,
+  // then over the 16 lanes in a fixed butterfly
+  constexpr int FB = KS == 1 ? 2 : 4;  // loads in flight, within the kernels' register budgets
+  int nth = 0;
+  for (int c0 = 0; c0 < tasks; c0 += 64) {
     uint64_t m = __ballot(c0 + lane < tasks && redo[c0 + lane] != 0);
     while (m) {
       const int task = c0 + __builtin_ctzll(m);
       m &= m - 1;
+      if ((nth++ & 3) != wave) continue;
       const int tt = task / G, g = task % G;
       const bf16_t* xr = x + static_cast<size_t>(blk0 + tt) * d;
       const int eg = lane >> 4, sl = lane & 15;
@@ -408,13 +413,20 @@ __global__ __launch_bounds__(256, KS == 1 ? 6 : 2) void router_bf16_kernel(
         const int e = e0 + eg;
         const bf16_t* wrow = wr + static_cast<size_t>(g * E + (e < E ? e : 0)) * d;
         double sacc = 0.0;
-#pragma unroll 8
-        for (int c = 8 * sl; c < d; c += 128) {
-          const bf16x8 xv = load_frag(xr + c), wv = load_frag(wrow + c);
+        for (int c0d = 8 * sl; c0d < d; c0d += 128 * FB) {
+          bf16x8 xv[FB], wv[FB];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            sacc = fma(static_cast<double>(static_cast<float>(xv[j])),
-                       static_cast<double>(static_cast<float>(wv[j])), sacc);
+          for (int u = 0; u < FB; ++u) {
+            const int c = c0d + 128 * u;
+            xv[u] = c < d ? load_frag(xr + c) : bf16x8{};
+            wv[u] = c < d ? load_frag(wrow + c) : bf16x8{};
+          }
+#pragma unroll
+          for (int u = 0; u < FB; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)  // zero padding past d adds exact zeros
+              sacc = fma(static_cast<double>(static_cast<float>(xv[u][j])),
+                         static_cast<double>(static_cast<float>(wv[u][j])), sacc);
         }
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) sacc += __shfl_xor(sacc, off, 64);
