@@ -415,6 +415,63 @@ def measure_sweep(gqe, torch, steps, warmup, batch=4, seq_len=8192):
     return {"workload": base.description, "points": out}
 
 
+def measure_ablation(gqe, torch, steps, warmup, name="b4_l8k"):
+    """The output constructions of the pages' ablation (pptc.cn section 4.3):
+    the full layer, hard concatenation only, and weighted concatenation
+    without the renormalized slot, each timed as one gqe_forward against dense
+    GQA on the same inputs (W_O of the ablations: its first k*G*d_h input
+    columns)."""
+    wl = W.WORKLOADS[name]
+    I = W.make_inputs(wl, with_gqa=True)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to("cuda")
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    d = {n: dev(v) for n, v in I.items()}
+    K = wl.top_k * wl.n_groups
+    d["wo_hard"] = dev(np.ascontiguousarray(I["wo"][:, :K * wl.head_dim]))
+    y = torch.empty((wl.batch, wl.seq_len, wl.d_model), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    out = []
+    t_gqa = None
+    for mode in ("full", "hard", "weighted_concat"):
+        cfg = gqe.make_config(wl.batch, wl.seq_len, wl.d_model, wl.n_groups, wl.n_experts,
+                              wl.top_k, wl.head_dim, dtype=wl.dtype, router_bias=d["br"],
+                              output_mode=mode)
+        ws = gqe.alloc_workspace(cfg)
+        wo = d["wo"] if mode == "full" else d["wo_hard"]
+        t = timed(lambda: gqe.gqe_forward(cfg, d["x"], d["wq"], d["wk"], d["wv"], d["wr"], wo,
+                                          y, ws))
+        if t_gqa is None:
+            ws_d = gqe.alloc_workspace(cfg, dense=True)
+            t_gqa = timed(lambda: gqe.gqa_forward(cfg, d["x"], d["wq_dense"], d["wk"], d["wv"],
+                                                  d["wo_dense"], y, ws_d))
+            del ws_d
+        out.append({"output_mode": mode, "slot_heads": K + (1 if mode == "full" else 0),
+                    "gqe_ms": round(t, 5), "gqa_ms": round(t_gqa, 5),
+                    "speedup_vs_gqa": round(t_gqa / t, 4)})
+        log(f"[bench]   ablation {out[-1]}")
+        del ws
+    del d, y
+    torch.cuda.empty_cache()
+    return {"workload": wl.description, "points": out}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.txt")
 KERNEL_SOURCES = ("attention.hip", "attention.h", "device_common.h")
 
@@ -598,7 +655,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the expert-pool and per-group-k sweep")
+                    help="skip the expert-pool and per-group-k sweep and the ablation timing")
     ap.add_argument("--training", default="l2k,b4_l8k",
                     help="workloads whose training step (forward + backward) is timed "
                          "(comma list, '' = none)")
@@ -702,6 +759,8 @@ def main():
     if not args.no_sweep:
         log("[bench] expert-pool and per-group-k sweep ...")
         line["sweep"] = measure_sweep(gqe, torch, min(args.steps, 20), 3)
+        log("[bench] output constructions of the ablation ...")
+        line["ablation"] = measure_ablation(gqe, torch, min(args.steps, 20), 3)
     if not args.no_decode:
         log("[bench] decode step ...")
         line["decode"] = measure_decode(gqe, torch, args.steps, args.warmup)
