@@ -218,10 +218,24 @@ int gqe_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace
 /* The whole GQE prefill layer: the work of gqe_route, gqe_dispatch,
  * gqe_project, gqe_attention and gqe_output, in that order on `stream` (the
  * dense and the gathered projections share one launch).  Works under HIP
- * graph capture of `stream`, first call included. */
+ * graph capture of `stream`, first call included.
+ *
+ * Short bf16 layers (gqe_forward_is_short) take four launches instead: the
+ * router beside one dense projection of every expert's query head (with the
+ * shared head, K and V^T), the attention reading each slot-head's query row
+ * through the routing indices, the dispatch lists beside the weighted slot,
+ * and W_O.  The workspace (every view of gqe_ws_layout) and `out` are then
+ * bit for bit what the staged calls produce; the workspace also holds the
+ * all-heads projection (gqe_workspace_bytes counts it). */
 int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,
                 const void* Wv, const void* Wr, const void* Wo, void* out,
                 void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* 1 when gqe_forward takes the short-layer launches for `cfg`: bf16 storage,
+ * d_model a multiple of 128, G*E <= 64, at most 8192 tokens (batch * seq_len),
+ * seq_len <= 8192 and every k_g <= 4; 0 otherwise; a negative status for an
+ * invalid cfg.  Host only: launches nothing. */
+int gqe_forward_is_short(const gqe_config* cfg);
 
 /* gqe_forward for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation): the

@@ -174,7 +174,19 @@ bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr
 struct Layout {
   gqe_ws_layout pub;
   size_t chunk_counts, tile_off, redo;
+  size_t qall;  // short forward: every expert's query head, then the shared one
 };
+
+// Short bf16 layers take the one-pass front (forward_short): at most
+// kShortTokens tokens, sequences the one-block dispatch covers, and a router
+// in its split bf16 form.
+constexpr long long kShortTokens = 8192;
+bool short_forward(const gqe_config* c) {
+  return c->dtype == GQE_DTYPE_BF16 && c->d_model % 128 == 0 &&
+         c->n_groups * c->n_experts <= 64 &&
+         static_cast<long long>(c->batch) * c->seq_len <= kShortTokens &&
+         c->seq_len <= kDispatchSmallMaxL && max_k(c) <= 4;
+}
 
 // slot-heads that attend: every routed slot and the shared head (full
 // output), or all G*E dense heads
@@ -219,6 +231,7 @@ Layout make_layout(const gqe_config* c, bool dense) {
   if (dense) l.pub.scratch = off;
   l.redo = take(static_cast<size_t>(attention_redo_ints(c->batch, attn_heads(c, dense),
                                                         c->seq_len)) * 4);
+  if (!dense && short_forward(c)) l.qall = take(B * (G * E + 1) * L * D * es);
   l.pub.total = off;
   l.pub.vt_tiles = static_cast<int64_t>(vt_tiles);
   return l;
@@ -296,11 +309,22 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
       stream));
 }
 
+// gather: the short forward's attention, whose slot-heads read their query
+// rows from the all-heads projection through the routing indices (and store
+// them into q)
 template <typename T>
-int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream) {
+int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream,
+                   bool gather = false) {
   const Layout l = make_layout(c, dense);
   const int G = c->n_groups, E = c->n_experts, D = c->head_dim;
-  AttnParams p;
+  AttnParams p{};
+  if (gather) {
+    p.q_idx = at<int32_t>(ws, l.pub.idx);
+    p.q_src = at<T>(ws, l.qall);
+    p.q_src_heads = G * E + 1;
+    p.q_E = E;
+    p.q_idx_stride = total_k(c);
+  }
   p.row_scale = nullptr;
   p.lse = at<float>(ws, l.pub.lse);
   p.redo = at<int>(ws, l.redo);
@@ -331,6 +355,86 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
   }
   p.scale_log2 = scale_log2(c);
   return hip_status(launch_attention<T>(p, D, stream));
+}
+
+// Short bf16 layers in four launches: (1) the router's blocks beside one
+// dense projection of every expert's query head, the shared head, K and V^T
+// (nothing there waits for the routing); (2) the attention, whose slot-heads
+// read their query rows through the routing indices; (3) the dispatch lists
+// beside the weighted slot; (4) W_O.  Every routed query is projected, G*E
+// heads instead of the k*G selected (about half again the projection's
+// work), which these lengths absorb: their kernels are bound by latency, and
+// the router and the dispatch leave the critical path.  The workspace ends up
+// as after the staged calls: the same idx, w, lists, q, K, V^T, s and lse.
+int forward_short(const gqe_config* c, const void* x, const void* wq, const void* wk,
+                  const void* wv, const void* wr, const void* wo, void* out, void* ws,
+                  hipStream_t stream) {
+  typedef bf16_t T;
+  const Layout l = make_layout(c, false);
+  const int B = c->batch, L = c->seq_len, G = c->n_groups, E = c->n_experts, D = c->head_dim;
+  const GroupK gk = make_group_k(c);
+  const bool shared = full_output(c);
+  RouterArgs r;
+  r.wr = static_cast<const T*>(wr);
+  r.bias = c->router_bias;
+  r.idx = at<int32_t>(ws, l.pub.idx);
+  r.w = at<float>(ws, l.pub.w);
+  r.G = G;
+  r.E = E;
+  r.gk = gk;
+  r.renorm = c->output_mode != GQE_OUTPUT_WEIGHTED_CONCAT ? 1 : 0;  // else w = p
+  ProjSeg seg[3];
+  const int nq = (G * E + (shared ? 1 : 0)) * D;
+  seg[0].w = wq;
+  seg[0].out = at<T>(ws, l.qall);
+  seg[0].n_begin = 0;
+  seg[0].n = nq;
+  seg[0].heads = G * E + 1;
+  seg[0].head_base = 0;
+  seg[0].transposed = 0;
+  seg[0].rope = 1;
+  seg[1].w = wk;
+  seg[1].out = at<T>(ws, l.pub.k);
+  seg[1].n_begin = nq;
+  seg[1].n = G * D;
+  seg[1].heads = G;
+  seg[1].head_base = 0;
+  seg[1].transposed = 0;
+  seg[1].rope = 1;
+  seg[2].w = wv;
+  seg[2].out = at<T>(ws, l.pub.vt);
+  seg[2].n_begin = nq + G * D;
+  seg[2].n = G * D;
+  seg[2].heads = G;
+  seg[2].head_base = 0;
+  seg[2].transposed = 1;
+  seg[2].rope = 0;
+  hipError_t e = launch_front(r, static_cast<const T*>(x), B * L, c->d_model, L, D,
+                              l.pub.vt_tiles, seg, 3, make_rope(c), stream);
+  if (e != hipSuccess) return GQE_ERR_HIP;
+  int st = attention_impl<T>(c, ws, false, stream, true);
+  if (st != GQE_OK) return st;
+  DispatchArgs da;
+  da.idx = at<int32_t>(ws, l.pub.idx);
+  da.counts = at<int32_t>(ws, l.pub.counts);
+  da.offsets = at<int32_t>(ws, l.pub.offsets);
+  da.tile_off = at<int32_t>(ws, l.tile_off);
+  da.pos = at<int32_t>(ws, l.pub.pos);
+  da.slot = at<int32_t>(ws, l.pub.slot);
+  da.L = L;
+  da.G = G;
+  da.E = E;
+  da.gk = gk;
+  da.tile_rows = kGatherRows;
+  da.n_lists = B * G * E;
+  da.blocks = B * G;
+  da.dbg = debug_word_of(stream);
+  e = launch_slot_dispatch<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), shared ? B * L : 0,
+                              total_k(c), D, da, stream);
+  if (e != hipSuccess) return GQE_ERR_HIP;
+  e = launch_out_proj<T>(at<T>(ws, l.pub.s), static_cast<const T*>(wo), static_cast<T*>(out),
+                         B * L, c->d_model, slot_count(c) * D, stream);
+  return debug_collect(stream, hip_status(e));
 }
 
 template <typename T>
@@ -809,11 +913,21 @@ int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void
   if (!aligned16(x) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(Wr) ||
       !aligned16(Wo) || !aligned16(out))
     return GQE_ERR_INVALID_ARG;
+  if (cfg->router_bias && (reinterpret_cast<uintptr_t>(cfg->router_bias) & 3u))
+    return GQE_ERR_INVALID_ARG;
+  if (short_forward(cfg))
+    return forward_short(cfg, x, Wq, Wk, Wv, Wr, Wo, out, workspace, stream);
   if ((st = gqe_route(cfg, x, Wr, workspace, ws_bytes, stream)) != GQE_OK) return st;
   if ((st = gqe_dispatch(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
   if ((st = gqe_project(cfg, x, Wq, Wk, Wv, workspace, ws_bytes, stream)) != GQE_OK) return st;
   if ((st = gqe_attention(cfg, workspace, ws_bytes, stream)) != GQE_OK) return st;
   return gqe_output(cfg, Wo, out, workspace, ws_bytes, stream);
+}
+
+int gqe_forward_is_short(const gqe_config* cfg) {
+  const int st = check_cfg(cfg);
+  if (st != GQE_OK) return st;
+  return short_forward(cfg) ? 1 : 0;
 }
 
 int gqe_forward_noalloc(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,

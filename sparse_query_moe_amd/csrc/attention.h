@@ -35,6 +35,14 @@ struct AttnParams {
   // scratch of attention_redo_ints(B, H, L) ints, or NULL: long launches then
   // run the fast path and the fallback as two launches (one flag per block)
   int* redo;
+  // optional query gather, or NULL: with it, head h < n_grouped of group g
+  // reads row t from head g*q_E + q_idx[(b*L + t)*q_idx_stride + h] of
+  // q_src ([B, q_src_heads, L, D]: every expert's query head, then the
+  // shared one), any other head from head q_src_heads - 1, and the block
+  // stores the rows it read into q at their slot-head and position
+  const int32_t* q_idx;
+  const void* q_src;
+  int q_src_heads, q_E, q_idx_stride;
 };
 // ints of the per-block flag array of a launch over B x H heads of L rows
 inline long long attention_redo_ints(int B, int H, int L) {

@@ -246,12 +246,26 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       qrow[qb] = qw0 + 32 * qb + (lane & 31);
+      // this lane's query row: from q, or through the routing indices
+      const T* qsrc = Q + static_cast<size_t>(qrow[qb]) * D;
+      if (p.q_idx != nullptr && qrow[qb] < L) {
+        int sh = p.q_src_heads - 1;  // the shared head
+        if (head < p.n_grouped) {
+          const int e = p.q_idx[(static_cast<size_t>(b) * L + qrow[qb]) * p.q_idx_stride + head];
+          sh = g * p.q_E + min(max(e, 0), p.q_E - 1);
+        }
+        qsrc = static_cast<const T*>(p.q_src) +
+               ((static_cast<size_t>(b) * p.q_src_heads + sh) * L + qrow[qb]) * D;
+      }
       float dot = 0.f;
 #pragma unroll
       for (int ks = 0; ks < S::NKS; ++ks) {
         if (qrow[qb] < L) {
-          qf[qb][ks] = scale_frag(load_frag(Q + static_cast<size_t>(qrow[qb]) * D + ks * 16 + 8 * half),
-                                  p.scale_log2);
+          const F raw = load_frag(qsrc + ks * 16 + 8 * half);
+          if (p.q_idx != nullptr && grp == 0)  // the slot-major copy of the row
+            *reinterpret_cast<F*>(const_cast<T*>(Q) + static_cast<size_t>(qrow[qb]) * D + ks * 16 +
+                                  8 * half) = raw;
+          qf[qb][ks] = scale_frag(raw, p.scale_log2);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) qf[qb][ks][j] = 0;

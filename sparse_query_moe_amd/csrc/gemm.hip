@@ -32,6 +32,8 @@
 #include "device_common.h"
 
 #include "kernels.h"
+#include "dispatch_dev.h"
+#include "router_dev.h"
 
 namespace gqe {
 
@@ -510,6 +512,37 @@ __global__ __launch_bounds__(256) void project_kernel(DenseArgs dargs, GatherArg
 }
 
 // ---------------------------------------------------------------------------
+// short sequences: the router's blocks, then the dense projection's tiles, in
+// one grid.  The routing and the projection of every query head, K and V^T
+// are independent, so the router's latency hides behind the GEMM tiles, and
+// the attention that follows reads each slot-head's query row through the
+// routing indices.  Tiles run in the XCD-aware order of xcd_tile when the
+// router blocks come in whole groups of 8.
+// ---------------------------------------------------------------------------
+template <class S, int NE>
+__global__ __launch_bounds__(256) void front_kernel(RouterArgs r, DenseArgs dargs,
+                                                    int router_blocks, int dense_nx,
+                                                    int dense_ny) {
+  extern __shared__ __align__(16) char smem[];
+  const int bid = blockIdx.x;
+  if (bid < router_blocks) {  // the router's LDS overlays the GEMM ring's
+    router_bf16_block<NE, 4, 1>(bid, *reinterpret_cast<RouterSmem<NE, 4, 1>*>(smem),
+                                static_cast<const bf16_t*>(dargs.x), r.wr, r.bias, r.idx, r.w,
+                                dargs.M, dargs.K, r.G, r.E, r.gk, r.renorm);
+    return;
+  }
+  const int t = bid - router_blocks;
+  int rb = t / dense_nx, c = t % dense_nx;
+  if ((dense_ny & 7) == 0 && (router_blocks & 7) == 0) {  // a row block's tiles on one XCD
+    const int sx = t >> 3;
+    rb = (sx / dense_nx) * 8 + (t & 7);
+    c = sx % dense_nx;
+  }
+  DenseProb<bf16_t, S> prob(dargs, rb * S::BM, c * S::BN);
+  gemm_block<bf16_t, S>(prob, smem);
+}
+
+// ---------------------------------------------------------------------------
 // output projection (row-major)
 // ---------------------------------------------------------------------------
 struct OutArgs {
@@ -626,11 +659,10 @@ __global__ __launch_bounds__(256) void nt_split_reduce_kernel(NtArgs a, int zs) 
 // experts' outputs with the router weights; a plain sum over groups)
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void weighted_slot_kernel(T* __restrict__ s,
-                                                            const float* __restrict__ w,
-                                                            int n_tokens, int K, int D) {
+__device__ __forceinline__ void weighted_slot_item(size_t gid, T* __restrict__ s,
+                                                   const float* __restrict__ w, int n_tokens,
+                                                   int K, int D) {
   const int per_tok = D / 4;
-  const size_t gid = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= static_cast<size_t>(n_tokens) * per_tok) return;
   const int t = static_cast<int>(gid / per_tok);
   const int c = static_cast<int>(gid % per_tok) * 4;
@@ -651,6 +683,32 @@ __global__ __launch_bounds__(256) void weighted_slot_kernel(T* __restrict__ s,
   dst[1] = from_f32<T>(acc1);
   dst[2] = from_f32<T>(acc2);
   dst[3] = from_f32<T>(acc3);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void weighted_slot_kernel(T* __restrict__ s,
+                                                            const float* __restrict__ w,
+                                                            int n_tokens, int K, int D) {
+  weighted_slot_item<T>(static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x, s, w,
+                        n_tokens, K, D);
+}
+
+// short sequences: the dispatch's blocks (one per (b, g)) beside the weighted
+// slot's, in one launch of 1024-thread blocks.  The short forward's
+// projection and attention read the routing indices directly, so nothing in
+// it waits for the lists: they are built here, off the critical path.
+template <typename T>
+__global__ __launch_bounds__(1024) void slot_dispatch_kernel(T* __restrict__ s,
+                                                             const float* __restrict__ w,
+                                                             int n_tokens, int K, int D,
+                                                             DispatchArgs da) {
+  if (static_cast<int>(blockIdx.x) < da.blocks) {
+    dispatch_small_block(blockIdx.x, da.idx, da.counts, da.offsets, da.tile_off, da.pos, da.slot,
+                         da.L, da.G, da.E, da.gk, da.tile_rows, da.n_lists, da.dbg);
+    return;
+  }
+  weighted_slot_item<T>(static_cast<size_t>(blockIdx.x - da.blocks) * 1024 + threadIdx.x, s, w,
+                        n_tokens, K, D);
 }
 
 }  // namespace
@@ -863,6 +921,59 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
   }
 }
 
+template <class S, int NE>
+static hipError_t launch_front_s(const RouterArgs& r, const DenseArgs& d, hipStream_t stream) {
+  const int router_blocks = (d.M + 15) / 16;
+  const int nx = (d.N + S::BN - 1) / S::BN, ny = (d.M + S::BM - 1) / S::BM;
+  auto kern = front_kernel<S, NE>;
+  constexpr int lds = sizeof(RouterSmem<NE, 4, 1>) > S::LDS ? sizeof(RouterSmem<NE, 4, 1>) : S::LDS;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(router_blocks + nx * ny)), dim3(256), lds,
+                     stream, r, d, router_blocks, nx, ny);
+  return hipGetLastError();
+}
+
+template <int NE>
+static hipError_t launch_front_ne(const RouterArgs& r, const DenseArgs& d, hipStream_t stream) {
+  switch (choose_tiles(d.M, d.N)) {
+    case Tiles::k64: return launch_front_s<GemmShape<bf16_t, 64, 128, 2, 2>, NE>(r, d, stream);
+    case Tiles::k64Deep: return launch_front_s<GemmShape<bf16_t, 64, 128, 2, 2, 4>, NE>(r, d, stream);
+    case Tiles::k128Deep: return launch_front_s<GemmShape<bf16_t, 128, 128, 2, 2, 4>, NE>(r, d, stream);
+    default: return launch_front_s<GemmShape<bf16_t, 128, 128, 2, 2>, NE>(r, d, stream);
+  }
+}
+
+hipError_t launch_front(const RouterArgs& r, const bf16_t* x, int M, int K, int L, int D,
+                        int64_t vt_tiles, const ProjSeg* segs, int nseg, const RopeTable& rope,
+                        hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int GE = r.G * r.E;
+  if (K % 128 != 0 || GE > 64 || GE <= 0 || M > kFrontMaxTokens) return hipErrorInvalidValue;
+  DenseArgs d;
+  d.rope = rope;
+  d.x = x;
+  d.M = M;
+  d.K = K;
+  d.L = L;
+  d.D = D;
+  d.vt_tiles = vt_tiles;
+  d.nseg = nseg;
+  int N = 0;
+  for (int i = 0; i < nseg; ++i) {
+    d.seg[i] = segs[i];
+    N = segs[i].n_begin + segs[i].n;
+  }
+  d.N = N;
+  switch ((GE + 15) / 16) {
+    case 1: return launch_front_ne<1>(r, d, stream);
+    case 2: return launch_front_ne<2>(r, d, stream);
+    case 3: return launch_front_ne<3>(r, d, stream);
+    default: return launch_front_ne<4>(r, d, stream);
+  }
+}
+
 template <typename T>
 hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream) {
@@ -938,6 +1049,18 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_slot_dispatch(T* s, const float* w, int n_tokens, int K, int D,
+                                const DispatchArgs& da, hipStream_t stream) {
+  if (da.L > kDispatchSmallMaxL || da.gk.kmax > 4) return hipErrorInvalidValue;
+  const long long items = static_cast<long long>(n_tokens) * (D / 4);
+  const long long blocks = da.blocks + (items + 1023) / 1024;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_dispatch_kernel<T>, dim3(static_cast<unsigned>(blocks)), dim3(1024), 0,
+                     stream, s, w, n_tokens, K, D, da);
+  return hipGetLastError();
+}
+
 #define GQE_INST(T)                                                                              \
   template hipError_t launch_dense_proj<T>(const T*, int, int, int, int, int64_t, const ProjSeg*, \
                                            int, const RopeTable&, hipStream_t);                  \
@@ -948,6 +1071,8 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
                                         hipStream_t);                                            \
   template hipError_t launch_out_proj<T>(const T*, const T*, T*, int, int, int, hipStream_t);    \
   template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, hipStream_t);      \
+  template hipError_t launch_slot_dispatch<T>(T*, const float*, int, int, int,                   \
+                                              const DispatchArgs&, hipStream_t);                 \
   template hipError_t launch_nt_gemm<T>(const NtArgs&, hipStream_t);
 GQE_INST(bf16_t)
 GQE_INST(float)

@@ -80,6 +80,25 @@ hipError_t launch_project(const T* x, int M, int K, int L, int D, int64_t vt_til
                           const GroupK& gk, const RopeTable& rope, uint32_t* dbg,
                           hipStream_t stream);
 
+// ---- short sequences: the router beside the dense projection ----------------
+// One launch of the bf16 router's blocks (the split form: 16 tokens per block,
+// the model dimension over 4 waves) and the dense projection's tiles (segments
+// as for launch_dense_proj); neither reads what the other writes.  Requires
+// d % 128 == 0, G*E <= 64 and at most kFrontMaxTokens tokens.
+constexpr int kFrontMaxTokens = 1 << 15;
+struct RouterArgs {
+  const bf16_t* wr;
+  const float* bias;
+  int32_t* idx;
+  float* w;
+  int G, E;
+  GroupK gk;
+  int renorm;
+};
+hipError_t launch_front(const RouterArgs& r, const bf16_t* x, int M, int K, int L, int D,
+                        int64_t vt_tiles, const ProjSeg* segs, int nseg, const RopeTable& rope,
+                        hipStream_t stream);
+
 // ---- K5 output -----------------------------------------------------------------
 // s[t] holds K hard slots, the shared slot and the weighted slot; w is [T, K]
 template <typename T>
@@ -88,6 +107,21 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
 template <typename T>
 hipError_t launch_out_proj(const T* a, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream);
+// Sequences of at most kDispatchSmallMaxL tokens with k_g <= 4: the dispatch
+// (as launch_dispatch, blocks = B*G, one per (b, g)) and the weighted slot
+// (as launch_weighted_slot; n_tokens = 0 for none) in one launch.
+constexpr int kDispatchSmallMaxL = 8192;
+struct DispatchArgs {
+  const int32_t* idx;
+  int32_t *counts, *offsets, *tile_off, *pos, *slot;
+  int L, G, E;
+  GroupK gk;
+  int tile_rows, n_lists, blocks;
+  uint32_t* dbg;
+};
+template <typename T>
+hipError_t launch_slot_dispatch(T* s, const float* w, int n_tokens, int K, int D,
+                                const DispatchArgs& da, hipStream_t stream);
 
 // ---- backward: C[M, N] = A[M, K] . B[N, K]^T in float32 ------------------------
 // Rows of C go to up to four segments: row m in [row_begin, row_begin + rows)

@@ -23,7 +23,8 @@ _TORCH_DTYPE = {DTYPE_BF16: torch.bfloat16, DTYPE_FP32: torch.float32}
 # every entry point include/gqe.h declares
 EXPORTS = (
     "gqe_workspace_bytes", "gqe_workspace_layout", "gqe_route", "gqe_dispatch", "gqe_project",
-    "gqe_attention", "gqe_output", "gqe_forward", "gqe_forward_noalloc", "gqa_workspace_bytes",
+    "gqe_attention", "gqe_output", "gqe_forward", "gqe_forward_is_short", "gqe_forward_noalloc",
+    "gqa_workspace_bytes",
     "gqa_workspace_layout",
     "gqa_project", "gqa_attention", "gqa_output", "gqa_forward", "gqe_decode_workspace_bytes",
     "gqe_decode", "gqa_decode_workspace_bytes", "gqa_decode", "gqe_backward_workspace_bytes",
@@ -74,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_output": (ctypes.c_int, [cfgp, vp, vp, vp, sz, vp]),
         "gqe_forward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "gqe_forward_noalloc": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "gqe_forward_is_short": (ctypes.c_int, [cfgp]),
         "gqa_project": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, sz, vp]),
         "gqa_attention": (ctypes.c_int, [cfgp, vp, sz, vp]),
         "gqa_output": (ctypes.c_int, [cfgp, vp, vp, vp, sz, vp]),
@@ -208,6 +210,13 @@ def gqe_forward(cfg, x, wq, wk, wv, wr, wo, out, ws, stream=None):
     _check(_lib.gqe_forward(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wr),
                             _ptr(wo), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
            "gqe_forward")
+
+
+def uses_short_forward(cfg) -> bool:
+    """Whether gqe_forward takes the short-layer launches for cfg."""
+    r = _lib.gqe_forward_is_short(ctypes.byref(cfg))
+    _check(min(r, 0), "gqe_forward_is_short")
+    return r == 1
 
 
 # size of the library-owned workspace of gqe_forward_noalloc (include/gqe.h)

@@ -230,3 +230,20 @@ def test_status_strings(gqe):
     for st, name in ((0, "GQE_OK"), (-1, "GQE_ERR_INVALID_ARG"), (-2, "GQE_ERR_UNSUPPORTED"),
                      (-3, "GQE_ERR_WORKSPACE"), (-4, "GQE_ERR_HIP"), (-5, "GQE_ERR_DEBUG")):
         assert gqe.status_string(st).startswith(name)
+
+
+def test_short_forward_predicate(gqe):
+    """gqe_forward takes the short-layer launches for bf16 layers of at most
+    8192 tokens (each sequence at most 8192) with k_g <= 4 and d_model a
+    multiple of 128; fp32 layers and longer ones take the staged sequence."""
+    for kw, want in (({"seq_len": 8192}, True), ({"seq_len": 8193}, False),
+                     ({"batch": 2, "seq_len": 4096}, True), ({"batch": 3, "seq_len": 4096}, False),
+                     ({"seq_len": 2048, "dtype": "fp32"}, False),
+                     ({"seq_len": 2048, "d_model": 1088}, False),
+                     ({"seq_len": 2048, "group_top_k": [1, 2, 3, 2]}, True),
+                     ({"seq_len": 2048, "n_experts": 8, "top_k": 5}, False)):
+        assert gqe.uses_short_forward(_cfg(gqe, **kw)) == want, kw
+    # the short forward's workspace also holds the all-heads projection
+    assert gqe.gqe_workspace_bytes(_cfg(gqe, seq_len=8192)) > \
+        gqe.gqe_workspace_bytes(_cfg(gqe, seq_len=8192, dtype="fp32")) // 2
+
