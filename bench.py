@@ -473,7 +473,8 @@ def measure_ablation(gqe, torch, steps, warmup, name="b4_l8k"):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.txt")
-KERNEL_SOURCES = ("attention.hip", "attention.h", "device_common.h")
+KERNEL_SOURCES = ("attention.hip", "attention.h", "device_common.h", "dispatch_dev.h", "kernels.h",
+                  "debug_check.h")
 
 
 def kernel_source_hash():

@@ -314,7 +314,7 @@ int project_impl(const gqe_config* c, const void* x, const void* wq, const void*
 // them into q)
 template <typename T>
 int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream,
-                   bool gather = false) {
+                   bool gather = false, const DispatchArgs* lists = nullptr) {
   const Layout l = make_layout(c, dense);
   const int G = c->n_groups, E = c->n_experts, D = c->head_dim;
   AttnParams p{};
@@ -354,14 +354,14 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
     if (c->output_mode == GQE_OUTPUT_WEIGHTED_CONCAT) p.row_scale = at<float>(ws, l.pub.w);
   }
   p.scale_log2 = scale_log2(c);
-  return hip_status(launch_attention<T>(p, D, stream));
+  return hip_status(launch_attention<T>(p, D, stream, lists));
 }
 
 // Short bf16 layers in four launches: (1) the router's blocks beside one
 // dense projection of every expert's query head, the shared head, K and V^T
-// (nothing there waits for the routing); (2) the attention, whose slot-heads
-// read their query rows through the routing indices; (3) the dispatch lists
-// beside the weighted slot; (4) W_O.  Every routed query is projected, G*E
+// (nothing there waits for the routing); (2) the dispatch lists' blocks
+// beside the attention, whose slot-heads read their query rows through the
+// routing indices; (3) the weighted slot; (4) W_O.  Every routed query is projected, G*E
 // heads instead of the k*G selected (about half again the projection's
 // work), which these lengths absorb: their kernels are bound by latency, and
 // the router and the dispatch leave the critical path.  The workspace ends up
@@ -412,8 +412,6 @@ int forward_short(const gqe_config* c, const void* x, const void* wq, const void
   hipError_t e = launch_front(r, static_cast<const T*>(x), B * L, c->d_model, L, D,
                               l.pub.vt_tiles, seg, 3, make_rope(c), stream);
   if (e != hipSuccess) return GQE_ERR_HIP;
-  int st = attention_impl<T>(c, ws, false, stream, true);
-  if (st != GQE_OK) return st;
   DispatchArgs da;
   da.idx = at<int32_t>(ws, l.pub.idx);
   da.counts = at<int32_t>(ws, l.pub.counts);
@@ -429,9 +427,13 @@ int forward_short(const gqe_config* c, const void* x, const void* wq, const void
   da.n_lists = B * G * E;
   da.blocks = B * G;
   da.dbg = debug_word_of(stream);
-  e = launch_slot_dispatch<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), shared ? B * L : 0,
-                              total_k(c), D, da, stream);
-  if (e != hipSuccess) return GQE_ERR_HIP;
+  const int st = attention_impl<T>(c, ws, false, stream, true, &da);
+  if (st != GQE_OK) return st;
+  if (shared) {
+    e = launch_weighted_slot<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), B * L, total_k(c), D,
+                                stream);
+    if (e != hipSuccess) return GQE_ERR_HIP;
+  }
   e = launch_out_proj<T>(at<T>(ws, l.pub.s), static_cast<const T*>(wo), static_cast<T*>(out),
                          B * L, c->d_model, slot_count(c) * D, stream);
   return debug_collect(stream, hip_status(e));

@@ -1,7 +1,8 @@
 // The causal attention step's launch interface (host side): the parameter
-// block the attention kernels read and their launcher.  Kept apart from the
-// other launchers so that the attention kernel's sources are exactly
-// attention.hip, this header and device_common.h.
+// block the attention kernels read and their launcher.  The attention
+// kernel's sources are attention.hip, this header, device_common.h, and the
+// headers of the dispatch blocks that can ride in its launch
+// (dispatch_dev.h, kernels.h, debug_check.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,7 +49,11 @@ struct AttnParams {
 inline long long attention_redo_ints(int B, int H, int L) {
   return static_cast<long long>(B) * H * ((L + 31) / 32);
 }
+// lists: optional (NULL for none): the short forward's dispatch blocks
+// (kernels.h, DispatchArgs), run as the launch's first blocks
+struct DispatchArgs;
 template <typename T>
-hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream);
+hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream,
+                            const DispatchArgs* lists = nullptr);
 
 }  // namespace gqe

@@ -42,6 +42,8 @@
 
 #include "attention.h"
 #include "device_common.h"
+#include "dispatch_dev.h"
+#include "kernels.h"
 
 namespace gqe {
 
@@ -144,15 +146,30 @@ __device__ __forceinline__ float dot8(const f32x8& a, const f32x8& b) {
 // split keeps the fallback's registers out of the fast path's allocation.
 enum { kInline = 0, kFastOnly = 1, kFallbackOnly = 2 };
 
+// lists: the short forward's dispatch (one block per (b, g), lists.blocks of
+// them) runs as the launch's first blocks, in the K/V stages' LDS; the
+// attention's blocks follow.  Only the first launch of a split pair takes it.
 template <typename T, int D, int QB, int QW, int NS, int MODE>
 __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) void attention_kernel(
-    AttnParams p) {
+    AttnParams p, DispatchArgs lists) {
   typedef AttnShape<T, D, QB, QW, NS> S;
+  extern __shared__ __align__(16) char smem[];
+  int bid = blockIdx.x;
+  if constexpr (MODE != kFallbackOnly) {
+    constexpr int W = S::THREADS / 64;  // (the launch sizes the LDS for these blocks too)
+    if (bid < lists.blocks) {
+      dispatch_small_block<W>(bid, *reinterpret_cast<DispatchSmem<W>*>(smem), lists.idx,
+                              lists.counts, lists.offsets, lists.tile_off, lists.pos, lists.slot,
+                              lists.L, lists.G, lists.E, lists.gk, lists.tile_rows, lists.n_lists,
+                              lists.dbg);
+      return;
+    }
+    bid -= lists.blocks;
+  }
   if constexpr (MODE == kFallbackOnly) {
-    if (p.redo[blockIdx.x] == 0) return;  // the fast path's result stands
+    if (p.redo[bid] == 0) return;  // the fast path's result stands
   }
   typedef typename Frag<T>::type F;
-  extern __shared__ __align__(16) char smem[];
 
   const int lane = threadIdx.x & 63, half = lane >> 5;
   const int grp = NS == 1 ? 0 : (threadIdx.x >> 6) / QW;  // key group
@@ -162,8 +179,8 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
   const int L = p.L;
   const int nq = (L + S::BQ - 1) / S::BQ;
   const int bh_count = p.B * p.H;
-  const int qi = blockIdx.x / bh_count;
-  const int bh = blockIdx.x % bh_count;
+  const int qi = bid / bh_count;
+  const int bh = bid % bh_count;
   const int qblk = nq - 1 - qi;  // heaviest first
   const int b = bh / p.H, head = bh % p.H;
   int g = p.extra_group;
@@ -428,7 +445,7 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
     }
     const int redo = __syncthreads_or(ok ? 0 : 1);
     if constexpr (MODE == kFastOnly) {
-      if (threadIdx.x == 0) p.redo[blockIdx.x] = redo;
+      if (threadIdx.x == 0) p.redo[bid] = redo;
       if (redo) return;
     } else if (redo) {
       reset(true);
@@ -436,7 +453,7 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
     }
   } else {
     if constexpr (MODE == kFastOnly) {
-      if (threadIdx.x == 0) p.redo[blockIdx.x] = 1;
+      if (threadIdx.x == 0) p.redo[bid] = 1;
       wait_vm(0);  // the first tile's copy lands before the block's LDS is released
       return;
     } else {
@@ -520,7 +537,8 @@ __global__ __launch_bounds__(64 * QW * NS, (QW * NS == 4 && D < 128) ? 2 : 1) vo
 }
 
 template <typename T, int D, int QB, int QW, int NS, int MODE>
-hipError_t launch_attention_mode(const AttnParams& p, long long blocks, hipStream_t stream) {
+hipError_t launch_attention_mode(const AttnParams& p, long long blocks, const DispatchArgs& lists,
+                                 hipStream_t stream) {
   typedef AttnShape<T, D, QB, QW, NS> S;
   if (S::LDS > 65536) {
     static const hipError_t attr = hipFuncSetAttribute(
@@ -528,24 +546,28 @@ hipError_t launch_attention_mode(const AttnParams& p, long long blocks, hipStrea
         hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((attention_kernel<T, D, QB, QW, NS, MODE>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(S::THREADS), S::LDS, stream, p);
+  constexpr int lists_lds = static_cast<int>(sizeof(DispatchSmem<S::THREADS / 64>));
+  const int lds = lists.blocks > 0 && lists_lds > S::LDS ? lists_lds : S::LDS;
+  hipLaunchKernelGGL((attention_kernel<T, D, QB, QW, NS, MODE>),
+                     dim3(static_cast<unsigned>(blocks + lists.blocks)), dim3(S::THREADS), lds,
+                     stream, p, lists);
   return hipGetLastError();
 }
 
 // SPLIT: the fast path and the fallback in two launches (p.redo must hold one
 // int per block); otherwise one launch with the fallback inline
 template <typename T, int D, int QB, int QW, int NS, bool SPLIT>
-hipError_t launch_attention_d(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attention_d(const AttnParams& p, const DispatchArgs& lists, hipStream_t stream) {
   typedef AttnShape<T, D, QB, QW, NS> S;
   const int nq = (p.L + S::BQ - 1) / S::BQ;
   const long long blocks = static_cast<long long>(nq) * p.B * p.H;
-  if (blocks == 0) return hipSuccess;
+  if (blocks == 0 && lists.blocks == 0) return hipSuccess;
   if (!SPLIT || p.redo == nullptr)
-    return launch_attention_mode<T, D, QB, QW, NS, kInline>(p, blocks, stream);
-  const hipError_t e = launch_attention_mode<T, D, QB, QW, NS, kFastOnly>(p, blocks, stream);
+    return launch_attention_mode<T, D, QB, QW, NS, kInline>(p, blocks, lists, stream);
+  const hipError_t e = launch_attention_mode<T, D, QB, QW, NS, kFastOnly>(p, blocks, lists, stream);
   if (e != hipSuccess) return e;
-  return launch_attention_mode<T, D, QB, QW, NS, kFallbackOnly>(p, blocks, stream);
+  DispatchArgs none{};
+  return launch_attention_mode<T, D, QB, QW, NS, kFallbackOnly>(p, blocks, none, stream);
 }
 
 }  // namespace
@@ -555,31 +577,38 @@ hipError_t launch_attention_d(const AttnParams& p, hipStream_t stream) {
 // chip, take 64-row blocks whose key range is split over NS groups of waves,
 // which shortens the causal critical path NS-fold.
 template <typename T>
-hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream) {
+hipError_t launch_attention(const AttnParams& p, int D, hipStream_t stream,
+                            const DispatchArgs* lists_in) {
+  DispatchArgs none{};
+  const DispatchArgs& lists = lists_in != nullptr ? *lists_in : none;
+  if (lists.blocks > 0 && (lists.L > kDispatchSmallMaxL || lists.gk.kmax > 4))
+    return hipErrorInvalidValue;
   const bool wide = static_cast<long long>(p.L) * p.B * p.H >= 256LL * 256 * 4;
   if constexpr (sizeof(T) == 2) {
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1, true>(p, stream)
-                           : launch_attention_d<T, 32, 1, 2, 4, false>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1, true>(p, stream)
-                           : launch_attention_d<T, 64, 1, 2, 4, false>(p, stream);
-      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1, true>(p, stream)
-                            : launch_attention_d<T, 128, 1, 2, 2, false>(p, stream);
+      case 32: return wide ? launch_attention_d<T, 32, 2, 4, 1, true>(p, lists, stream)
+                           : launch_attention_d<T, 32, 1, 2, 4, false>(p, lists, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 2, 4, 1, true>(p, lists, stream)
+                           : launch_attention_d<T, 64, 1, 2, 4, false>(p, lists, stream);
+      case 128: return wide ? launch_attention_d<T, 128, 1, 4, 1, true>(p, lists, stream)
+                            : launch_attention_d<T, 128, 1, 2, 2, false>(p, lists, stream);
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (D) {
-      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1, false>(p, stream)
-                           : launch_attention_d<T, 32, 1, 2, 4, false>(p, stream);
-      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1, false>(p, stream)
-                           : launch_attention_d<T, 64, 1, 2, 2, false>(p, stream);
-      case 128: return launch_attention_d<T, 128, 1, 4, 1, false>(p, stream);
+      case 32: return wide ? launch_attention_d<T, 32, 1, 4, 1, false>(p, lists, stream)
+                           : launch_attention_d<T, 32, 1, 2, 4, false>(p, lists, stream);
+      case 64: return wide ? launch_attention_d<T, 64, 1, 4, 1, false>(p, lists, stream)
+                           : launch_attention_d<T, 64, 1, 2, 2, false>(p, lists, stream);
+      case 128: return launch_attention_d<T, 128, 1, 4, 1, false>(p, lists, stream);
       default: return hipErrorInvalidValue;
     }
   }
 }
 
-template hipError_t launch_attention<bf16_t>(const AttnParams&, int, hipStream_t);
-template hipError_t launch_attention<float>(const AttnParams&, int, hipStream_t);
+template hipError_t launch_attention<bf16_t>(const AttnParams&, int, hipStream_t,
+                                             const DispatchArgs*);
+template hipError_t launch_attention<float>(const AttnParams&, int, hipStream_t,
+                                            const DispatchArgs*);
 
 }  // namespace gqe

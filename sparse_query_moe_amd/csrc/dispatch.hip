@@ -34,8 +34,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_off, int32_t* __restrict__ pos, int32_t* __restrict__ slot, int L,
     int G, int E, GroupK gk, int tile_rows, int n_lists, uint32_t* dbg) {
-  dispatch_small_block(blockIdx.x, idx, counts, offsets, tile_off, pos, slot, L, G, E, gk,
-                       tile_rows, n_lists, dbg);
+  __shared__ DispatchSmem<kSmallWaves> sm;
+  dispatch_small_block<kSmallWaves>(blockIdx.x, sm, idx, counts, offsets, tile_off, pos, slot, L,
+                                    G, E, gk, tile_rows, n_lists, dbg);
 }
 
 // ---------------------------------------------------------------------------

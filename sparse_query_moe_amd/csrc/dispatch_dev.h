@@ -14,9 +14,7 @@ namespace gqe {
 
 namespace {
 
-constexpr int kSmallWaves = 16;   // waves of the one-block-per-(b, g) path
-constexpr int kSmallRounds = 8;   // 1024-token rounds it covers: L <= 8192
-static_assert(kSmallRounds * 64 * kSmallWaves == kDispatchSmallMaxL, "the short path covers L <= 8192");
+constexpr int kSmallWaves = 16;   // waves of the one-block-per-(b, g) kernel
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
@@ -85,20 +83,34 @@ __device__ __forceinline__ void finish_lists(const int* cnt, int32_t* counts, in
 }
 
 // ---------------------------------------------------------------------------
-// short sequences: one block per (b, g).  Thread (wave w, lane) owns tokens
-// t = r*1024 + 64*w + lane for rounds r < kSmallRounds; all their expert ids
+// short sequences: one block per (b, g) of W waves.  Thread (wave w, lane)
+// owns tokens t = r*64*W + 64*w + lane for rounds r < 128/W; all their expert ids
 // are loaded at once.  Pass 1 ballots every (round, wave, expert) count into
 // LDS; one prefix over (expert, round, wave) gives every wave its list bases;
 // pass 2 scatters.  Three barriers in all.
 // ---------------------------------------------------------------------------
+// LDS of one block of W waves (R rounds of 64*W tokens cover 8192): a static
+// array of the dispatch kernel, or the start of the attention launch's
+// dynamic LDS when the short forward's lists ride in that launch
+template <int W>
+struct DispatchSmem {
+  static constexpr int R = 128 / W;
+  static_assert(R * W == 128 && R * 64 * W == kDispatchSmallMaxL, "rounds cover L <= 8192");
+  int wcnt[R][W][32];  // count, then offset in the list, per (round, wave, expert)
+  int total[32];
+  int start[32];
+};
+
+template <int W>
 __device__ __forceinline__ void dispatch_small_block(
-    int bg, const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
+    int bg, DispatchSmem<W>& sm, const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int32_t* __restrict__ pos,
     int32_t* __restrict__ slot, int L, int G, int E, const GroupK& gk, int tile_rows, int n_lists,
     uint32_t* dbg) {
-  __shared__ int wcnt[kSmallRounds][kSmallWaves][32];  // count, then offset in the list, per (r, w, e)
-  __shared__ int total[32];
-  __shared__ int start[32];
+  constexpr int kSmallWaves = W, kSmallRounds = DispatchSmem<W>::R;
+  auto& wcnt = sm.wcnt;
+  auto& total = sm.total;
+  auto& start = sm.start;
   const int b = bg / G, g = bg % G;
   const int k = gk.kg[g];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;

@@ -32,7 +32,6 @@
 #include "device_common.h"
 
 #include "kernels.h"
-#include "dispatch_dev.h"
 #include "router_dev.h"
 
 namespace gqe {
@@ -693,24 +692,6 @@ __global__ __launch_bounds__(256) void weighted_slot_kernel(T* __restrict__ s,
                         n_tokens, K, D);
 }
 
-// short sequences: the dispatch's blocks (one per (b, g)) beside the weighted
-// slot's, in one launch of 1024-thread blocks.  The short forward's
-// projection and attention read the routing indices directly, so nothing in
-// it waits for the lists: they are built here, off the critical path.
-template <typename T>
-__global__ __launch_bounds__(1024) void slot_dispatch_kernel(T* __restrict__ s,
-                                                             const float* __restrict__ w,
-                                                             int n_tokens, int K, int D,
-                                                             DispatchArgs da) {
-  if (static_cast<int>(blockIdx.x) < da.blocks) {
-    dispatch_small_block(blockIdx.x, da.idx, da.counts, da.offsets, da.tile_off, da.pos, da.slot,
-                         da.L, da.G, da.E, da.gk, da.tile_rows, da.n_lists, da.dbg);
-    return;
-  }
-  weighted_slot_item<T>(static_cast<size_t>(blockIdx.x - da.blocks) * 1024 + threadIdx.x, s, w,
-                        n_tokens, K, D);
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1049,18 +1030,6 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_slot_dispatch(T* s, const float* w, int n_tokens, int K, int D,
-                                const DispatchArgs& da, hipStream_t stream) {
-  if (da.L > kDispatchSmallMaxL || da.gk.kmax > 4) return hipErrorInvalidValue;
-  const long long items = static_cast<long long>(n_tokens) * (D / 4);
-  const long long blocks = da.blocks + (items + 1023) / 1024;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(slot_dispatch_kernel<T>, dim3(static_cast<unsigned>(blocks)), dim3(1024), 0,
-                     stream, s, w, n_tokens, K, D, da);
-  return hipGetLastError();
-}
-
 #define GQE_INST(T)                                                                              \
   template hipError_t launch_dense_proj<T>(const T*, int, int, int, int, int64_t, const ProjSeg*, \
                                            int, const RopeTable&, hipStream_t);                  \
@@ -1071,8 +1040,6 @@ hipError_t launch_slot_dispatch(T* s, const float* w, int n_tokens, int K, int D
                                         hipStream_t);                                            \
   template hipError_t launch_out_proj<T>(const T*, const T*, T*, int, int, int, hipStream_t);    \
   template hipError_t launch_weighted_slot<T>(T*, const float*, int, int, int, hipStream_t);      \
-  template hipError_t launch_slot_dispatch<T>(T*, const float*, int, int, int,                   \
-                                              const DispatchArgs&, hipStream_t);                 \
   template hipError_t launch_nt_gemm<T>(const NtArgs&, hipStream_t);
 GQE_INST(bf16_t)
 GQE_INST(float)

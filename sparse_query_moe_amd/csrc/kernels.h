@@ -38,6 +38,18 @@ hipError_t launch_router(const T* x, const T* wr, const float* bias, int32_t* id
                          hipStream_t stream);
 
 // ---- K2 dispatch -------------------------------------------------------------
+// Sequences of at most kDispatchSmallMaxL tokens with every k_g <= 4 are
+// dispatched by one block per (b, g).  DispatchArgs carries those blocks into
+// another launch (the short forward's attention): `blocks` = B*G of them.
+constexpr int kDispatchSmallMaxL = 8192;
+struct DispatchArgs {
+  const int32_t* idx;
+  int32_t *counts, *offsets, *tile_off, *pos, *slot;
+  int L, G, E;
+  GroupK gk;
+  int tile_rows, n_lists, blocks;
+  uint32_t* dbg;
+};
 int dispatch_chunks(int L);
 // dbg: the debug word of a debug build's expert-id checks (see launch_project)
 hipError_t launch_dispatch(const int32_t* idx, int32_t* chunk_counts, int32_t* counts,
@@ -107,21 +119,7 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
 template <typename T>
 hipError_t launch_out_proj(const T* a, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream);
-// Sequences of at most kDispatchSmallMaxL tokens with k_g <= 4: the dispatch
-// (as launch_dispatch, blocks = B*G, one per (b, g)) and the weighted slot
-// (as launch_weighted_slot; n_tokens = 0 for none) in one launch.
-constexpr int kDispatchSmallMaxL = 8192;
-struct DispatchArgs {
-  const int32_t* idx;
-  int32_t *counts, *offsets, *tile_off, *pos, *slot;
-  int L, G, E;
-  GroupK gk;
-  int tile_rows, n_lists, blocks;
-  uint32_t* dbg;
-};
-template <typename T>
-hipError_t launch_slot_dispatch(T* s, const float* w, int n_tokens, int K, int D,
-                                const DispatchArgs& da, hipStream_t stream);
+
 
 // ---- backward: C[M, N] = A[M, K] . B[N, K]^T in float32 ------------------------
 // Rows of C go to up to four segments: row m in [row_begin, row_begin + rows)
