@@ -232,8 +232,8 @@ int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void
                 void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* 1 when gqe_forward takes the short-layer launches for `cfg`: bf16 storage,
- * d_model a multiple of 128, G*E <= 64, at most 8192 tokens (batch * seq_len),
- * seq_len <= 8192 and every k_g <= 4; 0 otherwise; a negative status for an
+ * d_model a multiple of 128, G*E <= 64, at most 4096 tokens (batch * seq_len)
+ * and every k_g <= 4; 0 otherwise; a negative status for an
  * invalid cfg.  Host only: launches nothing. */
 int gqe_forward_is_short(const gqe_config* cfg);
 

@@ -234,16 +234,16 @@ def test_status_strings(gqe):
 
 def test_short_forward_predicate(gqe):
     """gqe_forward takes the short-layer launches for bf16 layers of at most
-    8192 tokens (each sequence at most 8192) with k_g <= 4 and d_model a
-    multiple of 128; fp32 layers and longer ones take the staged sequence."""
-    for kw, want in (({"seq_len": 8192}, True), ({"seq_len": 8193}, False),
-                     ({"batch": 2, "seq_len": 4096}, True), ({"batch": 3, "seq_len": 4096}, False),
+    4096 tokens with k_g <= 4 and d_model a multiple of 128; fp32 layers and
+    longer ones take the staged sequence."""
+    for kw, want in (({"seq_len": 4096}, True), ({"seq_len": 4097}, False),
+                     ({"batch": 2, "seq_len": 2048}, True), ({"batch": 3, "seq_len": 2048}, False),
                      ({"seq_len": 2048, "dtype": "fp32"}, False),
                      ({"seq_len": 2048, "d_model": 1088}, False),
                      ({"seq_len": 2048, "group_top_k": [1, 2, 3, 2]}, True),
                      ({"seq_len": 2048, "n_experts": 8, "top_k": 5}, False)):
         assert gqe.uses_short_forward(_cfg(gqe, **kw)) == want, kw
     # the short forward's workspace also holds the all-heads projection
-    assert gqe.gqe_workspace_bytes(_cfg(gqe, seq_len=8192)) > \
-        gqe.gqe_workspace_bytes(_cfg(gqe, seq_len=8192, dtype="fp32")) // 2
+    assert gqe.gqe_workspace_bytes(_cfg(gqe, seq_len=4096)) > \
+        gqe.gqe_workspace_bytes(_cfg(gqe, seq_len=4096, dtype="fp32")) // 2
 

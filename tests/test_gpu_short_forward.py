@@ -1,7 +1,7 @@
 """The short-sequence forward against the staged calls, bit for bit (needs an
 MI355X).
 
-bf16 layers of up to 8192 tokens run gqe_forward as one front launch (the
+bf16 layers of up to 4096 tokens run gqe_forward as one front launch (the
 router beside a dense projection of every expert's query head), the attention
 reading each slot-head's query row through the routing indices, the dispatch
 beside the weighted slot, and W_O.  Longer layers, and the stage entry points,
@@ -32,7 +32,7 @@ def gqe():
 CASES = [  # (name, L, B, config keywords)
     ("l2k", 0, 0, {}),
     ("l2k", 600, 2, {}),
-    ("l2k", 8192, 1, {}),
+    ("l2k", 4096, 1, {}),
     ("l2k", 1000, 3, {"rope_base": 10000.0}),
     ("l2k", 777, 1, {"output_mode": "hard"}),
     ("l2k", 777, 1, {"output_mode": "weighted_concat"}),
