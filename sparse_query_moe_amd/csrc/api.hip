@@ -368,6 +368,10 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
 // work), which these lengths absorb: their kernels are bound by latency, and
 // the router and the dispatch leave the critical path.  The workspace ends up
 // as after the staged calls: the same idx, w, lists, q, K, V^T, s and lse.
+template <typename T>
+int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool dense,
+                hipStream_t stream);
+
 int forward_short(const gqe_config* c, const void* x, const void* wq, const void* wk,
                   const void* wv, const void* wr, const void* wo, void* out, void* ws,
                   hipStream_t stream) {
@@ -431,14 +435,7 @@ int forward_short(const gqe_config* c, const void* x, const void* wq, const void
   da.dbg = debug_word_of(stream);
   const int st = attention_impl<T>(c, ws, false, stream, true, &da);
   if (st != GQE_OK) return st;
-  if (shared) {
-    e = launch_weighted_slot<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), B * L, total_k(c), D,
-                                stream);
-    if (e != hipSuccess) return GQE_ERR_HIP;
-  }
-  e = launch_out_proj<T>(at<T>(ws, l.pub.s), static_cast<const T*>(wo), static_cast<T*>(out),
-                         B * L, c->d_model, slot_count(c) * D, stream);
-  return debug_collect(stream, hip_status(e));
+  return debug_collect(stream, output_impl<T>(c, wo, out, ws, false, stream));
 }
 
 template <typename T>
@@ -450,12 +447,16 @@ int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool d
   hipError_t e = hipSuccess;
   int K;
   if (!dense) {
+    K = slot_count(c) * D;
+    if (full_output(c) && sizeof(T) == 2 && out_wslot_ok(K, D, total_k(c)))  // one launch
+      return hip_status(launch_out_proj_wslot(
+          at<bf16_t>(ws, l.pub.s), at<float>(ws, l.pub.w), static_cast<const bf16_t*>(wo),
+          static_cast<bf16_t*>(out), M, c->d_model, K, D, total_k(c), stream));
     if (full_output(c)) {
       e = launch_weighted_slot<T>(at<T>(ws, l.pub.s), at<float>(ws, l.pub.w), M, total_k(c), D,
                                   stream);
       if (e != hipSuccess) return GQE_ERR_HIP;
     }
-    K = slot_count(c) * D;
   } else {
     K = G * E * D;
   }

@@ -51,6 +51,13 @@ template <class P, class = void> struct HasRotate : std::false_type {};
 template <class P>
 struct HasRotate<P, std::void_t<decltype(std::declval<const P&>().rotate(0, 0, 0.f, 0.f))>>
     : std::true_type {};
+// A problem that defines wslot_k() may form its last K step's A tile in the
+// main loop (the output projection's weighted slot, below): wslot_k() hard
+// slots of one K step each, then the shared slot, then the weighted slot.
+template <class P, class = void> struct HasWslot : std::false_type {};
+template <class P>
+struct HasWslot<P, std::void_t<decltype(std::declval<const P&>().wslot_k())>> : std::true_type {};
+constexpr int kWslotMaxK = 32;  // hard slots the in-loop weighted slot takes
 
 template <typename T, int BM_, int BN_, int WGM_, int WGN_, int NST_ = 2>
 struct GemmShape {
@@ -109,11 +116,39 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
 
   const int nk = prob.K / S::BKE;
   constexpr int per_stage = S::A_CH + S::B_CH;
+  // The in-loop weighted slot (bf16, one K step per slot): every thread sums
+  // w[row, h] * A[row, chunk] over the hard-slot steps h < wk for the 16-byte
+  // chunks it copies itself, in slot order (the weighted-slot kernel's
+  // arithmetic), and at the shared step writes the bf16 sums where its copy
+  // of the last step's A chunk would land.  The routing weights of the tile's
+  // rows come to LDS after the ring, copied before the first stage.
+  constexpr bool WSL = HasWslot<P>::value && sizeof(T) == 2;
+  int wk = 0;
+  float wacc[WSL ? S::A_CH : 1][8];
+  if constexpr (WSL) {
+    wk = prob.wslot_k();
+    if (wk > 0) {
+#pragma unroll
+      for (int i = 0; i < S::A_CH; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wacc[i][j] = 0.f;
+      // [BM, wk] floats, 16 bytes per lane, runs of 1 KB over the 4 waves
+      const char* src = reinterpret_cast<const char*>(prob.wslot_rows());
+      const int valid = prob.wslot_valid_rows() * wk * 4;  // bytes inside w
+      char* dst = smem + S::NST * S::STAGE;
+      const int runs = (S::BM * wk * 4 + 1023) / 1024;
+      for (int rr = swave; rr < runs; rr += 4) {
+        const int off = rr * 1024 + 16 * lane;
+        dma16(src + (off + 16 <= valid ? off : 0), dst + rr * 1024);
+      }
+    }
+  }
   auto issue = [&](int kt) {
     char* st = smem + (kt % S::NST) * S::STAGE;
+    const bool own_a = WSL && wk > 0 && kt == nk - 1;  // the weighted slot's A is formed here
 #pragma unroll
     for (int i = 0; i < S::A_CH; ++i)
-      dma16(ap[i] + kt * S::BKE, st + (4 * i + swave) * 1024);
+      if (!own_a) dma16(ap[i] + kt * S::BKE, st + (4 * i + swave) * 1024);
 #pragma unroll
     for (int i = 0; i < S::B_CH; ++i)
       dma16(bp[i] + kt * S::BKE, st + S::BM * 128 + (4 * i + swave) * 1024);
@@ -136,12 +171,37 @@ __device__ __forceinline__ void gemm_block(const P& prob, char* smem) {
     if (st < nk) issue(st);
   for (int kt = 0; kt < nk; ++kt) {
     const int later = min(S::NST - 2, nk - 1 - kt);  // stages issued after kt
-    wait_vm(later * per_stage);
+    // (the last stage copies no A when the weighted slot is formed)
+    const bool last_later = WSL && wk > 0 && later > 0 && kt + later == nk - 1;
+    wait_vm(later * per_stage - (last_later ? S::A_CH : 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (kt + S::NST - 1 < nk) issue(kt + S::NST - 1);
     const char* sa = smem + (kt % S::NST) * S::STAGE;
     const char* sb = sa + S::BM * 128;
+    if constexpr (WSL) {
+      if (wk > 0 && kt < wk) {  // hard slot kt: accumulate this thread's chunks
+        const float* wt = reinterpret_cast<const float*>(smem + S::NST * S::STAGE);
+#pragma unroll
+        for (int i = 0; i < S::A_CH; ++i) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sa + (4 * i + swave) * 1024 + 16 * lane);
+          const float wv = wt[(r0 + 32 * i) * wk + kt];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) wacc[i][j] = fmaf(wv, static_cast<float>(v[j]), wacc[i][j]);
+        }
+      } else if (wk > 0 && kt == wk) {  // the shared step: the weighted slot's A chunks
+        char* sw = smem + ((nk - 1) % S::NST) * S::STAGE;
+#pragma unroll
+        for (int i = 0; i < S::A_CH; ++i) {
+          bf16x8 o;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[j] = static_cast<__bf16>(wacc[i][j]);
+          *reinterpret_cast<bf16x8*>(sw + (4 * i + swave) * 1024 + 16 * lane) = o;
+          const int r = r0 + 32 * i;
+          prob.wslot_store(r, pc ^ ((r >> 1) & 7), o);
+        }
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int e = ks * 16 + 8 * (lane >> 5);
@@ -549,6 +609,10 @@ struct OutArgs {
   const void* w;
   void* out;
   int M, N, K;
+  // the weighted slot formed in the main loop (bf16, d_h 64), or NULL: the
+  // router weights [M, wslot_k] and the slot buffer (a) it is also stored to
+  const float* wslot_w;
+  int wslot_k;
 };
 
 template <typename T, class S>
@@ -583,6 +647,40 @@ __global__ __launch_bounds__(256) void out_proj_kernel(OutArgs args) {
   int rt, ct;
   xcd_tile(rt, ct);
   OutProb<T, S> prob(args, rt * S::BM, ct * S::BN);
+  gemm_block<T, S>(prob, smem);
+}
+
+// The output projection with the weighted slot formed in its main loop (bf16,
+// d_h 64: slot h is K step h).  The slot's A chunks never come from HBM: the
+// weighted-slot kernel's pass over the hard slots is folded into the K steps
+// that stream them anyway.  The first column tile also stores the slot into
+// the slot buffer, so the workspace holds what the separate kernel writes.
+template <typename T, class S>
+struct OutWsProb : OutProb<T, S> {
+  typedef OutProb<T, S> Base;
+  __device__ OutWsProb(const OutArgs& args, int m0_, int n0_) : Base(args, m0_, n0_) {}
+  // hard slots; the tile's weight rows and how many of them exist
+  __device__ __forceinline__ int wslot_k() const { return this->a.wslot_k; }
+  __device__ __forceinline__ const float* wslot_rows() const {
+    return this->a.wslot_w + static_cast<size_t>(this->m0) * this->a.wslot_k;
+  }
+  __device__ __forceinline__ int wslot_valid_rows() const { return min(S::BM, this->a.M - this->m0); }
+  // one 8-element chunk of tile row r's weighted slot
+  __device__ __forceinline__ void wslot_store(int r, int chunk, const bf16x8& v) const {
+    const int m = this->m0 + r;
+    if (this->n0 != 0 || m >= this->a.M) return;
+    *reinterpret_cast<bf16x8*>(static_cast<bf16_t*>(const_cast<void*>(this->a.a)) +
+                               static_cast<size_t>(m) * this->a.K + (this->a.wslot_k + 1) * 64 +
+                               8 * chunk) = v;
+  }
+};
+
+template <typename T, class S>
+__global__ __launch_bounds__(256) void out_wslot_kernel(OutArgs args) {
+  extern __shared__ __align__(16) char smem[];
+  int rt, ct;
+  xcd_tile(rt, ct);
+  OutWsProb<T, S> prob(args, rt * S::BM, ct * S::BN);
   gemm_block<T, S>(prob, smem);
 }
 
@@ -958,7 +1056,7 @@ hipError_t launch_front(const RouterArgs& r, const bf16_t* x, int M, int K, int 
 template <typename T>
 hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream) {
-  OutArgs a;
+  OutArgs a{};
   a.a = a_;
   a.w = wo;
   a.out = out;
@@ -967,6 +1065,46 @@ hipError_t launch_out_proj(const T* a_, const T* wo, T* out, int M, int N, int K
   a.K = K;
   if (M == 0 || N == 0) return hipSuccess;
   GQE_LAUNCH_TILED(out_proj_kernel, T, M, N, stream, a);
+}
+
+// dynamic LDS of the in-loop weighted slot: the ring, then the weight rows
+template <class S>
+static hipError_t launch_out_wslot_s(const OutArgs& a, hipStream_t stream) {
+  constexpr int ring = S::NST * S::STAGE;
+  constexpr int cap = ring + S::BM * kWslotMaxK * 4 > S::LDS ? ring + S::BM * kWslotMaxK * 4 : S::LDS;
+  const int need = ring + S::BM * a.wslot_k * 4;
+  const int lds = need > S::LDS ? need : S::LDS;
+  auto kern = out_wslot_kernel<bf16_t, S>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, tile_grid(choose_tiles(a.M, a.N), a.M, a.N), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+bool out_wslot_ok(int K, int D, int hard) {
+  return D == 64 && hard > 0 && hard <= kWslotMaxK && hard % 4 == 0 && K == (hard + 2) * D;
+}
+
+hipError_t launch_out_proj_wslot(bf16_t* s, const float* w, const bf16_t* wo, bf16_t* out, int M,
+                                 int N, int K, int D, int hard, hipStream_t stream) {
+  if (!out_wslot_ok(K, D, hard)) return hipErrorInvalidValue;
+  OutArgs a{};
+  a.a = s;
+  a.w = wo;
+  a.out = out;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.wslot_w = w;
+  a.wslot_k = hard;
+  if (M == 0 || N == 0) return hipSuccess;
+  switch (choose_tiles(M, N)) {
+    case Tiles::k64: return launch_out_wslot_s<GemmShape<bf16_t, 64, 128, 2, 2>>(a, stream);
+    case Tiles::k64Deep: return launch_out_wslot_s<GemmShape<bf16_t, 64, 128, 2, 2, 4>>(a, stream);
+    case Tiles::k128Deep: return launch_out_wslot_s<GemmShape<bf16_t, 128, 128, 2, 2, 4>>(a, stream);
+    default: return launch_out_wslot_s<GemmShape<bf16_t, 128, 128, 2, 2>>(a, stream);
+  }
 }
 
 // The split count s minimizes the rounds of blocks over the compute units per

@@ -119,6 +119,16 @@ hipError_t launch_weighted_slot(T* s, const float* w, int n_tokens, int K, int D
 template <typename T>
 hipError_t launch_out_proj(const T* a, const T* wo, T* out, int M, int N, int K,
                            hipStream_t stream);
+// The weighted slot and the output projection in one launch (bf16, d_h 64,
+// `hard` slots, a multiple of 4 and at most 32, then the shared and the
+// weighted slot: K = (hard + 2) * 64): the weighted slot is formed from the
+// hard slots inside the GEMM's main loop, stored into s (its slot of every
+// token), and multiplied with its W_O columns.  out_wslot_ok tells whether a
+// shape qualifies; the results equal launch_weighted_slot then
+// launch_out_proj bit for bit.
+bool out_wslot_ok(int K, int D, int hard);
+hipError_t launch_out_proj_wslot(bf16_t* s, const float* w, const bf16_t* wo, bf16_t* out, int M,
+                                 int N, int K, int D, int hard, hipStream_t stream);
 
 
 // ---- backward: C[M, N] = A[M, K] . B[N, K]^T in float32 ------------------------

@@ -84,3 +84,40 @@ def test_short_forward_equals_staged(gqe, name, L, B, kw):
     if gk is None:
         assert int(v1["counts"].sum()) == wl.batch * wl.seq_len * wl.n_groups * wl.top_k
 
+
+
+@pytest.mark.parametrize("name,L,B", [("l2k", 0, 0), ("l2k", 600, 2), ("b4_l8k", 0, 0)])
+def test_output_forms_the_weighted_slot_in_its_main_loop(gqe, name, L, B):
+    """bf16 layers with d_h 64 form the weighted slot inside the W_O GEMM: the
+    slot it stores is sum_h w_h * s_h (float32 in slot order, rounded to bf16:
+    within one bf16 step of the float64 sum), and the output is bit for bit
+    the plain output GEMM (the dense baseline's, of the same width) over the
+    slot vector as stored."""
+    wl, I = inputs(name, L, B)
+    log(f"[in-loop weighted slot] {name} B={wl.batch} L={wl.seq_len}")
+    dev = {k: to_dev(v, wl.dtype) for k, v in I.items()}
+    cfg = gqe.make_config(wl.batch, wl.seq_len, wl.d_model, wl.n_groups, wl.n_experts, wl.top_k,
+                          wl.head_dim, dtype=wl.dtype, router_bias=dev["br"])
+    ws = gqe.alloc_workspace(cfg)
+    shape = (wl.batch, wl.seq_len, wl.d_model)
+    y = torch.empty(shape, dtype=cfg.torch_dtype, device="cuda")
+    gqe.gqe_forward(cfg, dev["x"], dev["wq"], dev["wk"], dev["wv"], dev["wr"], dev["wo"], y, ws)
+    torch.cuda.synchronize()
+    v = gqe.workspace_views(cfg, ws)
+    kG, D = wl.top_k * wl.n_groups, wl.head_dim
+    s = v["s"].double().cpu().numpy()
+    hard = s[..., :kG * D].reshape(wl.batch, wl.seq_len, kG, D)
+    w = v["w"].double().cpu().numpy().reshape(wl.batch, wl.seq_len, kG)
+    ref = np.einsum("blh,blhd->bld", w, hard)
+    got = s[..., (kG + 1) * D:]
+    mag = np.einsum("blh,blhd->bld", np.abs(w), np.abs(hard))  # float32 sums' scale
+    assert (np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + kG * 2.0 ** -23 * mag).all()
+    # the plain output GEMM over the same slot vector: a dense layout of width (kG+2)*d_h
+    cfg_d = gqe.make_config(wl.batch, wl.seq_len, wl.d_model, 2, (kG + 2) // 2, 1, D,
+                            dtype=wl.dtype)
+    wsd = gqe.alloc_workspace(cfg_d, dense=True)
+    gqe.workspace_views(cfg_d, wsd, dense=True)["s"].copy_(v["s"])
+    y2 = torch.empty_like(y)
+    gqe.gqa_output(cfg_d, dev["wo"], y2, wsd)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y), _bits(y2))
