@@ -220,11 +220,12 @@ int gqe_output(const gqe_config* cfg, const void* Wo, void* out, void* workspace
  * dense and the gathered projections share one launch).  Works under HIP
  * graph capture of `stream`, first call included.
  *
- * Short bf16 layers (gqe_forward_is_short) take four launches instead: the
+ * Short bf16 layers (gqe_forward_is_short) take three launches instead: the
  * router beside one dense projection of every expert's query head (with the
  * shared head, K and V^T), the dispatch lists' blocks beside the attention,
- * which reads each slot-head's query row through the routing indices, the
- * weighted slot, and W_O.  The workspace (every view of gqe_ws_layout) and `out` are then
+ * which reads each slot-head's query row through the routing indices, and
+ * W_O with the weighted slot formed in its main loop (as gqe_output does for
+ * every bf16 layer with d_h 64).  The workspace (every view of gqe_ws_layout) and `out` are then
  * bit for bit what the staged calls produce; the workspace also holds the
  * all-heads projection (gqe_workspace_bytes counts it). */
 int gqe_forward(const gqe_config* cfg, const void* x, const void* Wq, const void* Wk,

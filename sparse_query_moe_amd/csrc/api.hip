@@ -359,11 +359,12 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
   return hip_status(launch_attention<T>(p, D, stream, lists));
 }
 
-// Short bf16 layers in four launches: (1) the router's blocks beside one
+// Short bf16 layers in three launches: (1) the router's blocks beside one
 // dense projection of every expert's query head, the shared head, K and V^T
 // (nothing there waits for the routing); (2) the dispatch lists' blocks
 // beside the attention, whose slot-heads read their query rows through the
-// routing indices; (3) the weighted slot; (4) W_O.  Every routed query is projected, G*E
+// routing indices; (3) the output stage (W_O, with the weighted slot formed
+// in its main loop where d_h is 64).  Every routed query is projected, G*E
 // heads instead of the k*G selected (about half again the projection's
 // work), which these lengths absorb: their kernels are bound by latency, and
 // the router and the dispatch leave the critical path.  The workspace ends up
