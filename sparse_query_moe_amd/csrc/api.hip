@@ -359,6 +359,10 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
   return hip_status(launch_attention<T>(p, D, stream, lists));
 }
 
+template <typename T>
+int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool dense,
+                hipStream_t stream);
+
 // Short bf16 layers in three launches: (1) the router's blocks beside one
 // dense projection of every expert's query head, the shared head, K and V^T
 // (nothing there waits for the routing); (2) the dispatch lists' blocks
@@ -369,10 +373,6 @@ int attention_impl(const gqe_config* c, void* ws, bool dense, hipStream_t stream
 // work), which these lengths absorb: their kernels are bound by latency, and
 // the router and the dispatch leave the critical path.  The workspace ends up
 // as after the staged calls: the same idx, w, lists, q, K, V^T, s and lse.
-template <typename T>
-int output_impl(const gqe_config* c, const void* wo, void* out, void* ws, bool dense,
-                hipStream_t stream);
-
 int forward_short(const gqe_config* c, const void* x, const void* wq, const void* wk,
                   const void* wv, const void* wr, const void* wo, void* out, void* ws,
                   hipStream_t stream) {

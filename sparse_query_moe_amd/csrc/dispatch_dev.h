@@ -1,9 +1,10 @@
 // Device side of K2's short-sequence dispatch (per-(b, g, e) token
 // compaction, "sparse scheduling" in the pptc.cn review, section 6): the
 // helpers shared with the chunked path and the one-block-per-(b, g) body, a
-// device function of the (b, g) index so that the dispatch kernel and the
-// short-sequence weighted-slot launch, which runs these blocks beside its own,
-// share it.  The list layout is described in dispatch.hip.
+// device function of the (b, g) index and of its block's LDS, so that the
+// dispatch kernel and the short-sequence attention launch, which runs these
+// blocks first in its grid, share it.  The list layout is described in
+// dispatch.hip.
 #pragma once
 
 #include "debug_check.h"

@@ -3,9 +3,10 @@ MI355X).
 
 bf16 layers of up to 4096 tokens run gqe_forward as one front launch (the
 router beside a dense projection of every expert's query head), the attention
-reading each slot-head's query row through the routing indices, the dispatch
-beside the weighted slot, and W_O.  Longer layers, and the stage entry points,
-run the route / dispatch / gathered projection / attention / output sequence.
+reading each slot-head's query row through the routing indices with the
+dispatch's blocks in its grid, and W_O with the weighted slot formed in its
+main loop.  Longer layers, and the stage entry points, run the route /
+dispatch / gathered projection / attention / output sequence.
 Both compute every value with the same arithmetic in the same order, so the
 whole workspace (routing, lists, slot-major queries, K, V^T, slots, row
 log-sum-exps) and the output must agree bit for bit; each is also held to the
