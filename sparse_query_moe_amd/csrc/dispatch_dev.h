@@ -118,19 +118,49 @@ __device__ __forceinline__ void dispatch_small_block(
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int rounds = (L + 64 * kSmallWaves - 1) / (64 * kSmallWaves);
 
-  // expert ids of this thread's tokens, packed 8 bits each (E <= 32, k_g <= 4 here)
+  // expert ids of this thread's tokens, packed 8 bits each (E <= 32, k_g <= 4
+  // here).  Slot by slot (k_g is the same for the whole block), every round's
+  // load is issued before any is used (tokens past the sequence read token
+  // 0's ids, inside idx), so the rounds share their load latency.
+  const int K = gk.K, ko = gk.koff[g];
+  int32_t raw[kSmallRounds][4];
+  if (k == 2 && ((K | ko) & 1) == 0) {  // the pair as one 8-byte load per token
+#pragma unroll
+    for (int r = 0; r < kSmallRounds; ++r) {
+      const int t = r * 64 * kSmallWaves + wave * 64 + lane;
+      const int2 v = *reinterpret_cast<const int2*>(
+          idx + (static_cast<size_t>(b) * L + (t < L ? t : 0)) * K + ko);
+      raw[r][0] = v.x;
+      raw[r][1] = v.y;
+      raw[r][2] = raw[r][3] = 0xff;
+    }
+  } else {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j < k) {
+#pragma unroll
+      for (int r = 0; r < kSmallRounds; ++r) {
+        const int t = r * 64 * kSmallWaves + wave * 64 + lane;
+        raw[r][j] = idx[(static_cast<size_t>(b) * L + (t < L ? t : 0)) * K + ko + j];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kSmallRounds; ++r) raw[r][j] = 0xff;
+    }
+  }
+  }
   uint32_t packed[kSmallRounds];
 #pragma unroll
   for (int r = 0; r < kSmallRounds; ++r) {
     const int t = r * 64 * kSmallWaves + wave * 64 + lane;
     uint32_t v = 0xffffffffu;
     if (r < rounds && t < L) {
-      const int32_t* p = idx + (static_cast<size_t>(b) * L + t) * gk.K + gk.koff[g];
 #ifdef GQE_DEBUG
-      check_ids(p, k, E, dbg);
+      check_ids(raw[r], k, E, dbg);
 #endif
       v = 0u;
-      for (int j = 0; j < 4; ++j) v |= static_cast<uint32_t>(j < k ? p[j] : 0xff) << (8 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v |= static_cast<uint32_t>(j < k ? raw[r][j] : 0xff) << (8 * j);
     }
     packed[r] = v;
   }
